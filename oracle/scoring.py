@@ -1,0 +1,69 @@
+"""Pooled-key block scoring against the predicted queries, in pinned float32.
+
+Focus-dLLM (abstract; Elamur "Summary"): the predicted queries pick out the most relevant parts of the
+KV cache, so that redundant attention is estimated and skipped.  Prefilling-dLLM (abstract) ranks
+whole prefix chunks first, then tokens inside the chosen chunks.
+
+Readings (the pages give no formula):
+  * a KV unit (block, page or chunk) is represented by the float32 sum of its keys, summed with the
+    pinned tree over its tokens in logical order (a partial last block sums its valid tokens only);
+  * the predicted queries of a KV head's q-head group are summed: a tree over the T slots
+    (non-predicted slots contribute +0.0), then a tree over the group's q-heads padded to a power of
+    two;
+  * a unit's score is the pinned float32 dot product of the two sums; the 1/sqrt(D) scale and mean
+    pooling are left out because a positive scale does not change the ranking;
+  * a token's score (the chunked workload's second level) is the same dot product with that token's
+    key.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .fp32tree import tree_dot, tree_sum, values_f32
+
+
+def pool_keys(k, unit: int) -> np.ndarray:
+    """k [B][Hkv][L][D] -> unit sums [B][Hkv][ceil(L/unit)][D] float32 (tree over each unit's tokens)."""
+    kf = values_f32(k)
+    B, H, L, D = kf.shape
+    n = -(-L // unit)
+    if n * unit != L:
+        kf = np.concatenate([kf, np.zeros((B, H, n * unit - L, D), np.float32)], axis=2)
+    blocks = kf.reshape(B, H, n, unit, D)
+    return tree_sum(blocks, axis=3)
+
+
+def gather_logical(pool, page_table, page_tokens: int) -> np.ndarray:
+    """Paged pool [n_pages][Hkv][P][D] -> logical [B][Hkv][pages_per_seq * P][D] (copy)."""
+    pool = np.asarray(pool)
+    pt = np.asarray(page_table)
+    B, npp = pt.shape
+    _, H, P, D = pool.shape
+    assert P == page_tokens
+    out = pool[pt.reshape(-1)].reshape(B, npp, H, P, D).transpose(0, 2, 1, 3, 4)
+    return out.reshape(B, H, npp * P, D)
+
+
+def query_sum(q, pred_bits, n_kv_heads: int) -> np.ndarray:
+    """q [B][Hq][T][D], pred_bits [B] -> qs [B][Hkv][D] float32."""
+    qf = values_f32(q)
+    B, Hq, T, D = qf.shape
+    G = Hq // n_kv_heads
+    sel = np.zeros((B, T), dtype=bool)
+    for b in range(B):
+        v = int(pred_bits[b])
+        sel[b] = [(v >> p) & 1 for p in range(T)]
+    masked_q = np.where(sel[:, None, :, None], qf, np.float32(0.0)).astype(np.float32)
+    per_head = tree_sum(masked_q, axis=2)                         # [B][Hq][D]
+    grouped = per_head.reshape(B, n_kv_heads, G, D)
+    return tree_sum(grouped, axis=2)                              # [B][Hkv][D]
+
+
+def unit_scores(qs, ks) -> np.ndarray:
+    """qs [B][Hkv][D], ks [B][Hkv][n][D] -> [B][Hkv][n] float32."""
+    return tree_dot(np.asarray(qs, np.float32)[:, :, None, :], ks)
+
+
+def token_scores(qs, k_tokens) -> np.ndarray:
+    """qs [B][Hkv][D], k_tokens [B][Hkv][n][D] (bf16 bits or float32) -> [B][Hkv][n] float32."""
+    return tree_dot(np.asarray(qs, np.float32)[:, :, None, :], values_f32(k_tokens))
