@@ -1,0 +1,329 @@
+// libfdllm C ABI: argument validation, the handle and its workspace, and kernel launches.
+// Every check happens on the host before anything is launched; device-side conditions are latched
+// into the handle's status word.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "fdl_device.h"
+#include "fdl_internal.h"
+
+using fdl::Geom;
+
+namespace {
+
+fdl_status fail(fdl_handle h, fdl_status s, const char* fmt, ...) {
+  if (h) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(h->last_error, sizeof(h->last_error), fmt, ap);
+    va_end(ap);
+  }
+  return s;
+}
+
+fdl_status hip_status(fdl_handle h, hipError_t e, const char* what) {
+  if (e == hipSuccess) return FDL_OK;
+  return fail(h, FDL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(long long x) {
+  int l = 0;
+  while ((1LL << l) < x) ++l;
+  return l;
+}
+
+fdl_status check_geom(fdl_handle h, const fdl_geom* g, Geom& o) {
+  if (!g) return fail(h, FDL_EINVAL, "geom is NULL");
+  if (g->batch < 1) return fail(h, FDL_EINVAL, "batch must be >= 1");
+  if (g->n_kv_heads < 1 || g->n_q_heads < g->n_kv_heads || g->n_q_heads % g->n_kv_heads)
+    return fail(h, FDL_EINVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (g->n_q_heads / g->n_kv_heads > 8)
+    return fail(h, FDL_EUNSUPPORTED, "more than 8 query heads per KV head");
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return fail(h, FDL_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (g->ctx_len < 0) return fail(h, FDL_EINVAL, "ctx_len must be >= 0");
+  if (g->ctx_len >= (1 << 24)) return fail(h, FDL_EUNSUPPORTED, "ctx_len must be < 2^24");
+  if (!is_pow2(g->kv_block) || g->kv_block > 4096)
+    return fail(h, FDL_EINVAL, "kv_block must be a power of two in [1, 4096]");
+  if (g->dec_len < 1 || g->dec_len > 64) return fail(h, FDL_EINVAL, "dec_len must be in [1, 64]");
+  if (g->dtype != FDL_F32 && g->dtype != FDL_BF16) return fail(h, FDL_EINVAL, "unknown dtype");
+  if (g->paged) {
+    if (!is_pow2(g->page_tokens) || g->page_tokens > 4096)
+      return fail(h, FDL_EINVAL, "page_tokens must be a power of two in [1, 4096]");
+    if (g->pages_per_seq < 1 || (long long)g->pages_per_seq * g->page_tokens < g->ctx_len)
+      return fail(h, FDL_EINVAL, "pages_per_seq * page_tokens must cover ctx_len");
+    if (g->n_pages < 1) return fail(h, FDL_EINVAL, "n_pages must be >= 1");
+  }
+  o.B = g->batch;
+  o.Hq = g->n_q_heads;
+  o.Hkv = g->n_kv_heads;
+  o.G = g->n_q_heads / g->n_kv_heads;
+  o.D = g->head_dim;
+  o.L = g->ctx_len;
+  o.bt = g->kv_block;
+  o.T = g->dec_len;
+  o.dtype = g->dtype;
+  o.paged = g->paged ? 1 : 0;
+  o.page_tokens = g->paged ? g->page_tokens : 1;
+  o.page_log2 = g->paged ? ilog2(g->page_tokens) : 0;
+  o.pps = g->paged ? g->pages_per_seq : 0;
+  o.n_pages = g->paged ? g->n_pages : 0;
+  return FDL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fdl_status_string(fdl_status s) {
+  switch (s) {
+    case FDL_OK: return "ok";
+    case FDL_EINVAL: return "invalid argument";
+    case FDL_ENOMEM: return "out of memory (workspace too small or allocation failed)";
+    case FDL_EHIP: return "HIP runtime error";
+    case FDL_EOVERFLOW: return "device-side capacity overflow (sinks or sink candidates)";
+    case FDL_EUNSUPPORTED: return "shape outside the supported kernel set";
+    case FDL_EINDEX: return "out-of-range unit or page index (rows skipped)";
+  }
+  return "unknown status";
+}
+
+const char* fdl_last_error(fdl_handle h) { return h ? h->last_error : "no handle"; }
+
+fdl_status fdl_create(fdl_handle* out, void* hip_stream, size_t workspace_bytes) {
+  if (!out) return FDL_EINVAL;
+  *out = nullptr;
+  if (workspace_bytes == 0) workspace_bytes = (size_t)64 << 20;
+  if (workspace_bytes < fdl::kHeaderBytes + ((size_t)1 << 20))
+    workspace_bytes = fdl::kHeaderBytes + ((size_t)1 << 20);
+  fdl_ctx* h = new (std::nothrow) fdl_ctx();
+  if (!h) return FDL_ENOMEM;
+  h->stream = static_cast<hipStream_t>(hip_stream);
+  if (hipGetDevice(&h->device) != hipSuccess ||
+      hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device) !=
+          hipSuccess) {
+    delete h;
+    return FDL_EHIP;
+  }
+  void* ws = nullptr;
+  if (hipMalloc(&ws, workspace_bytes) != hipSuccess) {
+    delete h;
+    return FDL_ENOMEM;
+  }
+  if (hipMemset(ws, 0, fdl::kHeaderBytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(ws);
+    delete h;
+    return FDL_EHIP;
+  }
+  h->ws = static_cast<char*>(ws);
+  h->ws_bytes = workspace_bytes;
+  h->status = reinterpret_cast<uint32_t*>(h->ws);
+  h->tickets = reinterpret_cast<uint32_t*>(h->ws + fdl::kTicketOffset);
+  h->counters = reinterpret_cast<uint32_t*>(h->ws + fdl::kCounterOffset);
+  h->scratch = h->ws + fdl::kHeaderBytes;
+  h->scratch_bytes = workspace_bytes - fdl::kHeaderBytes;
+  h->last_error[0] = 0;
+  *out = h;
+  return FDL_OK;
+}
+
+fdl_status fdl_destroy(fdl_handle h) {
+  if (!h) return FDL_EINVAL;
+  (void)hipStreamSynchronize(h->stream);
+  (void)hipFree(h->ws);
+  delete h;
+  return FDL_OK;
+}
+
+fdl_status fdl_set_stream(fdl_handle h, void* hip_stream) {
+  if (!h) return FDL_EINVAL;
+  h->stream = static_cast<hipStream_t>(hip_stream);
+  return FDL_OK;
+}
+
+fdl_status fdl_get_status(fdl_handle h) {
+  if (!h) return FDL_EINVAL;
+  fdl_status st = hip_status(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+  if (st != FDL_OK) return st;
+  uint32_t word = 0;
+  st = hip_status(h, hipMemcpy(&word, h->status, sizeof(word), hipMemcpyDeviceToHost), "hipMemcpy");
+  if (st != FDL_OK) return st;
+  if (word) {
+    st = hip_status(h, hipMemset(h->status, 0, sizeof(uint32_t)), "hipMemset");
+    if (st != FDL_OK) return st;
+    st = hip_status(h, hipDeviceSynchronize(), "hipDeviceSynchronize");
+    if (st != FDL_OK) return st;
+  }
+  if (word & (fdl::ST_SINK_OVERFLOW | fdl::ST_CAND_OVERFLOW)) return FDL_EOVERFLOW;
+  if (word & fdl::ST_BAD_INDEX) return FDL_EINDEX;
+  return FDL_OK;
+}
+
+fdl_status fdl_pool_keys(fdl_handle h, const fdl_geom* gp, const void* k_cache,
+                         const int32_t* page_table, int32_t unit_tokens, float* ks) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!k_cache || !ks) return fail(h, FDL_EINVAL, "k_cache and ks must be non-NULL");
+  if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
+  if (!is_pow2(unit_tokens) || unit_tokens > 4096)
+    return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
+  return hip_status(h, fdl::launch_pool_keys(h->stream, g, k_cache, page_table, ilog2(unit_tokens), ks,
+                                             h->status),
+                    "pool_keys launch");
+}
+
+fdl_status fdl_predict_queries(fdl_handle h, int32_t batch, int32_t dec_len, const float* prev_conf,
+                               const uint8_t* masked, int32_t top_k, int32_t window,
+                               uint64_t* pred_mask, int32_t* n_pred) {
+  if (!h) return FDL_EINVAL;
+  if (batch < 1) return fail(h, FDL_EINVAL, "batch must be >= 1");
+  if (dec_len < 1 || dec_len > 64) return fail(h, FDL_EINVAL, "dec_len must be in [1, 64]");
+  if (top_k < 0) return fail(h, FDL_EINVAL, "top_k must be >= 0");
+  if (window < 0) return fail(h, FDL_EINVAL, "window must be >= 0");
+  if (!masked || !pred_mask || !n_pred)
+    return fail(h, FDL_EINVAL, "masked, pred_mask and n_pred must be non-NULL");
+  return hip_status(h, fdl::launch_predict(h->stream, batch, dec_len, prev_conf, masked, top_k, window,
+                                           pred_mask, n_pred),
+                    "predict launch");
+}
+
+fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* gp, const void* q, const uint64_t* pred_mask,
+                            const float* ks, int32_t unit_tokens, const int32_t* cand_idx,
+                            int32_t n_cand, const void* k_cache, const void* k_dec,
+                            const int32_t* page_table, float* scores, int32_t detect_sinks,
+                            float sink_tau, int32_t max_sinks, int32_t* sink_pos, int32_t* n_sinks) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!q || !pred_mask || !scores) return fail(h, FDL_EINVAL, "q, pred_mask and scores must be non-NULL");
+  if (!is_pow2(unit_tokens) || unit_tokens > 4096)
+    return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
+  const int n_units = (g.L + unit_tokens - 1) / unit_tokens;
+  if (cand_idx) {
+    if (detect_sinks) return fail(h, FDL_EINVAL, "sink detection is a level-1 (cand_idx == NULL) option");
+    if (n_cand < 1 || n_cand > n_units) return fail(h, FDL_EINVAL, "n_cand must be in [1, n_units]");
+    if (!k_cache) return fail(h, FDL_EINVAL, "level-2 scoring needs k_cache");
+    if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
+    if (g.L % unit_tokens) return fail(h, FDL_EINVAL, "level-2 scoring needs ctx_len %% unit_tokens == 0");
+    return hip_status(h, fdl::launch_score_tokens(h->stream, g, q, pred_mask, k_cache, page_table,
+                                                  ilog2(unit_tokens), cand_idx, n_cand, scores,
+                                                  h->status),
+                      "score_tokens launch");
+  }
+  if (!ks) return fail(h, FDL_EINVAL, "level-1 scoring needs ks");
+  int ns = 0, cap = 0;
+  size_t need = 0;
+  if (detect_sinks) {
+    if (!k_cache || !k_dec || !sink_pos || !n_sinks)
+      return fail(h, FDL_EINVAL, "sink detection needs k_cache, k_dec, sink_pos and n_sinks");
+    if (g.paged) return fail(h, FDL_EUNSUPPORTED, "sink detection reads a contiguous cache");
+    if (!(sink_tau > 0.f)) return fail(h, FDL_EINVAL, "sink_tau must be > 0");
+    if (max_sinks < 1) return fail(h, FDL_EINVAL, "max_sinks must be >= 1");
+    if (g.Hq > 255) return fail(h, FDL_EUNSUPPORTED, "sink detection supports up to 255 q-heads");
+    if (g.dtype == FDL_BF16 && g.T > 32)
+      return fail(h, FDL_EUNSUPPORTED, "bf16 sink detection needs dec_len <= 32");
+    need = fdl::sink_scratch_bytes(g, &ns, &cap);
+    if (need > h->scratch_bytes) return fail(h, FDL_ENOMEM, "workspace too small for sink detection");
+  }
+  st = hip_status(h, fdl::launch_score_units(h->stream, g, q, pred_mask, ks, n_units, scores),
+                  "score_units launch");
+  if (st != FDL_OK || !detect_sinks) return st;
+  return hip_status(h, fdl::launch_sinks(h->stream, g, q, pred_mask, k_cache, k_dec, sink_tau, max_sinks,
+                                         sink_pos, n_sinks, h->scratch, ns, cap, h->status,
+                                         h->num_cus),
+                    "sinks launch");
+}
+
+fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* gp, const float* scores, int32_t n_units,
+                             int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
+                             int32_t max_sinks, const int32_t* cand_idx, int32_t n_cand,
+                             int32_t top_k, int32_t force_first, int32_t max_sel, int32_t* sel_idx,
+                             int32_t* n_sel) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!scores || !sel_idx || !n_sel) return fail(h, FDL_EINVAL, "scores, sel_idx and n_sel must be non-NULL");
+  if (!is_pow2(unit_tokens) || unit_tokens > 8192)
+    return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 8192]");
+  if (n_units < 0 || n_units > 8192) return fail(h, FDL_EUNSUPPORTED, "n_units must be in [0, 8192]");
+  if (top_k < 0) return fail(h, FDL_EINVAL, "top_k must be >= 0");
+  if (max_sel < 1) return fail(h, FDL_EINVAL, "max_sel must be >= 1");
+  if (cand_idx) {
+    if (n_cand < 1 || n_cand > n_units) return fail(h, FDL_EINVAL, "n_cand must be in [1, n_units]");
+    const int ff = force_first ? 1 : 0;
+    if (top_k > unit_tokens - ff) return fail(h, FDL_EINVAL, "top_k exceeds the tokens of a unit");
+    if ((long long)n_cand * (ff + top_k) > max_sel) return fail(h, FDL_EINVAL, "max_sel too small");
+  } else {
+    if ((sink_pos == nullptr) != (n_sinks == nullptr))
+      return fail(h, FDL_EINVAL, "sink_pos and n_sinks go together");
+    if (sink_pos && max_sinks < 1) return fail(h, FDL_EINVAL, "max_sinks must be >= 1");
+    const long long forced_cap = sink_pos ? max_sinks : 0;
+    long long need = forced_cap + top_k;
+    if (need > n_units) need = n_units;
+    if (need > max_sel) return fail(h, FDL_EINVAL, "max_sel must cover min(n_units, max_sinks + top_k)");
+  }
+  return hip_status(h, fdl::launch_select(h->stream, g, scores, n_units, ilog2(unit_tokens), sink_pos,
+                                          n_sinks, max_sinks, cand_idx, n_cand, top_k,
+                                          force_first ? 1 : 0, max_sel, sel_idx, n_sel, h->status),
+                    "select launch");
+}
+
+static fdl_status attn_common(fdl_handle h, const fdl_geom* gp, const void* q, const void* k_cache,
+                              const void* v_cache, const void* k_dec, const void* v_dec,
+                              const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
+                              int32_t max_sel, int32_t sel_unit_tokens, int dense, void* out) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!q || !k_dec || !v_dec || !out) return fail(h, FDL_EINVAL, "q, k_dec, v_dec and out must be non-NULL");
+  if (g.L > 0 && (!k_cache || !v_cache)) return fail(h, FDL_EINVAL, "k_cache and v_cache must be non-NULL");
+  if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
+  int unit_log2 = 0;
+  long long list_tokens = g.L;
+  if (!dense) {
+    if (!sel_idx || !n_sel) return fail(h, FDL_EINVAL, "sel_idx and n_sel must be non-NULL");
+    if (max_sel < 1) return fail(h, FDL_EINVAL, "max_sel must be >= 1");
+    if (!is_pow2(sel_unit_tokens) || sel_unit_tokens > 4096)
+      return fail(h, FDL_EINVAL, "sel_unit_tokens must be a power of two in [1, 4096]");
+    unit_log2 = ilog2(sel_unit_tokens);
+    list_tokens = (long long)max_sel * sel_unit_tokens;
+    if (list_tokens > g.L) list_tokens = g.L;
+    if ((long long)max_sel * sel_unit_tokens >= (1LL << 30)) return fail(h, FDL_EUNSUPPORTED, "selection too large");
+  }
+  int n_splits = 1;
+  if (g.dtype == FDL_BF16) {
+    if (g.T > 32) return fail(h, FDL_EUNSUPPORTED, "bf16 attention needs dec_len <= 32");
+    n_splits = fdl::attn_choose_splits(g, list_tokens, h->num_cus);
+    while (n_splits > 1 && fdl::attn_scratch_bytes(g, n_splits) > h->scratch_bytes) n_splits /= 2;
+  }
+  return hip_status(h, fdl::launch_attn(h->stream, g, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx,
+                                        n_sel, max_sel, unit_log2, dense, out, h->scratch, n_splits,
+                                        h->tickets, h->status),
+                    "attention launch");
+}
+
+fdl_status fdl_sparse_attn(fdl_handle h, const fdl_geom* g, const void* q, const void* k_cache,
+                           const void* v_cache, const void* k_dec, const void* v_dec,
+                           const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
+                           int32_t max_sel, int32_t sel_unit_tokens, void* out) {
+  return attn_common(h, g, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel,
+                     sel_unit_tokens, 0, out);
+}
+
+fdl_status fdl_dense_attn(fdl_handle h, const fdl_geom* g, const void* q, const void* k_cache,
+                          const void* v_cache, const void* k_dec, const void* v_dec,
+                          const int32_t* page_table, void* out) {
+  return attn_common(h, g, q, k_cache, v_cache, k_dec, v_dec, page_table, nullptr, nullptr, 0, 1, 1, out);
+}
+
+}  // extern "C"

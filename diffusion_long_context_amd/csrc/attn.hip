@@ -1,0 +1,617 @@
+// Bidirectional attention of the decode block's queries over a gathered set of KV tokens.
+//
+// Focus-dLLM (abstract; Elamur "Summary"): the sparse step runs ordinary bidirectional attention for
+// the current block's queries over only the selected KV (plus the block itself); shallow layers and
+// the vanilla baseline run it over everything.  Prefilling-dLLM (abstract): the same over chunk KV
+// that sits non-contiguously in a paged cache.
+//
+// bf16 path (the hot one): one workgroup of 4 waves per (split, KV head, sequence) handles all G
+// q-heads of the KV head over a contiguous share of the gathered 64-token tiles (tile 0 is the
+// block's own tokens).  Tiles are read from HBM with coalesced 16-byte loads into registers one
+// round ahead, staged in LDS, and consumed by bf16 MFMA (32x32x16, f32 accumulate):
+//   S^T = K Q^T   (A = K rows from LDS, B = Q fragments held in registers),
+//   O^T = V^T P^T (A = V columns from LDS, B = the probabilities straight from the S^T registers),
+// which keeps every softmax statistic in the lane that owns its query, so the online softmax needs
+// one cross-lane exchange per tile.  Within a workgroup, waves that share a head merge through LDS;
+// across workgroups the partial (max, sum, O) go to scratch and the last workgroup of each KV head,
+// found with an atomic ticket, merges them and writes the bf16 output.
+//
+// float32 path: a plain per-query-row kernel for the small float32 workload.
+#include "fdl_device.h"
+#include "fdl_internal.h"
+
+namespace fdl {
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* k_dec;
+  const uint16_t* v_dec;
+  const int32_t* sel_idx;
+  const int32_t* n_sel;
+  uint16_t* out;
+  float* part_o;     // [B][Hq][S][32][D]
+  float2* part_ml;   // [B][Hq][S][32]  (max in log2 units, sum)
+  uint32_t* tickets;
+  uint32_t* status;
+  KvLayout lay;
+  int Hq, T, max_sel, unit_log2, n_units, dense, n_splits;
+  float scale_log2;  // log2(e) / sqrt(D)
+};
+
+// Source row of tile `e` (0 = the block's own tokens), row r; nullptr if the row is empty.
+template <int D>
+__device__ __forceinline__ const uint16_t* attn_row(const AttnParams& p, int b, int g, int e, int r,
+                                                    bool is_v, int n_list,
+                                                    const int32_t* __restrict__ sel_row) {
+  if (e == 0) {
+    if (r >= p.T) return nullptr;
+    return (is_v ? p.v_dec : p.k_dec) + ((int64_t)(b * p.lay.Hkv + g) * p.T + r) * D;
+  }
+  const int i = (e - 1) * 64 + r;
+  if (i >= n_list) return nullptr;
+  int t = i;
+  if (!p.dense) {
+    const int u = sel_row[i >> p.unit_log2];
+    if ((unsigned)u >= (unsigned)p.n_units) {
+      latch(p.status, ST_BAD_INDEX);
+      return nullptr;
+    }
+    t = (u << p.unit_log2) + (i & ((1 << p.unit_log2) - 1));
+  }
+  if (t >= p.lay.L) return nullptr;
+  int64_t off;
+  if (!p.lay.row_offset(b, g, t, off, p.status)) return nullptr;
+  return (is_v ? p.v : p.k) + off;
+}
+
+template <int G>
+struct AttnShape {
+  static constexpr int TPR = G == 1 ? 4 : (G == 2 ? 2 : 1);   // tiles per round
+  static constexpr int NW = G > 4 ? 8 : 4;                      // waves per workgroup
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(AttnShape<G>::NW * 64, 1) void attn_mfma_kernel(const AttnParams p) {
+  constexpr int TPR = AttnShape<G>::TPR;
+  constexpr int NW = AttnShape<G>::NW;
+  constexpr int NT = NW * 64;
+  constexpr int HPW = 1;                                // heads per wave
+  constexpr int RS = D + 8;                             // LDS row stride (elements)
+  constexpr int TILE = 64 * RS;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int PROW = D / 8;                           // 16-byte pieces per row
+  constexpr int PTILE = 64 * PROW;
+  constexpr int PPT = TPR * 2 * PTILE / NT;             // pieces per thread per round
+  static_assert((TPR * 2 * PTILE) % NT == 0 && PTILE % NT == 0, "pieces must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[TPR * 2 * TILE];
+  __shared__ float2 s_ml[4][32];
+  __shared__ uint32_t s_ticket;
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 31, hh = lane >> 5;
+  const int Hkv = p.lay.Hkv;
+  const int64_t seg = (int64_t)b * Hkv + g;
+  const int S = p.n_splits;
+
+  int n_list;
+  if (p.dense) {
+    n_list = p.lay.L;
+  } else {
+    int ns = p.n_sel[seg];
+    ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
+    n_list = ns << p.unit_log2;
+  }
+  const int n_tiles = 1 + (n_list + 63) / 64;
+  const int e0 = (int)((int64_t)n_tiles * s / S);
+  const int e1 = (int)((int64_t)n_tiles * (s + 1) / S);
+  const int32_t* sel_row = p.sel_idx + seg * p.max_sel;
+
+  const int slot = (TPR > 1) ? wave / G : 0;
+  int heads[HPW];
+#pragma unroll
+  for (int hi = 0; hi < HPW; ++hi) heads[hi] = (TPR > 1) ? wave % G : wave + NW * hi;
+
+  // Q fragments (B operand of S^T = K Q^T): lane (q, hh) holds q[q][hh*D/2 + 8ks .. +8]
+  bf16x8 qf[HPW][KS];
+#pragma unroll
+  for (int hi = 0; hi < HPW; ++hi) {
+    const int h = g * G + heads[hi];
+    const bool live = heads[hi] < G && ql < p.T;
+    const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.T + ql) * D + hh * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (live) v = *reinterpret_cast<const uint4*>(qrow + ks * 8);
+      qf[hi][ks] = as_bf16x8(v);
+    }
+  }
+
+  f32x16 oacc[HPW][DT];
+  float m_run[HPW], l_run[HPW];
+#pragma unroll
+  for (int hi = 0; hi < HPW; ++hi) {
+    m_run[hi] = -__builtin_inff();
+    l_run[hi] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[hi][dt][r] = 0.f;
+  }
+
+  const int rounds = (e1 - e0 + TPR - 1) / TPR;
+  uint4 stage[PPT];
+
+  auto load_round = [&](int rnd) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int pc = tid + NT * j;
+      const int sl = pc / (2 * PTILE);
+      const int isv = (pc / PTILE) & 1;
+      const int rem = pc % PTILE;
+      const int row = rem / PROW, chunk = rem % PROW;
+      const int e = e0 + rnd * TPR + sl;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (e < e1) {
+        const uint16_t* src = attn_row<D>(p, b, g, e, row, isv != 0, n_list, sel_row);
+        if (src) v = *reinterpret_cast<const uint4*>(src + chunk * 8);
+      }
+      stage[j] = v;
+    }
+  };
+  auto store_round = [&]() {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int pc = tid + NT * j;
+      const int sl = pc / (2 * PTILE);
+      const int isv = (pc / PTILE) & 1;
+      const int rem = pc % PTILE;
+      const int row = rem / PROW, chunk = rem % PROW;
+      *reinterpret_cast<uint4*>(lds + (sl * 2 + isv) * TILE + row * RS + chunk * 8) = stage[j];
+    }
+  };
+
+  if (rounds > 0) load_round(0);
+  for (int rnd = 0; rnd < rounds; ++rnd) {
+    store_round();
+    __syncthreads();
+    if (rnd + 1 < rounds) load_round(rnd + 1);
+    const int e = e0 + rnd * TPR + slot;
+    if (e < e1) {
+      const bool rv = attn_row<D>(p, b, g, e, lane, false, n_list, sel_row) != nullptr;
+      const uint64_t vm = __ballot(rv);
+      const uint16_t* Kt = lds + (slot * 2) * TILE;
+      const uint16_t* Vt = Kt + TILE;
+#pragma unroll
+      for (int hi = 0; hi < HPW; ++hi) {
+        if (heads[hi] >= G) continue;
+        f32x16 sacc[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[st][r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const uint4 a = *reinterpret_cast<const uint4*>(Kt + (st * 32 + ql) * RS + hh * (D / 2) + ks * 8);
+            sacc[st] = mfma32(as_bf16x8(a), qf[hi][ks], sacc[st]);
+          }
+        }
+        // S^T register r of sub-tile st is token st*32 + 8*(r/4) + 4*hh + r%4 for query ql
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = st * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            float x = sacc[st][r] * p.scale_log2;
+            if (!((vm >> row) & 1ull)) x = -__builtin_inff();
+            sacc[st][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[hi], mx);
+        if (m_new == -__builtin_inff()) continue;   // nothing valid seen yet
+        const float alpha = exp2f(m_run[hi] - m_new);
+        float rs = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = exp2f(sacc[st][r] - m_new);
+            sacc[st][r] = pr;
+            rs += pr;
+          }
+        rs += wave_shfl_xor(rs, 32);
+        l_run[hi] = l_run[hi] * alpha + rs;
+        m_run[hi] = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[hi][dt][r] *= alpha;
+        // O^T += V^T P^T over 4 k-steps of 16 tokens
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int kl = 0; kl < 2; ++kl) {
+            uint4 pb;
+            pb.x = pack_bf16x2(sacc[st][8 * kl + 0], sacc[st][8 * kl + 1]);
+            pb.y = pack_bf16x2(sacc[st][8 * kl + 2], sacc[st][8 * kl + 3]);
+            pb.z = pack_bf16x2(sacc[st][8 * kl + 4], sacc[st][8 * kl + 5]);
+            pb.w = pack_bf16x2(sacc[st][8 * kl + 6], sacc[st][8 * kl + 7]);
+            const bf16x8 bfr = as_bf16x8(pb);
+            const int r0 = st * 32 + 16 * kl + 4 * hh;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const uint16_t* col = Vt + dt * 32 + ql;
+              uint4 av;
+              av.x = (uint32_t)col[(r0 + 0) * RS] | ((uint32_t)col[(r0 + 1) * RS] << 16);
+              av.y = (uint32_t)col[(r0 + 2) * RS] | ((uint32_t)col[(r0 + 3) * RS] << 16);
+              av.z = (uint32_t)col[(r0 + 8) * RS] | ((uint32_t)col[(r0 + 9) * RS] << 16);
+              av.w = (uint32_t)col[(r0 + 10) * RS] | ((uint32_t)col[(r0 + 11) * RS] << 16);
+              oacc[hi][dt] = mfma32(as_bf16x8(av), bfr, oacc[hi][dt]);
+            }
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- this workgroup's result per head: (m, l, O) ------------------------------------------
+  float* po_base = p.part_o;
+  float2* pml_base = p.part_ml;
+  if constexpr (TPR == 1) {
+    // one wave owns each head: write straight from registers
+#pragma unroll
+    for (int hi = 0; hi < HPW; ++hi) {
+      if (heads[hi] >= G) continue;
+      const int h = g * G + heads[hi];
+      const int64_t hb = (int64_t)b * p.Hq + h;
+      if (S == 1) {
+        if (ql < p.T) {
+          const float inv = 1.f / l_run[hi];
+          uint16_t* orow = p.out + (hb * p.T + ql) * D;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const int d0 = dt * 32 + 8 * rg + 4 * hh;
+              uint2 w;
+              w.x = pack_bf16x2(oacc[hi][dt][4 * rg] * inv, oacc[hi][dt][4 * rg + 1] * inv);
+              w.y = pack_bf16x2(oacc[hi][dt][4 * rg + 2] * inv, oacc[hi][dt][4 * rg + 3] * inv);
+              *reinterpret_cast<uint2*>(orow + d0) = w;
+            }
+        }
+      } else {
+        float* po = po_base + ((hb * S + s) * 32 + ql) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int d0 = dt * 32 + 8 * rg + 4 * hh;
+            *reinterpret_cast<float4*>(po + d0) =
+                make_float4(oacc[hi][dt][4 * rg], oacc[hi][dt][4 * rg + 1], oacc[hi][dt][4 * rg + 2],
+                            oacc[hi][dt][4 * rg + 3]);
+          }
+        if (hh == 0) pml_base[(hb * S + s) * 32 + ql] = make_float2(m_run[hi], l_run[hi]);
+      }
+    }
+  } else {
+    // waves sharing a head merge through LDS (tiles are no longer needed)
+    constexpr int OS = D + 4;
+    float* mo = reinterpret_cast<float*>(lds);
+    const int id = heads[0] * TPR + slot;   // unique per wave
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = dt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        mo[(id * 32 + ql) * OS + d] = oacc[0][dt][r];
+      }
+    if (hh == 0) s_ml[id][ql] = make_float2(m_run[0], l_run[0]);
+    __syncthreads();
+    // thread -> (head j, query q, 4 dims)
+    constexpr int ITEMS = G * 32 * (D / 4);
+    for (int it = tid; it < ITEMS; it += NT) {
+      const int j = it / (32 * (D / 4));
+      const int q = (it / (D / 4)) % 32;
+      const int d0 = (it % (D / 4)) * 4;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < TPR; ++t) M = fmaxf(M, s_ml[j * TPR + t][q].x);
+      float Ls = 0.f;
+      float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (M != -__builtin_inff()) {
+#pragma unroll
+        for (int t = 0; t < TPR; ++t) {
+          const float2 ml = s_ml[j * TPR + t][q];
+          if (ml.y == 0.f) continue;
+          const float w = exp2f(ml.x - M);
+          Ls += ml.y * w;
+          const float* src = mo + ((j * TPR + t) * 32 + q) * OS + d0;
+          O.x += src[0] * w;
+          O.y += src[1] * w;
+          O.z += src[2] * w;
+          O.w += src[3] * w;
+        }
+      }
+      const int h = g * G + j;
+      const int64_t hb = (int64_t)b * p.Hq + h;
+      if (S == 1) {
+        if (q < p.T) {
+          const float inv = 1.f / Ls;
+          uint2 w;
+          w.x = pack_bf16x2(O.x * inv, O.y * inv);
+          w.y = pack_bf16x2(O.z * inv, O.w * inv);
+          *reinterpret_cast<uint2*>(p.out + (hb * p.T + q) * D + d0) = w;
+        }
+      } else {
+        *reinterpret_cast<float4*>(po_base + ((hb * S + s) * 32 + q) * D + d0) = O;
+        if (d0 == 0) pml_base[(hb * S + s) * 32 + q] = make_float2(M, Ls);
+      }
+    }
+  }
+  if (S == 1) return;
+
+  // ---- cross-split merge by the last workgroup of this KV head --------------------------------
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg], 1u);
+  __syncthreads();
+  if (s_ticket != (uint32_t)(S - 1)) return;
+  __threadfence();
+  constexpr int ITEMS = G * 32 * (D / 4);
+  for (int it = tid; it < ITEMS; it += NT) {
+    const int j = it / (32 * (D / 4));
+    const int q = (it / (D / 4)) % 32;
+    const int d0 = (it % (D / 4)) * 4;
+    if (q >= p.T) continue;
+    const int64_t hb = (int64_t)b * p.Hq + g * G + j;
+    const float2* ml = pml_base + hb * S * 32 + q;
+    float M = -__builtin_inff();
+    for (int t = 0; t < S; ++t) M = fmaxf(M, ml[t * 32].x);
+    float Ls = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int t = 0; t < S; ++t) {
+      const float2 v = ml[t * 32];
+      if (v.y == 0.f) continue;
+      const float w = exp2f(v.x - M);
+      Ls += v.y * w;
+      const float4 o = *reinterpret_cast<const float4*>(po_base + ((hb * S + t) * 32 + q) * D + d0);
+      O.x += o.x * w;
+      O.y += o.y * w;
+      O.z += o.z * w;
+      O.w += o.w * w;
+    }
+    const float inv = 1.f / Ls;
+    uint2 w;
+    w.x = pack_bf16x2(O.x * inv, O.y * inv);
+    w.y = pack_bf16x2(O.z * inv, O.w * inv);
+    *reinterpret_cast<uint2*>(p.out + (hb * p.T + q) * D + d0) = w;
+  }
+  if (tid == 0) p.tickets[seg] = 0u;
+}
+
+// ------------------------------------------------------------------------------------------------
+// float32 path: one thread per query row, 32-token chunks staged in LDS.
+// ------------------------------------------------------------------------------------------------
+
+struct F32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* k_dec;
+  const float* v_dec;
+  const int32_t* sel_idx;
+  const int32_t* n_sel;
+  float* out;
+  uint32_t* status;
+  KvLayout lay;
+  int Hq, G, T, max_sel, unit_log2, n_units, dense;
+  float scale;
+};
+
+template <int D>
+__device__ __forceinline__ const float* f32_row(const F32Params& p, int b, int g, int i, bool is_v,
+                                                int n_list, const int32_t* sel_row) {
+  // i < T: own block row i; else list position i - T
+  if (i < p.T) return (is_v ? p.v_dec : p.k_dec) + ((int64_t)(b * p.lay.Hkv + g) * p.T + i) * D;
+  i -= p.T;
+  if (i >= n_list) return nullptr;
+  int t = i;
+  if (!p.dense) {
+    const int u = sel_row[i >> p.unit_log2];
+    if ((unsigned)u >= (unsigned)p.n_units) {
+      latch(p.status, ST_BAD_INDEX);
+      return nullptr;
+    }
+    t = (u << p.unit_log2) + (i & ((1 << p.unit_log2) - 1));
+  }
+  if (t >= p.lay.L) return nullptr;
+  int64_t off;
+  if (!p.lay.row_offset(b, g, t, off, p.status)) return nullptr;
+  return (is_v ? p.v : p.k) + off;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(const F32Params p) {
+  __shared__ float kc[32][D + 1];
+  __shared__ float vc[32][D + 1];
+  __shared__ int valid[32];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int g = h / p.G;
+  const int qi = threadIdx.x;
+  const int64_t seg = (int64_t)b * p.lay.Hkv + g;
+  int n_list;
+  if (p.dense) {
+    n_list = p.lay.L;
+  } else {
+    int ns = p.n_sel[seg];
+    ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
+    n_list = ns << p.unit_log2;
+  }
+  const int32_t* sel_row = p.sel_idx + seg * p.max_sel;
+  const int total = p.T + n_list;
+  float qr[D], o[D];
+  const bool live = qi < p.T;
+  const float* qrow = p.q + (((int64_t)b * p.Hq + h) * p.T + (live ? qi : 0)) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qr[d] = live ? qrow[d] : 0.f;
+    o[d] = 0.f;
+  }
+  float m = -__builtin_inff(), l = 0.f;
+  for (int c0 = 0; c0 < total; c0 += 32) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 32 * D; idx += 64) {
+      const int r = idx / D, d = idx % D;
+      const float* ks = (c0 + r < total) ? f32_row<D>(p, b, g, c0 + r, false, n_list, sel_row) : nullptr;
+      const float* vs = ks ? f32_row<D>(p, b, g, c0 + r, true, n_list, sel_row) : nullptr;
+      kc[r][d] = ks ? ks[d] : 0.f;
+      vc[r][d] = vs ? vs[d] : 0.f;
+      if (d == 0) valid[r] = ks != nullptr;
+    }
+    __syncthreads();
+    float sc[32];
+    float mx = -__builtin_inff();
+    for (int r = 0; r < 32; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc += qr[d] * kc[r][d];
+      sc[r] = valid[r] ? acc * p.scale : -__builtin_inff();
+      mx = fmaxf(mx, sc[r]);
+    }
+    const float m_new = fmaxf(m, mx);
+    if (m_new == -__builtin_inff()) continue;
+    const float alpha = __expf(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < D; ++d) o[d] *= alpha;
+    for (int r = 0; r < 32; ++r) {
+      const float pr = valid[r] ? __expf(sc[r] - m_new) : 0.f;
+      l += pr;
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] += pr * vc[r][d];
+    }
+    m = m_new;
+  }
+  if (live) {
+    float* orow = p.out + (((int64_t)b * p.Hq + h) * p.T + qi) * D;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int d = 0; d < D; ++d) orow[d] = o[d] * inv;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+
+int attn_choose_splits(const Geom& g, long long max_list_tokens, int num_cus) {
+  const long long tiles = 1 + (max_list_tokens + 63) / 64;
+  const long long segs = (long long)g.B * g.Hkv;
+  long long s = (2LL * num_cus + segs - 1) / segs;   // about two workgroups per CU
+  if (s > tiles) s = tiles;
+  if (s < 1) s = 1;
+  if (segs > kMaxTickets) s = 1;
+  return (int)s;
+}
+
+size_t attn_scratch_bytes(const Geom& g, int n_splits) {
+  if (n_splits <= 1) return 0;
+  const size_t per = (size_t)g.B * g.Hq * n_splits * 32;
+  return per * g.D * sizeof(float) + per * sizeof(float2) + 256;
+}
+
+template <int D, int G>
+static hipError_t launch_mfma(hipStream_t s, const AttnParams& p, dim3 grid) {
+  hipLaunchKernelGGL((attn_mfma_kernel<D, G>), grid, dim3(AttnShape<G>::NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_mfma_g(hipStream_t s, const AttnParams& p, dim3 grid, int G) {
+  switch (G) {
+    case 1: return launch_mfma<D, 1>(s, p, grid);
+    case 2: return launch_mfma<D, 2>(s, p, grid);
+    case 3: return launch_mfma<D, 3>(s, p, grid);
+    case 4: return launch_mfma<D, 4>(s, p, grid);
+    case 5: return launch_mfma<D, 5>(s, p, grid);
+    case 6: return launch_mfma<D, 6>(s, p, grid);
+    case 7: return launch_mfma<D, 7>(s, p, grid);
+    case 8: return launch_mfma<D, 8>(s, p, grid);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,
+                       const void* k_dec, const void* v_dec, const int32_t* page_table,
+                       const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
+                       int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
+                       uint32_t* status) {
+  KvLayout lay;
+  lay.Hkv = g.Hkv;
+  lay.L = g.L;
+  lay.D = g.D;
+  lay.paged = g.paged;
+  lay.page_log2 = g.page_log2;
+  lay.pages_per_seq = g.pps;
+  lay.n_pages = g.n_pages;
+  lay.page_table = page_table;
+  const int unit = 1 << unit_log2;
+  const int n_units = (g.L + unit - 1) / unit;
+  if (g.dtype == FDL_F32) {
+    F32Params p;
+    p.q = static_cast<const float*>(q);
+    p.k = static_cast<const float*>(k);
+    p.v = static_cast<const float*>(v);
+    p.k_dec = static_cast<const float*>(k_dec);
+    p.v_dec = static_cast<const float*>(v_dec);
+    p.sel_idx = sel_idx;
+    p.n_sel = n_sel;
+    p.out = static_cast<float*>(out);
+    p.status = status;
+    p.lay = lay;
+    p.Hq = g.Hq;
+    p.G = g.G;
+    p.T = g.T;
+    p.max_sel = max_sel;
+    p.unit_log2 = unit_log2;
+    p.n_units = n_units;
+    p.dense = dense;
+    p.scale = 1.0f / sqrtf((float)g.D);
+    dim3 grid(g.Hq, g.B);
+    if (g.D == 128)
+      hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(64), 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_f32_kernel<64>), grid, dim3(64), 0, s, p);
+    return hipGetLastError();
+  }
+  AttnParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.k_dec = static_cast<const uint16_t*>(k_dec);
+  p.v_dec = static_cast<const uint16_t*>(v_dec);
+  p.sel_idx = sel_idx;
+  p.n_sel = n_sel;
+  p.out = static_cast<uint16_t*>(out);
+  const size_t per = (size_t)g.B * g.Hq * n_splits * 32;
+  p.part_o = reinterpret_cast<float*>(scratch);
+  p.part_ml = reinterpret_cast<float2*>(scratch + per * g.D * sizeof(float));
+  p.tickets = tickets;
+  p.status = status;
+  p.lay = lay;
+  p.Hq = g.Hq;
+  p.T = g.T;
+  p.max_sel = max_sel;
+  p.unit_log2 = unit_log2;
+  p.n_units = n_units;
+  p.dense = dense;
+  p.n_splits = n_splits;
+  p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
+  dim3 grid(n_splits, g.Hkv, g.B);
+  return g.D == 128 ? launch_mfma_g<128>(s, p, grid, g.G) : launch_mfma_g<64>(s, p, grid, g.G);
+}
+
+}  // namespace fdl

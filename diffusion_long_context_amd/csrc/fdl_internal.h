@@ -1,0 +1,76 @@
+// Host-side declarations shared by libfdllm's translation units (launchers and the handle).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/libfdllm.h"
+
+struct fdl_ctx {
+  hipStream_t stream;
+  int device;
+  int num_cus;
+  char* ws;              // workspace base (device)
+  size_t ws_bytes;
+  uint32_t* status;      // device status word
+  uint32_t* tickets;     // split-merge tickets, one per (b, kv head); left at zero by each kernel
+  uint32_t* counters;    // per-call counters, cleared by the call that uses them
+  char* scratch;         // general scratch after the fixed header
+  size_t scratch_bytes;
+  char last_error[256];
+};
+
+namespace fdl {
+
+constexpr size_t kHeaderBytes = 1u << 20;        // status + tickets + counters
+constexpr int kMaxTickets = 65536;               // B * Hkv limit for split attention
+constexpr size_t kTicketOffset = 4096;
+constexpr size_t kCounterOffset = kTicketOffset + kMaxTickets * sizeof(uint32_t);
+constexpr int kMaxCounters = (int)((kHeaderBytes - kCounterOffset) / sizeof(uint32_t));
+
+struct Geom {
+  int B, Hq, Hkv, G, D, L, bt, T, dtype;
+  int paged, page_tokens, page_log2, pps, n_pages;
+};
+
+hipError_t launch_predict(hipStream_t s, int batch, int T, const float* prev_conf,
+                          const uint8_t* masked, int top_k, int window, uint64_t* pred_mask,
+                          int32_t* n_pred);
+
+hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const int32_t* page_table,
+                            int unit_log2, float* ks, uint32_t* status);
+
+hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                              const float* ks, int n_units, float* scores);
+
+hipError_t launch_score_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                               const void* k, const int32_t* page_table, int unit_log2,
+                               const int32_t* cand_idx, int n_cand, float* scores,
+                               uint32_t* status);
+
+// Sink detection.  Needs scratch for per-split statistics, candidates and bitmaps.
+size_t sink_scratch_bytes(const Geom& g, int* n_splits, int* cand_cap);
+hipError_t launch_sinks(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                        const void* k, const void* k_dec, float tau, int max_sinks,
+                        int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
+                        int cand_cap, uint32_t* status, int num_cus);
+
+hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int n_units,
+                         int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,
+                         int max_sinks, const int32_t* cand_idx, int n_cand, int top_k,
+                         int force_first, int max_sel, int32_t* sel_idx, int32_t* n_sel,
+                         uint32_t* status);
+
+// Attention.  dense != 0 ignores sel_idx / n_sel.
+size_t attn_scratch_bytes(const Geom& g, int n_splits);
+int attn_choose_splits(const Geom& g, long long max_list_tokens, int num_cus);
+hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,
+                       const void* k_dec, const void* v_dec, const int32_t* page_table,
+                       const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
+                       int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
+                       uint32_t* status);
+
+hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, size_t n, uint32_t v);
+
+}  // namespace fdl

@@ -1,0 +1,427 @@
+// Pooled keys and unit / token scoring, in pinned float32.
+//
+// Focus-dLLM (abstract; Elamur "Summary"): the predicted queries estimate which KV matters, so
+// redundant attention can be skipped.  Prefilling-dLLM (abstract): whole prefix chunks are ranked
+// first, then tokens inside the chosen chunks.  The pages give no formula; the reading built here:
+// a unit is represented by the float32 sum of its keys, the predicted queries of a KV head's group
+// are summed, and the score is the dot product of the two sums.  Every sum is the same
+// adjacent-pair tree (operands zero-padded to a power of two; level by level, element 2j plus
+// element 2j+1), every product is rounded to float32 before it is added, and nothing is fused, so
+// the bits of every score are fixed by the inputs alone.  The whole file is compiled with
+// floating-point contraction off for that reason.
+//
+// All three kernels are HBM-bound streaming reads: each lane issues its whole share of loads before
+// the first add, rows are read as full 256-byte (bf16) or 512-byte (float32) lines by consecutive
+// lanes, and cross-lane tree levels are xor butterflies (which reproduce the adjacent-pair tree
+// exactly because float addition is commutative).
+#pragma clang fp contract(off)
+
+#include "fdl_device.h"
+#include "fdl_internal.h"
+
+namespace fdl {
+
+// ------------------------------------------------------------------------------------------------
+// Key pooling: ks[b][g][n][d] = tree over the unit's tokens of k[b][g][t][d]
+// ------------------------------------------------------------------------------------------------
+
+template <typename KT>
+__device__ __forceinline__ float2 load_pair(const KT* base, int64_t off, int pair);
+
+template <>
+__device__ __forceinline__ float2 load_pair<uint16_t>(const uint16_t* base, int64_t off, int pair) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(base + off + 2 * pair);
+  return make_float2(bf16_bits_to_f32(w & 0xFFFFu), bf16_bits_to_f32(w >> 16));
+}
+
+template <>
+__device__ __forceinline__ float2 load_pair<float>(const float* base, int64_t off, int pair) {
+  return *reinterpret_cast<const float2*>(base + off + 2 * pair);
+}
+
+__device__ __forceinline__ float2 add2(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+
+// Adjacent-pair tree over LEAVES consecutive tokens starting at t0 (tokens >= L are +0).
+template <typename KT, int LEAVES>
+__device__ __forceinline__ float2 leaf_tree(const KT* k, const KvLayout& lay, int b, int g, int t0,
+                                            int pair, uint32_t* status) {
+  float2 a[LEAVES];
+#pragma unroll
+  for (int i = 0; i < LEAVES; ++i) {
+    const int t = t0 + i;
+    int64_t off;
+    a[i] = make_float2(0.f, 0.f);
+    if (t < lay.L && lay.row_offset(b, g, t, off, status)) a[i] = load_pair<KT>(k, off, pair);
+  }
+#pragma unroll
+  for (int w = LEAVES / 2; w >= 1; w /= 2) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) a[i] = add2(a[2 * i], a[2 * i + 1]);
+  }
+  return a[0];
+}
+
+// One "team" of D/2 threads per unit; thread `pair` owns dimensions 2*pair and 2*pair+1.
+template <typename KT, int D, int LEAVES>
+__global__ __launch_bounds__(256) void pool_keys_kernel(const KT* __restrict__ k, KvLayout lay,
+                                                        int unit_log2, int n_units,
+                                                        float* __restrict__ ks,
+                                                        uint32_t* __restrict__ status) {
+  extern __shared__ float2 sub_sums[];  // [teams][n_sub][D/2], only when unit > LEAVES
+  constexpr int kTeam = D / 2;
+  constexpr int kTeams = 256 / kTeam;
+  const int team = threadIdx.x / kTeam;
+  const int pair = threadIdx.x % kTeam;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int n = blockIdx.x * kTeams + team;
+  if (n >= n_units) return;
+  const int unit = 1 << unit_log2;
+  const int t_unit = n << unit_log2;
+  float2 r;
+  if (unit <= LEAVES) {
+    r = leaf_tree<KT, LEAVES>(k, lay, b, g, t_unit, pair, status);
+  } else {
+    const int n_sub = unit / LEAVES;
+    float2* mine = sub_sums + (size_t)team * n_sub * kTeam;
+    for (int s = 0; s < n_sub; ++s)
+      mine[s * kTeam + pair] = leaf_tree<KT, LEAVES>(k, lay, b, g, t_unit + s * LEAVES, pair, status);
+    // tree over the sub-unit sums; each thread only touches its own column, so no barrier
+    for (int w = n_sub / 2; w >= 1; w /= 2)
+      for (int i = 0; i < w; ++i)
+        mine[i * kTeam + pair] = add2(mine[(2 * i) * kTeam + pair], mine[(2 * i + 1) * kTeam + pair]);
+    r = mine[pair];
+  }
+  float* dst = ks + (((int64_t)b * lay.Hkv + g) * n_units + n) * D;
+  *reinterpret_cast<float2*>(dst + 2 * pair) = r;
+}
+
+template <typename KT, int D>
+static hipError_t pool_dispatch(hipStream_t s, const Geom& g, const KT* k, const KvLayout& lay,
+                                int unit_log2, float* ks, uint32_t* status) {
+  const int unit = 1 << unit_log2;
+  const int n_units = (g.L + unit - 1) / unit;
+  if (n_units == 0) return hipSuccess;
+  constexpr int kTeams = 256 / (D / 2);
+  dim3 grid((n_units + kTeams - 1) / kTeams, g.Hkv, g.B);
+  size_t lds = 0;
+  if (unit > 64) lds = (size_t)kTeams * (unit / 64) * (D / 2) * sizeof(float2);
+  switch (unit_log2) {
+#define FDL_POOL_CASE(LG)                                                                          \
+  case LG:                                                                                         \
+    hipLaunchKernelGGL((pool_keys_kernel<KT, D, (1 << LG)>), grid, dim3(256), lds, s, k, lay,     \
+                       unit_log2, n_units, ks, status);                                            \
+    break;
+    FDL_POOL_CASE(0) FDL_POOL_CASE(1) FDL_POOL_CASE(2) FDL_POOL_CASE(3) FDL_POOL_CASE(4)
+    FDL_POOL_CASE(5)
+#undef FDL_POOL_CASE
+    default:
+      hipLaunchKernelGGL((pool_keys_kernel<KT, D, 64>), grid, dim3(256), lds, s, k, lay, unit_log2,
+                         n_units, ks, status);
+  }
+  return hipGetLastError();
+}
+
+static KvLayout make_layout(const Geom& g, const int32_t* page_table) {
+  KvLayout lay;
+  lay.Hkv = g.Hkv;
+  lay.L = g.L;
+  lay.D = g.D;
+  lay.paged = g.paged;
+  lay.page_log2 = g.page_log2;
+  lay.pages_per_seq = g.pps;
+  lay.n_pages = g.n_pages;
+  lay.page_table = page_table;
+  return lay;
+}
+
+hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const int32_t* page_table,
+                            int unit_log2, float* ks, uint32_t* status) {
+  const KvLayout lay = make_layout(g, page_table);
+  if (g.dtype == FDL_BF16) {
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    return g.D == 128 ? pool_dispatch<uint16_t, 128>(s, g, kk, lay, unit_log2, ks, status)
+                      : pool_dispatch<uint16_t, 64>(s, g, kk, lay, unit_log2, ks, status);
+  }
+  const float* kk = static_cast<const float*>(k);
+  return g.D == 128 ? pool_dispatch<float, 128>(s, g, kk, lay, unit_log2, ks, status)
+                    : pool_dispatch<float, 64>(s, g, kk, lay, unit_log2, ks, status);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Predicted-query sum: qs[d] = tree over the group's heads (padded to 2^m) of the tree over the T
+// slots (padded to 2^m; non-predicted slots +0) of q[b][h][p][d].  Computed by threads d < D of the
+// block into LDS.
+// ------------------------------------------------------------------------------------------------
+
+template <typename QT>
+__device__ __forceinline__ float load_q(const QT* q, int64_t i);
+template <>
+__device__ __forceinline__ float load_q<uint16_t>(const uint16_t* q, int64_t i) {
+  return bf16_bits_to_f32(q[i]);
+}
+template <>
+__device__ __forceinline__ float load_q<float>(const float* q, int64_t i) {
+  return q[i];
+}
+
+__device__ __forceinline__ int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+template <typename QT, int D>
+__device__ void query_sum_to_lds(const QT* __restrict__ q, uint64_t pred, int b, int g, int Hq,
+                                 int G, int T, float* qs_lds) {
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  const int T2 = pow2_ceil(T);
+  const int G2 = pow2_ceil(G);
+  float hv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    hv[j] = 0.f;
+    if (j < G) {
+      const int h = g * G + j;
+      const QT* qh = q + ((int64_t)b * Hq + h) * T * D + d;
+      float a[64];
+#pragma unroll
+      for (int p = 0; p < 64; ++p)
+        a[p] = (p < T && ((pred >> p) & 1ull)) ? load_q<QT>(qh, (int64_t)p * D) : 0.f;
+#pragma unroll
+      for (int lvl = 0; lvl < 6; ++lvl) {
+        if ((1 << lvl) < T2) {
+#pragma unroll
+          for (int i = 0; i < (32 >> lvl); ++i) a[i] = a[2 * i] + a[2 * i + 1];
+        }
+      }
+      hv[j] = a[0];
+    }
+  }
+#pragma unroll
+  for (int lvl = 0; lvl < 3; ++lvl) {
+    if ((1 << lvl) < G2) {
+#pragma unroll
+      for (int i = 0; i < (4 >> lvl); ++i) hv[i] = hv[2 * i] + hv[2 * i + 1];
+    }
+  }
+  qs_lds[d] = hv[0];
+}
+
+// Pinned dot product of one row: lane j of an LPR-lane team holds dimensions [16j, 16j+16).
+// Local tree over its 16 products (levels 0-3), then xor butterflies across the team.
+template <int LPR>
+__device__ __forceinline__ float row_dot(const float (&x)[16], const float (&qv)[16]) {
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = x[i] * qv[i];
+#pragma unroll
+  for (int w = 8; w >= 1; w /= 2) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+  }
+  float s = p[0];
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) s = s + wave_shfl_xor(s, m);
+  return s;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Level-1 unit scores from pooled keys: scores[b][g][n] = dot(qs, ks[b][g][n])
+// ------------------------------------------------------------------------------------------------
+
+constexpr int kUnitsPerWg = 64;
+constexpr int kScoreRowsPerIter = 2;   // rows per lane in flight
+
+template <typename QT, int D>
+__global__ __launch_bounds__(256) void score_units_kernel(const QT* __restrict__ q,
+                                                          const uint64_t* __restrict__ pred_mask,
+                                                          const float* __restrict__ ks, int Hq,
+                                                          int Hkv, int G, int T, int n_units,
+                                                          float* __restrict__ scores) {
+  constexpr int LPR = D / 16;            // lanes per row
+  constexpr int kRowsPerWave = 64 / LPR;
+  constexpr int kRowsPerPass = 4 * kRowsPerWave;
+  __shared__ float qs[D];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % LPR;
+  const int n0 = blockIdx.x * kUnitsPerWg;
+  const float* ksg = ks + ((int64_t)b * Hkv + g) * n_units * D;
+
+  // issue this lane's row loads before the query sum, so they are in flight meanwhile
+  constexpr int kPasses = kUnitsPerWg / kRowsPerPass;
+  float x[kPasses][16];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    if (n < n_units) {
+      const float4* src = reinterpret_cast<const float4*>(ksg + (int64_t)n * D + 16 * j);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 v = src[c];
+        x[ps][4 * c + 0] = v.x;
+        x[ps][4 * c + 1] = v.y;
+        x[ps][4 * c + 2] = v.z;
+        x[ps][4 * c + 3] = v.w;
+      }
+    }
+  }
+  query_sum_to_lds<QT, D>(q, pred_mask[b], b, g, Hq, G, T, qs);
+  __syncthreads();
+  float qv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    const float sc = row_dot<LPR>(x[ps], qv);
+    if (n < n_units && j == 0) scores[((int64_t)b * Hkv + g) * n_units + n] = sc;
+  }
+}
+
+hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                              const float* ks, int n_units, float* scores) {
+  if (n_units == 0) return hipSuccess;
+  dim3 grid((n_units + kUnitsPerWg - 1) / kUnitsPerWg, g.Hkv, g.B);
+  if (g.dtype == FDL_BF16) {
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    if (g.D == 128)
+      hipLaunchKernelGGL((score_units_kernel<uint16_t, 128>), grid, dim3(256), 0, s, qq, pred_mask,
+                         ks, g.Hq, g.Hkv, g.G, g.T, n_units, scores);
+    else
+      hipLaunchKernelGGL((score_units_kernel<uint16_t, 64>), grid, dim3(256), 0, s, qq, pred_mask,
+                         ks, g.Hq, g.Hkv, g.G, g.T, n_units, scores);
+  } else {
+    const float* qq = static_cast<const float*>(q);
+    if (g.D == 128)
+      hipLaunchKernelGGL((score_units_kernel<float, 128>), grid, dim3(256), 0, s, qq, pred_mask, ks,
+                         g.Hq, g.Hkv, g.G, g.T, n_units, scores);
+    else
+      hipLaunchKernelGGL((score_units_kernel<float, 64>), grid, dim3(256), 0, s, qq, pred_mask, ks,
+                         g.Hq, g.Hkv, g.G, g.T, n_units, scores);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
+// Level-2 token scores inside candidate units (chunks), keys read through the page table:
+// scores[b][g][c][i] = dot(qs, k[token = cand_idx[b][g][c] * unit + i])
+// ------------------------------------------------------------------------------------------------
+
+constexpr int kTokensPerWg = 256;
+
+template <typename KT>
+__device__ __forceinline__ void load16(const KT* src, float (&x)[16]);
+
+template <>
+__device__ __forceinline__ void load16<uint16_t>(const uint16_t* src, float (&x)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(src);
+  const uint4 a = p[0], c = p[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load16<float>(const float* src, float (&x)[16]) {
+  const float4* p = reinterpret_cast<const float4*>(src);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float4 v = p[c];
+    x[4 * c] = v.x;
+    x[4 * c + 1] = v.y;
+    x[4 * c + 2] = v.z;
+    x[4 * c + 3] = v.w;
+  }
+}
+
+template <typename KT, int D>
+__global__ __launch_bounds__(256) void score_tokens_kernel(
+    const KT* __restrict__ q, const uint64_t* __restrict__ pred_mask, const KT* __restrict__ k,
+    KvLayout lay, int Hq, int G, int T, int unit_log2, const int32_t* __restrict__ cand_idx,
+    int n_cand, float* __restrict__ scores, uint32_t* __restrict__ status) {
+  constexpr int LPR = D / 16;
+  constexpr int kRowsPerWave = 64 / LPR;
+  constexpr int kRowsPerPass = 4 * kRowsPerWave;
+  constexpr int kPasses = kTokensPerWg / kRowsPerPass;
+  __shared__ float qs[D];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % LPR;
+  const int unit = 1 << unit_log2;
+  const int64_t total = (int64_t)n_cand << unit_log2;
+  const int64_t r0 = (int64_t)blockIdx.x * kTokensPerWg;
+  const int n_units = (lay.L + unit - 1) >> unit_log2;
+  const int32_t* cands = cand_idx + ((int64_t)b * lay.Hkv + g) * n_cand;
+
+  float x[kPasses][16];
+  bool ok[kPasses];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int64_t r = r0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    ok[ps] = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[ps][i] = 0.f;
+    if (r < total) {
+      const int c = (int)(r >> unit_log2);
+      const int u = cands[c];
+      const int t = (u << unit_log2) + (int)(r & (unit - 1));
+      int64_t off;
+      if ((unsigned)u >= (unsigned)n_units) {
+        latch(status, ST_BAD_INDEX);
+      } else if (t < lay.L && lay.row_offset(b, g, t, off, status)) {
+        load16<KT>(k + off + 16 * j, x[ps]);
+        ok[ps] = true;
+      }
+    }
+  }
+  query_sum_to_lds<KT, D>(q, pred_mask[b], b, g, Hq, G, T, qs);
+  __syncthreads();
+  float qv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int64_t r = r0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    const float sc = row_dot<LPR>(x[ps], qv);
+    if (r < total && j == 0)
+      scores[((int64_t)b * lay.Hkv + g) * total + r] = ok[ps] ? sc : -__builtin_inff();
+  }
+  (void)unit;
+}
+
+hipError_t launch_score_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                               const void* k, const int32_t* page_table, int unit_log2,
+                               const int32_t* cand_idx, int n_cand, float* scores,
+                               uint32_t* status) {
+  const int64_t total = (int64_t)n_cand << unit_log2;
+  if (total == 0) return hipSuccess;
+  const KvLayout lay = make_layout(g, page_table);
+  dim3 grid((unsigned)((total + kTokensPerWg - 1) / kTokensPerWg), g.Hkv, g.B);
+  if (g.dtype == FDL_BF16) {
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    if (g.D == 128)
+      hipLaunchKernelGGL((score_tokens_kernel<uint16_t, 128>), grid, dim3(256), 0, s, qq, pred_mask,
+                         kk, lay, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
+    else
+      hipLaunchKernelGGL((score_tokens_kernel<uint16_t, 64>), grid, dim3(256), 0, s, qq, pred_mask,
+                         kk, lay, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
+  } else {
+    const float* qq = static_cast<const float*>(q);
+    const float* kk = static_cast<const float*>(k);
+    if (g.D == 128)
+      hipLaunchKernelGGL((score_tokens_kernel<float, 128>), grid, dim3(256), 0, s, qq, pred_mask, kk,
+                         lay, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
+    else
+      hipLaunchKernelGGL((score_tokens_kernel<float, 64>), grid, dim3(256), 0, s, qq, pred_mask, kk,
+                         lay, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fdl

@@ -1,0 +1,237 @@
+"""Thin Python binding of libfdllm (ctypes).
+
+Argument marshalling only: every function below checks that the tensors it is handed are CUDA
+(HIP) tensors, contiguous and large enough for the geometry, then passes raw device pointers and the
+current torch stream to the C call of the same name.  All arithmetic runs in the library's HIP
+kernels.  PyTorch only provides device memory and the stream.
+
+The library must have been built (``python -m diffusion_long_context_amd.build``); loading fails
+loudly otherwise -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfdllm.so")
+
+FDL_OK, FDL_EINVAL, FDL_ENOMEM, FDL_EHIP, FDL_EOVERFLOW, FDL_EUNSUPPORTED, FDL_EINDEX = 0, -1, -2, -3, -4, -5, -6
+FDL_F32, FDL_BF16 = 0, 1
+
+EXPORTED = (
+    "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_status_string",
+    "fdl_last_error", "fdl_pool_keys", "fdl_predict_queries", "fdl_score_blocks",
+    "fdl_select_blocks", "fdl_sparse_attn", "fdl_dense_attn",
+)
+
+
+class FdlError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libfdllm status {status}: {msg}")
+        self.status = status
+
+
+class fdl_geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_q_heads", "n_kv_heads", "head_dim", "ctx_len", "kv_block", "dec_len", "dtype",
+        "paged", "page_tokens", "pages_per_seq", "n_pages")]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "fdl_create": (_I, [ctypes.POINTER(_P), _P, ctypes.c_size_t]),
+    "fdl_destroy": (_I, [_P]),
+    "fdl_set_stream": (_I, [_P, _P]),
+    "fdl_get_status": (_I, [_P]),
+    "fdl_status_string": (ctypes.c_char_p, [_I]),
+    "fdl_last_error": (ctypes.c_char_p, [_P]),
+    "fdl_pool_keys": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _I, _P]),
+    "fdl_predict_queries": (_I, [_P, _I, _I, _P, _P, _I, _I, _P, _P]),
+    "fdl_score_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _I,
+                              ctypes.c_float, _I, _P, _P]),
+    "fdl_select_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I,
+                               _P, _P]),
+    "fdl_sparse_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
+    "fdl_dense_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfdllm.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FdlError(FDL_EINVAL, f"{path} not found: build it with "
+                                   "`python -m diffusion_long_context_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+@dataclass(frozen=True)
+class Geom:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ctx_len: int
+    kv_block: int
+    dec_len: int
+    dtype: int = FDL_BF16
+    paged: int = 0
+    page_tokens: int = 0
+    pages_per_seq: int = 0
+    n_pages: int = 0
+
+    def c(self) -> fdl_geom:
+        return fdl_geom(*[int(getattr(self, f)) for f, _ in fdl_geom._fields_])
+
+    @property
+    def elem(self) -> int:
+        return 4 if self.dtype == FDL_F32 else 2
+
+    @property
+    def kv_elems(self) -> int:
+        if self.paged:
+            return self.n_pages * self.n_kv_heads * self.page_tokens * self.head_dim
+        return self.batch * self.n_kv_heads * self.ctx_len * self.head_dim
+
+
+def _ptr(t, nbytes: int | None = None, name: str = "tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Handle:
+    """An fdl_handle bound to the current device and torch stream."""
+
+    def __init__(self, workspace_bytes: int = 0):
+        lib = load()
+        h = ctypes.c_void_p()
+        st = lib.fdl_create(ctypes.byref(h), _stream_ptr(), workspace_bytes)
+        if st != FDL_OK:
+            raise FdlError(st, lib.fdl_status_string(st).decode())
+        self.h = h
+        self.lib = lib
+
+    def close(self):
+        if self.h:
+            self.lib.fdl_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, st: int):
+        if st != FDL_OK:
+            msg = self.lib.fdl_last_error(self.h).decode() or self.lib.fdl_status_string(st).decode()
+            raise FdlError(st, msg)
+
+    def sync_stream(self):
+        self.lib.fdl_set_stream(self.h, _stream_ptr())
+
+    # ---- the C calls ------------------------------------------------------------------------
+
+    def fdl_get_status(self) -> int:
+        self.sync_stream()
+        return self.lib.fdl_get_status(self.h)
+
+    def fdl_pool_keys(self, g: Geom, k_cache, page_table, unit_tokens: int, ks):
+        self.sync_stream()
+        n_units = -(-g.ctx_len // unit_tokens)
+        self._check(self.lib.fdl_pool_keys(
+            self.h, ctypes.byref(g.c()), _ptr(k_cache, g.kv_elems * g.elem, "k_cache"),
+            _ptr(page_table, 4 * g.batch * g.pages_per_seq if g.paged else None, "page_table"),
+            unit_tokens, _ptr(ks, 4 * g.batch * g.n_kv_heads * n_units * g.head_dim, "ks")))
+
+    def fdl_predict_queries(self, batch: int, dec_len: int, prev_conf, masked, top_k: int, window: int,
+                            pred_mask, n_pred):
+        self.sync_stream()
+        self._check(self.lib.fdl_predict_queries(
+            self.h, batch, dec_len, _ptr(prev_conf, 4 * batch * dec_len, "prev_conf"),
+            _ptr(masked, batch * dec_len, "masked"), top_k, window,
+            _ptr(pred_mask, 8 * batch, "pred_mask"), _ptr(n_pred, 4 * batch, "n_pred")))
+
+    def fdl_score_blocks(self, g: Geom, q, pred_mask, ks, unit_tokens: int, scores, cand_idx=None,
+                         n_cand: int = 0, k_cache=None, k_dec=None, page_table=None,
+                         detect_sinks: bool = False, sink_tau: float = 0.03, max_sinks: int = 64,
+                         sink_pos=None, n_sinks=None):
+        self.sync_stream()
+        B, Hkv, D = g.batch, g.n_kv_heads, g.head_dim
+        n_units = -(-g.ctx_len // unit_tokens)
+        qbytes = B * g.n_q_heads * g.dec_len * D * g.elem
+        sbytes = 4 * B * Hkv * (n_cand * unit_tokens if cand_idx is not None else n_units)
+        self._check(self.lib.fdl_score_blocks(
+            self.h, ctypes.byref(g.c()), _ptr(q, qbytes, "q"), _ptr(pred_mask, 8 * B, "pred_mask"),
+            _ptr(ks, 4 * B * Hkv * n_units * D if cand_idx is None else None, "ks"), unit_tokens,
+            _ptr(cand_idx, 4 * B * Hkv * n_cand, "cand_idx"), n_cand,
+            _ptr(k_cache, g.kv_elems * g.elem, "k_cache"),
+            _ptr(k_dec, B * Hkv * g.dec_len * D * g.elem, "k_dec"),
+            _ptr(page_table, 4 * B * g.pages_per_seq if g.paged else None, "page_table"),
+            _ptr(scores, sbytes, "scores"), 1 if detect_sinks else 0, float(sink_tau), max_sinks,
+            _ptr(sink_pos, 4 * B * max_sinks, "sink_pos"), _ptr(n_sinks, 4 * B, "n_sinks")))
+
+    def fdl_select_blocks(self, g: Geom, scores, n_units: int, unit_tokens: int, sink_pos, n_sinks,
+                          max_sinks: int, top_k: int, max_sel: int, sel_idx, n_sel, cand_idx=None,
+                          n_cand: int = 0, force_first: bool = False):
+        self.sync_stream()
+        B, Hkv = g.batch, g.n_kv_heads
+        sbytes = 4 * B * Hkv * (n_cand * unit_tokens if cand_idx is not None else n_units)
+        self._check(self.lib.fdl_select_blocks(
+            self.h, ctypes.byref(g.c()), _ptr(scores, sbytes, "scores"), n_units, unit_tokens,
+            _ptr(sink_pos, 4 * B * max_sinks, "sink_pos"), _ptr(n_sinks, 4 * B, "n_sinks"), max_sinks,
+            _ptr(cand_idx, 4 * B * Hkv * n_cand, "cand_idx"), n_cand, top_k, 1 if force_first else 0,
+            max_sel, _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel")))
+
+    def _attn_ptrs(self, g: Geom, q, k_cache, v_cache, k_dec, v_dec, page_table, out):
+        B, D = g.batch, g.head_dim
+        qbytes = B * g.n_q_heads * g.dec_len * D * g.elem
+        dbytes = B * g.n_kv_heads * g.dec_len * D * g.elem
+        kv = g.kv_elems * g.elem if g.ctx_len > 0 else None
+        return (_ptr(q, qbytes, "q"), _ptr(k_cache, kv, "k_cache"), _ptr(v_cache, kv, "v_cache"),
+                _ptr(k_dec, dbytes, "k_dec"), _ptr(v_dec, dbytes, "v_dec"),
+                _ptr(page_table, 4 * B * g.pages_per_seq if g.paged else None, "page_table"),
+                _ptr(out, qbytes, "out"))
+
+    def fdl_sparse_attn(self, g: Geom, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx, n_sel,
+                        max_sel: int, sel_unit_tokens: int, out):
+        self.sync_stream()
+        qp, kp, vp, kdp, vdp, ptp, op = self._attn_ptrs(g, q, k_cache, v_cache, k_dec, v_dec, page_table, out)
+        B, Hkv = g.batch, g.n_kv_heads
+        self._check(self.lib.fdl_sparse_attn(
+            self.h, ctypes.byref(g.c()), qp, kp, vp, kdp, vdp, ptp,
+            _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel"),
+            max_sel, sel_unit_tokens, op))
+
+    def fdl_dense_attn(self, g: Geom, q, k_cache, v_cache, k_dec, v_dec, page_table, out):
+        self.sync_stream()
+        qp, kp, vp, kdp, vdp, ptp, op = self._attn_ptrs(g, q, k_cache, v_cache, k_dec, v_dec, page_table, out)
+        self._check(self.lib.fdl_dense_attn(self.h, ctypes.byref(g.c()), qp, kp, vp, kdp, vdp, ptp, op))

@@ -1,0 +1,198 @@
+/*
+ * libfdllm -- one denoising step of confidence-guided, sink-aware block-sparse attention for a
+ * diffusion LLM decoding over a long cached bidirectional KV context, on one AMD MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [FA]  "Focus-dLLM: Accelerating Long-Context Diffusion LLM Inference via Confidence-Guided
+ *         Context Focusing", the authors' abstract.
+ *   [FS]  the same paper, Elamur Research page, "Summary".
+ *   [FK]  the same page, "Key points".
+ *   [PA]  "Prefilling-dLLM: Predictive Prefilling for Long-Context Inference in Diffusion Language
+ *         Models", abstract.
+ * The pages give no formulas; the readings this library implements are stated at each call.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  fdl_geom lives on the host.
+ *   - Layouts are row-major with head_dim innermost:
+ *       q, out          [B][Hq][T][D]
+ *       contiguous KV   [B][Hkv][L][D]
+ *       paged KV pool   [n_pages][Hkv][page_tokens][D], page_table [B][pages_per_seq] int32
+ *       k_dec, v_dec    [B][Hkv][T][D]      (the current decode block's own keys / values)
+ *     q / k / v / out are bf16 (FDL_BF16, raw 16-bit patterns) or float32 (FDL_F32).
+ *   - Every call is asynchronous on the handle's HIP stream and never synchronises the host,
+ *     except fdl_get_status.  No call allocates or frees memory; fdl_create allocates the one
+ *     workspace.  Calls on one handle must come from one host thread at a time, and calls that
+ *     share a handle are ordered by its stream (they reuse its workspace).
+ *   - Argument errors return FDL_EINVAL (or FDL_EUNSUPPORTED for valid shapes outside the kernel
+ *     set, FDL_ENOMEM when the workspace is too small) synchronously, before anything is launched;
+ *     outputs are then untouched.  fdl_last_error() describes the last such error.
+ *   - Conditions only the device can see (more sinks than max_sinks, more sink candidates than the
+ *     workspace holds, an out-of-range page or unit index) are latched into a device status word
+ *     and returned by fdl_get_status().
+ *   - A launch failure returns FDL_EHIP.
+ */
+#ifndef LIBFDLLM_H
+#define LIBFDLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FDL_OK = 0,
+  FDL_EINVAL = -1,
+  FDL_ENOMEM = -2,
+  FDL_EHIP = -3,
+  FDL_EOVERFLOW = -4,
+  FDL_EUNSUPPORTED = -5,
+  FDL_EINDEX = -6
+} fdl_status;
+
+typedef enum { FDL_F32 = 0, FDL_BF16 = 1 } fdl_dtype;
+
+typedef struct fdl_ctx* fdl_handle;
+
+/* Shape of one attention layer.  Limits checked by every call that takes it:
+ *   batch >= 1; n_kv_heads >= 1; n_q_heads = G * n_kv_heads with 1 <= G <= 8;
+ *   head_dim in {64, 128}; ctx_len >= 0; kv_block a power of two in [1, 4096];
+ *   1 <= dec_len <= 64 (<= 32 for FDL_BF16 attention);
+ *   paged: page_tokens a power of two in [1, 4096], pages_per_seq * page_tokens >= ctx_len,
+ *   n_pages >= 1. */
+typedef struct {
+  int32_t batch;          /* B   sequences                                   */
+  int32_t n_q_heads;      /* Hq  query heads                                 */
+  int32_t n_kv_heads;     /* Hkv key/value heads (Hq / Hkv query heads each) */
+  int32_t head_dim;       /* D                                               */
+  int32_t ctx_len;        /* L   cached context tokens per sequence          */
+  int32_t kv_block;       /* tokens per KV block (the selection unit)        */
+  int32_t dec_len;        /* T   tokens of the current decode block          */
+  int32_t dtype;          /* fdl_dtype of q, KV and out                      */
+  int32_t paged;          /* 0: contiguous KV; 1: paged pool + page table    */
+  int32_t page_tokens;    /* paged: tokens per page                          */
+  int32_t pages_per_seq;  /* paged: page-table row length                    */
+  int32_t n_pages;        /* paged: physical pages in the pool               */
+} fdl_geom;
+
+/* ---- handle ------------------------------------------------------------------------------ */
+
+/* Create a handle bound to the current HIP device and to `hip_stream` (a hipStream_t; NULL = the
+ * null stream).  Allocates a device workspace of `workspace_bytes` (0 = 64 MiB), zeroes its
+ * counters and synchronises once.  Returns FDL_ENOMEM if the allocation fails. */
+fdl_status fdl_create(fdl_handle* h, void* hip_stream, size_t workspace_bytes);
+fdl_status fdl_destroy(fdl_handle h);
+fdl_status fdl_set_stream(fdl_handle h, void* hip_stream);
+
+/* Synchronise the handle's stream, return the first latched device condition (FDL_EOVERFLOW,
+ * FDL_EINDEX) or FDL_OK, and clear it. */
+fdl_status fdl_get_status(fdl_handle h);
+const char* fdl_status_string(fdl_status s);
+const char* fdl_last_error(fdl_handle h);
+
+/* ---- cache side: pooled keys ---------------------------------------------------------------- */
+
+/* Sum the keys of every `unit_tokens`-token unit (a KV block, or a prefix chunk) in float32, in the
+ * pinned order: an adjacent-pair tree over the unit's tokens in logical order, zero-padded to a
+ * power of two (tokens >= ctx_len count as +0).  Reading of [FS]/[FA] ("predicted queries select
+ * the most relevant KV": units are represented by their key sums) and [PA] (chunks are cached once).
+ *   k_cache     contiguous or paged keys (per g->paged); page_table used when paged, else ignored
+ *   unit_tokens power of two in [1, 4096]
+ *   ks          out: [B][Hkv][ceil(L / unit_tokens)][D] float32 */
+fdl_status fdl_pool_keys(fdl_handle h, const fdl_geom* g, const void* k_cache,
+                         const int32_t* page_table, int32_t unit_tokens, float* ks);
+
+/* ---- step 1: past-confidence-guided query prediction ----------------------------------------- */
+
+/* [FA], [FS], [FK]: the previous step's confidence predicts the next positions to be unmasked; the
+ * top `top_k` still-masked positions (confidence descending, NaN lowest, ties to the lower position)
+ * are widened to [i - window, i + window] clipped to [0, dec_len), and their union is the predicted
+ * query set.  prev_conf == NULL (first step of a block) predicts every position; no masked position
+ * predicts none.
+ *   prev_conf [batch][dec_len] float32 or NULL;  masked [batch][dec_len] uint8 (non-zero = masked)
+ *   pred_mask out [batch] uint64 (bit p = position p predicted);  n_pred out [batch] int32
+ *   1 <= dec_len <= 64, top_k >= 0, window >= 0 */
+fdl_status fdl_predict_queries(fdl_handle h, int32_t batch, int32_t dec_len, const float* prev_conf,
+                               const uint8_t* masked, int32_t top_k, int32_t window,
+                               uint64_t* pred_mask, int32_t* n_pred);
+
+/* ---- step 2: score KV units against the predicted queries; detect sinks ---------------------- */
+
+/* [FA], [FS]: the predicted queries estimate which KV matters.  Reading: per KV head g, the
+ * predicted queries of its q-head group are summed in float32 (adjacent-pair tree over the dec_len
+ * slots, non-predicted slots +0, then over the group's heads padded to a power of two); a unit's
+ * score is the pinned float32 dot product of that sum with the unit's key sum (products rounded,
+ * no fused multiply-add, adjacent-pair tree over D).
+ *
+ * Level 1 (cand_idx == NULL): scores [B][Hkv][n_units] from `ks` (fdl_pool_keys output with the
+ *   same unit_tokens), n_units = ceil(L / unit_tokens).
+ * Level 2 (cand_idx != NULL, [PA] token sparsity inside the chosen chunks): cand_idx
+ *   [B][Hkv][n_cand] ascending unit ids (e.g. fdl_select_blocks level-1 output); every token of
+ *   every candidate unit is scored against its own key from k_cache (paged through page_table if
+ *   g->paged): scores [B][Hkv][n_cand][unit_tokens]; requires L % unit_tokens == 0.
+ *
+ * detect_sinks != 0 (level 1 only; the source layer): [FA], [FS], [FK] attention sinks.  Reading:
+ *   for every q-head and predicted position p, softmax(q_p . k_t / sqrt(D)) over all L cached
+ *   tokens and the block's dec_len own tokens (k_dec); a cached token whose mean weight over the
+ *   predicted positions reaches sink_tau for at least one q-head is a sink.  The union over heads is
+ *   written ascending to sink_pos [B][max_sinks] int32 with the count in n_sinks [B]; more than
+ *   max_sinks sinks keeps the first max_sinks and latches FDL_EOVERFLOW.  Reads all of k_cache
+ *   (contiguous only).  sink_tau > 0.  With detect_sinks == 0, k_cache / k_dec / sink_* may be
+ *   NULL (level 1) and previously detected sinks are reused by fdl_select_blocks. */
+fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* g, const void* q, const uint64_t* pred_mask,
+                            const float* ks, int32_t unit_tokens, const int32_t* cand_idx,
+                            int32_t n_cand, const void* k_cache, const void* k_dec,
+                            const int32_t* page_table, float* scores, int32_t detect_sinks,
+                            float sink_tau, int32_t max_sinks, int32_t* sink_pos, int32_t* n_sinks);
+
+/* ---- step 3: keep sinks + top-K units; reuse sinks across layers ---------------------------- */
+
+/* [FA], [FS]: sinks are always kept and their locations are reused in deeper layers; the rest of
+ * the budget goes to the best-scoring units.  Ranking: score descending, -0 == +0, NaN lowest,
+ * ties to the lower index.  Output ascending.
+ *
+ * Level 1 (cand_idx == NULL): scores [B][Hkv][n_units]; every unit holding a sink position
+ *   (sink_pos[b][0 .. n_sinks[b]) / unit_tokens; sink_pos may be NULL for none) is forced in, plus
+ *   the top `top_k` of the other units.  sel_idx [B][Hkv][max_sel] gets the unit ids, n_sel
+ *   [B][Hkv] the count (= forced + min(top_k, n_units - forced)).  Passing the source layer's
+ *   sink_pos / n_sinks unchanged is the cross-layer reuse.  max_sel must cover min(n_units,
+ *   max_sinks + top_k); max_sinks bounds n_sinks.
+ * Level 2 ([PA]; cand_idx != NULL): scores [B][Hkv][n_cand][unit_tokens] (fdl_score_blocks level 2);
+ *   inside each candidate unit, token 0 (the chunk's leading BOS anchor) is forced when
+ *   force_first != 0, plus the top `top_k` of its other tokens; sel_idx [B][Hkv][max_sel] gets the
+ *   logical token ids (cand * unit_tokens + i), ascending; n_sel = n_cand * (force_first + top_k);
+ *   requires top_k <= unit_tokens - force_first and max_sel >= that count. */
+fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* g, const float* scores, int32_t n_units,
+                             int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
+                             int32_t max_sinks, const int32_t* cand_idx, int32_t n_cand,
+                             int32_t top_k, int32_t force_first, int32_t max_sel, int32_t* sel_idx,
+                             int32_t* n_sel);
+
+/* ---- step 4: sparse bidirectional attention over the selected KV ---------------------------- */
+
+/* [FA], [FS]: bidirectional attention of the current block's queries over only the selected KV;
+ * [PA]: over chunk KV cached non-contiguously.  For every q-head h (KV head h / G) and every one of
+ * the dec_len queries: out = softmax(q . k / sqrt(D)) v over the selected cached tokens plus the
+ * block's own dec_len tokens (k_dec / v_dec), no mask.  The selected tokens are the units
+ * sel_idx[b][g][0 .. n_sel[b][g]) of sel_unit_tokens tokens each (kv_block for blocks, 1 for token
+ * lists); tokens >= ctx_len are skipped; paged KV is resolved through page_table.  bf16 runs on
+ * MFMA with float32 accumulation and bf16 output; float32 runs in float32.
+ * Unit ids outside [0, ceil(L / sel_unit_tokens)) and page ids outside [0, n_pages) are skipped
+ * and latch FDL_EINDEX. */
+fdl_status fdl_sparse_attn(fdl_handle h, const fdl_geom* g, const void* q, const void* k_cache,
+                           const void* v_cache, const void* k_dec, const void* v_dec,
+                           const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
+                           int32_t max_sel, int32_t sel_unit_tokens, void* out);
+
+/* Dense baseline and the shallow full-attention layers ([FS]): the same attention over all L cached
+ * tokens plus the own block. */
+fdl_status fdl_dense_attn(fdl_handle h, const fdl_geom* g, const void* q, const void* k_cache,
+                          const void* v_cache, const void* k_dec, const void* v_dec,
+                          const int32_t* page_table, void* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFDLLM_H */

@@ -1,0 +1,214 @@
+"""Per-call GPU parity against the CPU oracle on small and medium inputs.
+
+Indices (predicted positions, pooled keys, scores, selections, sinks) must match bit for bit;
+attention outputs must satisfy |o - r| <= 1e-2 + 2e-2 |r| against the float64 oracle computed on
+the same bf16 / float32 inputs."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_close, dev, host, out_buffer, out_to_f64, require_gpu
+from oracle.attention import attend, blocks_to_tokens
+from oracle.pipeline import focus_layer_step
+from oracle.predictor import predict_positions
+from oracle.scoring import pool_keys, query_sum, unit_scores
+from oracle.selection import select_blocks
+from synth import get_config
+from synth.gen import make_single
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def h():
+    require_gpu()
+    from diffusion_long_context_amd import Handle
+    hh = Handle(workspace_bytes=256 << 20)
+    yield hh
+    hh.close()
+
+
+def _geom(cfg):
+    from diffusion_long_context_amd.step import geom_for
+    return geom_for(cfg)
+
+
+def _u64(bits):
+    return np.asarray(bits, dtype=np.uint64)
+
+
+# ---------------------------------------------------------------------------------------------
+# predictor
+# ---------------------------------------------------------------------------------------------
+
+def _gpu_predict(h, prev_conf, masked, k, w):
+    B, T = masked.shape
+    pm = torch.zeros(B, dtype=torch.int64, device="cuda")
+    npred = torch.zeros(B, dtype=torch.int32, device="cuda")
+    h.fdl_predict_queries(B, T, None if prev_conf is None else dev(prev_conf), dev(masked), k, w, pm, npred)
+    torch.cuda.synchronize()
+    return host(pm).view(np.uint64), host(npred)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_predict_random(h, seed):
+    rng = np.random.default_rng(seed)
+    for T in (1, 7, 32, 33, 64):
+        B = 5
+        conf = rng.choice([0.1, 0.5, 0.5, 0.9, np.nan, -0.0, 0.0, 0.3], size=(B, T)).astype(np.float32)
+        masked = (rng.random((B, T)) < 0.5).astype(np.uint8)
+        for k, w in [(0, 0), (1, 0), (4, 2), (4, 4), (100, 70)]:
+            got = _gpu_predict(h, conf, masked, k, w)
+            want = predict_positions(conf, masked, k, w)
+            assert np.array_equal(got[0], _u64(want[0])), (T, k, w)
+            assert np.array_equal(got[1], want[1])
+
+
+def test_predict_edge_cases(h):
+    T = 32
+    masked = np.ones((2, T), np.uint8)
+    got = _gpu_predict(h, None, masked, 4, 4)
+    assert all(int(v) == (1 << 32) - 1 for v in got[0])
+    got = _gpu_predict(h, np.ones((2, T), np.float32), np.zeros((2, T), np.uint8), 4, 4)
+    assert list(got[0]) == [0, 0] and list(got[1]) == [0, 0]
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2, 4])
+def test_predict_workloads(h, ci):
+    from synth.gen import decode_state
+    cfg = get_config(ci)
+    d = decode_state(cfg)
+    got = _gpu_predict(h, d["prev_conf"], d["masked"], cfg.top_k_pos, cfg.window)
+    want = predict_positions(d["prev_conf"], d["masked"], cfg.top_k_pos, cfg.window)
+    assert np.array_equal(got[0], _u64(want[0])) and np.array_equal(got[1], want[1])
+
+
+# ---------------------------------------------------------------------------------------------
+# pooled keys and scores
+# ---------------------------------------------------------------------------------------------
+
+def _small_bf16(**kw):
+    return get_config(1).with_(**kw)
+
+
+@pytest.mark.parametrize("cfg", [
+    get_config(0),
+    _small_bf16(n_q_heads=4, n_kv_heads=4, ctx_len=1000, kv_block=64),       # ragged last block
+    _small_bf16(n_q_heads=4, n_kv_heads=2, ctx_len=777, kv_block=16, head_dim=64),
+    _small_bf16(n_q_heads=2, n_kv_heads=2, ctx_len=4096, kv_block=2048),     # chunk-sized units
+], ids=["tiny", "ragged", "d64", "chunk"])
+def test_pool_and_scores_bit_exact(h, cfg):
+    x = make_single(cfg)
+    g = _geom(cfg)
+    n_units = -(-cfg.ctx_len // cfg.kv_block)
+    ks = torch.zeros(cfg.batch, cfg.n_kv_heads, n_units, cfg.head_dim, dtype=torch.float32, device="cuda")
+    h.fdl_pool_keys(g, dev(x["k"]), None, cfg.kv_block, ks)
+    want_ks = pool_keys(x["k"], cfg.kv_block)
+    bits, _ = predict_positions(x["prev_conf"], x["masked"], cfg.top_k_pos, cfg.window)
+    pm = dev(_u64(bits))
+    sc = torch.zeros(cfg.batch, cfg.n_kv_heads, n_units, dtype=torch.float32, device="cuda")
+    h.fdl_score_blocks(g, dev(x["q"]), pm, ks, cfg.kv_block, sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ks).view(np.uint32), want_ks.view(np.uint32))
+    want_sc = unit_scores(query_sum(x["q"], bits, cfg.n_kv_heads), want_ks)
+    assert np.array_equal(host(sc).view(np.uint32), want_sc.view(np.uint32))
+
+
+def test_scores_all_positions_predicted(h):
+    cfg = _small_bf16(n_q_heads=8, n_kv_heads=1, ctx_len=640, dec_len=20)
+    x = make_single(cfg)
+    g = _geom(cfg)
+    ks = torch.zeros(1, 1, 10, 128, dtype=torch.float32, device="cuda")
+    h.fdl_pool_keys(g, dev(x["k"]), None, 64, ks)
+    bits = _u64([(1 << 20) - 1])
+    sc = torch.zeros(1, 1, 10, dtype=torch.float32, device="cuda")
+    h.fdl_score_blocks(g, dev(x["q"]), dev(bits), ks, 64, sc)
+    torch.cuda.synchronize()
+    want = unit_scores(query_sum(x["q"], bits, 1), pool_keys(x["k"], 64))
+    assert np.array_equal(host(sc).view(np.uint32), want.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------------------------
+# selection on crafted scores (ties, -0/+0, NaN, forced sinks)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_select_crafted(h, seed):
+    rng = np.random.default_rng(seed)
+    B, Hkv, n = 2, 3, 300
+    cfg = _small_bf16(batch=B, n_q_heads=Hkv, n_kv_heads=Hkv, ctx_len=n * 64)
+    g = _geom(cfg)
+    scores = rng.choice([1.0, 2.0, -0.0, 0.0, np.nan, -np.inf, 3.5, 1e-40, -1e-40], size=(B, Hkv, n))
+    scores = scores.astype(np.float32)
+    scores[0, 0] = rng.standard_normal(n).astype(np.float32)
+    max_sinks = 8
+    sink_pos = np.full((B, max_sinks), -1, np.int32)
+    sink_pos[0, :3] = [0, 70, 71]
+    sink_pos[1, :1] = [64 * 299 + 5]
+    n_sinks = np.array([3, 1], np.int32)
+    for k in (0, 1, 17, 64, 297, 299, 500):
+        max_sel = min(n, max_sinks + k)
+        sel = torch.zeros(B, Hkv, max_sel, dtype=torch.int32, device="cuda")
+        nsel = torch.zeros(B, Hkv, dtype=torch.int32, device="cuda")
+        h.fdl_select_blocks(g, dev(scores), n, 64, dev(sink_pos), dev(n_sinks), max_sinks, k, max_sel,
+                            sel, nsel)
+        torch.cuda.synchronize()
+        want = select_blocks(scores, sink_pos, n_sinks, 64, k)
+        s, c = host(sel), host(nsel)
+        for b in range(B):
+            for gg in range(Hkv):
+                assert c[b, gg] == len(want[b][gg]), (k, b, gg)
+                assert s[b, gg, : c[b, gg]].tolist() == want[b][gg].tolist(), (k, b, gg)
+
+
+# ---------------------------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [
+    get_config(0),
+    _small_bf16(n_q_heads=4, n_kv_heads=4, ctx_len=1000),
+    _small_bf16(n_q_heads=8, n_kv_heads=4, ctx_len=1500, head_dim=64),
+    _small_bf16(n_q_heads=7, n_kv_heads=1, ctx_len=2000, dec_len=20),
+    _small_bf16(batch=2, n_q_heads=8, n_kv_heads=1, ctx_len=300, dec_len=32),
+    _small_bf16(n_q_heads=2, n_kv_heads=2, ctx_len=0),
+], ids=["tiny", "mha-ragged", "gqa2-d64", "gqa7-T20", "gqa8-b2", "empty-ctx"])
+def test_dense_attention(h, cfg):
+    x = make_single(cfg)
+    g = _geom(cfg)
+    out = out_buffer(cfg)
+    h.fdl_dense_attn(g, dev(x["q"]), dev(x["k"]) if cfg.ctx_len else None,
+                     dev(x["v"]) if cfg.ctx_len else None, dev(x["k_dec"]), dev(x["v_dec"]), None, out)
+    torch.cuda.synchronize()
+    ref = attend(x["q"], x["k"], x["v"], x["k_dec"], x["v_dec"], None)
+    assert_close(out_to_f64(cfg, out), ref, "dense")
+
+
+@pytest.mark.parametrize("cfg", [
+    get_config(0),
+    _small_bf16(n_q_heads=4, n_kv_heads=4, ctx_len=1000, top_k_blocks=5),
+    _small_bf16(n_q_heads=8, n_kv_heads=2, ctx_len=1500, head_dim=64, kv_block=32, top_k_blocks=9),
+    _small_bf16(n_q_heads=7, n_kv_heads=1, ctx_len=4096, dec_len=32, top_k_blocks=12),
+    _small_bf16(n_q_heads=2, n_kv_heads=2, ctx_len=2048, top_k_blocks=32),   # everything selected
+], ids=["tiny", "mha-ragged", "gqa4-d64-bt32", "gqa7", "all-blocks"])
+def test_sparse_attention_with_oracle_selection(h, cfg):
+    x = make_single(cfg)
+    g = _geom(cfg)
+    r = focus_layer_step(cfg, x, "source")
+    n_blk = -(-cfg.ctx_len // cfg.kv_block)
+    max_sel = max(len(s) for row in r["sel"] for s in row) + 3
+    sel = np.full((cfg.batch, cfg.n_kv_heads, max_sel), -7, np.int32)
+    nsel = np.zeros((cfg.batch, cfg.n_kv_heads), np.int32)
+    for b in range(cfg.batch):
+        for gg in range(cfg.n_kv_heads):
+            s = r["sel"][b][gg]
+            sel[b, gg, : len(s)] = s
+            nsel[b, gg] = len(s)
+    out = out_buffer(cfg)
+    h.fdl_sparse_attn(g, dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["k_dec"]), dev(x["v_dec"]), None,
+                      dev(sel), dev(nsel), max_sel, cfg.kv_block, out)
+    torch.cuda.synchronize()
+    assert_close(out_to_f64(cfg, out), r["out"], "sparse")
+    if max_sel >= n_blk:
+        dense = attend(x["q"], x["k"], x["v"], x["k_dec"], x["v_dec"], None)
+        assert_close(out_to_f64(cfg, out), dense, "sparse==dense")
