@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of one denoising step of confidence-guided, sink-aware block-sparse attention on the
+32K-context, 32-layer workload (LLaDA-8B-shaped attention: 32 heads, head_dim 128, bf16; 32-token
+decode blocks; generation of 256 tokens as 8 blocks of 32 steps; layers 0-1 dense, layer 2 finds the
+sinks, layers 3-31 reuse them; 64 blocks of 64 tokens kept per head).
+
+A step = one fdl_focus_step call (predict once, then the 32 layers) plus, at the first step of every
+generation block, the key pooling of all 32 layers (the cache-side refresh).  Inputs are resident in
+HBM before timing: 32 distinct layers of KV cache (16 GiB, far larger than the 256 MB last-level
+cache, so every layer reads cold data) and distinct per-(step, layer) queries and block keys/values.
+
+Prints one JSON line (rank 0, N = 1).  The CPU baseline times the oracle on a bounded sample in a
+single-threaded child process.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn step us + KV tokens/s at 32K ctx; achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, single-threaded, on one layer of the same workload
+# ------------------------------------------------------------------------------------------------
+
+def cpu_baseline_child() -> dict:
+    import numpy as np
+
+    from oracle.pipeline import focus_layer_step
+    from oracle.scoring import pool_keys
+    from synth import get_config
+    from synth.gen import context_kv, schedule_state, step_qkv
+
+    cfg = get_config(3)
+    layer, gstep = 3, 33
+    st = schedule_state(cfg, gstep)
+    x = dict(step_qkv(cfg, layer, st["block"], st["s"]))
+    x.update(context_kv(cfg, layer))
+    x["prev_conf"], x["masked"] = st["prev_conf"], st["masked"]
+    t = {}
+    t0 = time.perf_counter()
+    ks = pool_keys(x["k"], cfg.kv_block)
+    t["pool"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    r_src = focus_layer_step(cfg, x, "source", ks=ks)
+    t["source"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    focus_layer_step(cfg, x, "reuse", sinks=(r_src["sink_pos"], r_src["n_sinks"]), ks=ks)
+    t["reuse"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    focus_layer_step(cfg, x, "dense")
+    t["dense"] = time.perf_counter() - t0
+    step = (cfg.dense_layers * t["dense"] + t["source"]
+            + (cfg.n_layers - cfg.dense_layers - 1) * t["reuse"] + cfg.n_layers * t["pool"] / cfg.steps_per_block)
+    return {"layer_seconds": t, "step_seconds_extrapolated": step,
+            "kv_tokens_per_s": cfg.ctx_len * cfg.n_layers / step}
+
+
+def cpu_baseline() -> dict | None:
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    env["PYTHONPATH"] = ROOT + os.pathsep + env.get("PYTHONPATH", "")
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child"], env=env,
+                           capture_output=True, text=True, timeout=600)
+    except subprocess.TimeoutExpired:
+        log("cpu baseline timed out")
+        return None
+    if r.returncode != 0:
+        log("cpu baseline failed: " + r.stderr[-2000:])
+        return None
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    lt = d["layer_seconds"]
+    return {
+        "value": d["kv_tokens_per_s"], "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+        "sample": ("one 32K layer (32 heads) of the same workload, run once as dense, source and reuse "
+                   "layer plus its key pooling; step = 2 dense + 1 source + 29 reuse + 32 poolings/32 "
+                   f"(measured s: dense {lt['dense']:.2f}, source {lt['source']:.2f}, reuse "
+                   f"{lt['reuse']:.2f}, pool {lt['pool']:.2f})"),
+        "step_ms_extrapolated": 1e3 * d["step_seconds_extrapolated"],
+    }
+
+
+# ------------------------------------------------------------------------------------------------
+# GPU run
+# ------------------------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--dense-steps", type=int, default=8)
+    ap.add_argument("--diag-steps", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-child", action="store_true")
+    args = ap.parse_args()
+
+    if args.cpu_baseline_child:
+        print(json.dumps(cpu_baseline_child()))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from diffusion_long_context_amd import Handle
+    from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
+                                                  fdl_focus_params)
+    from diffusion_long_context_amd.step import geom_for
+    from synth import get_config
+    from synth.device import layer_kv, step_qkv_pool
+    from synth.gen import schedule_state
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = get_config(3)
+    g = geom_for(cfg)
+    NL, B, Hq, Hkv, D, T = cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len
+    n_blk = cfg.n_blk
+    spb, gen_steps = cfg.steps_per_block, cfg.n_gen_blocks * cfg.steps_per_block
+    h = Handle(workspace_bytes=256 << 20)
+    dev = torch.device("cuda")
+
+    log(f"drawing {NL} layers of KV cache on device")
+    K, V = [], []
+    for layer in range(NL):
+        k, v = layer_kv(cfg, layer, dev)
+        K.append(k)
+        V.append(v)
+    n_total = args.warmup + max(args.steps, args.diag_steps, args.dense_steps)
+    log(f"drawing per-step queries for {n_total} steps")
+    Q, KD, VD = step_qkv_pool(cfg, n_total, dev)
+    conf = torch.zeros((n_total, B, T), dtype=torch.float32)
+    masked = torch.zeros((n_total, B, T), dtype=torch.uint8)
+    has_prev = []
+    for i in range(n_total):
+        st = schedule_state(cfg, i % gen_steps)
+        has_prev.append(st["prev_conf"] is not None)
+        if st["prev_conf"] is not None:
+            conf[i] = torch.from_numpy(st["prev_conf"])
+        masked[i] = torch.from_numpy(st["masked"])
+    conf, masked = conf.to(dev), masked.to(dev)
+    ks = [torch.zeros((B, Hkv, n_blk, D), dtype=torch.float32, device=dev) for _ in range(NL)]
+    outs = [torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    pred_mask = torch.zeros(B, dtype=torch.int64, device=dev)
+    n_pred = torch.zeros(B, dtype=torch.int32, device=dev)
+    scores = torch.zeros((B, Hkv, n_blk), dtype=torch.float32, device=dev)
+    sink_pos = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device=dev)
+    n_sinks = torch.zeros(B, dtype=torch.int32, device=dev)
+    max_sel = cfg.max_sel_blocks
+    sel_idx = torch.zeros((B, Hkv, max_sel), dtype=torch.int32, device=dev)
+    n_sel = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, max_sel,
+                              cfg.sink_tau)
+
+    def modes(all_dense=False):
+        return [FDL_LAYER_DENSE if (all_dense or l < cfg.dense_layers)
+                else (FDL_LAYER_SOURCE if l == cfg.source_layer else FDL_LAYER_REUSE) for l in range(NL)]
+
+    def layer_array(i, all_dense=False):
+        return h.make_layers(g, [dict(q=Q[i, l], k_cache=K[l], v_cache=V[l], k_dec=KD[i, l], v_dec=VD[i, l],
+                                      ks=ks[l], out=outs[l], mode=m) for l, m in enumerate(modes(all_dense))])
+
+    log("building per-step layer tables")
+    arrays = [layer_array(i) for i in range(n_total)]
+    dense_arrays = [layer_array(i, all_dense=True) for i in range(args.dense_steps)]
+
+    def run(i0, n, tables, pool=True):
+        for i in range(i0, i0 + n):
+            if pool and (i % gen_steps) % spb == 0:
+                for layer in range(NL):
+                    h.fdl_pool_keys(g, K[layer], None, cfg.kv_block, ks[layer])
+            h.fdl_focus_step(g, params, conf[i] if has_prev[i] else None, masked[i], tables[i], pred_mask,
+                             n_pred, scores, sink_pos, n_sinks, sel_idx, n_sel)
+
+    log(f"warmup {args.warmup} steps")
+    run(0, args.warmup, arrays)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+
+    # ---- the timed region: exactly K steps; HIP events around every sparse-attention launch ----
+    log(f"timing {args.steps} steps")
+    h.fdl_profile_begin(args.steps * NL + 16, kinds=("sparse_attn",))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.warmup, args.steps, arrays)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    prof_main = h.fdl_profile_end()
+    assert h.fdl_get_status() == 0
+    nsel_last = n_sel.cpu().numpy()
+    nsinks_last = int(n_sinks.cpu().numpy()[0])
+
+    # ---- diagnostics (not the headline): per-kind breakdown, event overhead, dense baseline -------
+    log("diagnostic passes")
+    i0 = args.warmup
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(i0, args.diag_steps, arrays)
+    torch.cuda.synchronize()
+    t_plain = (time.perf_counter() - t0) / args.diag_steps
+    h.fdl_profile_begin(args.diag_steps * (NL * 6 + 8) + 64)
+    run(i0, args.diag_steps, arrays)
+    prof_all = h.fdl_profile_end()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(0, args.dense_steps, dense_arrays, pool=False)
+    torch.cuda.synchronize()
+    t_dense_step = (time.perf_counter() - t0) / args.dense_steps
+    assert h.fdl_get_status() == 0
+
+    def avg_us(prof, kind):
+        tot, cnt = prof[kind]
+        return tot / cnt if cnt else None
+
+    sparse_us = avg_us(prof_main, "sparse_attn")
+    units = int(nsel_last.sum())                       # selected 64-token blocks over all heads
+    unit_bytes = cfg.kv_block * D * 2 * 2              # K + V of one block, bf16
+    fixed_bytes = Hq * (T * D * 2 * 2) + Hkv * (T * D * 2 * 2) + units * 4 + B * Hkv * 4
+    launch_bytes = units * unit_bytes + fixed_bytes
+    achieved = launch_bytes / (sparse_us * 1e-6) / 1e9
+    ms_per_step = 1e3 * t_total / args.steps
+    value = cfg.ctx_len * B * NL * args.steps / t_total
+    reuse_layer_us = avg_us(prof_all, "layer_reuse")
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llada8b_32k_32layer", "batch": B, "ctx_len": cfg.ctx_len, "layers": NL,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "dec_len": T, "kv_block": cfg.kv_block,
+                   "top_k_blocks": cfg.top_k_blocks, "dense_layers": cfg.dense_layers,
+                   "sink_source_layer": cfg.source_layer, "gen_len": gen_steps},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "attn_mfma_kernel<128,1,false> (fdl_sparse_attn)",
+                     "avg_launch_us": sparse_us, "launches": prof_main["sparse_attn"][1],
+                     "bytes_per_launch": launch_bytes, "units_per_launch": units,
+                     "unit_bytes": unit_bytes},
+        "sparse_attn_layer_step_us": reuse_layer_us,
+        "sparse_attn_layer_kv_tokens_per_s": (cfg.ctx_len * B / (reuse_layer_us * 1e-6)) if reuse_layer_us else None,
+        "breakdown_us": {k: avg_us(prof_all, k) for k in prof_all if prof_all[k][1]},
+        "event_overhead_ms_per_step": 1e3 * (ms_per_step / 1e3 - t_plain),
+        "dense_step_ms": 1e3 * t_dense_step,
+        "speedup_vs_dense_hip": t_dense_step / t_plain,
+        "sinks_detected": nsinks_last,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, single thread)")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+    h.close()
+
+
+if __name__ == "__main__":
+    main()

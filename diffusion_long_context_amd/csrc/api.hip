@@ -76,6 +76,105 @@ fdl_status check_geom(fdl_handle h, const fdl_geom* g, Geom& o) {
   return FDL_OK;
 }
 
+// Records a pair of events around one launch (or one layer) when profiling is on.
+struct ProfScope {
+  fdl_handle h;
+  int kind;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(fdl_handle hh, int k) : h(hh), kind(k) {
+    if (h->prof_on && ((h->prof_mask >> k) & 1u) && h->prof_used + 2 <= h->prof_pool.size()) {
+      a = h->prof_pool[h->prof_used++];
+      b = h->prof_pool[h->prof_used++];
+      (void)hipEventRecord(a, h->stream);
+    }
+  }
+  ~ProfScope() {
+    if (a) {
+      (void)hipEventRecord(b, h->stream);
+      h->prof_recs.push_back({kind, a, b});
+    }
+  }
+};
+
+// ---- validated launches shared by the single calls and fdl_focus_step ----------------------
+
+fdl_status run_predict(fdl_handle h, int batch, int T, const float* prev_conf, const uint8_t* masked,
+                       int top_k, int window, uint64_t* pred_mask, int32_t* n_pred) {
+  ProfScope ps(h, FDL_PROF_PREDICT);
+  return hip_status(h, fdl::launch_predict(h->stream, batch, T, prev_conf, masked, top_k, window,
+                                           pred_mask, n_pred),
+                    "predict launch");
+}
+
+fdl_status run_score_units(fdl_handle h, const Geom& g, const void* q, const uint64_t* pred_mask,
+                           const float* ks, int n_units, float* scores) {
+  ProfScope ps(h, FDL_PROF_SCORE);
+  return hip_status(h, fdl::launch_score_units(h->stream, g, q, pred_mask, ks, n_units, scores),
+                    "score_units launch");
+}
+
+fdl_status check_sinks(fdl_handle h, const Geom& g, const void* k_cache, const void* k_dec,
+                       float tau, int max_sinks, const int32_t* sink_pos, const int32_t* n_sinks,
+                       int* ns, int* cap) {
+  if (!k_cache || !k_dec || !sink_pos || !n_sinks)
+    return fail(h, FDL_EINVAL, "sink detection needs k_cache, k_dec, sink_pos and n_sinks");
+  if (g.paged) return fail(h, FDL_EUNSUPPORTED, "sink detection reads a contiguous cache");
+  if (!(tau > 0.f)) return fail(h, FDL_EINVAL, "sink_tau must be > 0");
+  if (max_sinks < 1) return fail(h, FDL_EINVAL, "max_sinks must be >= 1");
+  if (g.Hq > 255) return fail(h, FDL_EUNSUPPORTED, "sink detection supports up to 255 q-heads");
+  if (g.dtype == FDL_BF16 && g.T > 32)
+    return fail(h, FDL_EUNSUPPORTED, "bf16 sink detection needs dec_len <= 32");
+  const size_t need = fdl::sink_scratch_bytes(g, ns, cap);
+  if (need > h->scratch_bytes) return fail(h, FDL_ENOMEM, "workspace too small for sink detection");
+  return FDL_OK;
+}
+
+fdl_status run_sinks(fdl_handle h, const Geom& g, const void* q, const uint64_t* pred_mask,
+                     const void* k_cache, const void* k_dec, float tau, int max_sinks,
+                     int32_t* sink_pos, int32_t* n_sinks, int ns, int cap) {
+  ProfScope ps(h, FDL_PROF_SINKS);
+  return hip_status(h, fdl::launch_sinks(h->stream, g, q, pred_mask, k_cache, k_dec, tau, max_sinks,
+                                         sink_pos, n_sinks, h->scratch, ns, cap, h->status,
+                                         h->num_cus),
+                    "sinks launch");
+}
+
+fdl_status run_select(fdl_handle h, const Geom& g, const float* scores, int n_units, int unit_log2,
+                      const int32_t* sink_pos, const int32_t* n_sinks, int max_sinks,
+                      const int32_t* cand_idx, int n_cand, int top_k, int force_first, int max_sel,
+                      int32_t* sel_idx, int32_t* n_sel) {
+  ProfScope ps(h, FDL_PROF_SELECT);
+  return hip_status(h, fdl::launch_select(h->stream, g, scores, n_units, unit_log2, sink_pos, n_sinks,
+                                          max_sinks, cand_idx, n_cand, top_k, force_first, max_sel,
+                                          sel_idx, n_sel, h->status),
+                    "select launch");
+}
+
+int attn_splits(fdl_handle h, const Geom& g, long long list_tokens) {
+  if (g.dtype != FDL_BF16) return 1;
+  int n_splits = g.G == 1 ? fdl::mha_choose_splits(g, list_tokens, h->num_cus)
+                          : fdl::attn_choose_splits(g, list_tokens, h->num_cus);
+  while (n_splits > 1 && fdl::attn_scratch_bytes(g, n_splits) > h->scratch_bytes) n_splits /= 2;
+  return n_splits;
+}
+
+fdl_status run_attn(fdl_handle h, const Geom& g, const void* q, const void* k_cache,
+                    const void* v_cache, const void* k_dec, const void* v_dec,
+                    const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
+                    int max_sel, int unit_log2, int dense, void* out) {
+  long long list_tokens = g.L;
+  if (!dense) {
+    list_tokens = (long long)max_sel << unit_log2;
+    if (list_tokens > g.L) list_tokens = g.L;
+  }
+  const int n_splits = attn_splits(h, g, list_tokens);
+  ProfScope ps(h, dense ? FDL_PROF_DENSE_ATTN : FDL_PROF_SPARSE_ATTN);
+  return hip_status(h, fdl::launch_attn(h->stream, g, q, k_cache, v_cache, k_dec, v_dec, page_table,
+                                        sel_idx, n_sel, max_sel, unit_log2, dense, out, h->scratch,
+                                        n_splits, h->tickets, h->status),
+                    "attention launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,6 +273,7 @@ fdl_status fdl_pool_keys(fdl_handle h, const fdl_geom* gp, const void* k_cache,
   if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
   if (!is_pow2(unit_tokens) || unit_tokens > 4096)
     return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
+  ProfScope ps(h, FDL_PROF_POOL);
   return hip_status(h, fdl::launch_pool_keys(h->stream, g, k_cache, page_table, ilog2(unit_tokens), ks,
                                              h->status),
                     "pool_keys launch");
@@ -189,9 +289,7 @@ fdl_status fdl_predict_queries(fdl_handle h, int32_t batch, int32_t dec_len, con
   if (window < 0) return fail(h, FDL_EINVAL, "window must be >= 0");
   if (!masked || !pred_mask || !n_pred)
     return fail(h, FDL_EINVAL, "masked, pred_mask and n_pred must be non-NULL");
-  return hip_status(h, fdl::launch_predict(h->stream, batch, dec_len, prev_conf, masked, top_k, window,
-                                           pred_mask, n_pred),
-                    "predict launch");
+  return run_predict(h, batch, dec_len, prev_conf, masked, top_k, window, pred_mask, n_pred);
 }
 
 fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* gp, const void* q, const uint64_t* pred_mask,
@@ -213,6 +311,7 @@ fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* gp, const void* q, con
     if (!k_cache) return fail(h, FDL_EINVAL, "level-2 scoring needs k_cache");
     if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
     if (g.L % unit_tokens) return fail(h, FDL_EINVAL, "level-2 scoring needs ctx_len %% unit_tokens == 0");
+    ProfScope ps(h, FDL_PROF_SCORE);
     return hip_status(h, fdl::launch_score_tokens(h->stream, g, q, pred_mask, k_cache, page_table,
                                                   ilog2(unit_tokens), cand_idx, n_cand, scores,
                                                   h->status),
@@ -220,26 +319,13 @@ fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* gp, const void* q, con
   }
   if (!ks) return fail(h, FDL_EINVAL, "level-1 scoring needs ks");
   int ns = 0, cap = 0;
-  size_t need = 0;
   if (detect_sinks) {
-    if (!k_cache || !k_dec || !sink_pos || !n_sinks)
-      return fail(h, FDL_EINVAL, "sink detection needs k_cache, k_dec, sink_pos and n_sinks");
-    if (g.paged) return fail(h, FDL_EUNSUPPORTED, "sink detection reads a contiguous cache");
-    if (!(sink_tau > 0.f)) return fail(h, FDL_EINVAL, "sink_tau must be > 0");
-    if (max_sinks < 1) return fail(h, FDL_EINVAL, "max_sinks must be >= 1");
-    if (g.Hq > 255) return fail(h, FDL_EUNSUPPORTED, "sink detection supports up to 255 q-heads");
-    if (g.dtype == FDL_BF16 && g.T > 32)
-      return fail(h, FDL_EUNSUPPORTED, "bf16 sink detection needs dec_len <= 32");
-    need = fdl::sink_scratch_bytes(g, &ns, &cap);
-    if (need > h->scratch_bytes) return fail(h, FDL_ENOMEM, "workspace too small for sink detection");
+    st = check_sinks(h, g, k_cache, k_dec, sink_tau, max_sinks, sink_pos, n_sinks, &ns, &cap);
+    if (st != FDL_OK) return st;
   }
-  st = hip_status(h, fdl::launch_score_units(h->stream, g, q, pred_mask, ks, n_units, scores),
-                  "score_units launch");
+  st = run_score_units(h, g, q, pred_mask, ks, n_units, scores);
   if (st != FDL_OK || !detect_sinks) return st;
-  return hip_status(h, fdl::launch_sinks(h->stream, g, q, pred_mask, k_cache, k_dec, sink_tau, max_sinks,
-                                         sink_pos, n_sinks, h->scratch, ns, cap, h->status,
-                                         h->num_cus),
-                    "sinks launch");
+  return run_sinks(h, g, q, pred_mask, k_cache, k_dec, sink_tau, max_sinks, sink_pos, n_sinks, ns, cap);
 }
 
 fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* gp, const float* scores, int32_t n_units,
@@ -271,10 +357,8 @@ fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* gp, const float* scor
     if (need > n_units) need = n_units;
     if (need > max_sel) return fail(h, FDL_EINVAL, "max_sel must cover min(n_units, max_sinks + top_k)");
   }
-  return hip_status(h, fdl::launch_select(h->stream, g, scores, n_units, ilog2(unit_tokens), sink_pos,
-                                          n_sinks, max_sinks, cand_idx, n_cand, top_k,
-                                          force_first ? 1 : 0, max_sel, sel_idx, n_sel, h->status),
-                    "select launch");
+  return run_select(h, g, scores, n_units, ilog2(unit_tokens), sink_pos, n_sinks, max_sinks, cand_idx,
+                    n_cand, top_k, force_first ? 1 : 0, max_sel, sel_idx, n_sel);
 }
 
 static fdl_status attn_common(fdl_handle h, const fdl_geom* gp, const void* q, const void* k_cache,
@@ -289,27 +373,18 @@ static fdl_status attn_common(fdl_handle h, const fdl_geom* gp, const void* q, c
   if (g.L > 0 && (!k_cache || !v_cache)) return fail(h, FDL_EINVAL, "k_cache and v_cache must be non-NULL");
   if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
   int unit_log2 = 0;
-  long long list_tokens = g.L;
   if (!dense) {
     if (!sel_idx || !n_sel) return fail(h, FDL_EINVAL, "sel_idx and n_sel must be non-NULL");
     if (max_sel < 1) return fail(h, FDL_EINVAL, "max_sel must be >= 1");
     if (!is_pow2(sel_unit_tokens) || sel_unit_tokens > 4096)
       return fail(h, FDL_EINVAL, "sel_unit_tokens must be a power of two in [1, 4096]");
     unit_log2 = ilog2(sel_unit_tokens);
-    list_tokens = (long long)max_sel * sel_unit_tokens;
-    if (list_tokens > g.L) list_tokens = g.L;
-    if ((long long)max_sel * sel_unit_tokens >= (1LL << 30)) return fail(h, FDL_EUNSUPPORTED, "selection too large");
+    if ((long long)max_sel * sel_unit_tokens >= (1LL << 30))
+      return fail(h, FDL_EUNSUPPORTED, "selection too large");
   }
-  int n_splits = 1;
-  if (g.dtype == FDL_BF16) {
-    if (g.T > 32) return fail(h, FDL_EUNSUPPORTED, "bf16 attention needs dec_len <= 32");
-    n_splits = fdl::attn_choose_splits(g, list_tokens, h->num_cus);
-    while (n_splits > 1 && fdl::attn_scratch_bytes(g, n_splits) > h->scratch_bytes) n_splits /= 2;
-  }
-  return hip_status(h, fdl::launch_attn(h->stream, g, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx,
-                                        n_sel, max_sel, unit_log2, dense, out, h->scratch, n_splits,
-                                        h->tickets, h->status),
-                    "attention launch");
+  if (g.dtype == FDL_BF16 && g.T > 32) return fail(h, FDL_EUNSUPPORTED, "bf16 attention needs dec_len <= 32");
+  return run_attn(h, g, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel, unit_log2,
+                  dense, out);
 }
 
 fdl_status fdl_sparse_attn(fdl_handle h, const fdl_geom* g, const void* q, const void* k_cache,
@@ -324,6 +399,129 @@ fdl_status fdl_dense_attn(fdl_handle h, const fdl_geom* g, const void* q, const 
                           const void* v_cache, const void* k_dec, const void* v_dec,
                           const int32_t* page_table, void* out) {
   return attn_common(h, g, q, k_cache, v_cache, k_dec, v_dec, page_table, nullptr, nullptr, 0, 1, 1, out);
+}
+
+fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_params* fp,
+                          const float* prev_conf, const uint8_t* masked, int32_t n_layers,
+                          const fdl_layer_io* layers, uint64_t* pred_mask, int32_t* n_pred,
+                          float* scores, int32_t* sink_pos, int32_t* n_sinks, int32_t* sel_idx,
+                          int32_t* n_sel) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!fp || !masked || !pred_mask || !n_pred || n_layers < 0 || (n_layers > 0 && !layers))
+    return fail(h, FDL_EINVAL, "params, masked, pred_mask, n_pred and layers must be non-NULL");
+  if (g.paged) return fail(h, FDL_EUNSUPPORTED, "fdl_focus_step runs contiguous caches");
+  if (g.dtype == FDL_BF16 && g.T > 32) return fail(h, FDL_EUNSUPPORTED, "bf16 attention needs dec_len <= 32");
+  if (fp->top_k_pos < 0 || fp->window < 0 || fp->top_k_blocks < 0)
+    return fail(h, FDL_EINVAL, "top_k_pos, window and top_k_blocks must be >= 0");
+  const int n_blk = (g.L + g.bt - 1) / g.bt;
+  const int bt_log2 = ilog2(g.bt);
+  bool any_sparse = false;
+  const fdl_layer_io* first_source = nullptr;
+  for (int l = 0; l < n_layers; ++l) {
+    const fdl_layer_io& io = layers[l];
+    if (io.mode < FDL_LAYER_DENSE || io.mode > FDL_LAYER_REUSE) return fail(h, FDL_EINVAL, "layer %d: bad mode", l);
+    if (!io.q || !io.k_dec || !io.v_dec || !io.out || (g.L > 0 && (!io.k_cache || !io.v_cache)))
+      return fail(h, FDL_EINVAL, "layer %d: NULL tensor", l);
+    if (io.mode != FDL_LAYER_DENSE) {
+      any_sparse = true;
+      if (!io.ks) return fail(h, FDL_EINVAL, "layer %d: sparse layer needs ks", l);
+    }
+    if (io.mode == FDL_LAYER_SOURCE && !first_source) first_source = &io;
+  }
+  int ns = 0, cap = 0;
+  if (any_sparse) {
+    if (!scores || !sel_idx || !n_sel || !sink_pos || !n_sinks)
+      return fail(h, FDL_EINVAL, "sparse layers need scores, sink_pos, n_sinks, sel_idx and n_sel");
+    if (n_blk > 8192) return fail(h, FDL_EUNSUPPORTED, "more than 8192 KV blocks");
+    if (fp->max_sinks < 1) return fail(h, FDL_EINVAL, "max_sinks must be >= 1");
+    long long need = (long long)fp->max_sinks + fp->top_k_blocks;
+    if (need > n_blk) need = n_blk;
+    if (fp->max_sel < 1 || need > fp->max_sel)
+      return fail(h, FDL_EINVAL, "max_sel must cover min(n_blk, max_sinks + top_k_blocks)");
+  }
+  if (first_source) {
+    st = check_sinks(h, g, first_source->k_cache, first_source->k_dec, fp->sink_tau, fp->max_sinks,
+                     sink_pos, n_sinks, &ns, &cap);
+    if (st != FDL_OK) return st;
+  }
+  st = run_predict(h, g.B, g.T, prev_conf, masked, fp->top_k_pos, fp->window, pred_mask, n_pred);
+  if (st != FDL_OK) return st;
+  for (int l = 0; l < n_layers; ++l) {
+    const fdl_layer_io& io = layers[l];
+    const int kind = io.mode == FDL_LAYER_DENSE ? FDL_PROF_LAYER_DENSE
+                   : io.mode == FDL_LAYER_SOURCE ? FDL_PROF_LAYER_SOURCE : FDL_PROF_LAYER_REUSE;
+    ProfScope layer_scope(h, kind);
+    if (io.mode == FDL_LAYER_DENSE) {
+      st = run_attn(h, g, io.q, io.k_cache, io.v_cache, io.k_dec, io.v_dec, nullptr, nullptr, nullptr, 0, 0,
+                    1, io.out);
+      if (st != FDL_OK) return st;
+      continue;
+    }
+    st = run_score_units(h, g, io.q, pred_mask, io.ks, n_blk, scores);
+    if (st != FDL_OK) return st;
+    if (io.mode == FDL_LAYER_SOURCE) {
+      st = run_sinks(h, g, io.q, pred_mask, io.k_cache, io.k_dec, fp->sink_tau, fp->max_sinks, sink_pos,
+                     n_sinks, ns, cap);
+      if (st != FDL_OK) return st;
+    }
+    st = run_select(h, g, scores, n_blk, bt_log2, sink_pos, n_sinks, fp->max_sinks, nullptr, 0,
+                    fp->top_k_blocks, 0, fp->max_sel, sel_idx, n_sel);
+    if (st != FDL_OK) return st;
+    st = run_attn(h, g, io.q, io.k_cache, io.v_cache, io.k_dec, io.v_dec, nullptr, sel_idx, n_sel,
+                  fp->max_sel, bt_log2, 0, io.out);
+    if (st != FDL_OK) return st;
+  }
+  return FDL_OK;
+}
+
+fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask) {
+  if (!h || max_records < 1) return h ? fail(h, FDL_EINVAL, "max_records must be >= 1") : FDL_EINVAL;
+  for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
+  h->prof_pool.clear();
+  h->prof_recs.clear();
+  h->prof_used = 0;
+  h->prof_pool.reserve((size_t)2 * max_records);
+  h->prof_recs.reserve((size_t)max_records);
+  for (int i = 0; i < 2 * max_records; ++i) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (hipEvent_t x : h->prof_pool) (void)hipEventDestroy(x);
+      h->prof_pool.clear();
+      return fail(h, FDL_EHIP, "hipEventCreate failed");
+    }
+    h->prof_pool.push_back(e);
+  }
+  h->prof_on = true;
+  h->prof_mask = kind_mask;
+  return FDL_OK;
+}
+
+fdl_status fdl_profile_end(fdl_handle h, double* total_us, int64_t* counts) {
+  if (!h) return FDL_EINVAL;
+  if (!total_us || !counts) return fail(h, FDL_EINVAL, "total_us and counts must be non-NULL");
+  fdl_status st = hip_status(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+  for (int k = 0; k < FDL_PROF_KINDS; ++k) {
+    total_us[k] = 0.0;
+    counts[k] = 0;
+  }
+  if (st == FDL_OK) {
+    for (const auto& r : h->prof_recs) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess && r.kind >= 0 && r.kind < FDL_PROF_KINDS) {
+        total_us[r.kind] += 1000.0 * ms;
+        counts[r.kind] += 1;
+      }
+    }
+  }
+  for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
+  h->prof_pool.clear();
+  h->prof_recs.clear();
+  h->prof_used = 0;
+  h->prof_on = false;
+  return st;
 }
 
 }  // extern "C"

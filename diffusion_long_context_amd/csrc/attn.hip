@@ -13,8 +13,8 @@
 //   O^T = V^T P^T (A = V columns from LDS, B = the probabilities straight from the S^T registers),
 // which keeps every softmax statistic in the lane that owns its query, so the online softmax needs
 // one cross-lane exchange per tile.  Within a workgroup, waves that share a head merge through LDS;
-// across workgroups the partial (max, sum, O) go to scratch and the last workgroup of each KV head,
-// found with an atomic ticket, merges them and writes the bf16 output.
+// across workgroups the partial (max, sum, O) go to scratch and are
+// merged by attn_combine_kernel.
 //
 // float32 path: a plain per-query-row kernel for the small float32 workload.
 #include "fdl_device.h"
@@ -35,36 +35,11 @@ struct AttnParams {
   float2* part_ml;   // [B][Hq][S][32]  (max in log2 units, sum)
   uint32_t* tickets;
   uint32_t* status;
-  KvLayout lay;
-  int Hq, T, max_sel, unit_log2, n_units, dense, n_splits;
+  const int32_t* page_table;
+  int Hq, Hkv, T, L, max_sel, unit_log2, n_units, n_splits;
+  int page_log2, pages_per_seq, n_pages;
   float scale_log2;  // log2(e) / sqrt(D)
 };
-
-// Source row of tile `e` (0 = the block's own tokens), row r; nullptr if the row is empty.
-template <int D>
-__device__ __forceinline__ const uint16_t* attn_row(const AttnParams& p, int b, int g, int e, int r,
-                                                    bool is_v, int n_list,
-                                                    const int32_t* __restrict__ sel_row) {
-  if (e == 0) {
-    if (r >= p.T) return nullptr;
-    return (is_v ? p.v_dec : p.k_dec) + ((int64_t)(b * p.lay.Hkv + g) * p.T + r) * D;
-  }
-  const int i = (e - 1) * 64 + r;
-  if (i >= n_list) return nullptr;
-  int t = i;
-  if (!p.dense) {
-    const int u = sel_row[i >> p.unit_log2];
-    if ((unsigned)u >= (unsigned)p.n_units) {
-      latch(p.status, ST_BAD_INDEX);
-      return nullptr;
-    }
-    t = (u << p.unit_log2) + (i & ((1 << p.unit_log2) - 1));
-  }
-  if (t >= p.lay.L) return nullptr;
-  int64_t off;
-  if (!p.lay.row_offset(b, g, t, off, p.status)) return nullptr;
-  return (is_v ? p.v : p.k) + off;
-}
 
 template <int G>
 struct AttnShape {
@@ -72,7 +47,43 @@ struct AttnShape {
   static constexpr int NW = G > 4 ? 8 : 4;                      // waves per workgroup
 };
 
-template <int D, int G>
+// Element offset of row r of tile e (0 = the block's own tokens, relative to k_dec / v_dec; >= 1:
+// list tiles, relative to the cache) and whether the row holds a token.  Branch-free, so that the
+// caller can issue every load of a round back to back.
+template <int D, bool DENSE, bool PAGED>
+__device__ __forceinline__ int64_t attn_row_off(const AttnParams& p, const KvRows<PAGED>& rows, int b,
+                                                int g, int e, bool tile_live, int r, int n_list,
+                                                const int32_t* __restrict__ sel_row, bool& ok,
+                                                bool& bad) {
+  if (e == 0) {   // uniform
+    ok = tile_live && r < p.T;
+    return ((int64_t)(b * p.Hkv + g) * p.T + (r < p.T ? r : p.T - 1)) * D;
+  }
+  if (!tile_live || p.L == 0) {   // uniform; the caller then reads from k_dec / v_dec
+    ok = false;
+    return 0;
+  }
+  const int i = (e - 1) * 64 + r;
+  ok = i < n_list;
+  const int ii = ok ? i : 0;
+  int t = ii;
+  if constexpr (!DENSE) {
+    const int u = sel_row[ii >> p.unit_log2];
+    const bool uok = (unsigned)u < (unsigned)p.n_units;
+    bad = bad || (ok && !uok);
+    ok = ok && uok;
+    t = uok ? (u << p.unit_log2) + (ii & ((1 << p.unit_log2) - 1)) : 0;
+  }
+  ok = ok && t < p.L;
+  t = (t < p.L) ? t : 0;
+  bool pbad = false;
+  const int64_t off = rows.off(b, g, t, pbad);
+  bad = bad || (ok && pbad);
+  ok = ok && !pbad;
+  return off;
+}
+
+template <int D, int G, bool DENSE, bool PAGED>
 __global__ __launch_bounds__(AttnShape<G>::NW * 64, 1) void attn_mfma_kernel(const AttnParams p) {
   constexpr int TPR = AttnShape<G>::TPR;
   constexpr int NW = AttnShape<G>::NW;
@@ -83,32 +94,44 @@ __global__ __launch_bounds__(AttnShape<G>::NW * 64, 1) void attn_mfma_kernel(con
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int PROW = D / 8;                           // 16-byte pieces per row
-  constexpr int PTILE = 64 * PROW;
-  constexpr int PPT = TPR * 2 * PTILE / NT;             // pieces per thread per round
-  static_assert((TPR * 2 * PTILE) % NT == 0 && PTILE % NT == 0, "pieces must split evenly");
+  constexpr int RPP = NT / PROW;                        // rows covered by one pass of the block
+  constexpr int RPT = 64 / RPP;                         // rows per thread per tile
+  static_assert(NT % PROW == 0 && 64 % RPP == 0, "tile rows must split evenly over the block");
   __shared__ __attribute__((aligned(16))) uint16_t lds[TPR * 2 * TILE];
+  __shared__ uint8_t s_valid[TPR][64];
   __shared__ float2 s_ml[4][32];
-  __shared__ uint32_t s_ticket;
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
-  const int Hkv = p.lay.Hkv;
+  const int Hkv = p.Hkv;
   const int64_t seg = (int64_t)b * Hkv + g;
   const int S = p.n_splits;
+  KvRows<PAGED> rows;
+  rows.Hkv = Hkv;
+  rows.L = p.L;
+  rows.D = D;
+  rows.page_log2 = p.page_log2;
+  rows.pages_per_seq = p.pages_per_seq;
+  rows.n_pages = p.n_pages;
+  rows.page_table = p.page_table;
+  bool bad = false;
 
   int n_list;
-  if (p.dense) {
-    n_list = p.lay.L;
+  if (DENSE) {
+    n_list = p.L;
   } else {
     int ns = p.n_sel[seg];
     ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
     n_list = ns << p.unit_log2;
   }
+  if (p.L == 0) n_list = 0;
   const int n_tiles = 1 + (n_list + 63) / 64;
   const int e0 = (int)((int64_t)n_tiles * s / S);
   const int e1 = (int)((int64_t)n_tiles * (s + 1) / S);
-  const int32_t* sel_row = p.sel_idx + seg * p.max_sel;
+  const int32_t* sel_row = DENSE ? nullptr : p.sel_idx + seg * p.max_sel;
+  const int chunk = tid % PROW;
+  const int rbase = tid / PROW;
 
   const int slot = (TPR > 1) ? wave / G : 0;
   int heads[HPW];
@@ -143,35 +166,50 @@ __global__ __launch_bounds__(AttnShape<G>::NW * 64, 1) void attn_mfma_kernel(con
   }
 
   const int rounds = (e1 - e0 + TPR - 1) / TPR;
-  uint4 stage[PPT];
+  uint4 stk[TPR][RPT], stv[TPR][RPT];
+  uint32_t okbits = 0;   // bit sl*RPT+m: row (sl, m) of the staged round holds a token
 
   auto load_round = [&](int rnd) {
+    int64_t off[TPR][RPT];
+    okbits = 0;
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int pc = tid + NT * j;
-      const int sl = pc / (2 * PTILE);
-      const int isv = (pc / PTILE) & 1;
-      const int rem = pc % PTILE;
-      const int row = rem / PROW, chunk = rem % PROW;
+    for (int sl = 0; sl < TPR; ++sl) {
       const int e = e0 + rnd * TPR + sl;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (e < e1) {
-        const uint16_t* src = attn_row<D>(p, b, g, e, row, isv != 0, n_list, sel_row);
-        if (src) v = *reinterpret_cast<const uint4*>(src + chunk * 8);
+      const bool live = e < e1;
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        bool ok;
+        off[sl][m] = attn_row_off<D, DENSE, PAGED>(p, rows, b, g, e, live, rbase + RPP * m, n_list,
+                                                   sel_row, ok, bad);
+        okbits |= (ok ? 1u : 0u) << (sl * RPT + m);
       }
-      stage[j] = v;
+    }
+#pragma unroll
+    for (int sl = 0; sl < TPR; ++sl) {
+      const int e = e0 + rnd * TPR + sl;
+      // the own block, dead slots and an empty cache all read from the (always valid) k_dec / v_dec
+      const bool use_dec = (e == 0) || (e >= e1) || (p.L == 0);
+      const uint16_t* kb = use_dec ? p.k_dec : p.k;
+      const uint16_t* vb = use_dec ? p.v_dec : p.v;
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        stk[sl][m] = *reinterpret_cast<const uint4*>(kb + off[sl][m] + chunk * 8);
+        stv[sl][m] = *reinterpret_cast<const uint4*>(vb + off[sl][m] + chunk * 8);
+      }
     }
   };
   auto store_round = [&]() {
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int pc = tid + NT * j;
-      const int sl = pc / (2 * PTILE);
-      const int isv = (pc / PTILE) & 1;
-      const int rem = pc % PTILE;
-      const int row = rem / PROW, chunk = rem % PROW;
-      *reinterpret_cast<uint4*>(lds + (sl * 2 + isv) * TILE + row * RS + chunk * 8) = stage[j];
-    }
+    for (int sl = 0; sl < TPR; ++sl)
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        const bool ok = (okbits >> (sl * RPT + m)) & 1u;
+        const int row = rbase + RPP * m;
+        *reinterpret_cast<uint4*>(lds + (sl * 2) * TILE + row * RS + chunk * 8) = ok ? stk[sl][m] : zero;
+        *reinterpret_cast<uint4*>(lds + (sl * 2 + 1) * TILE + row * RS + chunk * 8) = ok ? stv[sl][m] : zero;
+        if (chunk == 0) s_valid[sl][row] = ok ? 1 : 0;
+      }
   };
 
   if (rounds > 0) load_round(0);
@@ -181,8 +219,7 @@ __global__ __launch_bounds__(AttnShape<G>::NW * 64, 1) void attn_mfma_kernel(con
     if (rnd + 1 < rounds) load_round(rnd + 1);
     const int e = e0 + rnd * TPR + slot;
     if (e < e1) {
-      const bool rv = attn_row<D>(p, b, g, e, lane, false, n_list, sel_row) != nullptr;
-      const uint64_t vm = __ballot(rv);
+      const uint64_t vm = __ballot(s_valid[slot][lane] != 0);
       const uint16_t* Kt = lds + (slot * 2) * TILE;
       const uint16_t* Vt = Kt + TILE;
 #pragma unroll
@@ -258,6 +295,8 @@ __global__ __launch_bounds__(AttnShape<G>::NW * 64, 1) void attn_mfma_kernel(con
     }
     __syncthreads();
   }
+
+  latch_bad(p.status, bad);
 
   // ---- this workgroup's result per head: (m, l, O) ------------------------------------------
   float* po_base = p.part_o;
@@ -353,49 +392,10 @@ __global__ __launch_bounds__(AttnShape<G>::NW * 64, 1) void attn_mfma_kernel(con
       }
     }
   }
-  if (S == 1) return;
-
-  // ---- cross-split merge by the last workgroup of this KV head --------------------------------
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg], 1u);
-  __syncthreads();
-  if (s_ticket != (uint32_t)(S - 1)) return;
-  __threadfence();
-  constexpr int ITEMS = G * 32 * (D / 4);
-  for (int it = tid; it < ITEMS; it += NT) {
-    const int j = it / (32 * (D / 4));
-    const int q = (it / (D / 4)) % 32;
-    const int d0 = (it % (D / 4)) * 4;
-    if (q >= p.T) continue;
-    const int64_t hb = (int64_t)b * p.Hq + g * G + j;
-    const float2* ml = pml_base + hb * S * 32 + q;
-    float M = -__builtin_inff();
-    for (int t = 0; t < S; ++t) M = fmaxf(M, ml[t * 32].x);
-    float Ls = 0.f;
-    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t = 0; t < S; ++t) {
-      const float2 v = ml[t * 32];
-      if (v.y == 0.f) continue;
-      const float w = exp2f(v.x - M);
-      Ls += v.y * w;
-      const float4 o = *reinterpret_cast<const float4*>(po_base + ((hb * S + t) * 32 + q) * D + d0);
-      O.x += o.x * w;
-      O.y += o.y * w;
-      O.z += o.z * w;
-      O.w += o.w * w;
-    }
-    const float inv = 1.f / Ls;
-    uint2 w;
-    w.x = pack_bf16x2(O.x * inv, O.y * inv);
-    w.y = pack_bf16x2(O.z * inv, O.w * inv);
-    *reinterpret_cast<uint2*>(p.out + (hb * p.T + q) * D + d0) = w;
-  }
-  if (tid == 0) p.tickets[seg] = 0u;
 }
 
 // ------------------------------------------------------------------------------------------------
-// float32 path: one thread per query row, 32-token chunks staged in LDS.
+// float32 path: one thread per query row, 32-token chunks staged in LDS (small workloads only).
 // ------------------------------------------------------------------------------------------------
 
 struct F32Params {
@@ -408,34 +408,44 @@ struct F32Params {
   const int32_t* n_sel;
   float* out;
   uint32_t* status;
-  KvLayout lay;
-  int Hq, G, T, max_sel, unit_log2, n_units, dense;
+  const int32_t* page_table;
+  int Hq, Hkv, G, T, L, max_sel, unit_log2, n_units, dense;
+  int page_log2, pages_per_seq, n_pages;
   float scale;
 };
 
-template <int D>
-__device__ __forceinline__ const float* f32_row(const F32Params& p, int b, int g, int i, bool is_v,
-                                                int n_list, const int32_t* sel_row) {
-  // i < T: own block row i; else list position i - T
-  if (i < p.T) return (is_v ? p.v_dec : p.k_dec) + ((int64_t)(b * p.lay.Hkv + g) * p.T + i) * D;
-  i -= p.T;
-  if (i >= n_list) return nullptr;
-  int t = i;
-  if (!p.dense) {
-    const int u = sel_row[i >> p.unit_log2];
-    if ((unsigned)u >= (unsigned)p.n_units) {
-      latch(p.status, ST_BAD_INDEX);
-      return nullptr;
-    }
-    t = (u << p.unit_log2) + (i & ((1 << p.unit_log2) - 1));
+// Row i of the extended list (i < T: own block row i; else list position i - T): element offset
+// into k_dec / v_dec (own) or the cache, and whether it holds a token.
+template <int D, bool PAGED>
+__device__ __forceinline__ int64_t f32_row_off(const F32Params& p, const KvRows<PAGED>& rows, int b,
+                                               int g, int i, int n_list, const int32_t* sel_row,
+                                               bool& own, bool& ok, bool& bad) {
+  own = i < p.T;
+  if (own) {
+    ok = true;
+    return ((int64_t)(b * p.Hkv + g) * p.T + i) * D;
   }
-  if (t >= p.lay.L) return nullptr;
-  int64_t off;
-  if (!p.lay.row_offset(b, g, t, off, p.status)) return nullptr;
-  return (is_v ? p.v : p.k) + off;
+  const int li = i - p.T;
+  ok = li < n_list;
+  const int ii = ok ? li : 0;
+  int t = ii;
+  if (!p.dense) {
+    const int u = sel_row[ii >> p.unit_log2];
+    const bool uok = (unsigned)u < (unsigned)p.n_units;
+    bad = bad || (ok && !uok);
+    ok = ok && uok;
+    t = uok ? (u << p.unit_log2) + (ii & ((1 << p.unit_log2) - 1)) : 0;
+  }
+  ok = ok && t < p.L;
+  t = t < p.L ? t : 0;
+  bool pbad = false;
+  const int64_t off = rows.off(b, g, t, pbad);
+  bad = bad || (ok && pbad);
+  ok = ok && !pbad;
+  return off;
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const F32Params p) {
   __shared__ float kc[32][D + 1];
   __shared__ float vc[32][D + 1];
@@ -443,15 +453,25 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const F32Params p) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int g = h / p.G;
   const int qi = threadIdx.x;
-  const int64_t seg = (int64_t)b * p.lay.Hkv + g;
+  const int64_t seg = (int64_t)b * p.Hkv + g;
+  KvRows<PAGED> rows;
+  rows.Hkv = p.Hkv;
+  rows.L = p.L;
+  rows.D = D;
+  rows.page_log2 = p.page_log2;
+  rows.pages_per_seq = p.pages_per_seq;
+  rows.n_pages = p.n_pages;
+  rows.page_table = p.page_table;
+  bool bad = false;
   int n_list;
   if (p.dense) {
-    n_list = p.lay.L;
+    n_list = p.L;
   } else {
     int ns = p.n_sel[seg];
     ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
     n_list = ns << p.unit_log2;
   }
+  if (p.L == 0) n_list = 0;
   const int32_t* sel_row = p.sel_idx + seg * p.max_sel;
   const int total = p.T + n_list;
   float qr[D], o[D];
@@ -459,19 +479,26 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const F32Params p) {
   const float* qrow = p.q + (((int64_t)b * p.Hq + h) * p.T + (live ? qi : 0)) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    qr[d] = live ? qrow[d] : 0.f;
+    qr[d] = qrow[d];
     o[d] = 0.f;
   }
   float m = -__builtin_inff(), l = 0.f;
   for (int c0 = 0; c0 < total; c0 += 32) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 32 * D; idx += 64) {
-      const int r = idx / D, d = idx % D;
-      const float* ks = (c0 + r < total) ? f32_row<D>(p, b, g, c0 + r, false, n_list, sel_row) : nullptr;
-      const float* vs = ks ? f32_row<D>(p, b, g, c0 + r, true, n_list, sel_row) : nullptr;
-      kc[r][d] = ks ? ks[d] : 0.f;
-      vc[r][d] = vs ? vs[d] : 0.f;
-      if (d == 0) valid[r] = ks != nullptr;
+    if (threadIdx.x < 32) {
+      const int r = threadIdx.x;
+      bool own = false, ok = false;
+      const int i = c0 + r < total ? c0 + r : total - 1;
+      const int64_t off = f32_row_off<D, PAGED>(p, rows, b, g, i, n_list, sel_row, own, ok, bad);
+      ok = ok && (c0 + r < total);
+      const float* ks = (own ? p.k_dec : p.k) + off;
+      const float* vs = (own ? p.v_dec : p.v) + off;
+      for (int d = 0; d < D; ++d) {
+        const float kv = ks[d], vv = vs[d];
+        kc[r][d] = ok ? kv : 0.f;
+        vc[r][d] = ok ? vv : 0.f;
+      }
+      valid[r] = ok;
     }
     __syncthreads();
     float sc[32];
@@ -503,6 +530,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const F32Params p) {
 #pragma unroll
     for (int d = 0; d < D; ++d) orow[d] = o[d] * inv;
   }
+  latch_bad(p.status, bad);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -524,22 +552,30 @@ size_t attn_scratch_bytes(const Geom& g, int n_splits) {
 }
 
 template <int D, int G>
-static hipError_t launch_mfma(hipStream_t s, const AttnParams& p, dim3 grid) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, G>), grid, dim3(AttnShape<G>::NW * 64), 0, s, p);
+static hipError_t launch_mfma(hipStream_t s, const AttnParams& p, dim3 grid, bool dense, bool paged) {
+  const dim3 block(AttnShape<G>::NW * 64);
+  if (dense) {
+    if (paged) hipLaunchKernelGGL((attn_mfma_kernel<D, G, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_mfma_kernel<D, G, true, false>), grid, block, 0, s, p);
+  } else {
+    if (paged) hipLaunchKernelGGL((attn_mfma_kernel<D, G, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_mfma_kernel<D, G, false, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_mfma_g(hipStream_t s, const AttnParams& p, dim3 grid, int G) {
+static hipError_t launch_mfma_g(hipStream_t s, const AttnParams& p, dim3 grid, int G, bool dense,
+                                bool paged) {
   switch (G) {
-    case 1: return launch_mfma<D, 1>(s, p, grid);
-    case 2: return launch_mfma<D, 2>(s, p, grid);
-    case 3: return launch_mfma<D, 3>(s, p, grid);
-    case 4: return launch_mfma<D, 4>(s, p, grid);
-    case 5: return launch_mfma<D, 5>(s, p, grid);
-    case 6: return launch_mfma<D, 6>(s, p, grid);
-    case 7: return launch_mfma<D, 7>(s, p, grid);
-    case 8: return launch_mfma<D, 8>(s, p, grid);
+    case 1: return launch_mfma<D, 1>(s, p, grid, dense, paged);
+    case 2: return launch_mfma<D, 2>(s, p, grid, dense, paged);
+    case 3: return launch_mfma<D, 3>(s, p, grid, dense, paged);
+    case 4: return launch_mfma<D, 4>(s, p, grid, dense, paged);
+    case 5: return launch_mfma<D, 5>(s, p, grid, dense, paged);
+    case 6: return launch_mfma<D, 6>(s, p, grid, dense, paged);
+    case 7: return launch_mfma<D, 7>(s, p, grid, dense, paged);
+    case 8: return launch_mfma<D, 8>(s, p, grid, dense, paged);
   }
   return hipErrorInvalidValue;
 }
@@ -549,15 +585,6 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
                        const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                        int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
                        uint32_t* status) {
-  KvLayout lay;
-  lay.Hkv = g.Hkv;
-  lay.L = g.L;
-  lay.D = g.D;
-  lay.paged = g.paged;
-  lay.page_log2 = g.page_log2;
-  lay.pages_per_seq = g.pps;
-  lay.n_pages = g.n_pages;
-  lay.page_table = page_table;
   const int unit = 1 << unit_log2;
   const int n_units = (g.L + unit - 1) / unit;
   if (g.dtype == FDL_F32) {
@@ -571,22 +598,33 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
     p.n_sel = n_sel;
     p.out = static_cast<float*>(out);
     p.status = status;
-    p.lay = lay;
+    p.page_table = page_table;
     p.Hq = g.Hq;
+    p.Hkv = g.Hkv;
     p.G = g.G;
     p.T = g.T;
+    p.L = g.L;
     p.max_sel = max_sel;
     p.unit_log2 = unit_log2;
     p.n_units = n_units;
     p.dense = dense;
+    p.page_log2 = g.page_log2;
+    p.pages_per_seq = g.pps;
+    p.n_pages = g.n_pages;
     p.scale = 1.0f / sqrtf((float)g.D);
     dim3 grid(g.Hq, g.B);
-    if (g.D == 128)
-      hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(64), 0, s, p);
-    else
-      hipLaunchKernelGGL((attn_f32_kernel<64>), grid, dim3(64), 0, s, p);
+    if (g.D == 128) {
+      if (g.paged) hipLaunchKernelGGL((attn_f32_kernel<128, true>), grid, dim3(64), 0, s, p);
+      else hipLaunchKernelGGL((attn_f32_kernel<128, false>), grid, dim3(64), 0, s, p);
+    } else {
+      if (g.paged) hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, dim3(64), 0, s, p);
+      else hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, dim3(64), 0, s, p);
+    }
     return hipGetLastError();
   }
+  if (g.G == 1)
+    return launch_attn_mha(s, g, q, k, v, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel, unit_log2,
+                           dense, out, scratch, n_splits, tickets, status);
   AttnParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -601,17 +639,24 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
   p.part_ml = reinterpret_cast<float2*>(scratch + per * g.D * sizeof(float));
   p.tickets = tickets;
   p.status = status;
-  p.lay = lay;
+  p.page_table = page_table;
   p.Hq = g.Hq;
+  p.Hkv = g.Hkv;
   p.T = g.T;
+  p.L = g.L;
   p.max_sel = max_sel;
   p.unit_log2 = unit_log2;
   p.n_units = n_units;
-  p.dense = dense;
   p.n_splits = n_splits;
+  p.page_log2 = g.page_log2;
+  p.pages_per_seq = g.pps;
+  p.n_pages = g.n_pages;
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
   dim3 grid(n_splits, g.Hkv, g.B);
-  return g.D == 128 ? launch_mfma_g<128>(s, p, grid, g.G) : launch_mfma_g<64>(s, p, grid, g.G);
+  hipError_t err = g.D == 128 ? launch_mfma_g<128>(s, p, grid, g.G, dense != 0, g.paged != 0)
+                              : launch_mfma_g<64>(s, p, grid, g.G, dense != 0, g.paged != 0);
+  if (err != hipSuccess || n_splits == 1) return err;
+  return launch_attn_combine(s, p.part_o, p.part_ml, out, g.B * g.Hq, n_splits, g.T, g.D, false);
 }
 
 }  // namespace fdl

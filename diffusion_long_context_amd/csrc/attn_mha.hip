@@ -1,0 +1,514 @@
+// Gathered block-sparse (or dense) bidirectional attention for one query head per KV head.
+//
+// Focus-dLLM (abstract; Elamur "Summary"): the block's queries attend bidirectionally over only the
+// selected KV plus the block itself; Prefilling-dLLM (abstract): the same over chunk KV cached in
+// non-contiguous pages.  The arithmetic is softmax(q k^T / sqrt(D)) v with an online softmax over
+// 32-token tiles; the data movement is what this kernel is about.
+//
+// Layout of the work: one workgroup of 8 waves per (split, head, sequence); each wave streams its
+// own 32-token tiles (tile 0 is the block's own tokens) through a private 16 KiB LDS slot:
+//   1. the tile's K and V rows are fetched straight from HBM into LDS with global_load_lds_dwordx4
+//      (no register staging): each instruction moves 1 KiB, 64 lanes x 16 bytes, and lane l's bytes
+//      land at slot base + 16 l, so the lane -> global chunk map chooses the LDS layout; rows are
+//      stored with their 16-byte chunks XOR-swizzled by the row index so that the MFMA operand reads
+//      below are free of bank conflicts;
+//   2. the wave copies the tile from LDS into registers in MFMA operand order (K as the A operand of
+//      S^T = K Q^T; V read transposed as the A operand of O^T = V^T P^T);
+//   3. it issues the next tile's fetch into the same slot, and only then computes on the registers,
+//      so one tile per wave is always in flight while the MFMAs and the softmax run.
+// The compiler places a full vector-memory wait before any LDS read that follows an LDS fetch, which
+// is why the copy-to-registers step comes before the next fetch rather than double-buffering LDS.
+// Softmax statistics stay in the lane that owns the query (S^T puts queries on lanes), so one
+// cross-lane exchange per tile suffices.  At the end the 8 waves merge through LDS; with several
+// workgroups per head the partial (max, sum, O) go to scratch and attn_combine_kernel merges them.
+#include <type_traits>
+
+#include "fdl_device.h"
+#include "fdl_internal.h"
+
+namespace fdl {
+
+struct MhaParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* k_dec;
+  const uint16_t* v_dec;
+  const int32_t* sel_idx;
+  const int32_t* n_sel;
+  uint16_t* out;
+  float* part_o;     // [B][H][S][D][32] (d-major)
+  float2* part_ml;   // [B][H][S][32]
+  uint32_t* status;
+  const int32_t* page_table;
+  int H, T, L, max_sel, unit_log2, n_units, n_splits;
+  int page_log2, pages_per_seq, n_pages;
+  float scale_log2;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kMhaWaves = 8;
+constexpr int kTileTok = 32;
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int D>
+struct MhaShape {
+  static constexpr int PROW = D / 8;                 // 16-byte chunks per row
+  static constexpr int ROWS_PER_INSTR = 64 / PROW;   // rows one 1 KiB fetch covers
+  static constexpr int INSTR = kTileTok / ROWS_PER_INSTR;   // fetches per tile for K (same for V)
+  static constexpr int HALF = kTileTok * D;          // elements of K (or V) per tile
+  static constexpr int SLOT = 2 * HALF;              // elements per wave slot
+  static constexpr int KS = D / 16;
+  static constexpr int DT = D / 32;
+};
+
+// LDS chunk swizzle: chunk c of row r is stored at chunk slot c ^ swz(r).  swz permutes the low 4
+// bits of the row (bits 2 and 3 swapped) so that (a) the 16 rows read together by the K-operand
+// loads hit 16 different slots and (b) rows r and r + 4, which the two lane halves read together
+// for V, fall in different halves of the row's banks.
+__device__ __forceinline__ int swz(int r) { return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8); }
+
+// Offset type: contiguous caches address rows relative to the head's base with 32 bits
+// (L < 2^24, D <= 128); pages can sit anywhere in the pool and need 64 bits.
+template <bool PAGED>
+using RowOff = typename std::conditional<PAGED, int64_t, int32_t>::type;
+
+// A tile fetch in two steps, so that the selection-index loads of tile i+1 can fly together with
+// the data of tile i: mha_prepare resolves each of the lane's rows to a token (one batch of index
+// loads), mha_issue turns tokens into addresses (one batch of page-table loads when paged) and
+// launches the LDS fetches.
+template <int D>
+struct TilePrep {
+  int t[MhaShape<D>::INSTR];
+  uint32_t okbits;
+};
+
+template <int D, bool DENSE>
+__device__ __forceinline__ void mha_prepare(const MhaParams& p, int e, int n_list,
+                                            const int32_t* __restrict__ sel_row, int lane,
+                                            TilePrep<D>& tp, bool& bad) {
+  using S = MhaShape<D>;
+  constexpr int NI = S::INSTR;
+  const int rsub = lane / S::PROW;
+  tp.okbits = 0;
+  if (e == 0 || p.L == 0) {   // uniform: the own block (or an empty cache: nothing to fetch)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = j * S::ROWS_PER_INSTR + rsub;
+      const bool ok = (e == 0) && r < p.T;
+      tp.t[j] = (e == 0) ? (r < p.T ? r : p.T - 1) : 0;
+      tp.okbits |= (ok ? 1u : 0u) << j;
+    }
+    return;
+  }
+  bool ok[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int i = (e - 1) * kTileTok + j * S::ROWS_PER_INSTR + rsub;
+    ok[j] = i < n_list;
+    tp.t[j] = ok[j] ? i : 0;
+  }
+  if constexpr (!DENSE) {
+    int u[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) u[j] = sel_row[tp.t[j] >> p.unit_log2];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const bool uok = (unsigned)u[j] < (unsigned)p.n_units;
+      bad = bad || (ok[j] && !uok);
+      ok[j] = ok[j] && uok;
+      tp.t[j] = uok ? (u[j] << p.unit_log2) + (tp.t[j] & ((1 << p.unit_log2) - 1)) : 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    ok[j] = ok[j] && tp.t[j] < p.L;
+    tp.t[j] = tp.t[j] < p.L ? tp.t[j] : 0;
+    tp.okbits |= (ok[j] ? 1u : 0u) << j;
+  }
+}
+
+// Launch the LDS fetches of a prepared tile into the wave's slot; returns the 32-bit row mask.
+template <int D, bool PAGED>
+__device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<PAGED>& rows, int b, int h,
+                                              int e, const TilePrep<D>& tp, uint16_t* slot, int lane,
+                                              bool& bad) {
+  using S = MhaShape<D>;
+  constexpr int NI = S::INSTR;
+  const int rsub = lane / S::PROW;
+  const int sc = lane % S::PROW;
+  const int64_t head = (int64_t)b * p.H + h;
+  const bool dec = (e == 0) || (p.L == 0);   // uniform
+  const uint16_t* kb;
+  const uint16_t* vb;
+  RowOff<PAGED> off[NI];
+  uint32_t okbits = tp.okbits;
+  if (dec) {
+    kb = p.k_dec + head * p.T * D;
+    vb = p.v_dec + head * p.T * D;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) off[j] = (RowOff<PAGED>)(tp.t[j] * D);
+  } else if constexpr (PAGED) {
+    kb = p.k;
+    vb = p.v;
+    bool pb[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      pb[j] = false;
+      off[j] = rows.off(b, h, tp.t[j], pb[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const bool okj = (okbits >> j) & 1u;
+      bad = bad || (okj && pb[j]);
+      if (pb[j]) okbits &= ~(1u << j);
+    }
+  } else {
+    kb = p.k + head * p.L * D;
+    vb = p.v + head * p.L * D;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) off[j] = (RowOff<PAGED>)(tp.t[j] * D);
+  }
+  uint32_t okm = 0;
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int r = j * S::ROWS_PER_INSTR + rsub;
+    off[j] += (sc ^ (swz(r) & (S::PROW - 1))) * 8;   // global chunk stored at LDS slot sc of row r
+    const uint64_t bal = __ballot((okbits >> j) & 1u);
+#pragma unroll
+    for (int q = 0; q < S::ROWS_PER_INSTR; ++q)
+      okm |= (uint32_t)((bal >> (q * S::PROW)) & 1ull) << (j * S::ROWS_PER_INSTR + q);
+  }
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    __builtin_amdgcn_global_load_lds((const void*)(kb + off[j]), (lds_void_t*)(slot + j * 512), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    __builtin_amdgcn_global_load_lds((const void*)(vb + off[j]), (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, 0);
+  return okm;
+}
+
+template <int D, bool DENSE, bool PAGED>
+__global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaParams p) {
+  using S = MhaShape<D>;
+  constexpr int NT = kMhaWaves * 64;
+  constexpr int KS = S::KS, DT = S::DT, PROW = S::PROW;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kMhaWaves * S::SLOT];
+  __shared__ float2 s_ml[kMhaWaves][32];
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 31, hh = lane >> 5;
+  const int64_t seg = (int64_t)b * p.H + h;
+  const int NS = p.n_splits;
+  KvRows<PAGED> rows;
+  rows.Hkv = p.H;
+  rows.L = p.L;
+  rows.D = D;
+  rows.page_log2 = p.page_log2;
+  rows.pages_per_seq = p.pages_per_seq;
+  rows.n_pages = p.n_pages;
+  rows.page_table = p.page_table;
+  bool bad = false;
+
+  int n_list;
+  if (DENSE) {
+    n_list = p.L;
+  } else {
+    int ns = p.n_sel[seg];
+    ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
+    n_list = ns << p.unit_log2;
+  }
+  if (p.L == 0) n_list = 0;
+  const int n_tiles = 1 + (n_list + kTileTok - 1) / kTileTok;
+  const int e0 = (int)((int64_t)n_tiles * s / NS);
+  const int e1 = (int)((int64_t)n_tiles * (s + 1) / NS);
+  const int32_t* sel_row = DENSE ? nullptr : p.sel_idx + seg * p.max_sel;
+  uint16_t* slot = lds + wave * S::SLOT;
+
+  // Q fragments (B operand of S^T = K Q^T): lane (q, hh) holds q[q][hh*D/2 + 8ks .. +8]
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qrow = p.q + ((int64_t)seg * p.T + (ql < p.T ? ql : 0)) * D + hh * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + ks * 8);
+      if (ql >= p.T) v = make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  // this wave's tiles: e0 + wave, e0 + wave + 8, ...
+  int e = e0 + wave;
+  uint32_t vm_next = 0;
+  TilePrep<D> tp;
+  if (e < e1) {
+    mha_prepare<D, DENSE>(p, e, n_list, sel_row, lane, tp, bad);
+    vm_next = mha_issue<D, PAGED>(p, rows, b, h, e, tp, slot, lane, bad);
+  }
+  const int swz_k = swz(ql) & (PROW - 1);
+  for (; e < e1; e += kMhaWaves) {
+    const uint32_t vm = vm_next;
+    const bool more = e + kMhaWaves < e1;
+    if (more) mha_prepare<D, DENSE>(p, e + kMhaWaves, n_list, sel_row, lane, tp, bad);
+    // ---- K from LDS into A-operand registers, then S^T = K Q^T: register r holds token
+    //      8*(r/4) + 4*hh + r%4 for query ql (K registers die here) ----
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    {
+      uint4 ka[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = hh * (PROW / 2) + ks;
+        ka[ks] = *reinterpret_cast<const uint4*>(slot + ql * D + ((c ^ swz_k) * 8));
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc = mfma32(as_bf16x8(ka[ks]), qf[ks], sacc);
+    }
+    // ---- V from LDS, read transposed into the A operand of O^T = V^T P^T.  MFMA dt covers
+    //      d = 64*(dt/2) + 2*i + (dt%2), i = 0..31, so one 32-bit read (columns 2i, 2i+1) feeds the
+    //      operands of MFMAs 2p and 2p+1 at once ----
+    uint4 va[2][DT];
+#pragma unroll
+    for (int kl = 0; kl < 2; ++kl) {
+      const int r0 = 16 * kl + 4 * hh;
+#pragma unroll
+      for (int pp = 0; pp < DT / 2; ++pp) {
+        const int d = 64 * pp + 2 * ql;
+        const int cd = d >> 3, dd = d & 7;
+        const uint16_t* vbase = slot + S::HALF;
+        uint32_t w[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int row = r0 + (x < 4 ? x : x + 4);
+          w[x] = *reinterpret_cast<const uint32_t*>(vbase + row * D + ((cd ^ (swz(row) & (PROW - 1))) * 8) + dd);
+        }
+        va[kl][2 * pp] = make_uint4((w[0] & 0xFFFFu) | (w[1] << 16), (w[2] & 0xFFFFu) | (w[3] << 16),
+                                    (w[4] & 0xFFFFu) | (w[5] << 16), (w[6] & 0xFFFFu) | (w[7] << 16));
+        va[kl][2 * pp + 1] = make_uint4((w[0] >> 16) | (w[1] & 0xFFFF0000u), (w[2] >> 16) | (w[3] & 0xFFFF0000u),
+                                        (w[4] >> 16) | (w[5] & 0xFFFF0000u), (w[6] >> 16) | (w[7] & 0xFFFF0000u));
+      }
+    }
+    wait_lgkm0();
+    // ---- fetch the next tile into the same slot; it flies while this one is finished ----
+    if (more) vm_next = mha_issue<D, PAGED>(p, rows, b, h, e + kMhaWaves, tp, slot, lane, bad);
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+      float x = sacc[r] * p.scale_log2;
+      x = ((vm >> row) & 1u) ? x : -__builtin_inff();
+      sacc[r] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new != -__builtin_inff()) {
+      const float alpha = exp2f(m_run - m_new);
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = exp2f(sacc[r] - m_new);
+        sacc[r] = pr;
+        rs += pr;
+      }
+      rs += wave_shfl_xor(rs, 32);
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      // ---- O^T += V^T P^T over 2 k-steps of 16 tokens ----
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {
+        uint4 pb;
+        pb.x = pack_bf16x2(sacc[8 * kl + 0], sacc[8 * kl + 1]);
+        pb.y = pack_bf16x2(sacc[8 * kl + 2], sacc[8 * kl + 3]);
+        pb.z = pack_bf16x2(sacc[8 * kl + 4], sacc[8 * kl + 5]);
+        pb.w = pack_bf16x2(sacc[8 * kl + 6], sacc[8 * kl + 7]);
+        const bf16x8 bfr = as_bf16x8(pb);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(as_bf16x8(va[kl][dt]), bfr, oacc[dt]);
+      }
+    }
+  }
+  latch_bad(p.status, bad);
+
+  // ---- merge the 8 waves through LDS (every fetch has been consumed: the tiles are free) ----
+  // d-major [wave][D][32] so that a wave's 32 lanes (queries) store to consecutive words.
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(lds);
+  static_assert(kMhaWaves * 32 * D * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * S::SLOT,
+                "merge buffer must fit in the tile slots");
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int di = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int d = 64 * (dt >> 1) + 2 * di + (dt & 1);
+      mo[(wave * D + d) * 32 + ql] = oacc[dt][r];
+    }
+  if (hh == 0) s_ml[wave][ql] = make_float2(m_run, l_run);
+  __syncthreads();
+  // thread -> (dimension d, 4 queries q0..q0+3); partials are stored d-major as well
+  constexpr int ITEMS = D * 8;
+  float* po_base = p.part_o;
+  float2* pml_base = p.part_ml;
+  for (int it = tid; it < ITEMS; it += NT) {
+    const int d = it >> 3;
+    const int q0 = (it & 7) * 4;
+    float M[4], Ls[4], O[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      M[i] = -__builtin_inff();
+#pragma unroll
+      for (int w = 0; w < kMhaWaves; ++w) M[i] = fmaxf(M[i], s_ml[w][q0 + i].x);
+      Ls[i] = 0.f;
+      O[i] = 0.f;
+    }
+#pragma unroll
+    for (int w = 0; w < kMhaWaves; ++w) {
+      const float4 src = *reinterpret_cast<const float4*>(mo + (w * D + d) * 32 + q0);
+      const float sv[4] = {src.x, src.y, src.z, src.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 ml = s_ml[w][q0 + i];
+        if (ml.y == 0.f) continue;
+        const float wgt = exp2f(ml.x - M[i]);
+        Ls[i] += ml.y * wgt;
+        O[i] += sv[i] * wgt;
+      }
+    }
+    if (NS == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (q0 + i < p.T) p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(O[i] / Ls[i]);
+    } else {
+      *reinterpret_cast<float4*>(po_base + ((seg * NS + s) * D + d) * 32 + q0) =
+          make_float4(O[0], O[1], O[2], O[3]);
+      if (d == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pml_base[(seg * NS + s) * 32 + q0 + i] = make_float2(M[i], Ls[i]);
+    }
+  }
+}
+
+// Merge the per-split partials (max, sum, O) of every head into the bf16 output.  Separate kernel:
+// the kernel boundary makes the partials visible without a device-wide cache flush, which an
+// in-kernel "last workgroup merges" handoff would need on a multi-die GPU.
+// grid (B*H, 4): each workgroup merges 8 queries of one head.
+template <int D, bool DMAJOR>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float2* __restrict__ part_ml,
+                                                           uint16_t* __restrict__ out, int NS, int T) {
+  const int64_t seg = blockIdx.x;
+  const int qb = blockIdx.y * 8;
+  for (int it = threadIdx.x; it < 8 * D; it += 256) {
+    const int q = qb + it / D;
+    const int d = it % D;
+    if (q >= T) continue;
+    const float2* ml = part_ml + seg * NS * 32 + q;
+    float M = -__builtin_inff();
+    for (int t = 0; t < NS; ++t) M = fmaxf(M, ml[t * 32].x);
+    float Ls = 0.f, O = 0.f;
+    for (int t = 0; t < NS; ++t) {
+      const float2 v = ml[t * 32];
+      const float o = DMAJOR ? part_o[((seg * NS + t) * D + d) * 32 + q]
+                             : part_o[((seg * NS + t) * 32 + q) * D + d];
+      if (v.y == 0.f) continue;
+      const float wgt = exp2f(v.x - M);
+      Ls += v.y * wgt;
+      O += o * wgt;
+    }
+    out[(seg * T + q) * D + d] = (uint16_t)f32_to_bf16_bits(O / Ls);
+  }
+}
+
+hipError_t launch_attn_combine(hipStream_t st, const float* part_o, const float2* part_ml, void* out,
+                               int n_segs, int NS, int T, int D, bool dmajor) {
+  dim3 grid(n_segs, (T + 7) / 8);
+  uint16_t* o = static_cast<uint16_t*>(out);
+  if (D == 128) {
+    if (dmajor) hipLaunchKernelGGL((attn_combine_kernel<128, true>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
+    else hipLaunchKernelGGL((attn_combine_kernel<128, false>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
+  } else {
+    if (dmajor) hipLaunchKernelGGL((attn_combine_kernel<64, true>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
+    else hipLaunchKernelGGL((attn_combine_kernel<64, false>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
+  }
+  return hipGetLastError();
+}
+
+int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus) {
+  const long long tiles = 1 + (max_list_tokens + kTileTok - 1) / kTileTok;
+  const long long segs = (long long)g.B * g.Hkv;
+  long long s = (num_cus + segs - 1) / segs;   // one 8-wave workgroup per CU
+  const long long per_wave_min = 1;
+  if (s * kMhaWaves * per_wave_min > tiles) s = (tiles + kMhaWaves - 1) / kMhaWaves;
+  if (s < 1) s = 1;
+  if (segs > kMaxTickets) s = 1;
+  return (int)s;
+}
+
+template <int D>
+static hipError_t launch_mha_d(hipStream_t st, const MhaParams& p, dim3 grid, bool dense, bool paged) {
+  const dim3 block(kMhaWaves * 64);
+  if (dense) {
+    if (paged) hipLaunchKernelGGL((attn_mha_kernel<D, true, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((attn_mha_kernel<D, true, false>), grid, block, 0, st, p);
+  } else {
+    if (paged) hipLaunchKernelGGL((attn_mha_kernel<D, false, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((attn_mha_kernel<D, false, false>), grid, block, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const void* k, const void* v,
+                           const void* k_dec, const void* v_dec, const int32_t* page_table,
+                           const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
+                           int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
+                           uint32_t* status) {
+  MhaParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.k_dec = static_cast<const uint16_t*>(k_dec);
+  p.v_dec = static_cast<const uint16_t*>(v_dec);
+  p.sel_idx = sel_idx;
+  p.n_sel = n_sel;
+  p.out = static_cast<uint16_t*>(out);
+  const size_t per = (size_t)g.B * g.Hq * n_splits * 32;
+  p.part_o = reinterpret_cast<float*>(scratch);
+  p.part_ml = reinterpret_cast<float2*>(scratch + per * g.D * sizeof(float));
+  (void)tickets;
+  p.status = status;
+  p.page_table = page_table;
+  p.H = g.Hq;
+  p.T = g.T;
+  p.L = g.L;
+  p.max_sel = max_sel;
+  p.unit_log2 = unit_log2;
+  p.n_units = (g.L + (1 << unit_log2) - 1) >> unit_log2;
+  p.n_splits = n_splits;
+  p.page_log2 = g.page_log2;
+  p.pages_per_seq = g.pps;
+  p.n_pages = g.n_pages;
+  p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
+  dim3 grid(n_splits, g.Hq, g.B);
+  hipError_t err = g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0)
+                              : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0);
+  if (err != hipSuccess || n_splits == 1) return err;
+  return launch_attn_combine(st, p.part_o, p.part_ml, out, g.B * g.Hq, n_splits, g.T, g.D, true);
+}
+
+}  // namespace fdl

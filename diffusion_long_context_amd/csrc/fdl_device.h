@@ -60,28 +60,34 @@ __device__ __forceinline__ void latch(uint32_t* status, uint32_t bit) {
   atomicOr(status, bit);
 }
 
-// Address of row (b, g, token) of a KV cache, contiguous [B][Hkv][L][D] or paged
-// [n_pages][Hkv][page_tokens][D].  Returns false (and latches ST_BAD_INDEX) for a bad page id.
-struct KvLayout {
+// Element offset of row (b, g, t), 0 <= t < L, of a KV cache: contiguous [B][Hkv][L][D] or paged
+// [n_pages][Hkv][page_tokens][D] through page_table [B][pages_per_seq].  Branch-free: a bad page id
+// sets `bad` and the row of page 0 is addressed instead, so every returned offset is dereferenceable
+// and the caller can issue its loads unconditionally (a load inside a divergent branch whose value
+// is used after the branch costs a full memory round trip per load).
+template <bool PAGED>
+struct KvRows {
   int32_t Hkv, L, D;
-  int32_t paged, page_log2, pages_per_seq, n_pages;
+  int32_t page_log2, pages_per_seq, n_pages;
   const int32_t* page_table;
 
-  __device__ __forceinline__ bool row_offset(int b, int g, int t, int64_t& off,
-                                             uint32_t* status) const {
-    if (!paged) {
-      off = ((int64_t)(b * Hkv + g) * L + t) * D;
-      return true;
+  __device__ __forceinline__ int64_t off(int b, int g, int t, bool& bad) const {
+    if constexpr (!PAGED) {
+      return ((int64_t)(b * Hkv + g) * L + t) * D;
+    } else {
+      const int pp = page_table[(int64_t)b * pages_per_seq + (t >> page_log2)];
+      const bool good = (unsigned)pp < (unsigned)n_pages;
+      bad = bad || !good;
+      const int64_t pg = good ? pp : 0;
+      return (((pg * Hkv + g) << page_log2) | (int64_t)(t & ((1 << page_log2) - 1))) * (int64_t)D;
     }
-    int lp = t >> page_log2;
-    int pp = page_table[(int64_t)b * pages_per_seq + lp];
-    if ((unsigned)pp >= (unsigned)n_pages) {
-      latch(status, ST_BAD_INDEX);
-      return false;
-    }
-    off = (((int64_t)pp * Hkv + g) << page_log2 | (t & ((1 << page_log2) - 1))) * (int64_t)D;
-    return true;
   }
 };
+
+// Latch ST_BAD_INDEX once per wave if any lane saw a bad index.
+__device__ __forceinline__ void latch_bad(uint32_t* status, bool bad) {
+  const uint64_t m = __ballot(bad);
+  if (m && (threadIdx.x & 63) == (unsigned)(__ffsll((unsigned long long)m) - 1)) latch(status, ST_BAD_INDEX);
+}
 
 }  // namespace fdl

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/libfdllm.h"
 
 struct fdl_ctx {
@@ -19,6 +21,16 @@ struct fdl_ctx {
   char* scratch;         // general scratch after the fixed header
   size_t scratch_bytes;
   char last_error[256];
+  // optional event timing (fdl_profile_begin / fdl_profile_end)
+  struct ProfRec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  bool prof_on = false;
+  uint32_t prof_mask = 0;
+  size_t prof_used = 0;
+  std::vector<hipEvent_t> prof_pool;
+  std::vector<ProfRec> prof_recs;
 };
 
 namespace fdl {
@@ -70,6 +82,17 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
                        const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                        int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
                        uint32_t* status);
+
+// One query head per KV head (bf16): the LDS-DMA streaming kernel.
+int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus);
+hipError_t launch_attn_mha(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,
+                           const void* k_dec, const void* v_dec, const int32_t* page_table,
+                           const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
+                           int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
+                           uint32_t* status);
+
+hipError_t launch_attn_combine(hipStream_t s, const float* part_o, const float2* part_ml, void* out,
+                               int n_segs, int n_splits, int T, int D, bool dmajor);
 
 hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, size_t n, uint32_t v);
 

@@ -26,33 +26,38 @@ namespace fdl {
 // ------------------------------------------------------------------------------------------------
 
 template <typename KT>
-__device__ __forceinline__ float2 load_pair(const KT* base, int64_t off, int pair);
+__device__ __forceinline__ float2 load_pair(const KT* p);
 
 template <>
-__device__ __forceinline__ float2 load_pair<uint16_t>(const uint16_t* base, int64_t off, int pair) {
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(base + off + 2 * pair);
+__device__ __forceinline__ float2 load_pair<uint16_t>(const uint16_t* p) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
   return make_float2(bf16_bits_to_f32(w & 0xFFFFu), bf16_bits_to_f32(w >> 16));
 }
 
 template <>
-__device__ __forceinline__ float2 load_pair<float>(const float* base, int64_t off, int pair) {
-  return *reinterpret_cast<const float2*>(base + off + 2 * pair);
+__device__ __forceinline__ float2 load_pair<float>(const float* p) {
+  return *reinterpret_cast<const float2*>(p);
 }
 
 __device__ __forceinline__ float2 add2(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 
-// Adjacent-pair tree over LEAVES consecutive tokens starting at t0 (tokens >= L are +0).
-template <typename KT, int LEAVES>
-__device__ __forceinline__ float2 leaf_tree(const KT* k, const KvLayout& lay, int b, int g, int t0,
-                                            int pair, uint32_t* status) {
+// Adjacent-pair tree over LEAVES consecutive tokens starting at t0 (tokens >= L are +0).  Every
+// load is issued before the first add.
+template <typename KT, int LEAVES, bool PAGED>
+__device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRows<PAGED>& rows, int b,
+                                            int g, int t0, int pair, bool& bad) {
   float2 a[LEAVES];
+  int64_t off[LEAVES];
 #pragma unroll
   for (int i = 0; i < LEAVES; ++i) {
     const int t = t0 + i;
-    int64_t off;
-    a[i] = make_float2(0.f, 0.f);
-    if (t < lay.L && lay.row_offset(b, g, t, off, status)) a[i] = load_pair<KT>(k, off, pair);
+    off[i] = rows.off(b, g, t < rows.L ? t : rows.L - 1, bad);
   }
+#pragma unroll
+  for (int i = 0; i < LEAVES; ++i) a[i] = load_pair<KT>(k + off[i] + 2 * pair);
+#pragma unroll
+  for (int i = 0; i < LEAVES; ++i)
+    if (t0 + i >= rows.L) a[i] = make_float2(0.f, 0.f);
 #pragma unroll
   for (int w = LEAVES / 2; w >= 1; w /= 2) {
 #pragma unroll
@@ -62,8 +67,8 @@ __device__ __forceinline__ float2 leaf_tree(const KT* k, const KvLayout& lay, in
 }
 
 // One "team" of D/2 threads per unit; thread `pair` owns dimensions 2*pair and 2*pair+1.
-template <typename KT, int D, int LEAVES>
-__global__ __launch_bounds__(256) void pool_keys_kernel(const KT* __restrict__ k, KvLayout lay,
+template <typename KT, int D, int LEAVES, bool PAGED>
+__global__ __launch_bounds__(256) void pool_keys_kernel(const KT* __restrict__ k, KvRows<PAGED> rows,
                                                         int unit_log2, int n_units,
                                                         float* __restrict__ ks,
                                                         uint32_t* __restrict__ status) {
@@ -73,34 +78,53 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const KT* __restrict__ k
   const int team = threadIdx.x / kTeam;
   const int pair = threadIdx.x % kTeam;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int n = blockIdx.x * kTeams + team;
-  if (n >= n_units) return;
+  const int n_raw = blockIdx.x * kTeams + team;
+  const bool live = n_raw < n_units;
+  const int n = live ? n_raw : n_units - 1;
   const int unit = 1 << unit_log2;
   const int t_unit = n << unit_log2;
+  bool bad = false;
   float2 r;
   if (unit <= LEAVES) {
-    r = leaf_tree<KT, LEAVES>(k, lay, b, g, t_unit, pair, status);
+    r = leaf_tree<KT, LEAVES, PAGED>(k, rows, b, g, t_unit, pair, bad);
   } else {
     const int n_sub = unit / LEAVES;
     float2* mine = sub_sums + (size_t)team * n_sub * kTeam;
-    for (int s = 0; s < n_sub; ++s)
-      mine[s * kTeam + pair] = leaf_tree<KT, LEAVES>(k, lay, b, g, t_unit + s * LEAVES, pair, status);
+    for (int sb = 0; sb < n_sub; ++sb)
+      mine[sb * kTeam + pair] = leaf_tree<KT, LEAVES, PAGED>(k, rows, b, g, t_unit + sb * LEAVES, pair, bad);
     // tree over the sub-unit sums; each thread only touches its own column, so no barrier
     for (int w = n_sub / 2; w >= 1; w /= 2)
       for (int i = 0; i < w; ++i)
         mine[i * kTeam + pair] = add2(mine[(2 * i) * kTeam + pair], mine[(2 * i + 1) * kTeam + pair]);
     r = mine[pair];
   }
-  float* dst = ks + (((int64_t)b * lay.Hkv + g) * n_units + n) * D;
-  *reinterpret_cast<float2*>(dst + 2 * pair) = r;
+  if (live) {
+    float* dst = ks + (((int64_t)b * rows.Hkv + g) * n_units + n) * D;
+    *reinterpret_cast<float2*>(dst + 2 * pair) = r;
+  }
+  latch_bad(status, bad);
 }
 
-template <typename KT, int D>
-static hipError_t pool_dispatch(hipStream_t s, const Geom& g, const KT* k, const KvLayout& lay,
+template <bool PAGED>
+static KvRows<PAGED> make_rows(const Geom& g, const int32_t* page_table) {
+  KvRows<PAGED> r;
+  r.Hkv = g.Hkv;
+  r.L = g.L;
+  r.D = g.D;
+  r.page_log2 = g.page_log2;
+  r.pages_per_seq = g.pps;
+  r.n_pages = g.n_pages;
+  r.page_table = page_table;
+  return r;
+}
+
+template <typename KT, int D, bool PAGED>
+static hipError_t pool_dispatch(hipStream_t s, const Geom& g, const KT* k, const int32_t* page_table,
                                 int unit_log2, float* ks, uint32_t* status) {
   const int unit = 1 << unit_log2;
   const int n_units = (g.L + unit - 1) / unit;
   if (n_units == 0) return hipSuccess;
+  const KvRows<PAGED> rows = make_rows<PAGED>(g, page_table);
   constexpr int kTeams = 256 / (D / 2);
   dim3 grid((n_units + kTeams - 1) / kTeams, g.Hkv, g.B);
   size_t lds = 0;
@@ -108,60 +132,58 @@ static hipError_t pool_dispatch(hipStream_t s, const Geom& g, const KT* k, const
   switch (unit_log2) {
 #define FDL_POOL_CASE(LG)                                                                          \
   case LG:                                                                                         \
-    hipLaunchKernelGGL((pool_keys_kernel<KT, D, (1 << LG)>), grid, dim3(256), lds, s, k, lay,     \
-                       unit_log2, n_units, ks, status);                                            \
+    hipLaunchKernelGGL((pool_keys_kernel<KT, D, (1 << LG), PAGED>), grid, dim3(256), lds, s, k,   \
+                       rows, unit_log2, n_units, ks, status);                                      \
     break;
     FDL_POOL_CASE(0) FDL_POOL_CASE(1) FDL_POOL_CASE(2) FDL_POOL_CASE(3) FDL_POOL_CASE(4)
     FDL_POOL_CASE(5)
 #undef FDL_POOL_CASE
-    default:
-      hipLaunchKernelGGL((pool_keys_kernel<KT, D, 64>), grid, dim3(256), lds, s, k, lay, unit_log2,
-                         n_units, ks, status);
+    default: {
+      auto kern = pool_keys_kernel<KT, D, 64, PAGED>;
+      if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, k, rows, unit_log2, n_units, ks, status);
+    }
   }
   return hipGetLastError();
 }
 
-static KvLayout make_layout(const Geom& g, const int32_t* page_table) {
-  KvLayout lay;
-  lay.Hkv = g.Hkv;
-  lay.L = g.L;
-  lay.D = g.D;
-  lay.paged = g.paged;
-  lay.page_log2 = g.page_log2;
-  lay.pages_per_seq = g.pps;
-  lay.n_pages = g.n_pages;
-  lay.page_table = page_table;
-  return lay;
-}
-
 hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const int32_t* page_table,
                             int unit_log2, float* ks, uint32_t* status) {
-  const KvLayout lay = make_layout(g, page_table);
   if (g.dtype == FDL_BF16) {
     const uint16_t* kk = static_cast<const uint16_t*>(k);
-    return g.D == 128 ? pool_dispatch<uint16_t, 128>(s, g, kk, lay, unit_log2, ks, status)
-                      : pool_dispatch<uint16_t, 64>(s, g, kk, lay, unit_log2, ks, status);
+    if (g.paged)
+      return g.D == 128 ? pool_dispatch<uint16_t, 128, true>(s, g, kk, page_table, unit_log2, ks, status)
+                        : pool_dispatch<uint16_t, 64, true>(s, g, kk, page_table, unit_log2, ks, status);
+    return g.D == 128 ? pool_dispatch<uint16_t, 128, false>(s, g, kk, page_table, unit_log2, ks, status)
+                      : pool_dispatch<uint16_t, 64, false>(s, g, kk, page_table, unit_log2, ks, status);
   }
   const float* kk = static_cast<const float*>(k);
-  return g.D == 128 ? pool_dispatch<float, 128>(s, g, kk, lay, unit_log2, ks, status)
-                    : pool_dispatch<float, 64>(s, g, kk, lay, unit_log2, ks, status);
+  if (g.paged)
+    return g.D == 128 ? pool_dispatch<float, 128, true>(s, g, kk, page_table, unit_log2, ks, status)
+                      : pool_dispatch<float, 64, true>(s, g, kk, page_table, unit_log2, ks, status);
+  return g.D == 128 ? pool_dispatch<float, 128, false>(s, g, kk, page_table, unit_log2, ks, status)
+                    : pool_dispatch<float, 64, false>(s, g, kk, page_table, unit_log2, ks, status);
 }
 
 // ------------------------------------------------------------------------------------------------
 // Predicted-query sum: qs[d] = tree over the group's heads (padded to 2^m) of the tree over the T
 // slots (padded to 2^m; non-predicted slots +0) of q[b][h][p][d].  Computed by threads d < D of the
-// block into LDS.
+// block into LDS; every q load is issued before the first add.
 // ------------------------------------------------------------------------------------------------
 
 template <typename QT>
-__device__ __forceinline__ float load_q(const QT* q, int64_t i);
+__device__ __forceinline__ float load_q(const QT* q);
 template <>
-__device__ __forceinline__ float load_q<uint16_t>(const uint16_t* q, int64_t i) {
-  return bf16_bits_to_f32(q[i]);
+__device__ __forceinline__ float load_q<uint16_t>(const uint16_t* q) {
+  return bf16_bits_to_f32(*q);
 }
 template <>
-__device__ __forceinline__ float load_q<float>(const float* q, int64_t i) {
-  return q[i];
+__device__ __forceinline__ float load_q<float>(const float* q) {
+  return *q;
 }
 
 __device__ __forceinline__ int pow2_ceil(int x) {
@@ -170,29 +192,31 @@ __device__ __forceinline__ int pow2_ceil(int x) {
   return p;
 }
 
-template <typename QT, int D>
-__device__ void query_sum_to_lds(const QT* __restrict__ q, uint64_t pred, int b, int g, int Hq,
-                                 int G, int T, float* qs_lds) {
+// TMAX: 32 or 64, a compile-time bound on T.
+template <typename QT, int D, int TMAX>
+__device__ __forceinline__ void query_sum_to_lds(const QT* __restrict__ q, uint64_t pred, int b, int g,
+                                                 int Hq, int G, int T, float* qs_lds) {
   const int d = threadIdx.x;
   if (d >= D) return;
   const int T2 = pow2_ceil(T);
   const int G2 = pow2_ceil(G);
   float hv[8];
-#pragma unroll
   for (int j = 0; j < 8; ++j) {
     hv[j] = 0.f;
-    if (j < G) {
+    if (j < G) {   // uniform
       const int h = g * G + j;
       const QT* qh = q + ((int64_t)b * Hq + h) * T * D + d;
-      float a[64];
+      float a[TMAX];
 #pragma unroll
-      for (int p = 0; p < 64; ++p)
-        a[p] = (p < T && ((pred >> p) & 1ull)) ? load_q<QT>(qh, (int64_t)p * D) : 0.f;
+      for (int p = 0; p < TMAX; ++p) a[p] = load_q<QT>(qh + (int64_t)(p < T ? p : T - 1) * D);
+#pragma unroll
+      for (int p = 0; p < TMAX; ++p)
+        if (!(p < T && ((pred >> p) & 1ull))) a[p] = 0.f;
 #pragma unroll
       for (int lvl = 0; lvl < 6; ++lvl) {
-        if ((1 << lvl) < T2) {
+        if ((TMAX >> (lvl + 1)) >= 1 && (1 << lvl) < T2) {
 #pragma unroll
-          for (int i = 0; i < (32 >> lvl); ++i) a[i] = a[2 * i] + a[2 * i + 1];
+          for (int i = 0; i < (TMAX >> (lvl + 1)); ++i) a[i] = a[2 * i] + a[2 * i + 1];
         }
       }
       hv[j] = a[0];
@@ -226,91 +250,6 @@ __device__ __forceinline__ float row_dot(const float (&x)[16], const float (&qv)
   return s;
 }
 
-// ------------------------------------------------------------------------------------------------
-// Level-1 unit scores from pooled keys: scores[b][g][n] = dot(qs, ks[b][g][n])
-// ------------------------------------------------------------------------------------------------
-
-constexpr int kUnitsPerWg = 64;
-constexpr int kScoreRowsPerIter = 2;   // rows per lane in flight
-
-template <typename QT, int D>
-__global__ __launch_bounds__(256) void score_units_kernel(const QT* __restrict__ q,
-                                                          const uint64_t* __restrict__ pred_mask,
-                                                          const float* __restrict__ ks, int Hq,
-                                                          int Hkv, int G, int T, int n_units,
-                                                          float* __restrict__ scores) {
-  constexpr int LPR = D / 16;            // lanes per row
-  constexpr int kRowsPerWave = 64 / LPR;
-  constexpr int kRowsPerPass = 4 * kRowsPerWave;
-  __shared__ float qs[D];
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane % LPR;
-  const int n0 = blockIdx.x * kUnitsPerWg;
-  const float* ksg = ks + ((int64_t)b * Hkv + g) * n_units * D;
-
-  // issue this lane's row loads before the query sum, so they are in flight meanwhile
-  constexpr int kPasses = kUnitsPerWg / kRowsPerPass;
-  float x[kPasses][16];
-#pragma unroll
-  for (int ps = 0; ps < kPasses; ++ps) {
-    const int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
-    if (n < n_units) {
-      const float4* src = reinterpret_cast<const float4*>(ksg + (int64_t)n * D + 16 * j);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 v = src[c];
-        x[ps][4 * c + 0] = v.x;
-        x[ps][4 * c + 1] = v.y;
-        x[ps][4 * c + 2] = v.z;
-        x[ps][4 * c + 3] = v.w;
-      }
-    }
-  }
-  query_sum_to_lds<QT, D>(q, pred_mask[b], b, g, Hq, G, T, qs);
-  __syncthreads();
-  float qv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
-#pragma unroll
-  for (int ps = 0; ps < kPasses; ++ps) {
-    const int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
-    const float sc = row_dot<LPR>(x[ps], qv);
-    if (n < n_units && j == 0) scores[((int64_t)b * Hkv + g) * n_units + n] = sc;
-  }
-}
-
-hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
-                              const float* ks, int n_units, float* scores) {
-  if (n_units == 0) return hipSuccess;
-  dim3 grid((n_units + kUnitsPerWg - 1) / kUnitsPerWg, g.Hkv, g.B);
-  if (g.dtype == FDL_BF16) {
-    const uint16_t* qq = static_cast<const uint16_t*>(q);
-    if (g.D == 128)
-      hipLaunchKernelGGL((score_units_kernel<uint16_t, 128>), grid, dim3(256), 0, s, qq, pred_mask,
-                         ks, g.Hq, g.Hkv, g.G, g.T, n_units, scores);
-    else
-      hipLaunchKernelGGL((score_units_kernel<uint16_t, 64>), grid, dim3(256), 0, s, qq, pred_mask,
-                         ks, g.Hq, g.Hkv, g.G, g.T, n_units, scores);
-  } else {
-    const float* qq = static_cast<const float*>(q);
-    if (g.D == 128)
-      hipLaunchKernelGGL((score_units_kernel<float, 128>), grid, dim3(256), 0, s, qq, pred_mask, ks,
-                         g.Hq, g.Hkv, g.G, g.T, n_units, scores);
-    else
-      hipLaunchKernelGGL((score_units_kernel<float, 64>), grid, dim3(256), 0, s, qq, pred_mask, ks,
-                         g.Hq, g.Hkv, g.G, g.T, n_units, scores);
-  }
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------------------------
-// Level-2 token scores inside candidate units (chunks), keys read through the page table:
-// scores[b][g][c][i] = dot(qs, k[token = cand_idx[b][g][c] * unit + i])
-// ------------------------------------------------------------------------------------------------
-
-constexpr int kTokensPerWg = 256;
-
 template <typename KT>
 __device__ __forceinline__ void load16(const KT* src, float (&x)[16]);
 
@@ -339,10 +278,88 @@ __device__ __forceinline__ void load16<float>(const float* src, float (&x)[16]) 
   }
 }
 
-template <typename KT, int D>
+// ------------------------------------------------------------------------------------------------
+// Level-1 unit scores from pooled keys: scores[b][g][n] = dot(qs, ks[b][g][n])
+// ------------------------------------------------------------------------------------------------
+
+constexpr int kUnitsPerWg = 64;
+
+template <typename QT, int D, int TMAX>
+__global__ __launch_bounds__(256) void score_units_kernel(const QT* __restrict__ q,
+                                                          const uint64_t* __restrict__ pred_mask,
+                                                          const float* __restrict__ ks, int Hq,
+                                                          int Hkv, int G, int T, int n_units,
+                                                          float* __restrict__ scores) {
+  constexpr int LPR = D / 16;            // lanes per row
+  constexpr int kRowsPerWave = 64 / LPR;
+  constexpr int kRowsPerPass = 4 * kRowsPerWave;
+  constexpr int kPasses = kUnitsPerWg / kRowsPerPass;
+  __shared__ float qs[D];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % LPR;
+  const int n0 = blockIdx.x * kUnitsPerWg;
+  const float* ksg = ks + ((int64_t)b * Hkv + g) * n_units * D;
+
+  // this lane's row loads go out before the query sum, so they are in flight meanwhile
+  float x[kPasses][16];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    n = n < n_units ? n : n_units - 1;
+    load16<float>(ksg + (int64_t)n * D + 16 * j, x[ps]);
+  }
+  query_sum_to_lds<QT, D, TMAX>(q, pred_mask[b], b, g, Hq, G, T, qs);
+  __syncthreads();
+  float qv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    const float sc = row_dot<LPR>(x[ps], qv);
+    if (n < n_units && j == 0) scores[((int64_t)b * Hkv + g) * n_units + n] = sc;
+  }
+}
+
+template <typename QT, int D>
+static void launch_su(hipStream_t s, const Geom& g, const QT* q, const uint64_t* pm, const float* ks,
+                      int n_units, float* scores) {
+  dim3 grid((n_units + kUnitsPerWg - 1) / kUnitsPerWg, g.Hkv, g.B);
+  if (g.T <= 32)
+    hipLaunchKernelGGL((score_units_kernel<QT, D, 32>), grid, dim3(256), 0, s, q, pm, ks, g.Hq, g.Hkv,
+                       g.G, g.T, n_units, scores);
+  else
+    hipLaunchKernelGGL((score_units_kernel<QT, D, 64>), grid, dim3(256), 0, s, q, pm, ks, g.Hq, g.Hkv,
+                       g.G, g.T, n_units, scores);
+}
+
+hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                              const float* ks, int n_units, float* scores) {
+  if (n_units == 0) return hipSuccess;
+  if (g.dtype == FDL_BF16) {
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    if (g.D == 128) launch_su<uint16_t, 128>(s, g, qq, pred_mask, ks, n_units, scores);
+    else launch_su<uint16_t, 64>(s, g, qq, pred_mask, ks, n_units, scores);
+  } else {
+    const float* qq = static_cast<const float*>(q);
+    if (g.D == 128) launch_su<float, 128>(s, g, qq, pred_mask, ks, n_units, scores);
+    else launch_su<float, 64>(s, g, qq, pred_mask, ks, n_units, scores);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
+// Level-2 token scores inside candidate units (chunks), keys read through the page table:
+// scores[b][g][c][i] = dot(qs, k[token = cand_idx[b][g][c] * unit + i])
+// ------------------------------------------------------------------------------------------------
+
+constexpr int kTokensPerWg = 256;
+
+template <typename KT, int D, int TMAX, bool PAGED>
 __global__ __launch_bounds__(256) void score_tokens_kernel(
     const KT* __restrict__ q, const uint64_t* __restrict__ pred_mask, const KT* __restrict__ k,
-    KvLayout lay, int Hq, int G, int T, int unit_log2, const int32_t* __restrict__ cand_idx,
+    KvRows<PAGED> rows, int Hq, int G, int T, int unit_log2, const int32_t* __restrict__ cand_idx,
     int n_cand, float* __restrict__ scores, uint32_t* __restrict__ status) {
   constexpr int LPR = D / 16;
   constexpr int kRowsPerWave = 64 / LPR;
@@ -352,34 +369,39 @@ __global__ __launch_bounds__(256) void score_tokens_kernel(
   const int g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane % LPR;
-  const int unit = 1 << unit_log2;
   const int64_t total = (int64_t)n_cand << unit_log2;
   const int64_t r0 = (int64_t)blockIdx.x * kTokensPerWg;
-  const int n_units = (lay.L + unit - 1) >> unit_log2;
-  const int32_t* cands = cand_idx + ((int64_t)b * lay.Hkv + g) * n_cand;
+  const int n_units = (rows.L + (1 << unit_log2) - 1) >> unit_log2;
+  const int32_t* cands = cand_idx + ((int64_t)b * rows.Hkv + g) * n_cand;
+  bool bad = false;
 
-  float x[kPasses][16];
+  // candidate units -> tokens -> (pages) -> rows, each stage's loads issued together
+  int tok[kPasses];
   bool ok[kPasses];
 #pragma unroll
   for (int ps = 0; ps < kPasses; ++ps) {
-    const int64_t r = r0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
-    ok[ps] = false;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[ps][i] = 0.f;
-    if (r < total) {
-      const int c = (int)(r >> unit_log2);
-      const int u = cands[c];
-      const int t = (u << unit_log2) + (int)(r & (unit - 1));
-      int64_t off;
-      if ((unsigned)u >= (unsigned)n_units) {
-        latch(status, ST_BAD_INDEX);
-      } else if (t < lay.L && lay.row_offset(b, g, t, off, status)) {
-        load16<KT>(k + off + 16 * j, x[ps]);
-        ok[ps] = true;
-      }
-    }
+    int64_t r = r0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    ok[ps] = r < total;
+    r = ok[ps] ? r : 0;
+    const int u = cands[(int)(r >> unit_log2)];
+    const bool uok = (unsigned)u < (unsigned)n_units;
+    bad = bad || (ok[ps] && !uok);
+    int t = uok ? (u << unit_log2) + (int)(r & ((1 << unit_log2) - 1)) : 0;
+    ok[ps] = ok[ps] && uok && t < rows.L;
+    tok[ps] = t < rows.L ? t : 0;
   }
-  query_sum_to_lds<KT, D>(q, pred_mask[b], b, g, Hq, G, T, qs);
+  int64_t off[kPasses];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    bool pbad = false;
+    off[ps] = rows.off(b, g, tok[ps], pbad);
+    ok[ps] = ok[ps] && !pbad;
+    bad = bad || pbad;
+  }
+  float x[kPasses][16];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) load16<KT>(k + off[ps] + 16 * j, x[ps]);
+  query_sum_to_lds<KT, D, TMAX>(q, pred_mask[b], b, g, Hq, G, T, qs);
   __syncthreads();
   float qv[16];
 #pragma unroll
@@ -389,9 +411,32 @@ __global__ __launch_bounds__(256) void score_tokens_kernel(
     const int64_t r = r0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
     const float sc = row_dot<LPR>(x[ps], qv);
     if (r < total && j == 0)
-      scores[((int64_t)b * lay.Hkv + g) * total + r] = ok[ps] ? sc : -__builtin_inff();
+      scores[((int64_t)b * rows.Hkv + g) * total + r] = ok[ps] ? sc : -__builtin_inff();
   }
-  (void)unit;
+  latch_bad(status, bad);
+}
+
+template <typename KT, int D, bool PAGED>
+static void launch_st(hipStream_t s, const Geom& g, const KT* q, const uint64_t* pm, const KT* k,
+                      const int32_t* page_table, int unit_log2, const int32_t* cand_idx, int n_cand,
+                      float* scores, uint32_t* status) {
+  const int64_t total = (int64_t)n_cand << unit_log2;
+  const KvRows<PAGED> rows = make_rows<PAGED>(g, page_table);
+  dim3 grid((unsigned)((total + kTokensPerWg - 1) / kTokensPerWg), g.Hkv, g.B);
+  if (g.T <= 32)
+    hipLaunchKernelGGL((score_tokens_kernel<KT, D, 32, PAGED>), grid, dim3(256), 0, s, q, pm, k, rows, g.Hq,
+                       g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
+  else
+    hipLaunchKernelGGL((score_tokens_kernel<KT, D, 64, PAGED>), grid, dim3(256), 0, s, q, pm, k, rows, g.Hq,
+                       g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
+}
+
+template <typename KT, int D>
+static void launch_st_p(hipStream_t s, const Geom& g, const KT* q, const uint64_t* pm, const KT* k,
+                        const int32_t* pt, int unit_log2, const int32_t* cand_idx, int n_cand,
+                        float* scores, uint32_t* status) {
+  if (g.paged) launch_st<KT, D, true>(s, g, q, pm, k, pt, unit_log2, cand_idx, n_cand, scores, status);
+  else launch_st<KT, D, false>(s, g, q, pm, k, pt, unit_log2, cand_idx, n_cand, scores, status);
 }
 
 hipError_t launch_score_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
@@ -400,26 +445,16 @@ hipError_t launch_score_tokens(hipStream_t s, const Geom& g, const void* q, cons
                                uint32_t* status) {
   const int64_t total = (int64_t)n_cand << unit_log2;
   if (total == 0) return hipSuccess;
-  const KvLayout lay = make_layout(g, page_table);
-  dim3 grid((unsigned)((total + kTokensPerWg - 1) / kTokensPerWg), g.Hkv, g.B);
   if (g.dtype == FDL_BF16) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
-    if (g.D == 128)
-      hipLaunchKernelGGL((score_tokens_kernel<uint16_t, 128>), grid, dim3(256), 0, s, qq, pred_mask,
-                         kk, lay, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
-    else
-      hipLaunchKernelGGL((score_tokens_kernel<uint16_t, 64>), grid, dim3(256), 0, s, qq, pred_mask,
-                         kk, lay, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
+    if (g.D == 128) launch_st_p<uint16_t, 128>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand, scores, status);
+    else launch_st_p<uint16_t, 64>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand, scores, status);
   } else {
     const float* qq = static_cast<const float*>(q);
     const float* kk = static_cast<const float*>(k);
-    if (g.D == 128)
-      hipLaunchKernelGGL((score_tokens_kernel<float, 128>), grid, dim3(256), 0, s, qq, pred_mask, kk,
-                         lay, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
-    else
-      hipLaunchKernelGGL((score_tokens_kernel<float, 64>), grid, dim3(256), 0, s, qq, pred_mask, kk,
-                         lay, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, scores, status);
+    if (g.D == 128) launch_st_p<float, 128>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand, scores, status);
+    else launch_st_p<float, 64>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand, scores, status);
   }
   return hipGetLastError();
 }

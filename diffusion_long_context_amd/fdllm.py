@@ -25,8 +25,13 @@ FDL_F32, FDL_BF16 = 0, 1
 EXPORTED = (
     "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_predict_queries", "fdl_score_blocks",
-    "fdl_select_blocks", "fdl_sparse_attn", "fdl_dense_attn",
+    "fdl_select_blocks", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
+    "fdl_profile_begin", "fdl_profile_end",
 )
+
+FDL_LAYER_DENSE, FDL_LAYER_SOURCE, FDL_LAYER_REUSE = 0, 1, 2
+PROF_KINDS = ("predict", "pool", "score", "sinks", "select", "sparse_attn", "dense_attn",
+              "layer_dense", "layer_source", "layer_reuse")
 
 
 class FdlError(RuntimeError):
@@ -39,6 +44,18 @@ class fdl_geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "ctx_len", "kv_block", "dec_len", "dtype",
         "paged", "page_tokens", "pages_per_seq", "n_pages")]
+
+
+class fdl_layer_io(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("k_dec", ctypes.c_void_p), ("v_dec", ctypes.c_void_p), ("ks", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("mode", ctypes.c_int32)]
+
+
+class fdl_focus_params(ctypes.Structure):
+    _fields_ = [("top_k_pos", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("top_k_blocks", ctypes.c_int32), ("max_sinks", ctypes.c_int32),
+                ("max_sel", ctypes.c_int32), ("sink_tau", ctypes.c_float)]
 
 
 _P = ctypes.c_void_p
@@ -58,6 +75,10 @@ _SIGS = {
                                _P, _P]),
     "fdl_sparse_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
     "fdl_dense_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P]),
+    "fdl_focus_step": (_I, [_P, ctypes.POINTER(fdl_geom), ctypes.POINTER(fdl_focus_params), _P, _P, _I,
+                            ctypes.POINTER(fdl_layer_io), _P, _P, _P, _P, _P, _P, _P]),
+    "fdl_profile_begin": (_I, [_P, _I, ctypes.c_uint32]),
+    "fdl_profile_end": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }
 
 _lib = None
@@ -235,3 +256,51 @@ class Handle:
         self.sync_stream()
         qp, kp, vp, kdp, vdp, ptp, op = self._attn_ptrs(g, q, k_cache, v_cache, k_dec, v_dec, page_table, out)
         self._check(self.lib.fdl_dense_attn(self.h, ctypes.byref(g.c()), qp, kp, vp, kdp, vdp, ptp, op))
+
+    # ---- whole step and timing ------------------------------------------------------------------
+
+    def make_layers(self, g: Geom, layers) -> "ctypes.Array":
+        """layers: list of dicts with q, k_cache, v_cache, k_dec, v_dec, ks (or None), out, mode.
+        Returns a ctypes array that fdl_focus_step can be called with repeatedly."""
+        B, D = g.batch, g.head_dim
+        qbytes = B * g.n_q_heads * g.dec_len * D * g.elem
+        dbytes = B * g.n_kv_heads * g.dec_len * D * g.elem
+        kv = g.kv_elems * g.elem if g.ctx_len > 0 else None
+        n_blk = -(-g.ctx_len // g.kv_block)
+        arr = (fdl_layer_io * len(layers))()
+        for i, L in enumerate(layers):
+            arr[i] = fdl_layer_io(
+                _ptr(L["q"], qbytes, "q"), _ptr(L["k_cache"], kv, "k_cache"), _ptr(L["v_cache"], kv, "v_cache"),
+                _ptr(L["k_dec"], dbytes, "k_dec"), _ptr(L["v_dec"], dbytes, "v_dec"),
+                _ptr(L.get("ks"), 4 * B * g.n_kv_heads * n_blk * D, "ks"), _ptr(L["out"], qbytes, "out"),
+                int(L["mode"]))
+        return arr
+
+    def fdl_focus_step(self, g: Geom, params: fdl_focus_params, prev_conf, masked, layers_arr, pred_mask,
+                       n_pred, scores, sink_pos, n_sinks, sel_idx, n_sel):
+        """One denoising step over len(layers_arr) layers (see make_layers).  Pointers are trusted to
+        have been checked by make_layers / the caller's allocation."""
+        self.sync_stream()
+        B, Hkv = g.batch, g.n_kv_heads
+        n_blk = -(-g.ctx_len // g.kv_block)
+        self._check(self.lib.fdl_focus_step(
+            self.h, ctypes.byref(g.c()), ctypes.byref(params), _ptr(prev_conf, 4 * B * g.dec_len, "prev_conf"),
+            _ptr(masked, B * g.dec_len, "masked"), len(layers_arr), layers_arr,
+            _ptr(pred_mask, 8 * B, "pred_mask"), _ptr(n_pred, 4 * B, "n_pred"),
+            _ptr(scores, 4 * B * Hkv * n_blk, "scores"), _ptr(sink_pos, 4 * B * params.max_sinks, "sink_pos"),
+            _ptr(n_sinks, 4 * B, "n_sinks"), _ptr(sel_idx, 4 * B * Hkv * params.max_sel, "sel_idx"),
+            _ptr(n_sel, 4 * B * Hkv, "n_sel")))
+
+    def fdl_profile_begin(self, max_records: int, kinds=PROF_KINDS):
+        self.sync_stream()
+        mask = 0
+        for k in kinds:
+            mask |= 1 << PROF_KINDS.index(k)
+        self._check(self.lib.fdl_profile_begin(self.h, max_records, mask))
+
+    def fdl_profile_end(self) -> dict:
+        self.sync_stream()
+        tot = (ctypes.c_double * len(PROF_KINDS))()
+        cnt = (ctypes.c_int64 * len(PROF_KINDS))()
+        self._check(self.lib.fdl_profile_end(self.h, tot, cnt))
+        return {k: (tot[i], cnt[i]) for i, k in enumerate(PROF_KINDS)}

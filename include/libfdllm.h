@@ -191,6 +191,68 @@ fdl_status fdl_dense_attn(fdl_handle h, const fdl_geom* g, const void* q, const 
                           const void* v_cache, const void* k_dec, const void* v_dec,
                           const int32_t* page_table, void* out);
 
+
+/* ---- a whole denoising step over a stack of layers ------------------------------------------ */
+
+/* [FS]: shallow layers keep full attention; one source layer finds the sinks that deeper layers
+ * reuse.  fdl_focus_step runs one denoising step over `n_layers` layers with a single host call:
+ * fdl_predict_queries once, then per layer, by mode,
+ *   FDL_LAYER_DENSE : fdl_dense_attn;
+ *   FDL_LAYER_SOURCE: fdl_score_blocks with sink detection, fdl_select_blocks, fdl_sparse_attn;
+ *   FDL_LAYER_REUSE : fdl_score_blocks, fdl_select_blocks with the current sink_pos / n_sinks
+ *                     (those of the last source layer; on entry, whatever they hold), fdl_sparse_attn.
+ * The result is identical to issuing those calls one by one; only launches are issued (no host
+ * synchronisation).  Each layer's KV is contiguous (g->paged == 0), its `ks` is the fdl_pool_keys
+ * output with unit kv_block.  scores [B][Hkv][n_blk], sel_idx [B][Hkv][max_sel] and n_sel [B][Hkv]
+ * are scratch reused layer to layer and hold the last sparse layer's values on return;
+ * pred_mask / n_pred / sink_pos / n_sinks hold the step's.  max_sel must cover
+ * min(n_blk, max_sinks + top_k_blocks). */
+typedef enum { FDL_LAYER_DENSE = 0, FDL_LAYER_SOURCE = 1, FDL_LAYER_REUSE = 2 } fdl_layer_mode;
+
+typedef struct {
+  const void* q;        /* [B][Hq][T][D]   */
+  const void* k_cache;  /* [B][Hkv][L][D]  */
+  const void* v_cache;
+  const void* k_dec;    /* [B][Hkv][T][D]  */
+  const void* v_dec;
+  const float* ks;      /* [B][Hkv][n_blk][D] pooled keys (ignored by dense layers) */
+  void* out;            /* [B][Hq][T][D]   */
+  int32_t mode;         /* fdl_layer_mode  */
+} fdl_layer_io;
+
+typedef struct {
+  int32_t top_k_pos;     /* predictor: positions taken from the previous confidence */
+  int32_t window;        /* predictor: +/- widening                                   */
+  int32_t top_k_blocks;  /* non-sink blocks kept per KV head                          */
+  int32_t max_sinks;     /* capacity of sink_pos                                       */
+  int32_t max_sel;       /* capacity of sel_idx                                        */
+  float sink_tau;        /* sink threshold (> 0)                                       */
+} fdl_focus_params;
+
+fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* g, const fdl_focus_params* p,
+                          const float* prev_conf, const uint8_t* masked, int32_t n_layers,
+                          const fdl_layer_io* layers, uint64_t* pred_mask, int32_t* n_pred,
+                          float* scores, int32_t* sink_pos, int32_t* n_sinks, int32_t* sel_idx,
+                          int32_t* n_sel);
+
+/* ---- timing --------------------------------------------------------------------------------- */
+
+/* Optional per-call timing with HIP events recorded on the handle's stream around every kernel
+ * launch of the kinds below (and around whole layers inside fdl_focus_step) whose bit
+ * (1 << kind) is set in kind_mask.  fdl_profile_begin
+ * creates a pool of 2 * max_records events and clears the records; fdl_profile_end synchronises,
+ * writes the summed duration in microseconds and the launch count of every kind into
+ * total_us[FDL_PROF_KINDS] / counts[FDL_PROF_KINDS] and releases the pool.  Records beyond
+ * max_records are dropped. */
+typedef enum {
+  FDL_PROF_PREDICT = 0, FDL_PROF_POOL, FDL_PROF_SCORE, FDL_PROF_SINKS, FDL_PROF_SELECT,
+  FDL_PROF_SPARSE_ATTN, FDL_PROF_DENSE_ATTN, FDL_PROF_LAYER_DENSE, FDL_PROF_LAYER_SOURCE,
+  FDL_PROF_LAYER_REUSE, FDL_PROF_KINDS
+} fdl_prof_kind;
+
+fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask);
+fdl_status fdl_profile_end(fdl_handle h, double* total_us, int64_t* counts);
+
 #ifdef __cplusplus
 }
 #endif
