@@ -257,7 +257,7 @@ def main():
                    "sink_source_layer": cfg.source_layer, "gen_len": gen_steps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "attn_mfma_kernel<128,1,false> (fdl_sparse_attn)",
+                     "kernel": "attn_mha_kernel<128,false,false> (sparse attention)",
                      "avg_launch_us": sparse_us, "launches": prof_main["sparse_attn"][1],
                      "bytes_per_launch": launch_bytes, "units_per_launch": units,
                      "unit_bytes": unit_bytes},

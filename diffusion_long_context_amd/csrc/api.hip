@@ -161,7 +161,7 @@ int attn_splits(fdl_handle h, const Geom& g, long long list_tokens) {
 fdl_status run_attn(fdl_handle h, const Geom& g, const void* q, const void* k_cache,
                     const void* v_cache, const void* k_dec, const void* v_dec,
                     const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
-                    int max_sel, int unit_log2, int dense, void* out) {
+                    int max_sel, int unit_log2, int dense, void* out, int n_hint = 0) {
   long long list_tokens = g.L;
   if (!dense) {
     list_tokens = (long long)max_sel << unit_log2;
@@ -171,7 +171,7 @@ fdl_status run_attn(fdl_handle h, const Geom& g, const void* q, const void* k_ca
   ProfScope ps(h, dense ? FDL_PROF_DENSE_ATTN : FDL_PROF_SPARSE_ATTN);
   return hip_status(h, fdl::launch_attn(h->stream, g, q, k_cache, v_cache, k_dec, v_dec, page_table,
                                         sel_idx, n_sel, max_sel, unit_log2, dense, out, h->scratch,
-                                        n_splits, h->tickets, h->status),
+                                        n_splits, h->tickets, h->status, n_hint),
                     "attention launch");
 }
 
@@ -471,7 +471,7 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_para
                     fp->top_k_blocks, 0, fp->max_sel, sel_idx, n_sel);
     if (st != FDL_OK) return st;
     st = run_attn(h, g, io.q, io.k_cache, io.v_cache, io.k_dec, io.v_dec, nullptr, sel_idx, n_sel,
-                  fp->max_sel, bt_log2, 0, io.out);
+                  fp->max_sel, bt_log2, 0, io.out, fp->top_k_blocks);
     if (st != FDL_OK) return st;
   }
   return FDL_OK;

@@ -584,7 +584,7 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
                        const void* k_dec, const void* v_dec, const int32_t* page_table,
                        const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                        int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                       uint32_t* status) {
+                       uint32_t* status, int n_hint) {
   const int unit = 1 << unit_log2;
   const int n_units = (g.L + unit - 1) / unit;
   if (g.dtype == FDL_F32) {
@@ -624,7 +624,7 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
   }
   if (g.G == 1)
     return launch_attn_mha(s, g, q, k, v, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel, unit_log2,
-                           dense, out, scratch, n_splits, tickets, status);
+                           dense, out, scratch, n_splits, tickets, status, n_hint);
   AttnParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);

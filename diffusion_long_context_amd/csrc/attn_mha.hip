@@ -19,8 +19,10 @@
 // The compiler places a full vector-memory wait before any LDS read that follows an LDS fetch, which
 // is why the copy-to-registers step comes before the next fetch rather than double-buffering LDS.
 // Softmax statistics stay in the lane that owns the query (S^T puts queries on lanes), so one
-// cross-lane exchange per tile suffices.  At the end the 8 waves merge through LDS; with several
-// workgroups per head the partial (max, sum, O) go to scratch and attn_combine_kernel merges them.
+// cross-lane exchange per tile suffices.  At the end the 8 waves merge through LDS.  With several
+// workgroups (splits) per head, all of them are placed on the same XCD, so their partial
+// (max, sum, O) meet in that XCD's L2: each split stores its partial, waits for the stores to be
+// acknowledged, takes a ticket, and the last one merges -- no device-wide cache writeback.
 #include <type_traits>
 
 #include "fdl_device.h"
@@ -39,9 +41,11 @@ struct MhaParams {
   uint16_t* out;
   float* part_o;     // [B][H][S][D][32] (d-major)
   float2* part_ml;   // [B][H][S][32]
+  uint32_t* tickets;  // one per (b, h); left at zero by every launch
   uint32_t* status;
   const int32_t* page_table;
-  int H, T, L, max_sel, unit_log2, n_units, n_splits;
+  int H, T, L, max_sel, unit_log2, n_units, n_splits, n_segs;
+  int n_hint;   // expected selected units per head (0 = unknown)
   int page_log2, pages_per_seq, n_pages;
   float scale_log2;
 };
@@ -76,65 +80,35 @@ template <bool PAGED>
 using RowOff = typename std::conditional<PAGED, int64_t, int32_t>::type;
 
 // A tile fetch in two steps, so that the selection-index loads of tile i+1 can fly together with
-// the data of tile i: mha_prepare resolves each of the lane's rows to a token (one batch of index
-// loads), mha_issue turns tokens into addresses (one batch of page-table loads when paged) and
-// launches the LDS fetches.
+// the data of tile i: mha_prepare issues the index loads of the lane's rows (clamped, so it needs
+// neither the list length nor any earlier load), mha_issue resolves them to tokens, applies the
+// list length, adds the page-table step when paged, and launches the LDS fetches.
 template <int D>
 struct TilePrep {
-  int t[MhaShape<D>::INSTR];
-  uint32_t okbits;
+  int u[MhaShape<D>::INSTR];
 };
 
 template <int D, bool DENSE>
-__device__ __forceinline__ void mha_prepare(const MhaParams& p, int e, int n_list,
-                                            const int32_t* __restrict__ sel_row, int lane,
-                                            TilePrep<D>& tp, bool& bad) {
+__device__ __forceinline__ void mha_prepare(const MhaParams& p, int e, const int32_t* __restrict__ sel_row,
+                                            int lane, TilePrep<D>& tp) {
   using S = MhaShape<D>;
-  constexpr int NI = S::INSTR;
-  const int rsub = lane / S::PROW;
-  tp.okbits = 0;
-  if (e == 0 || p.L == 0) {   // uniform: the own block (or an empty cache: nothing to fetch)
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int r = j * S::ROWS_PER_INSTR + rsub;
-      const bool ok = (e == 0) && r < p.T;
-      tp.t[j] = (e == 0) ? (r < p.T ? r : p.T - 1) : 0;
-      tp.okbits |= (ok ? 1u : 0u) << j;
-    }
-    return;
-  }
-  bool ok[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int i = (e - 1) * kTileTok + j * S::ROWS_PER_INSTR + rsub;
-    ok[j] = i < n_list;
-    tp.t[j] = ok[j] ? i : 0;
-  }
   if constexpr (!DENSE) {
-    int u[NI];
+    const int rsub = lane / S::PROW;
+    if (e == 0) return;   // uniform: the own block needs no index
 #pragma unroll
-    for (int j = 0; j < NI; ++j) u[j] = sel_row[tp.t[j] >> p.unit_log2];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const bool uok = (unsigned)u[j] < (unsigned)p.n_units;
-      bad = bad || (ok[j] && !uok);
-      ok[j] = ok[j] && uok;
-      tp.t[j] = uok ? (u[j] << p.unit_log2) + (tp.t[j] & ((1 << p.unit_log2) - 1)) : 0;
+    for (int j = 0; j < S::INSTR; ++j) {
+      const int i = (e - 1) * kTileTok + j * S::ROWS_PER_INSTR + rsub;
+      const int si = i >> p.unit_log2;
+      tp.u[j] = sel_row[si < p.max_sel ? si : p.max_sel - 1];
     }
-  }
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    ok[j] = ok[j] && tp.t[j] < p.L;
-    tp.t[j] = tp.t[j] < p.L ? tp.t[j] : 0;
-    tp.okbits |= (ok[j] ? 1u : 0u) << j;
   }
 }
 
 // Launch the LDS fetches of a prepared tile into the wave's slot; returns the 32-bit row mask.
-template <int D, bool PAGED>
+template <int D, bool DENSE, bool PAGED>
 __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<PAGED>& rows, int b, int h,
-                                              int e, const TilePrep<D>& tp, uint16_t* slot, int lane,
-                                              bool& bad) {
+                                              int e, int n_list, const TilePrep<D>& tp, uint16_t* slot,
+                                              int lane, bool& bad) {
   using S = MhaShape<D>;
   constexpr int NI = S::INSTR;
   const int rsub = lane / S::PROW;
@@ -144,39 +118,60 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
   const uint16_t* kb;
   const uint16_t* vb;
   RowOff<PAGED> off[NI];
-  uint32_t okbits = tp.okbits;
+  bool ok[NI];
   if (dec) {
     kb = p.k_dec + head * p.T * D;
     vb = p.v_dec + head * p.T * D;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) off[j] = (RowOff<PAGED>)(tp.t[j] * D);
-  } else if constexpr (PAGED) {
-    kb = p.k;
-    vb = p.v;
-    bool pb[NI];
-#pragma unroll
     for (int j = 0; j < NI; ++j) {
-      pb[j] = false;
-      off[j] = rows.off(b, h, tp.t[j], pb[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const bool okj = (okbits >> j) & 1u;
-      bad = bad || (okj && pb[j]);
-      if (pb[j]) okbits &= ~(1u << j);
+      const int r = j * S::ROWS_PER_INSTR + rsub;
+      ok[j] = (e == 0) && r < p.T;
+      off[j] = (RowOff<PAGED>)(((e == 0) && r < p.T ? r : 0) * D);
     }
   } else {
-    kb = p.k + head * p.L * D;
-    vb = p.v + head * p.L * D;
+    int t[NI];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) off[j] = (RowOff<PAGED>)(tp.t[j] * D);
+    for (int j = 0; j < NI; ++j) {
+      const int i = (e - 1) * kTileTok + j * S::ROWS_PER_INSTR + rsub;
+      ok[j] = i < n_list;
+      t[j] = ok[j] ? i : 0;
+      if constexpr (!DENSE) {
+        const int u = tp.u[j];
+        const bool uok = (unsigned)u < (unsigned)p.n_units;
+        bad = bad || (ok[j] && !uok);
+        ok[j] = ok[j] && uok;
+        t[j] = uok ? (u << p.unit_log2) + (t[j] & ((1 << p.unit_log2) - 1)) : 0;
+      }
+      ok[j] = ok[j] && t[j] < p.L;
+      t[j] = t[j] < p.L ? t[j] : 0;
+    }
+    if constexpr (PAGED) {
+      kb = p.k;
+      vb = p.v;
+      bool pb[NI];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        pb[j] = false;
+        off[j] = rows.off(b, h, t[j], pb[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        bad = bad || (ok[j] && pb[j]);
+        ok[j] = ok[j] && !pb[j];
+      }
+    } else {
+      kb = p.k + head * p.L * D;
+      vb = p.v + head * p.L * D;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) off[j] = (RowOff<PAGED>)(t[j] * D);
+    }
   }
   uint32_t okm = 0;
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int r = j * S::ROWS_PER_INSTR + rsub;
     off[j] += (sc ^ (swz(r) & (S::PROW - 1))) * 8;   // global chunk stored at LDS slot sc of row r
-    const uint64_t bal = __ballot((okbits >> j) & 1u);
+    const uint64_t bal = __ballot(ok[j]);
 #pragma unroll
     for (int q = 0; q < S::ROWS_PER_INSTR; ++q)
       okm |= (uint32_t)((bal >> (q * S::PROW)) & 1ull) << (j * S::ROWS_PER_INSTR + q);
@@ -196,13 +191,19 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   constexpr int NT = kMhaWaves * 64;
   constexpr int KS = S::KS, DT = S::DT, PROW = S::PROW;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kMhaWaves * S::SLOT];
-  __shared__ float2 s_ml[kMhaWaves][32];
 
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Workgroup i runs on XCD i % 8 (the dispatcher's round-robin order).  All splits of one head
+  // are given workgroup ids with the same residue, so they share one L2 and the final merge can
+  // hand partials over through it.
+  const int NS = p.n_splits;
+  const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
+  const int s = xslot % NS;
+  const int seg_i = xcd + 8 * (xslot / NS);
+  if (seg_i >= p.n_segs) return;
+  const int b = seg_i / p.H, h = seg_i % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
-  const int64_t seg = (int64_t)b * p.H + h;
-  const int NS = p.n_splits;
+  const int64_t seg = seg_i;
   KvRows<PAGED> rows;
   rows.Hkv = p.H;
   rows.L = p.L;
@@ -213,20 +214,32 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   rows.page_table = p.page_table;
   bool bad = false;
 
-  int n_list;
-  if (DENSE) {
-    n_list = p.L;
-  } else {
-    int ns = p.n_sel[seg];
-    ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
-    n_list = ns << p.unit_log2;
-  }
-  if (p.L == 0) n_list = 0;
-  const int n_tiles = 1 + (n_list + kTileTok - 1) / kTileTok;
-  const int e0 = (int)((int64_t)n_tiles * s / NS);
-  const int e1 = (int)((int64_t)n_tiles * (s + 1) / NS);
   const int32_t* sel_row = DENSE ? nullptr : p.sel_idx + seg * p.max_sel;
   uint16_t* slot = lds + wave * S::SLOT;
+  // Tile partition.  Dense: the list is the whole cache.  Sparse: when the caller knows the usual
+  // selection size (n_hint units), the split ranges come from it, so the first tile's index loads
+  // can go out together with the read of the actual count; the actual count then trims the ranges
+  // and the last split takes any tiles beyond the hint.
+  int n_part = DENSE ? p.L : (p.n_hint > 0 ? (p.n_hint < p.max_sel ? p.n_hint : p.max_sel) << p.unit_log2 : -1);
+  int ns_raw = 0;
+  if (!DENSE && n_part < 0) ns_raw = p.n_sel[seg];   // no hint: the count comes first
+  if (n_part < 0) n_part = (ns_raw < 0 ? 0 : (ns_raw > p.max_sel ? p.max_sel : ns_raw)) << p.unit_log2;
+  if (p.L == 0) n_part = 0;
+  const int n_tiles_part = 1 + (n_part + kTileTok - 1) / kTileTok;
+  const int e0 = (int)((int64_t)n_tiles_part * s / NS);
+  int e1 = (int)((int64_t)n_tiles_part * (s + 1) / NS);
+  int e = e0 + wave;
+  TilePrep<D> tp;
+  if (e < e1) mha_prepare<D, DENSE>(p, e, sel_row, lane, tp);
+  int n_list = n_part;
+  if (!DENSE && p.n_hint > 0) {
+    int ns = p.n_sel[seg];
+    ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
+    n_list = p.L == 0 ? 0 : ns << p.unit_log2;
+    const int n_tiles = 1 + (n_list + kTileTok - 1) / kTileTok;
+    if (s == NS - 1) e1 = n_tiles;
+    e1 = e1 < n_tiles ? e1 : n_tiles;
+  }
 
   // Q fragments (B operand of S^T = K Q^T): lane (q, hh) holds q[q][hh*D/2 + 8ks .. +8]
   bf16x8 qf[KS];
@@ -248,18 +261,13 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   float m_run = -__builtin_inff(), l_run = 0.f;
 
   // this wave's tiles: e0 + wave, e0 + wave + 8, ...
-  int e = e0 + wave;
   uint32_t vm_next = 0;
-  TilePrep<D> tp;
-  if (e < e1) {
-    mha_prepare<D, DENSE>(p, e, n_list, sel_row, lane, tp, bad);
-    vm_next = mha_issue<D, PAGED>(p, rows, b, h, e, tp, slot, lane, bad);
-  }
+  if (e < e1) vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e, n_list, tp, slot, lane, bad);
   const int swz_k = swz(ql) & (PROW - 1);
   for (; e < e1; e += kMhaWaves) {
     const uint32_t vm = vm_next;
     const bool more = e + kMhaWaves < e1;
-    if (more) mha_prepare<D, DENSE>(p, e + kMhaWaves, n_list, sel_row, lane, tp, bad);
+    if (more) mha_prepare<D, DENSE>(p, e + kMhaWaves, sel_row, lane, tp);
     // ---- K from LDS into A-operand registers, then S^T = K Q^T: register r holds token
     //      8*(r/4) + 4*hh + r%4 for query ql (K registers die here) ----
     f32x16 sacc;
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     }
     wait_lgkm0();
     // ---- fetch the next tile into the same slot; it flies while this one is finished ----
-    if (more) vm_next = mha_issue<D, PAGED>(p, rows, b, h, e + kMhaWaves, tp, slot, lane, bad);
+    if (more) vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e + kMhaWaves, n_list, tp, slot, lane, bad);
     float mx = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -345,10 +353,31 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   }
   latch_bad(p.status, bad);
 
-  // ---- merge the 8 waves through LDS (every fetch has been consumed: the tiles are free) ----
-  // d-major [wave][D][32] so that a wave's 32 lanes (queries) store to consecutive words.
-  __syncthreads();
-  float* mo = reinterpret_cast<float*>(lds);
+  // ---- merge the 8 waves: common max per query, rescale in registers, sum through LDS ----
+  __shared__ float s_m[kMhaWaves][32], s_l[kMhaWaves][32];
+  __shared__ float s_fin[2][32];
+  __shared__ uint32_t s_ticket;
+  if (hh == 0) {
+    s_m[wave][ql] = m_run;
+    s_l[wave][ql] = l_run;
+  }
+  __syncthreads();   // also: every LDS fetch has been consumed, the slots are free
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < kMhaWaves; ++w) M = fmaxf(M, s_m[w][ql]);
+  const bool anyrow = M != -__builtin_inff();
+  const float scale = (anyrow && m_run != -__builtin_inff()) ? exp2f(m_run - M) : 0.f;
+  if (wave == 0 && hh == 0) {
+    float Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMhaWaves; ++w) {
+      const float mw = s_m[w][ql];
+      Ls += (anyrow && mw != -__builtin_inff()) ? s_l[w][ql] * exp2f(mw - M) : 0.f;
+    }
+    s_fin[0][ql] = M;
+    s_fin[1][ql] = Ls;
+  }
+  float* mo = reinterpret_cast<float*>(lds);   // [wave][D][32], d-major
   static_assert(kMhaWaves * 32 * D * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * S::SLOT,
                 "merge buffer must fit in the tile slots");
 #pragma unroll
@@ -357,51 +386,80 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     for (int r = 0; r < 16; ++r) {
       const int di = 8 * (r >> 2) + 4 * hh + (r & 3);
       const int d = 64 * (dt >> 1) + 2 * di + (dt & 1);
-      mo[(wave * D + d) * 32 + ql] = oacc[dt][r];
+      mo[(wave * D + d) * 32 + ql] = oacc[dt][r] * scale;
     }
-  if (hh == 0) s_ml[wave][ql] = make_float2(m_run, l_run);
   __syncthreads();
-  // thread -> (dimension d, 4 queries q0..q0+3); partials are stored d-major as well
-  constexpr int ITEMS = D * 8;
+  // thread -> (d, 8 queries q0..q0+7); 512 threads cover D * 4 items for D = 128 (loop for D = 64)
   float* po_base = p.part_o;
   float2* pml_base = p.part_ml;
-  for (int it = tid; it < ITEMS; it += NT) {
-    const int d = it >> 3;
-    const int q0 = (it & 7) * 4;
-    float M[4], Ls[4], O[4];
+  for (int it = tid; it < D * 4; it += NT) {
+    const int d = it >> 2;
+    const int q0 = (it & 3) * 8;
+    float o[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      M[i] = -__builtin_inff();
-#pragma unroll
-      for (int w = 0; w < kMhaWaves; ++w) M[i] = fmaxf(M[i], s_ml[w][q0 + i].x);
-      Ls[i] = 0.f;
-      O[i] = 0.f;
-    }
+    for (int i = 0; i < 8; ++i) o[i] = 0.f;
 #pragma unroll
     for (int w = 0; w < kMhaWaves; ++w) {
-      const float4 src = *reinterpret_cast<const float4*>(mo + (w * D + d) * 32 + q0);
-      const float sv[4] = {src.x, src.y, src.z, src.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float2 ml = s_ml[w][q0 + i];
-        if (ml.y == 0.f) continue;
-        const float wgt = exp2f(ml.x - M[i]);
-        Ls[i] += ml.y * wgt;
-        O[i] += sv[i] * wgt;
-      }
+      const float4 a = *reinterpret_cast<const float4*>(mo + (w * D + d) * 32 + q0);
+      const float4 c = *reinterpret_cast<const float4*>(mo + (w * D + d) * 32 + q0 + 4);
+      o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
+      o[4] += c.x; o[5] += c.y; o[6] += c.z; o[7] += c.w;
     }
     if (NS == 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (q0 + i < p.T) p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(O[i] / Ls[i]);
+      for (int i = 0; i < 8; ++i)
+        if (q0 + i < p.T) p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(o[i] / s_fin[1][q0 + i]);
     } else {
-      *reinterpret_cast<float4*>(po_base + ((seg * NS + s) * D + d) * 32 + q0) =
-          make_float4(O[0], O[1], O[2], O[3]);
-      if (d == 0)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pml_base[(seg * NS + s) * 32 + q0 + i] = make_float2(M[i], Ls[i]);
+      float* dst = po_base + ((seg * NS + s) * D + d) * 32 + q0;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
     }
   }
+  if (NS == 1) return;
+  if (tid < 32) pml_base[(seg * NS + s) * 32 + tid] = make_float2(s_fin[0][tid], s_fin[1][tid]);
+
+  // ---- same-XCD hand-over: the last split of this head to finish merges all of them.  The
+  //      partials sit in this XCD's L2: wait until our stores are acknowledged by it, take a
+  //      ticket, and the last taker drops its L1 copies before reading the partials back. ----
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg], 1u);
+  __syncthreads();
+  if (s_ticket != (uint32_t)(NS - 1)) return;
+  asm volatile("buffer_inv sc0" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int it = tid; it < D * 4; it += NT) {
+    const int d = it >> 2;
+    const int q0 = (it & 3) * 8;
+    float Mq[8], Lq[8], o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      Mq[i] = -__builtin_inff();
+      Lq[i] = 0.f;
+      o[i] = 0.f;
+    }
+    const float2* ml = pml_base + seg * NS * 32 + q0;
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Mq[i] = fmaxf(Mq[i], ml[t * 32 + i].x);
+    for (int t = 0; t < NS; ++t) {
+      const float* src = po_base + ((seg * NS + t) * D + d) * 32 + q0;
+      const float4 a = *reinterpret_cast<const float4*>(src);
+      const float4 c = *reinterpret_cast<const float4*>(src + 4);
+      const float ov[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float2 v = ml[t * 32 + i];
+        const float wgt = (v.x != -__builtin_inff() && Mq[i] != -__builtin_inff()) ? exp2f(v.x - Mq[i]) : 0.f;
+        Lq[i] += v.y * wgt;
+        o[i] += ov[i] * wgt;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (q0 + i < p.T) p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(o[i] / Lq[i]);
+  }
+  if (tid == 0) p.tickets[seg] = 0u;
 }
 
 // Merge the per-split partials (max, sum, O) of every head into the bf16 output.  Separate kernel:
@@ -477,7 +535,7 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
                            const void* k_dec, const void* v_dec, const int32_t* page_table,
                            const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                            int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                           uint32_t* status) {
+                           uint32_t* status, int n_hint) {
   MhaParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -490,7 +548,7 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
   const size_t per = (size_t)g.B * g.Hq * n_splits * 32;
   p.part_o = reinterpret_cast<float*>(scratch);
   p.part_ml = reinterpret_cast<float2*>(scratch + per * g.D * sizeof(float));
-  (void)tickets;
+  p.tickets = tickets;
   p.status = status;
   p.page_table = page_table;
   p.H = g.Hq;
@@ -504,11 +562,12 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
   p.pages_per_seq = g.pps;
   p.n_pages = g.n_pages;
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
-  dim3 grid(n_splits, g.Hq, g.B);
-  hipError_t err = g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0)
-                              : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0);
-  if (err != hipSuccess || n_splits == 1) return err;
-  return launch_attn_combine(st, p.part_o, p.part_ml, out, g.B * g.Hq, n_splits, g.T, g.D, true);
+  p.n_segs = g.B * g.Hq;
+  p.n_hint = dense ? 0 : n_hint;
+  // 8 XCDs; the splits of head seg run on XCD seg % 8 (see the kernel)
+  dim3 grid(8 * ((p.n_segs + 7) / 8) * n_splits);
+  return g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0)
+                    : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0);
 }
 
 }  // namespace fdl
