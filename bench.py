@@ -15,6 +15,7 @@ single-threaded child process.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import subprocess
@@ -27,6 +28,27 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-attn step us + KV tokens/s at 32K ctx; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
+WORKSPACE_BYTES = 256 << 20   # library workspace of the timed handle (sets the attention split count)
+
+
+# HBM bytes per sparse-attention dispatch, from two rocprofv3 counter runs of this benchmark
+# (FETCH_SIZE, WRITE_SIZE; scaled by a 1 GiB copy in the same runs).  Valid only for the kernel
+# sources they were taken on: the file records their hash.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llada8b_32k_32layer_sparse_attn_traffic.json")
+KERNEL_SOURCES = ("diffusion_long_context_amd/csrc/attn_mha.hip", "diffusion_long_context_amd/csrc/fdl_device.h")
+
+
+def measured_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return d["hbm_bytes_per_dispatch"] if h.hexdigest() == d.get("source_sha256") else None
 
 
 def log(msg: str):
@@ -107,6 +129,8 @@ def main():
     ap.add_argument("--diag-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-child", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the run, one plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.cpu_baseline_child:
@@ -134,7 +158,7 @@ def main():
     NL, B, Hq, Hkv, D, T = cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len
     n_blk = cfg.n_blk
     spb, gen_steps = cfg.steps_per_block, cfg.n_gen_blocks * cfg.steps_per_block
-    h = Handle(workspace_bytes=256 << 20)
+    h = Handle(workspace_bytes=WORKSPACE_BYTES)
     dev = torch.device("cuda")
 
     log(f"drawing {NL} layers of KV cache on device")
@@ -256,7 +280,7 @@ def main():
                    "top_k_blocks": cfg.top_k_blocks, "dense_layers": cfg.dense_layers,
                    "sink_source_layer": cfg.source_layer, "gen_len": gen_steps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
                      "kernel": "attn_mha_kernel<128,false,false> (sparse attention)",
                      "avg_launch_us": sparse_us, "launches": prof_main["sparse_attn"][1],
                      "bytes_per_launch": launch_bytes, "units_per_launch": units,
@@ -273,6 +297,15 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, single thread)")
         result["cpu_baseline"] = cpu_baseline()
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)   # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        log(f"copy calibration: one elementwise kernel read {n} and wrote {n} bytes")
+        del src, dst
     print(json.dumps(result), flush=True)
     h.close()
 

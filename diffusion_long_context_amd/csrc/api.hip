@@ -77,20 +77,26 @@ fdl_status check_geom(fdl_handle h, const fdl_geom* g, Geom& o) {
 }
 
 // Records a pair of events around one launch (or one layer) when profiling is on.
+// Times the launches in its scope when profiling is on for its kind.  Inner mode hands the events to
+// the launcher instead (timer()), which ties them to the kernel's own dispatch timestamps.
 struct ProfScope {
   fdl_handle h;
   int kind;
+  bool inner;
   hipEvent_t a = nullptr, b = nullptr;
-  ProfScope(fdl_handle hh, int k) : h(hh), kind(k) {
+  fdl::KernelTimer kt{};
+  ProfScope(fdl_handle hh, int k, bool inner_ = false) : h(hh), kind(k), inner(inner_) {
     if (h->prof_on && ((h->prof_mask >> k) & 1u) && h->prof_used + 2 <= h->prof_pool.size()) {
       a = h->prof_pool[h->prof_used++];
       b = h->prof_pool[h->prof_used++];
-      (void)hipEventRecord(a, h->stream);
+      kt = {a, b};
+      if (!inner) (void)hipEventRecord(a, h->stream);
     }
   }
+  const fdl::KernelTimer* timer() const { return a ? &kt : nullptr; }
   ~ProfScope() {
     if (a) {
-      (void)hipEventRecord(b, h->stream);
+      if (!inner) (void)hipEventRecord(b, h->stream);
       h->prof_recs.push_back({kind, a, b});
     }
   }
@@ -168,10 +174,10 @@ fdl_status run_attn(fdl_handle h, const Geom& g, const void* q, const void* k_ca
     if (list_tokens > g.L) list_tokens = g.L;
   }
   const int n_splits = attn_splits(h, g, list_tokens);
-  ProfScope ps(h, dense ? FDL_PROF_DENSE_ATTN : FDL_PROF_SPARSE_ATTN);
+  ProfScope ps(h, dense ? FDL_PROF_DENSE_ATTN : FDL_PROF_SPARSE_ATTN, /*inner=*/true);
   return hip_status(h, fdl::launch_attn(h->stream, g, q, k_cache, v_cache, k_dec, v_dec, page_table,
                                         sel_idx, n_sel, max_sel, unit_log2, dense, out, h->scratch,
-                                        n_splits, h->tickets, h->status, n_hint),
+                                        n_splits, h->tickets, h->status, n_hint, ps.timer()),
                     "attention launch");
 }
 

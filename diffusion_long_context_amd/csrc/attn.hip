@@ -580,11 +580,12 @@ static hipError_t launch_mfma_g(hipStream_t s, const AttnParams& p, dim3 grid, i
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,
-                       const void* k_dec, const void* v_dec, const int32_t* page_table,
-                       const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
-                       int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                       uint32_t* status, int n_hint) {
+// fp32 path and grouped-query bf16 path (the one-query-head bf16 path is attn_mha.hip's).
+static hipError_t launch_attn_other(hipStream_t s, const Geom& g, const void* q, const void* k,
+                                    const void* v, const void* k_dec, const void* v_dec,
+                                    const int32_t* page_table, const int32_t* sel_idx,
+                                    const int32_t* n_sel, int max_sel, int unit_log2, int dense, void* out,
+                                    char* scratch, int n_splits, uint32_t* tickets, uint32_t* status) {
   const int unit = 1 << unit_log2;
   const int n_units = (g.L + unit - 1) / unit;
   if (g.dtype == FDL_F32) {
@@ -622,9 +623,6 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
     }
     return hipGetLastError();
   }
-  if (g.G == 1)
-    return launch_attn_mha(s, g, q, k, v, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel, unit_log2,
-                           dense, out, scratch, n_splits, tickets, status, n_hint);
   AttnParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -657,6 +655,22 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
                               : launch_mfma_g<64>(s, p, grid, g.G, dense != 0, g.paged != 0);
   if (err != hipSuccess || n_splits == 1) return err;
   return launch_attn_combine(s, p.part_o, p.part_ml, out, g.B * g.Hq, n_splits, g.T, g.D, false);
+}
+
+hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,
+                       const void* k_dec, const void* v_dec, const int32_t* page_table,
+                       const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
+                       int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
+                       uint32_t* status, int n_hint, const KernelTimer* timer) {
+  if (g.dtype == FDL_BF16 && g.G == 1)
+    return launch_attn_mha(s, g, q, k, v, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel, unit_log2,
+                           dense, out, scratch, n_splits, tickets, status, n_hint, timer);
+  if (timer) (void)hipEventRecord(timer->a, s);
+  const hipError_t err = launch_attn_other(s, g, q, k, v, k_dec, v_dec, page_table, sel_idx, n_sel,
+                                           max_sel, unit_log2, dense, out, scratch, n_splits, tickets,
+                                           status);
+  if (timer) (void)hipEventRecord(timer->b, s);
+  return err;
 }
 
 }  // namespace fdl

@@ -16,13 +16,17 @@
 //      S^T = K Q^T; V read transposed as the A operand of O^T = V^T P^T);
 //   3. it issues the next tile's fetch into the same slot, and only then computes on the registers,
 //      so one tile per wave is always in flight while the MFMAs and the softmax run.
-// The compiler places a full vector-memory wait before any LDS read that follows an LDS fetch, which
-// is why the copy-to-registers step comes before the next fetch rather than double-buffering LDS.
+// An LDS read of the slot must follow a full vector-memory wait (the fetch only counts as done in
+// vmcnt), which would also wait for a second buffer's fetch; hence the copy-to-registers step before
+// the next fetch rather than double-buffering LDS.  The wait is written out at the top of the tile
+// loop: the compiler's automatic one is not placed reliably across the back-edge.
 // Softmax statistics stay in the lane that owns the query (S^T puts queries on lanes), so one
 // cross-lane exchange per tile suffices.  At the end the 8 waves merge through LDS.  With several
 // workgroups (splits) per head, all of them are placed on the same XCD, so their partial
 // (max, sum, O) meet in that XCD's L2: each split stores its partial, waits for the stores to be
 // acknowledged, takes a ticket, and the last one merges -- no device-wide cache writeback.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "fdl_device.h"
@@ -56,6 +60,7 @@ constexpr int kMhaWaves = 8;
 constexpr int kTileTok = 32;
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D>
 struct MhaShape {
@@ -230,7 +235,8 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   int e1 = (int)((int64_t)n_tiles_part * (s + 1) / NS);
   int e = e0 + wave;
   TilePrep<D> tp;
-  if (e < e1) mha_prepare<D, DENSE>(p, e, sel_row, lane, tp);
+  // unconditional: the last split may grow past the hinted range once the count is known
+  mha_prepare<D, DENSE>(p, e, sel_row, lane, tp);
   int n_list = n_part;
   if (!DENSE && p.n_hint > 0) {
     int ns = p.n_sel[seg];
@@ -265,6 +271,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   if (e < e1) vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e, n_list, tp, slot, lane, bad);
   const int swz_k = swz(ql) & (PROW - 1);
   for (; e < e1; e += kMhaWaves) {
+    // This tile's LDS fetches must have landed before the slot is read.  Explicit, because the
+    // compiler's own wait for LDS fetches is not placed reliably across the loop back-edge when
+    // other vector loads are in flight.
+    wait_vm0();
     const uint32_t vm = vm_next;
     const bool more = e + kMhaWaves < e1;
     if (more) mha_prepare<D, DENSE>(p, e + kMhaWaves, sel_row, lane, tp);
@@ -518,15 +528,24 @@ int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus) {
   return (int)s;
 }
 
-template <int D>
-static hipError_t launch_mha_d(hipStream_t st, const MhaParams& p, dim3 grid, bool dense, bool paged) {
+// With a timer, the kernel is launched with hipExtLaunchKernelGGL so that the two events carry the
+// dispatch's own start and end timestamps (no event packets around it).
+template <typename Kern>
+static void launch_one(Kern kern, dim3 grid, hipStream_t st, const MhaParams& p, const KernelTimer* timer) {
   const dim3 block(kMhaWaves * 64);
+  if (timer) hipExtLaunchKernelGGL(kern, grid, block, 0, st, timer->a, timer->b, 0, p);
+  else hipLaunchKernelGGL(kern, grid, block, 0, st, p);
+}
+
+template <int D>
+static hipError_t launch_mha_d(hipStream_t st, const MhaParams& p, dim3 grid, bool dense, bool paged,
+                               const KernelTimer* timer) {
   if (dense) {
-    if (paged) hipLaunchKernelGGL((attn_mha_kernel<D, true, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((attn_mha_kernel<D, true, false>), grid, block, 0, st, p);
+    if (paged) launch_one(attn_mha_kernel<D, true, true>, grid, st, p, timer);
+    else launch_one(attn_mha_kernel<D, true, false>, grid, st, p, timer);
   } else {
-    if (paged) hipLaunchKernelGGL((attn_mha_kernel<D, false, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((attn_mha_kernel<D, false, false>), grid, block, 0, st, p);
+    if (paged) launch_one(attn_mha_kernel<D, false, true>, grid, st, p, timer);
+    else launch_one(attn_mha_kernel<D, false, false>, grid, st, p, timer);
   }
   return hipGetLastError();
 }
@@ -535,7 +554,7 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
                            const void* k_dec, const void* v_dec, const int32_t* page_table,
                            const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                            int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                           uint32_t* status, int n_hint) {
+                           uint32_t* status, int n_hint, const KernelTimer* timer) {
   MhaParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -566,8 +585,8 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
   p.n_hint = dense ? 0 : n_hint;
   // 8 XCDs; the splits of head seg run on XCD seg % 8 (see the kernel)
   dim3 grid(8 * ((p.n_segs + 7) / 8) * n_splits);
-  return g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0)
-                    : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0);
+  return g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0, timer)
+                    : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0, timer);
 }
 
 }  // namespace fdl

@@ -41,6 +41,12 @@ constexpr size_t kTicketOffset = 4096;
 constexpr size_t kCounterOffset = kTicketOffset + kMaxTickets * sizeof(uint32_t);
 constexpr int kMaxCounters = (int)((kHeaderBytes - kCounterOffset) / sizeof(uint32_t));
 
+// Optional timing of one launcher call: a and b become the start and end of the launched work
+// (for a single-kernel launch, the kernel's own dispatch timestamps).
+struct KernelTimer {
+  hipEvent_t a, b;
+};
+
 struct Geom {
   int B, Hq, Hkv, G, D, L, bt, T, dtype;
   int paged, page_tokens, page_log2, pps, n_pages;
@@ -81,7 +87,7 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
                        const void* k_dec, const void* v_dec, const int32_t* page_table,
                        const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                        int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                       uint32_t* status, int n_hint);
+                       uint32_t* status, int n_hint, const KernelTimer* timer);
 
 // One query head per KV head (bf16): the LDS-DMA streaming kernel.
 int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus);
@@ -89,7 +95,7 @@ hipError_t launch_attn_mha(hipStream_t s, const Geom& g, const void* q, const vo
                            const void* k_dec, const void* v_dec, const int32_t* page_table,
                            const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                            int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                           uint32_t* status, int n_hint);
+                           uint32_t* status, int n_hint, const KernelTimer* timer);
 
 hipError_t launch_attn_combine(hipStream_t s, const float* part_o, const float2* part_ml, void* out,
                                int n_segs, int n_splits, int T, int D, bool dmajor);

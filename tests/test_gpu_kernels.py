@@ -190,7 +190,11 @@ def test_dense_attention(h, cfg):
     _small_bf16(n_q_heads=8, n_kv_heads=2, ctx_len=1500, head_dim=64, kv_block=32, top_k_blocks=9),
     _small_bf16(n_q_heads=7, n_kv_heads=1, ctx_len=4096, dec_len=32, top_k_blocks=12),
     _small_bf16(n_q_heads=2, n_kv_heads=2, ctx_len=2048, top_k_blocks=32),   # everything selected
-], ids=["tiny", "mha-ragged", "gqa4-d64-bt32", "gqa7", "all-blocks"])
+    # many tiles per wave: one workgroup per head (256 heads), and 4 splits per head
+    _small_bf16(batch=4, n_q_heads=64, n_kv_heads=64, ctx_len=4096, top_k_blocks=40),
+    _small_bf16(batch=2, n_q_heads=32, n_kv_heads=32, ctx_len=8192, top_k_blocks=48),
+], ids=["tiny", "mha-ragged", "gqa4-d64-bt32", "gqa7", "all-blocks", "mha-1split-10tiles",
+        "mha-4splits-3tiles"])
 def test_sparse_attention_with_oracle_selection(h, cfg):
     x = make_single(cfg)
     g = _geom(cfg)

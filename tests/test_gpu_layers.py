@@ -1,10 +1,11 @@
 """Whole layer-steps on the GPU (the chain of libfdllm calls the benchmark times) against the oracle:
-the tiny, 8K and 16K-GQA workloads in full, the chunked paged workload at reduced and full size."""
+the tiny, 8K and 16K-GQA workloads in full, the chunked paged workload at reduced size."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_close, dev, host, out_buffer, out_to_f64, require_gpu
+from gpu_util import assert_close, require_gpu
+from layer_util import _check_chunked, _check_layer, _chunked, _focus
 from oracle.pipeline import chunked_layer_step, focus_layer_step
 from synth import get_config
 from synth.gen import make_single, to_pages
@@ -19,53 +20,6 @@ def h():
     hh = Handle(workspace_bytes=512 << 20)
     yield hh
     hh.close()
-
-
-def _focus(h, cfg, x, modes=("source", "reuse")):
-    from diffusion_long_context_amd.step import FocusParams, FocusStep, geom_for
-    g = geom_for(cfg)
-    fs = FocusStep(h, g, FocusParams(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.sink_tau,
-                                     cfg.max_sinks))
-    t = {k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec", "masked")}
-    pc = dev(x["prev_conf"]) if x.get("prev_conf") is not None else None
-    fs.predict(pc, t["masked"])
-    ks = fs.new_ks()
-    fs.pool(t["k"], ks)
-    res = {}
-    for mode in modes:
-        out = out_buffer(cfg)
-        fs.layer(mode, t["q"], t["k"], t["v"], t["k_dec"], t["v_dec"], ks, out)
-        torch.cuda.synchronize()
-        res[mode] = {
-            "out": out_to_f64(cfg, out),
-            "pred_mask": host(fs.pred_mask).view(np.uint64).copy(),
-            "scores": host(fs.scores).copy(),
-            "sink_pos": host(fs.sink_pos).copy(),
-            "n_sinks": host(fs.n_sinks).copy(),
-            "sel": host(fs.sel_idx).copy(),
-            "n_sel": host(fs.n_sel).copy(),
-        }
-    assert h.fdl_get_status() == 0
-    return res
-
-
-def _check_layer(cfg, got, want, margin=None):
-    assert np.array_equal(got["pred_mask"], np.asarray(want["pred_mask"], np.uint64))
-    if "scores" in want:
-        assert np.array_equal(got["scores"].view(np.uint32), want["scores"].view(np.uint32))
-    if "sel" in want:
-        if margin is None or margin > 1e-4 * cfg.sink_tau:
-            ns = int(want["n_sinks"][0])
-            for b in range(cfg.batch):
-                nsb = int(want["n_sinks"][b])
-                assert got["n_sinks"][b] == nsb
-                assert got["sink_pos"][b, :nsb].tolist() == want["sink_pos"][b, :nsb].tolist()
-            for b in range(cfg.batch):
-                for g in range(cfg.n_kv_heads):
-                    w = want["sel"][b][g].tolist()
-                    assert got["n_sel"][b, g] == len(w)
-                    assert got["sel"][b, g, : len(w)].tolist() == w
-    assert_close(got["out"], want["out"], cfg.name)
 
 
 @pytest.mark.parametrize("ci", [0, 1, 2])
@@ -99,34 +53,6 @@ def test_source_layer_first_step_and_nothing_masked(h):
     _check_layer(cfg, got["source"], want, want["sink_margin"])
 
 
-def _chunked(h, cfg, x):
-    from diffusion_long_context_amd.step import ChunkedStep, ChunkParams, geom_for
-    g = geom_for(cfg)
-    cs_ = ChunkedStep(h, g, ChunkParams(cfg.top_k_pos, cfg.window, cfg.chunk_tokens, cfg.top_k_chunks,
-                                        cfg.tokens_per_chunk_kept))
-    t = {k: dev(x[k]) for k in ("q", "k_pool", "v_pool", "page_table", "k_dec", "v_dec", "masked",
-                                "prev_conf")}
-    cs_.predict(t["prev_conf"], t["masked"])
-    cs = cs_.new_chunk_sums()
-    cs_.pool(t["k_pool"], t["page_table"], cs)
-    out = out_buffer(cfg)
-    cs_.run(t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["k_dec"], t["v_dec"], cs, out)
-    torch.cuda.synchronize()
-    assert h.fdl_get_status() == 0
-    return {"chunk_scores": host(cs_.chunk_scores), "chunks": host(cs_.chunks),
-            "token_scores": host(cs_.token_scores), "tokens": host(cs_.tokens),
-            "n_tokens": host(cs_.n_tokens), "out": out_to_f64(cfg, out)}
-
-
-def _check_chunked(cfg, got, want):
-    assert np.array_equal(got["chunk_scores"].view(np.uint32), want["chunk_scores"].view(np.uint32))
-    assert np.array_equal(got["chunks"], want["chunks"])
-    assert np.array_equal(got["token_scores"].view(np.uint32), want["token_scores"].view(np.uint32))
-    assert np.array_equal(got["tokens"], want["tokens"])
-    assert np.all(got["n_tokens"] == want["tokens"].shape[-1])
-    assert_close(got["out"], want["out"], "chunked")
-
-
 def test_chunked_small(h):
     cfg = get_config(4).with_(batch=2, n_q_heads=4, n_kv_heads=4, ctx_len=4096, chunk_tokens=512)
     x = make_single(cfg)
@@ -144,3 +70,60 @@ def test_chunked_page_order_bitwise_invariant(h):
     b = _chunked(h, cfg, y)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ctx_len=1000, top_k_blocks=32),                  # fewer blocks than the top-K: list < hint
+    dict(ctx_len=6000, top_k_blocks=40),                  # sink block outside the top-K: list > hint
+    dict(ctx_len=6000, top_k_blocks=40, sink_kind="shared_dir_x8"),
+], ids=["list-below-hint", "list-above-hint", "scattered-sinks"])
+def test_focus_step_driver(h, kw):
+    """fdl_focus_step (one call: predict, then dense / source / reuse / reuse layers) against the
+    oracle layer by layer; its attention launches take the top-K size as their tile-partition hint."""
+    from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
+                                                  fdl_focus_params)
+    from diffusion_long_context_amd.step import geom_for
+    from gpu_util import bf16_out_to_f64, dev, host
+    cfg = get_config(1).with_(n_q_heads=8, n_kv_heads=8, **kw)
+    g = geom_for(cfg)
+    B, Hq, Hkv, D, T, nb, ms = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len,
+                                cfg.n_blk, cfg.max_sel_blocks)
+    modes = ["dense", "source", "reuse", "reuse"]
+    code = {"dense": FDL_LAYER_DENSE, "source": FDL_LAYER_SOURCE, "reuse": FDL_LAYER_REUSE}
+    xs = [make_single(cfg, layer=l) for l in range(len(modes))]
+    t = [{k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec")} for x in xs]
+    ks = [torch.zeros((B, Hkv, nb, D), dtype=torch.float32, device="cuda") for _ in modes]
+    outs = [torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device="cuda") for _ in modes]
+    for l in range(len(modes)):
+        h.fdl_pool_keys(g, t[l]["k"], None, cfg.kv_block, ks[l])
+    pm = torch.zeros(B, dtype=torch.int64, device="cuda")
+    npd = torch.zeros(B, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, Hkv, nb), dtype=torch.float32, device="cuda")
+    sp = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device="cuda")
+    nsk = torch.zeros(B, dtype=torch.int32, device="cuda")
+    sel = torch.zeros((B, Hkv, ms), dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, ms, cfg.sink_tau)
+    table = h.make_layers(g, [dict(q=t[l]["q"], k_cache=t[l]["k"], v_cache=t[l]["v"], k_dec=t[l]["k_dec"],
+                                   v_dec=t[l]["v_dec"], ks=ks[l], out=outs[l], mode=code[m])
+                              for l, m in enumerate(modes)])
+    x0 = xs[0]
+    h.fdl_focus_step(g, params, dev(x0["prev_conf"]), dev(x0["masked"]), table, pm, npd, sc, sp, nsk, sel, nsel)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    sinks = None
+    for l, m in enumerate(modes):
+        x = dict(xs[l], prev_conf=x0["prev_conf"], masked=x0["masked"])
+        want = focus_layer_step(cfg, x, m, sinks=sinks)
+        if m == "source":
+            assert want["sink_margin"] > 1e-4 * cfg.sink_tau
+            sinks = (want["sink_pos"], want["n_sinks"])
+            nsb = int(want["n_sinks"][0])
+            assert int(host(nsk)[0]) == nsb
+            assert host(sp)[0, :nsb].tolist() == want["sink_pos"][0, :nsb].tolist()
+        if l == len(modes) - 1:
+            for gh in range(Hkv):
+                w = want["sel"][0][gh].tolist()
+                assert int(host(nsel)[0, gh]) == len(w)
+                assert host(sel)[0, gh, : len(w)].tolist() == w
+        assert_close(bf16_out_to_f64(outs[l]), want["out"], f"layer {l} ({m})")
