@@ -256,7 +256,9 @@ def main():
     sparse_us = avg_us(prof_main, "sparse_attn")
     units = int(nsel_last.sum())                       # selected 64-token blocks over all heads
     unit_bytes = cfg.kv_block * D * 2 * 2              # K + V of one block, bf16
-    fixed_bytes = Hq * (T * D * 2 * 2) + Hkv * (T * D * 2 * 2) + units * 4 + B * Hkv * 4
+    # the sparse launch scores the blocks itself: pooled keys in, scores and selection out
+    fixed_bytes = (Hq * (T * D * 2 * 2) + Hkv * (T * D * 2 * 2) + units * 4 + B * Hkv * 4
+                   + B * Hkv * n_blk * D * 4 + B * Hkv * n_blk * 4)
     launch_bytes = units * unit_bytes + fixed_bytes
     achieved = launch_bytes / (sparse_us * 1e-6) / 1e9
     ms_per_step = 1e3 * t_total / args.steps
@@ -281,7 +283,7 @@ def main():
                    "sink_source_layer": cfg.source_layer, "gen_len": gen_steps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
-                     "kernel": "attn_mha_kernel<128,false,false> (sparse attention)",
+                     "kernel": "attn_mha_kernel<128,false,false,true> (block scoring + selection + sparse attention)",
                      "avg_launch_us": sparse_us, "launches": prof_main["sparse_attn"][1],
                      "bytes_per_launch": launch_bytes, "units_per_launch": units,
                      "unit_bytes": unit_bytes},

@@ -181,6 +181,28 @@ fdl_status run_attn(fdl_handle h, const Geom& g, const void* q, const void* k_ca
                     "attention launch");
 }
 
+// Score, select and attend in one kernel (one q-head per KV head, bf16, contiguous cache): same
+// outputs as run_score_units + run_select + run_attn.
+bool fused_select_ok(const Geom& g, int n_blk, int max_sel) {
+  return g.dtype == FDL_BF16 && g.G == 1 && !g.paged && g.L > 0 && n_blk <= fdl::kFusedMaxUnits &&
+         max_sel <= fdl::kFusedMaxSel;
+}
+
+fdl_status run_select_attn(fdl_handle h, const Geom& g, const fdl_layer_io& io, const uint64_t* pred_mask,
+                           const fdl_focus_params* fp, int bt_log2, const int32_t* sink_pos,
+                           const int32_t* n_sinks, float* scores, int32_t* sel_idx, int32_t* n_sel) {
+  long long list_tokens = (long long)fp->max_sel << bt_log2;
+  if (list_tokens > g.L) list_tokens = g.L;
+  const int n_splits = attn_splits(h, g, list_tokens);
+  const fdl::FusedSelect fs{pred_mask, io.ks,     sink_pos,    n_sinks,       fp->max_sinks, fp->top_k_blocks,
+                            scores,    sel_idx, n_sel, h->barriers, h->spin_limit};
+  ProfScope ps(h, FDL_PROF_SPARSE_ATTN, /*inner=*/true);
+  return hip_status(h, fdl::launch_attn_mha(h->stream, g, io.q, io.k_cache, io.v_cache, io.k_dec, io.v_dec,
+                                            nullptr, sel_idx, n_sel, fp->max_sel, bt_log2, 0, io.out,
+                                            h->scratch, n_splits, h->tickets, h->status, 0, ps.timer(), &fs),
+                    "select-attention launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,7 +251,11 @@ fdl_status fdl_create(fdl_handle* out, void* hip_stream, size_t workspace_bytes)
   h->ws_bytes = workspace_bytes;
   h->status = reinterpret_cast<uint32_t*>(h->ws);
   h->tickets = reinterpret_cast<uint32_t*>(h->ws + fdl::kTicketOffset);
-  h->counters = reinterpret_cast<uint32_t*>(h->ws + fdl::kCounterOffset);
+  h->barriers = reinterpret_cast<uint32_t*>(h->ws + fdl::kBarrierOffset);
+  {
+    const char* e = getenv("FDL_SPIN_LIMIT");
+    h->spin_limit = e ? atoi(e) : 200000;
+  }
   h->scratch = h->ws + fdl::kHeaderBytes;
   h->scratch_bytes = workspace_bytes - fdl::kHeaderBytes;
   h->last_error[0] = 0;
@@ -251,7 +277,14 @@ fdl_status fdl_set_stream(fdl_handle h, void* hip_stream) {
   return FDL_OK;
 }
 
-fdl_status fdl_get_status(fdl_handle h) {
+fdl_status fdl_get_status(fdl_handle h) { return fdl_get_status_bits(h, nullptr); }
+
+fdl_status fdl_get_status_bits(fdl_handle h, uint32_t* bits) {
+  static_assert(FDL_FLAG_SINK_OVERFLOW == fdl::ST_SINK_OVERFLOW && FDL_FLAG_CAND_OVERFLOW == fdl::ST_CAND_OVERFLOW &&
+                    FDL_FLAG_BAD_INDEX == fdl::ST_BAD_INDEX && FDL_FLAG_SEL_OVERFLOW == fdl::ST_SEL_OVERFLOW &&
+                    FDL_FLAG_SPLIT_FALLBACK == fdl::ST_SYNC_FALLBACK,
+                "status bits");
+  if (bits) *bits = 0;
   if (!h) return FDL_EINVAL;
   fdl_status st = hip_status(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
   if (st != FDL_OK) return st;
@@ -264,7 +297,8 @@ fdl_status fdl_get_status(fdl_handle h) {
     st = hip_status(h, hipDeviceSynchronize(), "hipDeviceSynchronize");
     if (st != FDL_OK) return st;
   }
-  if (word & (fdl::ST_SINK_OVERFLOW | fdl::ST_CAND_OVERFLOW)) return FDL_EOVERFLOW;
+  if (bits) *bits = word;
+  if (word & (fdl::ST_SINK_OVERFLOW | fdl::ST_CAND_OVERFLOW | fdl::ST_SEL_OVERFLOW)) return FDL_EOVERFLOW;
   if (word & fdl::ST_BAD_INDEX) return FDL_EINDEX;
   return FDL_OK;
 }
@@ -466,12 +500,20 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_para
       if (st != FDL_OK) return st;
       continue;
     }
-    st = run_score_units(h, g, io.q, pred_mask, io.ks, n_blk, scores);
-    if (st != FDL_OK) return st;
+    const bool fused = fused_select_ok(g, n_blk, fp->max_sel);
+    if (!fused) {
+      st = run_score_units(h, g, io.q, pred_mask, io.ks, n_blk, scores);
+      if (st != FDL_OK) return st;
+    }
     if (io.mode == FDL_LAYER_SOURCE) {
       st = run_sinks(h, g, io.q, pred_mask, io.k_cache, io.k_dec, fp->sink_tau, fp->max_sinks, sink_pos,
                      n_sinks, ns, cap);
       if (st != FDL_OK) return st;
+    }
+    if (fused) {
+      st = run_select_attn(h, g, io, pred_mask, fp, bt_log2, sink_pos, n_sinks, scores, sel_idx, n_sel);
+      if (st != FDL_OK) return st;
+      continue;
     }
     st = run_select(h, g, scores, n_blk, bt_log2, sink_pos, n_sinks, fp->max_sinks, nullptr, 0,
                     fp->top_k_blocks, 0, fp->max_sel, sel_idx, n_sel);

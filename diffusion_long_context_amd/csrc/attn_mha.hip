@@ -31,6 +31,8 @@
 
 #include "fdl_device.h"
 #include "fdl_internal.h"
+#include "fdl_score.h"
+#include "fdl_select.h"
 
 namespace fdl {
 
@@ -52,6 +54,9 @@ struct MhaParams {
   int n_hint;   // expected selected units per head (0 = unknown)
   int page_log2, pages_per_seq, n_pages;
   float scale_log2;
+  // fused selection (SEL): every workgroup scores the blocks of its head against the predicted
+  // queries and selects them itself; split 0 also writes the scores and the selection out
+  FusedSelect fs;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -93,9 +98,9 @@ struct TilePrep {
   int u[MhaShape<D>::INSTR];
 };
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool SEL>
 __device__ __forceinline__ void mha_prepare(const MhaParams& p, int e, const int32_t* __restrict__ sel_row,
-                                            int lane, TilePrep<D>& tp) {
+                                            const uint16_t* sel_lds, int lane, TilePrep<D>& tp) {
   using S = MhaShape<D>;
   if constexpr (!DENSE) {
     const int rsub = lane / S::PROW;
@@ -104,9 +109,180 @@ __device__ __forceinline__ void mha_prepare(const MhaParams& p, int e, const int
     for (int j = 0; j < S::INSTR; ++j) {
       const int i = (e - 1) * kTileTok + j * S::ROWS_PER_INSTR + rsub;
       const int si = i >> p.unit_log2;
-      tp.u[j] = sel_row[si < p.max_sel ? si : p.max_sel - 1];
+      if constexpr (SEL) tp.u[j] = sel_lds[si < p.max_sel ? si : p.max_sel - 1];
+      else tp.u[j] = sel_row[si < p.max_sel ? si : p.max_sel - 1];
     }
   }
+}
+
+// Barrier of the NS splits of one head.  They run on one XCD (see the kernel), so a relaxed
+// atomic at L2 orders them and data they stored before arriving is in that L2.  Arrival count and
+// generation live in `bar`; the last arrival resets the count and bumps the generation.  A waiter
+// gives up after spin_limit polls (returns false) instead of waiting on a sibling that is not
+// resident; the caller then recomputes what it would have read.  All threads must call.
+__device__ bool head_barrier(uint32_t* bar, int NS, int spin_limit, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are acknowledged by L2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t g0 = __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(g0));   // the arrival is issued after g0 is read
+    const uint32_t old = __hip_atomic_fetch_add(&bar[0], 1u + zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int ok = 1;
+    if (old == (uint32_t)(NS - 1)) {
+      __hip_atomic_store(&bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      int it = 0;
+      while (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+        if (++it > spin_limit) {
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    *s_flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *s_flag != 0;
+  asm volatile("buffer_inv sc0" ::: "memory");   // drop L1 lines: the siblings' stores are in L2
+  return ok;
+}
+
+// Pinned float32 scores of pooled-key rows (the same tree as score_units_kernel).  A batch covers
+// kRowBatch rows: lane l of wave w holds 16 floats of row base + ps*RPP + w*RPW + l/LPR.
+constexpr int kScoreBatch = 4;   // passes whose loads fly together
+
+template <int D>
+__device__ __forceinline__ void mha_load_rows(const float* __restrict__ ksh, int base, int rb,
+                                              float (&x)[kScoreBatch][16]) {
+  constexpr int LPR = D / 16, RPW = 64 / LPR, RPP = kMhaWaves * RPW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int ps = 0; ps < kScoreBatch; ++ps) {
+    int r = base + ps * RPP + wave * RPW + lane / LPR;
+    r = r < rb ? r : rb - 1;
+    load16<float>(ksh + (int64_t)r * D + 16 * (lane % LPR), x[ps]);
+  }
+}
+
+// keys[r] = order_key(score) and, when to_global, scores[r] as well, for the batch at base.
+template <int D>
+__device__ __forceinline__ void mha_dot_rows(const float (&x)[kScoreBatch][16], int base, int rb, const float (&qv)[16],
+                                             uint32_t* keys, float* __restrict__ scores, bool to_global) {
+  constexpr int LPR = D / 16, RPW = 64 / LPR, RPP = kMhaWaves * RPW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int ps = 0; ps < kScoreBatch; ++ps) {
+    const int r = base + ps * RPP + wave * RPW + lane / LPR;
+    const float sc = row_dot<LPR>(x[ps], qv);
+    if (lane % LPR == 0 && r < rb) {
+      keys[r] = order_key(sc);
+      if (to_global) scores[r] = sc;
+    }
+  }
+}
+
+// Rows [ra, rb); the first batch may already be loaded (x, pre = true).
+template <int D>
+__device__ __forceinline__ void mha_score_rows(const float* __restrict__ ksh, int ra, int rb, const float (&qv)[16],
+                                               uint32_t* keys, float* __restrict__ scores, bool to_global,
+                                               float (&x)[kScoreBatch][16], bool pre) {
+  constexpr int RPP = kMhaWaves * (64 / (D / 16));
+  if (rb <= ra) return;   // uniform
+  for (int base = ra; base < rb; base += kScoreBatch * RPP) {
+    if (!(pre && base == ra)) mha_load_rows<D>(ksh, base, rb, x);
+    mha_dot_rows<D>(x, base, rb, qv, keys, scores, to_global);
+  }
+}
+
+// Fused selection, first phase of the SEL kernel.  The NS splits of a head share the scoring: split
+// s scores rows [n s / NS, n (s+1) / NS) into the scores output, they meet at head_barrier, and each
+// then reads all n scores back (a split whose siblings do not arrive in time scores every row
+// itself).  Then every split selects the sink blocks plus the top-K others (select_core) into
+// sel_lds, ascending; split 0 writes the selection out.  The scratch of both steps lives in the
+// tile slots, which are free until the first fetch.  Returns the number of selected blocks.
+constexpr int kQbufOffsetF = 8192;   // floats: past qs, keys, forced bits and the selection scratch
+
+template <int D>
+__device__ int mha_select_phase(const MhaParams& p, int b, int h, int64_t seg, int s, int NS, uint16_t* lds_raw,
+                                uint16_t* sel_lds) {
+  constexpr int NT = kMhaWaves * 64;
+  constexpr int LPR = D / 16;
+  const FusedSelect& f = p.fs;
+  float* qs = reinterpret_cast<float*>(lds_raw);                           // [D]
+  uint32_t* keys = reinterpret_cast<uint32_t*>(lds_raw) + D;               // [kFusedMaxUnits]
+  uint32_t* forced = keys + kFusedMaxUnits;                                 // [kFusedMaxUnits / 32]
+  int* hist = reinterpret_cast<int*>(forced + kFusedMaxUnits / 32);        // [256]
+  int* tmp = hist + 256;                                                    // [NT / 64]
+  uint32_t* digit = reinterpret_cast<uint32_t*>(tmp + NT / 64);
+  int* above = reinterpret_cast<int*>(digit + 1);
+  int* flag = above + 1;
+  static_assert(D + kFusedMaxUnits + kFusedMaxUnits / 32 + 256 + NT / 64 + 4 <= kQbufOffsetF, "select scratch");
+  static_assert((kQbufOffsetF + 32 * D) * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * MhaShape<D>::SLOT,
+                "query staging must fit in the tile slots");
+  const int tid = threadIdx.x;
+  const int j = (tid & 63) % LPR;
+  const int n = p.n_units;
+  const float* ksh = f.ks + seg * (int64_t)n * D;
+  float* sc_out = f.scores + seg * (int64_t)n;
+
+  const int ra = (int)((int64_t)n * s / NS), rb = (int)((int64_t)n * (s + 1) / NS);
+  float x[kScoreBatch][16];
+  const bool pre = rb > ra;
+  if (pre) mha_load_rows<D>(ksh, ra, rb, x);   // in flight during the query sum
+  for (int i = tid; i < (n + 31) / 32; i += NT) forced[i] = 0u;
+  // the query staging area sits above the keys' scratch in the (still unused) tile slots
+  query_sum_g1_coop<D, 32, NT>(p.q + seg * (int64_t)p.T * D, f.pred_mask[b], p.T,
+                               reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, qs);
+  __syncthreads();   // qs and the cleared bits
+  if (f.sink_pos != nullptr) {
+    int ns = f.n_sinks[b];
+    ns = ns < f.max_sinks ? ns : f.max_sinks;
+    for (int t = tid; t < ns; t += NT) {
+      const int pos = f.sink_pos[(int64_t)b * f.max_sinks + t];
+      if (pos < 0) continue;
+      const int u = pos >> p.unit_log2;
+      if (u < n) atomicOr(&forced[u >> 5], 1u << (u & 31));
+    }
+  }
+  float qv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
+  mha_score_rows<D>(ksh, ra, rb, qv, keys, sc_out, true, x, pre);
+  if (NS > 1) {
+    if (head_barrier(f.barriers + seg * kSyncStride, NS, f.spin_limit, flag)) {
+      for (int i = tid; i < n; i += NT)
+        if (i < ra || i >= rb) keys[i] = order_key(sc_out[i]);
+    } else {
+      mha_score_rows<D>(ksh, 0, ra, qv, keys, sc_out, false, x, false);
+      mha_score_rows<D>(ksh, rb, n, qv, keys, sc_out, false, x, false);
+      if (tid == 0) latch(p.status, ST_SYNC_FALLBACK);
+    }
+  }
+  __syncthreads();
+  int32_t* gout = f.sel_idx + seg * p.max_sel;
+  const bool writer = s == 0;
+  auto emit = [&](int pos, int i) {
+    if (pos < p.max_sel) {
+      sel_lds[pos] = (uint16_t)i;
+      if (writer) gout[pos] = i;
+    }
+  };
+  SelResult r;
+  if (n <= NT) {
+    r = select_small<NT>(keys, forced, n, f.top_k, reinterpret_cast<uint64_t*>(keys + kFusedMaxUnits - 2 * NT),
+                         reinterpret_cast<uint32_t*>(hist), hist + 64, tmp, emit);
+  } else {
+    const SelScratch scr{hist, tmp, digit, above};
+    r = select_core<NT>(keys, forced, n, f.top_k, scr, emit);
+  }
+  if (writer && tid == 0) f.n_sel[seg] = r.total < p.max_sel ? r.total : p.max_sel;
+  if (tid == 0 && r.total > p.max_sel) latch(p.status, ST_SEL_OVERFLOW);
+  __syncthreads();   // sel_lds complete; the slots are free again
+  return r.total < p.max_sel ? r.total : p.max_sel;
 }
 
 // Launch the LDS fetches of a prepared tile into the wave's slot; returns the 32-bit row mask.
@@ -190,12 +366,14 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
   return okm;
 }
 
-template <int D, bool DENSE, bool PAGED>
+template <int D, bool DENSE, bool PAGED, bool SEL>
 __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaParams p) {
   using S = MhaShape<D>;
   constexpr int NT = kMhaWaves * 64;
   constexpr int KS = S::KS, DT = S::DT, PROW = S::PROW;
+  static_assert(!SEL || (!DENSE && !PAGED), "fused selection: contiguous sparse only");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kMhaWaves * S::SLOT];
+  __shared__ uint16_t sel_lds[SEL ? kFusedMaxSel : 1];
 
   // Workgroup i runs on XCD i % 8 (the dispatcher's round-robin order).  All splits of one head
   // are given workgroup ids with the same residue, so they share one L2 and the final merge can
@@ -227,7 +405,12 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   // and the last split takes any tiles beyond the hint.
   int n_part = DENSE ? p.L : (p.n_hint > 0 ? (p.n_hint < p.max_sel ? p.n_hint : p.max_sel) << p.unit_log2 : -1);
   int ns_raw = 0;
-  if (!DENSE && n_part < 0) ns_raw = p.n_sel[seg];   // no hint: the count comes first
+  if constexpr (SEL) {
+    ns_raw = mha_select_phase<D>(p, b, h, seg, s, NS, lds, sel_lds);
+    n_part = -1;
+  } else if (!DENSE && n_part < 0) {
+    ns_raw = p.n_sel[seg];   // no hint: the count comes first
+  }
   if (n_part < 0) n_part = (ns_raw < 0 ? 0 : (ns_raw > p.max_sel ? p.max_sel : ns_raw)) << p.unit_log2;
   if (p.L == 0) n_part = 0;
   const int n_tiles_part = 1 + (n_part + kTileTok - 1) / kTileTok;
@@ -236,9 +419,9 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   int e = e0 + wave;
   TilePrep<D> tp;
   // unconditional: the last split may grow past the hinted range once the count is known
-  mha_prepare<D, DENSE>(p, e, sel_row, lane, tp);
+  mha_prepare<D, DENSE, SEL>(p, e, sel_row, sel_lds, lane, tp);
   int n_list = n_part;
-  if (!DENSE && p.n_hint > 0) {
+  if (!DENSE && !SEL && p.n_hint > 0) {
     int ns = p.n_sel[seg];
     ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
     n_list = p.L == 0 ? 0 : ns << p.unit_log2;
@@ -277,7 +460,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     wait_vm0();
     const uint32_t vm = vm_next;
     const bool more = e + kMhaWaves < e1;
-    if (more) mha_prepare<D, DENSE>(p, e + kMhaWaves, sel_row, lane, tp);
+    if (more) mha_prepare<D, DENSE, SEL>(p, e + kMhaWaves, sel_row, sel_lds, lane, tp);
     // ---- K from LDS into A-operand registers, then S^T = K Q^T: register r holds token
     //      8*(r/4) + 4*hh + r%4 for query ql (K registers die here) ----
     f32x16 sacc;
@@ -433,7 +616,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   //      ticket, and the last taker drops its L1 copies before reading the partials back. ----
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg], 1u);
+  if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg * kSyncStride], 1u);
   __syncthreads();
   if (s_ticket != (uint32_t)(NS - 1)) return;
   asm volatile("buffer_inv sc0" ::: "memory");
@@ -469,7 +652,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     for (int i = 0; i < 8; ++i)
       if (q0 + i < p.T) p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(o[i] / Lq[i]);
   }
-  if (tid == 0) p.tickets[seg] = 0u;
+  if (tid == 0) p.tickets[seg * kSyncStride] = 0u;
 }
 
 // Merge the per-split partials (max, sum, O) of every head into the bf16 output.  Separate kernel:
@@ -524,7 +707,7 @@ int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus) {
   const long long per_wave_min = 1;
   if (s * kMhaWaves * per_wave_min > tiles) s = (tiles + kMhaWaves - 1) / kMhaWaves;
   if (s < 1) s = 1;
-  if (segs > kMaxTickets) s = 1;
+  if (segs > kMaxSplitSegs) s = 1;
   return (int)s;
 }
 
@@ -538,14 +721,16 @@ static void launch_one(Kern kern, dim3 grid, hipStream_t st, const MhaParams& p,
 }
 
 template <int D>
-static hipError_t launch_mha_d(hipStream_t st, const MhaParams& p, dim3 grid, bool dense, bool paged,
+static hipError_t launch_mha_d(hipStream_t st, const MhaParams& p, dim3 grid, bool dense, bool paged, bool sel,
                                const KernelTimer* timer) {
-  if (dense) {
-    if (paged) launch_one(attn_mha_kernel<D, true, true>, grid, st, p, timer);
-    else launch_one(attn_mha_kernel<D, true, false>, grid, st, p, timer);
+  if (sel) {
+    launch_one(attn_mha_kernel<D, false, false, true>, grid, st, p, timer);
+  } else if (dense) {
+    if (paged) launch_one(attn_mha_kernel<D, true, true, false>, grid, st, p, timer);
+    else launch_one(attn_mha_kernel<D, true, false, false>, grid, st, p, timer);
   } else {
-    if (paged) launch_one(attn_mha_kernel<D, false, true>, grid, st, p, timer);
-    else launch_one(attn_mha_kernel<D, false, false>, grid, st, p, timer);
+    if (paged) launch_one(attn_mha_kernel<D, false, true, false>, grid, st, p, timer);
+    else launch_one(attn_mha_kernel<D, false, false, false>, grid, st, p, timer);
   }
   return hipGetLastError();
 }
@@ -554,7 +739,7 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
                            const void* k_dec, const void* v_dec, const int32_t* page_table,
                            const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                            int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                           uint32_t* status, int n_hint, const KernelTimer* timer) {
+                           uint32_t* status, int n_hint, const KernelTimer* timer, const FusedSelect* fsel) {
   MhaParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -583,10 +768,12 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
   p.n_segs = g.B * g.Hq;
   p.n_hint = dense ? 0 : n_hint;
+  p.fs = fsel ? *fsel : FusedSelect{};
   // 8 XCDs; the splits of head seg run on XCD seg % 8 (see the kernel)
   dim3 grid(8 * ((p.n_segs + 7) / 8) * n_splits);
-  return g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0, timer)
-                    : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0, timer);
+  const bool sel = fsel != nullptr && !dense && !g.paged;
+  return g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0, sel, timer)
+                    : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0, sel, timer);
 }
 
 }  // namespace fdl

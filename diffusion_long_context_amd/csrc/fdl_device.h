@@ -11,6 +11,8 @@ enum : uint32_t {
   ST_SINK_OVERFLOW = 1u << 0,   // more sinks than max_sinks
   ST_CAND_OVERFLOW = 1u << 1,   // more sink candidates than the workspace holds
   ST_BAD_INDEX = 1u << 2,       // unit / page id out of range (row skipped)
+  ST_SEL_OVERFLOW = 1u << 3,    // more selected units than max_sel (list truncated)
+  ST_SYNC_FALLBACK = 1u << 4,   // a fused split scored every block itself (informational)
 };
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;

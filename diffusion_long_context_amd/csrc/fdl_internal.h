@@ -16,8 +16,9 @@ struct fdl_ctx {
   char* ws;              // workspace base (device)
   size_t ws_bytes;
   uint32_t* status;      // device status word
-  uint32_t* tickets;     // split-merge tickets, one per (b, kv head); left at zero by each kernel
-  uint32_t* counters;    // per-call counters, cleared by the call that uses them
+  uint32_t* tickets;     // split-merge tickets, kSyncStride apart per (b, head); left at zero
+  uint32_t* barriers;    // split barriers of the fused kernel, kSyncStride apart per (b, head)
+  int spin_limit;        // polls a fused-kernel split waits for its siblings (FDL_SPIN_LIMIT)
   char* scratch;         // general scratch after the fixed header
   size_t scratch_bytes;
   char last_error[256];
@@ -35,16 +36,39 @@ struct fdl_ctx {
 
 namespace fdl {
 
-constexpr size_t kHeaderBytes = 1u << 20;        // status + tickets + counters
+constexpr size_t kHeaderBytes = 1u << 20;        // status + tickets + barriers
 constexpr int kMaxTickets = 65536;               // B * Hkv limit for split attention
 constexpr size_t kTicketOffset = 4096;
-constexpr size_t kCounterOffset = kTicketOffset + kMaxTickets * sizeof(uint32_t);
-constexpr int kMaxCounters = (int)((kHeaderBytes - kCounterOffset) / sizeof(uint32_t));
+// Heads split over several workgroups synchronise through per-head words in the header, each in a
+// 256-byte line of its own so that the atomics of different heads do not queue on one L2 line.
+// Only launches with at most kMaxSplitSegs (sequence, head) pairs split at all.
+constexpr int kMaxSplitSegs = 256;
+constexpr int kSyncStride = 64;                  // uint32 words between two heads' sync words
+constexpr size_t kBarrierOffset = kTicketOffset + (size_t)kMaxSplitSegs * kSyncStride * sizeof(uint32_t);
+static_assert(kBarrierOffset + (size_t)kMaxSplitSegs * kSyncStride * sizeof(uint32_t) <= kHeaderBytes,
+              "header too small");
 
 // Optional timing of one launcher call: a and b become the start and end of the launched work
 // (for a single-kernel launch, the kernel's own dispatch timestamps).
 struct KernelTimer {
   hipEvent_t a, b;
+};
+
+// Fused selection for the one-q-head-per-KV-head sparse attention: the attention kernel scores the
+// blocks against the predicted queries and selects sinks + top-K itself.
+constexpr int kFusedMaxUnits = 4096;   // blocks per head the fused path keeps in LDS
+constexpr int kFusedMaxSel = 4096;     // selected blocks per head
+struct FusedSelect {
+  const uint64_t* pred_mask;   // [B]
+  const float* ks;             // pooled keys [B][H][n_units][D]
+  const int32_t* sink_pos;     // [B][max_sinks] or null
+  const int32_t* n_sinks;      // [B]
+  int max_sinks, top_k;
+  float* scores;               // out: [B][H][n_units]
+  int32_t* sel_idx;            // out: [B][H][max_sel], ascending
+  int32_t* n_sel;              // out: [B][H]
+  uint32_t* barriers;          // [B * H][2] split barrier state, left consistent by every launch
+  int spin_limit;              // polls before a split stops waiting for its siblings
 };
 
 struct Geom {
@@ -95,7 +119,8 @@ hipError_t launch_attn_mha(hipStream_t s, const Geom& g, const void* q, const vo
                            const void* k_dec, const void* v_dec, const int32_t* page_table,
                            const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                            int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                           uint32_t* status, int n_hint, const KernelTimer* timer);
+                           uint32_t* status, int n_hint, const KernelTimer* timer,
+                           const FusedSelect* fsel = nullptr);
 
 hipError_t launch_attn_combine(hipStream_t s, const float* part_o, const float2* part_ml, void* out,
                                int n_segs, int n_splits, int T, int D, bool dmajor);

@@ -1,0 +1,165 @@
+// Pinned float32 pieces of the scoring path, shared by the scoring kernels and the fused
+// select-and-attend kernel so that both produce the same bits.
+//
+// Every sum is the adjacent-pair tree (operands zero-padded to a power of two; level by level,
+// element 2j plus element 2j+1), every product is rounded to float32 before it is added, and nothing
+// is contracted into a fused multiply-add: each function turns contraction off for its own body.
+#pragma once
+
+#include "fdl_device.h"
+
+namespace fdl {
+
+template <typename QT>
+__device__ __forceinline__ float load_q(const QT* q);
+template <>
+__device__ __forceinline__ float load_q<uint16_t>(const uint16_t* q) {
+  return bf16_bits_to_f32(*q);
+}
+template <>
+__device__ __forceinline__ float load_q<float>(const float* q) {
+  return *q;
+}
+
+__device__ __forceinline__ int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// TMAX: 32 or 64, a compile-time bound on T.
+template <typename QT, int D, int TMAX>
+__device__ __forceinline__ void query_sum_to_lds(const QT* __restrict__ q, uint64_t pred, int b, int g,
+                                                 int Hq, int G, int T, float* qs_lds) {
+#pragma clang fp contract(off)
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  const int T2 = pow2_ceil(T);
+  const int G2 = pow2_ceil(G);
+  float hv[8];
+  for (int j = 0; j < 8; ++j) {
+    hv[j] = 0.f;
+    if (j < G) {   // uniform
+      const int h = g * G + j;
+      const QT* qh = q + ((int64_t)b * Hq + h) * T * D + d;
+      float a[TMAX];
+#pragma unroll
+      for (int p = 0; p < TMAX; ++p) a[p] = load_q<QT>(qh + (int64_t)(p < T ? p : T - 1) * D);
+      // keep the scheduler from interleaving the tree with the loads: all TMAX loads must be in
+      // flight together, not issued pairwise behind waits
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int p = 0; p < TMAX; ++p)
+        if (!(p < T && ((pred >> p) & 1ull))) a[p] = 0.f;
+#pragma unroll
+      for (int lvl = 0; lvl < 6; ++lvl) {
+        if ((TMAX >> (lvl + 1)) >= 1 && (1 << lvl) < T2) {
+#pragma unroll
+          for (int i = 0; i < (TMAX >> (lvl + 1)); ++i) a[i] = a[2 * i] + a[2 * i + 1];
+        }
+      }
+      hv[j] = a[0];
+    }
+  }
+#pragma unroll
+  for (int lvl = 0; lvl < 3; ++lvl) {
+    if ((1 << lvl) < G2) {
+#pragma unroll
+      for (int i = 0; i < (4 >> lvl); ++i) hv[i] = hv[2 * i] + hv[2 * i + 1];
+    }
+  }
+  qs_lds[d] = hv[0];
+}
+
+// query_sum_to_lds for one query head (G = 1) with every thread of an NT-thread block loading: row
+// p of the head's queries is read as D / 8 sixteen-byte chunks, masked (p predicted and p < T) into
+// qbuf [TMAX][D] float32 in LDS, and threads d < D then build the same adjacent-pair tree over the
+// TMAX rows as query_sum_to_lds.  Same bits; one round trip instead of TMAX narrow loads per thread.
+template <int D, int TMAX, int NT>
+__device__ __forceinline__ void query_sum_g1_coop(const uint16_t* __restrict__ qh, uint64_t pred, int T,
+                                                  float* qbuf, float* qs_lds) {
+#pragma clang fp contract(off)
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  static_assert(TMAX * CPR <= NT || (TMAX * CPR) % NT == 0, "chunking");
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int c0 = 0; c0 < TMAX * CPR; c0 += NT) {
+    const int c = c0 + t;
+    if (c < TMAX * CPR) {
+      const int p = c / CPR, ch = c % CPR;
+      uint4 v = *reinterpret_cast<const uint4*>(qh + (int64_t)(p < T ? p : T - 1) * D + ch * 8);
+      const bool keep = p < T && ((pred >> p) & 1ull);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float* dst = qbuf + p * D + ch * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = keep ? bf16_bits_to_f32(w[e] & 0xFFFFu) : 0.f;
+        dst[2 * e + 1] = keep ? bf16_bits_to_f32(w[e] >> 16) : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  if (t < D) {
+    const int T2 = pow2_ceil(T);
+    float a[TMAX];
+#pragma unroll
+    for (int p = 0; p < TMAX; ++p) a[p] = qbuf[p * D + t];
+#pragma unroll
+    for (int lvl = 0; lvl < 6; ++lvl) {
+      if ((TMAX >> (lvl + 1)) >= 1 && (1 << lvl) < T2) {
+#pragma unroll
+        for (int i = 0; i < (TMAX >> (lvl + 1)); ++i) a[i] = a[2 * i] + a[2 * i + 1];
+      }
+    }
+    qs_lds[t] = a[0];
+  }
+}
+
+// Pinned dot product of one row: lane j of an LPR-lane team holds dimensions [16j, 16j+16).
+// Local tree over its 16 products (levels 0-3), then xor butterflies across the team.
+template <int LPR>
+__device__ __forceinline__ float row_dot(const float (&x)[16], const float (&qv)[16]) {
+#pragma clang fp contract(off)
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = x[i] * qv[i];
+#pragma unroll
+  for (int w = 8; w >= 1; w /= 2) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+  }
+  float s = p[0];
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) s = s + wave_shfl_xor(s, m);
+  return s;
+}
+
+template <typename KT>
+__device__ __forceinline__ void load16(const KT* src, float (&x)[16]);
+
+template <>
+__device__ __forceinline__ void load16<uint16_t>(const uint16_t* src, float (&x)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(src);
+  const uint4 a = p[0], c = p[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load16<float>(const float* src, float (&x)[16]) {
+  const float4* p = reinterpret_cast<const float4*>(src);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float4 v = p[c];
+    x[4 * c] = v.x;
+    x[4 * c + 1] = v.y;
+    x[4 * c + 2] = v.z;
+    x[4 * c + 3] = v.w;
+  }
+}
+
+}  // namespace fdl

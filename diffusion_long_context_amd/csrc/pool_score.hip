@@ -18,6 +18,7 @@
 
 #include "fdl_device.h"
 #include "fdl_internal.h"
+#include "fdl_score.h"
 
 namespace fdl {
 
@@ -174,109 +175,6 @@ hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const i
 // slots (padded to 2^m; non-predicted slots +0) of q[b][h][p][d].  Computed by threads d < D of the
 // block into LDS; every q load is issued before the first add.
 // ------------------------------------------------------------------------------------------------
-
-template <typename QT>
-__device__ __forceinline__ float load_q(const QT* q);
-template <>
-__device__ __forceinline__ float load_q<uint16_t>(const uint16_t* q) {
-  return bf16_bits_to_f32(*q);
-}
-template <>
-__device__ __forceinline__ float load_q<float>(const float* q) {
-  return *q;
-}
-
-__device__ __forceinline__ int pow2_ceil(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
-// TMAX: 32 or 64, a compile-time bound on T.
-template <typename QT, int D, int TMAX>
-__device__ __forceinline__ void query_sum_to_lds(const QT* __restrict__ q, uint64_t pred, int b, int g,
-                                                 int Hq, int G, int T, float* qs_lds) {
-  const int d = threadIdx.x;
-  if (d >= D) return;
-  const int T2 = pow2_ceil(T);
-  const int G2 = pow2_ceil(G);
-  float hv[8];
-  for (int j = 0; j < 8; ++j) {
-    hv[j] = 0.f;
-    if (j < G) {   // uniform
-      const int h = g * G + j;
-      const QT* qh = q + ((int64_t)b * Hq + h) * T * D + d;
-      float a[TMAX];
-#pragma unroll
-      for (int p = 0; p < TMAX; ++p) a[p] = load_q<QT>(qh + (int64_t)(p < T ? p : T - 1) * D);
-#pragma unroll
-      for (int p = 0; p < TMAX; ++p)
-        if (!(p < T && ((pred >> p) & 1ull))) a[p] = 0.f;
-#pragma unroll
-      for (int lvl = 0; lvl < 6; ++lvl) {
-        if ((TMAX >> (lvl + 1)) >= 1 && (1 << lvl) < T2) {
-#pragma unroll
-          for (int i = 0; i < (TMAX >> (lvl + 1)); ++i) a[i] = a[2 * i] + a[2 * i + 1];
-        }
-      }
-      hv[j] = a[0];
-    }
-  }
-#pragma unroll
-  for (int lvl = 0; lvl < 3; ++lvl) {
-    if ((1 << lvl) < G2) {
-#pragma unroll
-      for (int i = 0; i < (4 >> lvl); ++i) hv[i] = hv[2 * i] + hv[2 * i + 1];
-    }
-  }
-  qs_lds[d] = hv[0];
-}
-
-// Pinned dot product of one row: lane j of an LPR-lane team holds dimensions [16j, 16j+16).
-// Local tree over its 16 products (levels 0-3), then xor butterflies across the team.
-template <int LPR>
-__device__ __forceinline__ float row_dot(const float (&x)[16], const float (&qv)[16]) {
-  float p[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) p[i] = x[i] * qv[i];
-#pragma unroll
-  for (int w = 8; w >= 1; w /= 2) {
-#pragma unroll
-    for (int i = 0; i < w; ++i) p[i] = p[2 * i] + p[2 * i + 1];
-  }
-  float s = p[0];
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) s = s + wave_shfl_xor(s, m);
-  return s;
-}
-
-template <typename KT>
-__device__ __forceinline__ void load16(const KT* src, float (&x)[16]);
-
-template <>
-__device__ __forceinline__ void load16<uint16_t>(const uint16_t* src, float (&x)[16]) {
-  const uint4* p = reinterpret_cast<const uint4*>(src);
-  const uint4 a = p[0], c = p[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-  }
-}
-
-template <>
-__device__ __forceinline__ void load16<float>(const float* src, float (&x)[16]) {
-  const float4* p = reinterpret_cast<const float4*>(src);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float4 v = p[c];
-    x[4 * c] = v.x;
-    x[4 * c + 1] = v.y;
-    x[4 * c + 2] = v.z;
-    x[4 * c + 3] = v.w;
-  }
-}
 
 // ------------------------------------------------------------------------------------------------
 // Level-1 unit scores from pooled keys: scores[b][g][n] = dot(qs, ks[b][g][n])

@@ -6,41 +6,16 @@
 // Prefilling-dLLM (abstract): top-K chunks, then token-level sparsity inside each chunk, whose
 // leading beginning-of-sequence token serves as an anchor.
 //
-// One 256-thread workgroup per segment.  Scores become order-preserving 32-bit keys (-0 == +0, NaN
-// lowest); a 4-pass, 8-bit radix select over the keys finds the K-th best key, and ties at that key
-// go to the lower index.  Compaction is an ordered block scan, so the output comes out ascending.
-// Everything is integer work on the keys, hence exact and deterministic.
+// One 256-thread workgroup per segment; the selection itself is select_core (fdl_select.h).
 #include "fdl_device.h"
 #include "fdl_internal.h"
+#include "fdl_select.h"
 
 namespace fdl {
 
 constexpr int kSelThreads = 256;
 constexpr int kMaxSelN = 8192;
 constexpr int kSelPerThread = kMaxSelN / kSelThreads;
-
-// Exclusive scan of one int per thread over the 256-thread block; also returns the total.
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  int off = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) {
-    const int t = tmp[w];
-    if (w < wave) off += t;
-    total += t;
-  }
-  __syncthreads();
-  return off + incl - v;
-}
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int n_units, int unit_log2, const int32_t* __restrict__ sink_pos,
@@ -78,107 +53,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
   __syncthreads();
 
-  // ownership for the ordered phases: thread t owns [t*E, (t+1)*E)
-  const int E = (n + kSelThreads - 1) / kSelThreads;
-  const int i0 = tid * E;
-  int nf_local = 0;
-  for (int e = 0; e < E; ++e) {
-    const int i = i0 + e;
-    if (i < n && ((forced[i >> 5] >> (i & 31)) & 1u)) ++nf_local;
-  }
-  int n_forced;
-  (void)block_excl_scan(nf_local, tmp, n_forced);
-  const int n_elig = n - n_forced;
-  const int kk = top_k < n_elig ? top_k : n_elig;
-
-  // radix select of the kk-th best key among eligible elements
-  uint32_t prefix = 0u, pmask = 0u;
-  int rem = kk;
-  const bool take_all = (kk == n_elig);
-  if (kk > 0 && !take_all) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kSelThreads) {
-        const uint32_t k = keys[i];
-        if (((forced[i >> 5] >> (i & 31)) & 1u) == 0u && (k & pmask) == prefix)
-          atomicAdd(&hist[(k >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l sums bins 255-4l .. 252-4l (descending digits)
-        int cnt[4], s = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          cnt[e] = hist[255 - 4 * tid - e];
-          s += cnt[e];
-        }
-        int incl = s;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int u = __shfl_up(incl, o, 64);
-          if (tid >= o) incl += u;
-        }
-        const uint64_t hit = __ballot(incl >= rem);
-        const int first = __ffsll((unsigned long long)hit) - 1;
-        if (tid == first) {
-          int above = incl - s;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (above + cnt[e] >= rem) {
-              s_digit = (uint32_t)(255 - 4 * tid - e);
-              s_above = above;
-              break;
-            }
-            above += cnt[e];
-          }
-        }
-      }
-      __syncthreads();
-      prefix |= s_digit << shift;
-      pmask |= 255u << shift;
-      rem -= s_above;
-      __syncthreads();
-    }
-  }
-  const uint32_t theta = prefix;
-
-  // ordered compaction: ties at theta go to the lowest indices
-  int tie_local = 0;
-  for (int e = 0; e < E; ++e) {
-    const int i = i0 + e;
-    if (i < n && ((forced[i >> 5] >> (i & 31)) & 1u) == 0u && keys[i] == theta) ++tie_local;
-  }
-  int tie_total;
-  int tie_rank = block_excl_scan(tie_local, tmp, tie_total);
-  uint32_t selbits = 0u;   // E <= 32
-  int sel_local = 0;
-  for (int e = 0; e < E; ++e) {
-    const int i = i0 + e;
-    if (i >= n) break;
-    const bool f = ((forced[i >> 5] >> (i & 31)) & 1u) != 0u;
-    bool take = f;
-    if (!f && kk > 0) {
-      const uint32_t k = keys[i];
-      if (take_all || k > theta) {
-        take = true;
-      } else if (k == theta) {
-        take = tie_rank < rem;
-        ++tie_rank;
-      }
-    }
-    if (take) {
-      selbits |= 1u << e;
-      ++sel_local;
-    }
-  }
-  int sel_total;
-  int pos = block_excl_scan(sel_local, tmp, sel_total);
-
+  const SelScratch scr{hist, tmp, &s_digit, &s_above};
   int32_t* out = sel_idx + seg * (int64_t)max_sel;
   int base = 0;
   if (level2) {
-    const int per_seg = (force_first ? 1 : 0) + kk;
+    const int nf = force_first ? 1 : 0;   // the only forced member at level 2
+    const int per_seg = nf + (top_k < n - nf ? top_k : n - nf);
     out += (int64_t)c * per_seg;
     const int u = cand_idx[seg * n_cand + c];
     const int n_units_all = n_units;
@@ -189,14 +69,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       base = u << unit_log2;
     }
   }
-  for (int e = 0; e < E; ++e) {
-    if ((selbits >> e) & 1u) {
-      const int i = i0 + e;
-      out[pos++] = (base < 0) ? -1 : base + i;
-    }
-  }
+  const SelResult r = select_core<kSelThreads>(keys, forced, n, top_k, scr,
+                                               [&](int pos, int i) { out[pos] = (base < 0) ? -1 : base + i; });
   if (tid == 0 && c == 0) {
-    n_sel[seg] = level2 ? n_cand * ((force_first ? 1 : 0) + kk) : sel_total;
+    n_sel[seg] = level2 ? n_cand * ((force_first ? 1 : 0) + r.kk) : r.total;
   }
 }
 

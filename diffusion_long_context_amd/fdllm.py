@@ -23,7 +23,8 @@ FDL_OK, FDL_EINVAL, FDL_ENOMEM, FDL_EHIP, FDL_EOVERFLOW, FDL_EUNSUPPORTED, FDL_E
 FDL_F32, FDL_BF16 = 0, 1
 
 EXPORTED = (
-    "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_status_string",
+    "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_get_status_bits",
+    "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_predict_queries", "fdl_score_blocks",
     "fdl_select_blocks", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_profile_begin", "fdl_profile_end",
@@ -65,6 +66,7 @@ _SIGS = {
     "fdl_destroy": (_I, [_P]),
     "fdl_set_stream": (_I, [_P, _P]),
     "fdl_get_status": (_I, [_P]),
+    "fdl_get_status_bits": (_I, [_P, ctypes.POINTER(ctypes.c_uint32)]),
     "fdl_status_string": (ctypes.c_char_p, [_I]),
     "fdl_last_error": (ctypes.c_char_p, [_P]),
     "fdl_pool_keys": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _I, _P]),
@@ -184,6 +186,13 @@ class Handle:
     def fdl_get_status(self) -> int:
         self.sync_stream()
         return self.lib.fdl_get_status(self.h)
+
+    def fdl_get_status_bits(self) -> tuple[int, int]:
+        """(status, raw FDL_FLAG_* bits); clears them like fdl_get_status."""
+        self.sync_stream()
+        bits = ctypes.c_uint32(0)
+        st = self.lib.fdl_get_status_bits(self.h, ctypes.byref(bits))
+        return st, bits.value
 
     def fdl_pool_keys(self, g: Geom, k_cache, page_table, unit_tokens: int, ks):
         self.sync_stream()

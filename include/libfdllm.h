@@ -88,6 +88,19 @@ fdl_status fdl_set_stream(fdl_handle h, void* hip_stream);
 /* Synchronise the handle's stream, return the first latched device condition (FDL_EOVERFLOW,
  * FDL_EINDEX) or FDL_OK, and clear it. */
 fdl_status fdl_get_status(fdl_handle h);
+
+/* Device condition bits, as latched by the kernels. */
+#define FDL_FLAG_SINK_OVERFLOW 1u   /* more sinks than max_sinks: list truncated (FDL_EOVERFLOW)     */
+#define FDL_FLAG_CAND_OVERFLOW 2u   /* more sink candidates than the workspace holds (FDL_EOVERFLOW) */
+#define FDL_FLAG_BAD_INDEX 4u       /* unit or page id out of range: row skipped (FDL_EINDEX)       */
+#define FDL_FLAG_SEL_OVERFLOW 8u    /* more selected units than max_sel: list truncated (EOVERFLOW) */
+#define FDL_FLAG_SPLIT_FALLBACK 16u /* informational: a split of fdl_focus_step's fused kernel did  */
+                                    /* not wait for its siblings and scored every block itself;     */
+                                    /* results are unaffected (FDL_OK)                               */
+
+/* Like fdl_get_status, but also stores the raw condition bits (FDL_FLAG_*) in *bits (may be NULL)
+ * before clearing them. */
+fdl_status fdl_get_status_bits(fdl_handle h, uint32_t* bits);
 const char* fdl_status_string(fdl_status s);
 const char* fdl_last_error(fdl_handle h);
 

@@ -81,6 +81,7 @@ def test_focus_step_32k_32layer_as_benchmarked():
             got_pred = host(pred_mask).view(np.uint64)
             got_sinks = (host(sink_pos).copy(), host(n_sinks).copy())
             got_sel = (host(sel_idx).copy(), host(n_sel).copy())
+            got_scores = host(scores).copy()
             got_out = {l: bf16_out_to_f64(outs[l]) for l in CHECK_LAYERS}
 
             sinks = None
@@ -102,6 +103,7 @@ def test_focus_step_32k_32layer_as_benchmarked():
                     assert got_sinks[0][0, :nsb].tolist() == want["sink_pos"][0, :nsb].tolist()
                     sinks = (want["sink_pos"], want["n_sinks"])
                 if l == NL - 1:
+                    assert np.array_equal(got_scores.view(np.uint32), want["scores"].view(np.uint32)), gstep
                     for gh in range(Hkv):
                         w = want["sel"][0][gh].tolist()
                         assert int(got_sel[1][0, gh]) == len(w), (gstep, gh)

@@ -73,57 +73,82 @@ def test_chunked_page_order_bitwise_invariant(h):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(ctx_len=1000, top_k_blocks=32),                  # fewer blocks than the top-K: list < hint
-    dict(ctx_len=6000, top_k_blocks=40),                  # sink block outside the top-K: list > hint
+    dict(ctx_len=1000, top_k_blocks=32),                  # fewer blocks than the top-K
+    dict(ctx_len=6000, top_k_blocks=40),                  # sink block outside the top-K
     dict(ctx_len=6000, top_k_blocks=40, sink_kind="shared_dir_x8"),
-], ids=["list-below-hint", "list-above-hint", "scattered-sinks"])
-def test_focus_step_driver(h, kw):
+    dict(ctx_len=6000, top_k_blocks=40, n_kv_heads=2),    # grouped-query: the unfused chain
+    dict(batch=8, n_q_heads=32, n_kv_heads=32, ctx_len=2048, top_k_blocks=8),   # one split per head
+    dict(ctx_len=41000, top_k_blocks=48),                 # 641 blocks: the radix selection path
+    dict(ctx_len=6000, top_k_blocks=40, spin_limit=0),    # splits never wait: redundant scoring
+], ids=["list-below-topk", "list-above-topk", "scattered-sinks", "gqa4", "one-split", "641-blocks",
+        "no-wait-fallback"])
+def test_focus_step_driver(kw, monkeypatch):
     """fdl_focus_step (one call: predict, then dense / source / reuse / reuse layers) against the
-    oracle layer by layer; its attention launches take the top-K size as their tile-partition hint."""
+    oracle layer by layer.  With one q-head per KV head the sparse layers run scoring, selection and
+    attention as one fused kernel whose splits share the scoring; with grouped-query heads as three
+    launches."""
+    require_gpu()
+    from diffusion_long_context_amd import Handle
     from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
                                                   fdl_focus_params)
     from diffusion_long_context_amd.step import geom_for
     from gpu_util import bf16_out_to_f64, dev, host
-    cfg = get_config(1).with_(n_q_heads=8, n_kv_heads=8, **kw)
+    kw = dict(kw)
+    spin = kw.pop("spin_limit", None)
+    if spin is not None:
+        monkeypatch.setenv("FDL_SPIN_LIMIT", str(spin))   # read when the handle is created
+    cfg = get_config(1).with_(**dict(dict(n_q_heads=8, n_kv_heads=8), **kw))
     g = geom_for(cfg)
     B, Hq, Hkv, D, T, nb, ms = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len,
                                 cfg.n_blk, cfg.max_sel_blocks)
     modes = ["dense", "source", "reuse", "reuse"]
     code = {"dense": FDL_LAYER_DENSE, "source": FDL_LAYER_SOURCE, "reuse": FDL_LAYER_REUSE}
     xs = [make_single(cfg, layer=l) for l in range(len(modes))]
-    t = [{k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec")} for x in xs]
-    ks = [torch.zeros((B, Hkv, nb, D), dtype=torch.float32, device="cuda") for _ in modes]
-    outs = [torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device="cuda") for _ in modes]
-    for l in range(len(modes)):
-        h.fdl_pool_keys(g, t[l]["k"], None, cfg.kv_block, ks[l])
-    pm = torch.zeros(B, dtype=torch.int64, device="cuda")
-    npd = torch.zeros(B, dtype=torch.int32, device="cuda")
-    sc = torch.zeros((B, Hkv, nb), dtype=torch.float32, device="cuda")
-    sp = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device="cuda")
-    nsk = torch.zeros(B, dtype=torch.int32, device="cuda")
-    sel = torch.zeros((B, Hkv, ms), dtype=torch.int32, device="cuda")
-    nsel = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
-    params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, ms, cfg.sink_tau)
-    table = h.make_layers(g, [dict(q=t[l]["q"], k_cache=t[l]["k"], v_cache=t[l]["v"], k_dec=t[l]["k_dec"],
-                                   v_dec=t[l]["v_dec"], ks=ks[l], out=outs[l], mode=code[m])
-                              for l, m in enumerate(modes)])
-    x0 = xs[0]
-    h.fdl_focus_step(g, params, dev(x0["prev_conf"]), dev(x0["masked"]), table, pm, npd, sc, sp, nsk, sel, nsel)
-    torch.cuda.synchronize()
-    assert h.fdl_get_status() == 0
-    sinks = None
-    for l, m in enumerate(modes):
-        x = dict(xs[l], prev_conf=x0["prev_conf"], masked=x0["masked"])
-        want = focus_layer_step(cfg, x, m, sinks=sinks)
-        if m == "source":
-            assert want["sink_margin"] > 1e-4 * cfg.sink_tau
-            sinks = (want["sink_pos"], want["n_sinks"])
-            nsb = int(want["n_sinks"][0])
-            assert int(host(nsk)[0]) == nsb
-            assert host(sp)[0, :nsb].tolist() == want["sink_pos"][0, :nsb].tolist()
-        if l == len(modes) - 1:
-            for gh in range(Hkv):
-                w = want["sel"][0][gh].tolist()
-                assert int(host(nsel)[0, gh]) == len(w)
-                assert host(sel)[0, gh, : len(w)].tolist() == w
-        assert_close(bf16_out_to_f64(outs[l]), want["out"], f"layer {l} ({m})")
+    h = Handle(workspace_bytes=512 << 20)
+    try:
+        t = [{k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec")} for x in xs]
+        ks = [torch.zeros((B, Hkv, nb, D), dtype=torch.float32, device="cuda") for _ in modes]
+        outs = [torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device="cuda") for _ in modes]
+        for l in range(len(modes)):
+            h.fdl_pool_keys(g, t[l]["k"], None, cfg.kv_block, ks[l])
+        pm = torch.zeros(B, dtype=torch.int64, device="cuda")
+        npd = torch.zeros(B, dtype=torch.int32, device="cuda")
+        sc = torch.zeros((B, Hkv, nb), dtype=torch.float32, device="cuda")
+        sp = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device="cuda")
+        nsk = torch.zeros(B, dtype=torch.int32, device="cuda")
+        sel = torch.zeros((B, Hkv, ms), dtype=torch.int32, device="cuda")
+        nsel = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+        params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, ms,
+                                  cfg.sink_tau)
+        table = h.make_layers(g, [dict(q=t[l]["q"], k_cache=t[l]["k"], v_cache=t[l]["v"],
+                                       k_dec=t[l]["k_dec"], v_dec=t[l]["v_dec"], ks=ks[l], out=outs[l],
+                                       mode=code[m]) for l, m in enumerate(modes)])
+        x0 = xs[0]
+        h.fdl_focus_step(g, params, dev(x0["prev_conf"]), dev(x0["masked"]), table, pm, npd, sc, sp, nsk,
+                         sel, nsel)
+        torch.cuda.synchronize()
+        status, bits = h.fdl_get_status_bits()
+        assert status == 0
+        # FDL_FLAG_SPLIT_FALLBACK: a fused split scored every block itself (only when it may not wait)
+        assert bits == (16 if spin == 0 else 0), bits
+        sinks = None
+        for l, m in enumerate(modes):
+            x = dict(xs[l], prev_conf=x0["prev_conf"], masked=x0["masked"])
+            want = focus_layer_step(cfg, x, m, sinks=sinks)
+            if m == "source":
+                assert want["sink_margin"] > 1e-4 * cfg.sink_tau
+                sinks = (want["sink_pos"], want["n_sinks"])
+                for b in range(B):
+                    nsb = int(want["n_sinks"][b])
+                    assert int(host(nsk)[b]) == nsb
+                    assert host(sp)[b, :nsb].tolist() == want["sink_pos"][b, :nsb].tolist()
+            if l == len(modes) - 1:
+                assert np.array_equal(host(sc).view(np.uint32), want["scores"].view(np.uint32))
+                for b in range(B):
+                    for gh in range(Hkv):
+                        w = want["sel"][b][gh].tolist()
+                        assert int(host(nsel)[b, gh]) == len(w), (b, gh)
+                        assert host(sel)[b, gh, : len(w)].tolist() == w, (b, gh)
+            assert_close(bf16_out_to_f64(outs[l]), want["out"], f"layer {l} ({m})")
+    finally:
+        h.close()
