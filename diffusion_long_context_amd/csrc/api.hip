@@ -141,7 +141,7 @@ fdl_status run_sinks(fdl_handle h, const Geom& g, const void* q, const uint64_t*
   ProfScope ps(h, FDL_PROF_SINKS);
   return hip_status(h, fdl::launch_sinks(h->stream, g, q, pred_mask, k_cache, k_dec, tau, max_sinks,
                                          sink_pos, n_sinks, h->scratch, ns, cap, h->status,
-                                         h->num_cus),
+                                         h->num_cus, h->tickets, h->sink_area),
                     "sinks launch");
 }
 
@@ -252,6 +252,7 @@ fdl_status fdl_create(fdl_handle* out, void* hip_stream, size_t workspace_bytes)
   h->status = reinterpret_cast<uint32_t*>(h->ws);
   h->tickets = reinterpret_cast<uint32_t*>(h->ws + fdl::kTicketOffset);
   h->barriers = reinterpret_cast<uint32_t*>(h->ws + fdl::kBarrierOffset);
+  h->sink_area = h->ws + fdl::kSinkOffset;
   {
     const char* e = getenv("FDL_SPIN_LIMIT");
     h->spin_limit = e ? atoi(e) : 200000;

@@ -33,6 +33,7 @@
 #include "fdl_internal.h"
 #include "fdl_score.h"
 #include "fdl_select.h"
+#include "fdl_stream.h"
 
 namespace fdl {
 
@@ -59,30 +60,19 @@ struct MhaParams {
   FusedSelect fs;
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 constexpr int kMhaWaves = 8;
 constexpr int kTileTok = 32;
 
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 template <int D>
 struct MhaShape {
-  static constexpr int PROW = D / 8;                 // 16-byte chunks per row
-  static constexpr int ROWS_PER_INSTR = 64 / PROW;   // rows one 1 KiB fetch covers
+  static constexpr int PROW = RowChunks<D>::PROW;                     // 16-byte chunks per row
+  static constexpr int ROWS_PER_INSTR = RowChunks<D>::ROWS_PER_INSTR;   // rows one 1 KiB fetch covers
   static constexpr int INSTR = kTileTok / ROWS_PER_INSTR;   // fetches per tile for K (same for V)
   static constexpr int HALF = kTileTok * D;          // elements of K (or V) per tile
   static constexpr int SLOT = 2 * HALF;              // elements per wave slot
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
 };
-
-// LDS chunk swizzle: chunk c of row r is stored at chunk slot c ^ swz(r).  swz permutes the low 4
-// bits of the row (bits 2 and 3 swapped) so that (a) the 16 rows read together by the K-operand
-// loads hit 16 different slots and (b) rows r and r + 4, which the two lane halves read together
-// for V, fall in different halves of the row's banks.
-__device__ __forceinline__ int swz(int r) { return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8); }
 
 // Offset type: contiguous caches address rows relative to the head's base with 32 bits
 // (L < 2^24, D <= 128); pages can sit anywhere in the pool and need 64 bits.
@@ -162,6 +152,7 @@ __device__ __forceinline__ void mha_load_rows(const float* __restrict__ ksh, int
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int ps = 0; ps < kScoreBatch; ++ps) {
+    if (base + ps * RPP >= rb) break;   // uniform: no row of this pass is wanted
     int r = base + ps * RPP + wave * RPW + lane / LPR;
     r = r < rb ? r : rb - 1;
     load16<float>(ksh + (int64_t)r * D + 16 * (lane % LPR), x[ps]);
@@ -176,6 +167,7 @@ __device__ __forceinline__ void mha_dot_rows(const float (&x)[kScoreBatch][16], 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int ps = 0; ps < kScoreBatch; ++ps) {
+    if (base + ps * RPP >= rb) break;   // uniform
     const int r = base + ps * RPP + wave * RPW + lane / LPR;
     const float sc = row_dot<LPR>(x[ps], qv);
     if (lane % LPR == 0 && r < rb) {
@@ -359,10 +351,10 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
   }
 #pragma unroll
   for (int j = 0; j < NI; ++j)
-    __builtin_amdgcn_global_load_lds((const void*)(kb + off[j]), (lds_void_t*)(slot + j * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(kb + off[j]), (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
 #pragma unroll
   for (int j = 0; j < NI; ++j)
-    __builtin_amdgcn_global_load_lds((const void*)(vb + off[j]), (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(vb + off[j]), (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, kStreamPolicy);
   return okm;
 }
 
@@ -512,7 +504,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
       sacc[r] = x;
       mx = fmaxf(mx, x);
     }
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    mx = fmaxf(mx, lane_xor32f(mx));
     const float m_new = fmaxf(m_run, mx);
     if (m_new != -__builtin_inff()) {
       const float alpha = exp2f(m_run - m_new);
@@ -523,7 +515,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
         sacc[r] = pr;
         rs += pr;
       }
-      rs += wave_shfl_xor(rs, 32);
+      rs += lane_xor32f(rs);
       l_run = l_run * alpha + rs;
       m_run = m_new;
 #pragma unroll

@@ -58,6 +58,25 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Value of lane (lane ^ J) for a compile-time J: quad permutes for 1 and 2, swizzles (within 32
+// lanes) for 4, 8 and 16, the half swap for 32.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (J == 4 || J == 8 || J == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
+  else if constexpr (J == 32) {
+    // swap of the two 32-lane halves; in every lane one of the two results is the lane's own value
+    // and the other the partner's (when they are equal, either is right)
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (r[0] == v) ? r[1] : r[0];
+  } else {
+    return (uint32_t)__shfl_xor((int)v, J, 64);
+  }
+}
+
+__device__ __forceinline__ float lane_xor32f(float v) { return __uint_as_float(lane_xor<32>(__float_as_uint(v))); }
+
 __device__ __forceinline__ void latch(uint32_t* status, uint32_t bit) {
   atomicOr(status, bit);
 }

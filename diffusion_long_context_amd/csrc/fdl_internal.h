@@ -19,6 +19,7 @@ struct fdl_ctx {
   uint32_t* tickets;     // split-merge tickets, kSyncStride apart per (b, head); left at zero
   uint32_t* barriers;    // split barriers of the fused kernel, kSyncStride apart per (b, head)
   int spin_limit;        // polls a fused-kernel split waits for its siblings (FDL_SPIN_LIMIT)
+  char* sink_area;       // header area of the sink detection state
   char* scratch;         // general scratch after the fixed header
   size_t scratch_bytes;
   char last_error[256];
@@ -45,7 +46,11 @@ constexpr size_t kTicketOffset = 4096;
 constexpr int kMaxSplitSegs = 256;
 constexpr int kSyncStride = 64;                  // uint32 words between two heads' sync words
 constexpr size_t kBarrierOffset = kTicketOffset + (size_t)kMaxSplitSegs * kSyncStride * sizeof(uint32_t);
-static_assert(kBarrierOffset + (size_t)kMaxSplitSegs * kSyncStride * sizeof(uint32_t) <= kHeaderBytes,
+// Sink detection keeps its candidate counts and bitmap here between calls (zero on entry, zeroed
+// again by the compaction) when they fit.
+constexpr size_t kSinkOffset = 256u << 10;
+constexpr size_t kSinkAreaBytes = kHeaderBytes - kSinkOffset;
+static_assert(kBarrierOffset + (size_t)kMaxSplitSegs * kSyncStride * sizeof(uint32_t) <= kSinkOffset,
               "header too small");
 
 // Optional timing of one launcher call: a and b become the start and end of the launched work
@@ -96,7 +101,8 @@ size_t sink_scratch_bytes(const Geom& g, int* n_splits, int* cand_cap);
 hipError_t launch_sinks(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                         const void* k, const void* k_dec, float tau, int max_sinks,
                         int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
-                        int cand_cap, uint32_t* status, int num_cus);
+                        int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
+                        char* sink_area);
 
 hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int n_units,
                          int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,

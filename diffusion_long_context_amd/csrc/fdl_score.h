@@ -129,8 +129,12 @@ __device__ __forceinline__ float row_dot(const float (&x)[16], const float (&qv)
     for (int i = 0; i < w; ++i) p[i] = p[2 * i] + p[2 * i + 1];
   }
   float s = p[0];
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) s = s + wave_shfl_xor(s, m);
+  // cross-lane tree levels; a + b and b + a round alike, so both lanes of a pair hold the same sum
+  if constexpr (LPR > 1) s = s + __uint_as_float(lane_xor<1>(__float_as_uint(s)));
+  if constexpr (LPR > 2) s = s + __uint_as_float(lane_xor<2>(__float_as_uint(s)));
+  if constexpr (LPR > 4) s = s + __uint_as_float(lane_xor<4>(__float_as_uint(s)));
+  if constexpr (LPR > 8) s = s + __uint_as_float(lane_xor<8>(__float_as_uint(s)));
+  static_assert(LPR <= 16, "row_dot: at most 16 lanes per row");
   return s;
 }
 

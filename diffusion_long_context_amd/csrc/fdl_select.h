@@ -160,16 +160,6 @@ __device__ SelResult select_core(const uint32_t* keys, const uint32_t* forced, i
 
 namespace fdl {
 
-// Value of lane (lane ^ J) for a compile-time J: quad permutes for 1 and 2, swizzles (within 32
-// lanes) for 4, 8 and 16, a permute through LDS for 32.
-template <int J>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-  else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-  else if constexpr (J == 4 || J == 8 || J == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
-  else return (uint32_t)__shfl_xor((int)v, J, 64);
-}
-
 // One compare-exchange step of a descending bitonic sort across the 64 lanes of a wave.
 template <int K, int J>
 __device__ __forceinline__ void bitonic_step(uint64_t& v, int lane) {

@@ -7,15 +7,17 @@
 // block's own tokens; a cached token whose mean weight over the predicted positions reaches tau for
 // some head is a sink; the union over heads is the sequence's sink list (ascending).
 //
-// One pass over K (the only full-K read of a step): each wave streams 64-token tiles through bf16
+// One pass over K (the only full-K read of a step): each wave streams 32-token tiles through bf16
 // MFMA (S^T = K Q^T) and keeps a running log-sum-exp per query.  Because a running log-sum-exp never
 // exceeds the final one, the mass a token gets under the running statistics is an upper bound of
 // its true mass, so every token whose bound reaches tau (less a small rounding margin) is recorded
-// as a candidate.  After the pass the partial statistics are merged into the exact log-sum-exp, the
-// few candidates are re-scored exactly in float32, and survivors are set in a per-sequence bitmap
-// that is compacted into the ascending sink list.
+// as a candidate.  In the same kernel, the last workgroup of each head merges the partial
+// statistics into the exact log-sum-exp, re-scores the head's few candidates in float32 and sets
+// the survivors in a per-sequence bitmap; a second kernel compacts the bitmap into the ascending
+// sink list.
 #include "fdl_device.h"
 #include "fdl_internal.h"
+#include "fdl_stream.h"
 
 namespace fdl {
 
@@ -39,182 +41,244 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 constexpr float kCandSlack = 0.999f;   // candidates use tau * (1 - 1e-3): absorbs float32 rounding
+constexpr int kSinkWaves = 4;
+constexpr int kSinkTile = 32;           // tokens per tile
 
 struct SinkParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* k_dec;
   const uint64_t* pred_mask;
-  float2* stats;         // [B][Hq][n_parts][32]  (running max in log2 units, running sum)
-  float* lse2;           // [B][Hq][32]
-  uint32_t* cand_count;  // [B]
-  uint32_t* cand;        // [B][cand_cap]  (h << 24 | t)
-  uint32_t* bitmap;      // [B][words]
+  float2* stats;         // [B * Hq][n_splits * 4][32]  (running max in log2 units, running sum)
+  uint32_t* cand_count;  // [B * Hq], zero on entry; sink_compact_kernel zeroes it again
+  uint32_t* cand;        // [B * Hq][cand_cap]  token positions
+  uint32_t* bitmap;      // [B][words], zero on entry; sink_compact_kernel zeroes it again
+  uint32_t* tickets;     // per (b, q-head), kSyncStride apart; left at zero
   uint32_t* status;
-  int Hq, Hkv, G, T, L, n_splits, cand_cap, words;
+  int Hq, Hkv, G, T, L, n_splits, n_segs, cand_cap, words;
   float scale_log2, tau;
 };
 
+// One pass over K per (sequence, q-head), split over n_splits workgroups of 4 waves that all run on
+// one XCD (workgroup id mod 8).  Each wave streams 32-token tiles of K from HBM into its own LDS slot
+// with LDS DMA (coalesced 1 KiB fetches), copies a tile into MFMA operand registers and fetches the
+// next one into the slot while the current one is scored.  The last
+// split of a head to finish (ticket) merges the partial statistics into the exact log-sum-exp per
+// query, re-scores the head's candidates in float32 and sets the survivors in the sequence's bitmap.
 template <int D>
-__global__ __launch_bounds__(256) void sink_scan_kernel(const SinkParams p) {
+__global__ __launch_bounds__(kSinkWaves * 64, 3) void sink_scan_kernel(const SinkParams p) {
   constexpr int KS = D / 16;
-  __shared__ float ebuf[4][64][33];
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  constexpr int NT = kSinkWaves * 64;
+  using RC = RowChunks<D>;
+  constexpr int PROW = RC::PROW, RPI = RC::ROWS_PER_INSTR, NI = kSinkTile / RPI;
+  __shared__ __attribute__((aligned(1024))) uint16_t kslot[kSinkWaves * kSinkTile * D];
+  __shared__ float ebuf[kSinkWaves][kSinkTile][33];
+  __shared__ float2 s_part[8][32];
+  __shared__ float s_lse[32];
+  __shared__ uint32_t s_ticket;
+  const int NS = p.n_splits;
+  const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
+  const int s = xslot % NS;
+  const int seg = xcd + 8 * (xslot / NS);
+  if (seg >= p.n_segs) return;
+  const int b = seg / p.Hq, h = seg % p.Hq, g = h / p.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
-  const int g = h / p.G;
   const uint64_t pred = p.pred_mask[b];
   const int n_pred = __popcll(pred);
-  const int n_parts = p.n_splits * 4;
-  float2* st_out = p.stats + (((int64_t)b * p.Hq + h) * n_parts + s * 4 + wave) * 32;
+  const int n_parts = NS * kSinkWaves;
   float m_run = -__builtin_inff(), l_run = 0.f;
-  if (n_pred > 0) {
+  const uint16_t* kdec = p.k_dec + ((int64_t)b * p.Hkv + g) * p.T * D;
+  const uint16_t* kctx = p.k + ((int64_t)b * p.Hkv + g) * (int64_t)p.L * D;
+  if (n_pred > 0) {   // uniform
     const bool qlive = ql < p.T && ((pred >> ql) & 1ull);
     bf16x8 qf[KS];
-    const uint16_t* qrow = p.q + (((int64_t)b * p.Hq + h) * p.T + (ql < p.T ? ql : 0)) * D + hh * (D / 2);
+    {
+      const uint16_t* qrow = p.q + ((int64_t)seg * p.T + (ql < p.T ? ql : 0)) * D + hh * (D / 2);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (ql < p.T) v = *reinterpret_cast<const uint4*>(qrow + ks * 8);
-      qf[ks] = as_bf16x8(v);
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = *reinterpret_cast<const uint4*>(qrow + ks * 8);
+        if (ql >= p.T) v = make_uint4(0u, 0u, 0u, 0u);
+        qf[ks] = as_bf16x8(v);
+      }
     }
     const float inv_np = 1.f / (float)n_pred;
-    const int n_tiles = 1 + (p.L + 63) / 64;
-    const int e0 = (int)((int64_t)n_tiles * s / p.n_splits);
-    const int e1 = (int)((int64_t)n_tiles * (s + 1) / p.n_splits);
-    const uint16_t* kdec = p.k_dec + ((int64_t)b * p.Hkv + g) * p.T * D;
-    const uint16_t* kctx = p.k + ((int64_t)b * p.Hkv + g) * (int64_t)p.L * D;
-    for (int e = e0 + wave; e < e1; e += 4) {
-      // A operand straight from HBM: lane (token, hh) reads 8 dims per k-step
-      uint4 ka[2][KS];
+    const int n_tiles = 1 + (p.L + kSinkTile - 1) / kSinkTile;
+    const int e0 = (int)((int64_t)n_tiles * s / NS);
+    const int e1 = (int)((int64_t)n_tiles * (s + 1) / NS);
+    // tile e -> the wave's slot; rows are clamped so that every fetch is in bounds
+    uint16_t* slot = kslot + wave * kSinkTile * D;
+    auto issue = [&](int e) {
+      const int rsub = lane / PROW, sc = lane % PROW;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int r = st * 32 + ql;
-        const uint16_t* row = nullptr;
-        if (e == 0) {
-          if (r < p.T) row = kdec + (int64_t)r * D;
-        } else {
-          const int t = (e - 1) * 64 + r;
-          if (t < p.L) row = kctx + (int64_t)t * D;
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[st][ks] = row ? *reinterpret_cast<const uint4*>(row + hh * (D / 2) + ks * 8)
-                           : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < NI; ++j) {
+        const int r = j * RPI + rsub;
+        const int t = (e - 1) * kSinkTile + r;
+        const uint16_t* row = (e == 0) ? kdec + (int64_t)(r < p.T ? r : p.T - 1) * D
+                                       : kctx + (int64_t)(t < p.L ? t : p.L - 1) * D;
+        __builtin_amdgcn_global_load_lds((const void*)(row + (sc ^ (swz(r) & (PROW - 1))) * 8),
+                                         (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
       }
-      const int nvalid = (e == 0) ? p.T : min(64, p.L - (e - 1) * 64);
-      f32x16 sacc[2];
+    };
+    const int swz_k = swz(ql) & (PROW - 1);
+    // upper-bound masses of a scored tile under the current running statistics, summed over the
+    // predicted queries; tokens whose bound reaches tau become candidates
+    const float log2_thr = __log2f(p.tau * kCandSlack);
+    auto eval_tile = [&](const f32x16& sc, int et, int nv) {
+      const float lse = m_run + __log2f(l_run);
+      // screen: a token's mean over the predicted queries reaches the threshold only if some single
+      // query's bound does, so a tile where no (query, token) bound does is skipped without the
+      // transpose (the usual case: only sink tiles pass)
+      bool hot = false;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int r = 0; r < 16; ++r) hot = hot || (qlive && sc[r] - lse >= log2_thr);
+      if (__ballot(hot) == 0ull) return;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[st][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc[st] = mfma32(as_bf16x8(ka[st][ks]), qf[ks], sacc[st]);
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+        ebuf[wave][row][ql] = qlive ? exp2f(sc[r] - lse) : 0.f;
       }
+      wave_lds_sync();
+      // lane (row ql, half hh) sums queries 16 hh .. 16 hh + 15 of token row ql
+      float u = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) u += ebuf[wave][ql][16 * hh + j];
+      u += lane_xor32f(u);
+      u *= inv_np;
+      if (hh == 0 && ql < nv && u >= p.tau * kCandSlack) {
+        const uint32_t idx = atomicAdd(&p.cand_count[seg], 1u);
+        if ((int)idx < p.cand_cap) p.cand[(int64_t)seg * p.cand_cap + idx] = (uint32_t)((et - 1) * kSinkTile + ql);
+        else latch(p.status, ST_CAND_OVERFLOW);
+      }
+      wave_lds_sync();
+    };
+    f32x16 sprev;
+    int prev_e = 0, prev_nvalid = 0;   // prev_e == 0: nothing pending (tile 0 is never evaluated)
+    int e = e0 + wave;
+    if (e < e1) issue(e);
+    for (; e < e1; e += kSinkWaves) {
+      wait_vm0();   // this tile's fetches have landed
+      // lane (token ql, half hh): dims hh*D/2 + 8 ks .. +8 of its token, as the MFMA A operand
+      uint4 ka[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = hh * (PROW / 2) + ks;
+        ka[ks] = *reinterpret_cast<const uint4*>(slot + ql * D + ((c ^ swz_k) * 8));
+      }
+      wait_lgkm0();
+      if (e + kSinkWaves < e1) issue(e + kSinkWaves);   // next tile flies while this one is scored
+      const int nvalid = (e == 0) ? p.T : min(kSinkTile, p.L - (e - 1) * kSinkTile);
+      f32x16 sacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc = mfma32(as_bf16x8(ka[ks]), qf[ks], sacc);
+      // register r: token 8*(r/4) + 4*hh + r%4 of the tile, query ql
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = st * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          float x = sacc[st][r] * p.scale_log2;
-          if (row >= nvalid) x = -__builtin_inff();
-          sacc[st][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+        float x = sacc[r] * p.scale_log2;
+        if (row >= nvalid) x = -__builtin_inff();
+        sacc[r] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, lane_xor32f(mx));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);
       float rs = 0.f;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rs += exp2f(sacc[st][r] - m_new);
-      rs += wave_shfl_xor(rs, 32);
+      for (int r = 0; r < 16; ++r) rs += exp2f(sacc[r] - m_new);
+      rs += lane_xor32f(rs);
       l_run = l_run * alpha + rs;
       m_run = m_new;
-      if (e == 0) continue;   // the block's own tokens are never sinks
-      // upper-bound masses under the running statistics, summed over predicted queries
-      const float lse = m_run + __log2f(l_run);
+      // candidates of the previous tile, bounded with the statistics that now include this one
+      // (a one-tile delay, so that no bound rests on fewer than two tiles of tokens)
+      if (prev_e > 0) eval_tile(sprev, prev_e, prev_nvalid);
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = st * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          ebuf[wave][row][ql] = qlive ? exp2f(sacc[st][r] - lse) : 0.f;
-        }
-      wave_lds_sync();
-      float u = 0.f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) u += ebuf[wave][lane][j];
-      u *= inv_np;
-      if (lane < nvalid && u >= p.tau * kCandSlack) {
-        const int t = (e - 1) * 64 + lane;
-        const uint32_t idx = atomicAdd(&p.cand_count[b], 1u);
-        if ((int)idx < p.cand_cap)
-          p.cand[(int64_t)b * p.cand_cap + idx] = ((uint32_t)h << 24) | (uint32_t)t;
-        else
-          latch(p.status, ST_CAND_OVERFLOW);
-      }
-      wave_lds_sync();
+      for (int r = 0; r < 16; ++r) sprev[r] = sacc[r];
+      prev_e = e;
+      prev_nvalid = nvalid;
     }
+    if (prev_e > 0) eval_tile(sprev, prev_e, prev_nvalid);   // the last tile, under the final stats
   }
-  if (hh == 0) st_out[ql] = make_float2(m_run, l_run);
-}
+  if (hh == 0) p.stats[((int64_t)seg * n_parts + s * kSinkWaves + wave) * 32 + ql] = make_float2(m_run, l_run);
 
-__global__ __launch_bounds__(64) void sink_lse_kernel(const SinkParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, q = threadIdx.x;
-  if (q >= 32) return;
-  const int n_parts = p.n_splits * 4;
-  const float2* st = p.stats + ((int64_t)b * p.Hq + h) * n_parts * 32 + q;
-  float M = -__builtin_inff();
-  for (int i = 0; i < n_parts; ++i) M = fmaxf(M, st[i * 32].x);
-  float S = 0.f;
-  for (int i = 0; i < n_parts; ++i) {
-    const float2 v = st[i * 32];
-    if (v.y > 0.f) S += v.y * exp2f(v.x - M);
+  // ---- the last split of the head (same XCD, so the partials are in its L2) finishes it ----
+  if (NS > 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg * kSyncStride], 1u);
+    __syncthreads();
+    if (s_ticket != (uint32_t)(NS - 1)) return;
+    asm volatile("buffer_inv sc0" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    if (tid == 0) p.tickets[seg * kSyncStride] = 0u;
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
-  p.lse2[((int64_t)b * p.Hq + h) * 32 + q] = M + __log2f(S);
-}
-
-// One wave per candidate: lane q (a predicted position) re-scores q . k_t in float32.
-template <int D>
-__global__ __launch_bounds__(256) void sink_final_kernel(const SinkParams p) {
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t pred = p.pred_mask[b];
-  const int n_pred = __popcll(pred);
   if (n_pred == 0) return;
-  int count = (int)p.cand_count[b];
+  {
+    // exact log-sum-exp per query: thread (q, j) merges parts j, j + 8, ...; then 8 -> 1
+    const int q = tid & 31, j = tid >> 5;
+    float M = -__builtin_inff(), S = 0.f;
+    for (int i = j; i < n_parts; i += 8) {
+      const float2 v = p.stats[((int64_t)seg * n_parts + i) * 32 + q];
+      if (v.y > 0.f) {
+        const float mn = fmaxf(M, v.x);
+        S = S * exp2f(M - mn) + v.y * exp2f(v.x - mn);
+        M = mn;
+      }
+    }
+    s_part[j][q] = make_float2(M, S);
+    __syncthreads();
+    if (tid < 32) {
+      float M2 = -__builtin_inff(), S2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float2 v = s_part[i][tid];
+        if (v.y > 0.f) {
+          const float mn = fmaxf(M2, v.x);
+          S2 = S2 * exp2f(M2 - mn) + v.y * exp2f(v.x - mn);
+          M2 = mn;
+        }
+      }
+      s_lse[tid] = M2 + __log2f(S2);
+    }
+    __syncthreads();
+  }
+  // re-score this head's candidates exactly: one wave per candidate, lane = predicted position
+  int count = (int)__hip_atomic_load(&p.cand_count[seg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   count = count < p.cand_cap ? count : p.cand_cap;
-  for (int c = blockIdx.x * 4 + wave; c < count; c += gridDim.x * 4) {
-    const uint32_t code = p.cand[(int64_t)b * p.cand_cap + c];
-    const int h = (int)(code >> 24), t = (int)(code & 0xFFFFFFu);
-    const int g = h / p.G;
+  const uint16_t* qh = p.q + (int64_t)seg * p.T * D;
+  for (int c = wave; c < count; c += kSinkWaves) {
+    const int t = (int)p.cand[(int64_t)seg * p.cand_cap + c];
     float e = 0.f;
     if (lane < p.T && ((pred >> lane) & 1ull)) {
-      const uint16_t* qr = p.q + (((int64_t)b * p.Hq + h) * p.T + lane) * D;
-      const uint16_t* kr = p.k + (((int64_t)b * p.Hkv + g) * p.L + t) * D;
+      const uint16_t* qr = qh + (int64_t)lane * D;
+      const uint16_t* kr = kctx + (int64_t)t * D;
       float acc = 0.f;
 #pragma unroll 8
       for (int d = 0; d < D; d += 8) {
         const uint4 qa = *reinterpret_cast<const uint4*>(qr + d);
-        const uint4 ka = *reinterpret_cast<const uint4*>(kr + d);
+        const uint4 ka2 = *reinterpret_cast<const uint4*>(kr + d);
         const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
-        const uint32_t kw[4] = {ka.x, ka.y, ka.z, ka.w};
+        const uint32_t kw[4] = {ka2.x, ka2.y, ka2.z, ka2.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc += bf16_bits_to_f32(qw[i] & 0xFFFFu) * bf16_bits_to_f32(kw[i] & 0xFFFFu);
           acc += bf16_bits_to_f32(qw[i] >> 16) * bf16_bits_to_f32(kw[i] >> 16);
         }
       }
-      e = exp2f(acc * p.scale_log2 - p.lse2[((int64_t)b * p.Hq + h) * 32 + lane]);
+      e = exp2f(acc * p.scale_log2 - s_lse[lane]);
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) e += wave_shfl_xor(e, o);
     if (lane == 0 && e / (float)n_pred >= p.tau)
       atomicOr(&p.bitmap[(int64_t)b * p.words + (t >> 5)], 1u << (t & 31));
   }
+  (void)NT;
 }
 
 // float32 path (small workloads): thread = query row; two passes over the keys.
@@ -288,11 +352,12 @@ __global__ __launch_bounds__(64) void sink_f32_kernel(const float* __restrict__ 
 }
 
 // Bitmap -> ascending sink positions; one workgroup per sequence.
-__global__ __launch_bounds__(256) void sink_compact_kernel(const uint32_t* __restrict__ bitmap,
-                                                           int words, int max_sinks,
+__global__ __launch_bounds__(256) void sink_compact_kernel(uint32_t* bitmap_rw, int words, int max_sinks,
                                                            int32_t* __restrict__ sink_pos,
                                                            int32_t* __restrict__ n_sinks,
+                                                           uint32_t* __restrict__ cand_count, int n_heads,
                                                            uint32_t* __restrict__ status) {
+  const uint32_t* bitmap = bitmap_rw;
   __shared__ int tmp[4];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -329,34 +394,56 @@ __global__ __launch_bounds__(256) void sink_compact_kernel(const uint32_t* __res
   }
   // pad the rest of the list with -1 so stale entries never look like sinks
   for (int i = total + tid; i < max_sinks; i += 256) sink_pos[(int64_t)b * max_sinks + i] = -1;
+  // leave the bitmap and the candidate counts of this sequence at zero for the next detection
+  for (int i = 0; i < per; ++i)
+    if (w0 + i < words) bitmap_rw[(int64_t)b * words + w0 + i] = 0u;
+  for (int i = tid; i < n_heads; i += 256) cand_count[(int64_t)b * n_heads + i] = 0u;
   if (tid == 0) {
     n_sinks[b] = total < max_sinks ? total : max_sinks;
     if (total > max_sinks) latch(status, ST_SINK_OVERFLOW);
   }
 }
 
+int sink_splits(const Geom& g) {
+  const int n_tiles = 1 + (g.L + kSinkTile - 1) / kSinkTile;
+  const long long segs = (long long)g.B * g.Hq;
+  if (segs > kMaxSplitSegs) return 1;
+  // about three 4-wave workgroups per CU (the kernel's occupancy) over all (sequence, q-head) pairs
+  int s = (int)((3LL * 256 + segs - 1) / segs);
+  // at least 4 tiles per wave, so that candidate bounds rest on enough tokens to be tight (with a
+  // one-tile delay, the first bound of a wave covers 64 tokens)
+  const int cap = n_tiles / (kSinkWaves * 4);
+  if (s > cap) s = cap;
+  return s < 1 ? 1 : s;
+}
+
+// Candidate counts and bitmap stay zero between detections: in the header's sink area when they
+// fit there, else in scratch (cleared by a fill before every detection).
+static bool sink_state_in_header(const Geom& g) {
+  const size_t words = (size_t)(g.L + 31) / 32;
+  return ((size_t)g.B * g.Hq + (size_t)g.B * words) * sizeof(uint32_t) <= kSinkAreaBytes;
+}
+
 size_t sink_scratch_bytes(const Geom& g, int* n_splits, int* cand_cap) {
-  const int n_tiles = 1 + (g.L + 63) / 64;
-  // about two workgroups (8 waves) per CU over all (head, sequence) pairs
-  int s = (int)((2LL * 256 + (long long)g.B * g.Hq - 1) / ((long long)g.B * g.Hq));
-  if (s > (n_tiles + 3) / 4) s = (n_tiles + 3) / 4;
-  if (s < 1) s = 1;
+  const int s = sink_splits(g);
   *n_splits = s;
-  *cand_cap = 16384;
+  // candidates per (sequence, q-head): every token when the context is short (a wave then has few
+  // tiles and loose bounds), else 1024 -- with 4+ tiles per wave a random token's bound is ~4 sigma
+  // below tau, so only true sinks and a rare few others are candidates
+  *cand_cap = g.L <= 4096 ? (g.L > 0 ? g.L : 1) : 1024;
   const int words = (g.L + 31) / 32;
   size_t bytes = 0;
-  bytes += (size_t)g.B * g.Hq * s * 4 * 32 * sizeof(float2);   // stats
-  bytes += (size_t)g.B * g.Hq * 32 * sizeof(float);            // lse2
-  bytes += 256 + (size_t)g.B * sizeof(uint32_t);               // cand_count (+align)
-  bytes += (size_t)g.B * words * sizeof(uint32_t);             // bitmap
-  bytes += (size_t)g.B * (*cand_cap) * sizeof(uint32_t);       // candidates
+  bytes += (size_t)g.B * g.Hq * s * kSinkWaves * 32 * sizeof(float2) + 256;   // stats
+  bytes += (size_t)g.B * g.Hq * (*cand_cap) * sizeof(uint32_t) + 256;         // candidates
+  if (!sink_state_in_header(g)) bytes += ((size_t)g.B * g.Hq + (size_t)g.B * words) * sizeof(uint32_t) + 256;
   return bytes + 1024;
 }
 
 hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint64_t* pred_mask,
                         const void* k, const void* k_dec, float tau, int max_sinks,
                         int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
-                        int cand_cap, uint32_t* status, int num_cus) {
+                        int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
+                        char* sink_area) {
   (void)num_cus;
   const int words = (g.L + 31) / 32;
   char* cur = scratch;
@@ -366,17 +453,18 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
     return r;
   };
   SinkParams p;
-  p.stats = reinterpret_cast<float2*>(take((size_t)g.B * g.Hq * n_splits * 4 * 32 * sizeof(float2)));
-  p.lse2 = reinterpret_cast<float*>(take((size_t)g.B * g.Hq * 32 * sizeof(float)));
-  // cand_count and bitmap are contiguous so one fill clears both
-  p.cand_count = reinterpret_cast<uint32_t*>(cur);
-  p.bitmap = p.cand_count + g.B;
-  take(((size_t)g.B + (size_t)g.B * words) * sizeof(uint32_t));
-  p.cand = reinterpret_cast<uint32_t*>(take((size_t)g.B * cand_cap * sizeof(uint32_t)));
+  p.stats = reinterpret_cast<float2*>(take((size_t)g.B * g.Hq * n_splits * kSinkWaves * 32 * sizeof(float2)));
+  p.cand = reinterpret_cast<uint32_t*>(take((size_t)g.B * g.Hq * cand_cap * sizeof(uint32_t)));
+  const bool in_header = sink_state_in_header(g);
+  // counts then bitmap, contiguous
+  p.cand_count = reinterpret_cast<uint32_t*>(
+      in_header ? sink_area : take(((size_t)g.B * g.Hq + (size_t)g.B * words) * sizeof(uint32_t)));
+  p.bitmap = p.cand_count + (size_t)g.B * g.Hq;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.k_dec = static_cast<const uint16_t*>(k_dec);
   p.pred_mask = pred_mask;
+  p.tickets = tickets;
   p.status = status;
   p.Hq = g.Hq;
   p.Hkv = g.Hkv;
@@ -384,12 +472,16 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
   p.T = g.T;
   p.L = g.L;
   p.n_splits = n_splits;
+  p.n_segs = g.B * g.Hq;
   p.cand_cap = cand_cap;
   p.words = words;
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
   p.tau = tau;
-  hipError_t err = launch_fill_u32(st, p.cand_count, (size_t)g.B + (size_t)g.B * words, 0u);
-  if (err != hipSuccess) return err;
+  hipError_t err;
+  if (!in_header) {
+    err = launch_fill_u32(st, p.cand_count, (size_t)g.B * g.Hq + (size_t)g.B * words, 0u);
+    if (err != hipSuccess) return err;
+  }
   if (g.dtype == FDL_F32) {
     dim3 grid(g.Hq, g.B);
     const float* qq = static_cast<const float*>(q);
@@ -401,24 +493,17 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
     else
       hipLaunchKernelGGL((sink_f32_kernel<64>), grid, dim3(64), 0, st, qq, kk, kd, pred_mask,
                          p.bitmap, g.Hq, g.Hkv, g.G, g.T, g.L, words, tau);
-  } else {
-    dim3 grid(n_splits, g.Hq, g.B);
+  } else if (g.L > 0) {
+    // the splits of head seg run on XCD seg % 8 (see the kernel)
+    dim3 grid(8 * ((p.n_segs + 7) / 8) * n_splits);
     if (g.D == 128)
-      hipLaunchKernelGGL((sink_scan_kernel<128>), grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((sink_scan_kernel<128>), grid, dim3(kSinkWaves * 64), 0, st, p);
     else
-      hipLaunchKernelGGL((sink_scan_kernel<64>), grid, dim3(256), 0, st, p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(sink_lse_kernel, dim3(g.Hq, g.B), dim3(64), 0, st, p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    dim3 fgrid(64, g.B);
-    if (g.D == 128)
-      hipLaunchKernelGGL((sink_final_kernel<128>), fgrid, dim3(256), 0, st, p);
-    else
-      hipLaunchKernelGGL((sink_final_kernel<64>), fgrid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((sink_scan_kernel<64>), grid, dim3(kSinkWaves * 64), 0, st, p);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(sink_compact_kernel, dim3(g.B), dim3(256), 0, st, p.bitmap, words, max_sinks,
-                     sink_pos, n_sinks, status);
+                     sink_pos, n_sinks, p.cand_count, g.Hq, status);
   return hipGetLastError();
 }
 
