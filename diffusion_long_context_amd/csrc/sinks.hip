@@ -42,7 +42,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 constexpr float kCandSlack = 0.999f;   // candidates use tau * (1 - 1e-3): absorbs float32 rounding
 constexpr int kSinkWaves = 4;
-constexpr int kSinkTile = 32;           // tokens per tile
+constexpr int kSinkTile = 64;           // tokens per tile
 
 struct SinkParams {
   const uint16_t* q;
@@ -60,19 +60,18 @@ struct SinkParams {
 };
 
 // One pass over K per (sequence, q-head), split over n_splits workgroups of 4 waves that all run on
-// one XCD (workgroup id mod 8).  Each wave streams 32-token tiles of K from HBM into its own LDS slot
-// with LDS DMA (coalesced 1 KiB fetches), copies a tile into MFMA operand registers and fetches the
-// next one into the slot while the current one is scored.  The last
-// split of a head to finish (ticket) merges the partial statistics into the exact log-sum-exp per
-// query, re-scores the head's candidates in float32 and sets the survivors in the sequence's bitmap.
+// one XCD (workgroup id mod 8).  Each wave streams 64-token tiles of K from HBM into its own 16 KiB
+// LDS slot with LDS DMA (coalesced 1 KiB fetches), copies a tile into MFMA operand registers and
+// fetches the next one into the slot while the current one is scored.  The last split of a head to
+// finish (ticket) merges the partial statistics into the exact log-sum-exp per query, re-scores
+// the head's candidates in float32 and sets the survivors in the sequence's bitmap.
 template <int D>
-__global__ __launch_bounds__(kSinkWaves * 64, 3) void sink_scan_kernel(const SinkParams p) {
+__global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const SinkParams p) {
   constexpr int KS = D / 16;
-  constexpr int NT = kSinkWaves * 64;
+  constexpr int RB = kSinkTile / 32;   // 32-row MFMA blocks per tile
   using RC = RowChunks<D>;
   constexpr int PROW = RC::PROW, RPI = RC::ROWS_PER_INSTR, NI = kSinkTile / RPI;
   __shared__ __attribute__((aligned(1024))) uint16_t kslot[kSinkWaves * kSinkTile * D];
-  __shared__ float ebuf[kSinkWaves][kSinkTile][33];
   __shared__ float2 s_part[8][32];
   __shared__ float s_lse[32];
   __shared__ uint32_t s_ticket;
@@ -121,82 +120,97 @@ __global__ __launch_bounds__(kSinkWaves * 64, 3) void sink_scan_kernel(const Sin
       }
     };
     const int swz_k = swz(ql) & (PROW - 1);
-    // upper-bound masses of a scored tile under the current running statistics, summed over the
-    // predicted queries; tokens whose bound reaches tau become candidates
+    // Upper-bound masses of a scored tile under the current running statistics, summed over the
+    // predicted queries; tokens whose bound reaches tau become candidates.  A token's mean reaches
+    // the threshold only if some single query's bound does, so a tile where none does is skipped
+    // at once (the usual case: only sink tiles pass).  Register r of block rb holds token
+    // 32 rb + 8 (r / 4) + 4 hh + r % 4 for query ql.
     const float log2_thr = __log2f(p.tau * kCandSlack);
-    auto eval_tile = [&](const f32x16& sc, int et, int nv) {
+    auto eval_tile = [&](const f32x16 (&sc)[RB], int et, int nv) {
       const float lse = m_run + __log2f(l_run);
-      // screen: a token's mean over the predicted queries reaches the threshold only if some single
-      // query's bound does, so a tile where no (query, token) bound does is skipped without the
-      // transpose (the usual case: only sink tiles pass)
       bool hot = false;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) hot = hot || (qlive && sc[r] - lse >= log2_thr);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hot = hot || (qlive && sc[rb][r] - lse >= log2_thr);
       if (__ballot(hot) == 0ull) return;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
-        ebuf[wave][row][ql] = qlive ? exp2f(sc[r] - lse) : 0.f;
-      }
-      wave_lds_sync();
-      // lane (row ql, half hh) sums queries 16 hh .. 16 hh + 15 of token row ql
-      float u = 0.f;
+      for (int rb = 0; rb < RB; ++rb) {
+        // sum over the 32 queries (lanes of a half) by butterflies: every lane of the half then
+        // holds the sums of its 16 tokens; lane ql < 16 of each half judges token register ql
+        float u[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) u += ebuf[wave][ql][16 * hh + j];
-      u += lane_xor32f(u);
-      u *= inv_np;
-      if (hh == 0 && ql < nv && u >= p.tau * kCandSlack) {
-        const uint32_t idx = atomicAdd(&p.cand_count[seg], 1u);
-        if ((int)idx < p.cand_cap) p.cand[(int64_t)seg * p.cand_cap + idx] = (uint32_t)((et - 1) * kSinkTile + ql);
-        else latch(p.status, ST_CAND_OVERFLOW);
+        for (int r = 0; r < 16; ++r) {
+          float m = qlive ? exp2f(sc[rb][r] - lse) : 0.f;
+          m += __uint_as_float(lane_xor<1>(__float_as_uint(m)));
+          m += __uint_as_float(lane_xor<2>(__float_as_uint(m)));
+          m += __uint_as_float(lane_xor<4>(__float_as_uint(m)));
+          m += __uint_as_float(lane_xor<8>(__float_as_uint(m)));
+          m += __uint_as_float(lane_xor<16>(__float_as_uint(m)));
+          u[r] = m;
+        }
+        float mine = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine = (ql == r) ? u[r] : mine;
+        const int row = 32 * rb + 8 * (ql >> 2) + 4 * hh + (ql & 3);
+        if (ql < 16 && row < nv && mine * inv_np >= p.tau * kCandSlack) {
+          const uint32_t idx = atomicAdd(&p.cand_count[seg], 1u);
+          if ((int)idx < p.cand_cap) p.cand[(int64_t)seg * p.cand_cap + idx] = (uint32_t)((et - 1) * kSinkTile + row);
+          else latch(p.status, ST_CAND_OVERFLOW);
+        }
       }
-      wave_lds_sync();
     };
-    f32x16 sprev;
+    f32x16 sprev[RB];
     int prev_e = 0, prev_nvalid = 0;   // prev_e == 0: nothing pending (tile 0 is never evaluated)
     int e = e0 + wave;
     if (e < e1) issue(e);
     for (; e < e1; e += kSinkWaves) {
       wait_vm0();   // this tile's fetches have landed
-      // lane (token ql, half hh): dims hh*D/2 + 8 ks .. +8 of its token, as the MFMA A operand
-      uint4 ka[KS];
+      // lane (token ql of block rb, half hh): dims hh*D/2 + 8 ks .. +8, as the MFMA A operand
+      uint4 ka[RB][KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int c = hh * (PROW / 2) + ks;
-        ka[ks] = *reinterpret_cast<const uint4*>(slot + ql * D + ((c ^ swz_k) * 8));
-      }
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c = hh * (PROW / 2) + ks;
+          ka[rb][ks] = *reinterpret_cast<const uint4*>(slot + (32 * rb + ql) * D + ((c ^ swz_k) * 8));
+        }
       wait_lgkm0();
       if (e + kSinkWaves < e1) issue(e + kSinkWaves);   // next tile flies while this one is scored
       const int nvalid = (e == 0) ? p.T : min(kSinkTile, p.L - (e - 1) * kSinkTile);
-      f32x16 sacc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc = mfma32(as_bf16x8(ka[ks]), qf[ks], sacc);
-      // register r: token 8*(r/4) + 4*hh + r%4 of the tile, query ql
+      f32x16 sacc[RB];
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
-        float x = sacc[r] * p.scale_log2;
-        if (row >= nvalid) x = -__builtin_inff();
-        sacc[r] = x;
-        mx = fmaxf(mx, x);
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sacc[rb] = mfma32(as_bf16x8(ka[rb][ks]), qf[ks], sacc[rb]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          float x = sacc[rb][r] * p.scale_log2;
+          if (row >= nvalid) x = -__builtin_inff();
+          sacc[rb][r] = x;
+          mx = fmaxf(mx, x);
+        }
       }
       mx = fmaxf(mx, lane_xor32f(mx));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);
       float rs = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) rs += exp2f(sacc[r] - m_new);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rs += exp2f(sacc[rb][r] - m_new);
       rs += lane_xor32f(rs);
       l_run = l_run * alpha + rs;
       m_run = m_new;
       // candidates of the previous tile, bounded with the statistics that now include this one
-      // (a one-tile delay, so that no bound rests on fewer than two tiles of tokens)
+      // (a one-tile delay, so that no bound rests on a single tile of tokens)
       if (prev_e > 0) eval_tile(sprev, prev_e, prev_nvalid);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sprev[r] = sacc[r];
+      for (int rb = 0; rb < RB; ++rb) sprev[rb] = sacc[rb];
       prev_e = e;
       prev_nvalid = nvalid;
     }
@@ -278,7 +292,6 @@ __global__ __launch_bounds__(kSinkWaves * 64, 3) void sink_scan_kernel(const Sin
     if (lane == 0 && e / (float)n_pred >= p.tau)
       atomicOr(&p.bitmap[(int64_t)b * p.words + (t >> 5)], 1u << (t & 31));
   }
-  (void)NT;
 }
 
 // float32 path (small workloads): thread = query row; two passes over the keys.
@@ -408,10 +421,10 @@ int sink_splits(const Geom& g) {
   const int n_tiles = 1 + (g.L + kSinkTile - 1) / kSinkTile;
   const long long segs = (long long)g.B * g.Hq;
   if (segs > kMaxSplitSegs) return 1;
-  // about three 4-wave workgroups per CU (the kernel's occupancy) over all (sequence, q-head) pairs
-  int s = (int)((3LL * 256 + segs - 1) / segs);
+  // about two 4-wave workgroups per CU (the kernel's occupancy) over all (sequence, q-head) pairs
+  int s = (int)((2LL * 256 + segs - 1) / segs);
   // at least 4 tiles per wave, so that candidate bounds rest on enough tokens to be tight (with a
-  // one-tile delay, the first bound of a wave covers 64 tokens)
+  // one-tile delay, the first bound of a wave covers 128 tokens)
   const int cap = n_tiles / (kSinkWaves * 4);
   if (s > cap) s = cap;
   return s < 1 ? 1 : s;
