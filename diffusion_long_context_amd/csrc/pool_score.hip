@@ -31,7 +31,8 @@ __device__ __forceinline__ float2 load_pair(const KT* p);
 
 template <>
 __device__ __forceinline__ float2 load_pair<uint16_t>(const uint16_t* p) {
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+  // non-temporal: the cache is streamed once per pooling
+  const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
   return make_float2(bf16_bits_to_f32(w & 0xFFFFu), bf16_bits_to_f32(w >> 16));
 }
 
