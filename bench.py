@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "sparse-attn step us + KV tokens/s at 32K ctx; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
 WORKSPACE_BYTES = 256 << 20   # library workspace of the timed handle (sets the attention split count)
+TIME_EVERY = 16               # timed region: one sparse-attention launch in 16 carries HIP events
 
 
 # HBM bytes per sparse-attention dispatch, from two rocprofv3 counter runs of this benchmark
@@ -220,7 +221,8 @@ def main():
 
     # ---- the timed region: exactly K steps; HIP events around every sparse-attention launch ----
     log(f"timing {args.steps} steps")
-    h.fdl_profile_begin(args.steps * NL + 16, kinds=("sparse_attn",))
+    # every TIME_EVERY-th sparse launch carries dispatch-timestamp events (≈ 4 µs each otherwise)
+    h.fdl_profile_begin(args.steps * NL // TIME_EVERY + 16, kinds=("sparse_attn",), every=TIME_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(args.warmup, args.steps, arrays)

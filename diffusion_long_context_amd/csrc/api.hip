@@ -86,7 +86,8 @@ struct ProfScope {
   hipEvent_t a = nullptr, b = nullptr;
   fdl::KernelTimer kt{};
   ProfScope(fdl_handle hh, int k, bool inner_ = false) : h(hh), kind(k), inner(inner_) {
-    if (h->prof_on && ((h->prof_mask >> k) & 1u) && h->prof_used + 2 <= h->prof_pool.size()) {
+    if (h->prof_on && ((h->prof_mask >> k) & 1u) && (h->prof_seen[k]++ % h->prof_every) == 0 &&
+        h->prof_used + 2 <= h->prof_pool.size()) {
       a = h->prof_pool[h->prof_used++];
       b = h->prof_pool[h->prof_used++];
       kt = {a, b};
@@ -526,8 +527,9 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_para
   return FDL_OK;
 }
 
-fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask) {
+fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask, int32_t every) {
   if (!h || max_records < 1) return h ? fail(h, FDL_EINVAL, "max_records must be >= 1") : FDL_EINVAL;
+  if (every < 1) return fail(h, FDL_EINVAL, "every must be >= 1");
   for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
   h->prof_pool.clear();
   h->prof_recs.clear();
@@ -545,6 +547,8 @@ fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_ma
   }
   h->prof_on = true;
   h->prof_mask = kind_mask;
+  h->prof_every = every;
+  for (int k = 0; k < FDL_PROF_KINDS; ++k) h->prof_seen[k] = 0;
   return FDL_OK;
 }
 

@@ -30,6 +30,8 @@ struct fdl_ctx {
   };
   bool prof_on = false;
   uint32_t prof_mask = 0;
+  int prof_every = 1;
+  long long prof_seen[FDL_PROF_KINDS] = {};
   size_t prof_used = 0;
   std::vector<hipEvent_t> prof_pool;
   std::vector<ProfRec> prof_recs;

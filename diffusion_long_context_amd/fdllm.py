@@ -79,7 +79,7 @@ _SIGS = {
     "fdl_dense_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P]),
     "fdl_focus_step": (_I, [_P, ctypes.POINTER(fdl_geom), ctypes.POINTER(fdl_focus_params), _P, _P, _I,
                             ctypes.POINTER(fdl_layer_io), _P, _P, _P, _P, _P, _P, _P]),
-    "fdl_profile_begin": (_I, [_P, _I, ctypes.c_uint32]),
+    "fdl_profile_begin": (_I, [_P, _I, ctypes.c_uint32, _I]),
     "fdl_profile_end": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }
 
@@ -300,12 +300,12 @@ class Handle:
             _ptr(n_sinks, 4 * B, "n_sinks"), _ptr(sel_idx, 4 * B * Hkv * params.max_sel, "sel_idx"),
             _ptr(n_sel, 4 * B * Hkv, "n_sel")))
 
-    def fdl_profile_begin(self, max_records: int, kinds=PROF_KINDS):
+    def fdl_profile_begin(self, max_records: int, kinds=PROF_KINDS, every: int = 1):
         self.sync_stream()
         mask = 0
         for k in kinds:
             mask |= 1 << PROF_KINDS.index(k)
-        self._check(self.lib.fdl_profile_begin(self.h, max_records, mask))
+        self._check(self.lib.fdl_profile_begin(self.h, max_records, mask, every))
 
     def fdl_profile_end(self) -> dict:
         self.sync_stream()

@@ -250,20 +250,22 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* g, const fdl_focus_param
 
 /* ---- timing --------------------------------------------------------------------------------- */
 
-/* Optional per-call timing with HIP events recorded on the handle's stream around every kernel
- * launch of the kinds below (and around whole layers inside fdl_focus_step) whose bit
- * (1 << kind) is set in kind_mask.  fdl_profile_begin
- * creates a pool of 2 * max_records events and clears the records; fdl_profile_end synchronises,
- * writes the summed duration in microseconds and the launch count of every kind into
- * total_us[FDL_PROF_KINDS] / counts[FDL_PROF_KINDS] and releases the pool.  Records beyond
- * max_records are dropped. */
+/* Optional per-call timing with HIP events on the handle's stream, for the launches of the kinds
+ * below (and whole layers inside fdl_focus_step) whose bit (1 << kind) is set in kind_mask.
+ * Attention launches carry the events in the kernel dispatch itself (start and end of the kernel);
+ * the other kinds are bracketed by event records.  Only every `every`-th launch of a kind is timed
+ * (every >= 1), which keeps the cost of the events -- a few microseconds each -- out of a timed
+ * run.  fdl_profile_begin creates a pool of 2 * max_records events and clears the records;
+ * fdl_profile_end synchronises, writes the summed duration in microseconds and the number of timed
+ * launches of every kind into total_us[FDL_PROF_KINDS] / counts[FDL_PROF_KINDS] and releases the
+ * pool.  Records beyond max_records are dropped. */
 typedef enum {
   FDL_PROF_PREDICT = 0, FDL_PROF_POOL, FDL_PROF_SCORE, FDL_PROF_SINKS, FDL_PROF_SELECT,
   FDL_PROF_SPARSE_ATTN, FDL_PROF_DENSE_ATTN, FDL_PROF_LAYER_DENSE, FDL_PROF_LAYER_SOURCE,
   FDL_PROF_LAYER_REUSE, FDL_PROF_KINDS
 } fdl_prof_kind;
 
-fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask);
+fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask, int32_t every);
 fdl_status fdl_profile_end(fdl_handle h, double* total_us, int64_t* counts);
 
 #ifdef __cplusplus
