@@ -61,6 +61,7 @@ struct MhaParams {
 };
 
 constexpr int kMhaWaves = 8;
+constexpr int kMaxSplits = 32;   // workgroups per head (the final merge keeps their weights in LDS)
 constexpr int kTileTok = 32;
 
 template <int D>
@@ -613,36 +614,53 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   if (s_ticket != (uint32_t)(NS - 1)) return;
   asm volatile("buffer_inv sc0" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
+  // every split's (max, sum) in one round trip, then per query the common max and the split weights
+  float* s_wt = reinterpret_cast<float*>(lds);   // [NS][32] weights, then [32] sums (slots are free)
+  float2* s_ml2 = reinterpret_cast<float2*>(lds + 4096);   // [NS][32]
+  for (int i = tid; i < NS * 32; i += NT) s_ml2[i] = pml_base[seg * NS * 32 + i];
+  __syncthreads();
+  if (tid < 32) {
+    float M = -__builtin_inff();
+    for (int t = 0; t < NS; ++t) M = fmaxf(M, s_ml2[t * 32 + tid].x);
+    float Ls = 0.f;
+    for (int t = 0; t < NS; ++t) {
+      const float2 v = s_ml2[t * 32 + tid];
+      const float w = (v.x != -__builtin_inff() && M != -__builtin_inff()) ? exp2f(v.x - M) : 0.f;
+      s_wt[t * 32 + tid] = w;
+      Ls += v.y * w;
+    }
+    s_wt[kMaxSplits * 32 + tid] = Ls;
+  }
+  __syncthreads();
+  // thread -> (d, 8 queries); the partials of kMergeBatch splits are loaded before any is used
+  constexpr int kMergeBatch = 8;
   for (int it = tid; it < D * 4; it += NT) {
     const int d = it >> 2;
     const int q0 = (it & 3) * 8;
-    float Mq[8], Lq[8], o[8];
+    float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      Mq[i] = -__builtin_inff();
-      Lq[i] = 0.f;
-      o[i] = 0.f;
-    }
-    const float2* ml = pml_base + seg * NS * 32 + q0;
-    for (int t = 0; t < NS; ++t)
+    for (int i = 0; i < 8; ++i) o[i] = 0.f;
+    for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
+      float4 a[kMergeBatch], c[kMergeBatch];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) Mq[i] = fmaxf(Mq[i], ml[t * 32 + i].x);
-    for (int t = 0; t < NS; ++t) {
-      const float* src = po_base + ((seg * NS + t) * D + d) * 32 + q0;
-      const float4 a = *reinterpret_cast<const float4*>(src);
-      const float4 c = *reinterpret_cast<const float4*>(src + 4);
-      const float ov[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int t = t0 + j < NS ? t0 + j : NS - 1;
+        const float* src = po_base + ((seg * NS + t) * D + d) * 32 + q0;
+        a[j] = *reinterpret_cast<const float4*>(src);
+        c[j] = *reinterpret_cast<const float4*>(src + 4);
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float2 v = ml[t * 32 + i];
-        const float wgt = (v.x != -__builtin_inff() && Mq[i] != -__builtin_inff()) ? exp2f(v.x - Mq[i]) : 0.f;
-        Lq[i] += v.y * wgt;
-        o[i] += ov[i] * wgt;
+      for (int j = 0; j < kMergeBatch; ++j) {
+        if (t0 + j >= NS) break;
+        const float* w = s_wt + (t0 + j) * 32 + q0;
+        o[0] += a[j].x * w[0]; o[1] += a[j].y * w[1]; o[2] += a[j].z * w[2]; o[3] += a[j].w * w[3];
+        o[4] += c[j].x * w[4]; o[5] += c[j].y * w[5]; o[6] += c[j].z * w[6]; o[7] += c[j].w * w[7];
       }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (q0 + i < p.T) p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(o[i] / Lq[i]);
+      if (q0 + i < p.T)
+        p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(o[i] / s_wt[kMaxSplits * 32 + q0 + i]);
   }
   if (tid == 0) p.tickets[seg * kSyncStride] = 0u;
 }
@@ -699,6 +717,7 @@ int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus) {
   const long long per_wave_min = 1;
   if (s * kMhaWaves * per_wave_min > tiles) s = (tiles + kMhaWaves - 1) / kMhaWaves;
   if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (segs > kMaxSplitSegs) s = 1;
   return (int)s;
 }
