@@ -237,12 +237,23 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     // exact log-sum-exp per query: thread (q, j) merges parts j, j + 8, ...; then 8 -> 1
     const int q = tid & 31, j = tid >> 5;
     float M = -__builtin_inff(), S = 0.f;
-    for (int i = j; i < n_parts; i += 8) {
-      const float2 v = p.stats[((int64_t)seg * n_parts + i) * 32 + q];
-      if (v.y > 0.f) {
-        const float mn = fmaxf(M, v.x);
-        S = S * exp2f(M - mn) + v.y * exp2f(v.x - mn);
-        M = mn;
+    // the parts j, j + 8, ... are loaded kPartBatch at a time before any is used
+    constexpr int kPartBatch = 8;
+    for (int i0 = j; i0 < n_parts; i0 += 8 * kPartBatch) {
+      float2 v[kPartBatch];
+#pragma unroll
+      for (int u = 0; u < kPartBatch; ++u) {
+        const int i = i0 + 8 * u;
+        v[u] = p.stats[((int64_t)seg * n_parts + (i < n_parts ? i : j)) * 32 + q];
+      }
+#pragma unroll
+      for (int u = 0; u < kPartBatch; ++u) {
+        if (i0 + 8 * u >= n_parts) break;
+        if (v[u].y > 0.f) {
+          const float mn = fmaxf(M, v[u].x);
+          S = S * exp2f(M - mn) + v[u].y * exp2f(v[u].x - mn);
+          M = mn;
+        }
       }
     }
     s_part[j][q] = make_float2(M, S);
