@@ -63,6 +63,7 @@ struct MhaParams {
 constexpr int kMhaWaves = 8;
 constexpr int kMaxSplits = 32;   // workgroups per head (the final merge keeps their weights in LDS)
 constexpr int kTileTok = 32;
+constexpr float kRescaleSlack = 8.f;   // log2 headroom of the lazily rescaled softmax weights
 
 template <int D>
 struct MhaShape {
@@ -107,23 +108,28 @@ __device__ __forceinline__ void mha_prepare(const MhaParams& p, int e, const int
 }
 
 // Barrier of the NS splits of one head.  They run on one XCD (see the kernel), so a relaxed
-// atomic at L2 orders them and data they stored before arriving is in that L2.  Arrival count and
-// generation live in `bar`; the last arrival resets the count and bumps the generation.  A waiter
-// gives up after spin_limit polls (returns false) instead of waiting on a sibling that is not
-// resident; the caller then recomputes what it would have read.  All threads must call.
-__device__ bool head_barrier(uint32_t* bar, int NS, int spin_limit, int* s_flag) {
+// atomic at L2 orders them and data they stored before arriving is in that L2.  `bar` is one 64-bit
+// word: arrival count in the low half, generation in the high half.  The generation only moves once
+// all NS splits of this launch have arrived, so thread 0 may read it (g0) any time before its own
+// arrival -- the kernel does so at its start, off the critical path.  The last arrival takes the
+// count back to 0 and bumps the generation with a single add.  A waiter gives up after spin_limit
+// polls (returns false) instead of waiting on a sibling that is not resident; the caller then
+// recomputes what it would have read.  All threads must call.
+__device__ __forceinline__ uint32_t head_barrier_gen(const uint32_t* bar) {
+  return __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ bool head_barrier(uint32_t* bar, uint32_t g0, int NS, int spin_limit, int* s_flag) {
   __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are acknowledged by L2
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t g0 = __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t zero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(g0));   // the arrival is issued after g0 is read
-    const uint32_t old = __hip_atomic_fetch_add(&bar[0], 1u + zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t* word = reinterpret_cast<uint64_t*>(bar);
+    const uint64_t old = __hip_atomic_fetch_add(word, 1ull + zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int ok = 1;
-    if (old == (uint32_t)(NS - 1)) {
-      __hip_atomic_store(&bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);
-      __hip_atomic_fetch_add(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)old == (uint32_t)(NS - 1)) {
+      __hip_atomic_fetch_add(word, (1ull << 32) - (uint64_t)NS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       int it = 0;
       while (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
@@ -191,45 +197,80 @@ __device__ __forceinline__ void mha_score_rows(const float* __restrict__ ksh, in
   }
 }
 
-// Fused selection, first phase of the SEL kernel.  The NS splits of a head share the scoring: split
-// s scores rows [n s / NS, n (s+1) / NS) into the scores output, they meet at head_barrier, and each
-// then reads all n scores back (a split whose siblings do not arrive in time scores every row
-// itself).  Then every split selects the sink blocks plus the top-K others (select_core) into
-// sel_lds, ascending; split 0 writes the selection out.  The scratch of both steps lives in the
-// tile slots, which are free until the first fetch.  Returns the number of selected blocks.
+// Fused selection, first phase of the SEL kernel, in two steps around the early tile fetches.
+//
+// mha_score_phase: the NS splits of a head share the scoring.  Split s scores rows
+// [n s / NS, n (s+1) / NS) into the scores output, they meet at head_barrier, and each then reads
+// all n scores back as order keys (a split whose siblings do not arrive in time scores every row
+// itself).  When the threshold selection applies (n <= NT, top_k <= 64), the forced units are
+// already known here, so their list goes to the front of sel_lds (ascending) and its length is
+// returned: those units' tiles can be fetched before the selection has run.
+// mha_choose_phase: every split selects the forced units plus the top-K others into sel_lds
+// (forced first, then the chosen, each ascending; the other selection paths write one ascending
+// list) and split 0 writes the ascending selection and its count out.  Returns the list length.
+// The scratch of both steps lives in the first tile slots, which hold no tile until then.
 constexpr int kQbufOffsetF = 8192;   // floats: past qs, keys, forced bits and the selection scratch
 
 template <int D>
-__device__ int mha_select_phase(const MhaParams& p, int b, int h, int64_t seg, int s, int NS, uint16_t* lds_raw,
-                                uint16_t* sel_lds) {
+struct SelLds {
+  float* qs;          // [D]
+  uint32_t* keys;     // [kFusedMaxUnits]
+  uint32_t* forced;   // [kFusedMaxUnits / 32]
+  int* hist;          // [256]
+  int* tmp;           // [NT / 64]
+  uint32_t* digit;
+  int* above;
+  int* flag;
+  __device__ explicit SelLds(uint16_t* lds_raw) {
+    constexpr int NT = kMhaWaves * 64;
+    qs = reinterpret_cast<float*>(lds_raw);
+    keys = reinterpret_cast<uint32_t*>(lds_raw) + D;
+    forced = keys + kFusedMaxUnits;
+    hist = reinterpret_cast<int*>(forced + kFusedMaxUnits / 32);
+    tmp = hist + 256;
+    digit = reinterpret_cast<uint32_t*>(tmp + NT / 64);
+    above = reinterpret_cast<int*>(digit + 1);
+    flag = above + 1;
+    static_assert(D + kFusedMaxUnits + kFusedMaxUnits / 32 + 256 + NT / 64 + 4 <= kQbufOffsetF, "select scratch");
+  }
+};
+
+// Scratch of the selection phase, in whole tile slots: waves from kFreeSlotWave on may fetch into
+// their slots while it runs.
+template <int D>
+constexpr int kFreeSlotWave =
+    (int)(((kQbufOffsetF + 32 * D) * sizeof(float) + 2 * MhaShape<D>::SLOT - 1) / (2 * MhaShape<D>::SLOT));
+
+__device__ __forceinline__ bool threshold_select_ok(int n, int top_k) {
+  return n <= kMhaWaves * 64 && top_k <= 64;
+}
+
+template <int D>
+__device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, int NS, uint16_t* lds_raw,
+                               uint16_t* sel_lds) {
   constexpr int NT = kMhaWaves * 64;
   constexpr int LPR = D / 16;
-  const FusedSelect& f = p.fs;
-  float* qs = reinterpret_cast<float*>(lds_raw);                           // [D]
-  uint32_t* keys = reinterpret_cast<uint32_t*>(lds_raw) + D;               // [kFusedMaxUnits]
-  uint32_t* forced = keys + kFusedMaxUnits;                                 // [kFusedMaxUnits / 32]
-  int* hist = reinterpret_cast<int*>(forced + kFusedMaxUnits / 32);        // [256]
-  int* tmp = hist + 256;                                                    // [NT / 64]
-  uint32_t* digit = reinterpret_cast<uint32_t*>(tmp + NT / 64);
-  int* above = reinterpret_cast<int*>(digit + 1);
-  int* flag = above + 1;
-  static_assert(D + kFusedMaxUnits + kFusedMaxUnits / 32 + 256 + NT / 64 + 4 <= kQbufOffsetF, "select scratch");
   static_assert((kQbufOffsetF + 32 * D) * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * MhaShape<D>::SLOT,
                 "query staging must fit in the tile slots");
+  const FusedSelect& f = p.fs;
+  const SelLds<D> L(lds_raw);
   const int tid = threadIdx.x;
   const int j = (tid & 63) % LPR;
   const int n = p.n_units;
   const float* ksh = f.ks + seg * (int64_t)n * D;
   float* sc_out = f.scores + seg * (int64_t)n;
+  uint32_t* bar = f.barriers + seg * kSyncStride;
+  uint32_t g0 = 0;
+  if (NS > 1 && tid == 0) g0 = head_barrier_gen(bar);
 
   const int ra = (int)((int64_t)n * s / NS), rb = (int)((int64_t)n * (s + 1) / NS);
   float x[kScoreBatch][16];
   const bool pre = rb > ra;
   if (pre) mha_load_rows<D>(ksh, ra, rb, x);   // in flight during the query sum
-  for (int i = tid; i < (n + 31) / 32; i += NT) forced[i] = 0u;
+  for (int i = tid; i < (n + 31) / 32; i += NT) L.forced[i] = 0u;
   // the query staging area sits above the keys' scratch in the (still unused) tile slots
   query_sum_g1_coop<D, 32, NT>(p.q + seg * (int64_t)p.T * D, f.pred_mask[b], p.T,
-                               reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, qs);
+                               reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, L.qs);
   __syncthreads();   // qs and the cleared bits
   if (f.sink_pos != nullptr) {
     int ns = f.n_sinks[b];
@@ -238,39 +279,69 @@ __device__ int mha_select_phase(const MhaParams& p, int b, int h, int64_t seg, i
       const int pos = f.sink_pos[(int64_t)b * f.max_sinks + t];
       if (pos < 0) continue;
       const int u = pos >> p.unit_log2;
-      if (u < n) atomicOr(&forced[u >> 5], 1u << (u & 31));
+      if (u < n) atomicOr(&L.forced[u >> 5], 1u << (u & 31));
     }
   }
   float qv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
-  mha_score_rows<D>(ksh, ra, rb, qv, keys, sc_out, true, x, pre);
+  for (int i = 0; i < 16; ++i) qv[i] = L.qs[16 * j + i];
+  mha_score_rows<D>(ksh, ra, rb, qv, L.keys, sc_out, true, x, pre);
   if (NS > 1) {
-    if (head_barrier(f.barriers + seg * kSyncStride, NS, f.spin_limit, flag)) {
+    if (head_barrier(bar, g0, NS, f.spin_limit, L.flag)) {
       for (int i = tid; i < n; i += NT)
-        if (i < ra || i >= rb) keys[i] = order_key(sc_out[i]);
+        if (i < ra || i >= rb) L.keys[i] = order_key(sc_out[i]);
     } else {
-      mha_score_rows<D>(ksh, 0, ra, qv, keys, sc_out, false, x, false);
-      mha_score_rows<D>(ksh, rb, n, qv, keys, sc_out, false, x, false);
+      mha_score_rows<D>(ksh, 0, ra, qv, L.keys, sc_out, false, x, false);
+      mha_score_rows<D>(ksh, rb, n, qv, L.keys, sc_out, false, x, false);
       if (tid == 0) latch(p.status, ST_SYNC_FALLBACK);
     }
   }
+  __syncthreads();   // keys and forced bits complete
+  if (!threshold_select_ok(n, f.top_k)) return 0;   // uniform
+  // forced list: the place of unit t is the number of forced units below it (n <= NT: at most
+  // NT / 32 words, all read at once)
+  int nf = 0, below = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 32; ++w) {
+    const uint32_t word = w < (n + 31) / 32 ? L.forced[w] : 0u;
+    nf += __popc(word);
+    below += (w < (tid >> 5)) ? __popc(word) : (w == (tid >> 5) ? __popc(word & ((1u << (tid & 31)) - 1u)) : 0);
+  }
+  if (tid < n && ((L.forced[tid >> 5] >> (tid & 31)) & 1u) && below < p.max_sel) sel_lds[below] = (uint16_t)tid;
   __syncthreads();
+  return nf < p.max_sel ? nf : p.max_sel;
+}
+
+template <int D>
+__device__ int mha_choose_phase(const MhaParams& p, int64_t seg, int s, uint16_t* lds_raw, uint16_t* sel_lds) {
+  constexpr int NT = kMhaWaves * 64;
+  const FusedSelect& f = p.fs;
+  const SelLds<D> L(lds_raw);
+  const int tid = threadIdx.x;
+  const int n = p.n_units;
   int32_t* gout = f.sel_idx + seg * p.max_sel;
   const bool writer = s == 0;
-  auto emit = [&](int pos, int i) {
-    if (pos < p.max_sel) {
-      sel_lds[pos] = (uint16_t)i;
-      if (writer) gout[pos] = i;
-    }
-  };
   SelResult r;
-  if (n <= NT) {
-    r = select_small<NT>(keys, forced, n, f.top_k, reinterpret_cast<uint64_t*>(keys + kFusedMaxUnits - 2 * NT),
-                         reinterpret_cast<uint32_t*>(hist), hist + 64, tmp, emit);
+  if (threshold_select_ok(n, f.top_k)) {
+    auto emit = [&](int gpos, int lpos, int i) {
+      if (lpos < p.max_sel) sel_lds[lpos] = (uint16_t)i;
+      if (writer && gpos < p.max_sel) gout[gpos] = i;
+    };
+    r = select_top64<NT>(L.keys, L.forced, n, f.top_k, L.keys + kFusedMaxUnits - NT, L.hist, emit);
   } else {
-    const SelScratch scr{hist, tmp, digit, above};
-    r = select_core<NT>(keys, forced, n, f.top_k, scr, emit);
+    auto emit = [&](int pos, int i) {
+      if (pos < p.max_sel) {
+        sel_lds[pos] = (uint16_t)i;
+        if (writer) gout[pos] = i;
+      }
+    };
+    if (n <= NT) {
+      r = select_small<NT>(L.keys, L.forced, n, f.top_k, reinterpret_cast<uint64_t*>(L.keys + kFusedMaxUnits - 2 * NT),
+                           reinterpret_cast<uint32_t*>(L.hist), L.hist + 64, L.tmp, emit);
+    } else {
+      const SelScratch scr{L.hist, L.tmp, L.digit, L.above};
+      r = select_core<NT>(L.keys, L.forced, n, f.top_k, scr, emit);
+    }
   }
   if (writer && tid == 0) f.n_sel[seg] = r.total < p.max_sel ? r.total : p.max_sel;
   if (tid == 0 && r.total > p.max_sel) latch(p.status, ST_SEL_OVERFLOW);
@@ -278,8 +349,18 @@ __device__ int mha_select_phase(const MhaParams& p, int b, int h, int64_t seg, i
   return r.total < p.max_sel ? r.total : p.max_sel;
 }
 
+// Source of one 16-byte fetch.  Contiguous caches: a uniform base plus an unsigned 32-bit byte
+// offset per lane, which the fetch takes in its scalar-base form.
+__device__ __forceinline__ const void* row_src(const uint16_t* base, int32_t off) {
+  return reinterpret_cast<const char*>(base) + (uint32_t)off * 2u;
+}
+__device__ __forceinline__ const void* row_src(const uint16_t* base, int64_t off) {
+  return base + off;
+}
+
 // Launch the LDS fetches of a prepared tile into the wave's slot; returns the 32-bit row mask.
-template <int D, bool DENSE, bool PAGED>
+// MAYBE_OWN = false: the caller knows e > 0 (a wave's later tiles), so the own-block branch goes.
+template <int D, bool DENSE, bool PAGED, bool MAYBE_OWN = true>
 __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<PAGED>& rows, int b, int h,
                                               int e, int n_list, const TilePrep<D>& tp, uint16_t* slot,
                                               int lane, bool& bad) {
@@ -288,7 +369,7 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
   const int rsub = lane / S::PROW;
   const int sc = lane % S::PROW;
   const int64_t head = (int64_t)b * p.H + h;
-  const bool dec = (e == 0) || (p.L == 0);   // uniform
+  const bool dec = MAYBE_OWN && ((e == 0) || (p.L == 0));   // uniform
   const uint16_t* kb;
   const uint16_t* vb;
   RowOff<PAGED> off[NI];
@@ -351,11 +432,15 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
       okm |= (uint32_t)((bal >> (q * S::PROW)) & 1ull) << (j * S::ROWS_PER_INSTR + q);
   }
 #pragma unroll
-  for (int j = 0; j < NI; ++j)
-    __builtin_amdgcn_global_load_lds((const void*)(kb + off[j]), (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+  for (int j = 0; j < NI; ++j) {
+    const void* src = row_src(kb, off[j]);
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+  }
 #pragma unroll
-  for (int j = 0; j < NI; ++j)
-    __builtin_amdgcn_global_load_lds((const void*)(vb + off[j]), (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, kStreamPolicy);
+  for (int j = 0; j < NI; ++j) {
+    const void* src = row_src(vb, off[j]);
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, kStreamPolicy);
+  }
   return okm;
 }
 
@@ -377,7 +462,8 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   const int seg_i = xcd + 8 * (xslot / NS);
   if (seg_i >= p.n_segs) return;
   const int b = seg_i / p.H, h = seg_i % p.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: in a scalar register, the per-tile bookkeeping stays scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hh = lane >> 5;
   const int64_t seg = seg_i;
   KvRows<PAGED> rows;
@@ -396,31 +482,61 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   // selection size (n_hint units), the split ranges come from it, so the first tile's index loads
   // can go out together with the read of the actual count; the actual count then trims the ranges
   // and the last split takes any tiles beyond the hint.
-  int n_part = DENSE ? p.L : (p.n_hint > 0 ? (p.n_hint < p.max_sel ? p.n_hint : p.max_sel) << p.unit_log2 : -1);
-  int ns_raw = 0;
-  if constexpr (SEL) {
-    ns_raw = mha_select_phase<D>(p, b, h, seg, s, NS, lds, sel_lds);
-    n_part = -1;
-  } else if (!DENSE && n_part < 0) {
-    ns_raw = p.n_sel[seg];   // no hint: the count comes first
-  }
-  if (n_part < 0) n_part = (ns_raw < 0 ? 0 : (ns_raw > p.max_sel ? p.max_sel : ns_raw)) << p.unit_log2;
-  if (p.L == 0) n_part = 0;
-  const int n_tiles_part = 1 + (n_part + kTileTok - 1) / kTileTok;
-  const int e0 = (int)((int64_t)n_tiles_part * s / NS);
-  int e1 = (int)((int64_t)n_tiles_part * (s + 1) / NS);
-  int e = e0 + wave;
+  // A wave's tiles: e, then e + e_step while below e1 -- except in the fused kernel, where tiles
+  // below e_pre (fetched early, one per wave) are followed by the wave's round-robin start e_rr.
+  int e, e1, n_list;
+  int e_step = kMhaWaves, e_pre = 0, e_rr = 0;
   TilePrep<D> tp;
-  // unconditional: the last split may grow past the hinted range once the count is known
-  mha_prepare<D, DENSE, SEL>(p, e, sel_row, sel_lds, lane, tp);
-  int n_list = n_part;
-  if (!DENSE && !SEL && p.n_hint > 0) {
-    int ns = p.n_sel[seg];
-    ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
+  uint32_t vm_next = 0;
+  bool issued = false;
+  if constexpr (SEL) {
+    const int nf = mha_score_phase<D>(p, b, seg, s, NS, lds, sel_lds);
+    // Known now: tile 0 (the block's own tokens) and the tiles of the nf forced units at the front
+    // of the list.  Up to one of them per wave whose slot the selection scratch leaves free is
+    // fetched while the selection runs.  The other tiles go round robin over all 8 NS waves of the
+    // head, so that no wave streams more than its share after the selection; the waves that
+    // fetched early come last in that order.
+    constexpr int FW = kFreeSlotWave<D>;
+    const int tpu = p.unit_log2 >= 5 ? 1 << (p.unit_log2 - 5) : 0;   // tiles per unit
+    const int n_known = 1 + (p.L > 0 ? nf * tpu : 0);
+    const int cap = (kMhaWaves - FW) * NS;
+    e_pre = n_known < cap ? n_known : cap;
+    const int rr = wave < FW ? wave : FW + (kMhaWaves - 1 - wave);
+    e_rr = e_pre + rr * NS + s;
+    e_step = kMhaWaves * NS;
+    const int jp = (wave - FW) * NS + s;
+    e = (wave >= FW && jp < e_pre) ? jp : e_rr;
+    if (e < e_pre) {   // uniform per wave
+      mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp);
+      vm_next = mha_issue<D, false, false>(p, rows, b, h, e, nf << p.unit_log2, tp, slot, lane, bad);
+      issued = true;
+    }
+    const int ns = mha_choose_phase<D>(p, seg, s, lds, sel_lds);
     n_list = p.L == 0 ? 0 : ns << p.unit_log2;
-    const int n_tiles = 1 + (n_list + kTileTok - 1) / kTileTok;
-    if (s == NS - 1) e1 = n_tiles;
-    e1 = e1 < n_tiles ? e1 : n_tiles;
+    e1 = 1 + (n_list + kTileTok - 1) / kTileTok;
+    if (!issued) mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp);
+  } else {
+    int n_part = DENSE ? p.L : (p.n_hint > 0 ? (p.n_hint < p.max_sel ? p.n_hint : p.max_sel) << p.unit_log2 : -1);
+    if (!DENSE && n_part < 0) {
+      const int ns_raw = p.n_sel[seg];   // no hint: the count comes first
+      n_part = (ns_raw < 0 ? 0 : (ns_raw > p.max_sel ? p.max_sel : ns_raw)) << p.unit_log2;
+    }
+    if (p.L == 0) n_part = 0;
+    const int n_tiles_part = 1 + (n_part + kTileTok - 1) / kTileTok;
+    const int e0 = (int)((int64_t)n_tiles_part * s / NS);
+    e1 = (int)((int64_t)n_tiles_part * (s + 1) / NS);
+    e = e0 + wave;
+    // unconditional: the last split may grow past the hinted range once the count is known
+    mha_prepare<D, DENSE, false>(p, e, sel_row, sel_lds, lane, tp);
+    n_list = n_part;
+    if (!DENSE && p.n_hint > 0) {
+      int ns = p.n_sel[seg];
+      ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
+      n_list = p.L == 0 ? 0 : ns << p.unit_log2;
+      const int n_tiles = 1 + (n_list + kTileTok - 1) / kTileTok;
+      if (s == NS - 1) e1 = n_tiles;
+      e1 = e1 < n_tiles ? e1 : n_tiles;
+    }
   }
 
   // Q fragments (B operand of S^T = K Q^T): lane (q, hh) holds q[q][hh*D/2 + 8ks .. +8]
@@ -441,19 +557,19 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -__builtin_inff(), l_run = 0.f;
+  bool fresh = true;   // no tile accumulated yet (uniform)
 
-  // this wave's tiles: e0 + wave, e0 + wave + 8, ...
-  uint32_t vm_next = 0;
-  if (e < e1) vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e, n_list, tp, slot, lane, bad);
+  if (!issued && e < e1) vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e, n_list, tp, slot, lane, bad);
   const int swz_k = swz(ql) & (PROW - 1);
-  for (; e < e1; e += kMhaWaves) {
+  for (int en; e < e1; e = en) {
     // This tile's LDS fetches must have landed before the slot is read.  Explicit, because the
     // compiler's own wait for LDS fetches is not placed reliably across the loop back-edge when
     // other vector loads are in flight.
     wait_vm0();
     const uint32_t vm = vm_next;
-    const bool more = e + kMhaWaves < e1;
-    if (more) mha_prepare<D, DENSE, SEL>(p, e + kMhaWaves, sel_row, sel_lds, lane, tp);
+    en = (SEL && e < e_pre) ? e_rr : e + e_step;
+    const bool more = en < e1;
+    if (more) mha_prepare<D, DENSE, SEL>(p, en, sel_row, sel_lds, lane, tp);
     // ---- K from LDS into A-operand registers, then S^T = K Q^T: register r holds token
     //      8*(r/4) + 4*hh + r%4 for query ql (K registers die here) ----
     f32x16 sacc;
@@ -487,15 +603,17 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
           const int row = r0 + (x < 4 ? x : x + 4);
           w[x] = *reinterpret_cast<const uint32_t*>(vbase + row * D + ((cd ^ (swz(row) & (PROW - 1))) * 8) + dd);
         }
-        va[kl][2 * pp] = make_uint4((w[0] & 0xFFFFu) | (w[1] << 16), (w[2] & 0xFFFFu) | (w[3] << 16),
-                                    (w[4] & 0xFFFFu) | (w[5] << 16), (w[6] & 0xFFFFu) | (w[7] << 16));
-        va[kl][2 * pp + 1] = make_uint4((w[0] >> 16) | (w[1] & 0xFFFF0000u), (w[2] >> 16) | (w[3] & 0xFFFF0000u),
-                                        (w[4] >> 16) | (w[5] & 0xFFFF0000u), (w[6] >> 16) | (w[7] & 0xFFFF0000u));
+        // low halves of (w[2i], w[2i+1]) -> one word, high halves -> another (one byte permute each)
+        constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
+        va[kl][2 * pp] = make_uint4(__builtin_amdgcn_perm(w[1], w[0], kLo), __builtin_amdgcn_perm(w[3], w[2], kLo),
+                                    __builtin_amdgcn_perm(w[5], w[4], kLo), __builtin_amdgcn_perm(w[7], w[6], kLo));
+        va[kl][2 * pp + 1] = make_uint4(__builtin_amdgcn_perm(w[1], w[0], kHi), __builtin_amdgcn_perm(w[3], w[2], kHi),
+                                        __builtin_amdgcn_perm(w[5], w[4], kHi), __builtin_amdgcn_perm(w[7], w[6], kHi));
       }
     }
     wait_lgkm0();
     // ---- fetch the next tile into the same slot; it flies while this one is finished ----
-    if (more) vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e + kMhaWaves, n_list, tp, slot, lane, bad);
+    if (more) vm_next = mha_issue<D, DENSE, PAGED, false>(p, rows, b, h, en, n_list, tp, slot, lane, bad);
     float mx = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -506,23 +624,34 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
       mx = fmaxf(mx, x);
     }
     mx = fmaxf(mx, lane_xor32f(mx));
-    const float m_new = fmaxf(m_run, mx);
-    if (m_new != -__builtin_inff()) {
-      const float alpha = exp2f(m_run - m_new);
+    // Lazy rescaling: a query's running max m_run only moves when the tile's max exceeds it by more
+    // than kRescaleSlack (log2 units); the weights exp2(s - m_run) then stay below 2^kRescaleSlack,
+    // and most later tiles skip the rescaling of the accumulators.  The first tile always moves it
+    // (m_run = -inf); its accumulators are still zero and need no rescaling.
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__ballot(grow) != 0) {   // uniform
+      const float m_new = grow ? mx : m_run;
+      const float alpha = exp2_fast(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      if (!fresh) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+    }
+    fresh = false;
+    if (m_run != -__builtin_inff()) {
       float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = exp2f(sacc[r] - m_new);
+        const float pr = exp2_fast(sacc[r] - m_run);
         sacc[r] = pr;
         rs += pr;
       }
       rs += lane_xor32f(rs);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      l_run += rs;
       // ---- O^T += V^T P^T over 2 k-steps of 16 tokens ----
 #pragma unroll
       for (int kl = 0; kl < 2; ++kl) {
@@ -552,13 +681,13 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
 #pragma unroll
   for (int w = 0; w < kMhaWaves; ++w) M = fmaxf(M, s_m[w][ql]);
   const bool anyrow = M != -__builtin_inff();
-  const float scale = (anyrow && m_run != -__builtin_inff()) ? exp2f(m_run - M) : 0.f;
+  const float scale = (anyrow && m_run != -__builtin_inff()) ? exp2_fast(m_run - M) : 0.f;
   if (wave == 0 && hh == 0) {
     float Ls = 0.f;
 #pragma unroll
     for (int w = 0; w < kMhaWaves; ++w) {
       const float mw = s_m[w][ql];
-      Ls += (anyrow && mw != -__builtin_inff()) ? s_l[w][ql] * exp2f(mw - M) : 0.f;
+      Ls += (anyrow && mw != -__builtin_inff()) ? s_l[w][ql] * exp2_fast(mw - M) : 0.f;
     }
     s_fin[0][ql] = M;
     s_fin[1][ql] = Ls;
@@ -614,10 +743,40 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   if (s_ticket != (uint32_t)(NS - 1)) return;
   asm volatile("buffer_inv sc0" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
-  // every split's (max, sum) in one round trip, then per query the common max and the split weights
+  // Every split's (max, sum) and the partials of the first kMergeBatch splits are requested in one
+  // round trip (the statistics first, so that waiting for them leaves the partials in flight); per
+  // query the common max and the split weights then go through LDS.  Thread -> (d, 8 queries).
+  constexpr int kMergeBatch = 8;
+  static_assert(D * 4 <= NT, "one (d, 8 queries) item per thread");
   float* s_wt = reinterpret_cast<float*>(lds);   // [NS][32] weights, then [32] sums (slots are free)
   float2* s_ml2 = reinterpret_cast<float2*>(lds + 4096);   // [NS][32]
-  for (int i = tid; i < NS * 32; i += NT) s_ml2[i] = pml_base[seg * NS * 32 + i];
+  const bool item = tid < D * 4;
+  const int d = (tid >> 2) < D ? tid >> 2 : D - 1;
+  const int q0 = (tid & 3) * 8;
+  float2 ml[(kMaxSplits * 32 + NT - 1) / NT];
+#pragma unroll
+  for (int k = 0; k < (kMaxSplits * 32 + NT - 1) / NT; ++k) {
+    const int i = tid + k * NT;
+    if (i < NS * 32) ml[k] = pml_base[seg * NS * 32 + i];
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep the statistics loads ahead of the partials
+  float4 a[kMergeBatch], c[kMergeBatch];
+  auto load_batch = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int t = t0 + j < NS ? t0 + j : NS - 1;
+      const float* src = po_base + ((seg * NS + t) * D + d) * 32 + q0;
+      a[j] = *reinterpret_cast<const float4*>(src);
+      c[j] = *reinterpret_cast<const float4*>(src + 4);
+    }
+  };
+  load_batch(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < (kMaxSplits * 32 + NT - 1) / NT; ++k) {
+    const int i = tid + k * NT;
+    if (i < NS * 32) s_ml2[i] = ml[k];
+  }
   __syncthreads();
   if (tid < 32) {
     float M = -__builtin_inff();
@@ -625,38 +784,27 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     float Ls = 0.f;
     for (int t = 0; t < NS; ++t) {
       const float2 v = s_ml2[t * 32 + tid];
-      const float w = (v.x != -__builtin_inff() && M != -__builtin_inff()) ? exp2f(v.x - M) : 0.f;
+      const float w = (v.x != -__builtin_inff() && M != -__builtin_inff()) ? exp2_fast(v.x - M) : 0.f;
       s_wt[t * 32 + tid] = w;
       Ls += v.y * w;
     }
     s_wt[kMaxSplits * 32 + tid] = Ls;
   }
   __syncthreads();
-  // thread -> (d, 8 queries); the partials of kMergeBatch splits are loaded before any is used
-  constexpr int kMergeBatch = 8;
-  for (int it = tid; it < D * 4; it += NT) {
-    const int d = it >> 2;
-    const int q0 = (it & 3) * 8;
-    float o[8];
+  float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = 0.f;
-    for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
-      float4 a[kMergeBatch], c[kMergeBatch];
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
+    if (t0 > 0) load_batch(t0);
 #pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int t = t0 + j < NS ? t0 + j : NS - 1;
-        const float* src = po_base + ((seg * NS + t) * D + d) * 32 + q0;
-        a[j] = *reinterpret_cast<const float4*>(src);
-        c[j] = *reinterpret_cast<const float4*>(src + 4);
-      }
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        if (t0 + j >= NS) break;
-        const float* w = s_wt + (t0 + j) * 32 + q0;
-        o[0] += a[j].x * w[0]; o[1] += a[j].y * w[1]; o[2] += a[j].z * w[2]; o[3] += a[j].w * w[3];
-        o[4] += c[j].x * w[4]; o[5] += c[j].y * w[5]; o[6] += c[j].z * w[6]; o[7] += c[j].w * w[7];
-      }
+    for (int j = 0; j < kMergeBatch; ++j) {
+      if (t0 + j >= NS) break;
+      const float* w = s_wt + (t0 + j) * 32 + q0;
+      o[0] += a[j].x * w[0]; o[1] += a[j].y * w[1]; o[2] += a[j].z * w[2]; o[3] += a[j].w * w[3];
+      o[4] += c[j].x * w[4]; o[5] += c[j].y * w[5]; o[6] += c[j].z * w[6]; o[7] += c[j].w * w[7];
     }
+  }
+  if (item) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (q0 + i < p.T)

@@ -23,15 +23,24 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round-to-nearest-even float -> bf16 bits (finite inputs; used for probabilities and outputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> two bf16 (round to nearest even) in one word, lo in bits 0-15: one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+// Round-to-nearest-even float -> bf16 bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return pack_bf16x2(f, 0.f) & 0xFFFFu;
+}
+
+// 2^x with the bare hardware instruction: results below 2^-126 come out as zero, which changes no
+// softmax weight the kernels use (they are sums of at least one term equal to 1).
+__device__ __forceinline__ float exp2_fast(float x) {
+  return __builtin_amdgcn_exp2f(x);
 }
 
 // Unsigned key whose order is the numeric order of a float: -0 == +0, NaN lowest (0).
@@ -58,16 +67,23 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
-// Value of lane (lane ^ J) for a compile-time J: quad permutes for 1 and 2, swizzles (within 32
-// lanes) for 4, 8 and 16, the half swap for 32.
+// Value of lane (lane ^ J) for a compile-time J, without the LDS pipe: DPP quad permutes for 1 and 2;
+// for 4 the half-row mirror (lane ^ 7) followed by the quad reversal (lane ^ 3); for 8 a rotation of
+// the 16-lane row by 8; for 16 and 32 the row / half swaps.  A swap of a register with itself
+// leaves, in every lane, the lane's own value in one result and the partner's in the other (when
+// the two are equal either is right).
 template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
   else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-  else if constexpr (J == 4 || J == 8 || J == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
-  else if constexpr (J == 32) {
-    // swap of the two 32-lane halves; in every lane one of the two results is the lane's own value
-    // and the other the partner's (when they are equal, either is right)
+  else if constexpr (J == 4) {
+    const int m = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);      // quad_perm 3,2,1,0
+  } else if constexpr (J == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);   // row_ror 8
+  else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (r[0] == v) ? r[1] : r[0];
+  } else if constexpr (J == 32) {
     const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return (r[0] == v) ? r[1] : r[0];
   } else {

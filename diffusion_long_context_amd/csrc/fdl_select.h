@@ -255,4 +255,163 @@ __device__ SelResult select_small(const uint32_t* keys, const uint32_t* forced, 
   return {total, kk};
 }
 
+// 32-bit descending bitonic sort across the wave: lane l ends with the l-th largest value.
+// Lanes that keep the larger value at step (K, J) of the network, as a 64-bit lane mask.
+constexpr uint64_t keep_max_mask(int K, int J) {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (((l & J) == 0) != ((l & K) != 0)) m |= 1ull << l;
+  return m;
+}
+
+// v = m[lane] ? a : b, with m a wave-uniform lane mask (one VALU select on a scalar pair).
+__device__ __forceinline__ uint32_t select_lanes(uint64_t m, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+  return r;
+}
+
+// hi / lo = max / min of v and the value of lane (lane ^ J).  For J = 1, 2, 8 the partner's value is
+// read through a DPP operand of the max and the min themselves; J = 4 takes one DPP move first
+// (half-row mirror, then the quad reversal in the operand: lane ^ 7 ^ 3); 16 and 32 use the row /
+// half swaps.  The leading s_nop covers the wait states a DPP read of a just-written VGPR needs.
+template <int J>
+__device__ __forceinline__ void xor_minmax(uint32_t v, uint32_t& hi, uint32_t& lo) {
+  if constexpr (J == 1) {
+    asm("s_nop 1\n\tv_max_u32_dpp %0, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_min_u32_dpp %1, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "=&v"(hi), "=&v"(lo) : "v"(v));
+  } else if constexpr (J == 2) {
+    asm("s_nop 1\n\tv_max_u32_dpp %0, %2, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_min_u32_dpp %1, %2, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "=&v"(hi), "=&v"(lo) : "v"(v));
+  } else if constexpr (J == 8) {
+    asm("s_nop 1\n\tv_max_u32_dpp %0, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_min_u32_dpp %1, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xf"
+        : "=&v"(hi), "=&v"(lo) : "v"(v));
+  } else if constexpr (J == 4) {
+    uint32_t t;
+    asm("s_nop 1\n\tv_mov_b32_dpp %2, %3 row_half_mirror row_mask:0xf bank_mask:0xf\n\ts_nop 1\n\t"
+        "v_max_u32_dpp %0, %2, %3 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_min_u32_dpp %1, %2, %3 quad_perm:[3,2,1,0] row_mask:0xf bank_mask:0xf"
+        : "=&v"(hi), "=&v"(lo), "=&v"(t) : "v"(v));
+  } else {
+    static_assert(J == 16 || J == 32, "lane distance");
+    // after a swap of v with itself the lanes with bit J set hold the partner in the first result,
+    // the others in the second
+    const auto r = J == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    constexpr uint64_t up = J == 16 ? 0xFFFF0000FFFF0000ull : 0xFFFFFFFF00000000ull;
+    const uint32_t o = select_lanes(up, r[0], r[1]);
+    hi = v > o ? v : o;
+    lo = v < o ? v : o;
+  }
+}
+
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step32(uint32_t& v) {
+  uint32_t hi, lo;
+  xor_minmax<J>(v, hi, lo);
+  v = select_lanes(keep_max_mask(K, J), hi, lo);
+}
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge32(uint32_t& v) {
+  bitonic_step32<K, J>(v);
+  if constexpr (J > 1) bitonic_merge32<K, J / 2>(v);
+}
+template <int K = 64>
+__device__ __forceinline__ void wave_sort_desc32(uint32_t& v) {
+  if constexpr (K > 2) wave_sort_desc32<K / 2>(v);
+  bitonic_merge32<K, K / 2>(v);
+}
+
+// The same selection as select_core for n <= NT and top_k <= 64, found through a threshold.  The
+// eligible keys (forced units and threads past n count as 0, which no eligible key is below) are
+// sorted within each wave; a tournament then keeps the 64 largest: two descending runs A and B
+// give the 64 largest of their union as the bitonic sequence max(A[l], B[63 - l]), which the last
+// six steps of the sort put in order.  The kk-th largest value theta is the threshold: every
+// eligible unit with a larger key is taken, and of those equal to theta the lowest-indexed ones, as
+// many as are still missing.  Forced units are always taken.  Ballots count all three kinds per
+// wave, so the output positions need no further pass: emit(gpos, lpos, i) gets unit i's place in
+// the ascending list of every taken unit (gpos) and in the list of the forced units (ascending)
+// followed by the chosen ones (ascending) (lpos).
+// runs: LDS [NT - 64] words; cnt: LDS [3 * NT / 64 + 1] ints.
+template <int NT, typename Emit>
+__device__ SelResult select_top64(const uint32_t* keys, const uint32_t* forced, int n, int top_k, uint32_t* runs,
+                                  int* cnt, Emit emit) {
+  constexpr int NW = NT / 64;
+  static_assert(NW >= 1 && (NW & (NW - 1)) == 0, "power-of-two wave count");
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  int* n_f = cnt;               // [NW] forced units per wave
+  int* n_gt = cnt + NW;         // [NW] eligible keys above theta
+  int* n_eq = cnt + 2 * NW;     // [NW] eligible keys equal to theta
+  int* theta_w = cnt + 3 * NW;  // [1]
+  const bool valid = t < n;
+  const bool f = valid && ((forced[t >> 5] >> (t & 31)) & 1u) != 0u;
+  const bool elig = valid && !f;
+  const uint32_t key = valid ? keys[t] : 0u;
+  uint32_t v = elig ? key : 0u;
+  const uint64_t fmask = __ballot(f);
+  if (lane == 0) n_f[wave] = __popcll(fmask);
+  wave_sort_desc32(v);
+  // tournament: at each level waves [half, 2 half) hand their runs to waves [0, half); every level
+  // has slots of its own, so a level's writers never meet the previous level's readers
+  uint32_t* slots = runs;
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) slots[(wave - half) * 64 + lane] = v;
+    __syncthreads();
+    if (wave < half) {
+      const uint32_t o = slots[wave * 64 + 63 - lane];
+      v = v > o ? v : o;
+      bitonic_merge32<64, 32>(v);
+    }
+    slots += half * 64;
+  }
+  if constexpr (NW == 1) __syncthreads();   // n_f
+  int n_forced = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) n_forced += n_f[w];
+  const int n_elig = n - n_forced;
+  const int kk = top_k < n_elig ? top_k : n_elig;
+  if (wave == 0) {
+    // with nothing to take the threshold is all ones, which no key reaches (+inf's key is below)
+    const uint32_t th = __shfl(v, kk > 0 ? kk - 1 : 0, 64);
+    if (lane == 0) *theta_w = kk > 0 ? (int)th : -1;
+  }
+  __syncthreads();
+  const uint32_t theta = (uint32_t)*theta_w;
+  const bool gt = elig && key > theta, eq = elig && key == theta;
+  const uint64_t gmask = __ballot(gt), emask = __ballot(eq);
+  if (lane == 0) {
+    n_gt[wave] = __popcll(gmask);
+    n_eq[wave] = __popcll(emask);
+  }
+  __syncthreads();
+  int above = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) above += n_gt[w];
+  const int rem = kk - above;   // ties still to take, lowest index first
+  int f_base = 0, c_base = 0, eq_before = 0, my_ties = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    int tw = rem - eq_before;
+    tw = tw < 0 ? 0 : (tw > n_eq[w] ? n_eq[w] : tw);
+    if (w < wave) {
+      f_base += n_f[w];
+      c_base += n_gt[w] + tw;
+    }
+    if (w == wave) my_ties = tw;
+    eq_before += n_eq[w];
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  const bool chosen = gt || (eq && __popcll(emask & below) < my_ties);
+  const uint64_t cmask = __ballot(chosen);
+  if (f || chosen) {
+    const int fr = f_base + __popcll(fmask & below), cr = c_base + __popcll(cmask & below);
+    emit(fr + cr, f ? fr : n_forced + cr, t);
+  }
+  return {n_forced + (kk > 0 ? kk : 0), kk};
+}
+
 }  // namespace fdl
