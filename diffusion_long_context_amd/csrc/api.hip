@@ -184,9 +184,9 @@ fdl_status run_attn(fdl_handle h, const Geom& g, const void* q, const void* k_ca
 
 // Score, select and attend in one kernel (one q-head per KV head, bf16, contiguous cache): same
 // outputs as run_score_units + run_select + run_attn.
-bool fused_select_ok(const Geom& g, int n_blk, int max_sel) {
+bool fused_select_ok(const Geom& g, int n_blk, int max_sel, int max_sinks) {
   return g.dtype == FDL_BF16 && g.G == 1 && !g.paged && g.L > 0 && n_blk <= fdl::kFusedMaxUnits &&
-         max_sel <= fdl::kFusedMaxSel;
+         max_sel <= fdl::kFusedMaxSel && max_sinks <= fdl::kFusedMaxSinks;
 }
 
 fdl_status run_select_attn(fdl_handle h, const Geom& g, const fdl_layer_io& io, const uint64_t* pred_mask,
@@ -502,7 +502,7 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_para
       if (st != FDL_OK) return st;
       continue;
     }
-    const bool fused = fused_select_ok(g, n_blk, fp->max_sel);
+    const bool fused = fused_select_ok(g, n_blk, fp->max_sel, fp->max_sinks);
     if (!fused) {
       st = run_score_units(h, g, io.q, pred_mask, io.ks, n_blk, scores);
       if (st != FDL_OK) return st;

@@ -654,7 +654,7 @@ static hipError_t launch_attn_other(hipStream_t s, const Geom& g, const void* q,
   hipError_t err = g.D == 128 ? launch_mfma_g<128>(s, p, grid, g.G, dense != 0, g.paged != 0)
                               : launch_mfma_g<64>(s, p, grid, g.G, dense != 0, g.paged != 0);
   if (err != hipSuccess || n_splits == 1) return err;
-  return launch_attn_combine(s, p.part_o, p.part_ml, out, g.B * g.Hq, n_splits, g.T, g.D, false);
+  return launch_attn_combine(s, p.part_o, p.part_ml, out, g.B * g.Hq, n_splits, g.T, g.D);
 }
 
 hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,

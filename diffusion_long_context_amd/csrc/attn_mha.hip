@@ -46,7 +46,7 @@ struct MhaParams {
   const int32_t* sel_idx;
   const int32_t* n_sel;
   uint16_t* out;
-  float* part_o;     // [B][H][S][D][32] (d-major)
+  float* part_o;     // [B][H][S][32][D]
   float2* part_ml;   // [B][H][S][32]
   uint32_t* tickets;  // one per (b, h); left at zero by every launch
   uint32_t* status;
@@ -152,18 +152,33 @@ __device__ bool head_barrier(uint32_t* bar, uint32_t g0, int NS, int spin_limit,
 // kRowBatch rows: lane l of wave w holds 16 floats of row base + ps*RPP + w*RPW + l/LPR.
 constexpr int kScoreBatch = 4;   // passes whose loads fly together
 
+// Passes [ps0, kScoreBatch) of the batch at base; ps0 = 1 after mha_load_first_pass.
 template <int D>
 __device__ __forceinline__ void mha_load_rows(const float* __restrict__ ksh, int base, int rb,
-                                              float (&x)[kScoreBatch][16]) {
+                                              float (&x)[kScoreBatch][16], int ps0 = 0) {
   constexpr int LPR = D / 16, RPW = 64 / LPR, RPP = kMhaWaves * RPW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int ps = 0; ps < kScoreBatch; ++ps) {
+    if (ps < ps0) continue;
     if (base + ps * RPP >= rb) break;   // uniform: no row of this pass is wanted
     int r = base + ps * RPP + wave * RPW + lane / LPR;
     r = r < rb ? r : rb - 1;
     load16<float>(ksh + (int64_t)r * D + 16 * (lane % LPR), x[ps]);
   }
+}
+
+// Pass 0 of the batch at base, loaded unconditionally (rows clamped to [0, rb - 1]): a fixed number
+// of loads, so that a later wait for loads issued before these can leave them in flight.
+template <int D>
+__device__ __forceinline__ void mha_load_first_pass(const float* __restrict__ ksh, int base, int rb,
+                                                    float (&x)[kScoreBatch][16]) {
+  constexpr int LPR = D / 16, RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int r = base + wave * RPW + lane / LPR;
+  r = r < rb ? r : rb - 1;
+  r = r > 0 ? r : 0;
+  load16<float>(ksh + (int64_t)r * D + 16 * (lane % LPR), x[0]);
 }
 
 // keys[r] = order_key(score) and, when to_global, scores[r] as well, for the batch at base.
@@ -184,7 +199,7 @@ __device__ __forceinline__ void mha_dot_rows(const float (&x)[kScoreBatch][16], 
   }
 }
 
-// Rows [ra, rb); the first batch may already be loaded (x, pre = true).
+// Rows [ra, rb); pass 0 of the first batch may already be loaded (x, pre = true).
 template <int D>
 __device__ __forceinline__ void mha_score_rows(const float* __restrict__ ksh, int ra, int rb, const float (&qv)[16],
                                                uint32_t* keys, float* __restrict__ scores, bool to_global,
@@ -192,7 +207,7 @@ __device__ __forceinline__ void mha_score_rows(const float* __restrict__ ksh, in
   constexpr int RPP = kMhaWaves * (64 / (D / 16));
   if (rb <= ra) return;   // uniform
   for (int base = ra; base < rb; base += kScoreBatch * RPP) {
-    if (!(pre && base == ra)) mha_load_rows<D>(ksh, base, rb, x);
+    mha_load_rows<D>(ksh, base, rb, x, (pre && base == ra) ? 1 : 0);
     mha_dot_rows<D>(x, base, rb, qv, keys, scores, to_global);
   }
 }
@@ -245,6 +260,27 @@ __device__ __forceinline__ bool threshold_select_ok(int n, int top_k) {
   return n <= kMhaWaves * 64 && top_k <= 64;
 }
 
+// The list of the forced units (ascending) at the front of sel_lds, written by one wave; the count
+// goes to *nf_out.  n <= NT, so the NT / 32 <= 16 bit words fit one 16-lane row: lane w holds word w,
+// a DPP scan along the row gives the number of forced units before it, and each lane writes its
+// own units.
+template <int NT>
+__device__ __forceinline__ void mha_forced_list(const uint32_t* forced, int n, int max_sel, uint16_t* sel_lds,
+                                                int* nf_out) {
+  static_assert(NT / 32 <= 16, "bit words in one row");
+  const int lane = threadIdx.x & 63;
+  const int nw = (n + 31) / 32;
+  uint32_t word = lane < nw ? forced[lane] : 0u;
+  if (lane == nw - 1 && (n & 31) != 0) word &= (1u << (n & 31)) - 1u;
+  const int c = __popc(word);
+  const int incl = row_incl_scan(c);
+  int pos = incl - c;
+  for (uint32_t w = word; w != 0u; w &= w - 1u, ++pos)
+    if (pos < max_sel) sel_lds[pos] = (uint16_t)(32 * lane + __builtin_ctz(w));
+  const int nf = __builtin_amdgcn_readlane(incl, 15);
+  if (lane == 0) *nf_out = nf;
+}
+
 template <int D>
 __device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, int NS, uint16_t* lds_raw,
                                uint16_t* sel_lds) {
@@ -252,6 +288,7 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, in
   constexpr int LPR = D / 16;
   static_assert((kQbufOffsetF + 32 * D) * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * MhaShape<D>::SLOT,
                 "query staging must fit in the tile slots");
+  static_assert(kFusedMaxSinks <= NT, "one sink list entry per thread");
   const FusedSelect& f = p.fs;
   const SelLds<D> L(lds_raw);
   const int tid = threadIdx.x;
@@ -263,31 +300,47 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, in
   uint32_t g0 = 0;
   if (NS > 1 && tid == 0) g0 = head_barrier_gen(bar);
 
+  // Loads in the order they are needed, so that each wait leaves the later ones in flight (the
+  // counter of outstanding loads drains in order): the queries, the sink list (thread t < max_sinks
+  // holds entry t; the count trims it once the loads are back), then the pooled-key rows.
+  QsumG1<D, 32, NT> qst;
+  qsum_g1_issue<D, 32, NT>(p.q + seg * (int64_t)p.T * D, p.T, qst);
+  // (every load unconditional, from a valid address: a load under a branch would make the waits
+  // below count conservatively)
+  const uint64_t pred = f.pred_mask[b];
+  const bool have_sinks = f.sink_pos != nullptr;
+  const bool sink_lane = have_sinks && tid < f.max_sinks;
+  const int32_t* sp = have_sinks ? f.sink_pos + (int64_t)b * f.max_sinks + (tid < f.max_sinks ? tid : 0)
+                                 : reinterpret_cast<const int32_t*>(f.pred_mask + b);
+  const int sink_p = *sp;
+  const int sink_n = have_sinks ? f.n_sinks[b] : 0;
   const int ra = (int)((int64_t)n * s / NS), rb = (int)((int64_t)n * (s + 1) / NS);
   float x[kScoreBatch][16];
   const bool pre = rb > ra;
-  if (pre) mha_load_rows<D>(ksh, ra, rb, x);   // in flight during the query sum
+  __builtin_amdgcn_sched_barrier(0);
+  mha_load_first_pass<D>(ksh, ra, rb, x);   // in flight during the query sum
+  __builtin_amdgcn_sched_barrier(0);
   for (int i = tid; i < (n + 31) / 32; i += NT) L.forced[i] = 0u;
   // the query staging area sits above the keys' scratch in the (still unused) tile slots
-  query_sum_g1_coop<D, 32, NT>(p.q + seg * (int64_t)p.T * D, f.pred_mask[b], p.T,
-                               reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, L.qs);
-  __syncthreads();   // qs and the cleared bits
-  if (f.sink_pos != nullptr) {
-    int ns = f.n_sinks[b];
-    ns = ns < f.max_sinks ? ns : f.max_sinks;
-    for (int t = tid; t < ns; t += NT) {
-      const int pos = f.sink_pos[(int64_t)b * f.max_sinks + t];
-      if (pos < 0) continue;
-      const int u = pos >> p.unit_log2;
-      if (u < n) atomicOr(&L.forced[u >> 5], 1u << (u & 31));
-    }
+  qsum_g1_finish<D, 32, NT>(qst, pred, p.T, reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, L.qs);
+  block_sync_lds();   // qs and the cleared bits
+  if (sink_lane && tid < sink_n && sink_p >= 0) {
+    const int u = sink_p >> p.unit_log2;
+    if (u < n) atomicOr(&L.forced[u >> 5], 1u << (u & 31));
   }
   float qv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) qv[i] = L.qs[16 * j + i];
   mha_score_rows<D>(ksh, ra, rb, qv, L.keys, sc_out, true, x, pre);
+  const bool listing = threshold_select_ok(n, f.top_k);   // uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  bool listed = false;
   if (NS > 1) {
-    if (head_barrier(bar, g0, NS, f.spin_limit, L.flag)) {
+    const bool synced = head_barrier(bar, g0, NS, f.spin_limit, L.flag);   // forced bits are complete
+    // wave 0 lists the forced units while the others read the scores back
+    if (listing && wave == 0) mha_forced_list<NT>(L.forced, n, p.max_sel, sel_lds, L.flag + 1);
+    listed = true;
+    if (synced) {
       for (int i = tid; i < n; i += NT)
         if (i < ra || i >= rb) L.keys[i] = order_key(sc_out[i]);
     } else {
@@ -296,19 +349,13 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, in
       if (tid == 0) latch(p.status, ST_SYNC_FALLBACK);
     }
   }
-  __syncthreads();   // keys and forced bits complete
-  if (!threshold_select_ok(n, f.top_k)) return 0;   // uniform
-  // forced list: the place of unit t is the number of forced units below it (n <= NT: at most
-  // NT / 32 words, all read at once)
-  int nf = 0, below = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 32; ++w) {
-    const uint32_t word = w < (n + 31) / 32 ? L.forced[w] : 0u;
-    nf += __popc(word);
-    below += (w < (tid >> 5)) ? __popc(word) : (w == (tid >> 5) ? __popc(word & ((1u << (tid & 31)) - 1u)) : 0);
+  block_sync_lds();   // keys and forced bits complete
+  if (!listing) return 0;   // uniform
+  if (!listed) {
+    if (wave == 0) mha_forced_list<NT>(L.forced, n, p.max_sel, sel_lds, L.flag + 1);
+    block_sync_lds();
   }
-  if (tid < n && ((L.forced[tid >> 5] >> (tid & 31)) & 1u) && below < p.max_sel) sel_lds[below] = (uint16_t)tid;
-  __syncthreads();
+  const int nf = __builtin_amdgcn_readfirstlane(L.flag[1]);
   return nf < p.max_sel ? nf : p.max_sel;
 }
 
@@ -345,7 +392,7 @@ __device__ int mha_choose_phase(const MhaParams& p, int64_t seg, int s, uint16_t
   }
   if (writer && tid == 0) f.n_sel[seg] = r.total < p.max_sel ? r.total : p.max_sel;
   if (tid == 0 && r.total > p.max_sel) latch(p.status, ST_SEL_OVERFLOW);
-  __syncthreads();   // sel_lds complete; the slots are free again
+  block_sync_lds();   // sel_lds complete; the slots are free again
   return r.total < p.max_sel ? r.total : p.max_sel;
 }
 
@@ -450,7 +497,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   constexpr int NT = kMhaWaves * 64;
   constexpr int KS = S::KS, DT = S::DT, PROW = S::PROW;
   static_assert(!SEL || (!DENSE && !PAGED), "fused selection: contiguous sparse only");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kMhaWaves * S::SLOT];
+  // tile slots; the 8-wave merge reuses them with 16 bytes of padding per query row
+  constexpr int kLdsElems = kMhaWaves * S::SLOT > kMhaWaves * 32 * (D + 4) * 2 ? kMhaWaves * S::SLOT
+                                                                               : kMhaWaves * 32 * (D + 4) * 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
   __shared__ uint16_t sel_lds[SEL ? kFusedMaxSel : 1];
 
   // Workgroup i runs on XCD i % 8 (the dispatcher's round-robin order).  All splits of one head
@@ -692,42 +742,54 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     s_fin[0][ql] = M;
     s_fin[1][ql] = Ls;
   }
-  float* mo = reinterpret_cast<float*>(lds);   // [wave][D][32], d-major
-  static_assert(kMhaWaves * 32 * D * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * S::SLOT,
-                "merge buffer must fit in the tile slots");
+  // Wave partials go to LDS query-major, rows padded by 4 floats (rows 16 bytes apart modulo the
+  // banks): lane (q, hh) holds, for each (dtp, rg), the eight consecutive d = 64 dtp + 16 rg + 8 hh
+  // + [0, 8) of query q (registers r = 4 rg + [0, 4) of MFMAs 2 dtp and 2 dtp + 1), two 16-byte
+  // writes.  Then thread -> (query q, 16-byte chunks dg and dg + D / 8 of its row): each group of
+  // 16 lanes reads 256 consecutive bytes.
+  constexpr int DP = D + 4;
+  constexpr int HC = D / 8;   // 16-byte chunks per half row
+  float* mo = reinterpret_cast<float*>(lds);   // [wave][32][DP]
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int dtp = 0; dtp < DT / 2; ++dtp)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int di = 8 * (r >> 2) + 4 * hh + (r & 3);
-      const int d = 64 * (dt >> 1) + 2 * di + (dt & 1);
-      mo[(wave * D + d) * 32 + ql] = oacc[dt][r] * scale;
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x16& a = oacc[2 * dtp];
+      const f32x16& c = oacc[2 * dtp + 1];
+      float* dst = mo + (wave * 32 + ql) * DP + 64 * dtp + 16 * rg + 8 * hh;
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(a[4 * rg] * scale, c[4 * rg] * scale, a[4 * rg + 1] * scale, c[4 * rg + 1] * scale);
+      *reinterpret_cast<float4*>(dst + 4) =
+          make_float4(a[4 * rg + 2] * scale, c[4 * rg + 2] * scale, a[4 * rg + 3] * scale, c[4 * rg + 3] * scale);
     }
   __syncthreads();
-  // thread -> (d, 8 queries q0..q0+7); 512 threads cover D * 4 items for D = 128 (loop for D = 64)
+  static_assert(32 * HC <= NT, "one (query, chunk pair) item per thread");
+  const bool item = tid < 32 * HC;
+  const int qi = item ? tid / HC : 0, dg = tid % HC;
   float* po_base = p.part_o;
   float2* pml_base = p.part_ml;
-  for (int it = tid; it < D * 4; it += NT) {
-    const int d = it >> 2;
-    const int q0 = (it & 3) * 8;
-    float o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  {
+    float4 o1 = make_float4(0.f, 0.f, 0.f, 0.f), o2 = o1;
 #pragma unroll
     for (int w = 0; w < kMhaWaves; ++w) {
-      const float4 a = *reinterpret_cast<const float4*>(mo + (w * D + d) * 32 + q0);
-      const float4 c = *reinterpret_cast<const float4*>(mo + (w * D + d) * 32 + q0 + 4);
-      o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
-      o[4] += c.x; o[5] += c.y; o[6] += c.z; o[7] += c.w;
+      const float* src = mo + (w * 32 + qi) * DP + 4 * dg;
+      const float4 a = *reinterpret_cast<const float4*>(src);
+      const float4 c = *reinterpret_cast<const float4*>(src + 4 * HC);
+      o1.x += a.x; o1.y += a.y; o1.z += a.z; o1.w += a.w;
+      o2.x += c.x; o2.y += c.y; o2.z += c.z; o2.w += c.w;
     }
     if (NS == 1) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (q0 + i < p.T) p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(o[i] / s_fin[1][q0 + i]);
-    } else {
-      float* dst = po_base + ((seg * NS + s) * D + d) * 32 + q0;
-      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      if (item && qi < p.T) {
+        const float inv = 1.f / s_fin[1][qi];
+        uint16_t* dst = p.out + (seg * p.T + qi) * D + 4 * dg;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o1.x * inv, o1.y * inv), pack_bf16x2(o1.z * inv, o1.w * inv));
+        *reinterpret_cast<uint2*>(dst + 4 * HC) =
+            make_uint2(pack_bf16x2(o2.x * inv, o2.y * inv), pack_bf16x2(o2.z * inv, o2.w * inv));
+      }
+    } else if (item) {
+      float* dst = po_base + ((seg * NS + s) * 32 + qi) * D + 4 * dg;
+      *reinterpret_cast<float4*>(dst) = o1;
+      *reinterpret_cast<float4*>(dst + 4 * HC) = o2;
     }
   }
   if (NS == 1) return;
@@ -745,14 +807,11 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   __builtin_amdgcn_s_waitcnt(0);
   // Every split's (max, sum) and the partials of the first kMergeBatch splits are requested in one
   // round trip (the statistics first, so that waiting for them leaves the partials in flight); per
-  // query the common max and the split weights then go through LDS.  Thread -> (d, 8 queries).
+  // query the common max and the split weights then go through LDS.  Same thread -> (query,
+  // chunk pair) items as above.
   constexpr int kMergeBatch = 8;
-  static_assert(D * 4 <= NT, "one (d, 8 queries) item per thread");
   float* s_wt = reinterpret_cast<float*>(lds);   // [NS][32] weights, then [32] sums (slots are free)
   float2* s_ml2 = reinterpret_cast<float2*>(lds + 4096);   // [NS][32]
-  const bool item = tid < D * 4;
-  const int d = (tid >> 2) < D ? tid >> 2 : D - 1;
-  const int q0 = (tid & 3) * 8;
   float2 ml[(kMaxSplits * 32 + NT - 1) / NT];
 #pragma unroll
   for (int k = 0; k < (kMaxSplits * 32 + NT - 1) / NT; ++k) {
@@ -765,9 +824,9 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       const int t = t0 + j < NS ? t0 + j : NS - 1;
-      const float* src = po_base + ((seg * NS + t) * D + d) * 32 + q0;
+      const float* src = po_base + ((seg * NS + t) * 32 + qi) * D + 4 * dg;
       a[j] = *reinterpret_cast<const float4*>(src);
-      c[j] = *reinterpret_cast<const float4*>(src + 4);
+      c[j] = *reinterpret_cast<const float4*>(src + 4 * HC);
     }
   };
   load_batch(0);
@@ -777,38 +836,43 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     const int i = tid + k * NT;
     if (i < NS * 32) s_ml2[i] = ml[k];
   }
-  __syncthreads();
+  block_sync_lds();   // the partial loads stay in flight
   if (tid < 32) {
+    // every split slot is read (in flight together) and the ones past NS masked: a read guarded by
+    // the runtime split count would be waited for one at a time
+    float2 v[kMaxSplits];
+#pragma unroll
+    for (int t = 0; t < kMaxSplits; ++t) v[t] = s_ml2[t * 32 + tid];
     float M = -__builtin_inff();
-    for (int t = 0; t < NS; ++t) M = fmaxf(M, s_ml2[t * 32 + tid].x);
+#pragma unroll
+    for (int t = 0; t < kMaxSplits; ++t) M = t < NS ? fmaxf(M, v[t].x) : M;
     float Ls = 0.f;
-    for (int t = 0; t < NS; ++t) {
-      const float2 v = s_ml2[t * 32 + tid];
-      const float w = (v.x != -__builtin_inff() && M != -__builtin_inff()) ? exp2_fast(v.x - M) : 0.f;
-      s_wt[t * 32 + tid] = w;
-      Ls += v.y * w;
+#pragma unroll
+    for (int t = 0; t < kMaxSplits; ++t) {
+      const float w = (t < NS && v[t].x != -__builtin_inff() && M != -__builtin_inff()) ? exp2_fast(v[t].x - M) : 0.f;
+      if (t < NS) s_wt[t * 32 + tid] = w;
+      Ls += t < NS ? v[t].y * w : 0.f;
     }
     s_wt[kMaxSplits * 32 + tid] = Ls;
   }
-  __syncthreads();
-  float o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  block_sync_lds();
+  float4 o1 = make_float4(0.f, 0.f, 0.f, 0.f), o2 = o1;
   for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
     if (t0 > 0) load_batch(t0);
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       if (t0 + j >= NS) break;
-      const float* w = s_wt + (t0 + j) * 32 + q0;
-      o[0] += a[j].x * w[0]; o[1] += a[j].y * w[1]; o[2] += a[j].z * w[2]; o[3] += a[j].w * w[3];
-      o[4] += c[j].x * w[4]; o[5] += c[j].y * w[5]; o[6] += c[j].z * w[6]; o[7] += c[j].w * w[7];
+      const float w = s_wt[(t0 + j) * 32 + qi];
+      o1.x += a[j].x * w; o1.y += a[j].y * w; o1.z += a[j].z * w; o1.w += a[j].w * w;
+      o2.x += c[j].x * w; o2.y += c[j].y * w; o2.z += c[j].z * w; o2.w += c[j].w * w;
     }
   }
-  if (item) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (q0 + i < p.T)
-        p.out[(seg * p.T + q0 + i) * D + d] = (uint16_t)f32_to_bf16_bits(o[i] / s_wt[kMaxSplits * 32 + q0 + i]);
+  if (item && qi < p.T) {
+    const float inv = 1.f / s_wt[kMaxSplits * 32 + qi];
+    uint16_t* dst = p.out + (seg * p.T + qi) * D + 4 * dg;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o1.x * inv, o1.y * inv), pack_bf16x2(o1.z * inv, o1.w * inv));
+    *reinterpret_cast<uint2*>(dst + 4 * HC) =
+        make_uint2(pack_bf16x2(o2.x * inv, o2.y * inv), pack_bf16x2(o2.z * inv, o2.w * inv));
   }
   if (tid == 0) p.tickets[seg * kSyncStride] = 0u;
 }
@@ -817,7 +881,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
 // the kernel boundary makes the partials visible without a device-wide cache flush, which an
 // in-kernel "last workgroup merges" handoff would need on a multi-die GPU.
 // grid (B*H, 4): each workgroup merges 8 queries of one head.
-template <int D, bool DMAJOR>
+template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float2* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out, int NS, int T) {
@@ -833,8 +897,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     float Ls = 0.f, O = 0.f;
     for (int t = 0; t < NS; ++t) {
       const float2 v = ml[t * 32];
-      const float o = DMAJOR ? part_o[((seg * NS + t) * D + d) * 32 + q]
-                             : part_o[((seg * NS + t) * 32 + q) * D + d];
+      const float o = part_o[((seg * NS + t) * 32 + q) * D + d];
       if (v.y == 0.f) continue;
       const float wgt = exp2f(v.x - M);
       Ls += v.y * wgt;
@@ -845,15 +908,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 }
 
 hipError_t launch_attn_combine(hipStream_t st, const float* part_o, const float2* part_ml, void* out,
-                               int n_segs, int NS, int T, int D, bool dmajor) {
+                               int n_segs, int NS, int T, int D) {
   dim3 grid(n_segs, (T + 7) / 8);
   uint16_t* o = static_cast<uint16_t*>(out);
   if (D == 128) {
-    if (dmajor) hipLaunchKernelGGL((attn_combine_kernel<128, true>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
-    else hipLaunchKernelGGL((attn_combine_kernel<128, false>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
+    hipLaunchKernelGGL((attn_combine_kernel<128>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
   } else {
-    if (dmajor) hipLaunchKernelGGL((attn_combine_kernel<64, true>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
-    else hipLaunchKernelGGL((attn_combine_kernel<64, false>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
+    hipLaunchKernelGGL((attn_combine_kernel<64>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
   }
   return hipGetLastError();
 }

@@ -93,6 +93,17 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
 
 __device__ __forceinline__ float lane_xor32f(float v) { return __uint_as_float(lane_xor<32>(__float_as_uint(v))); }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are complete, then s_barrier.
+// __syncthreads() also waits for every outstanding vector-memory operation (its release fence has to
+// cover LDS written by global->LDS fetches still in flight), which would hold the barrier behind
+// loads and fetches issued for later use.  The memory clobbers keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void latch(uint32_t* status, uint32_t bit) {
   atomicOr(status, bit);
 }

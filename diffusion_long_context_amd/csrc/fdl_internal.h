@@ -65,6 +65,7 @@ struct KernelTimer {
 // blocks against the predicted queries and selects sinks + top-K itself.
 constexpr int kFusedMaxUnits = 4096;   // blocks per head the fused path keeps in LDS
 constexpr int kFusedMaxSel = 4096;     // selected blocks per head
+constexpr int kFusedMaxSinks = 512;    // sink list entries (one per thread of the fused kernel)
 struct FusedSelect {
   const uint64_t* pred_mask;   // [B]
   const float* ks;             // pooled keys [B][H][n_units][D]
@@ -131,7 +132,7 @@ hipError_t launch_attn_mha(hipStream_t s, const Geom& g, const void* q, const vo
                            const FusedSelect* fsel = nullptr);
 
 hipError_t launch_attn_combine(hipStream_t s, const float* part_o, const float2* part_ml, void* out,
-                               int n_segs, int n_splits, int T, int D, bool dmajor);
+                               int n_segs, int n_splits, int T, int D);
 
 hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, size_t n, uint32_t v);
 

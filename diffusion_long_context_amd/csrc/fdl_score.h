@@ -75,21 +75,42 @@ __device__ __forceinline__ void query_sum_to_lds(const QT* __restrict__ q, uint6
 // p of the head's queries is read as D / 8 sixteen-byte chunks, masked (p predicted and p < T) into
 // qbuf [TMAX][D] float32 in LDS, and threads d < D then build the same adjacent-pair tree over the
 // TMAX rows as query_sum_to_lds.  Same bits; one round trip instead of TMAX narrow loads per thread.
+// Two halves, so that a caller can issue other loads between them: qsum_g1_issue loads this thread's
+// chunks into registers; qsum_g1_finish (every thread calls it) stages them and sums.
 template <int D, int TMAX, int NT>
-__device__ __forceinline__ void query_sum_g1_coop(const uint16_t* __restrict__ qh, uint64_t pred, int T,
-                                                  float* qbuf, float* qs_lds) {
-#pragma clang fp contract(off)
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
+struct QsumG1 {
+  static constexpr int CPR = D / 8;   // 16-byte chunks per row
+  static constexpr int PER = (TMAX * CPR + NT - 1) / NT;
   static_assert(TMAX * CPR <= NT || (TMAX * CPR) % NT == 0, "chunking");
+  uint4 v[PER];
+};
+
+template <int D, int TMAX, int NT>
+__device__ __forceinline__ void qsum_g1_issue(const uint16_t* __restrict__ qh, int T, QsumG1<D, TMAX, NT>& st) {
+  using S = QsumG1<D, TMAX, NT>;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int c0 = 0; c0 < TMAX * CPR; c0 += NT) {
-    const int c = c0 + t;
-    if (c < TMAX * CPR) {
-      const int p = c / CPR, ch = c % CPR;
-      uint4 v = *reinterpret_cast<const uint4*>(qh + (int64_t)(p < T ? p : T - 1) * D + ch * 8);
+  for (int k = 0; k < S::PER; ++k) {
+    const int c = k * NT + t;
+    const int p = c / S::CPR, ch = c % S::CPR;
+    st.v[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (c < TMAX * S::CPR) st.v[k] = *reinterpret_cast<const uint4*>(qh + (int64_t)(p < T ? p : T - 1) * D + ch * 8);
+  }
+}
+
+template <int D, int TMAX, int NT>
+__device__ __forceinline__ void qsum_g1_finish(const QsumG1<D, TMAX, NT>& st, uint64_t pred, int T, float* qbuf,
+                                               float* qs_lds) {
+#pragma clang fp contract(off)
+  using S = QsumG1<D, TMAX, NT>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < S::PER; ++k) {
+    const int c = k * NT + t;
+    if (c < TMAX * S::CPR) {
+      const int p = c / S::CPR, ch = c % S::CPR;
       const bool keep = p < T && ((pred >> p) & 1ull);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t w[4] = {st.v[k].x, st.v[k].y, st.v[k].z, st.v[k].w};
       float* dst = qbuf + p * D + ch * 8;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -98,7 +119,7 @@ __device__ __forceinline__ void query_sum_g1_coop(const uint16_t* __restrict__ q
       }
     }
   }
-  __syncthreads();
+  block_sync_lds();
   if (t < D) {
     const int T2 = pow2_ceil(T);
     float a[TMAX];

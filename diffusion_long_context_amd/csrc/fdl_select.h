@@ -31,7 +31,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
     if (lane >= o) incl += u;
   }
   if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
+  block_sync_lds();
   int off = 0;
   total = 0;
 #pragma unroll
@@ -40,7 +40,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
     if (w < wave) off += t;
     total += t;
   }
-  __syncthreads();
+  block_sync_lds();
   return off + incl - v;
 }
 
@@ -75,13 +75,13 @@ __device__ SelResult select_core(const uint32_t* keys, const uint32_t* forced, i
   if (kk > 0 && !take_all) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int i = tid; i < 256; i += NT) sc.hist[i] = 0;
-      __syncthreads();
+      block_sync_lds();
       for (int i = tid; i < n; i += NT) {
         const uint32_t k = keys[i];
         if (((forced[i >> 5] >> (i & 31)) & 1u) == 0u && (k & pmask) == prefix)
           atomicAdd(&sc.hist[(k >> shift) & 255u], 1);
       }
-      __syncthreads();
+      block_sync_lds();
       if (tid < 64) {
         // lane l sums bins 255-4l .. 252-4l (descending digits)
         int cnt[4], s = 0;
@@ -111,11 +111,11 @@ __device__ SelResult select_core(const uint32_t* keys, const uint32_t* forced, i
           }
         }
       }
-      __syncthreads();
+      block_sync_lds();
       prefix |= *sc.digit << shift;
       pmask |= 255u << shift;
       rem -= *sc.above;
-      __syncthreads();
+      block_sync_lds();
     }
   }
   const uint32_t theta = prefix;
@@ -203,7 +203,7 @@ __device__ SelResult select_small(const uint32_t* keys, const uint32_t* forced, 
   wave_sort_desc(v, lane);
   runs[t] = v;
   if (t < NT / 32) bits[t] = 0u;
-  __syncthreads();
+  block_sync_lds();
   int n_forced = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) n_forced += nfw[w];
@@ -240,7 +240,7 @@ __device__ SelResult select_small(const uint32_t* keys, const uint32_t* forced, 
     const int i = (int)(~(uint32_t)v);
     atomicOr(&bits[i >> 5], 1u << (i & 31));
   }
-  __syncthreads();
+  block_sync_lds();
   // output position of index t = taken indices below t: popcounts of the bit words (no scan)
   int pos = 0, total = 0;
 #pragma unroll
@@ -325,6 +325,16 @@ __device__ __forceinline__ void wave_sort_desc32(uint32_t& v) {
   bitonic_merge32<K, K / 2>(v);
 }
 
+// Inclusive prefix sum along each 16-lane row (DPP row shifts by 1, 2, 4, 8; lanes without a source
+// add 0).
+__device__ __forceinline__ int row_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  return x;
+}
+
 // The same selection as select_core for n <= NT and top_k <= 64, found through a threshold.  The
 // eligible keys (forced units and threads past n count as 0, which no eligible key is below) are
 // sorted within each wave; a tournament then keeps the 64 largest: two descending runs A and B
@@ -335,17 +345,16 @@ __device__ __forceinline__ void wave_sort_desc32(uint32_t& v) {
 // wave, so the output positions need no further pass: emit(gpos, lpos, i) gets unit i's place in
 // the ascending list of every taken unit (gpos) and in the list of the forced units (ascending)
 // followed by the chosen ones (ascending) (lpos).
-// runs: LDS [NT - 64] words; cnt: LDS [3 * NT / 64 + 1] ints.
+// runs: LDS [NT - 64] words; cnt: LDS [2 * NT / 64 + 1] ints.
 template <int NT, typename Emit>
 __device__ SelResult select_top64(const uint32_t* keys, const uint32_t* forced, int n, int top_k, uint32_t* runs,
                                   int* cnt, Emit emit) {
   constexpr int NW = NT / 64;
-  static_assert(NW >= 1 && (NW & (NW - 1)) == 0, "power-of-two wave count");
+  static_assert(NW >= 1 && (NW & (NW - 1)) == 0 && NW <= 16, "power-of-two wave count, one row of lanes");
   const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   int* n_f = cnt;               // [NW] forced units per wave
-  int* n_gt = cnt + NW;         // [NW] eligible keys above theta
-  int* n_eq = cnt + 2 * NW;     // [NW] eligible keys equal to theta
-  int* theta_w = cnt + 3 * NW;  // [1]
+  int* n_gt = cnt + NW;         // [NW] eligible keys above theta | equal to theta << 16
+  int* theta_w = cnt + 2 * NW;  // [1]
   const bool valid = t < n;
   const bool f = valid && ((forced[t >> 5] >> (t & 31)) & 1u) != 0u;
   const bool elig = valid && !f;
@@ -360,7 +369,7 @@ __device__ SelResult select_top64(const uint32_t* keys, const uint32_t* forced, 
 #pragma unroll
   for (int half = NW / 2; half >= 1; half >>= 1) {
     if (wave >= half && wave < 2 * half) slots[(wave - half) * 64 + lane] = v;
-    __syncthreads();
+    block_sync_lds();
     if (wave < half) {
       const uint32_t o = slots[wave * 64 + 63 - lane];
       v = v > o ? v : o;
@@ -368,42 +377,36 @@ __device__ SelResult select_top64(const uint32_t* keys, const uint32_t* forced, 
     }
     slots += half * 64;
   }
-  if constexpr (NW == 1) __syncthreads();   // n_f
-  int n_forced = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) n_forced += n_f[w];
+  if constexpr (NW == 1) block_sync_lds();   // n_f
+  // Per-wave counts are combined lane-parallel: lane w < NW holds wave w's count and a scan along
+  // the 16-lane row gives the prefixes (rather than every wave adding all NW counts in scalar code).
+  const int fl = lane < NW ? n_f[lane] : 0;
+  const int f_incl = row_incl_scan(fl);
+  const int n_forced = __builtin_amdgcn_readlane(f_incl, NW - 1);
   const int n_elig = n - n_forced;
   const int kk = top_k < n_elig ? top_k : n_elig;
   if (wave == 0) {
     // with nothing to take the threshold is all ones, which no key reaches (+inf's key is below)
-    const uint32_t th = __shfl(v, kk > 0 ? kk - 1 : 0, 64);
+    const uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)v, kk > 0 ? kk - 1 : 0);
     if (lane == 0) *theta_w = kk > 0 ? (int)th : -1;
   }
-  __syncthreads();
-  const uint32_t theta = (uint32_t)*theta_w;
+  block_sync_lds();
+  const uint32_t theta = (uint32_t)__builtin_amdgcn_readfirstlane(*theta_w);
   const bool gt = elig && key > theta, eq = elig && key == theta;
   const uint64_t gmask = __ballot(gt), emask = __ballot(eq);
-  if (lane == 0) {
-    n_gt[wave] = __popcll(gmask);
-    n_eq[wave] = __popcll(emask);
-  }
-  __syncthreads();
-  int above = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) above += n_gt[w];
-  const int rem = kk - above;   // ties still to take, lowest index first
-  int f_base = 0, c_base = 0, eq_before = 0, my_ties = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    int tw = rem - eq_before;
-    tw = tw < 0 ? 0 : (tw > n_eq[w] ? n_eq[w] : tw);
-    if (w < wave) {
-      f_base += n_f[w];
-      c_base += n_gt[w] + tw;
-    }
-    if (w == wave) my_ties = tw;
-    eq_before += n_eq[w];
-  }
+  if (lane == 0) n_gt[wave] = __popcll(gmask) | (__popcll(emask) << 16);
+  block_sync_lds();
+  const int both = lane < NW ? n_gt[lane] : 0;
+  const int gtl = both & 0xFFFF, eql = both >> 16;
+  const int gt_incl = row_incl_scan(gtl), eq_incl = row_incl_scan(eql);
+  const int rem = kk - __builtin_amdgcn_readlane(gt_incl, NW - 1);   // ties still to take, lowest index first
+  int tw = rem - (eq_incl - eql);   // wave (lane)'s share of them
+  tw = tw < 0 ? 0 : (tw > eql ? eql : tw);
+  const int cw = gtl + tw;
+  const int c_incl = row_incl_scan(cw);
+  const int f_base = __builtin_amdgcn_readlane(f_incl - fl, wave);
+  const int c_base = __builtin_amdgcn_readlane(c_incl - cw, wave);
+  const int my_ties = __builtin_amdgcn_readlane(tw, wave);
   const uint64_t below = (1ull << lane) - 1ull;
   const bool chosen = gt || (eq && __popcll(emask & below) < my_ties);
   const uint64_t cmask = __ballot(chosen);
