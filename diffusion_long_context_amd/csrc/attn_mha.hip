@@ -92,11 +92,19 @@ struct TilePrep {
 
 template <int D, bool DENSE, bool SEL>
 __device__ __forceinline__ void mha_prepare(const MhaParams& p, int e, const int32_t* __restrict__ sel_row,
-                                            const uint16_t* sel_lds, int lane, TilePrep<D>& tp) {
+                                            const uint16_t* sel_lds, int lane, TilePrep<D>& tp, bool contig) {
   using S = MhaShape<D>;
   if constexpr (!DENSE) {
     const int rsub = lane / S::PROW;
     if (e == 0) return;   // uniform: the own block needs no index
+    if (contig) {   // uniform: the whole tile lies in one unit
+      const int si = ((e - 1) * kTileTok) >> p.unit_log2;
+      if constexpr (SEL) tp.u[0] = sel_lds[si < p.max_sel ? si : p.max_sel - 1];
+      else tp.u[0] = sel_row[si < p.max_sel ? si : p.max_sel - 1];
+#pragma unroll
+      for (int j = 1; j < S::INSTR; ++j) tp.u[j] = tp.u[0];
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < S::INSTR; ++j) {
       const int i = (e - 1) * kTileTok + j * S::ROWS_PER_INSTR + rsub;
@@ -405,18 +413,64 @@ __device__ __forceinline__ const void* row_src(const uint16_t* base, int64_t off
   return base + off;
 }
 
+// Per-lane byte offsets, within a run of 32 consecutive rows, of the 16-byte chunks the NI fetches
+// of a tile move: fetch j, lane l covers row j * ROWS_PER_INSTR + l / PROW and stores the global
+// chunk (l % PROW) ^ swz(row) at LDS chunk slot l % PROW.  They do not depend on the tile.
+template <int D>
+__device__ __forceinline__ void tile_chunk_offsets(int lane, uint32_t (&voff)[MhaShape<D>::INSTR]) {
+  using S = MhaShape<D>;
+  const int rsub = lane / S::PROW, sc = lane % S::PROW;
+#pragma unroll
+  for (int j = 0; j < S::INSTR; ++j) {
+    const int r = j * S::ROWS_PER_INSTR + rsub;
+    voff[j] = (uint32_t)((r * D + (sc ^ (swz(r) & (S::PROW - 1))) * 8) * 2);
+  }
+}
+
 // Launch the LDS fetches of a prepared tile into the wave's slot; returns the 32-bit row mask.
 // MAYBE_OWN = false: the caller knows e > 0 (a wave's later tiles), so the own-block branch goes.
+// contig (uniform; contiguous caches with units of at least 32 tokens, or dense): a full tile is one
+// run of 32 consecutive cache rows, fetched from a scalar base plus the fixed offsets voff.
 template <int D, bool DENSE, bool PAGED, bool MAYBE_OWN = true>
 __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<PAGED>& rows, int b, int h,
                                               int e, int n_list, const TilePrep<D>& tp, uint16_t* slot,
-                                              int lane, bool& bad) {
+                                              int lane, bool& bad, bool contig,
+                                              const uint32_t (&voff)[MhaShape<D>::INSTR]) {
   using S = MhaShape<D>;
   constexpr int NI = S::INSTR;
   const int rsub = lane / S::PROW;
   const int sc = lane % S::PROW;
   const int64_t head = (int64_t)b * p.H + h;
   const bool dec = MAYBE_OWN && ((e == 0) || (p.L == 0));   // uniform
+  if constexpr (!PAGED) {
+    const int t0 = (e - 1) * kTileTok;   // list position of the tile's first row
+    int tok0 = t0;
+    bool uok = true;
+    if (!dec && contig && !DENSE) {
+      const int u = __builtin_amdgcn_readfirstlane(tp.u[0]);
+      uok = (unsigned)u < (unsigned)p.n_units;
+      tok0 = (u << p.unit_log2) + (t0 & ((1 << p.unit_log2) - 1));
+    }
+    // a full tile of a valid unit that ends inside the cache (a cache whose last unit is partial
+    // takes the general path for that unit's tiles)
+    if (!dec && contig && t0 + kTileTok <= n_list && (!uok || tok0 + kTileTok <= p.L)) {   // uniform
+      bad = bad || !uok;
+      tok0 = uok ? tok0 : 0;   // an unusable unit reads the head's first rows and is masked out
+      const char* kbase = reinterpret_cast<const char*>(p.k + (head * p.L + tok0) * D);
+      const char* vbase = reinterpret_cast<const char*>(p.v + (head * p.L + tok0) * D);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const void* src = kbase + voff[j];
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const void* src = vbase + voff[j];
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, kStreamPolicy);
+      }
+      return uok ? 0xFFFFFFFFu : 0u;
+    }
+  }
   const uint16_t* kb;
   const uint16_t* vb;
   RowOff<PAGED> off[NI];
@@ -532,6 +586,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   // selection size (n_hint units), the split ranges come from it, so the first tile's index loads
   // can go out together with the read of the actual count; the actual count then trims the ranges
   // and the last split takes any tiles beyond the hint.
+  // contiguous tiles (see mha_issue) and the fixed chunk offsets of their fetches
+  const bool contig = !PAGED && (DENSE || p.unit_log2 >= 5);
+  uint32_t voff[S::INSTR];
+  tile_chunk_offsets<D>(lane, voff);
   // A wave's tiles: e, then e + e_step while below e1 -- except in the fused kernel, where tiles
   // below e_pre (fetched early, one per wave) are followed by the wave's round-robin start e_rr.
   int e, e1, n_list;
@@ -557,14 +615,14 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     const int jp = (wave - FW) * NS + s;
     e = (wave >= FW && jp < e_pre) ? jp : e_rr;
     if (e < e_pre) {   // uniform per wave
-      mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp);
-      vm_next = mha_issue<D, false, false>(p, rows, b, h, e, nf << p.unit_log2, tp, slot, lane, bad);
+      mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp, contig);
+      vm_next = mha_issue<D, false, false>(p, rows, b, h, e, nf << p.unit_log2, tp, slot, lane, bad, contig, voff);
       issued = true;
     }
     const int ns = mha_choose_phase<D>(p, seg, s, lds, sel_lds);
     n_list = p.L == 0 ? 0 : ns << p.unit_log2;
     e1 = 1 + (n_list + kTileTok - 1) / kTileTok;
-    if (!issued) mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp);
+    if (!issued) mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp, contig);
   } else {
     int n_part = DENSE ? p.L : (p.n_hint > 0 ? (p.n_hint < p.max_sel ? p.n_hint : p.max_sel) << p.unit_log2 : -1);
     if (!DENSE && n_part < 0) {
@@ -577,7 +635,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     e1 = (int)((int64_t)n_tiles_part * (s + 1) / NS);
     e = e0 + wave;
     // unconditional: the last split may grow past the hinted range once the count is known
-    mha_prepare<D, DENSE, false>(p, e, sel_row, sel_lds, lane, tp);
+    mha_prepare<D, DENSE, false>(p, e, sel_row, sel_lds, lane, tp, contig);
     n_list = n_part;
     if (!DENSE && p.n_hint > 0) {
       int ns = p.n_sel[seg];
@@ -609,7 +667,8 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   float m_run = -__builtin_inff(), l_run = 0.f;
   bool fresh = true;   // no tile accumulated yet (uniform)
 
-  if (!issued && e < e1) vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e, n_list, tp, slot, lane, bad);
+  if (!issued && e < e1)
+    vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e, n_list, tp, slot, lane, bad, contig, voff);
   const int swz_k = swz(ql) & (PROW - 1);
   for (int en; e < e1; e = en) {
     // This tile's LDS fetches must have landed before the slot is read.  Explicit, because the
@@ -619,7 +678,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     const uint32_t vm = vm_next;
     en = (SEL && e < e_pre) ? e_rr : e + e_step;
     const bool more = en < e1;
-    if (more) mha_prepare<D, DENSE, SEL>(p, en, sel_row, sel_lds, lane, tp);
+    if (more) mha_prepare<D, DENSE, SEL>(p, en, sel_row, sel_lds, lane, tp, contig);
     // ---- K from LDS into A-operand registers, then S^T = K Q^T: register r holds token
     //      8*(r/4) + 4*hh + r%4 for query ql (K registers die here) ----
     f32x16 sacc;
@@ -663,15 +722,23 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     }
     wait_lgkm0();
     // ---- fetch the next tile into the same slot; it flies while this one is finished ----
-    if (more) vm_next = mha_issue<D, DENSE, PAGED, false>(p, rows, b, h, en, n_list, tp, slot, lane, bad);
+    if (more) vm_next = mha_issue<D, DENSE, PAGED, false>(p, rows, b, h, en, n_list, tp, slot, lane, bad, contig, voff);
     float mx = -__builtin_inff();
+    if (vm == 0xFFFFFFFFu) {   // uniform: every row of the tile is valid
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
-      float x = sacc[r] * p.scale_log2;
-      x = ((vm >> row) & 1u) ? x : -__builtin_inff();
-      sacc[r] = x;
-      mx = fmaxf(mx, x);
+      for (int r = 0; r < 16; ++r) {
+        sacc[r] *= p.scale_log2;
+        mx = fmaxf(mx, sacc[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+        float x = sacc[r] * p.scale_log2;
+        x = ((vm >> row) & 1u) ? x : -__builtin_inff();
+        sacc[r] = x;
+        mx = fmaxf(mx, x);
+      }
     }
     mx = fmaxf(mx, lane_xor32f(mx));
     // Lazy rescaling: a query's running max m_run only moves when the tile's max exceeds it by more
@@ -806,12 +873,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   asm volatile("buffer_inv sc0" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
   // Every split's (max, sum) and the partials of the first kMergeBatch splits are requested in one
-  // round trip (the statistics first, so that waiting for them leaves the partials in flight); per
-  // query the common max and the split weights then go through LDS.  Same thread -> (query,
-  // chunk pair) items as above.
+  // round trip (the statistics first, so that waiting for them leaves the partials in flight); the
+  // statistics are shared through LDS.  Same thread -> (query, chunk pair) items as above.
   constexpr int kMergeBatch = 8;
-  float* s_wt = reinterpret_cast<float*>(lds);   // [NS][32] weights, then [32] sums (slots are free)
-  float2* s_ml2 = reinterpret_cast<float2*>(lds + 4096);   // [NS][32]
+  float2* s_ml2 = reinterpret_cast<float2*>(lds);   // [NS][32] (the slots are free)
   float2 ml[(kMaxSplits * 32 + NT - 1) / NT];
 #pragma unroll
   for (int k = 0; k < (kMaxSplits * 32 + NT - 1) / NT; ++k) {
@@ -837,38 +902,33 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     if (i < NS * 32) s_ml2[i] = ml[k];
   }
   block_sync_lds();   // the partial loads stay in flight
-  if (tid < 32) {
-    // every split slot is read (in flight together) and the ones past NS masked: a read guarded by
-    // the runtime split count would be waited for one at a time
-    float2 v[kMaxSplits];
+  // Every thread derives its query's split weights itself (no separate pass): the common max, then
+  // per split exp2(m - M), the sum of l times the weight and the weighted partials.  Reads past NS
+  // are clamped to the last split and masked, so that they go out together.
+  float Mh = -__builtin_inff();
+  for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
 #pragma unroll
-    for (int t = 0; t < kMaxSplits; ++t) v[t] = s_ml2[t * 32 + tid];
-    float M = -__builtin_inff();
-#pragma unroll
-    for (int t = 0; t < kMaxSplits; ++t) M = t < NS ? fmaxf(M, v[t].x) : M;
-    float Ls = 0.f;
-#pragma unroll
-    for (int t = 0; t < kMaxSplits; ++t) {
-      const float w = (t < NS && v[t].x != -__builtin_inff() && M != -__builtin_inff()) ? exp2_fast(v[t].x - M) : 0.f;
-      if (t < NS) s_wt[t * 32 + tid] = w;
-      Ls += t < NS ? v[t].y * w : 0.f;
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int t = t0 + j < NS ? t0 + j : NS - 1;
+      Mh = fmaxf(Mh, s_ml2[t * 32 + qi].x);
     }
-    s_wt[kMaxSplits * 32 + tid] = Ls;
   }
-  block_sync_lds();
+  float Ls = 0.f;
   float4 o1 = make_float4(0.f, 0.f, 0.f, 0.f), o2 = o1;
   for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
     if (t0 > 0) load_batch(t0);
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      if (t0 + j >= NS) break;
-      const float w = s_wt[(t0 + j) * 32 + qi];
+      const int t = t0 + j < NS ? t0 + j : NS - 1;
+      const float2 v = s_ml2[t * 32 + qi];
+      const float w = (t0 + j < NS && v.x != -__builtin_inff() && Mh != -__builtin_inff()) ? exp2_fast(v.x - Mh) : 0.f;
+      Ls += v.y * w;
       o1.x += a[j].x * w; o1.y += a[j].y * w; o1.z += a[j].z * w; o1.w += a[j].w * w;
       o2.x += c[j].x * w; o2.y += c[j].y * w; o2.z += c[j].z * w; o2.w += c[j].w * w;
     }
   }
   if (item && qi < p.T) {
-    const float inv = 1.f / s_wt[kMaxSplits * 32 + qi];
+    const float inv = 1.f / Ls;
     uint16_t* dst = p.out + (seg * p.T + qi) * D + 4 * dg;
     *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o1.x * inv, o1.y * inv), pack_bf16x2(o1.z * inv, o1.w * inv));
     *reinterpret_cast<uint2*>(dst + 4 * HC) =
