@@ -551,10 +551,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   constexpr int NT = kMhaWaves * 64;
   constexpr int KS = S::KS, DT = S::DT, PROW = S::PROW;
   static_assert(!SEL || (!DENSE && !PAGED), "fused selection: contiguous sparse only");
-  // tile slots; the 8-wave merge reuses them with 16 bytes of padding per query row
-  constexpr int kLdsElems = kMhaWaves * S::SLOT > kMhaWaves * 32 * (D + 4) * 2 ? kMhaWaves * S::SLOT
-                                                                               : kMhaWaves * 32 * (D + 4) * 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kMhaWaves * S::SLOT];
   __shared__ uint16_t sel_lds[SEL ? kFusedMaxSel : 1];
 
   // Workgroup i runs on XCD i % 8 (the dispatcher's round-robin order).  All splits of one head
@@ -785,69 +782,68 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   }
   latch_bad(p.status, bad);
 
-  // ---- merge the 8 waves: common max per query, rescale in registers, sum through LDS ----
+  // ---- merge the 8 waves.  Each wave stores its unnormalized O^T (relative to its own running
+  //      max) and its (max, sum) as soon as its last tile is done, into its own slot (its fetches
+  //      have all been consumed); after one barrier every thread combines its (query, chunk pair)
+  //      over the waves with the weights exp2(m_w - M).
+  //      Slot layout: query-major rows of D floats, 16-byte chunk c of row q stored at chunk
+  //      c ^ (q & 15), so that both the writes (16 rows, one chunk) and the reads (one row, 16
+  //      chunks) hit 16 different bank groups.  Lane (q, hh) holds, for each (dtp, rg), the eight
+  //      consecutive d = 64 dtp + 16 rg + 8 hh + [0, 8) of query q (registers r = 4 rg + [0, 4) of
+  //      MFMAs 2 dtp and 2 dtp + 1): chunks 16 dtp + 4 rg + 2 hh and the next. ----
   __shared__ float s_m[kMhaWaves][32], s_l[kMhaWaves][32];
-  __shared__ float s_fin[2][32];
   __shared__ uint32_t s_ticket;
-  if (hh == 0) {
-    s_m[wave][ql] = m_run;
-    s_l[wave][ql] = l_run;
-  }
-  __syncthreads();   // also: every LDS fetch has been consumed, the slots are free
-  float M = -__builtin_inff();
+  constexpr int CH = D / 4;   // 16-byte chunks per row
+  constexpr int HC = D / 8;   // chunks per half row
+  static_assert(32 * D * sizeof(float) == sizeof(uint16_t) * S::SLOT, "a wave's rows fill its slot");
+  {
+    float* mo = reinterpret_cast<float*>(slot);   // [32][D]
 #pragma unroll
-  for (int w = 0; w < kMhaWaves; ++w) M = fmaxf(M, s_m[w][ql]);
-  const bool anyrow = M != -__builtin_inff();
-  const float scale = (anyrow && m_run != -__builtin_inff()) ? exp2_fast(m_run - M) : 0.f;
-  if (wave == 0 && hh == 0) {
-    float Ls = 0.f;
+    for (int dtp = 0; dtp < DT / 2; ++dtp)
 #pragma unroll
-    for (int w = 0; w < kMhaWaves; ++w) {
-      const float mw = s_m[w][ql];
-      Ls += (anyrow && mw != -__builtin_inff()) ? s_l[w][ql] * exp2_fast(mw - M) : 0.f;
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x16& a = oacc[2 * dtp];
+        const f32x16& c = oacc[2 * dtp + 1];
+        const int c0 = 16 * dtp + 4 * rg + 2 * hh;
+        float* row = mo + ql * D;
+        *reinterpret_cast<float4*>(row + 4 * ((c0 ^ (ql & 15)) & (CH - 1))) =
+            make_float4(a[4 * rg], c[4 * rg], a[4 * rg + 1], c[4 * rg + 1]);
+        *reinterpret_cast<float4*>(row + 4 * (((c0 + 1) ^ (ql & 15)) & (CH - 1))) =
+            make_float4(a[4 * rg + 2], c[4 * rg + 2], a[4 * rg + 3], c[4 * rg + 3]);
+      }
+    if (hh == 0) {
+      s_m[wave][ql] = m_run;
+      s_l[wave][ql] = l_run;
     }
-    s_fin[0][ql] = M;
-    s_fin[1][ql] = Ls;
   }
-  // Wave partials go to LDS query-major, rows padded by 4 floats (rows 16 bytes apart modulo the
-  // banks): lane (q, hh) holds, for each (dtp, rg), the eight consecutive d = 64 dtp + 16 rg + 8 hh
-  // + [0, 8) of query q (registers r = 4 rg + [0, 4) of MFMAs 2 dtp and 2 dtp + 1), two 16-byte
-  // writes.  Then thread -> (query q, 16-byte chunks dg and dg + D / 8 of its row): each group of
-  // 16 lanes reads 256 consecutive bytes.
-  constexpr int DP = D + 4;
-  constexpr int HC = D / 8;   // 16-byte chunks per half row
-  float* mo = reinterpret_cast<float*>(lds);   // [wave][32][DP]
-#pragma unroll
-  for (int dtp = 0; dtp < DT / 2; ++dtp)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const f32x16& a = oacc[2 * dtp];
-      const f32x16& c = oacc[2 * dtp + 1];
-      float* dst = mo + (wave * 32 + ql) * DP + 64 * dtp + 16 * rg + 8 * hh;
-      *reinterpret_cast<float4*>(dst) =
-          make_float4(a[4 * rg] * scale, c[4 * rg] * scale, a[4 * rg + 1] * scale, c[4 * rg + 1] * scale);
-      *reinterpret_cast<float4*>(dst + 4) =
-          make_float4(a[4 * rg + 2] * scale, c[4 * rg + 2] * scale, a[4 * rg + 3] * scale, c[4 * rg + 3] * scale);
-    }
   __syncthreads();
   static_assert(32 * HC <= NT, "one (query, chunk pair) item per thread");
   const bool item = tid < 32 * HC;
   const int qi = item ? tid / HC : 0, dg = tid % HC;
   float* po_base = p.part_o;
   float2* pml_base = p.part_ml;
+  float Mq = -__builtin_inff(), Lq = 0.f;
   {
+    float mw[kMhaWaves];
+#pragma unroll
+    for (int w = 0; w < kMhaWaves; ++w) {
+      mw[w] = s_m[w][qi];
+      Mq = fmaxf(Mq, mw[w]);
+    }
     float4 o1 = make_float4(0.f, 0.f, 0.f, 0.f), o2 = o1;
 #pragma unroll
     for (int w = 0; w < kMhaWaves; ++w) {
-      const float* src = mo + (w * 32 + qi) * DP + 4 * dg;
-      const float4 a = *reinterpret_cast<const float4*>(src);
-      const float4 c = *reinterpret_cast<const float4*>(src + 4 * HC);
-      o1.x += a.x; o1.y += a.y; o1.z += a.z; o1.w += a.w;
-      o2.x += c.x; o2.y += c.y; o2.z += c.z; o2.w += c.w;
+      const float ww = (mw[w] != -__builtin_inff()) ? exp2_fast(mw[w] - Mq) : 0.f;
+      Lq += s_l[w][qi] * ww;
+      const float* row = reinterpret_cast<const float*>(lds + w * S::SLOT) + qi * D;
+      const float4 a = *reinterpret_cast<const float4*>(row + 4 * ((dg ^ (qi & 15)) & (CH - 1)));
+      const float4 c = *reinterpret_cast<const float4*>(row + 4 * (((dg + HC) ^ (qi & 15)) & (CH - 1)));
+      o1.x += a.x * ww; o1.y += a.y * ww; o1.z += a.z * ww; o1.w += a.w * ww;
+      o2.x += c.x * ww; o2.y += c.y * ww; o2.z += c.z * ww; o2.w += c.w * ww;
     }
     if (NS == 1) {
       if (item && qi < p.T) {
-        const float inv = 1.f / s_fin[1][qi];
+        const float inv = 1.f / Lq;
         uint16_t* dst = p.out + (seg * p.T + qi) * D + 4 * dg;
         *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o1.x * inv, o1.y * inv), pack_bf16x2(o1.z * inv, o1.w * inv));
         *reinterpret_cast<uint2*>(dst + 4 * HC) =
@@ -857,10 +853,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
       float* dst = po_base + ((seg * NS + s) * 32 + qi) * D + 4 * dg;
       *reinterpret_cast<float4*>(dst) = o1;
       *reinterpret_cast<float4*>(dst + 4 * HC) = o2;
+      if (dg == 0) pml_base[(seg * NS + s) * 32 + qi] = make_float2(Mq, Lq);
     }
   }
   if (NS == 1) return;
-  if (tid < 32) pml_base[(seg * NS + s) * 32 + tid] = make_float2(s_fin[0][tid], s_fin[1][tid]);
 
   // ---- same-XCD hand-over: the last split of this head to finish merges all of them.  The
   //      partials sit in this XCD's L2: wait until our stores are acknowledged by it, take a
