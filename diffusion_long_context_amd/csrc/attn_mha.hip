@@ -866,8 +866,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg * kSyncStride], 1u);
   __syncthreads();
   if (s_ticket != (uint32_t)(NS - 1)) return;
-  asm volatile("buffer_inv sc0" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("buffer_inv sc0" ::: "memory");   // later loads miss L1 and read the partials from L2
   // Every split's (max, sum) and the partials of the first kMergeBatch splits are requested in one
   // round trip (the statistics first, so that waiting for them leaves the partials in flight); the
   // statistics are shared through LDS.  Same thread -> (query, chunk pair) items as above.
