@@ -40,7 +40,22 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-constexpr float kCandSlack = 0.999f;   // candidates use tau * (1 - 1e-3): absorbs float32 rounding
+// One level of a transposing sum over lanes: values [0, 2H) -> [0, H).  A lane with bit J clear keeps
+// its values [0, H) plus the partner's (lane ^ J) values [0, H); a lane with bit J set keeps its
+// values [H, 2H) plus the partner's [H, 2H), stored at [0, H).
+template <int H, int J>
+__device__ __forceinline__ void reduce_half(float (&u)[16], int lane) {
+  const bool up = (lane & J) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float send = up ? u[i] : u[i + H];
+    const float keep = up ? u[i + H] : u[i];
+    u[i] = keep + __uint_as_float(lane_xor<J>(__float_as_uint(send)));
+  }
+}
+
+constexpr float kCandSlack = 0.999f;
+constexpr int kSinkLocalCand = 128;     // candidates a wave keeps in LDS before appending   // candidates use tau * (1 - 1e-3): absorbs float32 rounding
 constexpr int kSinkWaves = 4;
 constexpr int kSinkTile = 64;           // tokens per tile
 
@@ -73,6 +88,12 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   constexpr int PROW = RC::PROW, RPI = RC::ROWS_PER_INSTR, NI = kSinkTile / RPI;
   __shared__ __attribute__((aligned(1024))) uint16_t kslot[kSinkWaves * kSinkTile * D];
   __shared__ float2 s_part[8][32];
+  __shared__ float2 s_run[kSinkWaves][32];   // each wave's latest running (max, sum) per query
+  // Candidates found by each wave, kept in its quarter of an LDS list during the scan with the count
+  // in a register (a global atomic's result, and an LDS atomic, would each be waited for behind the
+  // tile fetch in flight), appended to the head's list after the scan.
+  __shared__ uint32_t s_cand[kSinkWaves][kSinkLocalCand];
+  __shared__ uint32_t s_ncand[kSinkWaves], s_cbase;
   __shared__ float s_lse[32];
   __shared__ uint32_t s_ticket;
   const int NS = p.n_splits;
@@ -87,6 +108,9 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   const int n_pred = __popcll(pred);
   const int n_parts = NS * kSinkWaves;
   float m_run = -__builtin_inff(), l_run = 0.f;
+  if (tid < kSinkWaves * 32) s_run[tid >> 5][tid & 31] = make_float2(-__builtin_inff(), 0.f);
+  __syncthreads();
+  uint32_t n_local = 0;   // this wave's candidates in s_cand[wave] (uniform)
   const uint16_t* kdec = p.k_dec + ((int64_t)b * p.Hkv + g) * p.T * D;
   const uint16_t* kctx = p.k + ((int64_t)b * p.Hkv + g) * (int64_t)p.L * D;
   if (n_pred > 0) {   // uniform
@@ -105,18 +129,37 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     const int n_tiles = 1 + (p.L + kSinkTile - 1) / kSinkTile;
     const int e0 = (int)((int64_t)n_tiles * s / NS);
     const int e1 = (int)((int64_t)n_tiles * (s + 1) / NS);
-    // tile e -> the wave's slot; rows are clamped so that every fetch is in bounds
+    // tile e -> the wave's slot; rows are clamped so that every fetch is in bounds.  A full cache
+    // tile is one run of kSinkTile rows: a scalar base plus per-lane chunk offsets fixed up front.
     uint16_t* slot = kslot + wave * kSinkTile * D;
+    uint32_t voff[NI];
+    {
+      const int rsub = lane / PROW, sc = lane % PROW;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int r = j * RPI + rsub;
+        voff[j] = (uint32_t)((r * D + (sc ^ (swz(r) & (PROW - 1))) * 8) * 2);
+      }
+    }
     auto issue = [&](int e) {
       const int rsub = lane / PROW, sc = lane % PROW;
+      if (e > 0 && e * kSinkTile <= p.L) {   // uniform: a full tile of the cache
+        const char* base = reinterpret_cast<const char*>(kctx + (int64_t)(e - 1) * kSinkTile * D);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const void* src = base + voff[j];
+          __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+        }
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int r = j * RPI + rsub;
         const int t = (e - 1) * kSinkTile + r;
         const uint16_t* row = (e == 0) ? kdec + (int64_t)(r < p.T ? r : p.T - 1) * D
                                        : kctx + (int64_t)(t < p.L ? t : p.L - 1) * D;
-        __builtin_amdgcn_global_load_lds((const void*)(row + (sc ^ (swz(r) & (PROW - 1))) * 8),
-                                         (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+        const void* src = row + (sc ^ (swz(r) & (PROW - 1))) * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
       }
     };
     const int swz_k = swz(ql) & (PROW - 1);
@@ -126,8 +169,23 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     // at once (the usual case: only sink tiles pass).  Register r of block rb holds token
     // 32 rb + 8 (r / 4) + 4 hh + r % 4 for query ql.
     const float log2_thr = __log2f(p.tau * kCandSlack);
+    // The bound's log-sum-exp covers this wave's tokens and the ones the workgroup's other waves
+    // have scored so far (their latest (max, sum), published in LDS as one 8-byte pair): a log-sum-
+    // exp over any subset of the row stays below the row's own, so the bound stays an upper bound,
+    // and with four waves' tokens it is tight enough that most tiles are not evaluated further.
     auto eval_tile = [&](const f32x16 (&sc)[RB], int et, int nv) {
-      const float lse = m_run + __log2f(l_run);
+      float mc = m_run, lc = l_run;
+#pragma unroll
+      for (int w = 0; w < kSinkWaves; ++w) {
+        if (w == wave) continue;
+        const float2 o = s_run[w][ql];
+        if (o.y > 0.f) {
+          const float mn = fmaxf(mc, o.x);
+          lc = lc * exp2f(mc - mn) + o.y * exp2f(o.x - mn);
+          mc = mn;
+        }
+      }
+      const float lse = mc + __log2f(lc);
       bool hot = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -136,28 +194,34 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
       if (__ballot(hot) == 0ull) return;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        // sum over the 32 queries (lanes of a half) by butterflies: every lane of the half then
-        // holds the sums of its 16 tokens; lane ql < 16 of each half judges token register ql
+        // sum over the 32 queries (lanes of a half) of the 16 token registers by a transposing
+        // reduction: at the level of lane distance J the lane keeps half of its values and sends the
+        // other half, so the count halves each level; lane ql of a half ends with the sum of token
+        // register tr = 8 b0 + 4 b1 + 2 b2 + b3 (b_i = bit i of ql; lanes ql and ql ^ 16 agree)
         float u[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float m = qlive ? exp2f(sc[rb][r] - lse) : 0.f;
-          m += __uint_as_float(lane_xor<1>(__float_as_uint(m)));
-          m += __uint_as_float(lane_xor<2>(__float_as_uint(m)));
-          m += __uint_as_float(lane_xor<4>(__float_as_uint(m)));
-          m += __uint_as_float(lane_xor<8>(__float_as_uint(m)));
-          m += __uint_as_float(lane_xor<16>(__float_as_uint(m)));
-          u[r] = m;
+        for (int r = 0; r < 16; ++r) u[r] = qlive ? exp2_fast(sc[rb][r] - lse) : 0.f;
+        reduce_half<8, 1>(u, ql);
+        reduce_half<4, 2>(u, ql);
+        reduce_half<2, 4>(u, ql);
+        reduce_half<1, 8>(u, ql);
+        const float mine = u[0] + __uint_as_float(lane_xor<16>(__float_as_uint(u[0])));
+        const int tr = 8 * (ql & 1) + 4 * ((ql >> 1) & 1) + 2 * ((ql >> 2) & 1) + ((ql >> 3) & 1);
+        const int row = 32 * rb + 8 * (tr >> 2) + 4 * hh + (tr & 3);
+        const bool is_cand = ql < 16 && row < nv && mine * inv_np >= p.tau * kCandSlack;
+        const uint64_t cm = __ballot(is_cand);
+        if (is_cand) {
+          const uint32_t tok = (uint32_t)((et - 1) * kSinkTile + row);
+          const uint32_t li = n_local + (uint32_t)__popcll(cm & ((1ull << lane) - 1ull));
+          if (li < (uint32_t)kSinkLocalCand) {
+            s_cand[wave][li] = tok;
+          } else {   // the wave's list is full: straight to the head's list
+            const uint32_t idx = atomicAdd(&p.cand_count[seg], 1u);
+            if ((int)idx < p.cand_cap) p.cand[(int64_t)seg * p.cand_cap + idx] = tok;
+            else latch(p.status, ST_CAND_OVERFLOW);
+          }
         }
-        float mine = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mine = (ql == r) ? u[r] : mine;
-        const int row = 32 * rb + 8 * (ql >> 2) + 4 * hh + (ql & 3);
-        if (ql < 16 && row < nv && mine * inv_np >= p.tau * kCandSlack) {
-          const uint32_t idx = atomicAdd(&p.cand_count[seg], 1u);
-          if ((int)idx < p.cand_cap) p.cand[(int64_t)seg * p.cand_cap + idx] = (uint32_t)((et - 1) * kSinkTile + row);
-          else latch(p.status, ST_CAND_OVERFLOW);
-        }
+        n_local += (uint32_t)__popcll(cm);
       }
     };
     f32x16 sprev[RB];
@@ -180,32 +244,55 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
       const int nvalid = (e == 0) ? p.T : min(kSinkTile, p.L - (e - 1) * kSinkTile);
       f32x16 sacc[RB];
       float mx = -__builtin_inff();
+      {
+        // two independent accumulation chains per 32-row block (even and odd k-steps), so that
+        // the MFMA latency of one chain is covered by the other
+        f32x16 acc2[RB][2];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
+          for (int r = 0; r < 16; ++r) acc2[rb][0][r] = acc2[rb][1][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc[rb] = mfma32(as_bf16x8(ka[rb][ks]), qf[ks], sacc[rb]);
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          float x = sacc[rb][r] * p.scale_log2;
-          if (row >= nvalid) x = -__builtin_inff();
-          sacc[rb][r] = x;
-          mx = fmaxf(mx, x);
-        }
+          for (int rb = 0; rb < RB; ++rb) acc2[rb][ks & 1] = mfma32(as_bf16x8(ka[rb][ks]), qf[ks], acc2[rb][ks & 1]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[rb][r] = acc2[rb][0][r] + acc2[rb][1][r];
+      }
+      if (nvalid == kSinkTile) {   // uniform: every row of the tile is valid
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sacc[rb][r] *= p.scale_log2;
+            mx = fmaxf(mx, sacc[rb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            float x = sacc[rb][r] * p.scale_log2;
+            if (row >= nvalid) x = -__builtin_inff();
+            sacc[rb][r] = x;
+            mx = fmaxf(mx, x);
+          }
       }
       mx = fmaxf(mx, lane_xor32f(mx));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = exp2_fast(m_run - m_new);
       float rs = 0.f;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) rs += exp2f(sacc[rb][r] - m_new);
+        for (int r = 0; r < 16; ++r) rs += exp2_fast(sacc[rb][r] - m_new);
       rs += lane_xor32f(rs);
       l_run = l_run * alpha + rs;
       m_run = m_new;
+      if (hh == 0) s_run[wave][ql] = make_float2(m_run, l_run);
       // candidates of the previous tile, bounded with the statistics that now include this one
       // (a one-tile delay, so that no bound rests on a single tile of tokens)
       if (prev_e > 0) eval_tile(sprev, prev_e, prev_nvalid);
@@ -217,6 +304,30 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     if (prev_e > 0) eval_tile(sprev, prev_e, prev_nvalid);   // the last tile, under the final stats
   }
   if (hh == 0) p.stats[((int64_t)seg * n_parts + s * kSinkWaves + wave) * 32 + ql] = make_float2(m_run, l_run);
+  // append the workgroup's candidates to the head's list (one global atomic reserves the range)
+  if (lane == 0) s_ncand[wave] = n_local < (uint32_t)kSinkLocalCand ? n_local : (uint32_t)kSinkLocalCand;
+  __syncthreads();
+  {
+    uint32_t nw[kSinkWaves], nl = 0;
+#pragma unroll
+    for (int w = 0; w < kSinkWaves; ++w) {
+      nw[w] = s_ncand[w];
+      nl += nw[w];
+    }
+    if (nl > 0u) {   // uniform
+      if (tid == 0) s_cbase = atomicAdd(&p.cand_count[seg], nl);
+      __syncthreads();
+      uint32_t base = s_cbase;
+#pragma unroll
+      for (int w = 0; w < kSinkWaves; ++w) {
+        for (uint32_t i = tid; i < nw[w]; i += kSinkWaves * 64) {
+          if (base + i < (uint32_t)p.cand_cap) p.cand[(int64_t)seg * p.cand_cap + base + i] = s_cand[w][i];
+          else if (base + i == (uint32_t)p.cand_cap) latch(p.status, ST_CAND_OVERFLOW);
+        }
+        base += nw[w];
+      }
+    }
+  }
 
   // ---- the last split of the head (same XCD, so the partials are in its L2) finishes it ----
   if (NS > 1) {
