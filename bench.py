@@ -121,6 +121,122 @@ def cpu_baseline() -> dict | None:
 # GPU run
 # ------------------------------------------------------------------------------------------------
 
+def sparse_launch_bytes(cfg, units: int) -> int:
+    """Bytes one select-and-attend launch must move: K and V of the selected 64-token blocks, Q and O,
+    the decode block's own K and V, the pooled keys (f32) and the scores and selection it writes."""
+    B, Hq, Hkv, D, T, n_blk = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len, cfg.n_blk
+    unit_bytes = cfg.kv_block * D * 2 * 2
+    fixed = (B * Hq * T * D * 2 * 2 + B * Hkv * T * D * 2 * 2 + units * 4 + B * Hkv * 4
+             + B * Hkv * n_blk * D * 4 + B * Hkv * n_blk * 4)
+    return units * unit_bytes + fixed
+
+
+def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
+    """Diagnostics on the other workloads of the benchmark description (not the headline): the 8K MHA
+    and 16K grouped-query single-layer configurations (per-layer GPU time of each layer kind through
+    fdl_focus_step, 32 layers of one kind per step) and the chunked paged batch-4 32K configuration
+    (the whole select-and-attend chain), each with the dense baseline on the same inputs and the
+    achieved rate on the bytes the sparse path must move.  Inputs are drawn on the device (seeded)."""
+    import torch
+
+    from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
+                                                  fdl_focus_params)
+    from diffusion_long_context_amd.step import ChunkedStep, ChunkParams, geom_for
+    from synth import get_config
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()   # warm
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n   # us per call
+
+    out = {}
+    for ci in (1, 2):
+        cfg = get_config(ci)
+        g = geom_for(cfg)
+        B, Hq, Hkv, D, L, T = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len, cfg.dec_len
+        gen = torch.Generator(device=dev).manual_seed(7000 + ci)
+
+        def rn(*shape):
+            return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+        q, k, v = rn(B, Hq, T, D), rn(B, Hkv, L, D), rn(B, Hkv, L, D)
+        k[:, :, :4] *= 6   # sink keys
+        kd, vd = rn(B, Hkv, T, D), rn(B, Hkv, T, D)
+        n_blk, max_sel = cfg.n_blk, cfg.max_sel_blocks
+        ks = torch.zeros((B, Hkv, n_blk, D), dtype=torch.float32, device=dev)
+        h.fdl_pool_keys(g, k, None, cfg.kv_block, ks)
+        o = torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device=dev)
+        pred_mask = torch.zeros(B, dtype=torch.int64, device=dev)
+        n_pred = torch.zeros(B, dtype=torch.int32, device=dev)
+        scores = torch.zeros((B, Hkv, n_blk), dtype=torch.float32, device=dev)
+        sink_pos = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device=dev)
+        n_sinks = torch.zeros(B, dtype=torch.int32, device=dev)
+        sel_idx = torch.zeros((B, Hkv, max_sel), dtype=torch.int32, device=dev)
+        n_sel = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        conf = torch.rand((B, T), generator=gen, device=dev)
+        masked = (torch.rand((B, T), generator=gen, device=dev) < 0.5).to(torch.uint8)
+        params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, max_sel,
+                                  cfg.sink_tau)
+        per = {}
+        for name, mode in (("dense", FDL_LAYER_DENSE), ("source", FDL_LAYER_SOURCE), ("reuse", FDL_LAYER_REUSE)):
+            table = h.make_layers(g, [dict(q=q, k_cache=k, v_cache=v, k_dec=kd, v_dec=vd, ks=ks, out=o,
+                                           mode=mode)] * 32)
+            per[name] = timed(lambda: h.fdl_focus_step(g, params, conf, masked, table, pred_mask, n_pred, scores,
+                                                       sink_pos, n_sinks, sel_idx, n_sel), steps) / 32
+        assert h.fdl_get_status() == 0
+        sel_blocks = int(n_sel.sum())
+        reuse_bytes = sparse_launch_bytes(cfg, sel_blocks)
+        out[cfg.name] = {
+            "layer_us": per, "speedup_reuse_vs_dense": per["dense"] / per["reuse"],
+            "reuse_kv_tokens_per_s": B * L / (per["reuse"] * 1e-6),
+            "reuse_bytes": reuse_bytes, "reuse_GBps": reuse_bytes / (per["reuse"] * 1e-6) / 1e9,
+            "reuse_frac_of_peak": reuse_bytes / (per["reuse"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "sel_blocks_per_kv_head": sel_blocks / (B * Hkv)}
+        del q, k, v, kd, vd, ks, o
+    # chunked, paged: the pool is [n_pages][Hkv][page][D]; each sequence's pages in shuffled order
+    cfg = get_config(4)
+    g = geom_for(cfg)
+    B, Hq, Hkv, D, L, T = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len, cfg.dec_len
+    gen = torch.Generator(device=dev).manual_seed(7004)
+    n_pages, pps = cfg.n_pages, cfg.pages_per_seq
+
+    def rn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    kp, vp = rn(n_pages, Hkv, cfg.page_tokens, D), rn(n_pages, Hkv, cfg.page_tokens, D)
+    pt = torch.randperm(n_pages, generator=gen, device=dev).to(torch.int32).view(B, pps).contiguous()
+    q, kd, vd = rn(B, Hq, T, D), rn(B, Hkv, T, D), rn(B, Hkv, T, D)
+    conf = torch.rand((B, T), generator=gen, device=dev)
+    masked = (torch.rand((B, T), generator=gen, device=dev) < 0.5).to(torch.uint8)
+    cs_ = ChunkedStep(h, g, ChunkParams(cfg.top_k_pos, cfg.window, cfg.chunk_tokens, cfg.top_k_chunks,
+                                        cfg.tokens_per_chunk_kept))
+    cs_.predict(conf, masked)
+    cs = cs_.new_chunk_sums()
+    cs_.pool(kp, pt, cs)
+    o = torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device=dev)
+    t_step = timed(lambda: cs_.run(q, kp, vp, pt, kd, vd, cs, o), chunk_runs)
+    t_dense = timed(lambda: h.fdl_dense_attn(g, q, kp, vp, kd, vd, pt, o), chunk_runs)
+    assert h.fdl_get_status() == 0
+    n_tok = int(cs_.n_tokens.sum())
+    kept = cfg.top_k_chunks * cfg.chunk_tokens
+    # chunk sums, level-2 token scoring over the chosen chunks' K, the attended tokens' K and V, the
+    # own block, Q and O
+    step_bytes = (B * Hkv * (cfg.n_chunks * D * 4 + kept * D * 2 + T * D * 4) + n_tok * D * 4
+                  + B * Hq * T * D * 4)
+    out[cfg.name] = {
+        "step_us": t_step, "dense_us": t_dense, "speedup_vs_dense": t_dense / t_step,
+        "kv_tokens_per_s": B * L / (t_step * 1e-6), "step_bytes": step_bytes,
+        "GBps": step_bytes / (t_step * 1e-6) / 1e9, "frac_of_peak": step_bytes / (t_step * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "tokens_per_kv_head": n_tok / (B * Hkv)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +245,7 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=8)
     ap.add_argument("--diag-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the other workloads' diagnostics")
     ap.add_argument("--cpu-baseline-child", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, one plain elementwise copy of this many MiB (counter calibration)")
@@ -259,9 +376,7 @@ def main():
     units = int(nsel_last.sum())                       # selected 64-token blocks over all heads
     unit_bytes = cfg.kv_block * D * 2 * 2              # K + V of one block, bf16
     # the sparse launch scores the blocks itself: pooled keys in, scores and selection out
-    fixed_bytes = (Hq * (T * D * 2 * 2) + Hkv * (T * D * 2 * 2) + units * 4 + B * Hkv * 4
-                   + B * Hkv * n_blk * D * 4 + B * Hkv * n_blk * 4)
-    launch_bytes = units * unit_bytes + fixed_bytes
+    launch_bytes = sparse_launch_bytes(cfg, units)
     achieved = launch_bytes / (sparse_us * 1e-6) / 1e9
     ms_per_step = 1e3 * t_total / args.steps
     value = cfg.ctx_len * B * NL * args.steps / t_total
@@ -296,8 +411,13 @@ def main():
         "dense_step_ms": 1e3 * t_dense_step,
         "speedup_vs_dense_hip": t_dense_step / t_plain,
         "sinks_detected": nsinks_last,
+        "workloads": None,
         "cpu_baseline": None,
     }
+    if not args.no_workloads:
+        log("other workloads (diagnostics)")
+        del K, V, arrays, dense_arrays
+        result["workloads"] = other_workloads(h, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, single thread)")
         result["cpu_baseline"] = cpu_baseline()

@@ -159,8 +159,7 @@ fdl_status run_select(fdl_handle h, const Geom& g, const float* scores, int n_un
 
 int attn_splits(fdl_handle h, const Geom& g, long long list_tokens) {
   if (g.dtype != FDL_BF16) return 1;
-  int n_splits = g.G == 1 ? fdl::mha_choose_splits(g, list_tokens, h->num_cus)
-                          : fdl::attn_choose_splits(g, list_tokens, h->num_cus);
+  int n_splits = fdl::mha_choose_splits(g, list_tokens, h->num_cus);
   while (n_splits > 1 && fdl::attn_scratch_bytes(g, n_splits) > h->scratch_bytes) n_splits /= 2;
   return n_splits;
 }

@@ -1,4 +1,4 @@
-// Gathered block-sparse (or dense) bidirectional attention for one query head per KV head.
+// Gathered block-sparse (or dense) bidirectional attention, bf16.
 //
 // Focus-dLLM (abstract; Elamur "Summary"): the block's queries attend bidirectionally over only the
 // selected KV plus the block itself; Prefilling-dLLM (abstract): the same over chunk KV cached in
@@ -25,6 +25,10 @@
 // workgroups (splits) per head, all of them are placed on the same XCD, so their partial
 // (max, sum, O) meet in that XCD's L2: each split stores its partial, waits for the stores to be
 // acknowledged, takes a ticket, and the last one merges -- no device-wide cache writeback.
+// Grouped-query heads (G query heads per KV head): one workgroup per (query head, split), the G
+// workgroups of a (KV head, split) placed next to each other on one XCD so that the tiles they all
+// read come from HBM once and from that XCD's L2 for the others; the splits of a KV head go to
+// different XCDs (there are fewer KV heads than XCDs) and attn_combine_kernel merges them.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -52,6 +56,8 @@ struct MhaParams {
   uint32_t* status;
   const int32_t* page_table;
   int H, T, L, max_sel, unit_log2, n_units, n_splits, n_segs;
+  int Hkv, G;     // KV heads and query heads per KV head (H = Hkv * G)
+  int n_groups;   // G > 1: (sequence, KV head, split) triples
   int n_hint;   // expected selected units per head (0 = unknown)
   int page_log2, pages_per_seq, n_pages;
   float scale_log2;
@@ -440,7 +446,7 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
   constexpr int NI = S::INSTR;
   const int rsub = lane / S::PROW;
   const int sc = lane % S::PROW;
-  const int64_t head = (int64_t)b * p.H + h;
+  const int64_t head = (int64_t)b * p.Hkv + h;   // h: the KV head within sequence b
   const bool dec = MAYBE_OWN && ((e == 0) || (p.L == 0));   // uniform
   if constexpr (!PAGED) {
     const int t0 = (e - 1) * kTileTok;   // list position of the tile's first row
@@ -554,21 +560,34 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kMhaWaves * S::SLOT];
   __shared__ uint16_t sel_lds[SEL ? kFusedMaxSel : 1];
 
-  // Workgroup i runs on XCD i % 8 (the dispatcher's round-robin order).  All splits of one head
-  // are given workgroup ids with the same residue, so they share one L2 and the final merge can
-  // hand partials over through it.
+  // Workgroup i runs on XCD i % 8 (the dispatcher's round-robin order).  One query head per KV
+  // head: all splits of a head are given workgroup ids with the same residue, so they share one L2
+  // and the final merge can hand partials over through it.  G query heads per KV head: the G
+  // workgroups of one (KV head, split) get consecutive ids of one residue, so they stream the same
+  // tiles through one L2 at about the same time (one HBM read serves all G); the splits of a KV
+  // head spread over the XCDs and their partials are merged by a second kernel.
   const int NS = p.n_splits;
   const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
-  const int s = xslot % NS;
-  const int seg_i = xcd + 8 * (xslot / NS);
-  if (seg_i >= p.n_segs) return;
-  const int b = seg_i / p.H, h = seg_i % p.H;
+  int s, seg_i, kv_i;   // split, query head (b * H + h), KV head (b * Hkv + g)
+  if (p.G == 1) {
+    s = xslot % NS;
+    seg_i = xcd + 8 * (xslot / NS);
+    if (seg_i >= p.n_segs) return;
+    kv_i = seg_i;
+  } else {
+    const int gi = xcd + 8 * (xslot / p.G);
+    if (gi >= p.n_groups) return;
+    kv_i = gi / NS;
+    s = gi % NS;
+    seg_i = (kv_i / p.Hkv) * p.H + (kv_i % p.Hkv) * p.G + xslot % p.G;
+  }
+  const int b = kv_i / p.Hkv, h = kv_i % p.Hkv;   // h: KV head within the sequence
   // the wave index is uniform: in a scalar register, the per-tile bookkeeping stays scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hh = lane >> 5;
-  const int64_t seg = seg_i;
+  const int64_t seg = seg_i, kvseg = kv_i;
   KvRows<PAGED> rows;
-  rows.Hkv = p.H;
+  rows.Hkv = p.Hkv;
   rows.L = p.L;
   rows.D = D;
   rows.page_log2 = p.page_log2;
@@ -577,7 +596,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   rows.page_table = p.page_table;
   bool bad = false;
 
-  const int32_t* sel_row = DENSE ? nullptr : p.sel_idx + seg * p.max_sel;
+  const int32_t* sel_row = DENSE ? nullptr : p.sel_idx + kvseg * p.max_sel;
   uint16_t* slot = lds + wave * S::SLOT;
   // Tile partition.  Dense: the list is the whole cache.  Sparse: when the caller knows the usual
   // selection size (n_hint units), the split ranges come from it, so the first tile's index loads
@@ -623,7 +642,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   } else {
     int n_part = DENSE ? p.L : (p.n_hint > 0 ? (p.n_hint < p.max_sel ? p.n_hint : p.max_sel) << p.unit_log2 : -1);
     if (!DENSE && n_part < 0) {
-      const int ns_raw = p.n_sel[seg];   // no hint: the count comes first
+      const int ns_raw = p.n_sel[kvseg];   // no hint: the count comes first
       n_part = (ns_raw < 0 ? 0 : (ns_raw > p.max_sel ? p.max_sel : ns_raw)) << p.unit_log2;
     }
     if (p.L == 0) n_part = 0;
@@ -635,7 +654,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     mha_prepare<D, DENSE, false>(p, e, sel_row, sel_lds, lane, tp, contig);
     n_list = n_part;
     if (!DENSE && p.n_hint > 0) {
-      int ns = p.n_sel[seg];
+      int ns = p.n_sel[kvseg];
       ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
       n_list = p.L == 0 ? 0 : ns << p.unit_log2;
       const int n_tiles = 1 + (n_list + kTileTok - 1) / kTileTok;
@@ -856,7 +875,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
       if (dg == 0) pml_base[(seg * NS + s) * 32 + qi] = make_float2(Mq, Lq);
     }
   }
-  if (NS == 1) return;
+  if (NS == 1 || p.G > 1) return;   // G > 1: attn_combine_kernel merges the splits
 
   // ---- same-XCD hand-over: the last split of this head to finish merges all of them.  The
   //      partials sit in this XCD's L2: wait until our stores are acknowledged by it, take a
@@ -932,39 +951,73 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   if (tid == 0) p.tickets[seg * kSyncStride] = 0u;
 }
 
-// Merge the per-split partials (max, sum, O) of every head into the bf16 output.  Separate kernel:
-// the kernel boundary makes the partials visible without a device-wide cache flush, which an
-// in-kernel "last workgroup merges" handoff would need on a multi-die GPU.
-// grid (B*H, 4): each workgroup merges 8 queries of one head.
+// Merge the per-split partials (max, sum, O) of every head into the bf16 output (grouped-query
+// heads, whose splits run on different XCDs).  Separate kernel: the kernel boundary makes the
+// partials visible without a device-wide cache flush.
+// grid (B*H, ceil(T / QW)), 4 waves: lane (query qb + lane / CH, 16-byte chunk lane % CH); wave w
+// takes the splits w, w + 4, ...; the four waves' (max, sum, O) meet in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float2* __restrict__ part_ml,
                                                            uint16_t* __restrict__ out, int NS, int T) {
+  constexpr int CH = D / 4;      // 16-byte chunks per row
+  constexpr int QW = 64 / CH;    // queries per workgroup
+  constexpr int NB = 4;          // splits in flight per lane
+  __shared__ float s_m[4][64], s_l[4][64];
+  __shared__ float4 s_o[4][64];
   const int64_t seg = blockIdx.x;
-  const int qb = blockIdx.y * 8;
-  for (int it = threadIdx.x; it < 8 * D; it += 256) {
-    const int q = qb + it / D;
-    const int d = it % D;
-    if (q >= T) continue;
-    const float2* ml = part_ml + seg * NS * 32 + q;
-    float M = -__builtin_inff();
-    for (int t = 0; t < NS; ++t) M = fmaxf(M, ml[t * 32].x);
-    float Ls = 0.f, O = 0.f;
-    for (int t = 0; t < NS; ++t) {
-      const float2 v = ml[t * 32];
-      const float o = part_o[((seg * NS + t) * 32 + q) * D + d];
-      if (v.y == 0.f) continue;
-      const float wgt = exp2f(v.x - M);
-      Ls += v.y * wgt;
-      O += o * wgt;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int q = blockIdx.y * QW + lane / CH, c = lane % CH;
+  const int qc = q < 32 ? q : 31;   // partial rows exist for all 32 queries
+  const float2* ml = part_ml + seg * NS * 32 + qc;
+  const float* po = part_o + (seg * NS * 32 + qc) * D + 4 * c;
+  float M = -__builtin_inff();
+  for (int t = w; t < NS; t += 4) M = fmaxf(M, ml[t * 32].x);
+  float Ls = 0.f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int t0 = w; t0 < NS; t0 += 4 * NB) {
+    float4 a[NB];
+    float2 v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int t = t0 + 4 * j < NS ? t0 + 4 * j : w;   // clamped reads go out together
+      a[j] = *reinterpret_cast<const float4*>(po + (int64_t)t * 32 * D);
+      v[j] = ml[t * 32];
     }
-    out[(seg * T + q) * D + d] = (uint16_t)f32_to_bf16_bits(O / Ls);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float wt = (t0 + 4 * j < NS && v[j].x != -__builtin_inff()) ? exp2f(v[j].x - M) : 0.f;
+      Ls += v[j].y * wt;
+      O.x += a[j].x * wt; O.y += a[j].y * wt; O.z += a[j].z * wt; O.w += a[j].w * wt;
+    }
   }
+  s_m[w][lane] = M;
+  s_l[w][lane] = Ls;
+  s_o[w][lane] = O;
+  __syncthreads();
+  if (w != 0 || q >= T) return;
+  float Mx = s_m[0][lane];
+#pragma unroll
+  for (int k = 1; k < 4; ++k) Mx = fmaxf(Mx, s_m[k][lane]);
+  float L = 0.f;
+  float4 R = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float mk = s_m[k][lane];
+    const float wt = mk != -__builtin_inff() ? exp2f(mk - Mx) : 0.f;
+    const float4 o = s_o[k][lane];
+    L += s_l[k][lane] * wt;
+    R.x += o.x * wt; R.y += o.y * wt; R.z += o.z * wt; R.w += o.w * wt;
+  }
+  const float inv = 1.f / L;
+  *reinterpret_cast<uint2*>(out + (seg * T + q) * D + 4 * c) =
+      make_uint2(pack_bf16x2(R.x * inv, R.y * inv), pack_bf16x2(R.z * inv, R.w * inv));
 }
 
 hipError_t launch_attn_combine(hipStream_t st, const float* part_o, const float2* part_ml, void* out,
                                int n_segs, int NS, int T, int D) {
-  dim3 grid(n_segs, (T + 7) / 8);
+  const int qw = 64 / (D / 4);
+  dim3 grid(n_segs, (T + qw - 1) / qw);
   uint16_t* o = static_cast<uint16_t*>(out);
   if (D == 128) {
     hipLaunchKernelGGL((attn_combine_kernel<128>), grid, dim3(256), 0, st, part_o, part_ml, o, NS, T);
@@ -977,12 +1030,13 @@ hipError_t launch_attn_combine(hipStream_t st, const float* part_o, const float2
 int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus) {
   const long long tiles = 1 + (max_list_tokens + kTileTok - 1) / kTileTok;
   const long long segs = (long long)g.B * g.Hkv;
-  long long s = (num_cus + segs - 1) / segs;   // one 8-wave workgroup per CU
+  // about one 8-wave workgroup per CU: G workgroups per (KV head, split)
+  long long s = g.G == 1 ? (num_cus + segs - 1) / segs : num_cus / (segs * g.G);
   const long long per_wave_min = 1;
   if (s * kMhaWaves * per_wave_min > tiles) s = (tiles + kMhaWaves - 1) / kMhaWaves;
   if (s < 1) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
-  if (segs > kMaxSplitSegs) s = 1;
+  if (g.G == 1 && segs > kMaxSplitSegs) s = 1;   // the in-kernel merge's tickets
   return (int)s;
 }
 
@@ -1042,13 +1096,20 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
   p.n_pages = g.n_pages;
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)g.D);
   p.n_segs = g.B * g.Hq;
+  p.Hkv = g.Hkv;
+  p.G = g.G;
+  p.n_groups = g.B * g.Hkv * n_splits;
   p.n_hint = dense ? 0 : n_hint;
   p.fs = fsel ? *fsel : FusedSelect{};
-  // 8 XCDs; the splits of head seg run on XCD seg % 8 (see the kernel)
-  dim3 grid(8 * ((p.n_segs + 7) / 8) * n_splits);
+  // 8 XCDs: the splits of head seg run on XCD seg % 8; grouped-query heads: the G heads of KV
+  // group i (a KV head and a split) run on XCD i % 8 (see the kernel)
+  const dim3 grid(g.G == 1 ? 8 * ((p.n_segs + 7) / 8) * n_splits : 8 * ((p.n_groups + 7) / 8) * g.G);
   const bool sel = fsel != nullptr && !dense && !g.paged;
-  return g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0, sel, timer)
-                    : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0, sel, timer);
+  if (sel && g.G != 1) return hipErrorInvalidValue;   // fused selection: one q-head per KV head
+  const hipError_t err = g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0, sel, timer)
+                                    : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0, sel, timer);
+  if (err != hipSuccess || g.G == 1 || n_splits == 1) return err;
+  return launch_attn_combine(st, p.part_o, p.part_ml, out, g.B * g.Hq, n_splits, g.T, g.D);
 }
 
 }  // namespace fdl

@@ -115,14 +115,13 @@ hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int 
 
 // Attention.  dense != 0 ignores sel_idx / n_sel.
 size_t attn_scratch_bytes(const Geom& g, int n_splits);
-int attn_choose_splits(const Geom& g, long long max_list_tokens, int num_cus);
 hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,
                        const void* k_dec, const void* v_dec, const int32_t* page_table,
                        const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                        int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
                        uint32_t* status, int n_hint, const KernelTimer* timer);
 
-// One query head per KV head (bf16): the LDS-DMA streaming kernel.
+// bf16, any number of query heads per KV head: the LDS-DMA streaming kernel.
 int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus);
 hipError_t launch_attn_mha(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,
                            const void* k_dec, const void* v_dec, const int32_t* page_table,

@@ -4,8 +4,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_close, require_gpu
+from gpu_util import assert_close, dev, out_buffer, out_to_f64, require_gpu
 from layer_util import _check_chunked, _check_layer, _chunked, _focus
+from oracle.attention import attend
 from oracle.pipeline import chunked_layer_step, focus_layer_step
 from synth import get_config
 from synth.gen import make_single, to_pages
@@ -70,6 +71,30 @@ def test_chunked_page_order_bitwise_invariant(h):
     b = _chunked(h, cfg, y)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
+
+
+def test_chunked_grouped_query(h):
+    cfg = get_config(4).with_(batch=2, n_q_heads=8, n_kv_heads=2, ctx_len=4096, chunk_tokens=512)
+    x = make_single(cfg)
+    _check_chunked(cfg, _chunked(h, cfg, x), chunked_layer_step(cfg, x))
+
+
+@pytest.mark.parametrize("kw", [dict(n_q_heads=4, n_kv_heads=4), dict(n_q_heads=8, n_kv_heads=2)],
+                         ids=["mha", "gqa4"])
+def test_dense_attention_paged(h, kw):
+    """The dense baseline over a paged cache with shuffled pages equals attention over the
+    contiguous cache."""
+    from diffusion_long_context_amd.step import geom_for
+    cfg = get_config(4).with_(batch=2, ctx_len=4096, chunk_tokens=512, **kw)
+    x = make_single(cfg)
+    assert not np.array_equal(x["page_table"].ravel(), np.arange(cfg.n_pages))
+    out = out_buffer(cfg)
+    h.fdl_dense_attn(geom_for(cfg), dev(x["q"]), dev(x["k_pool"]), dev(x["v_pool"]), dev(x["k_dec"]),
+                     dev(x["v_dec"]), dev(x["page_table"]), out)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    assert_close(out_to_f64(cfg, out), attend(x["q"], x["k"], x["v"], x["k_dec"], x["v_dec"], None),
+                 "dense paged")
 
 
 @pytest.mark.parametrize("kw", [
