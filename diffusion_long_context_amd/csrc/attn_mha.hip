@@ -437,7 +437,7 @@ __device__ __forceinline__ void tile_chunk_offsets(int lane, uint32_t (&voff)[Mh
 // MAYBE_OWN = false: the caller knows e > 0 (a wave's later tiles), so the own-block branch goes.
 // contig (uniform; contiguous caches with units of at least 32 tokens, or dense): a full tile is one
 // run of 32 consecutive cache rows, fetched from a scalar base plus the fixed offsets voff.
-template <int D, bool DENSE, bool PAGED, bool MAYBE_OWN = true>
+template <int D, bool DENSE, bool PAGED, bool MAYBE_OWN = true, int POL = kStreamPolicy>
 __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<PAGED>& rows, int b, int h,
                                               int e, int n_list, const TilePrep<D>& tp, uint16_t* slot,
                                               int lane, bool& bad, bool contig,
@@ -467,12 +467,12 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const void* src = kbase + voff[j];
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
       }
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const void* src = vbase + voff[j];
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, kStreamPolicy);
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, POL);
       }
       return uok ? 0xFFFFFFFFu : 0u;
     }
@@ -541,22 +541,25 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const void* src = row_src(kb, off[j]);
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
   }
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const void* src = row_src(vb, off[j]);
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, kStreamPolicy);
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + S::HALF + j * 512), 16, 0, POL);
   }
   return okm;
 }
 
-template <int D, bool DENSE, bool PAGED, bool SEL>
+template <int D, bool DENSE, bool PAGED, bool SEL, bool GQA = false>
 __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaParams p) {
   using S = MhaShape<D>;
   constexpr int NT = kMhaWaves * 64;
   constexpr int KS = S::KS, DT = S::DT, PROW = S::PROW;
-  static_assert(!SEL || (!DENSE && !PAGED), "fused selection: contiguous sparse only");
+  static_assert(!SEL || (!DENSE && !PAGED && !GQA), "fused selection: contiguous sparse, one q-head per KV head");
+  // grouped-query heads read every tile G times, through L2: their fetches keep the default
+  // (cached) policy; one reader per tile streams with the non-temporal one
+  constexpr int POL = GQA ? 0 : kStreamPolicy;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kMhaWaves * S::SLOT];
   __shared__ uint16_t sel_lds[SEL ? kFusedMaxSel : 1];
 
@@ -569,7 +572,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   const int NS = p.n_splits;
   const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
   int s, seg_i, kv_i;   // split, query head (b * H + h), KV head (b * Hkv + g)
-  if (p.G == 1) {
+  if constexpr (!GQA) {
     s = xslot % NS;
     seg_i = xcd + 8 * (xslot / NS);
     if (seg_i >= p.n_segs) return;
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   bool fresh = true;   // no tile accumulated yet (uniform)
 
   if (!issued && e < e1)
-    vm_next = mha_issue<D, DENSE, PAGED>(p, rows, b, h, e, n_list, tp, slot, lane, bad, contig, voff);
+    vm_next = mha_issue<D, DENSE, PAGED, true, POL>(p, rows, b, h, e, n_list, tp, slot, lane, bad, contig, voff);
   const int swz_k = swz(ql) & (PROW - 1);
   for (int en; e < e1; e = en) {
     // This tile's LDS fetches must have landed before the slot is read.  Explicit, because the
@@ -738,7 +741,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     }
     wait_lgkm0();
     // ---- fetch the next tile into the same slot; it flies while this one is finished ----
-    if (more) vm_next = mha_issue<D, DENSE, PAGED, false>(p, rows, b, h, en, n_list, tp, slot, lane, bad, contig, voff);
+    if (more) vm_next = mha_issue<D, DENSE, PAGED, false, POL>(p, rows, b, h, en, n_list, tp, slot, lane, bad, contig, voff);
     float mx = -__builtin_inff();
     if (vm == 0xFFFFFFFFu) {   // uniform: every row of the tile is valid
 #pragma unroll
@@ -875,7 +878,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
       if (dg == 0) pml_base[(seg * NS + s) * 32 + qi] = make_float2(Mq, Lq);
     }
   }
-  if (NS == 1 || p.G > 1) return;   // G > 1: attn_combine_kernel merges the splits
+  if (NS == 1 || GQA) return;   // grouped-query heads: attn_combine_kernel merges the splits
 
   // ---- same-XCD hand-over: the last split of this head to finish merges all of them.  The
   //      partials sit in this XCD's L2: wait until our stores are acknowledged by it, take a
@@ -1030,8 +1033,17 @@ hipError_t launch_attn_combine(hipStream_t st, const float* part_o, const float2
 int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus) {
   const long long tiles = 1 + (max_list_tokens + kTileTok - 1) / kTileTok;
   const long long segs = (long long)g.B * g.Hkv;
-  // about one 8-wave workgroup per CU: G workgroups per (KV head, split)
-  long long s = g.G == 1 ? (num_cus + segs - 1) / segs : num_cus / (segs * g.G);
+  // At most one 8-wave workgroup per CU of every XCD (a second round on some CUs would double the
+  // time): one q-head per KV head puts all splits of a head on one XCD, ceil(segs / 8) heads each;
+  // grouped-query heads put G workgroups per (KV head, split) group on one XCD.
+  const long long per_xcd = num_cus / 8 > 0 ? num_cus / 8 : 1;
+  long long s;
+  if (g.G == 1) {
+    s = per_xcd / ((segs + 7) / 8);
+  } else {
+    const long long groups_per_xcd = per_xcd / g.G > 0 ? per_xcd / g.G : 1;
+    s = 8 * groups_per_xcd / segs;
+  }
   const long long per_wave_min = 1;
   if (s * kMhaWaves * per_wave_min > tiles) s = (tiles + kMhaWaves - 1) / kMhaWaves;
   if (s < 1) s = 1;
@@ -1054,6 +1066,11 @@ static hipError_t launch_mha_d(hipStream_t st, const MhaParams& p, dim3 grid, bo
                                const KernelTimer* timer) {
   if (sel) {
     launch_one(attn_mha_kernel<D, false, false, true>, grid, st, p, timer);
+  } else if (p.G > 1) {
+    if (dense && paged) launch_one(attn_mha_kernel<D, true, true, false, true>, grid, st, p, timer);
+    else if (dense) launch_one(attn_mha_kernel<D, true, false, false, true>, grid, st, p, timer);
+    else if (paged) launch_one(attn_mha_kernel<D, false, true, false, true>, grid, st, p, timer);
+    else launch_one(attn_mha_kernel<D, false, false, false, true>, grid, st, p, timer);
   } else if (dense) {
     if (paged) launch_one(attn_mha_kernel<D, true, true, false>, grid, st, p, timer);
     else launch_one(attn_mha_kernel<D, true, false, false>, grid, st, p, timer);
