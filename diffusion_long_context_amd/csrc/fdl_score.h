@@ -71,6 +71,65 @@ __device__ __forceinline__ void query_sum_to_lds(const QT* __restrict__ q, uint6
   qs_lds[d] = hv[0];
 }
 
+// query_sum_to_lds for bf16 queries with every thread of an NT-thread block loading: the TMAX rows
+// of each of the G (<= GMAX) heads go to stage [GMAX][TMAX][D] (bf16 bits, LDS) as 16-byte chunks in
+// one round trip, then threads d < D build the same trees from LDS.  Same bits.
+template <int D, int TMAX, int NT, int GMAX>
+__device__ __forceinline__ void query_sum_grouped(const uint16_t* __restrict__ q, uint64_t pred, int b, int g,
+                                                  int Hq, int G, int T, uint16_t* stage, float* qs_lds) {
+#pragma clang fp contract(off)
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int CH = GMAX * TMAX * CPR;       // chunks of the stage
+  constexpr int PER = (CH + NT - 1) / NT;
+  static_assert(GMAX == 8, "the head tree below has three levels");
+  const int t = threadIdx.x;
+  uint4 v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int c = k * NT + t;
+    const int j = c / (TMAX * CPR), p = (c / CPR) % TMAX, ch = c % CPR;
+    const int jj = j < G ? j : G - 1;   // heads past G read a valid row and are never used
+    const uint16_t* src = q + (((int64_t)b * Hq + g * G + jj) * T + (p < T ? p : T - 1)) * D + ch * 8;
+    v[k] = *reinterpret_cast<const uint4*>(src);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int c = k * NT + t;
+    if (c < CH) *reinterpret_cast<uint4*>(stage + c * 8) = v[k];
+  }
+  block_sync_lds();
+  if (t < D) {
+    const int T2 = pow2_ceil(T);
+    const int G2 = pow2_ceil(G);
+    float hv[GMAX];
+#pragma unroll
+    for (int j = 0; j < GMAX; ++j) {
+      float a[TMAX];
+#pragma unroll
+      for (int p = 0; p < TMAX; ++p) {
+        const bool keep = j < G && p < T && ((pred >> p) & 1ull);
+        a[p] = keep ? bf16_bits_to_f32(stage[(j * TMAX + p) * D + t]) : 0.f;
+      }
+#pragma unroll
+      for (int lvl = 0; lvl < 6; ++lvl) {
+        if ((TMAX >> (lvl + 1)) >= 1 && (1 << lvl) < T2) {
+#pragma unroll
+          for (int i = 0; i < (TMAX >> (lvl + 1)); ++i) a[i] = a[2 * i] + a[2 * i + 1];
+        }
+      }
+      hv[j] = a[0];
+    }
+#pragma unroll
+    for (int lvl = 0; lvl < 3; ++lvl) {
+      if ((1 << lvl) < G2) {
+#pragma unroll
+        for (int i = 0; i < (4 >> lvl); ++i) hv[i] = hv[2 * i] + hv[2 * i + 1];
+      }
+    }
+    qs_lds[t] = hv[0];
+  }
+}
+
 // query_sum_to_lds for one query head (G = 1) with every thread of an NT-thread block loading: row
 // p of the head's queries is read as D / 8 sixteen-byte chunks, masked (p predicted and p < T) into
 // qbuf [TMAX][D] float32 in LDS, and threads d < D then build the same adjacent-pair tree over the

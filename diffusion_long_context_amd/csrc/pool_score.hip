@@ -16,6 +16,8 @@
 // exactly because float addition is commutative).
 #pragma clang fp contract(off)
 
+#include <type_traits>
+
 #include "fdl_device.h"
 #include "fdl_internal.h"
 #include "fdl_score.h"
@@ -208,7 +210,12 @@ __global__ __launch_bounds__(256) void score_units_kernel(const QT* __restrict__
     n = n < n_units ? n : n_units - 1;
     load16<float>(ksg + (int64_t)n * D + 16 * j, x[ps]);
   }
-  query_sum_to_lds<QT, D, TMAX>(q, pred_mask[b], b, g, Hq, G, T, qs);
+  if constexpr (std::is_same<QT, uint16_t>::value && TMAX == 32) {
+    __shared__ __attribute__((aligned(16))) uint16_t stage[8 * 32 * D];
+    query_sum_grouped<D, 32, 256, 8>(q, pred_mask[b], b, g, Hq, G, T, stage, qs);
+  } else {
+    query_sum_to_lds<QT, D, TMAX>(q, pred_mask[b], b, g, Hq, G, T, qs);
+  }
   __syncthreads();
   float qv[16];
 #pragma unroll

@@ -6,7 +6,8 @@
 // Prefilling-dLLM (abstract): top-K chunks, then token-level sparsity inside each chunk, whose
 // leading beginning-of-sequence token serves as an anchor.
 //
-// One 256-thread workgroup per segment; the selection itself is select_core (fdl_select.h).
+// One 256-thread workgroup per segment; the selection itself is select_top64 (up to 256 units, top-K
+// <= 64) or select_core (fdl_select.h).
 #include "fdl_device.h"
 #include "fdl_internal.h"
 #include "fdl_select.h"
@@ -69,8 +70,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       base = u << unit_log2;
     }
   }
-  const SelResult r = select_core<kSelThreads>(keys, forced, n, top_k, scr,
-                                               [&](int pos, int i) { out[pos] = (base < 0) ? -1 : base + i; });
+  SelResult r;
+  if (!level2 && n <= kSelThreads && top_k <= 64) {   // uniform: the sort-and-threshold form
+    // runs live in keys past the n keys it reads; the counts in hist
+    r = select_top64<kSelThreads>(keys, forced, n, top_k, keys + kSelThreads, hist,
+                                  [&](int gpos, int, int i) {
+                                    if (gpos < max_sel) out[gpos] = i;
+                                  });
+  } else {
+    r = select_core<kSelThreads>(keys, forced, n, top_k, scr,
+                                 [&](int pos, int i) { out[pos] = (base < 0) ? -1 : base + i; });
+  }
   if (tid == 0 && c == 0) {
     n_sel[seg] = level2 ? n_cand * ((force_first ? 1 : 0) + r.kk) : r.total;
   }
