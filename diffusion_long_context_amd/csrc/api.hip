@@ -181,11 +181,18 @@ fdl_status run_attn(fdl_handle h, const Geom& g, const void* q, const void* k_ca
                     "attention launch");
 }
 
-// Score, select and attend in one kernel (one q-head per KV head, bf16, contiguous cache): same
-// outputs as run_score_units + run_select + run_attn.
+// Score, select and attend in one kernel (bf16, contiguous cache): same outputs as
+// run_score_units + run_select + run_attn.
 bool fused_select_ok(const Geom& g, int n_blk, int max_sel, int max_sinks) {
-  return g.dtype == FDL_BF16 && g.G == 1 && !g.paged && g.L > 0 && n_blk <= fdl::kFusedMaxUnits &&
-         max_sel <= fdl::kFusedMaxSel && max_sinks <= fdl::kFusedMaxSinks;
+  return g.dtype == FDL_BF16 && g.T <= 32 && !g.paged && g.L > 0 && n_blk <= fdl::kFusedMaxUnits &&
+         max_sel <= fdl::kFusedMaxSel && max_sinks <= fdl::kFusedMaxSinks &&
+         (g.G == 1 || (long long)g.B * g.Hkv <= fdl::kMaxSplitSegs);
+}
+
+// Grouped-query heads in the fused kernel: the (KV head, split) groups need a barrier word each
+// and, past split 0, score-exchange rows after the attention partials in the scratch.
+static size_t fused_xchg_offset(const Geom& g, int n_splits) {
+  return (fdl::attn_scratch_bytes(g, n_splits) + 255) & ~(size_t)255;
 }
 
 fdl_status run_select_attn(fdl_handle h, const Geom& g, const fdl_layer_io& io, const uint64_t* pred_mask,
@@ -193,9 +200,20 @@ fdl_status run_select_attn(fdl_handle h, const Geom& g, const fdl_layer_io& io, 
                            const int32_t* n_sinks, float* scores, int32_t* sel_idx, int32_t* n_sel) {
   long long list_tokens = (long long)fp->max_sel << bt_log2;
   if (list_tokens > g.L) list_tokens = g.L;
-  const int n_splits = attn_splits(h, g, list_tokens);
-  const fdl::FusedSelect fs{pred_mask, io.ks,     sink_pos,    n_sinks,       fp->max_sinks, fp->top_k_blocks,
-                            scores,    sel_idx, n_sel, h->barriers, h->spin_limit};
+  int n_splits = attn_splits(h, g, list_tokens);
+  const int n_blk = (g.L + g.bt - 1) / g.bt;
+  float* xchg = nullptr;
+  if (g.G > 1) {
+    while (n_splits > 1 && ((long long)g.B * g.Hkv * n_splits > fdl::kMaxSplitSegs ||
+                            fused_xchg_offset(g, n_splits) + (size_t)g.B * g.Hkv * n_splits * n_blk * sizeof(float) >
+                                h->scratch_bytes))
+      --n_splits;
+    if (fused_xchg_offset(g, n_splits) + (size_t)g.B * g.Hkv * n_splits * n_blk * sizeof(float) > h->scratch_bytes)
+      return fail(h, FDL_ENOMEM, "workspace too small for the score exchange");
+    xchg = reinterpret_cast<float*>(h->scratch + fused_xchg_offset(g, n_splits));
+  }
+  const fdl::FusedSelect fs{pred_mask, io.ks,   sink_pos,    n_sinks,        fp->max_sinks, fp->top_k_blocks,
+                            scores,    sel_idx, n_sel,       h->barriers,    h->spin_limit, xchg};
   ProfScope ps(h, FDL_PROF_SPARSE_ATTN, /*inner=*/true);
   return hip_status(h, fdl::launch_attn_mha(h->stream, g, io.q, io.k_cache, io.v_cache, io.k_dec, io.v_dec,
                                             nullptr, sel_idx, n_sel, fp->max_sel, bt_log2, 0, io.out,

@@ -228,10 +228,11 @@ __device__ __forceinline__ void mha_score_rows(const float* __restrict__ ksh, in
 
 // Fused selection, first phase of the SEL kernel, in two steps around the early tile fetches.
 //
-// mha_score_phase: the NS splits of a head share the scoring.  Split s scores rows
-// [n s / NS, n (s+1) / NS) into the scores output, they meet at head_barrier, and each then reads
-// all n scores back as order keys (a split whose siblings do not arrive in time scores every row
-// itself).  When the threshold selection applies (n <= NT, top_k <= 64), the forced units are
+// mha_score_phase: the M members of a sharing group split the scoring -- the NS splits of a head
+// (one query head per KV head), or the G query heads of one (KV head, split) (grouped-query heads,
+// whose splits sit on different XCDs).  Member m scores rows [n m / M, n (m+1) / M) into sc_out,
+// the members meet at head_barrier, and each then reads all n scores back as order keys (a member
+// whose siblings do not arrive in time scores every row itself).  When the threshold selection applies (n <= NT, top_k <= 64), the forced units are
 // already known here, so their list goes to the front of sel_lds (ascending) and its length is
 // returned: those units' tiles can be fetched before the selection has run.
 // mha_choose_phase: every split selects the forced units plus the top-K others into sel_lds
@@ -295,30 +296,36 @@ __device__ __forceinline__ void mha_forced_list(const uint32_t* forced, int n, i
   if (lane == 0) *nf_out = nf;
 }
 
-template <int D>
-__device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, int NS, uint16_t* lds_raw,
-                               uint16_t* sel_lds) {
+// kvh: the KV head within sequence b; kvseg = b * Hkv + kvh; bar_i: the group's barrier word.
+template <int D, bool GQA>
+__device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg, int64_t bar_i, float* sc_out,
+                               int m, int M, uint16_t* lds_raw, uint16_t* sel_lds) {
   constexpr int NT = kMhaWaves * 64;
   constexpr int LPR = D / 16;
   static_assert((kQbufOffsetF + 32 * D) * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * MhaShape<D>::SLOT,
                 "query staging must fit in the tile slots");
+  static_assert(kQbufOffsetF * sizeof(float) + 8 * 32 * D * sizeof(uint16_t) <=
+                    sizeof(uint16_t) * kMhaWaves * MhaShape<D>::SLOT,
+                "grouped query staging must fit in the tile slots");
   static_assert(kFusedMaxSinks <= NT, "one sink list entry per thread");
   const FusedSelect& f = p.fs;
   const SelLds<D> L(lds_raw);
   const int tid = threadIdx.x;
   const int j = (tid & 63) % LPR;
   const int n = p.n_units;
-  const float* ksh = f.ks + seg * (int64_t)n * D;
-  float* sc_out = f.scores + seg * (int64_t)n;
-  uint32_t* bar = f.barriers + seg * kSyncStride;
+  const float* ksh = f.ks + kvseg * (int64_t)n * D;
+  uint32_t* bar = f.barriers + bar_i * kSyncStride;
   uint32_t g0 = 0;
-  if (NS > 1 && tid == 0) g0 = head_barrier_gen(bar);
+  if (M > 1 && tid == 0) g0 = head_barrier_gen(bar);
 
   // Loads in the order they are needed, so that each wait leaves the later ones in flight (the
   // counter of outstanding loads drains in order): the queries, the sink list (thread t < max_sinks
   // holds entry t; the count trims it once the loads are back), then the pooled-key rows.
+  // (grouped-query heads: the G heads' rows go to LDS by fetches that hold no registers)
+  uint16_t* qstage = reinterpret_cast<uint16_t*>(reinterpret_cast<float*>(lds_raw) + kQbufOffsetF);
   QsumG1<D, 32, NT> qst;
-  qsum_g1_issue<D, 32, NT>(p.q + seg * (int64_t)p.T * D, p.T, qst);
+  if constexpr (GQA) qsum_grouped_fetch<D, 32, NT, 8>(p.q + (int64_t)b * p.H * p.T * D, kvh * p.G, p.G, p.T, qstage);
+  else qsum_g1_issue<D, 32, NT>(p.q + kvseg * (int64_t)p.T * D, p.T, qst);
   // (every load unconditional, from a valid address: a load under a branch would make the waits
   // below count conservatively)
   const uint64_t pred = f.pred_mask[b];
@@ -328,7 +335,7 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, in
                                  : reinterpret_cast<const int32_t*>(f.pred_mask + b);
   const int sink_p = *sp;
   const int sink_n = have_sinks ? f.n_sinks[b] : 0;
-  const int ra = (int)((int64_t)n * s / NS), rb = (int)((int64_t)n * (s + 1) / NS);
+  const int ra = (int)((int64_t)n * m / M), rb = (int)((int64_t)n * (m + 1) / M);
   float x[kScoreBatch][16];
   const bool pre = rb > ra;
   __builtin_amdgcn_sched_barrier(0);
@@ -336,7 +343,12 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, in
   __builtin_amdgcn_sched_barrier(0);
   for (int i = tid; i < (n + 31) / 32; i += NT) L.forced[i] = 0u;
   // the query staging area sits above the keys' scratch in the (still unused) tile slots
-  qsum_g1_finish<D, 32, NT>(qst, pred, p.T, reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, L.qs);
+  if constexpr (GQA) {
+    __syncthreads();   // full vector-memory wait: every wave's query fetches have landed
+    qsum_grouped_tree<D, 32, 8>(pred, p.G, p.T, qstage, L.qs);
+  } else {
+    qsum_g1_finish<D, 32, NT>(qst, pred, p.T, reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, L.qs);
+  }
   block_sync_lds();   // qs and the cleared bits
   if (sink_lane && tid < sink_n && sink_p >= 0) {
     const int u = sink_p >> p.unit_log2;
@@ -349,8 +361,8 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, in
   const bool listing = threshold_select_ok(n, f.top_k);   // uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   bool listed = false;
-  if (NS > 1) {
-    const bool synced = head_barrier(bar, g0, NS, f.spin_limit, L.flag);   // forced bits are complete
+  if (M > 1) {
+    const bool synced = head_barrier(bar, g0, M, f.spin_limit, L.flag);   // forced bits are complete
     // wave 0 lists the forced units while the others read the scores back
     if (listing && wave == 0) mha_forced_list<NT>(L.forced, n, p.max_sel, sel_lds, L.flag + 1);
     listed = true;
@@ -373,15 +385,15 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int64_t seg, int s, in
   return nf < p.max_sel ? nf : p.max_sel;
 }
 
+// writer: the one workgroup of the KV head that writes the selection out.
 template <int D>
-__device__ int mha_choose_phase(const MhaParams& p, int64_t seg, int s, uint16_t* lds_raw, uint16_t* sel_lds) {
+__device__ int mha_choose_phase(const MhaParams& p, int64_t kvseg, bool writer, uint16_t* lds_raw, uint16_t* sel_lds) {
   constexpr int NT = kMhaWaves * 64;
   const FusedSelect& f = p.fs;
   const SelLds<D> L(lds_raw);
   const int tid = threadIdx.x;
   const int n = p.n_units;
-  int32_t* gout = f.sel_idx + seg * p.max_sel;
-  const bool writer = s == 0;
+  int32_t* gout = f.sel_idx + kvseg * p.max_sel;
   SelResult r;
   if (threshold_select_ok(n, f.top_k)) {
     auto emit = [&](int gpos, int lpos, int i) {
@@ -404,7 +416,7 @@ __device__ int mha_choose_phase(const MhaParams& p, int64_t seg, int s, uint16_t
       r = select_core<NT>(L.keys, L.forced, n, f.top_k, scr, emit);
     }
   }
-  if (writer && tid == 0) f.n_sel[seg] = r.total < p.max_sel ? r.total : p.max_sel;
+  if (writer && tid == 0) f.n_sel[kvseg] = r.total < p.max_sel ? r.total : p.max_sel;
   if (tid == 0 && r.total > p.max_sel) latch(p.status, ST_SEL_OVERFLOW);
   block_sync_lds();   // sel_lds complete; the slots are free again
   return r.total < p.max_sel ? r.total : p.max_sel;
@@ -556,7 +568,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   using S = MhaShape<D>;
   constexpr int NT = kMhaWaves * 64;
   constexpr int KS = S::KS, DT = S::DT, PROW = S::PROW;
-  static_assert(!SEL || (!DENSE && !PAGED && !GQA), "fused selection: contiguous sparse, one q-head per KV head");
+  static_assert(!SEL || (!DENSE && !PAGED), "fused selection: contiguous sparse only");
   // grouped-query heads read every tile G times, through L2: their fetches keep the default
   // (cached) policy; one reader per tile streams with the non-temporal one
   constexpr int POL = GQA ? 0 : kStreamPolicy;
@@ -572,17 +584,19 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   const int NS = p.n_splits;
   const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
   int s, seg_i, kv_i;   // split, query head (b * H + h), KV head (b * Hkv + g)
+  int gi = 0, member = 0;   // grouped-query heads: the (KV head, split) group and the head in it
   if constexpr (!GQA) {
     s = xslot % NS;
     seg_i = xcd + 8 * (xslot / NS);
     if (seg_i >= p.n_segs) return;
     kv_i = seg_i;
   } else {
-    const int gi = xcd + 8 * (xslot / p.G);
+    gi = xcd + 8 * (xslot / p.G);
     if (gi >= p.n_groups) return;
     kv_i = gi / NS;
     s = gi % NS;
-    seg_i = (kv_i / p.Hkv) * p.H + (kv_i % p.Hkv) * p.G + xslot % p.G;
+    member = xslot % p.G;
+    seg_i = (kv_i / p.Hkv) * p.H + (kv_i % p.Hkv) * p.G + member;
   }
   const int b = kv_i / p.Hkv, h = kv_i % p.Hkv;   // h: KV head within the sequence
   // the wave index is uniform: in a scalar register, the per-tile bookkeeping stays scalar
@@ -617,7 +631,15 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   uint32_t vm_next = 0;
   bool issued = false;
   if constexpr (SEL) {
-    const int nf = mha_score_phase<D>(p, b, seg, s, NS, lds, sel_lds);
+    // sharing group: the NS splits of the head, or the G heads of this (KV head, split); split 0's
+    // group exchanges its scores through the scores output, the others through their own rows
+    int nf;
+    if constexpr (GQA) {
+      float* xo = s == 0 ? p.fs.scores + kvseg * p.n_units : p.fs.xchg + (int64_t)gi * p.n_units;
+      nf = mha_score_phase<D, true>(p, b, h, kvseg, gi, xo, member, p.G, lds, sel_lds);
+    } else {
+      nf = mha_score_phase<D, false>(p, b, h, kvseg, seg, p.fs.scores + kvseg * p.n_units, s, NS, lds, sel_lds);
+    }
     // Known now: tile 0 (the block's own tokens) and the tiles of the nf forced units at the front
     // of the list.  Up to one of them per wave whose slot the selection scratch leaves free is
     // fetched while the selection runs.  The other tiles go round robin over all 8 NS waves of the
@@ -635,10 +657,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     e = (wave >= FW && jp < e_pre) ? jp : e_rr;
     if (e < e_pre) {   // uniform per wave
       mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp, contig);
-      vm_next = mha_issue<D, false, false>(p, rows, b, h, e, nf << p.unit_log2, tp, slot, lane, bad, contig, voff);
+      vm_next = mha_issue<D, false, false, true, POL>(p, rows, b, h, e, nf << p.unit_log2, tp, slot, lane, bad, contig, voff);
       issued = true;
     }
-    const int ns = mha_choose_phase<D>(p, seg, s, lds, sel_lds);
+    const int ns = mha_choose_phase<D>(p, kvseg, s == 0 && member == 0, lds, sel_lds);
     n_list = p.L == 0 ? 0 : ns << p.unit_log2;
     e1 = 1 + (n_list + kTileTok - 1) / kTileTok;
     if (!issued) mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp, contig);
@@ -1064,7 +1086,9 @@ static void launch_one(Kern kern, dim3 grid, hipStream_t st, const MhaParams& p,
 template <int D>
 static hipError_t launch_mha_d(hipStream_t st, const MhaParams& p, dim3 grid, bool dense, bool paged, bool sel,
                                const KernelTimer* timer) {
-  if (sel) {
+  if (sel && p.G > 1) {
+    launch_one(attn_mha_kernel<D, false, false, true, true>, grid, st, p, timer);
+  } else if (sel) {
     launch_one(attn_mha_kernel<D, false, false, true>, grid, st, p, timer);
   } else if (p.G > 1) {
     if (dense && paged) launch_one(attn_mha_kernel<D, true, true, false, true>, grid, st, p, timer);
@@ -1122,7 +1146,7 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
   // group i (a KV head and a split) run on XCD i % 8 (see the kernel)
   const dim3 grid(g.G == 1 ? 8 * ((p.n_segs + 7) / 8) * n_splits : 8 * ((p.n_groups + 7) / 8) * g.G);
   const bool sel = fsel != nullptr && !dense && !g.paged;
-  if (sel && g.G != 1) return hipErrorInvalidValue;   // fused selection: one q-head per KV head
+  if (sel && g.G > 1 && p.n_groups > kMaxSplitSegs) return hipErrorInvalidValue;   // barrier words
   const hipError_t err = g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0, sel, timer)
                                     : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0, sel, timer);
   if (err != hipSuccess || g.G == 1 || n_splits == 1) return err;

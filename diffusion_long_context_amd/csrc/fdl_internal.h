@@ -77,6 +77,8 @@ struct FusedSelect {
   int32_t* n_sel;              // out: [B][H]
   uint32_t* barriers;          // [B * H][2] split barrier state, left consistent by every launch
   int spin_limit;              // polls before a split stops waiting for its siblings
+  float* xchg;                 // grouped-query heads: [B * Hkv * n_splits][n_units] score exchange
+                               // of every (KV head, split) group but split 0's (which uses scores)
 };
 
 struct Geom {

@@ -73,31 +73,39 @@ __device__ __forceinline__ void query_sum_to_lds(const QT* __restrict__ q, uint6
 
 // query_sum_to_lds for bf16 queries with every thread of an NT-thread block loading: the TMAX rows
 // of each of the G (<= GMAX) heads go to stage [GMAX][TMAX][D] (bf16 bits, LDS) as 16-byte chunks in
-// one round trip, then threads d < D build the same trees from LDS.  Same bits.
+// one round trip, then threads d < D build the same trees from LDS.  Same bits.  Two halves, so
+// that a caller can issue other loads between them: qsum_grouped_issue loads this thread's chunks
+// into registers; qsum_grouped_finish (every thread calls it) stages them and sums.
 template <int D, int TMAX, int NT, int GMAX>
-__device__ __forceinline__ void query_sum_grouped(const uint16_t* __restrict__ q, uint64_t pred, int b, int g,
-                                                  int Hq, int G, int T, uint16_t* stage, float* qs_lds) {
-#pragma clang fp contract(off)
-  constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  constexpr int CH = GMAX * TMAX * CPR;       // chunks of the stage
-  constexpr int PER = (CH + NT - 1) / NT;
-  static_assert(GMAX == 8, "the head tree below has three levels");
-  const int t = threadIdx.x;
+struct QsumGrouped {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int CH = GMAX * TMAX * CPR;       // chunks of the stage
+  static constexpr int PER = CH / NT;
+  static_assert(GMAX == 8, "the head tree has three levels");
+  static_assert(CH % NT == 0, "every thread moves the same number of chunks");
   uint4 v[PER];
+};
+
+// q: the sequence's queries [Hq][T][D]; g0: the group's first query head.
+template <int D, int TMAX, int NT, int GMAX>
+__device__ __forceinline__ void qsum_grouped_issue(const uint16_t* __restrict__ q, int g0, int G, int T,
+                                                   QsumGrouped<D, TMAX, NT, GMAX>& st) {
+  using S = QsumGrouped<D, TMAX, NT, GMAX>;
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
+  for (int k = 0; k < S::PER; ++k) {
     const int c = k * NT + t;
-    const int j = c / (TMAX * CPR), p = (c / CPR) % TMAX, ch = c % CPR;
+    const int j = c / (TMAX * S::CPR), p = (c / S::CPR) % TMAX, ch = c % S::CPR;
     const int jj = j < G ? j : G - 1;   // heads past G read a valid row and are never used
-    const uint16_t* src = q + (((int64_t)b * Hq + g * G + jj) * T + (p < T ? p : T - 1)) * D + ch * 8;
-    v[k] = *reinterpret_cast<const uint4*>(src);
+    st.v[k] = *reinterpret_cast<const uint4*>(q + ((int64_t)(g0 + jj) * T + (p < T ? p : T - 1)) * D + ch * 8);
   }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int c = k * NT + t;
-    if (c < CH) *reinterpret_cast<uint4*>(stage + c * 8) = v[k];
-  }
-  block_sync_lds();
+}
+
+// The trees over a filled stage (threads d < D; the stage must be visible to them).
+template <int D, int TMAX, int GMAX>
+__device__ __forceinline__ void qsum_grouped_tree(uint64_t pred, int G, int T, const uint16_t* stage, float* qs_lds) {
+#pragma clang fp contract(off)
+  const int t = threadIdx.x;
   if (t < D) {
     const int T2 = pow2_ceil(T);
     const int G2 = pow2_ceil(G);
@@ -105,10 +113,16 @@ __device__ __forceinline__ void query_sum_grouped(const uint16_t* __restrict__ q
 #pragma unroll
     for (int j = 0; j < GMAX; ++j) {
       float a[TMAX];
+      // every read is unconditional (a masked read becomes a branch and a wait per element), and
+      // the head's reads all go out before its tree starts
+      uint32_t raw[TMAX];
+#pragma unroll
+      for (int p = 0; p < TMAX; ++p) raw[p] = stage[(j * TMAX + p) * D + t];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int p = 0; p < TMAX; ++p) {
         const bool keep = j < G && p < T && ((pred >> p) & 1ull);
-        a[p] = keep ? bf16_bits_to_f32(stage[(j * TMAX + p) * D + t]) : 0.f;
+        a[p] = keep ? bf16_bits_to_f32(raw[p]) : 0.f;
       }
 #pragma unroll
       for (int lvl = 0; lvl < 6; ++lvl) {
@@ -127,6 +141,37 @@ __device__ __forceinline__ void query_sum_grouped(const uint16_t* __restrict__ q
       }
     }
     qs_lds[t] = hv[0];
+  }
+}
+
+template <int D, int TMAX, int NT, int GMAX>
+__device__ __forceinline__ void qsum_grouped_finish(const QsumGrouped<D, TMAX, NT, GMAX>& st, uint64_t pred, int G,
+                                                    int T, uint16_t* stage, float* qs_lds) {
+  using S = QsumGrouped<D, TMAX, NT, GMAX>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < S::PER; ++k) *reinterpret_cast<uint4*>(stage + (k * NT + t) * 8) = st.v[k];
+  block_sync_lds();
+  qsum_grouped_tree<D, TMAX, GMAX>(pred, G, T, stage, qs_lds);
+}
+
+// The same stage filled by LDS fetches (no registers held while they fly): chunk c = k NT + t lands
+// at stage + 8 c.  The caller must wait for its own fetches (vector-memory count) and then meet the
+// other waves at a barrier before qsum_grouped_tree.
+template <int D, int TMAX, int NT, int GMAX>
+__device__ __forceinline__ void qsum_grouped_fetch(const uint16_t* __restrict__ q, int g0, int G, int T,
+                                                   uint16_t* stage) {
+  using S = QsumGrouped<D, TMAX, NT, GMAX>;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+#pragma unroll
+  for (int k = 0; k < S::PER; ++k) {
+    const int c = k * NT + wave * 64 + lane;
+    const int j = c / (TMAX * S::CPR), p = (c / S::CPR) % TMAX, ch = c % S::CPR;
+    const int jj = j < G ? j : G - 1;
+    const void* src = q + ((int64_t)(g0 + jj) * T + (p < T ? p : T - 1)) * D + ch * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(stage + (k * NT + wave * 64) * 8),
+                                     16, 0, 0);
   }
 }
 

@@ -212,7 +212,9 @@ __global__ __launch_bounds__(256) void score_units_kernel(const QT* __restrict__
   }
   if constexpr (std::is_same<QT, uint16_t>::value && TMAX == 32) {
     __shared__ __attribute__((aligned(16))) uint16_t stage[8 * 32 * D];
-    query_sum_grouped<D, 32, 256, 8>(q, pred_mask[b], b, g, Hq, G, T, stage, qs);
+    QsumGrouped<D, 32, 256, 8> qst;
+    qsum_grouped_issue<D, 32, 256, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
+    qsum_grouped_finish<D, 32, 256, 8>(qst, pred_mask[b], G, T, stage, qs);
   } else {
     query_sum_to_lds<QT, D, TMAX>(q, pred_mask[b], b, g, Hq, G, T, qs);
   }

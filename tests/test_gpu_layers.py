@@ -101,7 +101,7 @@ def test_dense_attention_paged(h, kw):
     dict(ctx_len=1000, top_k_blocks=32),                  # fewer blocks than the top-K
     dict(ctx_len=6000, top_k_blocks=40),                  # sink block outside the top-K
     dict(ctx_len=6000, top_k_blocks=40, sink_kind="shared_dir_x8"),
-    dict(ctx_len=6000, top_k_blocks=40, n_kv_heads=2),    # grouped-query: the unfused chain
+    dict(ctx_len=6000, top_k_blocks=40, n_kv_heads=2),    # grouped-query heads (G = 4)
     dict(batch=8, n_q_heads=32, n_kv_heads=32, ctx_len=2048, top_k_blocks=8),   # one split per head
     dict(ctx_len=41000, top_k_blocks=48),                 # 641 blocks: the radix selection path
     dict(ctx_len=6000, top_k_blocks=40, spin_limit=0),    # splits never wait: redundant scoring
