@@ -400,7 +400,7 @@ def main():
                    "sink_source_layer": cfg.source_layer, "gen_len": gen_steps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
-                     "kernel": "attn_mha_kernel<128,false,false,true> (block scoring + selection + sparse attention)",
+                     "kernel": "attn_mha_kernel<128,false,false,true,false> (block scoring + selection + sparse attention)",
                      "avg_launch_us": sparse_us, "launches": prof_main["sparse_attn"][1],
                      "bytes_per_launch": launch_bytes, "units_per_launch": units,
                      "unit_bytes": unit_bytes},
