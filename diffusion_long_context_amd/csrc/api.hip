@@ -334,7 +334,7 @@ fdl_status fdl_pool_keys(fdl_handle h, const fdl_geom* gp, const void* k_cache,
     return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
   ProfScope ps(h, FDL_PROF_POOL);
   return hip_status(h, fdl::launch_pool_keys(h->stream, g, k_cache, page_table, ilog2(unit_tokens), ks,
-                                             h->status),
+                                             h->status, reinterpret_cast<float*>(h->scratch), h->scratch_bytes),
                     "pool_keys launch");
 }
 

@@ -90,8 +90,10 @@ hipError_t launch_predict(hipStream_t s, int batch, int T, const float* prev_con
                           const uint8_t* masked, int top_k, int window, uint64_t* pred_mask,
                           int32_t* n_pred);
 
+// sub / sub_bytes: scratch for the sub-unit sums of units longer than 64 tokens (two passes); with
+// too little of it one pass runs.
 hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const int32_t* page_table,
-                            int unit_log2, float* ks, uint32_t* status);
+                            int unit_log2, float* ks, uint32_t* status, float* sub, size_t sub_bytes);
 
 hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                               const float* ks, int n_units, float* scores);

@@ -45,6 +45,8 @@ __device__ __forceinline__ float2 load_pair<float>(const float* p) {
 
 __device__ __forceinline__ float2 add2(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 
+constexpr int ilog2_const(int x) { return x <= 1 ? 0 : 1 + ilog2_const(x / 2); }
+
 // Adjacent-pair tree over LEAVES consecutive tokens starting at t0 (tokens >= L are +0).  Every
 // load is issued before the first add.
 template <typename KT, int LEAVES, bool PAGED>
@@ -52,10 +54,17 @@ __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRo
                                             int g, int t0, int pair, bool& bad) {
   float2 a[LEAVES];
   int64_t off[LEAVES];
+  if (PAGED && (t0 & (LEAVES - 1)) == 0 && rows.page_log2 >= ilog2_const(LEAVES) && t0 + LEAVES <= rows.L) {
+    // uniform: the run lies in one page, so one table lookup gives every row
+    const int64_t base = rows.off(b, g, t0, bad);
 #pragma unroll
-  for (int i = 0; i < LEAVES; ++i) {
-    const int t = t0 + i;
-    off[i] = rows.off(b, g, t < rows.L ? t : rows.L - 1, bad);
+    for (int i = 0; i < LEAVES; ++i) off[i] = base + (int64_t)i * rows.D;
+  } else {
+#pragma unroll
+    for (int i = 0; i < LEAVES; ++i) {
+      const int t = t0 + i;
+      off[i] = rows.off(b, g, t < rows.L ? t : rows.L - 1, bad);
+    }
   }
 #pragma unroll
   for (int i = 0; i < LEAVES; ++i) a[i] = load_pair<KT>(k + off[i] + 2 * pair);
@@ -68,6 +77,41 @@ __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRo
     for (int i = 0; i < w; ++i) a[i] = add2(a[2 * i], a[2 * i + 1]);
   }
   return a[0];
+}
+
+// Second pass of the pooling of units longer than 64 tokens: ks[b][g][n] = adjacent-pair tree over
+// the unit's n_sub sub-unit sums sub[b][g][n * n_sub + i] (each the tree over 64 tokens; indices past
+// n_sub_all are +0).  The tree over a power-of-two unit is the tree over its aligned 64-token
+// sub-trees, so the bits are those of the one-pass tree.  Thread (unit, dimension pair).
+template <int D>
+__global__ __launch_bounds__(256) void pool_merge_kernel(const float* __restrict__ sub, int n_sub, int n_sub_all,
+                                                         int n_units, int Hkv, float* __restrict__ ks) {
+  constexpr int kTeam = D / 2;
+  constexpr int kTeams = 256 / kTeam;
+  const int team = threadIdx.x / kTeam, pair = threadIdx.x % kTeam;
+  const int n = blockIdx.x * kTeams + team;
+  const int g = blockIdx.y, b = blockIdx.z;
+  if (n >= n_units) return;
+  const float* src = sub + ((int64_t)b * Hkv + g) * n_sub_all * D + 2 * pair;
+  float2 a[64];
+  // every load unconditional (clamped index), masked afterwards: a guarded load would be waited for
+  // on its own
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int si = n * n_sub + i;
+    a[i] = *reinterpret_cast<const float2*>(src + (int64_t)(si < n_sub_all ? si : n_sub_all - 1) * D);
+  }
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+    if (!(i < n_sub && n * n_sub + i < n_sub_all)) a[i] = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int w = 32; w >= 1; w /= 2) {
+    if (w < n_sub) {   // uniform: levels of the n_sub-leaf tree only
+#pragma unroll
+      for (int i = 0; i < w; ++i) a[i] = add2(a[2 * i], a[2 * i + 1]);
+    }
+  }
+  *reinterpret_cast<float2*>(ks + (((int64_t)b * Hkv + g) * n_units + n) * D + 2 * pair) = a[0];
 }
 
 // One "team" of D/2 threads per unit; thread `pair` owns dimensions 2*pair and 2*pair+1.
@@ -124,12 +168,24 @@ static KvRows<PAGED> make_rows(const Geom& g, const int32_t* page_table) {
 
 template <typename KT, int D, bool PAGED>
 static hipError_t pool_dispatch(hipStream_t s, const Geom& g, const KT* k, const int32_t* page_table,
-                                int unit_log2, float* ks, uint32_t* status) {
+                                int unit_log2, float* ks, uint32_t* status, float* sub, size_t sub_bytes) {
   const int unit = 1 << unit_log2;
   const int n_units = (g.L + unit - 1) / unit;
   if (n_units == 0) return hipSuccess;
   const KvRows<PAGED> rows = make_rows<PAGED>(g, page_table);
   constexpr int kTeams = 256 / (D / 2);
+  const int n_sub_all = (g.L + 63) / 64;
+  if (unit > 64 && unit / 64 <= 64 && sub != nullptr &&
+      (size_t)g.B * g.Hkv * n_sub_all * D * sizeof(float) <= sub_bytes) {
+    // two passes: 64-token sub-unit sums over the whole chip, then the tree over each unit's
+    // sub-sums (one pass would give each unit's 64-token runs to one team, one after another)
+    dim3 g1((n_sub_all + kTeams - 1) / kTeams, g.Hkv, g.B);
+    hipLaunchKernelGGL((pool_keys_kernel<KT, D, 64, PAGED>), g1, dim3(256), 0, s, k, rows, 6, n_sub_all, sub,
+                       status);
+    dim3 g2((n_units + kTeams - 1) / kTeams, g.Hkv, g.B);
+    hipLaunchKernelGGL((pool_merge_kernel<D>), g2, dim3(256), 0, s, sub, unit / 64, n_sub_all, n_units, g.Hkv, ks);
+    return hipGetLastError();
+  }
   dim3 grid((n_units + kTeams - 1) / kTeams, g.Hkv, g.B);
   size_t lds = 0;
   if (unit > 64) lds = (size_t)kTeams * (unit / 64) * (D / 2) * sizeof(float2);
@@ -156,21 +212,21 @@ static hipError_t pool_dispatch(hipStream_t s, const Geom& g, const KT* k, const
 }
 
 hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const int32_t* page_table,
-                            int unit_log2, float* ks, uint32_t* status) {
+                            int unit_log2, float* ks, uint32_t* status, float* sub, size_t sub_bytes) {
   if (g.dtype == FDL_BF16) {
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     if (g.paged)
-      return g.D == 128 ? pool_dispatch<uint16_t, 128, true>(s, g, kk, page_table, unit_log2, ks, status)
-                        : pool_dispatch<uint16_t, 64, true>(s, g, kk, page_table, unit_log2, ks, status);
-    return g.D == 128 ? pool_dispatch<uint16_t, 128, false>(s, g, kk, page_table, unit_log2, ks, status)
-                      : pool_dispatch<uint16_t, 64, false>(s, g, kk, page_table, unit_log2, ks, status);
+      return g.D == 128 ? pool_dispatch<uint16_t, 128, true>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes)
+                        : pool_dispatch<uint16_t, 64, true>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes);
+    return g.D == 128 ? pool_dispatch<uint16_t, 128, false>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes)
+                      : pool_dispatch<uint16_t, 64, false>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes);
   }
   const float* kk = static_cast<const float*>(k);
   if (g.paged)
-    return g.D == 128 ? pool_dispatch<float, 128, true>(s, g, kk, page_table, unit_log2, ks, status)
-                      : pool_dispatch<float, 64, true>(s, g, kk, page_table, unit_log2, ks, status);
-  return g.D == 128 ? pool_dispatch<float, 128, false>(s, g, kk, page_table, unit_log2, ks, status)
-                    : pool_dispatch<float, 64, false>(s, g, kk, page_table, unit_log2, ks, status);
+    return g.D == 128 ? pool_dispatch<float, 128, true>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes)
+                      : pool_dispatch<float, 64, true>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes);
+  return g.D == 128 ? pool_dispatch<float, 128, false>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes)
+                    : pool_dispatch<float, 64, false>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes);
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -96,7 +96,8 @@ def _small_bf16(**kw):
     _small_bf16(n_q_heads=4, n_kv_heads=4, ctx_len=1000, kv_block=64),       # ragged last block
     _small_bf16(n_q_heads=4, n_kv_heads=2, ctx_len=777, kv_block=16, head_dim=64),
     _small_bf16(n_q_heads=2, n_kv_heads=2, ctx_len=4096, kv_block=2048),     # chunk-sized units
-], ids=["tiny", "ragged", "d64", "chunk"])
+    _small_bf16(n_q_heads=2, n_kv_heads=2, ctx_len=5000, kv_block=1024),     # ragged last chunk
+], ids=["tiny", "ragged", "d64", "chunk", "chunk-ragged"])
 def test_pool_and_scores_bit_exact(h, cfg):
     x = make_single(cfg)
     g = _geom(cfg)
@@ -112,6 +113,24 @@ def test_pool_and_scores_bit_exact(h, cfg):
     assert np.array_equal(host(ks).view(np.uint32), want_ks.view(np.uint32))
     want_sc = unit_scores(query_sum(x["q"], bits, cfg.n_kv_heads), want_ks)
     assert np.array_equal(host(sc).view(np.uint32), want_sc.view(np.uint32))
+
+
+def test_pool_chunks_one_pass_fallback():
+    """With too little workspace for the sub-unit sums, chunk pooling runs in one pass: same bits."""
+    require_gpu()
+    from diffusion_long_context_amd import Handle
+    # sub-unit sums: 8 heads x 313 runs x 512 B = 1.28 MB > the 1 MiB of scratch of the smallest workspace
+    cfg = _small_bf16(n_q_heads=8, n_kv_heads=8, ctx_len=20000, kv_block=2048)
+    x = make_single(cfg)
+    hs = Handle(workspace_bytes=2 << 20)
+    try:
+        ks = torch.zeros(cfg.batch, cfg.n_kv_heads, 10, cfg.head_dim, dtype=torch.float32, device="cuda")
+        hs.fdl_pool_keys(_geom(cfg), dev(x["k"]), None, cfg.kv_block, ks)
+        torch.cuda.synchronize()
+        assert hs.fdl_get_status() == 0
+        assert np.array_equal(host(ks).view(np.uint32), pool_keys(x["k"], cfg.kv_block).view(np.uint32))
+    finally:
+        hs.close()
 
 
 def test_scores_all_positions_predicted(h):
