@@ -105,13 +105,15 @@ def test_dense_attention_paged(h, kw):
     dict(batch=8, n_q_heads=32, n_kv_heads=32, ctx_len=2048, top_k_blocks=8),   # one split per head
     dict(ctx_len=41000, top_k_blocks=48),                 # 641 blocks: the radix selection path
     dict(ctx_len=6000, top_k_blocks=40, spin_limit=0),    # splits never wait: redundant scoring
+    dict(ctx_len=6000, top_k_blocks=40, n_kv_heads=2, spin_limit=0),   # the same, grouped-query
 ], ids=["list-below-topk", "list-above-topk", "scattered-sinks", "gqa4", "one-split", "641-blocks",
-        "no-wait-fallback"])
+        "no-wait-fallback", "gqa4-no-wait-fallback"])
 def test_focus_step_driver(kw, monkeypatch):
     """fdl_focus_step (one call: predict, then dense / source / reuse / reuse layers) against the
-    oracle layer by layer.  With one q-head per KV head the sparse layers run scoring, selection and
-    attention as one fused kernel whose splits share the scoring; with grouped-query heads as three
-    launches."""
+    oracle layer by layer.  The sparse layers run scoring, selection and attention as one fused
+    kernel: with one q-head per KV head the splits of a head share the scoring, with grouped-query
+    heads the G heads of a (KV head, split) group do (the other groups exchange through workspace
+    rows)."""
     require_gpu()
     from diffusion_long_context_amd import Handle
     from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
