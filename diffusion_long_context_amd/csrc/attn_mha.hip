@@ -246,22 +246,18 @@ struct SelLds {
   float* qs;          // [D]
   uint32_t* keys;     // [kFusedMaxUnits]
   uint32_t* forced;   // [kFusedMaxUnits / 32]
-  int* hist;          // [256]
+  int* hist;          // [4 * 256]
   int* tmp;           // [NT / 64]
-  uint32_t* digit;
-  int* above;
-  int* flag;
+  int* flag;          // [2]
   __device__ explicit SelLds(uint16_t* lds_raw) {
     constexpr int NT = kMhaWaves * 64;
     qs = reinterpret_cast<float*>(lds_raw);
     keys = reinterpret_cast<uint32_t*>(lds_raw) + D;
     forced = keys + kFusedMaxUnits;
     hist = reinterpret_cast<int*>(forced + kFusedMaxUnits / 32);
-    tmp = hist + 256;
-    digit = reinterpret_cast<uint32_t*>(tmp + NT / 64);
-    above = reinterpret_cast<int*>(digit + 1);
-    flag = above + 1;
-    static_assert(D + kFusedMaxUnits + kFusedMaxUnits / 32 + 256 + NT / 64 + 4 <= kQbufOffsetF, "select scratch");
+    tmp = hist + 4 * 256;
+    flag = tmp + NT / 64;
+    static_assert(D + kFusedMaxUnits + kFusedMaxUnits / 32 + 4 * 256 + NT / 64 + 2 <= kQbufOffsetF, "select scratch");
   }
 };
 
@@ -412,8 +408,8 @@ __device__ int mha_choose_phase(const MhaParams& p, int64_t kvseg, bool writer, 
       r = select_small<NT>(L.keys, L.forced, n, f.top_k, reinterpret_cast<uint64_t*>(L.keys + kFusedMaxUnits - 2 * NT),
                            reinterpret_cast<uint32_t*>(L.hist), L.hist + 64, L.tmp, emit);
     } else {
-      const SelScratch scr{L.hist, L.tmp, L.digit, L.above};
-      r = select_core<NT>(L.keys, L.forced, n, f.top_k, scr, emit);
+      const SelScratch scr{L.hist, L.tmp};
+      r = select_core<NT, kFusedMaxUnits / NT>(L.keys, L.forced, n, f.top_k, scr, emit);
     }
   }
   if (writer && tid == 0) f.n_sel[kvseg] = r.total < p.max_sel ? r.total : p.max_sel;

@@ -12,35 +12,45 @@
 
 namespace fdl {
 
-// LDS scratch of select_core: hist[256], tmp[NT / 64], digit, above.
+// Inclusive prefix sum along each 16-lane row (DPP row shifts by 1, 2, 4, 8; lanes without a source
+// add 0).
+__device__ __forceinline__ int row_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes: row scans, then each row adds the totals of the rows
+// before it (read from lanes 15, 31, 47).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int incl = row_incl_scan(x);
+  const int r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31),
+            r2 = __builtin_amdgcn_readlane(incl, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return incl + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// LDS scratch of select_core: hist[4 * 256] (one histogram per radix pass), tmp[NT / 64].
 struct SelScratch {
   int* hist;
   int* tmp;
-  uint32_t* digit;
-  int* above;
 };
 
-// Exclusive scan of one int per thread over an NT-thread block; also returns the total.
+// Exclusive scan of one int per thread over an NT-thread block; also returns the total.  One
+// barrier; tmp must not be written again before a later barrier.
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  constexpr int NW = NT / 64;
+  static_assert(NW <= 16, "wave totals in one row of lanes");
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int incl = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = incl;
   block_sync_lds();
-  int off = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int t = tmp[w];
-    if (w < wave) off += t;
-    total += t;
-  }
-  block_sync_lds();
+  const int wt = row_incl_scan(lane < NW ? tmp[lane] : 0);
+  total = __builtin_amdgcn_readlane(wt, NW - 1);
+  const int off = wave > 0 ? __builtin_amdgcn_readlane(wt, wave > 0 ? wave - 1 : 0) : 0;
   return off + incl - v;
 }
 
@@ -49,111 +59,133 @@ struct SelResult {
   int kk;      // chosen among the non-forced: min(top_k, n - forced)
 };
 
-// n <= 32 * NT.  emit(pos, i) is called by the owning thread for every taken index i, with pos its
-// rank in ascending order.  Every thread of the block must call this.
-template <int NT, typename Emit>
+// n <= EMAX * NT (EMAX a multiple of 4; keys and forced hold at least EMAX * NT elements).
+// emit(pos, i) is called by the owning thread for every taken index i, with pos its rank in
+// ascending order.  Every thread of the block must call this.
+// Thread t owns the E4 consecutive elements from t E4 (E4 = ceil(n / NT) rounded up to 4) and holds
+// their keys and forced bits in registers for every phase.  Barriers: one to clear the histograms,
+// one per radix pass, one for the ordered scan.  Every wave counts the forced members and finds each
+// pass's digit itself (the same integers in every wave), so nothing is broadcast; each pass has a
+// histogram of its own, so none is cleared in between.
+template <int NT, int EMAX, typename Emit>
 __device__ SelResult select_core(const uint32_t* keys, const uint32_t* forced, int n, int top_k,
                                  const SelScratch& sc, Emit emit) {
-  const int tid = threadIdx.x;
-  // ownership for the ordered phases: thread t owns [t*E, (t+1)*E)
-  const int E = (n + NT - 1) / NT;
-  const int i0 = tid * E;
-  int nf_local = 0;
-  for (int e = 0; e < E; ++e) {
-    const int i = i0 + e;
-    if (i < n && ((forced[i >> 5] >> (i & 31)) & 1u)) ++nf_local;
+  static_assert(EMAX % 4 == 0 && EMAX <= 32, "register-held elements");
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (n <= 0) return {0, 0};   // uniform
+  const int E4 = (((n + NT - 1) / NT) + 3) & ~3;
+  const int i0 = tid * E4;
+  const int n_words = (n + 31) / 32;
+  int fl = 0;
+  for (int w = lane; w < n_words; w += 64) {
+    uint32_t word = forced[w];
+    if (w == n_words - 1 && (n & 31) != 0) word &= (1u << (n & 31)) - 1u;
+    fl += __popc(word);
   }
-  int n_forced;
-  (void)block_excl_scan<NT>(nf_local, sc.tmp, n_forced);
+  const int n_forced = __builtin_amdgcn_readlane(wave_incl_scan(fl), 63);
   const int n_elig = n - n_forced;
   const int kk = top_k < n_elig ? top_k : n_elig;
+
+  // this thread's keys and forced bits (bit e: element i0 + e); elements past n are not live
+  uint32_t kv[EMAX];
+#pragma unroll
+  for (int c = 0; c < EMAX / 4; ++c) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (4 * c < E4) v = *reinterpret_cast<const uint4*>(keys + i0 + 4 * c);   // uniform bound
+    kv[4 * c] = v.x;
+    kv[4 * c + 1] = v.y;
+    kv[4 * c + 2] = v.z;
+    kv[4 * c + 3] = v.w;
+  }
+  const int wi = (i0 >> 5) < n_words - 1 ? (i0 >> 5) : n_words - 1;
+  const int wj = wi + 1 < n_words ? wi + 1 : n_words - 1;
+  const uint64_t fw = (uint64_t)forced[wi] | ((uint64_t)forced[wj] << 32);
+  const int live_n = n - i0 < 0 ? 0 : (n - i0 > E4 ? E4 : n - i0);
+  const uint32_t live = live_n >= 32 ? 0xFFFFFFFFu : ((1u << live_n) - 1u);
+  const uint32_t fb = (uint32_t)(fw >> (i0 & 31)) & live;
+  const uint32_t elig = live & ~fb;
 
   // radix select of the kk-th best key among the eligible elements
   uint32_t prefix = 0u, pmask = 0u;
   int rem = kk;
   const bool take_all = (kk == n_elig);
-  if (kk > 0 && !take_all) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += NT) sc.hist[i] = 0;
-      block_sync_lds();
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t k = keys[i];
-        if (((forced[i >> 5] >> (i & 31)) & 1u) == 0u && (k & pmask) == prefix)
-          atomicAdd(&sc.hist[(k >> shift) & 255u], 1);
+  if (kk > 0 && !take_all) {   // uniform
+    for (int i = tid; i < 4 * 256; i += NT) sc.hist[i] = 0;
+    block_sync_lds();
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      int* h = sc.hist + 256 * pass;
+      // in chunks of 4 owned elements, skipping the chunks past E4 (a uniform test)
+#pragma unroll
+      for (int c = 0; c < EMAX / 4; ++c) {
+        if (4 * c >= E4) break;
+#pragma unroll
+        for (int e = 4 * c; e < 4 * c + 4; ++e)
+          if (((elig >> e) & 1u) && (kv[e] & pmask) == prefix) atomicAdd(&h[(kv[e] >> shift) & 255u], 1);
       }
       block_sync_lds();
-      if (tid < 64) {
-        // lane l sums bins 255-4l .. 252-4l (descending digits)
-        int cnt[4], s = 0;
+      // lane l holds bins 255-4l .. 252-4l (descending digits); the first lane whose running count
+      // reaches rem holds the digit
+      int cnt[4], sl = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          cnt[e] = sc.hist[255 - 4 * tid - e];
-          s += cnt[e];
-        }
-        int incl = s;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int u = __shfl_up(incl, o, 64);
-          if (tid >= o) incl += u;
-        }
-        const uint64_t hit = __ballot(incl >= rem);
-        const int first = __ffsll((unsigned long long)hit) - 1;
-        if (tid == first) {
-          int above = incl - s;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (above + cnt[e] >= rem) {
-              *sc.digit = (uint32_t)(255 - 4 * tid - e);
-              *sc.above = above;
-              break;
-            }
-            above += cnt[e];
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        cnt[e] = h[255 - 4 * lane - e];
+        sl += cnt[e];
       }
-      block_sync_lds();
-      prefix |= *sc.digit << shift;
+      const int incl = wave_incl_scan(sl);
+      const uint64_t hit = __ballot(incl >= rem);
+      const int first = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+      // within the lane, the first of its bins (descending) where the count reaches rem, and the
+      // members above that bin
+      int a = incl - sl, found = -1, above = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (found < 0 && a + cnt[e] >= rem) {
+          found = e;
+          above = a;
+        }
+        a += cnt[e];
+      }
+      const int dig = 255 - 4 * lane - (found < 0 ? 0 : found);
+      const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(dig, first);
+      prefix |= digit << shift;
       pmask |= 255u << shift;
-      rem -= *sc.above;
-      block_sync_lds();
+      rem -= __builtin_amdgcn_readlane(above, first);
     }
   }
   const uint32_t theta = prefix;
 
-  // ordered compaction: ties at theta go to the lowest indices
-  int tie_local = 0;
-  for (int e = 0; e < E; ++e) {
-    const int i = i0 + e;
-    if (i < n && ((forced[i >> 5] >> (i & 31)) & 1u) == 0u && keys[i] == theta) ++tie_local;
-  }
-  int tie_total;
-  int tie_rank = block_excl_scan<NT>(tie_local, sc.tmp, tie_total);
-  uint32_t selbits = 0u;   // E <= 32
-  int sel_local = 0;
-  for (int e = 0; e < E; ++e) {
-    const int i = i0 + e;
-    if (i >= n) break;
-    const bool f = ((forced[i >> 5] >> (i & 31)) & 1u) != 0u;
-    bool take = f;
-    if (!f && kk > 0) {
-      const uint32_t k = keys[i];
-      if (take_all || k > theta) {
-        take = true;
-      } else if (k == theta) {
-        take = tie_rank < rem;
-        ++tie_rank;
+  // ordered emission: per thread, members above theta (and forced ones) and ties at theta, counted
+  // together in one scan (16 bits each); ties go to the lowest indices
+  uint32_t above_m = fb, tie_m = 0u;
+  if (kk > 0) {   // uniform
+#pragma unroll
+    for (int c = 0; c < EMAX / 4; ++c) {
+      if (4 * c >= E4) break;
+#pragma unroll
+      for (int e = 4 * c; e < 4 * c + 4; ++e) {
+        const bool el = (elig >> e) & 1u;
+        above_m |= (el && (take_all || kv[e] > theta)) ? 1u << e : 0u;
+        tie_m |= (el && !take_all && kv[e] == theta) ? 1u << e : 0u;
       }
     }
-    if (take) {
-      selbits |= 1u << e;
-      ++sel_local;
-    }
   }
-  int sel_total;
-  int pos = block_excl_scan<NT>(sel_local, sc.tmp, sel_total);
-  for (int e = 0; e < E; ++e)
-    if ((selbits >> e) & 1u) emit(pos++, i0 + e);
-  return {sel_total, kk};
+  int tot;
+  const int ex = block_excl_scan<NT>(__popc(above_m) | (__popc(tie_m) << 16), sc.tmp, tot);
+  const int tr = ex >> 16;
+  // ties of this thread still taken: the lowest ones, up to rem - tr
+  const int my_ties = rem - tr <= 0 ? 0 : rem - tr;
+  uint32_t take_m = above_m;
+  uint32_t tm = tie_m;
+  for (int c = 0; c < my_ties && tm != 0u; ++c) {
+    take_m |= tm & (0u - tm);   // lowest remaining tie
+    tm &= tm - 1u;
+  }
+  int pos = (ex & 0xFFFF) + (tr < rem ? tr : rem);
+  for (uint32_t m = take_m; m != 0u; m &= m - 1u) emit(pos++, i0 + __builtin_ctz(m));
+  const int tot_ties = tot >> 16;
+  return {(tot & 0xFFFF) + (tot_ties < rem ? tot_ties : rem), kk};
 }
 
 }  // namespace fdl
@@ -325,15 +357,6 @@ __device__ __forceinline__ void wave_sort_desc32(uint32_t& v) {
   bitonic_merge32<K, K / 2>(v);
 }
 
-// Inclusive prefix sum along each 16-lane row (DPP row shifts by 1, 2, 4, 8; lanes without a source
-// add 0).
-__device__ __forceinline__ int row_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
-  return x;
-}
 
 // The same selection as select_core for n <= NT and top_k <= 64, found through a threshold.  The
 // eligible keys (forced units and threads past n count as 0, which no eligible key is below) are

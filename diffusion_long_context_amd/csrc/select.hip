@@ -25,10 +25,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t* __restrict__ n_sel, uint32_t* __restrict__ status) {
   __shared__ uint32_t keys[kMaxSelN];
   __shared__ uint32_t forced[kMaxSelN / 32];
-  __shared__ int hist[256];
+  __shared__ int hist[4 * 256];
   __shared__ int tmp[8];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_above;
 
   const int tid = threadIdx.x;
   const int g = blockIdx.y, b = blockIdx.z, c = blockIdx.x;
@@ -54,7 +52,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
   __syncthreads();
 
-  const SelScratch scr{hist, tmp, &s_digit, &s_above};
+  const SelScratch scr{hist, tmp};
   int32_t* out = sel_idx + seg * (int64_t)max_sel;
   int base = 0;
   if (level2) {
@@ -78,7 +76,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                                     if (gpos < max_sel) out[gpos] = i;
                                   });
   } else {
-    r = select_core<kSelThreads>(keys, forced, n, top_k, scr,
+    r = select_core<kSelThreads, kSelPerThread>(keys, forced, n, top_k, scr,
                                  [&](int pos, int i) { out[pos] = (base < 0) ? -1 : base + i; });
   }
   if (tid == 0 && c == 0) {

@@ -151,10 +151,11 @@ def test_scores_all_positions_predicted(h):
 # selection on crafted scores (ties, -0/+0, NaN, forced sinks)
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("seed", range(4))
-def test_select_crafted(h, seed):
+@pytest.mark.parametrize("seed,n", [(0, 300), (1, 300), (2, 300), (3, 300), (4, 200), (5, 200), (6, 2000)])
+def test_select_crafted(h, seed, n):
+    """n <= 256 with K <= 64 takes the sort-and-threshold form, the rest the radix select."""
     rng = np.random.default_rng(seed)
-    B, Hkv, n = 2, 3, 300
+    B, Hkv = 2, 3
     cfg = _small_bf16(batch=B, n_q_heads=Hkv, n_kv_heads=Hkv, ctx_len=n * 64)
     g = _geom(cfg)
     scores = rng.choice([1.0, 2.0, -0.0, 0.0, np.nan, -np.inf, 3.5, 1e-40, -1e-40], size=(B, Hkv, n))
@@ -163,9 +164,9 @@ def test_select_crafted(h, seed):
     max_sinks = 8
     sink_pos = np.full((B, max_sinks), -1, np.int32)
     sink_pos[0, :3] = [0, 70, 71]
-    sink_pos[1, :1] = [64 * 299 + 5]
+    sink_pos[1, :1] = [64 * (n - 1) + 5]
     n_sinks = np.array([3, 1], np.int32)
-    for k in (0, 1, 17, 64, 297, 299, 500):
+    for k in (0, 1, 17, 64, n - 3, n - 1, 500):
         max_sel = min(n, max_sinks + k)
         sel = torch.zeros(B, Hkv, max_sel, dtype=torch.int32, device="cuda")
         nsel = torch.zeros(B, Hkv, dtype=torch.int32, device="cuda")
