@@ -420,6 +420,43 @@ fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* gp, const float* scor
                     n_cand, top_k, force_first ? 1 : 0, max_sel, sel_idx, n_sel);
 }
 
+fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* gp, const void* q, const uint64_t* pred_mask,
+                                   const void* k_cache, const int32_t* page_table, int32_t unit_tokens,
+                                   const int32_t* cand_idx, int32_t n_cand, int32_t top_k, int32_t max_sel,
+                                   float* scores, int32_t* sel_idx, int32_t* n_sel) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!q || !pred_mask || !k_cache || !cand_idx || !scores || !sel_idx || !n_sel)
+    return fail(h, FDL_EINVAL, "q, pred_mask, k_cache, cand_idx, scores, sel_idx and n_sel must be non-NULL");
+  if (!is_pow2(unit_tokens) || unit_tokens > 4096)
+    return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
+  if (g.L % unit_tokens) return fail(h, FDL_EINVAL, "level-2 scoring needs ctx_len %% unit_tokens == 0");
+  const int n_units = g.L / unit_tokens;
+  if (n_cand < 1 || n_cand > n_units) return fail(h, FDL_EINVAL, "n_cand must be in [1, n_units]");
+  if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
+  if (top_k < 0 || top_k > unit_tokens - 1) return fail(h, FDL_EINVAL, "top_k must be in [0, unit_tokens - 1]");
+  if (max_sel < 1 || (long long)n_cand * (1 + top_k) > max_sel) return fail(h, FDL_EINVAL, "max_sel too small");
+  const int lg = ilog2(unit_tokens);
+  if (fdl::score_select_tokens_ok(g, lg)) {
+    ProfScope ps(h, FDL_PROF_SCORE);
+    return hip_status(h, fdl::launch_score_select_tokens(h->stream, g, q, pred_mask, k_cache, page_table, lg,
+                                                         cand_idx, n_cand, top_k, max_sel, scores, sel_idx,
+                                                         n_sel, h->status),
+                      "score_select_tokens launch");
+  }
+  {
+    ProfScope ps(h, FDL_PROF_SCORE);
+    st = hip_status(h, fdl::launch_score_tokens(h->stream, g, q, pred_mask, k_cache, page_table, lg, cand_idx,
+                                                n_cand, scores, h->status),
+                    "score_tokens launch");
+    if (st != FDL_OK) return st;
+  }
+  return run_select(h, g, scores, n_units, lg, nullptr, nullptr, 0, cand_idx, n_cand, top_k, 1, max_sel, sel_idx,
+                    n_sel);
+}
+
 static fdl_status attn_common(fdl_handle h, const fdl_geom* gp, const void* q, const void* k_cache,
                               const void* v_cache, const void* k_dec, const void* v_dec,
                               const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,

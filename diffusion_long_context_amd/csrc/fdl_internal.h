@@ -111,6 +111,15 @@ hipError_t launch_sinks(hipStream_t s, const Geom& g, const void* q, const uint6
                         int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
                         char* sink_area);
 
+// Level 2 in one kernel (tokens.hip): launch_score_tokens + launch_select with force_first, same
+// outputs.  score_select_tokens_ok: the shapes it takes (bf16, dec_len <= 32, units of 256 to 4096
+// tokens, pages of at least 16 tokens).
+bool score_select_tokens_ok(const Geom& g, int unit_log2);
+hipError_t launch_score_select_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                                      const void* k, const int32_t* page_table, int unit_log2,
+                                      const int32_t* cand_idx, int n_cand, int top_k, int max_sel,
+                                      float* scores, int32_t* sel_idx, int32_t* n_sel, uint32_t* status);
+
 hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int n_units,
                          int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,
                          int max_sinks, const int32_t* cand_idx, int n_cand, int top_k,

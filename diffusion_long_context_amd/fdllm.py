@@ -26,7 +26,7 @@ EXPORTED = (
     "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_get_status_bits",
     "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_predict_queries", "fdl_score_blocks",
-    "fdl_select_blocks", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
+    "fdl_select_blocks", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_profile_begin", "fdl_profile_end",
 )
 
@@ -75,6 +75,8 @@ _SIGS = {
                               ctypes.c_float, _I, _P, _P]),
     "fdl_select_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I,
                                _P, _P]),
+    "fdl_score_select_tokens": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P,
+                                     _P]),
     "fdl_sparse_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
     "fdl_dense_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P]),
     "fdl_focus_step": (_I, [_P, ctypes.POINTER(fdl_geom), ctypes.POINTER(fdl_focus_params), _P, _P, _I,
@@ -240,6 +242,18 @@ class Handle:
             _ptr(sink_pos, 4 * B * max_sinks, "sink_pos"), _ptr(n_sinks, 4 * B, "n_sinks"), max_sinks,
             _ptr(cand_idx, 4 * B * Hkv * n_cand, "cand_idx"), n_cand, top_k, 1 if force_first else 0,
             max_sel, _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel")))
+
+    def fdl_score_select_tokens(self, g: Geom, q, pred_mask, k_cache, page_table, unit_tokens: int, cand_idx,
+                                n_cand: int, top_k: int, max_sel: int, scores, sel_idx, n_sel):
+        self.sync_stream()
+        B, Hkv = g.batch, g.n_kv_heads
+        self._check(self.lib.fdl_score_select_tokens(
+            self.h, ctypes.byref(g.c()), _ptr(q, B * g.n_q_heads * g.dec_len * g.head_dim * g.elem, "q"),
+            _ptr(pred_mask, 8 * B, "pred_mask"), _ptr(k_cache, g.kv_elems * g.elem, "k_cache"),
+            _ptr(page_table, 4 * B * g.pages_per_seq if g.paged else None, "page_table"), unit_tokens,
+            _ptr(cand_idx, 4 * B * Hkv * n_cand, "cand_idx"), n_cand, top_k, max_sel,
+            _ptr(scores, 4 * B * Hkv * n_cand * unit_tokens, "scores"), _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"),
+            _ptr(n_sel, 4 * B * Hkv, "n_sel")))
 
     def _attn_ptrs(self, g: Geom, q, k_cache, v_cache, k_dec, v_dec, page_table, out):
         B, D = g.batch, g.head_dim

@@ -182,6 +182,20 @@ fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* g, const float* score
                              int32_t top_k, int32_t force_first, int32_t max_sel, int32_t* sel_idx,
                              int32_t* n_sel);
 
+/* [PA] level 2 in one call: fdl_score_blocks at level 2 (token scores inside the n_cand candidate
+ * units, written to scores [B][Hkv][n_cand][unit_tokens]) followed by fdl_select_blocks at level 2
+ * with force_first = 1 (each unit's token 0 forced, plus the top `top_k` of its other tokens) --
+ * the same scores, sel_idx [B][Hkv][max_sel] and n_sel [B][Hkv], bit for bit.  For bf16, dec_len <=
+ * 32, units of 256 to 4096 tokens and pages of at least 16 tokens it runs as one kernel (scores and
+ * selection without a round trip through memory); otherwise as the two calls.  Requirements are
+ * those of the two calls: L % unit_tokens == 0, n_cand in [1, n_units], top_k <= unit_tokens - 1,
+ * max_sel >= n_cand * (1 + top_k).  Out-of-range candidate units and page ids latch FDL_EINDEX (the
+ * unit's selection is then -1s). */
+fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* g, const void* q, const uint64_t* pred_mask,
+                                   const void* k_cache, const int32_t* page_table, int32_t unit_tokens,
+                                   const int32_t* cand_idx, int32_t n_cand, int32_t top_k, int32_t max_sel,
+                                   float* scores, int32_t* sel_idx, int32_t* n_sel);
+
 /* ---- step 4: sparse bidirectional attention over the selected KV ---------------------------- */
 
 /* [FA], [FS]: bidirectional attention of the current block's queries over only the selected KV;

@@ -47,6 +47,8 @@ def test_null_handle_is_einval(lib):
                                 0.03, 64, None, None) == FDL_EINVAL
     assert lib.fdl_select_blocks(None, None, None, 0, 64, None, None, 0, None, 0, 4, 0, 4, None,
                                  None) == FDL_EINVAL
+    assert lib.fdl_score_select_tokens(None, None, None, None, None, None, 2048, None, 4, 512, 2052, None, None,
+                                       None) == FDL_EINVAL
     assert lib.fdl_sparse_attn(None, None, None, None, None, None, None, None, None, None, 1, 64,
                                None) == FDL_EINVAL
     assert lib.fdl_dense_attn(None, None, None, None, None, None, None, None, None) == FDL_EINVAL

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_close, dev, out_buffer, out_to_f64, require_gpu
+from gpu_util import assert_close, dev, host, out_buffer, out_to_f64, require_gpu
 from layer_util import _check_chunked, _check_layer, _chunked, _focus
 from oracle.attention import attend
 from oracle.pipeline import chunked_layer_step, focus_layer_step
@@ -71,6 +71,33 @@ def test_chunked_page_order_bitwise_invariant(h):
     b = _chunked(h, cfg, y)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(n_q_heads=8, n_kv_heads=2), dict(chunk_tokens=256, page_tokens=16),
+                                dict(chunk_tokens=1024, head_dim=64)],
+                         ids=["mha", "gqa4", "chunk256-page16", "chunk1024-d64"])
+def test_level2_one_call_equals_two_calls(h, kw):
+    """fdl_score_select_tokens (one kernel) against fdl_score_blocks + fdl_select_blocks at level 2:
+    token scores, selections and counts bit for bit."""
+    from diffusion_long_context_amd.step import ChunkedStep, ChunkParams, geom_for
+    cfg = get_config(4).with_(**dict(dict(batch=2, n_q_heads=4, n_kv_heads=4, ctx_len=4096, chunk_tokens=512), **kw))
+    x = make_single(cfg)
+    g = geom_for(cfg)
+    res = []
+    for separate in (False, True):
+        cs_ = ChunkedStep(h, g, ChunkParams(cfg.top_k_pos, cfg.window, cfg.chunk_tokens, cfg.top_k_chunks,
+                                            cfg.tokens_per_chunk_kept))
+        t = {k: dev(x[k]) for k in ("q", "k_pool", "page_table", "masked", "prev_conf")}
+        cs_.predict(t["prev_conf"], t["masked"])
+        cs = cs_.new_chunk_sums()
+        cs_.pool(t["k_pool"], t["page_table"], cs)
+        cs_.select(t["q"], t["k_pool"], t["page_table"], cs, separate=separate)
+        torch.cuda.synchronize()
+        assert h.fdl_get_status() == 0
+        res.append([host(v) for v in (cs_.token_scores, cs_.tokens, cs_.n_tokens)])
+    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
+    assert np.array_equal(res[0][1], res[1][1])
+    assert np.array_equal(res[0][2], res[1][2])
 
 
 def test_chunked_grouped_query(h):
