@@ -70,6 +70,7 @@ constexpr int kMhaWaves = 8;
 constexpr int kMaxSplits = 32;   // workgroups per head (the final merge keeps their weights in LDS)
 constexpr int kTileTok = 32;
 constexpr float kRescaleSlack = 8.f;   // log2 headroom of the lazily rescaled softmax weights
+constexpr int kPageTableLds = 2048;    // page entries per sequence kept in LDS (paged caches)
 
 template <int D>
 struct MhaShape {
@@ -449,7 +450,8 @@ template <int D, bool DENSE, bool PAGED, bool MAYBE_OWN = true, int POL = kStrea
 __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<PAGED>& rows, int b, int h,
                                               int e, int n_list, const TilePrep<D>& tp, uint16_t* slot,
                                               int lane, bool& bad, bool contig,
-                                              const uint32_t (&voff)[MhaShape<D>::INSTR]) {
+                                              const uint32_t (&voff)[MhaShape<D>::INSTR],
+                                              const int32_t* spt = nullptr) {
   using S = MhaShape<D>;
   constexpr int NI = S::INSTR;
   const int rsub = lane / S::PROW;
@@ -519,10 +521,21 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
       kb = p.k;
       vb = p.v;
       bool pb[NI];
+      if (spt != nullptr) {   // uniform: the sequence's page table sits in LDS
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        pb[j] = false;
-        off[j] = rows.off(b, h, t[j], pb[j]);
+        for (int j = 0; j < NI; ++j) {
+          const int pp = spt[t[j] >> p.page_log2];
+          const bool good = (unsigned)pp < (unsigned)p.n_pages;
+          pb[j] = !good;
+          const int64_t pg = good ? pp : 0;
+          off[j] = (((pg * p.Hkv + h) << p.page_log2) | (int64_t)(t[j] & ((1 << p.page_log2) - 1))) * D;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          pb[j] = false;
+          off[j] = rows.off(b, h, t[j], pb[j]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
@@ -608,6 +621,18 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   rows.n_pages = p.n_pages;
   rows.page_table = p.page_table;
   bool bad = false;
+  // Paged caches: the sequence's page-table entries are copied to LDS once, so that a tile's row
+  // addresses need no dependent global load.
+  __shared__ int32_t s_pt[PAGED ? kPageTableLds : 1];
+  const int32_t* spt = nullptr;
+  if constexpr (PAGED) {
+    if (p.pages_per_seq <= kPageTableLds) {   // uniform
+      for (int i = tid; i < p.pages_per_seq; i += kMhaWaves * 64)
+        s_pt[i] = p.page_table[(int64_t)b * p.pages_per_seq + i];
+      __syncthreads();
+      spt = s_pt;
+    }
+  }
 
   const int32_t* sel_row = DENSE ? nullptr : p.sel_idx + kvseg * p.max_sel;
   uint16_t* slot = lds + wave * S::SLOT;
@@ -705,7 +730,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   bool fresh = true;   // no tile accumulated yet (uniform)
 
   if (!issued && e < e1)
-    vm_next = mha_issue<D, DENSE, PAGED, true, POL>(p, rows, b, h, e, n_list, tp, slot, lane, bad, contig, voff);
+    vm_next = mha_issue<D, DENSE, PAGED, true, POL>(p, rows, b, h, e, n_list, tp, slot, lane, bad, contig, voff, spt);
   const int swz_k = swz(ql) & (PROW - 1);
   for (int en; e < e1; e = en) {
     // This tile's LDS fetches must have landed before the slot is read.  Explicit, because the
@@ -759,7 +784,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     }
     wait_lgkm0();
     // ---- fetch the next tile into the same slot; it flies while this one is finished ----
-    if (more) vm_next = mha_issue<D, DENSE, PAGED, false, POL>(p, rows, b, h, en, n_list, tp, slot, lane, bad, contig, voff);
+    if (more) vm_next = mha_issue<D, DENSE, PAGED, false, POL>(p, rows, b, h, en, n_list, tp, slot, lane, bad, contig, voff, spt);
     float mx = -__builtin_inff();
     if (vm == 0xFFFFFFFFu) {   // uniform: every row of the tile is valid
 #pragma unroll
