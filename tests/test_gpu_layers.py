@@ -133,8 +133,10 @@ def test_dense_attention_paged(h, kw):
     dict(ctx_len=41000, top_k_blocks=48),                 # 641 blocks: the radix selection path
     dict(ctx_len=6000, top_k_blocks=40, spin_limit=0),    # splits never wait: redundant scoring
     dict(ctx_len=6000, top_k_blocks=40, n_kv_heads=2, spin_limit=0),   # the same, grouped-query
+    dict(ctx_len=5000, top_k_blocks=24, n_kv_heads=1, head_dim=64, dec_len=20),   # G = 8, D 64, ragged
+    dict(batch=3, ctx_len=3000, top_k_blocks=16, n_kv_heads=4, kv_block=32),      # G = 2, 32-token blocks
 ], ids=["list-below-topk", "list-above-topk", "scattered-sinks", "gqa4", "one-split", "641-blocks",
-        "no-wait-fallback", "gqa4-no-wait-fallback"])
+        "no-wait-fallback", "gqa4-no-wait-fallback", "gqa8-d64-ragged-T20", "gqa2-b3-bt32"])
 def test_focus_step_driver(kw, monkeypatch):
     """fdl_focus_step (one call: predict, then dense / source / reuse / reuse layers) against the
     oracle layer by layer.  The sparse layers run scoring, selection and attention as one fused
