@@ -48,35 +48,62 @@ __device__ __forceinline__ float2 add2(float2 a, float2 b) { return make_float2(
 constexpr int ilog2_const(int x) { return x <= 1 ? 0 : 1 + ilog2_const(x / 2); }
 
 // Adjacent-pair tree over LEAVES consecutive tokens starting at t0 (tokens >= L are +0).  Every
-// load is issued before the first add.
-template <typename KT, int LEAVES, bool PAGED>
+// load is issued before the first add.  A full, aligned run of rows that lies in one page (or in a
+// contiguous cache) is addressed from one base with compile-time strides, which keeps the loads'
+// address registers few (and the waves per SIMD many).
+template <typename KT, int D, int LEAVES, bool PAGED>
 __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRows<PAGED>& rows, int b,
                                             int g, int t0, int pair, bool& bad) {
-  float2 a[LEAVES];
-  int64_t off[LEAVES];
-  if (PAGED && (t0 & (LEAVES - 1)) == 0 && rows.page_log2 >= ilog2_const(LEAVES) && t0 + LEAVES <= rows.L) {
-    // uniform: the run lies in one page, so one table lookup gives every row
-    const int64_t base = rows.off(b, g, t0, bad);
+  // bf16 leaves stay packed (one register per leaf) until the first tree level converts them
+  constexpr bool kPacked = std::is_same<KT, uint16_t>::value && LEAVES >= 2;
+  using Leaf = typename std::conditional<kPacked, uint32_t, float2>::type;
+  auto load_leaf = [&](const KT* p) -> Leaf {
+    if constexpr (kPacked) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    else return load_pair<KT>(p);
+  };
+  Leaf a[LEAVES];
+  const bool run = (t0 & (LEAVES - 1)) == 0 && t0 + LEAVES <= rows.L &&
+                   (!PAGED || rows.page_log2 >= ilog2_const(LEAVES));
+  if (run) {   // uniform per team
+    const KT* base = k + rows.off(b, g, t0, bad) + 2 * pair;
 #pragma unroll
-    for (int i = 0; i < LEAVES; ++i) off[i] = base + (int64_t)i * rows.D;
+    for (int i = 0; i < LEAVES; ++i) a[i] = load_leaf(base + i * D);
   } else {
 #pragma unroll
     for (int i = 0; i < LEAVES; ++i) {
       const int t = t0 + i;
-      off[i] = rows.off(b, g, t < rows.L ? t : rows.L - 1, bad);
+      a[i] = load_leaf(k + rows.off(b, g, t < rows.L ? t : rows.L - 1, bad) + 2 * pair);
     }
   }
+  const int live = rows.L - t0;   // leaves at or past it are +0
+  if constexpr (kPacked) {
+    float2 s[LEAVES / 2];
 #pragma unroll
-  for (int i = 0; i < LEAVES; ++i) a[i] = load_pair<KT>(k + off[i] + 2 * pair);
+    for (int i = 0; i < LEAVES / 2; ++i) {
+      const uint32_t w0 = a[2 * i], w1 = a[2 * i + 1];
+      const float2 x0 = 2 * i < live ? make_float2(bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16))
+                                     : make_float2(0.f, 0.f);
+      const float2 x1 = 2 * i + 1 < live ? make_float2(bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16))
+                                         : make_float2(0.f, 0.f);
+      s[i] = add2(x0, x1);
+    }
 #pragma unroll
-  for (int i = 0; i < LEAVES; ++i)
-    if (t0 + i >= rows.L) a[i] = make_float2(0.f, 0.f);
+    for (int w = LEAVES / 4; w >= 1; w /= 2) {
 #pragma unroll
-  for (int w = LEAVES / 2; w >= 1; w /= 2) {
+      for (int i = 0; i < w; ++i) s[i] = add2(s[2 * i], s[2 * i + 1]);
+    }
+    return s[0];
+  } else {
 #pragma unroll
-    for (int i = 0; i < w; ++i) a[i] = add2(a[2 * i], a[2 * i + 1]);
+    for (int i = 0; i < LEAVES; ++i)
+      if (i >= live) a[i] = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int w = LEAVES / 2; w >= 1; w /= 2) {
+#pragma unroll
+      for (int i = 0; i < w; ++i) a[i] = add2(a[2 * i], a[2 * i + 1]);
+    }
+    return a[0];
   }
-  return a[0];
 }
 
 // Second pass of the pooling of units longer than 64 tokens: ks[b][g][n] = adjacent-pair tree over
@@ -123,7 +150,9 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const KT* __restrict__ k
   extern __shared__ float2 sub_sums[];  // [teams][n_sub][D/2], only when unit > LEAVES
   constexpr int kTeam = D / 2;
   constexpr int kTeams = 256 / kTeam;
-  const int team = threadIdx.x / kTeam;
+  // a team of 64 threads is one wave: its unit, rows and page entries are then uniform (scalar
+  // registers and scalar loads), and the loads' only per-lane address part is the column pair
+  const int team = kTeam == 64 ? __builtin_amdgcn_readfirstlane(threadIdx.x / kTeam) : threadIdx.x / kTeam;
   const int pair = threadIdx.x % kTeam;
   const int g = blockIdx.y, b = blockIdx.z;
   const int n_raw = blockIdx.x * kTeams + team;
@@ -134,12 +163,12 @@ __global__ __launch_bounds__(256) void pool_keys_kernel(const KT* __restrict__ k
   bool bad = false;
   float2 r;
   if (unit <= LEAVES) {
-    r = leaf_tree<KT, LEAVES, PAGED>(k, rows, b, g, t_unit, pair, bad);
+    r = leaf_tree<KT, D, LEAVES, PAGED>(k, rows, b, g, t_unit, pair, bad);
   } else {
     const int n_sub = unit / LEAVES;
     float2* mine = sub_sums + (size_t)team * n_sub * kTeam;
     for (int sb = 0; sb < n_sub; ++sb)
-      mine[sb * kTeam + pair] = leaf_tree<KT, LEAVES, PAGED>(k, rows, b, g, t_unit + sb * LEAVES, pair, bad);
+      mine[sb * kTeam + pair] = leaf_tree<KT, D, LEAVES, PAGED>(k, rows, b, g, t_unit + sb * LEAVES, pair, bad);
     // tree over the sub-unit sums; each thread only touches its own column, so no barrier
     for (int w = n_sub / 2; w >= 1; w /= 2)
       for (int i = 0; i < w; ++i)
