@@ -338,6 +338,34 @@ fdl_status fdl_pool_keys(fdl_handle h, const fdl_geom* gp, const void* k_cache,
                     "pool_keys launch");
 }
 
+fdl_status fdl_cache_write(fdl_handle h, const fdl_geom* gp, const void* k_new, const void* v_new, int32_t t0,
+                           int32_t n_tok, void* k_cache, void* v_cache, const int32_t* page_table,
+                           int32_t unit_tokens, float* ks) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!k_new || !v_new || !k_cache || !v_cache)
+    return fail(h, FDL_EINVAL, "k_new, v_new, k_cache and v_cache must be non-NULL");
+  if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
+  if (t0 < 0 || n_tok < 1 || (long long)t0 + n_tok > g.L)
+    return fail(h, FDL_EINVAL, "the rows [t0, t0 + n_tok) must lie in [0, ctx_len) and be non-empty");
+  int lg = 6;
+  if (ks) {
+    if (!is_pow2(unit_tokens) || unit_tokens < 16 || unit_tokens > 4096)
+      return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [16, 4096]");
+    lg = ilog2(unit_tokens);
+    if (unit_tokens > 64 &&
+        (size_t)g.B * g.Hkv * ((g.L + 63) / 64) * g.D * sizeof(float) > h->scratch_bytes)
+      return fail(h, FDL_ENOMEM, "workspace too small for the sub-unit sums");
+  }
+  ProfScope ps(h, FDL_PROF_POOL);
+  return hip_status(h, fdl::launch_cache_write(h->stream, g, k_new, v_new, t0, n_tok, k_cache, v_cache, page_table,
+                                               lg, ks, h->status, reinterpret_cast<float*>(h->scratch),
+                                               h->scratch_bytes),
+                    "cache_write launch");
+}
+
 fdl_status fdl_predict_queries(fdl_handle h, int32_t batch, int32_t dec_len, const float* prev_conf,
                                const uint8_t* masked, int32_t top_k, int32_t window,
                                uint64_t* pred_mask, int32_t* n_pred) {

@@ -86,6 +86,13 @@ struct Geom {
   int paged, page_tokens, page_log2, pps, n_pages;
 };
 
+// Cache write of rows [t0, t0 + n_tok) (K and V) with, when ks != NULL, the pooling of the units
+// the write touches (units of 2^unit_log2 >= 16 tokens; longer than 64 tokens through the sub-sum
+// scratch `sub`).
+hipError_t launch_cache_write(hipStream_t s, const Geom& g, const void* k_new, const void* v_new, int t0, int n_tok,
+                              void* k, void* v, const int32_t* page_table, int unit_log2, float* ks, uint32_t* status,
+                              float* sub, size_t sub_bytes);
+
 hipError_t launch_predict(hipStream_t s, int batch, int T, const float* prev_conf,
                           const uint8_t* masked, int top_k, int window, uint64_t* pred_mask,
                           int32_t* n_pred);

@@ -110,15 +110,17 @@ __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRo
 // the unit's n_sub sub-unit sums sub[b][g][n * n_sub + i] (each the tree over 64 tokens; indices past
 // n_sub_all are +0).  The tree over a power-of-two unit is the tree over its aligned 64-token
 // sub-trees, so the bits are those of the one-pass tree.  Thread (unit, dimension pair).
+// Units [n0, n0 + n_cnt) of the n_units.
 template <int D>
 __global__ __launch_bounds__(256) void pool_merge_kernel(const float* __restrict__ sub, int n_sub, int n_sub_all,
-                                                         int n_units, int Hkv, float* __restrict__ ks) {
+                                                         int n0, int n_cnt, int n_units, int Hkv,
+                                                         float* __restrict__ ks) {
   constexpr int kTeam = D / 2;
   constexpr int kTeams = 256 / kTeam;
   const int team = threadIdx.x / kTeam, pair = threadIdx.x % kTeam;
-  const int n = blockIdx.x * kTeams + team;
+  const int n = n0 + blockIdx.x * kTeams + team;
   const int g = blockIdx.y, b = blockIdx.z;
-  if (n >= n_units) return;
+  if (n >= n0 + n_cnt) return;
   const float* src = sub + ((int64_t)b * Hkv + g) * n_sub_all * D + 2 * pair;
   float2 a[64];
   // every load unconditional (clamped index), masked afterwards: a guarded load would be waited for
@@ -212,7 +214,8 @@ static hipError_t pool_dispatch(hipStream_t s, const Geom& g, const KT* k, const
     hipLaunchKernelGGL((pool_keys_kernel<KT, D, 64, PAGED>), g1, dim3(256), 0, s, k, rows, 6, n_sub_all, sub,
                        status);
     dim3 g2((n_units + kTeams - 1) / kTeams, g.Hkv, g.B);
-    hipLaunchKernelGGL((pool_merge_kernel<D>), g2, dim3(256), 0, s, sub, unit / 64, n_sub_all, n_units, g.Hkv, ks);
+    hipLaunchKernelGGL((pool_merge_kernel<D>), g2, dim3(256), 0, s, sub, unit / 64, n_sub_all, 0, n_units, n_units,
+                       g.Hkv, ks);
     return hipGetLastError();
   }
   dim3 grid((n_units + kTeams - 1) / kTeams, g.Hkv, g.B);
@@ -256,6 +259,158 @@ hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const i
                       : pool_dispatch<float, 64, true>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes);
   return g.D == 128 ? pool_dispatch<float, 128, false>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes)
                     : pool_dispatch<float, 64, false>(s, g, kk, page_table, unit_log2, ks, status, sub, sub_bytes);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Cache write with the pooling of the units it touches: the new rows [t0, t0 + n_tok) of every
+// (sequence, KV head) go to the cache (contiguous or paged), and each touched unit's keys are pooled
+// from the rows it then holds -- the new rows straight from the registers they were loaded into, so
+// the written keys are read once instead of written and read back by a separate pooling.
+// ------------------------------------------------------------------------------------------------
+
+struct CacheWrite {
+  const void* k_new;   // [B][Hkv][n_tok][D]
+  const void* v_new;
+  void* k;             // cache: [B][Hkv][L][D], or the page pool [n_pages][Hkv][P][D]
+  void* v;
+  int t0, n_tok;
+};
+
+template <typename KT>
+struct PairOf {
+  using T = float2;
+};
+template <>
+struct PairOf<uint16_t> {
+  using T = uint32_t;   // two bf16 kept packed
+};
+
+// One team of D/2 threads per run of RUN tokens (RUN = min(unit, 64)) of the touched units; thread
+// `pair` owns dimensions 2 pair, 2 pair + 1.  Every row of the run is read from the new rows when it
+// is written, else from the cache (rows past L read a valid row and count +0); the written rows of K
+// and V are stored to the cache; with pooling, the run's adjacent-pair tree goes to out[b][g][run]
+// (the pooled keys when the unit is the run, else the sub-sums of the two-pass pooling).
+template <typename KT, int D, int RUN, bool PAGED>
+__global__ __launch_bounds__(256) void cache_write_pool_kernel(CacheWrite w, KvRows<PAGED> rows, int run0,
+                                                               int n_runs, int out_units, float* __restrict__ out,
+                                                               uint32_t* __restrict__ status) {
+  using PT = typename PairOf<KT>::T;
+  constexpr int kTeam = D / 2;
+  constexpr int kTeams = 256 / kTeam;
+  const int team = kTeam == 64 ? __builtin_amdgcn_readfirstlane(threadIdx.x / kTeam) : threadIdx.x / kTeam;
+  const int pair = threadIdx.x % kTeam;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int run = run0 + blockIdx.x * kTeams + team;
+  if (run >= run0 + n_runs) return;
+  const int t_run = run * RUN;
+  const int64_t seg = (int64_t)b * rows.Hkv + g;
+  const KT* kn = static_cast<const KT*>(w.k_new) + seg * w.n_tok * D + 2 * pair;
+  const KT* vn = static_cast<const KT*>(w.v_new) + seg * w.n_tok * D + 2 * pair;
+  KT* kc = static_cast<KT*>(w.k);
+  KT* vc = static_cast<KT*>(w.v);
+  bool bad = false;
+  PT ka[RUN], va[RUN];
+  // every load unconditional: the source is chosen by address (a guarded load would be waited for on
+  // its own); a row's cache offset is uniform per team and recomputed for the stores rather than kept
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    const int t = t_run + i;
+    const bool in = t >= w.t0 && t < w.t0 + w.n_tok;   // uniform per team
+    const int64_t coff = rows.off(b, g, t < rows.L ? t : rows.L - 1, bad);
+    const int64_t noff = (int64_t)(in ? t - w.t0 : 0) * D;
+    ka[i] = *reinterpret_cast<const PT*>(in ? kn + noff : kc + coff + 2 * pair);
+    va[i] = *reinterpret_cast<const PT*>(in ? vn + noff : vc + coff + 2 * pair);
+  }
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    const int t = t_run + i;
+    if (t >= w.t0 && t < w.t0 + w.n_tok) {   // uniform per team
+      bool unused = false;
+      const int64_t coff = rows.off(b, g, t, unused) + 2 * pair;
+      *reinterpret_cast<PT*>(kc + coff) = ka[i];
+      *reinterpret_cast<PT*>(vc + coff) = va[i];
+    }
+  }
+  latch_bad(status, bad);
+  if (out == nullptr) return;
+  float2 x[RUN];
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    if constexpr (std::is_same<KT, uint16_t>::value)
+      x[i] = make_float2(bf16_bits_to_f32(ka[i] & 0xFFFFu), bf16_bits_to_f32(ka[i] >> 16));
+    else
+      x[i] = ka[i];
+    if (t_run + i >= rows.L) x[i] = make_float2(0.f, 0.f);
+  }
+#pragma unroll
+  for (int wdt = RUN / 2; wdt >= 1; wdt /= 2) {
+#pragma unroll
+    for (int i = 0; i < wdt; ++i) x[i] = add2(x[2 * i], x[2 * i + 1]);
+  }
+  *reinterpret_cast<float2*>(out + (seg * out_units + run) * D + 2 * pair) = x[0];
+}
+
+template <typename KT, int D, bool PAGED>
+static hipError_t cache_write_dispatch(hipStream_t s, const Geom& g, const CacheWrite& w, const int32_t* page_table,
+                                       int unit_log2, float* ks, uint32_t* status, float* sub, size_t sub_bytes) {
+  const KvRows<PAGED> rows = make_rows<PAGED>(g, page_table);
+  constexpr int kTeams = 256 / (D / 2);
+  const int unit = 1 << unit_log2;
+  const int run_tok = ks == nullptr ? 64 : (unit < 64 ? unit : 64);
+  const int n_runs_all = (g.L + run_tok - 1) / run_tok;
+  int r0, r1;   // runs [r0, r1)
+  int u0 = 0, u1 = 0;
+  if (ks == nullptr) {
+    r0 = w.t0 / run_tok;
+    r1 = (w.t0 + w.n_tok - 1) / run_tok + 1;
+  } else {
+    u0 = w.t0 >> unit_log2;
+    u1 = ((w.t0 + w.n_tok - 1) >> unit_log2) + 1;
+    r0 = (int)(((int64_t)u0 << unit_log2) / run_tok);
+    r1 = (int)(((int64_t)u1 << unit_log2) / run_tok);
+    if (r1 > n_runs_all) r1 = n_runs_all;
+  }
+  float* out = ks;
+  int out_units = (g.L + unit - 1) / unit;
+  if (ks != nullptr && unit > 64) {
+    if (unit / 64 > 64 || sub == nullptr || (size_t)g.B * g.Hkv * n_runs_all * D * sizeof(float) > sub_bytes)
+      return hipErrorOutOfMemory;
+    out = sub;
+    out_units = n_runs_all;
+  }
+  if (run_tok != 16 && run_tok != 32 && run_tok != 64) return hipErrorInvalidValue;
+  const dim3 grid((r1 - r0 + kTeams - 1) / kTeams, g.Hkv, g.B);
+  switch (run_tok) {
+    case 16: hipLaunchKernelGGL((cache_write_pool_kernel<KT, D, 16, PAGED>), grid, dim3(256), 0, s, w, rows, r0, r1 - r0,
+                                out_units, out, status); break;
+    case 32: hipLaunchKernelGGL((cache_write_pool_kernel<KT, D, 32, PAGED>), grid, dim3(256), 0, s, w, rows, r0, r1 - r0,
+                                out_units, out, status); break;
+    default: hipLaunchKernelGGL((cache_write_pool_kernel<KT, D, 64, PAGED>), grid, dim3(256), 0, s, w, rows, r0, r1 - r0,
+                                out_units, out, status);
+  }
+  if (ks == nullptr || unit <= 64) return hipGetLastError();
+  const dim3 g2((u1 - u0 + kTeams - 1) / kTeams, g.Hkv, g.B);
+  hipLaunchKernelGGL((pool_merge_kernel<D>), g2, dim3(256), 0, s, sub, unit / 64, n_runs_all, u0, u1 - u0,
+                     (g.L + unit - 1) / unit, g.Hkv, ks);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write(hipStream_t s, const Geom& g, const void* k_new, const void* v_new, int t0, int n_tok,
+                              void* k, void* v, const int32_t* page_table, int unit_log2, float* ks, uint32_t* status,
+                              float* sub, size_t sub_bytes) {
+  const CacheWrite w{k_new, v_new, k, v, t0, n_tok};
+  if (g.dtype == FDL_BF16) {
+    if (g.paged)
+      return g.D == 128 ? cache_write_dispatch<uint16_t, 128, true>(s, g, w, page_table, unit_log2, ks, status, sub, sub_bytes)
+                        : cache_write_dispatch<uint16_t, 64, true>(s, g, w, page_table, unit_log2, ks, status, sub, sub_bytes);
+    return g.D == 128 ? cache_write_dispatch<uint16_t, 128, false>(s, g, w, page_table, unit_log2, ks, status, sub, sub_bytes)
+                      : cache_write_dispatch<uint16_t, 64, false>(s, g, w, page_table, unit_log2, ks, status, sub, sub_bytes);
+  }
+  if (g.paged)
+    return g.D == 128 ? cache_write_dispatch<float, 128, true>(s, g, w, page_table, unit_log2, ks, status, sub, sub_bytes)
+                      : cache_write_dispatch<float, 64, true>(s, g, w, page_table, unit_log2, ks, status, sub, sub_bytes);
+  return g.D == 128 ? cache_write_dispatch<float, 128, false>(s, g, w, page_table, unit_log2, ks, status, sub, sub_bytes)
+                    : cache_write_dispatch<float, 64, false>(s, g, w, page_table, unit_log2, ks, status, sub, sub_bytes);
 }
 
 // ------------------------------------------------------------------------------------------------

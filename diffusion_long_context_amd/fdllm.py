@@ -25,7 +25,7 @@ FDL_F32, FDL_BF16 = 0, 1
 EXPORTED = (
     "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_get_status_bits",
     "fdl_status_string",
-    "fdl_last_error", "fdl_pool_keys", "fdl_predict_queries", "fdl_score_blocks",
+    "fdl_last_error", "fdl_pool_keys", "fdl_cache_write", "fdl_predict_queries", "fdl_score_blocks",
     "fdl_select_blocks", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_profile_begin", "fdl_profile_end",
 )
@@ -70,6 +70,7 @@ _SIGS = {
     "fdl_status_string": (ctypes.c_char_p, [_I]),
     "fdl_last_error": (ctypes.c_char_p, [_P]),
     "fdl_pool_keys": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _I, _P]),
+    "fdl_cache_write": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _I, _I, _P, _P, _P, _I, _P]),
     "fdl_predict_queries": (_I, [_P, _I, _I, _P, _P, _I, _I, _P, _P]),
     "fdl_score_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _I,
                               ctypes.c_float, _I, _P, _P]),
@@ -203,6 +204,21 @@ class Handle:
             self.h, ctypes.byref(g.c()), _ptr(k_cache, g.kv_elems * g.elem, "k_cache"),
             _ptr(page_table, 4 * g.batch * g.pages_per_seq if g.paged else None, "page_table"),
             unit_tokens, _ptr(ks, 4 * g.batch * g.n_kv_heads * n_units * g.head_dim, "ks")))
+
+    def fdl_cache_write(self, g: Geom, k_new, v_new, t0: int, k_cache, v_cache, page_table, unit_tokens: int,
+                        ks=None):
+        """Write rows [t0, t0 + n_tok) of k_new / v_new [B][Hkv][n_tok][D] into the cache and, with ks,
+        re-pool the units they touch."""
+        self.sync_stream()
+        B, Hkv, D = g.batch, g.n_kv_heads, g.head_dim
+        n_tok = k_new.shape[2]
+        nbytes = B * Hkv * n_tok * D * g.elem
+        n_units = -(-g.ctx_len // unit_tokens)
+        self._check(self.lib.fdl_cache_write(
+            self.h, ctypes.byref(g.c()), _ptr(k_new, nbytes, "k_new"), _ptr(v_new, nbytes, "v_new"), t0, n_tok,
+            _ptr(k_cache, g.kv_elems * g.elem, "k_cache"), _ptr(v_cache, g.kv_elems * g.elem, "v_cache"),
+            _ptr(page_table, 4 * B * g.pages_per_seq if g.paged else None, "page_table"), unit_tokens,
+            _ptr(ks, 4 * B * Hkv * n_units * D, "ks") if ks is not None else None))
 
     def fdl_predict_queries(self, batch: int, dec_len: int, prev_conf, masked, top_k: int, window: int,
                             pred_mask, n_pred):

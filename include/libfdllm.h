@@ -116,6 +116,21 @@ const char* fdl_last_error(fdl_handle h);
 fdl_status fdl_pool_keys(fdl_handle h, const fdl_geom* g, const void* k_cache,
                          const int32_t* page_table, int32_t unit_tokens, float* ks);
 
+/* Cache side, written and pooled in one pass (no rereading of the written keys).  [FA] the context
+ * cache is built once and reused, and the block scoring ranks units by their pooled keys; [PA] the
+ * cache may be paged.  Reading: the write replaces the logical rows [t0, t0 + n_tok) of every
+ * (sequence, KV head) with k_new / v_new [B][Hkv][n_tok][D] (g->dtype), bit for bit, in the
+ * contiguous cache [B][Hkv][L][D] or, when g->paged, in the page pool through page_table; when ks
+ * is not NULL, every unit of unit_tokens tokens that holds a written row gets the pooled key of the
+ * updated cache (the same tree as fdl_pool_keys), and the other units of ks [B][Hkv][n_units][D] are
+ * left as they are.  Requires 0 <= t0, n_tok >= 1, t0 + n_tok <= L and, with ks, unit_tokens a power
+ * of two in [16, 4096]; units longer than 64 tokens use workspace scratch (B * Hkv * ceil(L / 64) * D
+ * floats; FDL_ENOMEM if the workspace is smaller).  Page ids outside [0, n_pages) latch FDL_EINDEX
+ * (the rows are then written to page 0). */
+fdl_status fdl_cache_write(fdl_handle h, const fdl_geom* g, const void* k_new, const void* v_new, int32_t t0,
+                           int32_t n_tok, void* k_cache, void* v_cache, const int32_t* page_table,
+                           int32_t unit_tokens, float* ks);
+
 /* ---- step 1: past-confidence-guided query prediction ----------------------------------------- */
 
 /* [FA], [FS], [FK]: the previous step's confidence predicts the next positions to be unmasked; the

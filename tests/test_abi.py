@@ -43,6 +43,7 @@ def test_null_handle_is_einval(lib):
     assert lib.fdl_set_stream(None, None) == FDL_EINVAL
     assert lib.fdl_predict_queries(None, 1, 32, None, None, 4, 4, None, None) == FDL_EINVAL
     assert lib.fdl_pool_keys(None, None, None, None, 64, None) == FDL_EINVAL
+    assert lib.fdl_cache_write(None, None, None, None, 0, 1, None, None, None, 64, None) == FDL_EINVAL
     assert lib.fdl_score_blocks(None, None, None, None, None, 64, None, 0, None, None, None, None, 0,
                                 0.03, 64, None, None) == FDL_EINVAL
     assert lib.fdl_select_blocks(None, None, None, 0, 64, None, None, 0, None, 0, 4, 0, 4, None,
