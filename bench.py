@@ -234,6 +234,31 @@ def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
         "kv_tokens_per_s": B * L / (t_step * 1e-6), "step_bytes": step_bytes,
         "GBps": step_bytes / (t_step * 1e-6) / 1e9, "frac_of_peak": step_bytes / (t_step * 1e-6) / 1e9 / PEAK_HBM_GBS,
         "tokens_per_kv_head": n_tok / (B * Hkv)}
+    del kp, vp, q, kd, vd, o
+    # cache side: a full refresh of one 32K layer's cache (new K and V written, keys re-pooled per
+    # 64-token block) in one pass, against copying K and V and pooling the cache afterwards
+    cfg = get_config(3)
+    g = geom_for(cfg)
+    B, Hkv, D, L = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len
+    gen = torch.Generator(device=dev).manual_seed(7003)
+    kn, vn = rn(B, Hkv, L, D), rn(B, Hkv, L, D)
+    kc, vc = torch.empty_like(kn), torch.empty_like(vn)
+    ks = torch.zeros((B, Hkv, cfg.n_blk, D), dtype=torch.float32, device=dev)
+    t_fused = timed(lambda: h.fdl_cache_write(g, kn, vn, 0, kc, vc, None, cfg.kv_block, ks), chunk_runs)
+
+    def unfused():
+        kc.copy_(kn)
+        vc.copy_(vn)
+        h.fdl_pool_keys(g, kc, None, cfg.kv_block, ks)
+
+    t_unfused = timed(unfused, chunk_runs)
+    assert h.fdl_get_status() == 0
+    kv_bytes = B * Hkv * L * D * 2
+    refresh_bytes = 4 * kv_bytes + B * Hkv * cfg.n_blk * D * 4   # read new K, V; write K, V; write ks
+    out["cache_refresh_32k_layer"] = {
+        "fused_us": t_fused, "copy_then_pool_us": t_unfused, "speedup": t_unfused / t_fused,
+        "bytes": refresh_bytes, "GBps": refresh_bytes / (t_fused * 1e-6) / 1e9,
+        "frac_of_peak": refresh_bytes / (t_fused * 1e-6) / 1e9 / PEAK_HBM_GBS}
     return out
 
 
