@@ -80,8 +80,14 @@ struct SinkParams {
 // fetches the next one into the slot while the current one is scored.  The last split of a head to
 // finish (ticket) merges the partial statistics into the exact log-sum-exp per query, re-scores
 // the head's candidates in float32 and sets the survivors in the sequence's bitmap.
-template <int D>
+// Placement: workgroup i runs on XCD i % 8; slot k = xcd + 8 (xslot / NS) and its NS splits share
+// that XCD.  Slots go to q-heads KV-segment-major (k = kv + (B Hkv) j for the j-th head of KV
+// segment kv), so the q-heads of one KV head sit on as few XCDs as there are slots per XCD for them
+// and read the KV head's key tiles through one L2 (default cache policy for grouped-query heads;
+// one reader per tile streams non-temporally).  With one q-head per KV head, k is the head.
+template <int D, bool GQA>
 __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const SinkParams p) {
+  constexpr int POL = GQA ? 0 : kStreamPolicy;
   constexpr int KS = D / 16;
   constexpr int RB = kSinkTile / 32;   // 32-row MFMA blocks per tile
   using RC = RowChunks<D>;
@@ -99,9 +105,12 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   const int NS = p.n_splits;
   const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
   const int s = xslot % NS;
-  const int seg = xcd + 8 * (xslot / NS);
-  if (seg >= p.n_segs) return;
-  const int b = seg / p.Hq, h = seg % p.Hq, g = h / p.G;
+  const int k_slot = xcd + 8 * (xslot / NS);
+  if (k_slot >= p.n_segs) return;
+  const int n_kv = p.n_segs / p.G;   // (sequence, KV head) segments
+  const int kvs = k_slot % n_kv, jh = k_slot / n_kv;
+  const int b = kvs / p.Hkv, g = kvs % p.Hkv, h = g * p.G + jh;
+  const int seg = b * p.Hq + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
   const uint64_t pred = p.pred_mask[b];
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           const void* src = base + voff[j];
-          __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+          __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
         }
         return;
       }
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
         const uint16_t* row = (e == 0) ? kdec + (int64_t)(r < p.T ? r : p.T - 1) * D
                                        : kctx + (int64_t)(t < p.L ? t : p.L - 1) * D;
         const void* src = row + (sc ^ (swz(r) & (PROW - 1))) * 8;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, kStreamPolicy);
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
       }
     };
     const int swz_k = swz(ql) & (PROW - 1);
@@ -629,12 +638,15 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
       hipLaunchKernelGGL((sink_f32_kernel<64>), grid, dim3(64), 0, st, qq, kk, kd, pred_mask,
                          p.bitmap, g.Hq, g.Hkv, g.G, g.T, g.L, words, tau);
   } else if (g.L > 0) {
-    // the splits of head seg run on XCD seg % 8 (see the kernel)
+    // the splits of slot k run on XCD k % 8 (see the kernel)
     dim3 grid(8 * ((p.n_segs + 7) / 8) * n_splits);
-    if (g.D == 128)
-      hipLaunchKernelGGL((sink_scan_kernel<128>), grid, dim3(kSinkWaves * 64), 0, st, p);
-    else
-      hipLaunchKernelGGL((sink_scan_kernel<64>), grid, dim3(kSinkWaves * 64), 0, st, p);
+    if (g.D == 128) {
+      if (g.G > 1) hipLaunchKernelGGL((sink_scan_kernel<128, true>), grid, dim3(kSinkWaves * 64), 0, st, p);
+      else hipLaunchKernelGGL((sink_scan_kernel<128, false>), grid, dim3(kSinkWaves * 64), 0, st, p);
+    } else {
+      if (g.G > 1) hipLaunchKernelGGL((sink_scan_kernel<64, true>), grid, dim3(kSinkWaves * 64), 0, st, p);
+      else hipLaunchKernelGGL((sink_scan_kernel<64, false>), grid, dim3(kSinkWaves * 64), 0, st, p);
+    }
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(sink_compact_kernel, dim3(g.B), dim3(256), 0, st, p.bitmap, words, max_sinks,
