@@ -64,6 +64,30 @@ def unit_scores(qs, ks) -> np.ndarray:
     return tree_dot(np.asarray(qs, np.float32)[:, :, None, :], ks)
 
 
+def unit_scores_max(q, pred_bits, ks, n_kv_heads: int) -> np.ndarray:
+    """Per-query scoring, a reading the pages leave open next to the summed-query one: a unit's score
+    is the largest pinned float32 dot product of one predicted query of the KV head's q-head group
+    with the unit's key sum (a unit that matters to any single predicted position ranks high).  +0
+    when no position is predicted; a -0 result reads +0.  q [B][Hq][T][D], pred_bits [B], ks
+    [B][Hkv][n][D] -> [B][Hkv][n] float32."""
+    qf = values_f32(q)
+    B, Hq, T, D = qf.shape
+    G = Hq // n_kv_heads
+    ks = np.asarray(ks, dtype=np.float32)
+    out = np.zeros((B, n_kv_heads, ks.shape[2]), dtype=np.float32)
+    for b in range(B):
+        P = [p for p in range(T) if (int(pred_bits[b]) >> p) & 1]
+        for g in range(n_kv_heads):
+            best = None
+            for j in range(G):
+                for p in P:
+                    s = tree_dot(qf[b, g * G + j, p][None, :], ks[b, g])
+                    best = s if best is None else np.maximum(best, s)
+            if best is not None:
+                out[b, g] = best + np.float32(0.0)
+    return out
+
+
 def token_scores(qs, k_tokens) -> np.ndarray:
     """qs [B][Hkv][D], k_tokens [B][Hkv][n][D] (bf16 bits or float32) -> [B][Hkv][n] float32."""
     return tree_dot(np.asarray(qs, np.float32)[:, :, None, :], values_f32(k_tokens))
