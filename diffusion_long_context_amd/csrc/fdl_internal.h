@@ -102,6 +102,9 @@ hipError_t launch_predict(hipStream_t s, int batch, int T, const float* prev_con
 hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const int32_t* page_table,
                             int unit_log2, float* ks, uint32_t* status, float* sub, size_t sub_bytes);
 
+// Per-query (max) unit scores, bf16 queries, dec_len <= 32.
+hipError_t launch_score_units_max(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                                  const float* ks, int n_units, float* scores);
 hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                               const float* ks, int n_units, float* scores);
 

@@ -498,6 +498,83 @@ hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const
 }
 
 // ------------------------------------------------------------------------------------------------
+// Per-query (max) unit scores: scores[b][g][n] = max over the group's predicted queries q of the
+// pinned dot(q, ks[b][g][n]) (+0 when nothing is predicted; -0 reads +0).  The group's query rows are
+// staged in LDS once (bf16, one round of 16-byte loads); each lane group keeps its unit rows in
+// registers and runs the row dot of every predicted query against them.
+// ------------------------------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void score_units_max_kernel(const uint16_t* __restrict__ q,
+                                                              const uint64_t* __restrict__ pred_mask,
+                                                              const float* __restrict__ ks, int Hq, int Hkv,
+                                                              int G, int T, int n_units, float* __restrict__ scores) {
+  constexpr int LPR = D / 16;
+  constexpr int kRowsPerWave = 64 / LPR;
+  constexpr int kRowsPerPass = 4 * kRowsPerWave;
+  constexpr int kPasses = kUnitsPerWg / kRowsPerPass;
+  __shared__ __attribute__((aligned(16))) uint16_t stage[8 * 32 * D];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % LPR;
+  const int n0 = blockIdx.x * kUnitsPerWg;
+  const float* ksg = ks + ((int64_t)b * Hkv + g) * n_units * D;
+  float x[kPasses][16];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    n = n < n_units ? n : n_units - 1;
+    load16<float>(ksg + (int64_t)n * D + 16 * j, x[ps]);
+  }
+  QsumGrouped<D, 32, 256, 8> qst;
+  qsum_grouped_issue<D, 32, 256, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
+#pragma unroll
+  for (int k = 0; k < QsumGrouped<D, 32, 256, 8>::PER; ++k)
+    *reinterpret_cast<uint4*>(stage + (k * 256 + threadIdx.x) * 8) = qst.v[k];
+  block_sync_lds();
+  const uint64_t pred = pred_mask[b] & (T >= 64 ? ~0ull : ((1ull << T) - 1ull));
+  float best[kPasses];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) best[ps] = -__builtin_inff();
+  for (int jh = 0; jh < G; ++jh) {
+    for (uint64_t m = pred; m != 0ull; m &= m - 1ull) {   // uniform: the predicted positions
+      const int pp = __builtin_ctzll(m);
+      const uint4* src = reinterpret_cast<const uint4*>(stage + (jh * 32 + pp) * D + 16 * j);
+      const uint4 a = src[0], c = src[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      float qv[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qv[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        qv[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+#pragma unroll
+      for (int ps = 0; ps < kPasses; ++ps) best[ps] = fmaxf(best[ps], row_dot<LPR>(x[ps], qv));
+    }
+  }
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    if (n < n_units && j == 0) scores[((int64_t)b * Hkv + g) * n_units + n] = pred != 0ull ? best[ps] + 0.f : 0.f;
+  }
+}
+
+hipError_t launch_score_units_max(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                                  const float* ks, int n_units, float* scores) {
+  if (n_units == 0) return hipSuccess;
+  if (g.dtype != FDL_BF16 || g.T > 32 || g.G > 8) return hipErrorInvalidValue;
+  dim3 grid((n_units + kUnitsPerWg - 1) / kUnitsPerWg, g.Hkv, g.B);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  if (g.D == 128)
+    hipLaunchKernelGGL((score_units_max_kernel<128>), grid, dim3(256), 0, s, qq, pred_mask, ks, g.Hq, g.Hkv, g.G,
+                       g.T, n_units, scores);
+  else
+    hipLaunchKernelGGL((score_units_max_kernel<64>), grid, dim3(256), 0, s, qq, pred_mask, ks, g.Hq, g.Hkv, g.G,
+                       g.T, n_units, scores);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
 // Level-2 token scores inside candidate units (chunks), keys read through the page table:
 // scores[b][g][c][i] = dot(qs, k[token = cand_idx[b][g][c] * unit + i])
 // ------------------------------------------------------------------------------------------------

@@ -26,7 +26,7 @@ EXPORTED = (
     "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_get_status_bits",
     "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_cache_write", "fdl_predict_queries", "fdl_score_blocks",
-    "fdl_select_blocks", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
+    "fdl_score_blocks_max", "fdl_select_blocks", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_profile_begin", "fdl_profile_end",
 )
 
@@ -74,6 +74,7 @@ _SIGS = {
     "fdl_predict_queries": (_I, [_P, _I, _I, _P, _P, _I, _I, _P, _P]),
     "fdl_score_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _I,
                               ctypes.c_float, _I, _P, _P]),
+    "fdl_score_blocks_max": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P]),
     "fdl_select_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I,
                                _P, _P]),
     "fdl_score_select_tokens": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P,
@@ -246,6 +247,15 @@ class Handle:
             _ptr(page_table, 4 * B * g.pages_per_seq if g.paged else None, "page_table"),
             _ptr(scores, sbytes, "scores"), 1 if detect_sinks else 0, float(sink_tau), max_sinks,
             _ptr(sink_pos, 4 * B * max_sinks, "sink_pos"), _ptr(n_sinks, 4 * B, "n_sinks")))
+
+    def fdl_score_blocks_max(self, g: Geom, q, pred_mask, ks, unit_tokens: int, scores):
+        self.sync_stream()
+        B, Hkv = g.batch, g.n_kv_heads
+        n_units = -(-g.ctx_len // unit_tokens)
+        self._check(self.lib.fdl_score_blocks_max(
+            self.h, ctypes.byref(g.c()), _ptr(q, B * g.n_q_heads * g.dec_len * g.head_dim * g.elem, "q"),
+            _ptr(pred_mask, 8 * B, "pred_mask"), _ptr(ks, 4 * B * Hkv * n_units * g.head_dim, "ks"), unit_tokens,
+            _ptr(scores, 4 * B * Hkv * n_units, "scores")))
 
     def fdl_select_blocks(self, g: Geom, scores, n_units: int, unit_tokens: int, sink_pos, n_sinks,
                           max_sinks: int, top_k: int, max_sel: int, sel_idx, n_sel, cand_idx=None,

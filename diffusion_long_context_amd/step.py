@@ -52,7 +52,17 @@ class FocusStep:
         self.h.fdl_predict_queries(self.g.batch, self.g.dec_len, prev_conf, masked, self.fp.top_k_pos,
                                    self.fp.window, self.pred_mask, self.n_pred)
 
-    def score(self, q, ks, k_cache=None, k_dec=None, detect_sinks=False):
+    def score(self, q, ks, k_cache=None, k_dec=None, detect_sinks=False, scorer: str = "sum"):
+        """scorer "sum": the summed predicted query against each pooled key; "max": the best single
+        predicted query (fdl_score_blocks_max; sinks, when asked for, still by fdl_score_blocks)."""
+        if scorer == "max":
+            if detect_sinks:   # the sink pass also writes summed scores, which the max scores replace
+                self.h.fdl_score_blocks(self.g, q, self.pred_mask, ks, self.g.kv_block, self.scores,
+                                        k_cache=k_cache, k_dec=k_dec, detect_sinks=True,
+                                        sink_tau=self.fp.sink_tau, max_sinks=self.fp.max_sinks,
+                                        sink_pos=self.sink_pos, n_sinks=self.n_sinks)
+            self.h.fdl_score_blocks_max(self.g, q, self.pred_mask, ks, self.g.kv_block, self.scores)
+            return
         self.h.fdl_score_blocks(self.g, q, self.pred_mask, ks, self.g.kv_block, self.scores,
                                 k_cache=k_cache, k_dec=k_dec, detect_sinks=detect_sinks,
                                 sink_tau=self.fp.sink_tau, max_sinks=self.fp.max_sinks,
@@ -71,12 +81,12 @@ class FocusStep:
     def dense(self, q, k, v, k_dec, v_dec, out):
         self.h.fdl_dense_attn(self.g, q, k, v, k_dec, v_dec, None, out)
 
-    def layer(self, mode: str, q, k, v, k_dec, v_dec, ks, out):
+    def layer(self, mode: str, q, k, v, k_dec, v_dec, ks, out, scorer: str = "sum"):
         """mode: "dense", "source" (detect sinks here) or "reuse" (keep the last source's sinks)."""
         if mode == "dense":
             self.dense(q, k, v, k_dec, v_dec, out)
             return
-        self.score(q, ks, k_cache=k, k_dec=k_dec, detect_sinks=(mode == "source"))
+        self.score(q, ks, k_cache=k, k_dec=k_dec, detect_sinks=(mode == "source"), scorer=scorer)
         self.select()
         self.attend(q, k, v, k_dec, v_dec, out)
 

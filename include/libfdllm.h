@@ -174,6 +174,16 @@ fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* g, const void* q, cons
                             const int32_t* page_table, float* scores, int32_t detect_sinks,
                             float sink_tau, int32_t max_sinks, int32_t* sink_pos, int32_t* n_sinks);
 
+/* Per-query scoring, a reading the pages leave open next to the summed-query one of
+ * fdl_score_blocks (level 1): a unit's score is the largest pinned float32 dot product of one
+ * predicted query of the KV head's q-head group with the unit's key sum (same dot product tree as
+ * fdl_score_blocks), so a unit that matters to any single predicted position ranks high; +0 when no
+ * position is predicted, and a -0 result is written as +0.  scores [B][Hkv][n_units] from ks
+ * (fdl_pool_keys output with the same unit_tokens).  bf16 queries with dec_len <= 32 only
+ * (FDL_EUNSUPPORTED otherwise).  Its scores go to fdl_select_blocks like those of fdl_score_blocks. */
+fdl_status fdl_score_blocks_max(fdl_handle h, const fdl_geom* g, const void* q, const uint64_t* pred_mask,
+                                const float* ks, int32_t unit_tokens, float* scores);
+
 /* ---- step 3: keep sinks + top-K units; reuse sinks across layers ---------------------------- */
 
 /* [FA], [FS]: sinks are always kept and their locations are reused in deeper layers; the rest of

@@ -50,6 +50,7 @@ def test_null_handle_is_einval(lib):
                                  None) == FDL_EINVAL
     assert lib.fdl_score_select_tokens(None, None, None, None, None, None, 2048, None, 4, 512, 2052, None, None,
                                        None) == FDL_EINVAL
+    assert lib.fdl_score_blocks_max(None, None, None, None, None, 64, None) == FDL_EINVAL
     assert lib.fdl_sparse_attn(None, None, None, None, None, None, None, None, None, None, 1, 64,
                                None) == FDL_EINVAL
     assert lib.fdl_dense_attn(None, None, None, None, None, None, None, None, None) == FDL_EINVAL

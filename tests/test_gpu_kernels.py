@@ -11,7 +11,7 @@ from gpu_util import assert_close, dev, host, out_buffer, out_to_f64, require_gp
 from oracle.attention import attend, blocks_to_tokens
 from oracle.pipeline import focus_layer_step
 from oracle.predictor import predict_positions
-from oracle.scoring import pool_keys, query_sum, unit_scores
+from oracle.scoring import pool_keys, query_sum, unit_scores, unit_scores_max
 from oracle.selection import select_blocks
 from synth import get_config
 from synth.gen import make_single
@@ -131,6 +131,41 @@ def test_pool_chunks_one_pass_fallback():
         assert np.array_equal(host(ks).view(np.uint32), pool_keys(x["k"], cfg.kv_block).view(np.uint32))
     finally:
         hs.close()
+
+
+@pytest.mark.parametrize("kw,bits", [
+    (dict(n_q_heads=4, n_kv_heads=4, ctx_len=3000), None),
+    (dict(n_q_heads=28, n_kv_heads=4, ctx_len=4096), None),
+    (dict(n_q_heads=8, n_kv_heads=2, ctx_len=2000, head_dim=64, dec_len=20), None),
+    (dict(n_q_heads=4, n_kv_heads=2, ctx_len=1000), [0]),
+    (dict(n_q_heads=4, n_kv_heads=1, ctx_len=1000), [(1 << 32) - 1]),
+], ids=["mha", "gqa7", "gqa4-d64-T20", "nothing-predicted", "all-predicted"])
+def test_scores_max_bit_exact(h, kw, bits):
+    """Per-query (max) scores against the oracle, bit for bit, and the selection they lead to."""
+    cfg = _small_bf16(**kw)
+    x = make_single(cfg)
+    g = _geom(cfg)
+    if bits is None:
+        bits, _ = predict_positions(x["prev_conf"], x["masked"], cfg.top_k_pos, cfg.window)
+    bits = _u64(bits)
+    n_units = -(-cfg.ctx_len // 64)
+    ks = torch.zeros(cfg.batch, cfg.n_kv_heads, n_units, cfg.head_dim, dtype=torch.float32, device="cuda")
+    h.fdl_pool_keys(g, dev(x["k"]), None, 64, ks)
+    sc = torch.zeros(cfg.batch, cfg.n_kv_heads, n_units, dtype=torch.float32, device="cuda")
+    h.fdl_score_blocks_max(g, dev(x["q"]), dev(bits), ks, 64, sc)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    want = unit_scores_max(x["q"], bits, pool_keys(x["k"], 64), cfg.n_kv_heads)
+    assert np.array_equal(host(sc).view(np.uint32), want.view(np.uint32))
+    k = min(8, n_units)
+    sel = torch.zeros(cfg.batch, cfg.n_kv_heads, k, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros(cfg.batch, cfg.n_kv_heads, dtype=torch.int32, device="cuda")
+    h.fdl_select_blocks(g, sc, n_units, 64, None, None, 1, k, k, sel, nsel)
+    torch.cuda.synchronize()
+    ws = select_blocks(want, np.full((cfg.batch, 1), -1, np.int32), np.zeros(cfg.batch, np.int32), 64, k)
+    for b in range(cfg.batch):
+        for gg in range(cfg.n_kv_heads):
+            assert host(sel)[b, gg, :host(nsel)[b, gg]].tolist() == ws[b][gg].tolist()
 
 
 def test_scores_all_positions_predicted(h):
