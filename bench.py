@@ -253,6 +253,20 @@ def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
 
     t_unfused = timed(unfused, chunk_runs)
     assert h.fdl_get_status() == 0
+    # scorer readings on the same layer's pooled keys: the summed predicted query (the step's) against
+    # the best single predicted query
+    q = rn(B, cfg.n_q_heads, cfg.dec_len, D)
+    conf = torch.rand((B, cfg.dec_len), generator=gen, device=dev)
+    masked = (torch.rand((B, cfg.dec_len), generator=gen, device=dev) < 0.5).to(torch.uint8)
+    pm = torch.zeros(B, dtype=torch.int64, device=dev)
+    npred = torch.zeros(B, dtype=torch.int32, device=dev)
+    h.fdl_predict_queries(B, cfg.dec_len, conf, masked, cfg.top_k_pos, cfg.window, pm, npred)
+    sc = torch.zeros((B, Hkv, cfg.n_blk), dtype=torch.float32, device=dev)
+    t_sum = timed(lambda: h.fdl_score_blocks(g, q, pm, ks, cfg.kv_block, sc), chunk_runs)
+    t_max = timed(lambda: h.fdl_score_blocks_max(g, q, pm, ks, cfg.kv_block, sc), chunk_runs)
+    assert h.fdl_get_status() == 0
+    out["block_scoring_32k_layer"] = {"summed_query_us": t_sum, "per_query_max_us": t_max,
+                                      "predicted_positions": int(npred.sum())}
     kv_bytes = B * Hkv * L * D * 2
     refresh_bytes = 4 * kv_bytes + B * Hkv * cfg.n_blk * D * 4   # read new K, V; write K, V; write ks
     out["cache_refresh_32k_layer"] = {
