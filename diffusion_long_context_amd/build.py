@@ -8,6 +8,8 @@ import glob
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -15,7 +17,7 @@ LIB = os.path.join(HERE, "libfdllm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep hipcc from forming packed fp32 ops by itself
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
@@ -26,15 +28,32 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB) -> str:
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-o", tmp, *sources()]
+def _run(cmd: list[str], verbose: bool) -> subprocess.CompletedProcess:
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libfdllm.so")
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB) -> str:
+    """Every source compiled to an object in parallel (relocatable device code is not needed: each
+    kernel lives in one translation unit), then one link."""
+    srcs = sources()
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with tempfile.TemporaryDirectory(prefix="fdllm_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in srcs]
+        cmds = [[HIPCC, *FLAGS, *(extra or []), "-c", "-o", obj, src] for src, obj in zip(srcs, objs)]
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            results = list(pool.map(lambda c: _run(c, verbose), cmds))
+        failed = [r for r in results if r.returncode != 0]
+        if failed:
+            for r in failed:
+                sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed compiling libfdllm.so sources")
+        tmp = out + ".tmp"
+        r = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking libfdllm.so")
     os.replace(tmp, out)
     return out
 
