@@ -29,7 +29,6 @@ if ROOT not in sys.path:
 METRIC = "sparse-attn step us + KV tokens/s at 32K ctx; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
 WORKSPACE_BYTES = 256 << 20   # library workspace of the timed handle (sets the attention split count)
-TIME_EVERY = 16               # timed region: one sparse-attention launch in 16 carries HIP events
 
 
 # HBM bytes per sparse-attention dispatch, from two rocprofv3 counter runs of this benchmark
@@ -375,10 +374,10 @@ def main():
     torch.cuda.synchronize()
     assert h.fdl_get_status() == 0
 
-    # ---- the timed region: exactly K steps; HIP events around every sparse-attention launch ----
+    # ---- the timed region: exactly K steps; one pair of HIP events around each step's run of reuse
+    # layers (one fused sparse-attention launch per layer, back to back on the library's stream) ----
     log(f"timing {args.steps} steps")
-    # every TIME_EVERY-th sparse launch carries dispatch-timestamp events (≈ 4 µs each otherwise)
-    h.fdl_profile_begin(args.steps * NL // TIME_EVERY + 16, kinds=("sparse_attn",), every=TIME_EVERY)
+    h.fdl_profile_begin(args.steps + 16, kinds=("reuse_run",), every=1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(args.warmup, args.steps, arrays)
@@ -411,7 +410,7 @@ def main():
         tot, cnt = prof[kind]
         return tot / cnt if cnt else None
 
-    sparse_us = avg_us(prof_main, "sparse_attn")
+    sparse_us = avg_us(prof_main, "reuse_run")      # stream time per reuse launch, gaps included
     units = int(nsel_last.sum())                       # selected 64-token blocks over all heads
     unit_bytes = cfg.kv_block * D * 2 * 2              # K + V of one block, bf16
     # the sparse launch scores the blocks itself: pooled keys in, scores and selection out
@@ -440,7 +439,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
                      "kernel": "attn_mha_kernel<128,false,false,true,false> (block scoring + selection + sparse attention)",
-                     "avg_launch_us": sparse_us, "launches": prof_main["sparse_attn"][1],
+                     "avg_launch_us": sparse_us, "launches": prof_main["reuse_run"][1],
                      "bytes_per_launch": launch_bytes, "units_per_launch": units,
                      "unit_bytes": unit_bytes},
         "sparse_attn_layer_step_us": reuse_layer_us,

@@ -590,8 +590,30 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_para
   }
   st = run_predict(h, g.B, g.T, prev_conf, masked, fp->top_k_pos, fp->window, pred_mask, n_pred);
   if (st != FDL_OK) return st;
+  // runs of consecutive reuse layers, bracketed by one pair of events when FDL_PROF_REUSE_RUN is on
+  hipEvent_t run_a = nullptr, run_b = nullptr;
+  int run_n = 0;
+  auto run_end = [&]() {
+    if (run_a) {
+      (void)hipEventRecord(run_b, h->stream);
+      h->prof_recs.push_back({FDL_PROF_REUSE_RUN, run_a, run_b, run_n});
+    }
+    run_a = run_b = nullptr;
+    run_n = 0;
+  };
   for (int l = 0; l < n_layers; ++l) {
     const fdl_layer_io& io = layers[l];
+    if (io.mode == FDL_LAYER_REUSE) {
+      if (run_n == 0 && h->prof_on && ((h->prof_mask >> FDL_PROF_REUSE_RUN) & 1u) &&
+          (h->prof_seen[FDL_PROF_REUSE_RUN]++ % h->prof_every) == 0 && h->prof_used + 2 <= h->prof_pool.size()) {
+        run_a = h->prof_pool[h->prof_used++];
+        run_b = h->prof_pool[h->prof_used++];
+        (void)hipEventRecord(run_a, h->stream);
+      }
+      ++run_n;
+    } else if (run_n > 0) {
+      run_end();
+    }
     const int kind = io.mode == FDL_LAYER_DENSE ? FDL_PROF_LAYER_DENSE
                    : io.mode == FDL_LAYER_SOURCE ? FDL_PROF_LAYER_SOURCE : FDL_PROF_LAYER_REUSE;
     ProfScope layer_scope(h, kind);
@@ -623,6 +645,7 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_para
                   fp->max_sel, bt_log2, 0, io.out, fp->top_k_blocks);
     if (st != FDL_OK) return st;
   }
+  if (run_n > 0) run_end();
   return FDL_OK;
 }
 
@@ -664,7 +687,7 @@ fdl_status fdl_profile_end(fdl_handle h, double* total_us, int64_t* counts) {
       float ms = 0.f;
       if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess && r.kind >= 0 && r.kind < FDL_PROF_KINDS) {
         total_us[r.kind] += 1000.0 * ms;
-        counts[r.kind] += 1;
+        counts[r.kind] += r.n;
       }
     }
   }

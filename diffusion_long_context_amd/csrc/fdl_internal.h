@@ -27,6 +27,7 @@ struct fdl_ctx {
   struct ProfRec {
     int kind;
     hipEvent_t a, b;
+    int n = 1;   // launches (layers) the pair brackets
   };
   bool prof_on = false;
   uint32_t prof_mask = 0;

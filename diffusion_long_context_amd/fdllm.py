@@ -32,7 +32,7 @@ EXPORTED = (
 
 FDL_LAYER_DENSE, FDL_LAYER_SOURCE, FDL_LAYER_REUSE = 0, 1, 2
 PROF_KINDS = ("predict", "pool", "score", "sinks", "select", "sparse_attn", "dense_attn",
-              "layer_dense", "layer_source", "layer_reuse")
+              "layer_dense", "layer_source", "layer_reuse", "reuse_run")
 
 
 class FdlError(RuntimeError):

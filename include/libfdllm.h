@@ -299,11 +299,13 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* g, const fdl_focus_param
  * run.  fdl_profile_begin creates a pool of 2 * max_records events and clears the records;
  * fdl_profile_end synchronises, writes the summed duration in microseconds and the number of timed
  * launches of every kind into total_us[FDL_PROF_KINDS] / counts[FDL_PROF_KINDS] and releases the
- * pool.  Records beyond max_records are dropped. */
+ * pool.  Records beyond max_records are dropped.  FDL_PROF_REUSE_RUN brackets each run of
+ * consecutive reuse layers of fdl_focus_step with one pair of events and counts the layers of the
+ * run, so total / count is the stream time per reuse layer (kernel plus the gap to the next). */
 typedef enum {
   FDL_PROF_PREDICT = 0, FDL_PROF_POOL, FDL_PROF_SCORE, FDL_PROF_SINKS, FDL_PROF_SELECT,
   FDL_PROF_SPARSE_ATTN, FDL_PROF_DENSE_ATTN, FDL_PROF_LAYER_DENSE, FDL_PROF_LAYER_SOURCE,
-  FDL_PROF_LAYER_REUSE, FDL_PROF_KINDS
+  FDL_PROF_LAYER_REUSE, FDL_PROF_REUSE_RUN, FDL_PROF_KINDS
 } fdl_prof_kind;
 
 fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask, int32_t every);

@@ -180,8 +180,13 @@ def test_focus_step_driver(kw, monkeypatch):
                                        k_dec=t[l]["k_dec"], v_dec=t[l]["v_dec"], ks=ks[l], out=outs[l],
                                        mode=code[m]) for l, m in enumerate(modes)])
         x0 = xs[0]
+        h.fdl_profile_begin(16, kinds=("reuse_run", "layer_reuse", "layer_dense"), every=1)
         h.fdl_focus_step(g, params, dev(x0["prev_conf"]), dev(x0["masked"]), table, pm, npd, sc, sp, nsk,
                          sel, nsel)
+        prof = h.fdl_profile_end()
+        # the two trailing reuse layers: one run of two launches; a run spans at least its layers
+        assert prof["reuse_run"][1] == 2 and prof["layer_reuse"][1] == 2 and prof["layer_dense"][1] == 1
+        assert prof["reuse_run"][0] >= 0.9 * prof["layer_reuse"][0] > 0
         torch.cuda.synchronize()
         status, bits = h.fdl_get_status_bits()
         assert status == 0
