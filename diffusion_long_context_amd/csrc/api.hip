@@ -284,6 +284,10 @@ fdl_status fdl_create(fdl_handle* out, void* hip_stream, size_t workspace_bytes)
 
 fdl_status fdl_destroy(fdl_handle h) {
   if (!h) return FDL_EINVAL;
+  if (h->capturing) {   // abandon an open capture
+    hipGraph_t graph = nullptr;
+    if (hipStreamEndCapture(h->stream, &graph) == hipSuccess && graph) (void)hipGraphDestroy(graph);
+  }
   (void)hipStreamSynchronize(h->stream);
   (void)hipFree(h->ws);
   delete h;
@@ -292,6 +296,8 @@ fdl_status fdl_destroy(fdl_handle h) {
 
 fdl_status fdl_set_stream(fdl_handle h, void* hip_stream) {
   if (!h) return FDL_EINVAL;
+  if (h->capturing && static_cast<hipStream_t>(hip_stream) != h->stream)
+    return fail(h, FDL_EINVAL, "the handle's stream is being captured");
   h->stream = static_cast<hipStream_t>(hip_stream);
   return FDL_OK;
 }
@@ -305,6 +311,7 @@ fdl_status fdl_get_status_bits(fdl_handle h, uint32_t* bits) {
                 "status bits");
   if (bits) *bits = 0;
   if (!h) return FDL_EINVAL;
+  if (h->capturing) return fail(h, FDL_EINVAL, "the handle's stream is being captured");
   fdl_status st = hip_status(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
   if (st != FDL_OK) return st;
   uint32_t word = 0;
@@ -542,11 +549,12 @@ fdl_status fdl_dense_attn(fdl_handle h, const fdl_geom* g, const void* q, const 
   return attn_common(h, g, q, k_cache, v_cache, k_dec, v_dec, page_table, nullptr, nullptr, 0, 1, 1, out);
 }
 
-fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_params* fp,
-                          const float* prev_conf, const uint8_t* masked, int32_t n_layers,
-                          const fdl_layer_io* layers, uint64_t* pred_mask, int32_t* n_pred,
-                          float* scores, int32_t* sink_pos, int32_t* n_sinks, int32_t* sel_idx,
-                          int32_t* n_sel) {
+// One denoising step over the layer table; dry: validate only (nothing is launched).
+static fdl_status focus_step_impl(fdl_handle h, const fdl_geom* gp, const fdl_focus_params* fp,
+                                  const float* prev_conf, const uint8_t* masked, int32_t n_layers,
+                                  const fdl_layer_io* layers, uint64_t* pred_mask, int32_t* n_pred,
+                                  float* scores, int32_t* sink_pos, int32_t* n_sinks, int32_t* sel_idx,
+                                  int32_t* n_sel, bool dry) {
   if (!h) return FDL_EINVAL;
   Geom g;
   fdl_status st = check_geom(h, gp, g);
@@ -588,6 +596,7 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_para
                      sink_pos, n_sinks, &ns, &cap);
     if (st != FDL_OK) return st;
   }
+  if (dry) return FDL_OK;
   st = run_predict(h, g.B, g.T, prev_conf, masked, fp->top_k_pos, fp->window, pred_mask, n_pred);
   if (st != FDL_OK) return st;
   // runs of consecutive reuse layers, bracketed by one pair of events when FDL_PROF_REUSE_RUN is on
@@ -649,8 +658,126 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_para
   return FDL_OK;
 }
 
+fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* gp, const fdl_focus_params* fp,
+                          const float* prev_conf, const uint8_t* masked, int32_t n_layers,
+                          const fdl_layer_io* layers, uint64_t* pred_mask, int32_t* n_pred,
+                          float* scores, int32_t* sink_pos, int32_t* n_sinks, int32_t* sel_idx,
+                          int32_t* n_sel) {
+  return focus_step_impl(h, gp, fp, prev_conf, masked, n_layers, layers, pred_mask, n_pred, scores, sink_pos,
+                         n_sinks, sel_idx, n_sel, false);
+}
+
+// ---- the decode loop: the unmask update, several steps in one call, graph capture -------------
+
+static fdl_status check_unmask(fdl_handle h, int32_t batch, int32_t dec_len, const float* conf,
+                               const uint8_t* masked, int32_t n_unmask) {
+  if (batch < 1) return fail(h, FDL_EINVAL, "batch must be >= 1");
+  if (dec_len < 1 || dec_len > 64) return fail(h, FDL_EINVAL, "dec_len must be in [1, 64]");
+  if (n_unmask < 0 || n_unmask > 64) return fail(h, FDL_EINVAL, "n_unmask must be in [0, 64]");
+  if (!conf || !masked) return fail(h, FDL_EINVAL, "conf and masked must be non-NULL");
+  return FDL_OK;
+}
+
+fdl_status fdl_unmask(fdl_handle h, int32_t batch, int32_t dec_len, const float* conf, uint8_t* masked,
+                      int32_t n_unmask, int32_t* decoded) {
+  if (!h) return FDL_EINVAL;
+  fdl_status st = check_unmask(h, batch, dec_len, conf, masked, n_unmask);
+  if (st != FDL_OK) return st;
+  return hip_status(h, fdl::launch_unmask(h->stream, batch, dec_len, conf, masked, n_unmask, decoded),
+                    "unmask launch");
+}
+
+fdl_status fdl_decode_steps(fdl_handle h, const fdl_geom* gp, const fdl_focus_params* fp, int32_t n_steps,
+                            const float* prev_conf0, const float* conf, uint8_t* masked, int32_t n_unmask,
+                            int32_t* decoded, int32_t n_layers, const fdl_layer_io* layers,
+                            uint64_t* pred_mask, int32_t* n_pred, float* scores, int32_t* sink_pos,
+                            int32_t* n_sinks, int32_t* sel_idx, int32_t* n_sel) {
+  if (!h) return FDL_EINVAL;
+  if (n_steps < 0) return fail(h, FDL_EINVAL, "n_steps must be >= 0");
+  if (n_steps == 0) return FDL_OK;
+  if (!gp) return fail(h, FDL_EINVAL, "geometry must be non-NULL");
+  if (n_layers > 0 && !layers) return fail(h, FDL_EINVAL, "layers must be non-NULL");
+  fdl_status st = check_unmask(h, gp->batch, gp->dec_len, conf, masked, n_unmask);
+  if (st != FDL_OK) return st;
+  const int64_t bt = (int64_t)gp->batch * gp->dec_len;
+  for (int s = 0; s < n_steps; ++s) {   // every step's table first: nothing runs unless all are valid
+    st = focus_step_impl(h, gp, fp, s == 0 ? prev_conf0 : conf + (s - 1) * bt, masked, n_layers,
+                         layers + (int64_t)s * n_layers, pred_mask, n_pred, scores, sink_pos, n_sinks, sel_idx,
+                         n_sel, true);
+    if (st != FDL_OK) return st;
+  }
+  for (int s = 0; s < n_steps; ++s) {
+    st = focus_step_impl(h, gp, fp, s == 0 ? prev_conf0 : conf + (s - 1) * bt, masked, n_layers,
+                         layers + (int64_t)s * n_layers, pred_mask, n_pred, scores, sink_pos, n_sinks, sel_idx,
+                         n_sel, false);
+    if (st != FDL_OK) return st;
+    st = hip_status(h, fdl::launch_unmask(h->stream, gp->batch, gp->dec_len, conf + s * bt, masked, n_unmask,
+                                          decoded ? decoded + (int64_t)s * gp->batch * n_unmask : nullptr),
+                    "unmask launch");
+    if (st != FDL_OK) return st;
+  }
+  return FDL_OK;
+}
+
+struct fdl_graph_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+fdl_status fdl_capture_begin(fdl_handle h) {
+  if (!h) return FDL_EINVAL;
+  if (h->capturing) return fail(h, FDL_EINVAL, "already capturing");
+  if (h->prof_on) return fail(h, FDL_EINVAL, "profiling is on: end it before capturing");
+  if (h->stream == nullptr) return fail(h, FDL_EINVAL, "the null stream cannot be captured: set another stream");
+  fdl_status st = hip_status(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal),
+                             "hipStreamBeginCapture");
+  if (st == FDL_OK) h->capturing = true;
+  return st;
+}
+
+fdl_status fdl_capture_end(fdl_handle h, fdl_graph* out) {
+  if (!h) return FDL_EINVAL;
+  if (!out) return fail(h, FDL_EINVAL, "out must be non-NULL");
+  *out = nullptr;
+  if (!h->capturing) return fail(h, FDL_EINVAL, "not capturing");
+  h->capturing = false;
+  hipGraph_t graph = nullptr;
+  fdl_status st = hip_status(h, hipStreamEndCapture(h->stream, &graph), "hipStreamEndCapture");
+  if (st != FDL_OK) return st;
+  hipGraphExec_t exec = nullptr;
+  st = hip_status(h, hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "hipGraphInstantiate");
+  if (st != FDL_OK) {
+    (void)hipGraphDestroy(graph);
+    return st;
+  }
+  fdl_graph g = new (std::nothrow) fdl_graph_s{graph, exec};
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return fail(h, FDL_ENOMEM, "out of host memory");
+  }
+  *out = g;
+  return FDL_OK;
+}
+
+fdl_status fdl_graph_launch(fdl_handle h, fdl_graph g) {
+  if (!h) return FDL_EINVAL;
+  if (!g) return fail(h, FDL_EINVAL, "graph must be non-NULL");
+  if (h->capturing) return fail(h, FDL_EINVAL, "the handle's stream is being captured");
+  return hip_status(h, hipGraphLaunch(g->exec, h->stream), "hipGraphLaunch");
+}
+
+fdl_status fdl_graph_destroy(fdl_graph g) {
+  if (!g) return FDL_OK;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
+  return FDL_OK;
+}
+
 fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask, int32_t every) {
   if (!h || max_records < 1) return h ? fail(h, FDL_EINVAL, "max_records must be >= 1") : FDL_EINVAL;
+  if (h->capturing) return fail(h, FDL_EINVAL, "the handle's stream is being captured");
   if (every < 1) return fail(h, FDL_EINVAL, "every must be >= 1");
   for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
   h->prof_pool.clear();
@@ -677,6 +804,7 @@ fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_ma
 fdl_status fdl_profile_end(fdl_handle h, double* total_us, int64_t* counts) {
   if (!h) return FDL_EINVAL;
   if (!total_us || !counts) return fail(h, FDL_EINVAL, "total_us and counts must be non-NULL");
+  if (h->capturing) return fail(h, FDL_EINVAL, "the handle's stream is being captured");
   fdl_status st = hip_status(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
   for (int k = 0; k < FDL_PROF_KINDS; ++k) {
     total_us[k] = 0.0;

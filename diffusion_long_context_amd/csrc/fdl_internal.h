@@ -23,6 +23,7 @@ struct fdl_ctx {
   char* scratch;         // general scratch after the fixed header
   size_t scratch_bytes;
   char last_error[256];
+  bool capturing = false;   // between fdl_capture_begin and fdl_capture_end
   // optional event timing (fdl_profile_begin / fdl_profile_end)
   struct ProfRec {
     int kind;
@@ -93,6 +94,10 @@ struct Geom {
 hipError_t launch_cache_write(hipStream_t s, const Geom& g, const void* k_new, const void* v_new, int t0, int n_tok,
                               void* k, void* v, const int32_t* page_table, int unit_log2, float* ks, uint32_t* status,
                               float* sub, size_t sub_bytes);
+
+// The unmask update after a step (decoded may be NULL).
+hipError_t launch_unmask(hipStream_t s, int batch, int T, const float* conf, uint8_t* masked, int n_unmask,
+                         int32_t* decoded);
 
 hipError_t launch_predict(hipStream_t s, int batch, int T, const float* prev_conf,
                           const uint8_t* masked, int top_k, int window, uint64_t* pred_mask,

@@ -27,7 +27,8 @@ EXPORTED = (
     "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_cache_write", "fdl_predict_queries", "fdl_score_blocks",
     "fdl_score_blocks_max", "fdl_select_blocks", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
-    "fdl_profile_begin", "fdl_profile_end",
+    "fdl_unmask", "fdl_decode_steps", "fdl_capture_begin", "fdl_capture_end", "fdl_graph_launch",
+    "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end",
 )
 
 FDL_LAYER_DENSE, FDL_LAYER_SOURCE, FDL_LAYER_REUSE = 0, 1, 2
@@ -83,6 +84,13 @@ _SIGS = {
     "fdl_dense_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P]),
     "fdl_focus_step": (_I, [_P, ctypes.POINTER(fdl_geom), ctypes.POINTER(fdl_focus_params), _P, _P, _I,
                             ctypes.POINTER(fdl_layer_io), _P, _P, _P, _P, _P, _P, _P]),
+    "fdl_unmask": (_I, [_P, _I, _I, _P, _P, _I, _P]),
+    "fdl_decode_steps": (_I, [_P, ctypes.POINTER(fdl_geom), ctypes.POINTER(fdl_focus_params), _I, _P, _P, _P, _I,
+                              _P, _I, ctypes.POINTER(fdl_layer_io), _P, _P, _P, _P, _P, _P, _P]),
+    "fdl_capture_begin": (_I, [_P]),
+    "fdl_capture_end": (_I, [_P, ctypes.POINTER(_P)]),
+    "fdl_graph_launch": (_I, [_P, _P]),
+    "fdl_graph_destroy": (_I, [_P]),
     "fdl_profile_begin": (_I, [_P, _I, ctypes.c_uint32, _I]),
     "fdl_profile_end": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -339,6 +347,51 @@ class Handle:
             _ptr(scores, 4 * B * Hkv * n_blk, "scores"), _ptr(sink_pos, 4 * B * params.max_sinks, "sink_pos"),
             _ptr(n_sinks, 4 * B, "n_sinks"), _ptr(sel_idx, 4 * B * Hkv * params.max_sel, "sel_idx"),
             _ptr(n_sel, 4 * B * Hkv, "n_sel")))
+
+    # ---- the decode loop ---------------------------------------------------------------------
+
+    def fdl_unmask(self, batch: int, dec_len: int, conf, masked, n_unmask: int = 1, decoded=None):
+        self.sync_stream()
+        self._check(self.lib.fdl_unmask(self.h, batch, dec_len, _ptr(conf, 4 * batch * dec_len, "conf"),
+                                        _ptr(masked, batch * dec_len, "masked"), n_unmask,
+                                        _ptr(decoded, 4 * batch * n_unmask, "decoded")))
+
+    def fdl_decode_steps(self, g: Geom, params: fdl_focus_params, n_steps: int, prev_conf0, conf, masked,
+                         n_unmask: int, decoded, layers_arr, pred_mask, n_pred, scores, sink_pos, n_sinks,
+                         sel_idx, n_sel):
+        """n_steps steps of one block: layers_arr holds n_steps tables of equal length, step-major
+        (make_layers over the concatenated lists)."""
+        self.sync_stream()
+        if n_steps > 0 and len(layers_arr) % n_steps:
+            raise ValueError("layers_arr must hold n_steps tables of equal length")
+        n_layers = len(layers_arr) // n_steps if n_steps > 0 else 0
+        B, T, Hkv = g.batch, g.dec_len, g.n_kv_heads
+        n_blk = -(-g.ctx_len // g.kv_block)
+        self._check(self.lib.fdl_decode_steps(
+            self.h, ctypes.byref(g.c()), ctypes.byref(params), n_steps, _ptr(prev_conf0, 4 * B * T, "prev_conf0"),
+            _ptr(conf, 4 * n_steps * B * T, "conf"), _ptr(masked, B * T, "masked"), n_unmask,
+            _ptr(decoded, 4 * n_steps * B * n_unmask, "decoded"), n_layers, layers_arr,
+            _ptr(pred_mask, 8 * B, "pred_mask"), _ptr(n_pred, 4 * B, "n_pred"),
+            _ptr(scores, 4 * B * Hkv * n_blk, "scores"), _ptr(sink_pos, 4 * B * params.max_sinks, "sink_pos"),
+            _ptr(n_sinks, 4 * B, "n_sinks"), _ptr(sel_idx, 4 * B * Hkv * params.max_sel, "sel_idx"),
+            _ptr(n_sel, 4 * B * Hkv, "n_sel")))
+
+    def fdl_capture_begin(self):
+        """Start capturing the current torch stream (not the default stream)."""
+        self.sync_stream()
+        self._check(self.lib.fdl_capture_begin(self.h))
+
+    def fdl_capture_end(self) -> ctypes.c_void_p:
+        out = _P()
+        self._check(self.lib.fdl_capture_end(self.h, ctypes.byref(out)))
+        return out
+
+    def fdl_graph_launch(self, graph):
+        self.sync_stream()
+        self._check(self.lib.fdl_graph_launch(self.h, graph))
+
+    def fdl_graph_destroy(self, graph):
+        self._check(self.lib.fdl_graph_destroy(graph))
 
     def fdl_profile_begin(self, max_records: int, kinds=PROF_KINDS, every: int = 1):
         self.sync_stream()

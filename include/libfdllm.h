@@ -20,8 +20,9 @@
  *       k_dec, v_dec    [B][Hkv][T][D]      (the current decode block's own keys / values)
  *     q / k / v / out are bf16 (FDL_BF16, raw 16-bit patterns) or float32 (FDL_F32).
  *   - Every call is asynchronous on the handle's HIP stream and never synchronises the host,
- *     except fdl_get_status.  No call allocates or frees memory; fdl_create allocates the one
- *     workspace.  Calls on one handle must come from one host thread at a time, and calls that
+ *     except fdl_get_status and fdl_profile_end.  No call allocates or frees device memory;
+ *     fdl_create allocates the one workspace (fdl_capture_end leaves the graph's own resources to
+ *     the HIP runtime).  Calls on one handle must come from one host thread at a time, and calls that
  *     share a handle are ordered by its stream (they reuse its workspace).
  *   - Argument errors return FDL_EINVAL (or FDL_EUNSUPPORTED for valid shapes outside the kernel
  *     set, FDL_ENOMEM when the workspace is too small) synchronously, before anything is launched;
@@ -288,6 +289,51 @@ fdl_status fdl_focus_step(fdl_handle h, const fdl_geom* g, const fdl_focus_param
                           const fdl_layer_io* layers, uint64_t* pred_mask, int32_t* n_pred,
                           float* scores, int32_t* sink_pos, int32_t* n_sinks, int32_t* sel_idx,
                           int32_t* n_sel);
+
+/* ---- the step after the path: the unmask update and the denoising loop ----------------------- */
+
+/* [FA] Elamur "Summary": a block is decoded by denoising its masked positions step after step;
+ * "Key points": the tokens a step decodes are the highest-confidence ones still masked, one position
+ * per step at generation length = steps.  Reading: after a step, the n_unmask masked positions of
+ * each sequence with the highest confidence conf[b] are decoded, ranked as fdl_predict_queries
+ * ranks (ties to the lower position, NaN below every number, -0 == +0).
+ *   conf    [batch][dec_len] float32, device, read only at masked positions.
+ *   masked  [batch][dec_len] uint8, device, updated in place: decoded positions become 0.
+ *   decoded [batch][n_unmask] int32, device, may be NULL: the decoded positions in rank order, -1
+ *           past the number decoded (fewer masked positions than n_unmask: all of them).
+ * 1 <= dec_len <= 64; 0 <= n_unmask <= 64.  FDL_EINVAL otherwise, before any launch. */
+fdl_status fdl_unmask(fdl_handle h, int32_t batch, int32_t dec_len, const float* conf, uint8_t* masked,
+                      int32_t n_unmask, int32_t* decoded);
+
+/* n_steps denoising steps of one decode block with no host round trip: step s is fdl_focus_step
+ * with prev_conf = (s == 0 ? prev_conf0 : conf + (s - 1) * B * T), the current masked flags and the
+ * layer table layers + s * n_layers, followed by fdl_unmask(conf + s * B * T, masked, n_unmask,
+ * decoded ? decoded + s * B * n_unmask : NULL).  conf [n_steps][B][T] holds the confidence each
+ * step produces (supplied by the caller: the model's head is not part of this library);
+ * prev_conf0 may be NULL (the first step of a block).  The other arguments are fdl_focus_step's and
+ * hold the last step's values on return.  Every step's arguments are validated before anything is
+ * launched.  Together with fdl_capture_begin / fdl_capture_end, a whole block (or a whole run of
+ * blocks) becomes one graph launch. */
+fdl_status fdl_decode_steps(fdl_handle h, const fdl_geom* g, const fdl_focus_params* p, int32_t n_steps,
+                            const float* prev_conf0, const float* conf, uint8_t* masked, int32_t n_unmask,
+                            int32_t* decoded, int32_t n_layers, const fdl_layer_io* layers,
+                            uint64_t* pred_mask, int32_t* n_pred, float* scores, int32_t* sink_pos,
+                            int32_t* n_sinks, int32_t* sel_idx, int32_t* n_sel);
+
+/* HIP-graph capture of the launches issued on the handle's stream.  fdl_capture_begin starts
+ * capturing that stream (not the null stream; not while profiling); every library call until
+ * fdl_capture_end is recorded instead of run (argument errors are still reported at once, and a
+ * call that failed records nothing).  fdl_capture_end ends the capture and instantiates the graph;
+ * fdl_graph_launch replays it on the handle's stream, with the pointers and scalars of the captured
+ * calls; fdl_graph_destroy releases it.  The library's launches record no memset node.  While
+ * capturing, fdl_get_status, fdl_profile_* and switching the stream fail with FDL_EINVAL.  A graph
+ * holds driver resources (allocated by the HIP runtime at fdl_capture_end) until it is destroyed;
+ * replays that share a handle are ordered by its stream, like any other calls on it. */
+typedef struct fdl_graph_s* fdl_graph;
+fdl_status fdl_capture_begin(fdl_handle h);
+fdl_status fdl_capture_end(fdl_handle h, fdl_graph* graph);
+fdl_status fdl_graph_launch(fdl_handle h, fdl_graph graph);
+fdl_status fdl_graph_destroy(fdl_graph graph);
 
 /* ---- timing --------------------------------------------------------------------------------- */
 
