@@ -130,6 +130,63 @@ def sparse_launch_bytes(cfg, units: int) -> int:
     return units * unit_bytes + fixed
 
 
+def time_decode_loop(h, g, cfg, params, Q, K, V, KD, VD, ks, outs, modes, pred_mask, n_pred, scores, sink_pos,
+                     n_sinks, sel_idx, n_sel, reps: int = 3) -> dict:
+    """One decode block (steps_per_block steps of all layers, each step followed by the unmask
+    update) as one fdl_decode_steps call, eager and replayed from a HIP graph, on a side stream.
+    Confidences are seeded U(0, 1); the masked flags start all set and evolve on the device."""
+    import torch
+    spb, B, T, NL = min(cfg.steps_per_block, Q.shape[0]), cfg.batch, cfg.dec_len, cfg.n_layers
+    dev = Q.device
+    table = h.make_layers(g, [dict(q=Q[i, l], k_cache=K[l], v_cache=V[l], k_dec=KD[i, l], v_dec=VD[i, l], ks=ks[l],
+                                   out=outs[l], mode=m) for i in range(spb) for l, m in enumerate(modes())])
+    confs = torch.rand((spb, B, T), generator=torch.Generator(device=dev).manual_seed(7), device=dev)
+    masked = torch.ones((B, T), dtype=torch.uint8, device=dev)
+    decoded = torch.zeros((spb, B, 1), dtype=torch.int32, device=dev)
+
+    def block():
+        h.fdl_decode_steps(g, params, spb, None, confs, masked, 1, decoded, table, pred_mask, n_pred, scores,
+                           sink_pos, n_sinks, sel_idx, n_sel)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    res = {}
+    with torch.cuda.stream(side):
+        masked.fill_(1)
+        block()
+        side.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            masked.fill_(1)
+            block()
+        side.synchronize()
+        res["eager_ms_per_step"] = 1e3 * (time.perf_counter() - t0) / (reps * spb)
+        h.fdl_capture_begin()
+        try:
+            block()
+        finally:
+            graph = h.fdl_capture_end()
+        try:
+            masked.fill_(1)
+            h.fdl_graph_launch(graph)
+            side.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                masked.fill_(1)
+                h.fdl_graph_launch(graph)
+            side.synchronize()
+            res["graph_ms_per_step"] = 1e3 * (time.perf_counter() - t0) / (reps * spb)
+        finally:
+            h.fdl_graph_destroy(graph)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    dec = decoded.cpu().numpy()
+    res.update(steps=spb, layers=NL, kv_tokens_per_s_graph=cfg.ctx_len * B * NL / (res["graph_ms_per_step"] * 1e-3),
+               decoded_distinct=all(len(set(dec[:, b, 0].tolist())) == spb for b in range(B)),
+               masked_left=int(masked.sum().item()))
+    return res
+
+
 def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
     """Diagnostics on the other workloads of the benchmark description (not the headline): the 8K MHA
     and 16K grouped-query single-layer configurations (per-layer GPU time of each layer kind through
@@ -405,6 +462,9 @@ def main():
     torch.cuda.synchronize()
     t_dense_step = (time.perf_counter() - t0) / args.dense_steps
     assert h.fdl_get_status() == 0
+    decode_loop = None if args.no_workloads else time_decode_loop(h, g, cfg, params, Q, K, V, KD, VD, ks, outs, modes,
+                                                                  pred_mask, n_pred, scores, sink_pos, n_sinks,
+                                                                  sel_idx, n_sel)
 
     def avg_us(prof, kind):
         tot, cnt = prof[kind]
@@ -449,6 +509,7 @@ def main():
         "dense_step_ms": 1e3 * t_dense_step,
         "speedup_vs_dense_hip": t_dense_step / t_plain,
         "sinks_detected": nsinks_last,
+        "decode_loop": decode_loop,
         "workloads": None,
         "cpu_baseline": None,
     }
