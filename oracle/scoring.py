@@ -88,6 +88,37 @@ def unit_scores_max(q, pred_bits, ks, n_kv_heads: int) -> np.ndarray:
     return out
 
 
+def unit_scores_mass(q, pred_bits, ks, n_kv_heads: int, unit: int, ctx_len: int) -> np.ndarray:
+    """Softmax-mass scoring, a third reading of how the predicted queries estimate which units
+    matter (the pages speak of estimating attention importance): every predicted query of the KV
+    head's q-head group attends to the units' mean keys (the key sum divided by the number of tokens
+    in the unit; a partial last unit counts its valid tokens) with the attention scale 1/sqrt(D), a
+    softmax over all units of the head; a unit's score is the probability mass it receives, summed
+    over those queries.  float64 throughout; zeros when nothing is predicted.  q [B][Hq][T][D],
+    pred_bits [B], ks [B][Hkv][n][D] -> [B][Hkv][n] float64."""
+    qf = values_f32(q).astype(np.float64)
+    B, Hq, T, D = qf.shape
+    G = Hq // n_kv_heads
+    ks64 = np.asarray(ks, dtype=np.float64)
+    n = ks64.shape[2]
+    counts = np.minimum(unit, ctx_len - unit * np.arange(n)).astype(np.float64)
+    assert (counts > 0).all()
+    kbar = ks64 / counts[None, None, :, None]
+    out = np.zeros((B, n_kv_heads, n), dtype=np.float64)
+    for b in range(B):
+        P = [p for p in range(T) if (int(pred_bits[b]) >> p) & 1]
+        if not P:
+            continue
+        for g in range(n_kv_heads):
+            queries = qf[b, g * G:(g + 1) * G][:, P].reshape(-1, D)
+            z = queries @ kbar[b, g].T / np.sqrt(D)
+            z -= z.max(axis=1, keepdims=True)
+            w = np.exp(z)
+            w /= w.sum(axis=1, keepdims=True)
+            out[b, g] = w.sum(axis=0)
+    return out
+
+
 def token_scores(qs, k_tokens) -> np.ndarray:
     """qs [B][Hkv][D], k_tokens [B][Hkv][n][D] (bf16 bits or float32) -> [B][Hkv][n] float32."""
     return tree_dot(np.asarray(qs, np.float32)[:, :, None, :], values_f32(k_tokens))
