@@ -309,8 +309,8 @@ def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
 
     t_unfused = timed(unfused, chunk_runs)
     assert h.fdl_get_status() == 0
-    # scorer readings on the same layer's pooled keys: the summed predicted query (the step's) against
-    # the best single predicted query
+    # scorer readings on the same layer's pooled keys: the summed predicted query (the step's), the
+    # best single predicted query and the softmax mass over the units' mean keys
     q = rn(B, cfg.n_q_heads, cfg.dec_len, D)
     conf = torch.rand((B, cfg.dec_len), generator=gen, device=dev)
     masked = (torch.rand((B, cfg.dec_len), generator=gen, device=dev) < 0.5).to(torch.uint8)
@@ -320,8 +320,10 @@ def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
     sc = torch.zeros((B, Hkv, cfg.n_blk), dtype=torch.float32, device=dev)
     t_sum = timed(lambda: h.fdl_score_blocks(g, q, pm, ks, cfg.kv_block, sc), chunk_runs)
     t_max = timed(lambda: h.fdl_score_blocks_max(g, q, pm, ks, cfg.kv_block, sc), chunk_runs)
+    t_mass = timed(lambda: h.fdl_score_blocks_mass(g, q, pm, ks, cfg.kv_block, sc), chunk_runs)
     assert h.fdl_get_status() == 0
     out["block_scoring_32k_layer"] = {"summed_query_us": t_sum, "per_query_max_us": t_max,
+                                      "softmax_mass_us": t_mass,
                                       "predicted_positions": int(npred.sum())}
     kv_bytes = B * Hkv * L * D * 2
     refresh_bytes = 4 * kv_bytes + B * Hkv * cfg.n_blk * D * 4   # read new K, V; write K, V; write ks

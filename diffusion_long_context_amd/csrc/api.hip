@@ -439,6 +439,26 @@ fdl_status fdl_score_blocks_max(fdl_handle h, const fdl_geom* gp, const void* q,
                     "score_units_max launch");
 }
 
+fdl_status fdl_score_blocks_mass(fdl_handle h, const fdl_geom* gp, const void* q, const uint64_t* pred_mask,
+                                 const float* ks, int32_t unit_tokens, float* scores) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!q || !pred_mask || !ks || !scores) return fail(h, FDL_EINVAL, "q, pred_mask, ks and scores must be non-NULL");
+  if (!is_pow2(unit_tokens) || unit_tokens > 4096)
+    return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
+  if (g.dtype != FDL_BF16 || g.T > 32)
+    return fail(h, FDL_EUNSUPPORTED, "softmax-mass scoring runs bf16 queries with dec_len <= 32");
+  const int n_units = (g.L + unit_tokens - 1) / unit_tokens;
+  if (fdl::mass_scratch_bytes(g, n_units) > h->scratch_bytes)
+    return fail(h, FDL_ENOMEM, "workspace too small for softmax-mass scoring");
+  ProfScope ps(h, FDL_PROF_SCORE);
+  return hip_status(h, fdl::launch_score_units_mass(h->stream, g, q, pred_mask, ks, n_units, ilog2(unit_tokens),
+                                                    scores, h->scratch),
+                    "score_units_mass launch");
+}
+
 fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* gp, const float* scores, int32_t n_units,
                              int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
                              int32_t max_sinks, const int32_t* cand_idx, int32_t n_cand,

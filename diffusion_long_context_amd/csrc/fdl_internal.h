@@ -113,6 +113,10 @@ hipError_t launch_score_units_max(hipStream_t s, const Geom& g, const void* q, c
                                   const float* ks, int n_units, float* scores);
 hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                               const float* ks, int n_units, float* scores);
+// Softmax-mass unit scores, bf16 queries, dec_len <= 32; scratch of mass_scratch_bytes.
+size_t mass_scratch_bytes(const Geom& g, int n_units);
+hipError_t launch_score_units_mass(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                                   const float* ks, int n_units, int unit_log2, float* scores, char* scratch);
 
 hipError_t launch_score_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                                const void* k, const int32_t* page_table, int unit_log2,

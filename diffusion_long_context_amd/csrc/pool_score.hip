@@ -575,6 +575,140 @@ hipError_t launch_score_units_max(hipStream_t s, const Geom& g, const void* q, c
 }
 
 // ------------------------------------------------------------------------------------------------
+// Softmax-mass unit scores: every predicted query q of the group attends to the units' mean keys
+// (key sum / valid tokens of the unit) with the scale 1/sqrt(D), softmax over the head's units;
+// scores[b][g][n] = sum over those queries of the probability of unit n (zeros when nothing is
+// predicted).  Three launches: the scaled logits of every (predicted query, unit) into the scratch
+// z[b][g][G * T][n_units] (same row layout and dot product as the max scorer), one wave per
+// (query, head) for the query's log-sum-exp statistics, and one workgroup per (unit chunk, head)
+// summing the probabilities.
+// ------------------------------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void mass_logits_kernel(const uint16_t* __restrict__ q,
+                                                          const uint64_t* __restrict__ pred_mask,
+                                                          const float* __restrict__ ks, int Hq, int Hkv, int G,
+                                                          int T, int n_units, int unit_log2, int L,
+                                                          float* __restrict__ z) {
+  constexpr int LPR = D / 16;
+  constexpr int kRowsPerWave = 64 / LPR;
+  constexpr int kRowsPerPass = 4 * kRowsPerWave;
+  constexpr int kPasses = kUnitsPerWg / kRowsPerPass;
+  __shared__ __attribute__((aligned(16))) uint16_t stage[8 * 32 * D];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % LPR;
+  const int n0 = blockIdx.x * kUnitsPerWg;
+  const float* ksg = ks + ((int64_t)b * Hkv + g) * n_units * D;
+  float x[kPasses][16];
+  float scale[kPasses];   // 1 / (valid tokens of the unit * sqrt(D))
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+    n = n < n_units ? n : n_units - 1;
+    load16<float>(ksg + (int64_t)n * D + 16 * j, x[ps]);
+    const int first = n << unit_log2;
+    const int cnt = (L - first) < (1 << unit_log2) ? (L - first) : (1 << unit_log2);
+    scale[ps] = 1.f / ((float)cnt * sqrtf((float)D));
+  }
+  QsumGrouped<D, 32, 256, 8> qst;
+  qsum_grouped_issue<D, 32, 256, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
+#pragma unroll
+  for (int k = 0; k < QsumGrouped<D, 32, 256, 8>::PER; ++k)
+    *reinterpret_cast<uint4*>(stage + (k * 256 + threadIdx.x) * 8) = qst.v[k];
+  block_sync_lds();
+  const uint64_t pred = pred_mask[b] & (T >= 64 ? ~0ull : ((1ull << T) - 1ull));
+  float* zg = z + ((int64_t)b * Hkv + g) * (int64_t)G * T * n_units;
+  for (int jh = 0; jh < G; ++jh) {
+    for (uint64_t m = pred; m != 0ull; m &= m - 1ull) {   // uniform: the predicted positions
+      const int pp = __builtin_ctzll(m);
+      const uint4* src = reinterpret_cast<const uint4*>(stage + (jh * 32 + pp) * D + 16 * j);
+      const uint4 a = src[0], c = src[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      float qv[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qv[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        qv[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+      float* zrow = zg + (int64_t)(jh * T + pp) * n_units;
+#pragma unroll
+      for (int ps = 0; ps < kPasses; ++ps) {
+        const float d = row_dot<LPR>(x[ps], qv);
+        const int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
+        if (n < n_units && j == 0) zrow[n] = d * scale[ps];
+      }
+    }
+  }
+}
+
+// One wave per (predicted query slot, head): max and sum of exp over the head's units.
+__global__ __launch_bounds__(64) void mass_stats_kernel(const uint64_t* __restrict__ pred_mask, int Hkv, int G,
+                                                        int T, int n_units, const float* __restrict__ z,
+                                                        float2* __restrict__ stats) {
+  const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;   // slot = jh * T + position
+  const int lane = threadIdx.x;
+  if (!((pred_mask[b] >> (slot % T)) & 1ull)) return;   // uniform
+  const int64_t row = ((int64_t)b * Hkv + g) * G * T + slot;
+  const float* zr = z + row * n_units;
+  float m = -__builtin_inff();
+  for (int n = lane; n < n_units; n += 64) m = fmaxf(m, zr[n]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float sum = 0.f;
+  for (int n = lane; n < n_units; n += 64) sum += expf(zr[n] - m);
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if (lane == 0) stats[row] = make_float2(m, sum);
+}
+
+// One workgroup per (chunk of 256 units, head): each thread sums its unit's probabilities over the
+// predicted queries.
+__global__ __launch_bounds__(256) void mass_sum_kernel(const uint64_t* __restrict__ pred_mask, int Hkv, int G,
+                                                       int T, int n_units, const float* __restrict__ z,
+                                                       const float2* __restrict__ stats, float* __restrict__ scores) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= n_units) return;
+  const uint64_t pred = pred_mask[b] & (T >= 64 ? ~0ull : ((1ull << T) - 1ull));
+  const int64_t row0 = ((int64_t)b * Hkv + g) * G * T;
+  float acc = 0.f;
+  for (int jh = 0; jh < G; ++jh) {
+    for (uint64_t m = pred; m != 0ull; m &= m - 1ull) {   // uniform
+      const int64_t row = row0 + jh * T + __builtin_ctzll(m);
+      const float2 st = stats[row];
+      acc += expf(z[row * n_units + n] - st.x) / st.y;
+    }
+  }
+  scores[((int64_t)b * Hkv + g) * n_units + n] = acc;
+}
+
+size_t mass_scratch_bytes(const Geom& g, int n_units) {
+  const size_t rows = (size_t)g.B * g.Hkv * g.G * g.T;
+  return ((rows * n_units * sizeof(float) + 255) & ~(size_t)255) + rows * sizeof(float2);
+}
+
+hipError_t launch_score_units_mass(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                                   const float* ks, int n_units, int unit_log2, float* scores, char* scratch) {
+  if (n_units == 0) return hipSuccess;
+  if (g.dtype != FDL_BF16 || g.T > 32 || g.G > 8) return hipErrorInvalidValue;
+  const size_t rows = (size_t)g.B * g.Hkv * g.G * g.T;
+  float* z = reinterpret_cast<float*>(scratch);
+  float2* stats = reinterpret_cast<float2*>(scratch + ((rows * n_units * sizeof(float) + 255) & ~(size_t)255));
+  dim3 grid((n_units + kUnitsPerWg - 1) / kUnitsPerWg, g.Hkv, g.B);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  if (g.D == 128)
+    hipLaunchKernelGGL((mass_logits_kernel<128>), grid, dim3(256), 0, s, qq, pred_mask, ks, g.Hq, g.Hkv, g.G, g.T,
+                       n_units, unit_log2, g.L, z);
+  else
+    hipLaunchKernelGGL((mass_logits_kernel<64>), grid, dim3(256), 0, s, qq, pred_mask, ks, g.Hq, g.Hkv, g.G, g.T,
+                       n_units, unit_log2, g.L, z);
+  hipLaunchKernelGGL(mass_stats_kernel, dim3(g.G * g.T, g.Hkv, g.B), dim3(64), 0, s, pred_mask, g.Hkv, g.G, g.T,
+                     n_units, z, stats);
+  hipLaunchKernelGGL(mass_sum_kernel, dim3((n_units + 255) / 256, g.Hkv, g.B), dim3(256), 0, s, pred_mask, g.Hkv,
+                     g.G, g.T, n_units, z, stats, scores);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
 // Level-2 token scores inside candidate units (chunks), keys read through the page table:
 // scores[b][g][c][i] = dot(qs, k[token = cand_idx[b][g][c] * unit + i])
 // ------------------------------------------------------------------------------------------------

@@ -26,7 +26,7 @@ EXPORTED = (
     "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_get_status_bits",
     "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_cache_write", "fdl_predict_queries", "fdl_score_blocks",
-    "fdl_score_blocks_max", "fdl_select_blocks", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
+    "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_unmask", "fdl_decode_steps", "fdl_capture_begin", "fdl_capture_end", "fdl_graph_launch",
     "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end",
 )
@@ -76,6 +76,7 @@ _SIGS = {
     "fdl_score_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _I,
                               ctypes.c_float, _I, _P, _P]),
     "fdl_score_blocks_max": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P]),
+    "fdl_score_blocks_mass": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P]),
     "fdl_select_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I,
                                _P, _P]),
     "fdl_score_select_tokens": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P,
@@ -261,6 +262,15 @@ class Handle:
         B, Hkv = g.batch, g.n_kv_heads
         n_units = -(-g.ctx_len // unit_tokens)
         self._check(self.lib.fdl_score_blocks_max(
+            self.h, ctypes.byref(g.c()), _ptr(q, B * g.n_q_heads * g.dec_len * g.head_dim * g.elem, "q"),
+            _ptr(pred_mask, 8 * B, "pred_mask"), _ptr(ks, 4 * B * Hkv * n_units * g.head_dim, "ks"), unit_tokens,
+            _ptr(scores, 4 * B * Hkv * n_units, "scores")))
+
+    def fdl_score_blocks_mass(self, g: Geom, q, pred_mask, ks, unit_tokens: int, scores):
+        self.sync_stream()
+        B, Hkv = g.batch, g.n_kv_heads
+        n_units = -(-g.ctx_len // unit_tokens)
+        self._check(self.lib.fdl_score_blocks_mass(
             self.h, ctypes.byref(g.c()), _ptr(q, B * g.n_q_heads * g.dec_len * g.head_dim * g.elem, "q"),
             _ptr(pred_mask, 8 * B, "pred_mask"), _ptr(ks, 4 * B * Hkv * n_units * g.head_dim, "ks"), unit_tokens,
             _ptr(scores, 4 * B * Hkv * n_units, "scores")))

@@ -54,14 +54,18 @@ class FocusStep:
 
     def score(self, q, ks, k_cache=None, k_dec=None, detect_sinks=False, scorer: str = "sum"):
         """scorer "sum": the summed predicted query against each pooled key; "max": the best single
-        predicted query (fdl_score_blocks_max; sinks, when asked for, still by fdl_score_blocks)."""
-        if scorer == "max":
+        predicted query (fdl_score_blocks_max); "mass": the softmax mass over the units' mean keys
+        (fdl_score_blocks_mass).  Sinks, when asked for, are detected by fdl_score_blocks."""
+        if scorer not in ("sum", "max", "mass"):
+            raise ValueError(f"unknown scorer {scorer!r}")
+        if scorer != "sum":
             if detect_sinks:   # the sink pass also writes summed scores, which the max scores replace
                 self.h.fdl_score_blocks(self.g, q, self.pred_mask, ks, self.g.kv_block, self.scores,
                                         k_cache=k_cache, k_dec=k_dec, detect_sinks=True,
                                         sink_tau=self.fp.sink_tau, max_sinks=self.fp.max_sinks,
                                         sink_pos=self.sink_pos, n_sinks=self.n_sinks)
-            self.h.fdl_score_blocks_max(self.g, q, self.pred_mask, ks, self.g.kv_block, self.scores)
+            score = self.h.fdl_score_blocks_max if scorer == "max" else self.h.fdl_score_blocks_mass
+            score(self.g, q, self.pred_mask, ks, self.g.kv_block, self.scores)
             return
         self.h.fdl_score_blocks(self.g, q, self.pred_mask, ks, self.g.kv_block, self.scores,
                                 k_cache=k_cache, k_dec=k_dec, detect_sinks=detect_sinks,

@@ -185,6 +185,20 @@ fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* g, const void* q, cons
 fdl_status fdl_score_blocks_max(fdl_handle h, const fdl_geom* g, const void* q, const uint64_t* pred_mask,
                                 const float* ks, int32_t unit_tokens, float* scores);
 
+/* Softmax-mass scoring, a third reading of how the predicted queries estimate attention
+ * importance ([FA] Elamur "Summary"): every predicted query of the KV head's q-head group attends to
+ * the units' mean keys (ks / valid tokens of the unit; a partial last unit counts its valid tokens)
+ * with the scale 1/sqrt(head_dim), a softmax over the head's units; a unit's score is the
+ * probability mass it receives summed over those queries (zeros when nothing is predicted, so each
+ * head's scores sum to G * |predicted positions|).  float32 arithmetic with expf: scores agree with
+ * a float64 evaluation to rounding, and units whose masses differ by less than that may rank
+ * either way.  scores [B][Hkv][n_units] from ks (fdl_pool_keys output with the same unit_tokens).
+ * bf16 queries with dec_len <= 32 only (FDL_EUNSUPPORTED otherwise); uses
+ * B * Hkv * G * dec_len * (4 * n_units + 8) bytes of workspace (FDL_ENOMEM beyond it).  Its
+ * scores go to fdl_select_blocks like those of fdl_score_blocks. */
+fdl_status fdl_score_blocks_mass(fdl_handle h, const fdl_geom* g, const void* q, const uint64_t* pred_mask,
+                                 const float* ks, int32_t unit_tokens, float* scores);
+
 /* ---- step 3: keep sinks + top-K units; reuse sinks across layers ---------------------------- */
 
 /* [FA], [FS]: sinks are always kept and their locations are reused in deeper layers; the rest of

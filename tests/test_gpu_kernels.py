@@ -11,7 +11,7 @@ from gpu_util import assert_close, dev, host, out_buffer, out_to_f64, require_gp
 from oracle.attention import attend, blocks_to_tokens
 from oracle.pipeline import focus_layer_step
 from oracle.predictor import predict_positions
-from oracle.scoring import pool_keys, query_sum, unit_scores, unit_scores_max
+from oracle.scoring import pool_keys, query_sum, unit_scores, unit_scores_mass, unit_scores_max
 from oracle.selection import select_blocks
 from synth import get_config
 from synth.gen import make_single
@@ -166,6 +166,62 @@ def test_scores_max_bit_exact(h, kw, bits):
     for b in range(cfg.batch):
         for gg in range(cfg.n_kv_heads):
             assert host(sel)[b, gg, :host(nsel)[b, gg]].tolist() == ws[b][gg].tolist()
+
+
+@pytest.mark.parametrize("kw,bits", [
+    (dict(n_q_heads=4, n_kv_heads=4, ctx_len=3000), None),
+    (dict(n_q_heads=28, n_kv_heads=4, ctx_len=4096), None),
+    (dict(n_q_heads=8, n_kv_heads=2, ctx_len=2000, head_dim=64, dec_len=20), None),
+    (dict(n_q_heads=4, n_kv_heads=2, ctx_len=1000), [0]),
+    (dict(n_q_heads=4, n_kv_heads=1, ctx_len=1000), [(1 << 32) - 1]),
+    (dict(n_q_heads=2, n_kv_heads=2, ctx_len=32768), None),
+], ids=["mha", "gqa7", "gqa4-d64-T20", "nothing-predicted", "all-predicted", "32k"])
+def test_scores_mass(h, kw, bits):
+    """Softmax-mass scores against the float64 oracle.  float32 logits of 64- and 128-term dot
+    products carry a relative error of a few 1e-6 of the logit's terms, which moves each
+    probability by about as much relatively: |gpu - oracle| <= 1e-4 |oracle| + 1e-6.  The selection
+    made from the GPU scores is a valid top-k of the oracle's (no unselected unit beats a selected
+    one by more than that tolerance) and equals the oracle's own where its k-th and (k+1)-th scores
+    are further apart."""
+    cfg = _small_bf16(**kw)
+    x = make_single(cfg)
+    g = _geom(cfg)
+    if bits is None:
+        bits, _ = predict_positions(x["prev_conf"], x["masked"], cfg.top_k_pos, cfg.window)
+    bits = _u64(bits)
+    n_units = -(-cfg.ctx_len // 64)
+    ks = torch.zeros(cfg.batch, cfg.n_kv_heads, n_units, cfg.head_dim, dtype=torch.float32, device="cuda")
+    h.fdl_pool_keys(g, dev(x["k"]), None, 64, ks)
+    sc = torch.full((cfg.batch, cfg.n_kv_heads, n_units), 7.0, dtype=torch.float32, device="cuda")
+    h.fdl_score_blocks_mass(g, dev(x["q"]), dev(bits), ks, 64, sc)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    want = unit_scores_mass(x["q"], bits, pool_keys(x["k"], 64), cfg.n_kv_heads, 64, cfg.ctx_len)
+    got = host(sc).astype(np.float64)
+    err = np.abs(got - want) - (1e-4 * np.abs(want) + 1e-6)
+    assert err.max() <= 0, float(err.max())
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    for b in range(cfg.batch):
+        npred = bin(int(bits[b])).count("1")
+        assert np.allclose(got[b].sum(axis=1), G * npred, rtol=1e-4, atol=1e-6)
+    k = min(8, n_units)
+    sel = torch.zeros(cfg.batch, cfg.n_kv_heads, k, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros(cfg.batch, cfg.n_kv_heads, dtype=torch.int32, device="cuda")
+    h.fdl_select_blocks(g, sc, n_units, 64, None, None, 1, k, k, sel, nsel)
+    torch.cuda.synchronize()
+    ws = select_blocks(want.astype(np.float32), np.full((cfg.batch, 1), -1, np.int32),
+                       np.zeros(cfg.batch, np.int32), 64, k)
+    for b in range(cfg.batch):
+        for gg in range(cfg.n_kv_heads):
+            chosen = host(sel)[b, gg, :host(nsel)[b, gg]].tolist()
+            assert len(chosen) == k and chosen == sorted(set(chosen))
+            w = want[b, gg]
+            tol = 2e-4 * np.abs(w).max() + 2e-6
+            rest = np.delete(w, chosen)
+            assert rest.size == 0 or w[chosen].min() >= rest.max() - tol, (b, gg)
+            srt = np.sort(w)[::-1]
+            if k < n_units and srt[k - 1] - srt[k] > tol:
+                assert chosen == ws[b][gg].tolist(), (b, gg)
 
 
 def test_scores_all_positions_predicted(h):
