@@ -8,7 +8,9 @@ attention anchor.
 Readings:
   * chunk score = pinned dot product of the predicted-query sum with the chunk's key sum (a tree over
     all of the chunk's tokens in logical order, anchor included);
-  * the top-K chunks are chosen per KV head (ties to the lower chunk);
+  * the top-K chunks are chosen per KV head (ties to the lower chunk); the other reading, one chunk
+    set per sequence shared by all its KV heads, ranks chunks by their scores summed over the KV
+    heads (pinned float32 tree over the heads, zero-padded to a power of two), same tie rule;
   * inside a chosen chunk its anchor (token 0) is always kept and the top ceil(frac * chunk) of the
     remaining tokens by token score (ties to the lower token) are added;
   * unchosen chunks contribute nothing; attention then runs over the kept tokens plus the block's
@@ -18,6 +20,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .fp32tree import tree_sum
 from .scoring import pool_keys, token_scores, unit_scores
 from .selection import topk_indices
 
@@ -32,6 +35,18 @@ def select_chunks(qs, k_logical, chunk_tokens: int, top_k_chunks: int):
         for g in range(H):
             chosen[b, g] = sorted(topk_indices(sc[b, g], top_k_chunks))
     return sc, chosen
+
+
+def select_chunks_shared(qs, k_logical, chunk_tokens: int, top_k_chunks: int):
+    """Per-sequence reading -> (chunk scores [B][Hkv][n_chunks] f32, summed over the heads [B][n_chunks]
+    f32, chosen [B][Hkv][top_k] ascending int32, the same row for every head)."""
+    sc = unit_scores(qs, pool_keys(k_logical, chunk_tokens))
+    seq = tree_sum(sc, axis=1)
+    B, H, _ = sc.shape
+    chosen = np.zeros((B, H, top_k_chunks), dtype=np.int32)
+    for b in range(B):
+        chosen[b, :] = sorted(topk_indices(seq[b], top_k_chunks))
+    return sc, seq, chosen
 
 
 def select_tokens(qs, k_logical, chosen, chunk_tokens: int, keep: int):

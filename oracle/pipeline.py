@@ -14,7 +14,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import attend, blocks_to_tokens
-from .chunked import select_chunks, select_tokens
+from .chunked import select_chunks, select_chunks_shared, select_tokens
 from .predictor import predict_positions
 from .scoring import gather_logical, pool_keys, query_sum, unit_scores
 from .selection import select_blocks
@@ -56,15 +56,20 @@ def focus_layer_step(p, x: dict, mode: str, sinks=None, ks=None, with_output: bo
     return r
 
 
-def chunked_layer_step(p, x: dict, with_output: bool = True) -> dict:
-    """Chunked, paged workload: x holds q, k_pool, v_pool, page_table, k_dec, v_dec, prev_conf, masked."""
+def chunked_layer_step(p, x: dict, with_output: bool = True, per_sequence: bool = False) -> dict:
+    """Chunked, paged workload: x holds q, k_pool, v_pool, page_table, k_dec, v_dec, prev_conf, masked.
+    per_sequence: one chunk set per sequence, from the chunk scores summed over the KV heads."""
     r: dict = {}
     bits, npred = predict_positions(x.get("prev_conf"), x["masked"], p.top_k_pos, p.window)
     r["pred_mask"], r["n_pred"] = bits, npred
     kl = gather_logical(x["k_pool"], x["page_table"], p.page_tokens)
     qs = query_sum(x["q"], bits, p.n_kv_heads)
     r["qs"] = qs
-    r["chunk_scores"], r["chunks"] = select_chunks(qs, kl, p.chunk_tokens, p.top_k_chunks)
+    if per_sequence:
+        r["chunk_scores"], r["seq_chunk_scores"], r["chunks"] = select_chunks_shared(qs, kl, p.chunk_tokens,
+                                                                                     p.top_k_chunks)
+    else:
+        r["chunk_scores"], r["chunks"] = select_chunks(qs, kl, p.chunk_tokens, p.top_k_chunks)
     r["token_scores"], r["tokens"] = select_tokens(qs, kl, r["chunks"], p.chunk_tokens,
                                                    p.tokens_per_chunk_kept)
     if with_output:
