@@ -459,15 +459,16 @@ fdl_status fdl_score_blocks_mass(fdl_handle h, const fdl_geom* gp, const void* q
                     "score_units_mass launch");
 }
 
-fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* gp, const float* scores, int32_t n_units,
-                             int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
-                             int32_t max_sinks, const int32_t* cand_idx, int32_t n_cand,
-                             int32_t top_k, int32_t force_first, int32_t max_sel, int32_t* sel_idx,
-                             int32_t* n_sel) {
+static fdl_status select_blocks_impl(fdl_handle h, const fdl_geom* gp, const float* scores, int32_t n_units,
+                                     int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
+                                     int32_t max_sinks, const int32_t* cand_idx, int32_t n_cand,
+                                     int32_t top_k, int32_t force_first, int32_t max_sel, int32_t* sel_idx,
+                                     int32_t* n_sel, int shared) {
   if (!h) return FDL_EINVAL;
   Geom g;
   fdl_status st = check_geom(h, gp, g);
   if (st != FDL_OK) return st;
+  if (shared && g.Hkv > 32) return fail(h, FDL_EUNSUPPORTED, "per-sequence selection takes at most 32 KV heads");
   if (!scores || !sel_idx || !n_sel) return fail(h, FDL_EINVAL, "scores, sel_idx and n_sel must be non-NULL");
   if (!is_pow2(unit_tokens) || unit_tokens > 8192)
     return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 8192]");
@@ -488,8 +489,28 @@ fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* gp, const float* scor
     if (need > n_units) need = n_units;
     if (need > max_sel) return fail(h, FDL_EINVAL, "max_sel must cover min(n_units, max_sinks + top_k)");
   }
-  return run_select(h, g, scores, n_units, ilog2(unit_tokens), sink_pos, n_sinks, max_sinks, cand_idx,
-                    n_cand, top_k, force_first ? 1 : 0, max_sel, sel_idx, n_sel);
+  ProfScope ps(h, FDL_PROF_SELECT);
+  return hip_status(h, fdl::launch_select(h->stream, g, scores, n_units, ilog2(unit_tokens), sink_pos, n_sinks,
+                                          max_sinks, cand_idx, n_cand, top_k, force_first ? 1 : 0, max_sel,
+                                          sel_idx, n_sel, h->status, shared),
+                    "select launch");
+}
+
+fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* gp, const float* scores, int32_t n_units,
+                             int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
+                             int32_t max_sinks, const int32_t* cand_idx, int32_t n_cand,
+                             int32_t top_k, int32_t force_first, int32_t max_sel, int32_t* sel_idx,
+                             int32_t* n_sel) {
+  return select_blocks_impl(h, gp, scores, n_units, unit_tokens, sink_pos, n_sinks, max_sinks, cand_idx, n_cand,
+                            top_k, force_first, max_sel, sel_idx, n_sel, 0);
+}
+
+fdl_status fdl_select_blocks_shared(fdl_handle h, const fdl_geom* gp, const float* scores, int32_t n_units,
+                                    int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
+                                    int32_t max_sinks, int32_t top_k, int32_t max_sel, int32_t* sel_idx,
+                                    int32_t* n_sel) {
+  return select_blocks_impl(h, gp, scores, n_units, unit_tokens, sink_pos, n_sinks, max_sinks, nullptr, 0, top_k,
+                            0, max_sel, sel_idx, n_sel, 1);
 }
 
 fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* gp, const void* q, const uint64_t* pred_mask,

@@ -144,7 +144,7 @@ hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int 
                          int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,
                          int max_sinks, const int32_t* cand_idx, int n_cand, int top_k,
                          int force_first, int max_sel, int32_t* sel_idx, int32_t* n_sel,
-                         uint32_t* status);
+                         uint32_t* status, int shared = 0);
 
 // Attention.  dense != 0 ignores sel_idx / n_sel.
 size_t attn_scratch_bytes(const Geom& g, int n_splits);

@@ -18,11 +18,25 @@ constexpr int kSelThreads = 256;
 constexpr int kMaxSelN = 8192;
 constexpr int kSelPerThread = kMaxSelN / kSelThreads;
 
+// Level 1, one selection per sequence: unit i's key is that of its scores summed over the Hkv <= 32
+// heads with the adjacent-pair tree (padded with +0 to 32 leaves, which changes no sum but the sign
+// of a zero, and the keys take -0 as +0).
+__device__ __forceinline__ float heads_tree_sum(const float* __restrict__ s, int H, int stride, int i) {
+  float v[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) v[k] = k < H ? s[(int64_t)k * stride + i] : 0.f;
+#pragma unroll
+  for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+    for (int j = 0; j < w; ++j) v[j] = v[2 * j] + v[2 * j + 1];
+  return v[0];
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int n_units, int unit_log2, const int32_t* __restrict__ sink_pos,
     const int32_t* __restrict__ n_sinks, int max_sinks, const int32_t* __restrict__ cand_idx,
     int n_cand, int top_k, int force_first, int max_sel, int Hkv, int32_t* __restrict__ sel_idx,
-    int32_t* __restrict__ n_sel, uint32_t* __restrict__ status) {
+    int32_t* __restrict__ n_sel, uint32_t* __restrict__ status, int shared) {
   __shared__ uint32_t keys[kMaxSelN];
   __shared__ uint32_t forced[kMaxSelN / 32];
   __shared__ int hist[4 * 256];
@@ -35,7 +49,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int64_t seg = (int64_t)b * Hkv + g;
   const float* sc = level2 ? scores + (seg * n_cand + c) * (int64_t)n : scores + seg * n;
 
-  for (int i = tid; i < n; i += kSelThreads) keys[i] = order_key(sc[i]);
+  if (shared && !level2) {   // uniform; every head's workgroup derives the same keys
+    const float* sb = scores + (int64_t)b * Hkv * n;
+    for (int i = tid; i < n; i += kSelThreads) keys[i] = order_key(heads_tree_sum(sb, Hkv, n, i));
+  } else {
+    for (int i = tid; i < n; i += kSelThreads) keys[i] = order_key(sc[i]);
+  }
   for (int i = tid; i < (n + 31) / 32; i += kSelThreads) forced[i] = 0u;
   __syncthreads();
   if (level2) {
@@ -88,12 +107,12 @@ hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int 
                          int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,
                          int max_sinks, const int32_t* cand_idx, int n_cand, int top_k,
                          int force_first, int max_sel, int32_t* sel_idx, int32_t* n_sel,
-                         uint32_t* status) {
+                         uint32_t* status, int shared) {
   dim3 grid(cand_idx ? n_cand : 1, g.Hkv, g.B);
   if (grid.x == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, s, scores, n_units, unit_log2,
                      sink_pos, n_sinks, max_sinks, cand_idx, n_cand, top_k, force_first, max_sel,
-                     g.Hkv, sel_idx, n_sel, status);
+                     g.Hkv, sel_idx, n_sel, status, shared);
   return hipGetLastError();
 }
 

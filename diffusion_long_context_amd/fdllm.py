@@ -26,7 +26,7 @@ EXPORTED = (
     "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_get_status_bits",
     "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_cache_write", "fdl_predict_queries", "fdl_score_blocks",
-    "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
+    "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_select_blocks_shared", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_unmask", "fdl_decode_steps", "fdl_capture_begin", "fdl_capture_end", "fdl_graph_launch",
     "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end",
 )
@@ -79,6 +79,7 @@ _SIGS = {
     "fdl_score_blocks_mass": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P]),
     "fdl_select_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I,
                                _P, _P]),
+    "fdl_select_blocks_shared": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _I, _I, _P, _P]),
     "fdl_score_select_tokens": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P,
                                      _P]),
     "fdl_sparse_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
@@ -285,6 +286,15 @@ class Handle:
             self.h, ctypes.byref(g.c()), _ptr(scores, sbytes, "scores"), n_units, unit_tokens,
             _ptr(sink_pos, 4 * B * max_sinks, "sink_pos"), _ptr(n_sinks, 4 * B, "n_sinks"), max_sinks,
             _ptr(cand_idx, 4 * B * Hkv * n_cand, "cand_idx"), n_cand, top_k, 1 if force_first else 0,
+            max_sel, _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel")))
+
+    def fdl_select_blocks_shared(self, g: Geom, scores, n_units: int, unit_tokens: int, sink_pos, n_sinks,
+                                 max_sinks: int, top_k: int, max_sel: int, sel_idx, n_sel):
+        self.sync_stream()
+        B, Hkv = g.batch, g.n_kv_heads
+        self._check(self.lib.fdl_select_blocks_shared(
+            self.h, ctypes.byref(g.c()), _ptr(scores, 4 * B * Hkv * n_units, "scores"), n_units, unit_tokens,
+            _ptr(sink_pos, 4 * B * max_sinks, "sink_pos"), _ptr(n_sinks, 4 * B, "n_sinks"), max_sinks, top_k,
             max_sel, _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel")))
 
     def fdl_score_select_tokens(self, g: Geom, q, pred_mask, k_cache, page_table, unit_tokens: int, cand_idx,

@@ -137,13 +137,15 @@ class ChunkedStep:
         self.h.fdl_predict_queries(self.g.batch, self.g.dec_len, prev_conf, masked, self.cp.top_k_pos,
                                    self.cp.window, self.pred_mask, self.n_pred)
 
-    def select(self, q, k_pool, page_table, cs, separate: bool = False):
-        """Level 1 (chunk scores, top chunks), then level 2 (token scores inside them, anchor + top
-        tokens) -- as one call, or with separate=True as the score and select calls."""
+    def select(self, q, k_pool, page_table, cs, separate: bool = False, per_sequence: bool = False):
+        """Level 1 (chunk scores, top chunks per KV head, or with per_sequence=True one chunk set per
+        sequence from the scores summed over its KV heads), then level 2 (token scores inside them,
+        anchor + top tokens) -- as one call, or with separate=True as the score and select calls."""
         g, cp = self.g, self.cp
         self.h.fdl_score_blocks(g, q, self.pred_mask, cs, cp.chunk_tokens, self.chunk_scores)
-        self.h.fdl_select_blocks(g, self.chunk_scores, self.n_chunks, cp.chunk_tokens, None, None, 1,
-                                 cp.top_k_chunks, cp.top_k_chunks, self.chunks, self.n_chunks_sel)
+        select = self.h.fdl_select_blocks_shared if per_sequence else self.h.fdl_select_blocks
+        select(g, self.chunk_scores, self.n_chunks, cp.chunk_tokens, None, None, 1, cp.top_k_chunks, cp.top_k_chunks,
+               self.chunks, self.n_chunks_sel)
         if not separate:
             self.h.fdl_score_select_tokens(g, q, self.pred_mask, k_pool, page_table, cp.chunk_tokens, self.chunks,
                                            cp.top_k_chunks, cp.keep_tokens, self.max_tok, self.token_scores,
@@ -160,8 +162,9 @@ class ChunkedStep:
         self.h.fdl_sparse_attn(self.g, q, k_pool, v_pool, k_dec, v_dec, page_table, self.tokens,
                                self.n_tokens, self.max_tok, 1, out)
 
-    def run(self, q, k_pool, v_pool, page_table, k_dec, v_dec, cs, out, separate: bool = False):
-        self.select(q, k_pool, page_table, cs, separate)
+    def run(self, q, k_pool, v_pool, page_table, k_dec, v_dec, cs, out, separate: bool = False,
+            per_sequence: bool = False):
+        self.select(q, k_pool, page_table, cs, separate, per_sequence)
         self.attend(q, k_pool, v_pool, page_table, k_dec, v_dec, out)
 
 

@@ -222,6 +222,16 @@ fdl_status fdl_select_blocks(fdl_handle h, const fdl_geom* g, const float* score
                              int32_t top_k, int32_t force_first, int32_t max_sel, int32_t* sel_idx,
                              int32_t* n_sel);
 
+/* Level 1 with one selection per sequence, the other reading of [PA]'s "top-K most relevant chunks"
+ * (per KV head above): unit i ranks by its scores summed over the sequence's KV heads (float32
+ * adjacent-pair tree over the heads in head order, zero-padded), with the same forced units, ranking
+ * and count as fdl_select_blocks level 1; every head's row of sel_idx / n_sel gets the same list.
+ * n_kv_heads <= 32 (FDL_EUNSUPPORTED beyond); arguments and errors as fdl_select_blocks level 1. */
+fdl_status fdl_select_blocks_shared(fdl_handle h, const fdl_geom* g, const float* scores, int32_t n_units,
+                                    int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
+                                    int32_t max_sinks, int32_t top_k, int32_t max_sel, int32_t* sel_idx,
+                                    int32_t* n_sel);
+
 /* [PA] level 2 in one call: fdl_score_blocks at level 2 (token scores inside the n_cand candidate
  * units, written to scores [B][Hkv][n_cand][unit_tokens]) followed by fdl_select_blocks at level 2
  * with force_first = 1 (each unit's token 0 forced, plus the top `top_k` of its other tokens) --

@@ -56,7 +56,7 @@ def _check_layer(cfg, got, want, margin=None):
     assert_close(got["out"], want["out"], cfg.name)
 
 
-def _chunked(h, cfg, x):
+def _chunked(h, cfg, x, per_sequence=False):
     from diffusion_long_context_amd.step import ChunkedStep, ChunkParams, geom_for
     g = geom_for(cfg)
     cs_ = ChunkedStep(h, g, ChunkParams(cfg.top_k_pos, cfg.window, cfg.chunk_tokens, cfg.top_k_chunks,
@@ -67,7 +67,8 @@ def _chunked(h, cfg, x):
     cs = cs_.new_chunk_sums()
     cs_.pool(t["k_pool"], t["page_table"], cs)
     out = out_buffer(cfg)
-    cs_.run(t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["k_dec"], t["v_dec"], cs, out)
+    cs_.run(t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["k_dec"], t["v_dec"], cs, out,
+            per_sequence=per_sequence)
     torch.cuda.synchronize()
     assert h.fdl_get_status() == 0
     return {"chunk_scores": host(cs_.chunk_scores), "chunks": host(cs_.chunks),

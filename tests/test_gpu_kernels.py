@@ -224,6 +224,45 @@ def test_scores_mass(h, kw, bits):
                 assert chosen == ws[b][gg].tolist(), (b, gg)
 
 
+@pytest.mark.parametrize("Hkv,n,k,sinks", [(1, 16, 4, False), (3, 100, 10, True), (8, 700, 40, True),
+                                           (32, 16, 4, False), (5, 3000, 64, True)],
+                         ids=["h1", "h3-sinks", "h8-sinks-700", "h32", "h5-radix"])
+def test_select_shared_bit_exact(h, Hkv, n, k, sinks):
+    """One selection per sequence from the scores summed over the KV heads: every head's row equals
+    the oracle's selection on the pinned head sum (ties, signed zeros and NaN included)."""
+    from oracle.fp32tree import tree_sum
+    from diffusion_long_context_amd.step import geom_for
+    rng = np.random.default_rng(Hkv * 1000 + n)
+    B = 3
+    cfg = _small_bf16(batch=B, n_q_heads=Hkv, n_kv_heads=Hkv, ctx_len=n * 64)
+    g = geom_for(cfg)
+    pool = np.array([0.5, -0.0, 0.0, np.nan, 1.0, -1.0], np.float32)
+    sc = np.where(rng.random((B, Hkv, n)) < 0.3, rng.choice(pool, (B, Hkv, n)),
+                  rng.standard_normal((B, Hkv, n)).astype(np.float32)).astype(np.float32)
+    sc[0, :, : n // 2] = 0.25        # exact ties across a whole half
+    max_sinks = 4
+    sp = np.full((B, max_sinks), -1, np.int32)
+    ns = np.zeros(B, np.int32)
+    if sinks:
+        for b in range(B):
+            pos = sorted(rng.choice(n * 64, 3, replace=False).tolist())
+            sp[b, :3], ns[b] = pos, 3
+    max_sel = max_sinks + k
+    sel = torch.full((B, Hkv, max_sel), -7, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    h.fdl_select_blocks_shared(g, dev(sc), n, 64, dev(sp) if sinks else None, dev(ns) if sinks else None,
+                               max_sinks, k, max_sel, sel, nsel)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    seq = tree_sum(sc, axis=1)[:, None, :]
+    want = select_blocks(seq, sp if sinks else None, ns, 64, k)
+    for b in range(B):
+        w = want[b][0].tolist()
+        for gg in range(Hkv):
+            assert int(host(nsel)[b, gg]) == len(w)
+            assert host(sel)[b, gg, :len(w)].tolist() == w, (b, gg)
+
+
 def test_scores_all_positions_predicted(h):
     cfg = _small_bf16(n_q_heads=8, n_kv_heads=1, ctx_len=640, dec_len=20)
     x = make_single(cfg)

@@ -100,6 +100,21 @@ def test_level2_one_call_equals_two_calls(h, kw):
     assert np.array_equal(res[0][2], res[1][2])
 
 
+@pytest.mark.parametrize("kw", [dict(batch=2, n_q_heads=4, n_kv_heads=4, ctx_len=4096, chunk_tokens=512),
+                                dict(batch=2, n_q_heads=8, n_kv_heads=2, ctx_len=8192, chunk_tokens=1024)],
+                         ids=["mha", "gqa4"])
+def test_chunked_per_sequence(h, kw):
+    """The per-sequence reading of the chunk selection through the whole chunked step: chunk scores,
+    the shared chunk set, token scores, kept tokens and the output against the oracle."""
+    cfg = get_config(4).with_(**kw)
+    x = make_single(cfg)
+    got = _chunked(h, cfg, x, per_sequence=True)
+    want = chunked_layer_step(cfg, x, per_sequence=True)
+    _check_chunked(cfg, got, want)
+    for b in range(cfg.batch):
+        assert all(got["chunks"][b, g].tolist() == got["chunks"][b, 0].tolist() for g in range(cfg.n_kv_heads))
+
+
 def test_chunked_grouped_query(h):
     cfg = get_config(4).with_(batch=2, n_q_heads=8, n_kv_heads=2, ctx_len=4096, chunk_tokens=512)
     x = make_single(cfg)
