@@ -17,11 +17,12 @@ from .attention import attend, blocks_to_tokens
 from .chunked import select_chunks, select_chunks_shared, select_tokens
 from .predictor import predict_positions
 from .scoring import gather_logical, pool_keys, query_sum, unit_scores
-from .selection import select_blocks
+from .selection import select_blocks, select_token_sinks
 from .sinks import detect_sinks
 
 
-def focus_layer_step(p, x: dict, mode: str, sinks=None, ks=None, with_output: bool = True) -> dict:
+def focus_layer_step(p, x: dict, mode: str, sinks=None, ks=None, with_output: bool = True,
+                     sink_tokens: bool = False) -> dict:
     """mode: "dense" (full attention), "source" (detect sinks here) or "reuse" (take ``sinks``).
 
     x holds q, k, v, k_dec, v_dec, prev_conf (or None), masked.  ``sinks`` = (sink_pos, n_sinks) from
@@ -48,6 +49,13 @@ def focus_layer_step(p, x: dict, mode: str, sinks=None, ks=None, with_output: bo
         r["sink_pos"], r["n_sinks"] = pos, n
     else:
         raise ValueError(mode)
+    if sink_tokens:   # token-granular sink retention: sinks as tokens, top-K of all blocks
+        toks = select_token_sinks(r["scores"], r["sink_pos"], r["n_sinks"], p.kv_block, p.top_k_blocks,
+                                  p.ctx_len)
+        r["tokens"] = toks
+        if with_output:
+            r["out"] = attend(x["q"], x["k"], x["v"], x["k_dec"], x["v_dec"], toks)
+        return r
     sel = select_blocks(r["scores"], r["sink_pos"], r["n_sinks"], p.kv_block, p.top_k_blocks)
     r["sel"] = sel
     if with_output:

@@ -8,7 +8,9 @@ Readings:
   * every block holding a sink token is forced in; K counts the other (non-forced) blocks;
   * ranking is by score, highest first, with -0 equal to +0, NaN below everything, and ties to the
     lower index; K larger than what is left keeps everything;
-  * the kept set is reported in ascending order.
+  * the kept set is reported in ascending order;
+  * the other reading of sink retention (token granularity): the sink tokens themselves are kept and
+    the top-K blocks are chosen among all blocks.
 """
 from __future__ import annotations
 
@@ -35,6 +37,27 @@ def select_units(scores, forced, k: int) -> np.ndarray:
 
 def sink_blocks(sink_pos, n_sinks: int, kv_block: int) -> list[int]:
     return sorted(set(int(s) // kv_block for s in list(sink_pos)[: int(n_sinks)]))
+
+
+def select_token_sinks(scores, sink_pos, n_sinks, kv_block: int, k: int, ctx_len: int):
+    """Token-granular sink retention, the other reading of how sinks are kept: the top k blocks of
+    all blocks (sink blocks compete like the others), and the sink tokens themselves.  -> list over
+    b of list over g of the ascending cached-token ids attended (each id once)."""
+    scores = np.asarray(scores)
+    B, H, _ = scores.shape
+    out = []
+    for b in range(B):
+        sinks = set()
+        if sink_pos is not None:
+            sinks = {int(t) for t in list(sink_pos[b])[: int(n_sinks[b])] if 0 <= int(t) < ctx_len}
+        row = []
+        for g in range(H):
+            toks = set(sinks)
+            for blk in select_units(scores[b, g], [], k):
+                toks.update(range(int(blk) * kv_block, min((int(blk) + 1) * kv_block, ctx_len)))
+            row.append(np.array(sorted(toks), dtype=np.int32))
+        out.append(row)
+    return out
 
 
 def select_blocks(scores, sink_pos, n_sinks, kv_block: int, k: int):

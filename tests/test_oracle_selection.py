@@ -89,3 +89,37 @@ def test_invariants():
 def test_topk_excludes():
     s = np.array([5, 4, 3, 2, 1], np.float32)
     assert topk_indices(s, 2, exclude=[0]) == [1, 2]
+
+
+# ---- token-granular sink retention ------------------------------------------------------------
+
+def test_token_sinks_worked_case():
+    """Blocks of 4 tokens, 5 blocks, L = 18 (the last block holds 2 tokens); scores [9, 1, 5, 7, 3],
+    sinks at tokens 0, 1 and 9, K = 2.  The top 2 blocks of all five are 0 and 3 (tokens 0-3 and
+    12-15); the sinks add token 9 only (0 and 1 are inside block 0): 9 tokens.  With block-granular
+    retention block 2 (tokens 8-11) would be forced in and K = 2 would pick blocks 3 and 2."""
+    from oracle.selection import select_token_sinks
+    sc = np.array([[[9, 1, 5, 7, 3]]], np.float32)
+    got = select_token_sinks(sc, np.array([[0, 1, 9, -1]]), np.array([3]), 4, 2, 18)
+    assert got[0][0].tolist() == [0, 1, 2, 3, 9, 12, 13, 14, 15]
+    got = select_token_sinks(sc, np.array([[17, 16]]), np.array([2]), 4, 1, 18)
+    assert got[0][0].tolist() == [0, 1, 2, 3, 16, 17]     # sinks inside the partial last block
+    got = select_token_sinks(sc, None, None, 4, 9, 18)
+    assert got[0][0].tolist() == list(range(18))           # K above the block count: everything
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_token_sinks_brute_force(seed):
+    """Against an independent formulation: the union of the sink tokens with the tokens of the k
+    blocks that beat all others (brute force over k-subsets: best score sum, ties to the
+    lexicographically smallest subset, distinct integer scores so the order is total)."""
+    from oracle.selection import select_token_sinks
+    rng = np.random.default_rng(seed)
+    n_blk, bt, k = 7, 8, 3
+    L = n_blk * bt - int(rng.integers(0, bt))
+    sc = rng.permutation(n_blk).astype(np.float32)[None, None, :]
+    sinks = rng.choice(L, 3, replace=False)
+    best = max(itertools.combinations(range(n_blk), k), key=lambda c: (sum(sc[0, 0, list(c)]), [-i for i in c]))
+    want = sorted(set(sinks.tolist()) | {t for blk in best for t in range(blk * bt, min((blk + 1) * bt, L))})
+    got = select_token_sinks(sc, sinks[None, :], np.array([3]), bt, k, L)
+    assert got[0][0].tolist() == want
