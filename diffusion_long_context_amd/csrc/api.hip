@@ -513,6 +513,28 @@ fdl_status fdl_select_blocks_shared(fdl_handle h, const fdl_geom* gp, const floa
                             0, max_sel, sel_idx, n_sel, 1);
 }
 
+fdl_status fdl_expand_tokens(fdl_handle h, const fdl_geom* gp, const int32_t* sel_idx, const int32_t* n_sel,
+                             int32_t max_sel, int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
+                             int32_t max_sinks, int32_t* tok_idx, int32_t* n_tok, int32_t max_tok) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!sel_idx || !n_sel || !tok_idx || !n_tok) return fail(h, FDL_EINVAL, "sel_idx, n_sel, tok_idx and n_tok must be non-NULL");
+  if (!is_pow2(unit_tokens) || unit_tokens > 4096)
+    return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
+  if ((sink_pos == nullptr) != (n_sinks == nullptr)) return fail(h, FDL_EINVAL, "sink_pos and n_sinks go together");
+  if (max_sel < 1 || (sink_pos && max_sinks < 1)) return fail(h, FDL_EINVAL, "max_sel and max_sinks must be >= 1");
+  const int ms = sink_pos ? max_sinks : 0;
+  if (!fdl::expand_tokens_ok(max_sel, ms)) return fail(h, FDL_EUNSUPPORTED, "max_sel <= 4096 and max_sinks <= 512");
+  if ((long long)max_sel * unit_tokens + ms > max_tok)
+    return fail(h, FDL_EINVAL, "max_tok must cover max_sel * unit_tokens + max_sinks");
+  ProfScope ps(h, FDL_PROF_SELECT);
+  return hip_status(h, fdl::launch_expand_tokens(h->stream, g, sel_idx, n_sel, max_sel, ilog2(unit_tokens), sink_pos,
+                                                 n_sinks, ms, tok_idx, n_tok, max_tok, h->status),
+                    "expand_tokens launch");
+}
+
 fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* gp, const void* q, const uint64_t* pred_mask,
                                    const void* k_cache, const int32_t* page_table, int32_t unit_tokens,
                                    const int32_t* cand_idx, int32_t n_cand, int32_t top_k, int32_t max_sel,

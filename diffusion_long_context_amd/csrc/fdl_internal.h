@@ -146,6 +146,13 @@ hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int 
                          int force_first, int max_sel, int32_t* sel_idx, int32_t* n_sel,
                          uint32_t* status, int shared = 0);
 
+// Token-granular sink retention: selected units + the sink tokens outside them -> ascending token
+// list.  expand_tokens_ok: max_sel <= 4096 and max_sinks <= 512.
+bool expand_tokens_ok(int max_sel, int max_sinks);
+hipError_t launch_expand_tokens(hipStream_t s, const Geom& g, const int32_t* sel_idx, const int32_t* n_sel,
+                                int max_sel, int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,
+                                int max_sinks, int32_t* tok_idx, int32_t* n_tok, int max_tok, uint32_t* status);
+
 // Attention.  dense != 0 ignores sel_idx / n_sel.
 size_t attn_scratch_bytes(const Geom& g, int n_splits);
 hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,

@@ -103,6 +103,126 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
+// Token-granular sink retention: the attended token list of a (sequence, KV head) is the tokens
+// of its selected units (ascending unit ids, each unit's valid tokens) merged with the sink tokens
+// that lie outside those units (each once), ascending.  One workgroup per (b, head).  Positions
+// are computed, not appended: a unit token goes to (its rank among the unit tokens) + (extra sinks
+// below it), an extra sink to (unit tokens below it) + (its rank among the extra sinks); every
+// position stays below units * unit + sinks <= max_tok whatever the lists hold.
+constexpr int kExpandMaxSel = 4096;
+constexpr int kExpandMaxSinks = 512;
+
+__device__ __forceinline__ int count_below(const int* a, int n, int v) {   // a ascending: #{a[i] < v}
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void expand_tokens_kernel(
+    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ n_sel, int max_sel, int unit_log2, int L,
+    int n_units, const int32_t* __restrict__ sink_pos, const int32_t* __restrict__ n_sinks, int max_sinks, int Hkv,
+    int32_t* __restrict__ tok_idx, int32_t* __restrict__ n_tok, int max_tok, uint32_t* __restrict__ status) {
+  __shared__ int s_blk[kExpandMaxSel];     // unit ids (invalid ones become empty units)
+  __shared__ int s_pre[kExpandMaxSel + 1]; // unit tokens before unit i
+  __shared__ int s_ext[kExpandMaxSinks];   // extra sinks, ascending
+  __shared__ int s_raw[kExpandMaxSinks];
+  __shared__ int s_keep[kExpandMaxSinks];
+  __shared__ int s_next;
+  const int tid = threadIdx.x, g = blockIdx.x, b = blockIdx.y;
+  const int64_t seg = (int64_t)b * Hkv + g;
+  const int unit = 1 << unit_log2;
+  int ns = n_sel[seg];
+  ns = ns < 0 ? 0 : (ns > max_sel ? max_sel : ns);
+  bool bad = false;
+  for (int i = tid; i < ns; i += 256) {
+    const int u = sel_idx[seg * max_sel + i];
+    const bool ok = (unsigned)u < (unsigned)n_units;
+    bad = bad || !ok;
+    s_blk[i] = ok ? u : -1;
+  }
+  int nk = sink_pos != nullptr ? n_sinks[b] : 0;
+  nk = nk < 0 ? 0 : (nk > max_sinks ? max_sinks : nk);
+  for (int i = tid; i < nk; i += 256) s_raw[i] = sink_pos[(int64_t)b * max_sinks + i];
+  __syncthreads();
+  if (tid == 0) {   // exclusive prefix of the unit lengths (at most kExpandMaxSel serial adds)
+    int acc = 0;
+    for (int i = 0; i < ns; ++i) {
+      s_pre[i] = acc;
+      const int u = s_blk[i];
+      const int len = u < 0 ? 0 : ((L - (u << unit_log2)) < unit ? (L - (u << unit_log2)) : unit);
+      acc += len;
+    }
+    s_pre[ns] = acc;
+    s_next = 0;
+  }
+  __syncthreads();
+  // extra sinks: valid, first occurrence, outside every selected unit; then each kept one goes to
+  // its rank among the kept ones (their values are distinct)
+  for (int i = tid; i < nk; i += 256) {
+    const int t = s_raw[i];
+    bool keep = t >= 0 && t < L;
+    for (int j = 0; keep && j < i; ++j) keep = s_raw[j] != t;
+    if (keep) {
+      const int u = t >> unit_log2;
+      for (int j = 0; keep && j < ns; ++j) keep = s_blk[j] != u;
+    }
+    s_keep[i] = keep ? 1 : 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < nk; i += 256) {
+    if (!s_keep[i]) continue;
+    const int t = s_raw[i];
+    int rank = 0;
+    for (int j = 0; j < nk; ++j) rank += (s_keep[j] && s_raw[j] < t) ? 1 : 0;
+    s_ext[rank] = t;
+    atomicAdd(&s_next, 1);
+  }
+  __syncthreads();
+  const int n_ext = s_next;
+  const int total_units = s_pre[ns];
+  int32_t* out = tok_idx + seg * (int64_t)max_tok;
+  for (int idx = tid; idx < total_units; idx += 256) {
+    int lo = 0, hi = ns - 1;   // the unit holding token idx: the last i with s_pre[i] <= idx
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= idx) lo = mid;
+      else hi = mid - 1;
+    }
+    const int t = (s_blk[lo] << unit_log2) + (idx - s_pre[lo]);
+    out[idx + count_below(s_ext, n_ext, t)] = t;
+  }
+  for (int e = tid; e < n_ext; e += 256) {
+    const int t = s_ext[e];
+    // unit tokens below t: the units (ascending) whose id is below t's unit
+    int lo = 0, hi = ns;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_blk[mid] < (t >> unit_log2)) lo = mid + 1;
+      else hi = mid;
+    }
+    out[s_pre[lo] + e] = t;
+  }
+  if (tid == 0) n_tok[seg] = total_units + n_ext;
+  latch_bad(status, bad);
+}
+
+bool expand_tokens_ok(int max_sel, int max_sinks) {
+  return max_sel <= kExpandMaxSel && max_sinks <= kExpandMaxSinks;
+}
+
+hipError_t launch_expand_tokens(hipStream_t s, const Geom& g, const int32_t* sel_idx, const int32_t* n_sel,
+                                int max_sel, int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,
+                                int max_sinks, int32_t* tok_idx, int32_t* n_tok, int max_tok, uint32_t* status) {
+  const int n_units = (g.L + (1 << unit_log2) - 1) >> unit_log2;
+  hipLaunchKernelGGL(expand_tokens_kernel, dim3(g.Hkv, g.B), dim3(256), 0, s, sel_idx, n_sel, max_sel, unit_log2,
+                     g.L, n_units, sink_pos, n_sinks, max_sinks, g.Hkv, tok_idx, n_tok, max_tok, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int n_units,
                          int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,
                          int max_sinks, const int32_t* cand_idx, int n_cand, int top_k,

@@ -26,7 +26,7 @@ EXPORTED = (
     "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_get_status_bits",
     "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_cache_write", "fdl_predict_queries", "fdl_score_blocks",
-    "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_select_blocks_shared", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
+    "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_select_blocks_shared", "fdl_expand_tokens", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_unmask", "fdl_decode_steps", "fdl_capture_begin", "fdl_capture_end", "fdl_graph_launch",
     "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end",
 )
@@ -79,6 +79,7 @@ _SIGS = {
     "fdl_score_blocks_mass": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _I, _P]),
     "fdl_select_blocks": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _P, _I, _I, _I, _I,
                                _P, _P]),
+    "fdl_expand_tokens": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _I, _I, _P, _P, _I, _P, _P, _I]),
     "fdl_select_blocks_shared": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _I, _I, _P, _P]),
     "fdl_score_select_tokens": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P,
                                      _P]),
@@ -296,6 +297,15 @@ class Handle:
             self.h, ctypes.byref(g.c()), _ptr(scores, 4 * B * Hkv * n_units, "scores"), n_units, unit_tokens,
             _ptr(sink_pos, 4 * B * max_sinks, "sink_pos"), _ptr(n_sinks, 4 * B, "n_sinks"), max_sinks, top_k,
             max_sel, _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel")))
+
+    def fdl_expand_tokens(self, g: Geom, sel_idx, n_sel, max_sel: int, unit_tokens: int, sink_pos, n_sinks,
+                          max_sinks: int, tok_idx, n_tok, max_tok: int):
+        self.sync_stream()
+        B, Hkv = g.batch, g.n_kv_heads
+        self._check(self.lib.fdl_expand_tokens(
+            self.h, ctypes.byref(g.c()), _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel"),
+            max_sel, unit_tokens, _ptr(sink_pos, 4 * B * max_sinks, "sink_pos"), _ptr(n_sinks, 4 * B, "n_sinks"),
+            max_sinks, _ptr(tok_idx, 4 * B * Hkv * max_tok, "tok_idx"), _ptr(n_tok, 4 * B * Hkv, "n_tok"), max_tok))
 
     def fdl_score_select_tokens(self, g: Geom, q, pred_mask, k_cache, page_table, unit_tokens: int, cand_idx,
                                 n_cand: int, top_k: int, max_sel: int, scores, sel_idx, n_sel):

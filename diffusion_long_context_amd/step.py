@@ -85,12 +85,32 @@ class FocusStep:
     def dense(self, q, k, v, k_dec, v_dec, out):
         self.h.fdl_dense_attn(self.g, q, k, v, k_dec, v_dec, None, out)
 
-    def layer(self, mode: str, q, k, v, k_dec, v_dec, ks, out, scorer: str = "sum"):
-        """mode: "dense", "source" (detect sinks here) or "reuse" (keep the last source's sinks)."""
+    def select_token_sinks(self):
+        """Token-granular sink retention: the top-K of all blocks (no block forced), then the list of
+        their tokens merged with the sink tokens outside them (tok_idx / n_tok)."""
+        g, fp = self.g, self.fp
+        k = min(self.n_blk, fp.top_k_blocks)
+        if not hasattr(self, "tok_idx"):
+            self.max_tok = max(1, k) * g.kv_block + fp.max_sinks
+            self.tok_idx = torch.zeros(g.batch, g.n_kv_heads, self.max_tok, dtype=torch.int32, device=self.scores.device)
+            self.n_tok = torch.zeros(g.batch, g.n_kv_heads, dtype=torch.int32, device=self.scores.device)
+        self.h.fdl_select_blocks(g, self.scores, self.n_blk, g.kv_block, None, None, 1, k, max(1, k), self.sel_idx,
+                                 self.n_sel)
+        self.h.fdl_expand_tokens(g, self.sel_idx, self.n_sel, max(1, k), g.kv_block, self.sink_pos, self.n_sinks,
+                                 fp.max_sinks, self.tok_idx, self.n_tok, self.max_tok)
+
+    def layer(self, mode: str, q, k, v, k_dec, v_dec, ks, out, scorer: str = "sum", sink_tokens: bool = False):
+        """mode: "dense", "source" (detect sinks here) or "reuse" (keep the last source's sinks).
+        sink_tokens: keep the sinks as tokens, the top-K from all blocks (select_token_sinks)."""
         if mode == "dense":
             self.dense(q, k, v, k_dec, v_dec, out)
             return
         self.score(q, ks, k_cache=k, k_dec=k_dec, detect_sinks=(mode == "source"), scorer=scorer)
+        if sink_tokens:
+            self.select_token_sinks()
+            self.h.fdl_sparse_attn(self.g, q, k, v, k_dec, v_dec, None, self.tok_idx, self.n_tok, self.max_tok, 1,
+                                   out)
+            return
         self.select()
         self.attend(q, k, v, k_dec, v_dec, out)
 

@@ -246,6 +246,20 @@ fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* g, const void* 
                                    const int32_t* cand_idx, int32_t n_cand, int32_t top_k, int32_t max_sel,
                                    float* scores, int32_t* sel_idx, int32_t* n_sel);
 
+/* Token-granular sink retention, the other reading of how sinks are kept ([FA] Elamur "Summary":
+ * sinks are always preserved; at which granularity is left open): select the units with
+ * fdl_select_blocks level 1 WITHOUT sinks (so the top-K comes from all units), then this call
+ * writes, per (sequence, KV head), the ascending list of the selected units' valid tokens merged
+ * with the sink tokens sink_pos[b][0 .. n_sinks[b]) that lie outside those units (each token once;
+ * positions outside [0, ctx_len) are dropped): tok_idx [B][Hkv][max_tok], n_tok [B][Hkv].  Feed the
+ * list to fdl_sparse_attn with sel_unit_tokens = 1.  sel_idx [B][Hkv][max_sel] ascending unit ids
+ * (out-of-range ids latch FDL_EINDEX and contribute nothing), n_sel [B][Hkv]; sink_pos / n_sinks
+ * may both be NULL.  max_sel <= 4096 and max_sinks <= 512 (FDL_EUNSUPPORTED beyond); max_tok >=
+ * max_sel * unit_tokens + max_sinks (FDL_EINVAL otherwise). */
+fdl_status fdl_expand_tokens(fdl_handle h, const fdl_geom* g, const int32_t* sel_idx, const int32_t* n_sel,
+                             int32_t max_sel, int32_t unit_tokens, const int32_t* sink_pos, const int32_t* n_sinks,
+                             int32_t max_sinks, int32_t* tok_idx, int32_t* n_tok, int32_t max_tok);
+
 /* ---- step 4: sparse bidirectional attention over the selected KV ---------------------------- */
 
 /* [FA], [FS]: bidirectional attention of the current block's queries over only the selected KV;

@@ -9,7 +9,7 @@ import torch
 from gpu_util import assert_close, dev, host, out_buffer, out_to_f64
 
 
-def _focus(h, cfg, x, modes=("source", "reuse")):
+def _focus(h, cfg, x, modes=("source", "reuse"), sink_tokens=False):
     from diffusion_long_context_amd.step import FocusParams, FocusStep, geom_for
     g = geom_for(cfg)
     fs = FocusStep(h, g, FocusParams(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.sink_tau,
@@ -22,7 +22,7 @@ def _focus(h, cfg, x, modes=("source", "reuse")):
     res = {}
     for mode in modes:
         out = out_buffer(cfg)
-        fs.layer(mode, t["q"], t["k"], t["v"], t["k_dec"], t["v_dec"], ks, out)
+        fs.layer(mode, t["q"], t["k"], t["v"], t["k_dec"], t["v_dec"], ks, out, sink_tokens=sink_tokens)
         torch.cuda.synchronize()
         res[mode] = {
             "out": out_to_f64(cfg, out),
@@ -33,6 +33,9 @@ def _focus(h, cfg, x, modes=("source", "reuse")):
             "sel": host(fs.sel_idx).copy(),
             "n_sel": host(fs.n_sel).copy(),
         }
+        if sink_tokens:
+            res[mode]["tokens"] = host(fs.tok_idx).copy()
+            res[mode]["n_tok"] = host(fs.n_tok).copy()
     assert h.fdl_get_status() == 0
     return res
 

@@ -115,6 +115,67 @@ def test_chunked_per_sequence(h, kw):
         assert all(got["chunks"][b, g].tolist() == got["chunks"][b, 0].tolist() for g in range(cfg.n_kv_heads))
 
 
+@pytest.mark.parametrize("ci,kw", [(1, {}), (2, {}), (1, dict(ctx_len=5000, n_q_heads=8, n_kv_heads=2))],
+                         ids=["8k", "16k-gqa", "ragged-gqa4"])
+def test_token_granular_sinks(h, ci, kw):
+    """Sinks kept as tokens, the top-K from all blocks: the attended token lists bit for bit and the
+    outputs of a source and a reuse layer against the oracle."""
+    cfg = get_config(ci).with_(**kw)
+    x = make_single(cfg)
+    got = _focus(h, cfg, x, sink_tokens=True)
+    sinks = None
+    for mode in ("source", "reuse"):
+        want = focus_layer_step(cfg, x, mode, sinks=sinks, sink_tokens=True)
+        if mode == "source":
+            assert want["sink_margin"] > 1e-4 * cfg.sink_tau
+            sinks = (want["sink_pos"], want["n_sinks"])
+        gm = got[mode]
+        for b in range(cfg.batch):
+            for g in range(cfg.n_kv_heads):
+                w = want["tokens"][b][g].tolist()
+                assert int(gm["n_tok"][b, g]) == len(w), (mode, b, g)
+                assert gm["tokens"][b, g, :len(w)].tolist() == w, (mode, b, g)
+        assert_close(gm["out"], want["out"], f"token sinks ({mode})")
+
+
+def test_expand_tokens_edge_cases(h):
+    """Duplicate, negative and out-of-range sink positions, sinks inside chosen blocks and in the
+    partial last block, no sinks at all, and an out-of-range block id (latched, contributes nothing)."""
+    from diffusion_long_context_amd.fdllm import FdlError
+    from diffusion_long_context_amd.step import geom_for
+    from oracle.selection import select_token_sinks
+    cfg = get_config(1).with_(batch=3, n_q_heads=2, n_kv_heads=2, ctx_len=1000)
+    g = geom_for(cfg)
+    n_blk, bt, k, ms = 16, 64, 3, 6
+    sc = np.zeros((3, 2, n_blk), np.float32)
+    sc[:, 0, [2, 9, 15]] = [3, 2, 1]
+    sc[:, 1, [0, 5, 7]] = [3, 2, 1]
+    sp = np.array([[5, 5, -3, 1000, 999, 130], [140, 0, 12, 64, 700, 2000], [-1] * 6], np.int32)
+    ns = np.array([6, 5, 0], np.int32)
+    sel = torch.zeros((3, 2, k), dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((3, 2), dtype=torch.int32, device="cuda")
+    h.fdl_select_blocks(g, dev(sc), n_blk, bt, None, None, 1, k, k, sel, nsel)
+    max_tok = k * bt + ms
+    tok = torch.full((3, 2, max_tok), -9, dtype=torch.int32, device="cuda")
+    ntok = torch.zeros((3, 2), dtype=torch.int32, device="cuda")
+    h.fdl_expand_tokens(g, sel, nsel, k, bt, dev(sp), dev(ns), ms, tok, ntok, max_tok)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    want = select_token_sinks(sc, sp, ns, bt, k, cfg.ctx_len)
+    for b in range(3):
+        for gg in range(2):
+            w = want[b][gg].tolist()
+            assert int(host(ntok)[b, gg]) == len(w) and host(tok)[b, gg, :len(w)].tolist() == w, (b, gg)
+    # an out-of-range unit id is reported and skipped
+    bad = torch.tensor([[[1, 3, 99]] * 2] * 3, dtype=torch.int32, device="cuda")
+    h.fdl_expand_tokens(g, bad, nsel, k, bt, None, None, 1, tok, ntok, max_tok)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() != 0
+    assert host(ntok)[0, 0] == 2 * bt and host(tok)[0, 0, :2 * bt].tolist() == list(range(64, 128)) + list(range(192, 256))
+    with pytest.raises(FdlError):
+        h.fdl_expand_tokens(g, sel, nsel, k, bt, dev(sp), dev(ns), ms, tok, ntok, max_tok - 1)
+
+
 def test_chunked_grouped_query(h):
     cfg = get_config(4).with_(batch=2, n_q_heads=8, n_kv_heads=2, ctx_len=4096, chunk_tokens=512)
     x = make_single(cfg)
