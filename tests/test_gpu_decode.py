@@ -200,3 +200,74 @@ def test_capture_rules(h):
         h.fdl_graph_destroy(graph)
     torch.cuda.synchronize()
     assert h.fdl_get_status() == 0
+
+
+def test_decode_steps_validates_every_step_before_launching(h):
+    """A bad layer table in the last step is reported before anything runs: the masked flags and
+    the outputs of the earlier steps stay untouched."""
+    from diffusion_long_context_amd.fdllm import FDL_LAYER_REUSE, FdlError, fdl_layer_io
+    S, modes, n = 3, ["dense", "source", "reuse"], 1
+    cfg, g, params, xs, outs, table, b, confs = _setup(h, S, modes)
+    B, T = cfg.batch, cfg.dec_len
+    bad = (fdl_layer_io * len(table))()
+    for i in range(len(table)):
+        bad[i] = table[i]
+    bad[len(table) - 1].ks = None            # a reuse layer without pooled keys
+    assert bad[len(table) - 1].mode == FDL_LAYER_REUSE
+    masked_d = torch.ones((B, T), dtype=torch.uint8, device="cuda")
+    for row in outs:
+        for o in row:
+            o.fill_(3.0)
+    torch.cuda.synchronize()
+    with pytest.raises(FdlError):
+        h.fdl_decode_steps(g, params, S, None, dev(confs), masked_d, n, None, bad, b["pm"], b["npd"], b["sc"],
+                           b["sp"], b["nsk"], b["sel"], b["nsel"])
+    torch.cuda.synchronize()
+    assert bool((masked_d == 1).all())
+    assert all(bool((o == 3.0).all()) for row in outs for o in row)
+
+
+def test_graph_of_the_chunked_paged_step(h):
+    """The chunked, paged select-and-attend chain (chunk scores, chunk selection, level 2 in one
+    kernel, paged attention) captured once and replayed: every replay equals the eager run."""
+    from diffusion_long_context_amd.step import ChunkedStep, ChunkParams, geom_for
+    cfg = get_config(4).with_(batch=2, n_q_heads=4, n_kv_heads=2, ctx_len=4096, chunk_tokens=512)
+    g = geom_for(cfg)
+    x = make_single(cfg)
+    t = {k: dev(x[k]) for k in ("q", "k_pool", "v_pool", "page_table", "k_dec", "v_dec", "masked", "prev_conf")}
+    cs_ = ChunkedStep(h, g, ChunkParams(cfg.top_k_pos, cfg.window, cfg.chunk_tokens, cfg.top_k_chunks,
+                                        cfg.tokens_per_chunk_kept))
+    cs = cs_.new_chunk_sums()
+    cs_.pool(t["k_pool"], t["page_table"], cs)
+    out = torch.zeros((cfg.batch, cfg.n_q_heads, cfg.dec_len, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        cs_.predict(t["prev_conf"], t["masked"])
+        cs_.run(t["q"], t["k_pool"], t["v_pool"], t["page_table"], t["k_dec"], t["v_dec"], cs, out)
+
+    step()
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    want_out, want_tok = out.clone(), cs_.tokens.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        h.fdl_capture_begin()
+        try:
+            step()
+        finally:
+            graph = h.fdl_capture_end()
+    try:
+        for rep in range(3):
+            with torch.cuda.stream(side):
+                out.zero_()
+                cs_.tokens.zero_()
+                h.fdl_graph_launch(graph)
+            torch.cuda.synchronize()
+            assert h.fdl_get_status() == 0
+            assert torch.equal(out.view(torch.int16), want_out.view(torch.int16)), rep
+            assert torch.equal(cs_.tokens, want_tok), rep
+            step()                                # eager work between replays
+            torch.cuda.synchronize()
+    finally:
+        h.fdl_graph_destroy(graph)
