@@ -113,3 +113,86 @@ def test_shared_chunks_in_the_layer_step():
     a = chunked_layer_step(allc, x, with_output=False, per_sequence=True)
     p = chunked_layer_step(allc, x, with_output=False, per_sequence=False)
     assert np.array_equal(a["tokens"], p["tokens"])
+
+
+# ---- level 2 (tokens inside the chosen chunks), pinned independently of the oracle's code ------
+
+def test_select_tokens_hand_worked():
+    """One head, head_dim 2, four chunks of four tokens, query sum (1, 0): a token's score is the
+    first component of its key, a chunk's score the sum of those.  Chunk sums 4, 6, 3, 8 choose
+    chunks 1 and 3 (a strict, non-adjacent subset).  Chunk 1 = (-5, 2, 7, 2): the anchor (token 4)
+    is kept although it scores lowest, then token 6 (7) and, of the tie 2 = 2 between tokens 5 and
+    7, the lower token 5.  Chunk 3 = (8, 1, -1, 0): the anchor (token 12) scores highest but is kept
+    once; the best two others are tokens 13 (1) and 15 (0)."""
+    from oracle.chunked import select_chunks, select_tokens
+    s = [1, 1, 1, 1, -5, 2, 7, 2, 0, 0, 0, 3, 8, 1, -1, 0]
+    k = np.zeros((1, 1, 16, 2), dtype=np.float32)
+    k[0, 0, :, 0] = s
+    k[0, 0, :, 1] = [3] * 16          # ignored by the query sum below
+    qs = np.array([[[1.0, 0.0]]], dtype=np.float32)
+    sc, chosen = select_chunks(qs, k, 4, 2)
+    assert sc[0, 0].tolist() == [4.0, 6.0, 3.0, 8.0]
+    assert chosen[0, 0].tolist() == [1, 3]
+    ts, kept = select_tokens(qs, k, chosen, 4, 2)
+    assert ts[0, 0].tolist() == [[-5.0, 2.0, 7.0, 2.0], [8.0, 1.0, -1.0, 0.0]]
+    assert kept[0, 0].tolist() == [4, 5, 6, 12, 13, 15]
+
+
+def _brute_layer(cfg, q_int, k_int, pt, chunk, K, keep):
+    """Python-integer brute force of the chunked selection: predicted query sum over all positions
+    and all heads of a group, chunk scores, top-K chunks, then anchor + top-keep other tokens of
+    every chosen chunk (ties to the lower chunk / token).  k_int is the logical [B][Hkv][L][D]."""
+    B, Hq, T, D = q_int.shape
+    Hkv = k_int.shape[1]
+    G = Hq // Hkv
+    L = k_int.shape[2]
+    n_chunks = L // chunk
+    out_chunks, out_tokens = [], []
+    for b in range(B):
+        rc, rt = [], []
+        for g in range(Hkv):
+            qs = [sum(int(q_int[b, g * G + m, p, d]) for m in range(G) for p in range(T)) for d in range(D)]
+            tok = [sum(qs[d] * int(k_int[b, g, t, d]) for d in range(D)) for t in range(L)]
+            csum = [sum(tok[c * chunk:(c + 1) * chunk]) for c in range(n_chunks)]
+            chosen = sorted(sorted(range(n_chunks), key=lambda c: (-csum[c], c))[:K])
+            row = []
+            for c in chosen:
+                others = sorted(range(c * chunk + 1, (c + 1) * chunk), key=lambda t: (-tok[t], t))[:keep]
+                row.extend(sorted([c * chunk] + others))
+            rc.append(chosen)
+            rt.append(row)
+        out_chunks.append(rc)
+        out_tokens.append(rt)
+    return out_chunks, out_tokens
+
+
+def test_select_tokens_integer_brute_force():
+    """Integer-valued queries and keys small enough that every float32 product and sum is exact, so
+    the oracle's chunk and token choices must equal a Python-integer brute force under any order.
+    Chunks are a strict subset (2 of 8), pages shuffled, several KV heads with two query heads each;
+    a ranking turned around, or a chosen chunk's tokens scored under another slot, fails."""
+    from types import SimpleNamespace
+
+    from oracle.pipeline import chunked_layer_step
+    from synth.gen import round_to_bf16, to_pages
+    for seed in range(6):
+        rng = np.random.default_rng(1000 + seed)
+        B, Hq, Hkv, T, D, chunk, n_chunks, K, keep, page = 2, 6, 3, 4, 8, 16, 8, 2, 3, 4
+        L = chunk * n_chunks
+        q_int = rng.integers(-2, 3, size=(B, Hq, T, D))
+        k_int = rng.integers(-3, 4, size=(B, Hkv, L, D))
+        p = SimpleNamespace(top_k_pos=4, window=0, n_kv_heads=Hkv, chunk_tokens=chunk, top_k_chunks=K,
+                            tokens_per_chunk_kept=keep, page_tokens=page)
+        npp = L // page
+        pt = rng.permutation(B * npp).astype(np.int32).reshape(B, npp)
+        cfg = SimpleNamespace(batch=B, n_kv_heads=Hkv, ctx_len=L, head_dim=D, n_pages=B * npp, page_tokens=page)
+        kb = round_to_bf16(k_int.astype(np.float32))
+        x = {"q": round_to_bf16(q_int.astype(np.float32)), "k_pool": to_pages(cfg, kb, pt),
+             "v_pool": to_pages(cfg, kb, pt), "page_table": pt, "k_dec": kb[:, :, :T], "v_dec": kb[:, :, :T],
+             "prev_conf": None, "masked": np.ones((B, T), dtype=np.uint8)}
+        r = chunked_layer_step(p, x, with_output=False)
+        want_c, want_t = _brute_layer(cfg, q_int, k_int, pt, chunk, K, keep)
+        assert r["chunks"].tolist() == want_c, seed
+        assert r["tokens"].tolist() == want_t, seed
+        # the chosen chunks are a strict subset, and the kept tokens are not simply the first ones
+        assert all(len(c) == K for row in want_c for c in row)
