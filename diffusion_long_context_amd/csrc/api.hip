@@ -838,6 +838,19 @@ fdl_status fdl_graph_destroy(fdl_graph g) {
   return FDL_OK;
 }
 
+fdl_status fdl_bandwidth_probe(fdl_handle h, int32_t mode, const void* src, size_t bytes, void* dst,
+                               size_t dst_bytes, int32_t n_blocks) {
+  if (!h) return FDL_EINVAL;
+  if (mode < FDL_PROBE_READ || mode > FDL_PROBE_COPY) return fail(h, FDL_EINVAL, "unknown probe mode");
+  if (!src || !dst) return fail(h, FDL_EINVAL, "src and dst must be non-NULL");
+  if (bytes == 0 || bytes % 1024) return fail(h, FDL_EINVAL, "bytes must be a positive multiple of 1024");
+  if (n_blocks < 0) return fail(h, FDL_EINVAL, "n_blocks must be >= 0");
+  const int nb = n_blocks > 0 ? n_blocks : 4 * h->num_cus;
+  const size_t need = mode == FDL_PROBE_COPY ? bytes : fdl::probe_out_words(nb) * sizeof(uint32_t);
+  if (dst_bytes < need) return fail(h, FDL_EINVAL, "dst holds %zu bytes, needs %zu", dst_bytes, need);
+  return hip_status(h, fdl::launch_probe(h->stream, mode, src, bytes, dst, nb), "probe launch");
+}
+
 fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask, int32_t every) {
   if (!h || max_records < 1) return h ? fail(h, FDL_EINVAL, "max_records must be >= 1") : FDL_EINVAL;
   if (h->capturing) return fail(h, FDL_EINVAL, "the handle's stream is being captured");

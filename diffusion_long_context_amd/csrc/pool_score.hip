@@ -64,27 +64,36 @@ __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRo
   Leaf a[LEAVES];
   const bool run = (t0 & (LEAVES - 1)) == 0 && t0 + LEAVES <= rows.L &&
                    (!PAGED || rows.page_log2 >= ilog2_const(LEAVES));
+  // a row whose page id is out of range has no key: it reads a valid row (so that the loads stay
+  // unconditional), counts +0 and latches `bad`
+  uint64_t badm = 0;
   if (run) {   // uniform per team
-    const KT* base = k + rows.off(b, g, t0, bad) + 2 * pair;
+    bool rb = false;
+    const KT* base = k + rows.off(b, g, t0, rb) + 2 * pair;
+    badm = rb ? ~0ull : 0ull;
 #pragma unroll
     for (int i = 0; i < LEAVES; ++i) a[i] = load_leaf(base + i * D);
   } else {
 #pragma unroll
     for (int i = 0; i < LEAVES; ++i) {
       const int t = t0 + i;
-      a[i] = load_leaf(k + rows.off(b, g, t < rows.L ? t : rows.L - 1, bad) + 2 * pair);
+      bool rb = false;
+      a[i] = load_leaf(k + rows.off(b, g, t < rows.L ? t : rows.L - 1, rb) + 2 * pair);
+      badm |= (uint64_t)(rb && t < rows.L) << i;
     }
   }
+  bad = bad || badm != 0;
   const int live = rows.L - t0;   // leaves at or past it are +0
+  auto keep = [&](int i) { return i < live && ((badm >> i) & 1ull) == 0; };
   if constexpr (kPacked) {
     float2 s[LEAVES / 2];
 #pragma unroll
     for (int i = 0; i < LEAVES / 2; ++i) {
       const uint32_t w0 = a[2 * i], w1 = a[2 * i + 1];
-      const float2 x0 = 2 * i < live ? make_float2(bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16))
-                                     : make_float2(0.f, 0.f);
-      const float2 x1 = 2 * i + 1 < live ? make_float2(bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16))
-                                         : make_float2(0.f, 0.f);
+      const float2 x0 = keep(2 * i) ? make_float2(bf16_bits_to_f32(w0 & 0xFFFFu), bf16_bits_to_f32(w0 >> 16))
+                                    : make_float2(0.f, 0.f);
+      const float2 x1 = keep(2 * i + 1) ? make_float2(bf16_bits_to_f32(w1 & 0xFFFFu), bf16_bits_to_f32(w1 >> 16))
+                                        : make_float2(0.f, 0.f);
       s[i] = add2(x0, x1);
     }
 #pragma unroll
@@ -96,7 +105,7 @@ __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRo
   } else {
 #pragma unroll
     for (int i = 0; i < LEAVES; ++i)
-      if (i >= live) a[i] = make_float2(0.f, 0.f);
+      if (!keep(i)) a[i] = make_float2(0.f, 0.f);
 #pragma unroll
     for (int w = LEAVES / 2; w >= 1; w /= 2) {
 #pragma unroll
@@ -308,15 +317,20 @@ __global__ __launch_bounds__(256) void cache_write_pool_kernel(CacheWrite w, KvR
   const KT* vn = static_cast<const KT*>(w.v_new) + seg * w.n_tok * D + 2 * pair;
   KT* kc = static_cast<KT*>(w.k);
   KT* vc = static_cast<KT*>(w.v);
-  bool bad = false;
   PT ka[RUN], va[RUN];
   // every load unconditional: the source is chosen by address (a guarded load would be waited for on
-  // its own); a row's cache offset is uniform per team and recomputed for the stores rather than kept
+  // its own); a row's cache offset is uniform per team and recomputed for the stores rather than kept.
+  // A row whose page id is out of range has no place in the cache: it is neither stored nor read
+  // (its cache load reads page 0 and is dropped), it counts +0 in the pooled keys, and it latches
+  // ST_BAD_INDEX (bit i of badm: row t_run + i).
+  uint64_t badm = 0;
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
     const int t = t_run + i;
     const bool in = t >= w.t0 && t < w.t0 + w.n_tok;   // uniform per team
-    const int64_t coff = rows.off(b, g, t < rows.L ? t : rows.L - 1, bad);
+    bool rb = false;
+    const int64_t coff = rows.off(b, g, t < rows.L ? t : rows.L - 1, rb);
+    badm |= (uint64_t)(rb && t < rows.L) << i;
     const int64_t noff = (int64_t)(in ? t - w.t0 : 0) * D;
     ka[i] = *reinterpret_cast<const PT*>(in ? kn + noff : kc + coff + 2 * pair);
     va[i] = *reinterpret_cast<const PT*>(in ? vn + noff : vc + coff + 2 * pair);
@@ -324,14 +338,14 @@ __global__ __launch_bounds__(256) void cache_write_pool_kernel(CacheWrite w, KvR
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
     const int t = t_run + i;
-    if (t >= w.t0 && t < w.t0 + w.n_tok) {   // uniform per team
+    if (t >= w.t0 && t < w.t0 + w.n_tok && ((badm >> i) & 1ull) == 0) {   // uniform per team
       bool unused = false;
       const int64_t coff = rows.off(b, g, t, unused) + 2 * pair;
       *reinterpret_cast<PT*>(kc + coff) = ka[i];
       *reinterpret_cast<PT*>(vc + coff) = va[i];
     }
   }
-  latch_bad(status, bad);
+  latch_bad(status, badm != 0);
   if (out == nullptr) return;
   float2 x[RUN];
 #pragma unroll
@@ -340,7 +354,7 @@ __global__ __launch_bounds__(256) void cache_write_pool_kernel(CacheWrite w, KvR
       x[i] = make_float2(bf16_bits_to_f32(ka[i] & 0xFFFFu), bf16_bits_to_f32(ka[i] >> 16));
     else
       x[i] = ka[i];
-    if (t_run + i >= rows.L) x[i] = make_float2(0.f, 0.f);
+    if (t_run + i >= rows.L || ((badm >> i) & 1ull) != 0) x[i] = make_float2(0.f, 0.f);
   }
 #pragma unroll
   for (int wdt = RUN / 2; wdt >= 1; wdt /= 2) {

@@ -28,10 +28,11 @@ EXPORTED = (
     "fdl_last_error", "fdl_pool_keys", "fdl_cache_write", "fdl_predict_queries", "fdl_score_blocks",
     "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_select_blocks_shared", "fdl_expand_tokens", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_unmask", "fdl_decode_steps", "fdl_capture_begin", "fdl_capture_end", "fdl_graph_launch",
-    "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end",
+    "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end", "fdl_bandwidth_probe",
 )
 
 FDL_LAYER_DENSE, FDL_LAYER_SOURCE, FDL_LAYER_REUSE = 0, 1, 2
+FDL_PROBE_READ, FDL_PROBE_READ_LDS, FDL_PROBE_COPY = 0, 1, 2
 PROF_KINDS = ("predict", "pool", "score", "sinks", "select", "sparse_attn", "dense_attn",
               "layer_dense", "layer_source", "layer_reuse", "reuse_run")
 
@@ -96,6 +97,7 @@ _SIGS = {
     "fdl_graph_destroy": (_I, [_P]),
     "fdl_profile_begin": (_I, [_P, _I, ctypes.c_uint32, _I]),
     "fdl_profile_end": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+    "fdl_bandwidth_probe": (_I, [_P, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _I]),
 }
 
 _lib = None
@@ -436,3 +438,11 @@ class Handle:
         cnt = (ctypes.c_int64 * len(PROF_KINDS))()
         self._check(self.lib.fdl_profile_end(self.h, tot, cnt))
         return {k: (tot[i], cnt[i]) for i, k in enumerate(PROF_KINDS)}
+
+    def fdl_bandwidth_probe(self, mode: int, src, dst, n_blocks: int = 0):
+        """Stream all of src once (mode FDL_PROBE_READ / _READ_LDS / _COPY); see the header."""
+        self.sync_stream()
+        nbytes = src.numel() * src.element_size()
+        self._check(self.lib.fdl_bandwidth_probe(self.h, mode, _ptr(src, None, "src"), nbytes,
+                                                 _ptr(dst, None, "dst"), dst.numel() * dst.element_size(),
+                                                 n_blocks))

@@ -93,7 +93,8 @@ fdl_status fdl_get_status(fdl_handle h);
 /* Device condition bits, as latched by the kernels. */
 #define FDL_FLAG_SINK_OVERFLOW 1u   /* more sinks than max_sinks: list truncated (FDL_EOVERFLOW)     */
 #define FDL_FLAG_CAND_OVERFLOW 2u   /* more sink candidates than the workspace holds (FDL_EOVERFLOW) */
-#define FDL_FLAG_BAD_INDEX 4u       /* unit or page id out of range: row skipped (FDL_EINDEX)       */
+#define FDL_FLAG_BAD_INDEX 4u       /* unit or page id out of range: row skipped, not read or       */
+                                    /* written, +0 in a key sum (FDL_EINDEX)                         */
 #define FDL_FLAG_SEL_OVERFLOW 8u    /* more selected units than max_sel: list truncated (EOVERFLOW) */
 #define FDL_FLAG_SPLIT_FALLBACK 16u /* informational: a split of fdl_focus_step's fused kernel did  */
                                     /* not wait for its siblings and scored every block itself;     */
@@ -113,7 +114,8 @@ const char* fdl_last_error(fdl_handle h);
  * the most relevant KV": units are represented by their key sums) and [PA] (chunks are cached once).
  *   k_cache     contiguous or paged keys (per g->paged); page_table used when paged, else ignored
  *   unit_tokens power of two in [1, 4096]
- *   ks          out: [B][Hkv][ceil(L / unit_tokens)][D] float32 */
+ *   ks          out: [B][Hkv][ceil(L / unit_tokens)][D] float32
+ * A paged row whose page id lies outside [0, n_pages) counts +0 and latches FDL_EINDEX. */
 fdl_status fdl_pool_keys(fdl_handle h, const fdl_geom* g, const void* k_cache,
                          const int32_t* page_table, int32_t unit_tokens, float* ks);
 
@@ -126,8 +128,9 @@ fdl_status fdl_pool_keys(fdl_handle h, const fdl_geom* g, const void* k_cache,
  * updated cache (the same tree as fdl_pool_keys), and the other units of ks [B][Hkv][n_units][D] are
  * left as they are.  Requires 0 <= t0, n_tok >= 1, t0 + n_tok <= L and, with ks, unit_tokens a power
  * of two in [16, 4096]; units longer than 64 tokens use workspace scratch (B * Hkv * ceil(L / 64) * D
- * floats; FDL_ENOMEM if the workspace is smaller).  Page ids outside [0, n_pages) latch FDL_EINDEX
- * (the rows are then written to page 0). */
+ * floats; FDL_ENOMEM if the workspace is smaller).  A row whose page id lies outside [0, n_pages)
+ * has no place in the pool: it is not written (no page is touched for it), it counts +0 in the
+ * pooled keys of its unit, and FDL_EINDEX is latched. */
 fdl_status fdl_cache_write(fdl_handle h, const fdl_geom* g, const void* k_new, const void* v_new, int32_t t0,
                            int32_t n_tok, void* k_cache, void* v_cache, const int32_t* page_table,
                            int32_t unit_tokens, float* ks);
@@ -394,6 +397,19 @@ typedef enum {
 
 fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask, int32_t every);
 fdl_status fdl_profile_end(fdl_handle h, double* total_us, int64_t* counts);
+
+/* Measurement aid, not part of the method: stream `bytes` (a positive multiple of 1024) of the
+ * device buffer `src` once, the way the HBM-bound kernels stream their inputs, so that their rate
+ * can be set against what the memory system delivers to a plain coalesced stream as well as against
+ * the vendor peak.  FDL_PROBE_READ: 16-byte non-temporal loads into registers, eight in flight per
+ * thread; FDL_PROBE_READ_LDS: 1 KiB fetches straight into LDS (global_load_lds_dwordx4), eight in
+ * flight per wave; both write one xor checksum word per wave to dst (n_blocks * 8 uint32,
+ * dst_bytes at least that).  FDL_PROBE_COPY: the same read stream written to dst (dst_bytes >= bytes).
+ * n_blocks workgroups of 512 threads (0 = four per compute unit).  Asynchronous on the handle's
+ * stream; time it with events around the call. */
+typedef enum { FDL_PROBE_READ = 0, FDL_PROBE_READ_LDS = 1, FDL_PROBE_COPY = 2 } fdl_probe_mode;
+fdl_status fdl_bandwidth_probe(fdl_handle h, int32_t mode, const void* src, size_t bytes, void* dst,
+                               size_t dst_bytes, int32_t n_blocks);
 
 #ifdef __cplusplus
 }

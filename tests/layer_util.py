@@ -45,17 +45,19 @@ def _check_layer(cfg, got, want, margin=None):
     if "scores" in want:
         assert np.array_equal(got["scores"].view(np.uint32), want["scores"].view(np.uint32))
     if "sel" in want:
-        if margin is None or margin > 1e-4 * cfg.sink_tau:
-            ns = int(want["n_sinks"][0])
-            for b in range(cfg.batch):
-                nsb = int(want["n_sinks"][b])
-                assert got["n_sinks"][b] == nsb
-                assert got["sink_pos"][b, :nsb].tolist() == want["sink_pos"][b, :nsb].tolist()
-            for b in range(cfg.batch):
-                for g in range(cfg.n_kv_heads):
-                    w = want["sel"][b][g].tolist()
-                    assert got["n_sel"][b, g] == len(w)
-                    assert got["sel"][b, g, : len(w)].tolist() == w
+        if margin is not None:
+            # a sink mass within 1e-4 tau of the threshold may land on either side in float32: such
+            # inputs are a flagged case, not a pass; none of the seeded workloads is one
+            assert margin > 1e-4 * cfg.sink_tau, f"flagged case: sink margin {margin:.3g} within 1e-4 tau"
+        for b in range(cfg.batch):
+            nsb = int(want["n_sinks"][b])
+            assert got["n_sinks"][b] == nsb
+            assert got["sink_pos"][b, :nsb].tolist() == want["sink_pos"][b, :nsb].tolist()
+        for b in range(cfg.batch):
+            for g in range(cfg.n_kv_heads):
+                w = want["sel"][b][g].tolist()
+                assert got["n_sel"][b, g] == len(w)
+                assert got["sel"][b, g, : len(w)].tolist() == w
     assert_close(got["out"], want["out"], cfg.name)
 
 
@@ -86,3 +88,85 @@ def _check_chunked(cfg, got, want):
     assert np.array_equal(got["tokens"], want["tokens"])
     assert np.all(got["n_tokens"] == want["tokens"].shape[-1])
     assert_close(got["out"], want["out"], "chunked")
+
+
+def focus_step_layers(h, cfg, xs, modes, prev_conf, masked):
+    """fdl_focus_step over one layer table (xs[l] holds layer l's q, k, v, k_dec, v_dec; modes[l] is
+    "dense", "source" or "reuse"), with every sparse layer's scores and selection captured: the step
+    is run once with the table cut after each sparse layer (the buffers then hold that layer's
+    values), then once in full for the outputs, predicted positions and sinks.  Returns
+    {"layers": {l: (scores, sel, n_sel)}, "outs": [...], "pred_mask", "sink_pos", "n_sinks", "bits"}."""
+    from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
+                                                  fdl_focus_params)
+    from diffusion_long_context_amd.step import geom_for
+    g = geom_for(cfg)
+    B, Hq, Hkv, D, T, nb, ms = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len,
+                                cfg.n_blk, cfg.max_sel_blocks)
+    code = {"dense": FDL_LAYER_DENSE, "source": FDL_LAYER_SOURCE, "reuse": FDL_LAYER_REUSE}
+    t = [{k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec")} for x in xs]
+    ks = [torch.zeros((B, Hkv, nb, D), dtype=torch.float32, device="cuda") for _ in modes]
+    outs = [torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device="cuda") for _ in modes]
+    for l in range(len(modes)):
+        h.fdl_pool_keys(g, t[l]["k"], None, cfg.kv_block, ks[l])
+    pm = torch.zeros(B, dtype=torch.int64, device="cuda")
+    npd = torch.zeros(B, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, Hkv, nb), dtype=torch.float32, device="cuda")
+    sp = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device="cuda")
+    nsk = torch.zeros(B, dtype=torch.int32, device="cuda")
+    sel = torch.zeros((B, Hkv, ms), dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, ms, cfg.sink_tau)
+    table = h.make_layers(g, [dict(q=t[l]["q"], k_cache=t[l]["k"], v_cache=t[l]["v"], k_dec=t[l]["k_dec"],
+                                   v_dec=t[l]["v_dec"], ks=ks[l], out=outs[l], mode=code[m])
+                              for l, m in enumerate(modes)])
+    pc = dev(prev_conf) if prev_conf is not None else None
+    mk = dev(masked)
+    res = {"layers": {}}
+
+    def step(n):
+        sub = (table._type_ * n)(*table[:n]) if n < len(modes) else table
+        h.fdl_focus_step(g, params, pc, mk, sub, pm, npd, sc, sp, nsk, sel, nsel)
+        torch.cuda.synchronize()
+
+    for l, m in enumerate(modes):
+        if m != "dense":
+            step(l + 1)
+            res["layers"][l] = (host(sc).copy(), host(sel).copy(), host(nsel).copy())
+    step(len(modes))
+    st, bits = h.fdl_get_status_bits()
+    assert st == 0, st
+    res.update(outs=outs, pred_mask=host(pm).view(np.uint64).copy(), sink_pos=host(sp).copy(),
+               n_sinks=host(nsk).copy(), bits=bits)
+    return res
+
+
+def check_focus_step_layers(cfg, got, xs, modes, prev_conf, masked, what=""):
+    """Every layer of a focus_step_layers run against the oracle run one layer at a time: predicted
+    positions and sinks bit for bit, every sparse layer's scores and selection bit for bit, outputs
+    within tolerance.  Returns the oracle's per-layer results."""
+    from gpu_util import bf16_out_to_f64
+    from oracle.pipeline import focus_layer_step
+    sinks = None
+    wants = []
+    for l, m in enumerate(modes):
+        x = dict(xs[l], prev_conf=prev_conf, masked=masked)
+        want = focus_layer_step(cfg, x, m, sinks=sinks)
+        wants.append(want)
+        assert np.array_equal(got["pred_mask"], np.asarray(want["pred_mask"], np.uint64)), (what, l)
+        if m == "source":
+            assert want["sink_margin"] > 1e-4 * cfg.sink_tau, f"flagged case: sink margin {want['sink_margin']:.3g}"
+            sinks = (want["sink_pos"], want["n_sinks"])
+            for b in range(cfg.batch):
+                nsb = int(want["n_sinks"][b])
+                assert int(got["n_sinks"][b]) == nsb, (what, b)
+                assert got["sink_pos"][b, :nsb].tolist() == want["sink_pos"][b, :nsb].tolist(), (what, b)
+        if m != "dense":
+            sc, sel, nsel = got["layers"][l]
+            assert np.array_equal(sc.view(np.uint32), want["scores"].view(np.uint32)), (what, l)
+            for b in range(cfg.batch):
+                for gh in range(cfg.n_kv_heads):
+                    w = want["sel"][b][gh].tolist()
+                    assert int(nsel[b, gh]) == len(w), (what, l, b, gh)
+                    assert sel[b, gh, :len(w)].tolist() == w, (what, l, b, gh)
+        assert_close(bf16_out_to_f64(got["outs"][l]), want["out"], f"{what} layer {l} ({m})")
+    return wants

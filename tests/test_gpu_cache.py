@@ -125,3 +125,53 @@ def test_cache_write_float32(h):
     assert np.array_equal(_bits(host(kc)), _bits(wk))
     assert np.array_equal(_bits(host(vc)), _bits(wv))
     assert np.array_equal(host(ks).view(np.uint32), wks.view(np.uint32))
+
+
+@pytest.mark.parametrize("unit", [64, 512], ids=["block-units", "chunk-units"])
+def test_cache_write_bad_page(h, unit):
+    """One page-table entry out of range inside the written rows: those rows are written nowhere
+    (every page of the pool other than the rows the valid entries own is bit-identical afterwards,
+    page 0 included), they count +0 in the pooled keys, and FDL_EINDEX is reported.  fdl_pool_keys
+    over the same table pools those rows as +0 too."""
+    from diffusion_long_context_amd.fdllm import FDL_EINDEX
+    from diffusion_long_context_amd.step import geom_for
+    cfg = get_config(4).with_(batch=2, n_q_heads=4, n_kv_heads=4, ctx_len=4096, chunk_tokens=512)
+    g = geom_for(cfg)
+    rng = np.random.default_rng(77 + unit)
+    P, npp, n_pages = cfg.page_tokens, cfg.pages_per_seq, cfg.n_pages
+    B, H, D, L = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len
+    kp, vp = _vals(rng, (n_pages, H, P, D), False), _vals(rng, (n_pages, H, P, D), False)
+    pt = rng.permutation(n_pages).astype(np.int32).reshape(B, npp)
+    t0, n = 900, 1500                       # logical pages 14 .. 37 of each sequence
+    bad_b, bad_j = 1, 20
+    orphan = int(pt[bad_b, bad_j])
+    pt[bad_b, bad_j] = n_pages + 5
+    kn, vn = _vals(rng, (B, H, n, D), False), _vals(rng, (B, H, n, D), False)
+    n_units = L // unit
+    stale = rng.standard_normal((B, H, n_units, D)).astype(np.float32)
+    kc, vc, ks = dev(kp), dev(vp), dev(stale)
+    h.fdl_cache_write(g, dev(kn), dev(vn), t0, kc, vc, dev(pt), unit, ks)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == FDL_EINDEX
+    # the expected pool: the bad entry redirected to an extra page that is dropped afterwards
+    pt_ext = pt.copy()
+    pt_ext[bad_b, bad_j] = n_pages
+    zero_page = np.zeros((1, H, P, D), np.uint16)
+    want_k = write_paged(np.concatenate([kp, zero_page]), pt_ext, P, kn, t0)
+    want_v = write_paged(np.concatenate([vp, zero_page]), pt_ext, P, vn, t0)
+    got_k, got_v = host(kc).view(np.uint16), host(vc).view(np.uint16)
+    assert np.array_equal(got_k, want_k[:n_pages]) and np.array_equal(got_v, want_v[:n_pages])
+    assert np.array_equal(got_k[orphan], kp[orphan]) and np.array_equal(got_k[0], want_k[0])
+    want_k[n_pages] = 0                     # a row without a page has no key
+    fresh = pool_keys(gather_logical(want_k, pt_ext, P), unit)
+    touched = set(touched_units(t0, n, unit))
+    got = host(ks)
+    for u in range(n_units):
+        want = fresh[:, :, u] if u in touched else stale[:, :, u]
+        assert np.array_equal(got[:, :, u].view(np.uint32), want.view(np.uint32)), u
+    # the pooling call on the same table
+    ks2 = dev(np.zeros((B, H, n_units, D), np.float32))
+    h.fdl_pool_keys(g, kc, dev(pt), unit, ks2)
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == FDL_EINDEX
+    assert np.array_equal(host(ks2).view(np.uint32), fresh.view(np.uint32))

@@ -1,0 +1,205 @@
+"""Failure handling on the GPU: device-side overflows, out-of-range page ids and the geometry checks,
+each through the bound library with real device buffers.
+
+* More sinks than max_sinks: FDL_EOVERFLOW, and the list is the oracle's truncation (the first
+  max_sinks positions, ascending); the selection that follows uses exactly that list.
+* More sink candidates than the workspace holds: FDL_EOVERFLOW with the candidate flag, and the list
+  is still a valid ascending list of positions.
+* A page id outside the pool in paged attention: FDL_EINDEX, and that page's rows are skipped (the
+  output equals the oracle's attention without them).
+* Geometry outside the limits: FDL_EINVAL / FDL_EUNSUPPORTED before anything runs, outputs untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_close, dev, host, out_buffer, out_to_f64, require_gpu
+from layer_util import _focus
+from oracle.attention import attend, blocks_to_tokens
+from oracle.pipeline import focus_layer_step
+from synth import get_config
+from synth.gen import make_single
+
+pytestmark = pytest.mark.gpu
+
+FLAG_SINK, FLAG_CAND, FLAG_BAD = 1, 2, 4
+
+
+@pytest.fixture(scope="module")
+def h():
+    require_gpu()
+    from diffusion_long_context_amd import Handle
+    hh = Handle(workspace_bytes=256 << 20)
+    yield hh
+    hh.close()
+
+
+def _overflow_cfg():
+    # tau far below the planted sinks' mass: 23 tokens pass it (margin 0.4 % of tau), 8 fit
+    return get_config(1).with_(n_q_heads=4, n_kv_heads=4, ctx_len=4096, sink_tau=5e-4, max_sinks=8)
+
+
+def test_sink_overflow_keeps_the_oracle_truncation(h):
+    from diffusion_long_context_amd.fdllm import FDL_EOVERFLOW
+    from diffusion_long_context_amd.step import FocusParams, FocusStep, geom_for
+    cfg = _overflow_cfg()
+    x = make_single(cfg)
+    want = focus_layer_step(cfg, x, "source")
+    assert want["sink_overflow"][0] and want["sink_margin"] > 1e-4 * cfg.sink_tau
+    g = geom_for(cfg)
+    fs = FocusStep(h, g, FocusParams(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.sink_tau, cfg.max_sinks))
+    t = {k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec", "masked", "prev_conf")}
+    fs.predict(t["prev_conf"], t["masked"])
+    ks = fs.new_ks()
+    fs.pool(t["k"], ks)
+    out = out_buffer(cfg)
+    fs.layer("source", t["q"], t["k"], t["v"], t["k_dec"], t["v_dec"], ks, out)
+    st, bits = h.fdl_get_status_bits()
+    assert st == FDL_EOVERFLOW and bits & FLAG_SINK and not bits & FLAG_CAND, (st, bits)
+    n = int(want["n_sinks"][0])
+    assert n == cfg.max_sinks
+    assert int(host(fs.n_sinks)[0]) == n
+    assert host(fs.sink_pos)[0, :n].tolist() == want["sink_pos"][0, :n].tolist()
+    for gg in range(cfg.n_kv_heads):
+        w = want["sel"][0][gg].tolist()
+        assert int(host(fs.n_sel)[0, gg]) == len(w) and host(fs.sel_idx)[0, gg, :len(w)].tolist() == w
+    assert_close(out_to_f64(cfg, out), want["out"], "source layer after a sink overflow")
+    # the same layer through the one-call step driver (fused scoring, selection and attention)
+    from diffusion_long_context_amd.fdllm import FDL_LAYER_SOURCE, fdl_focus_params
+    out2 = out_buffer(cfg)
+    table = h.make_layers(g, [dict(q=t["q"], k_cache=t["k"], v_cache=t["v"], k_dec=t["k_dec"], v_dec=t["v_dec"],
+                                   ks=ks, out=out2, mode=FDL_LAYER_SOURCE)])
+    params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, fs.max_sel, cfg.sink_tau)
+    h.fdl_focus_step(g, params, t["prev_conf"], t["masked"], table, fs.pred_mask, fs.n_pred, fs.scores,
+                     fs.sink_pos, fs.n_sinks, fs.sel_idx, fs.n_sel)
+    st, bits = h.fdl_get_status_bits()
+    assert st == FDL_EOVERFLOW and bits & FLAG_SINK, (st, bits)
+    assert host(fs.sink_pos)[0, :n].tolist() == want["sink_pos"][0, :n].tolist()
+    for gg in range(cfg.n_kv_heads):
+        w = want["sel"][0][gg].tolist()
+        assert host(fs.sel_idx)[0, gg, :len(w)].tolist() == w
+    assert_close(out_to_f64(cfg, out2), want["out"], "fused source layer after a sink overflow")
+
+
+def test_sink_candidate_overflow(h):
+    """tau far below every token's mass at 8K: every token of every head is a candidate, past the
+    workspace's 1024 per head.  The call reports it; the list it leaves is valid."""
+    from diffusion_long_context_amd.fdllm import FDL_EOVERFLOW
+    from diffusion_long_context_amd.step import FocusParams, FocusStep, geom_for
+    cfg = get_config(1).with_(n_q_heads=4, n_kv_heads=4, sink_tau=1e-7, max_sinks=64)
+    x = make_single(cfg)
+    g = geom_for(cfg)
+    fs = FocusStep(h, g, FocusParams(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.sink_tau, cfg.max_sinks))
+    t = {k: dev(x[k]) for k in ("q", "k", "k_dec", "masked", "prev_conf")}
+    fs.predict(t["prev_conf"], t["masked"])
+    ks = fs.new_ks()
+    fs.pool(t["k"], ks)
+    print("candidate overflow: 8K, 4 heads", flush=True)
+    h.fdl_score_blocks(g, t["q"], fs.pred_mask, ks, cfg.kv_block, fs.scores, k_cache=t["k"], k_dec=t["k_dec"],
+                       detect_sinks=True, sink_tau=cfg.sink_tau, max_sinks=cfg.max_sinks, sink_pos=fs.sink_pos,
+                       n_sinks=fs.n_sinks)
+    st, bits = h.fdl_get_status_bits()
+    assert st == FDL_EOVERFLOW and bits & FLAG_CAND, (st, bits)
+    n = int(host(fs.n_sinks)[0])
+    assert 0 < n <= cfg.max_sinks
+    sp = host(fs.sink_pos)[0, :n].tolist()
+    assert sp == sorted(set(sp)) and all(0 <= s < cfg.ctx_len for s in sp)
+    # the next detection on the same handle starts clean
+    cfg2 = cfg.with_(sink_tau=0.03)
+    h.fdl_score_blocks(g, t["q"], fs.pred_mask, ks, cfg.kv_block, fs.scores, k_cache=t["k"], k_dec=t["k_dec"],
+                       detect_sinks=True, sink_tau=cfg2.sink_tau, max_sinks=cfg.max_sinks, sink_pos=fs.sink_pos,
+                       n_sinks=fs.n_sinks)
+    assert h.fdl_get_status() == 0
+    want = focus_layer_step(cfg2, x, "source", with_output=False)
+    nw = int(want["n_sinks"][0])
+    assert int(host(fs.n_sinks)[0]) == nw and host(fs.sink_pos)[0, :nw].tolist() == want["sink_pos"][0, :nw].tolist()
+
+
+@pytest.mark.parametrize("sparse", [False, True], ids=["dense", "sparse"])
+def test_paged_attention_bad_page(h, sparse):
+    """One page-table entry of sequence 1 points outside the pool: its 64 rows are skipped (read from
+    nowhere), FDL_EINDEX is reported, every other output is the oracle's, and the rows of that
+    sequence are attended without the page."""
+    from diffusion_long_context_amd.fdllm import FDL_EINDEX
+    from diffusion_long_context_amd.step import geom_for
+    cfg = get_config(4).with_(batch=2, n_q_heads=4, n_kv_heads=4, ctx_len=4096, chunk_tokens=512)
+    x = make_single(cfg)
+    g = geom_for(cfg)
+    P = cfg.page_tokens
+    pt = x["page_table"].copy()
+    bad_j = 9
+    pt[1, bad_j] = cfg.n_pages + 3
+    L, B, Hkv = cfg.ctx_len, cfg.batch, cfg.n_kv_heads
+    blocks = [[[0, 3, 9, 10, 40, 63] for _ in range(Hkv)] for _ in range(B)]
+    out = out_buffer(cfg)
+    if sparse:
+        sel = dev(np.array(blocks, np.int32))
+        nsel = dev(np.full((B, Hkv), 6, np.int32))
+        h.fdl_sparse_attn(g, dev(x["q"]), dev(x["k_pool"]), dev(x["v_pool"]), dev(x["k_dec"]), dev(x["v_dec"]),
+                          dev(pt), sel, nsel, 6, cfg.kv_block, out)
+        toks = [[blocks_to_tokens(blocks[b][gg], cfg.kv_block, L) for gg in range(Hkv)] for b in range(B)]
+    else:
+        h.fdl_dense_attn(g, dev(x["q"]), dev(x["k_pool"]), dev(x["v_pool"]), dev(x["k_dec"]), dev(x["v_dec"]),
+                         dev(pt), out)
+        toks = [[np.arange(L) for _ in range(Hkv)] for _ in range(B)]
+    torch.cuda.synchronize()
+    st, bits = h.fdl_get_status_bits()
+    assert st == FDL_EINDEX and bits & FLAG_BAD, (st, bits)
+    skip = set(range(bad_j * P, (bad_j + 1) * P))
+    toks[1] = [np.array([t for t in ts if t not in skip], np.int64) for ts in toks[1]]
+    want = attend(x["q"], x["k"], x["v"], x["k_dec"], x["v_dec"], toks)
+    assert_close(out_to_f64(cfg, out), want, "paged attention with a bad page")
+
+
+def test_geometry_errors_leave_outputs_untouched(h):
+    """Shapes outside the limits fail before anything is launched: the output keeps its sentinel."""
+    from diffusion_long_context_amd.fdllm import (FDL_EINVAL, FDL_EUNSUPPORTED, FdlError, Geom,
+                                                  FDL_LAYER_REUSE, fdl_focus_params)
+    B, L, D, T = 1, 1024, 128, 32
+    q = torch.zeros((B, 16, 65, D), dtype=torch.int16, device="cuda")
+    k = torch.zeros((B, 8, L, D), dtype=torch.int16, device="cuda")
+    ks = torch.zeros((B, 8, L // 64, D), dtype=torch.float32, device="cuda")
+    out = torch.full((B, 16, 65, D), 7, dtype=torch.int16, device="cuda")
+    sel = torch.zeros((B, 8, 16), dtype=torch.int32, device="cuda")
+    nsel = torch.full((B, 8), 4, dtype=torch.int32, device="cuda")
+    cases = [
+        (Geom(B, 6, 4, D, L, 64, T), FDL_EINVAL),            # Hq not a multiple of Hkv
+        (Geom(B, 8, 8, 96, L, 64, T), FDL_EUNSUPPORTED),     # head_dim 96
+        (Geom(B, 8, 8, D, L, 64, 65), FDL_EINVAL),           # dec_len 65
+        (Geom(B, 8, 8, D, L, 64, 48), FDL_EUNSUPPORTED),     # bf16 attention needs dec_len <= 32
+        (Geom(B, 8, 8, D, L, 48, T), FDL_EINVAL),            # kv_block not a power of two
+        (Geom(B, 16, 1, D, L, 64, T), FDL_EUNSUPPORTED),     # more than 8 q-heads per KV head
+    ]
+    for g, code in cases:
+        with pytest.raises(FdlError) as e:
+            h.fdl_sparse_attn(g, q, k, k, q, q, None, sel, nsel, 16, 64, out)
+        assert e.value.status == code, (g, e.value)
+    g = Geom(B, 8, 8, D, L, 64, T)
+    params = fdl_focus_params(4, 4, 8, 4, 2, 0.03)           # max_sel 2 < max_sinks + top_k
+    table = h.make_layers(g, [dict(q=q, k_cache=k, v_cache=k, k_dec=q, v_dec=q, ks=ks, out=out, mode=FDL_LAYER_REUSE)])
+    masked = torch.ones((B, T), dtype=torch.uint8, device="cuda")
+    pm = torch.zeros(B, dtype=torch.int64, device="cuda")
+    npd = torch.zeros(B, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, 8, L // 64), dtype=torch.float32, device="cuda")
+    sp = torch.zeros((B, 4), dtype=torch.int32, device="cuda")
+    nsk = torch.zeros(B, dtype=torch.int32, device="cuda")
+    with pytest.raises(FdlError) as e:
+        h.fdl_focus_step(g, params, None, masked, table, pm, npd, sc, sp, nsk, sel, nsel)
+    assert e.value.status == FDL_EINVAL
+    torch.cuda.synchronize()
+    assert h.fdl_get_status() == 0
+    assert bool((out == 7).all())
+    assert int(npd.abs().sum()) == 0 and int(pm.abs().sum()) == 0
+
+
+def test_top_k_beyond_the_blocks_keeps_everything(h):
+    """K larger than the blocks left after the sinks is no error: every block is kept (the sparse
+    layer then equals the dense one up to rounding)."""
+    cfg = get_config(1).with_(n_q_heads=4, n_kv_heads=4, ctx_len=1000, top_k_blocks=40)
+    x = make_single(cfg)
+    got = _focus(h, cfg, x, modes=("source", "dense"))
+    n_blk = -(-cfg.ctx_len // cfg.kv_block)
+    for gg in range(cfg.n_kv_heads):
+        assert got["source"]["n_sel"][0, gg] == n_blk
+        assert got["source"]["sel"][0, gg, :n_blk].tolist() == list(range(n_blk))
+    assert_close(got["source"]["out"], got["dense"]["out"], "all blocks kept vs dense")

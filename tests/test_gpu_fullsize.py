@@ -5,8 +5,9 @@
   generation steps: the first step of the first block (no previous confidence, every position
   predicted), a mid-block step and the last step.  Sampled outputs -- a dense layer, the sink-source
   layer, the first reuse layer and the last one -- are checked element by element against the
-  oracle run one layer at a time; the predicted positions, the sinks and the last layer's selection
-  are checked bit for bit.
+  oracle run one layer at a time; the predicted positions and the sinks are checked bit for bit, and
+  so are the block scores and the selection of the sink-source layer, the first reuse layer and the
+  last layer (the step is run again cut after layers 2 and 3 to read theirs).
 * The chunked, paged 32K workload with batch 4, in full.
 """
 import numpy as np
@@ -81,8 +82,18 @@ def test_focus_step_32k_32layer_as_benchmarked():
             got_pred = host(pred_mask).view(np.uint64)
             got_sinks = (host(sink_pos).copy(), host(n_sinks).copy())
             got_sel = (host(sel_idx).copy(), host(n_sel).copy())
-            got_scores = host(scores).copy()
             got_out = {l: bf16_out_to_f64(outs[l]) for l in CHECK_LAYERS}
+            # scores and selection of every checked sparse layer: the full step leaves the last
+            # layer's; the step cut after layer 2 (the sink source) and after layer 3 (the first reuse
+            # layer) leaves theirs
+            cut = {NL - 1: (host(scores).copy(), got_sel[0], got_sel[1])}
+            for lc in (cfg.source_layer, cfg.source_layer + 1):
+                sub = (table._type_ * (lc + 1))(*table[:lc + 1])
+                h.fdl_focus_step(g, params, conf, masked, sub, pred_mask, n_pred, scores, sink_pos, n_sinks,
+                                 sel_idx, n_sel)
+                torch.cuda.synchronize()
+                assert h.fdl_get_status() == 0
+                cut[lc] = (host(scores).copy(), host(sel_idx).copy(), host(n_sel).copy())
 
             sinks = None
             for l in CHECK_LAYERS:
@@ -102,12 +113,13 @@ def test_focus_step_32k_32layer_as_benchmarked():
                     assert int(got_sinks[1][0]) == nsb
                     assert got_sinks[0][0, :nsb].tolist() == want["sink_pos"][0, :nsb].tolist()
                     sinks = (want["sink_pos"], want["n_sinks"])
-                if l == NL - 1:
-                    assert np.array_equal(got_scores.view(np.uint32), want["scores"].view(np.uint32)), gstep
+                if l in cut:
+                    c_scores, c_sel, c_nsel = cut[l]
+                    assert np.array_equal(c_scores.view(np.uint32), want["scores"].view(np.uint32)), (gstep, l)
                     for gh in range(Hkv):
                         w = want["sel"][0][gh].tolist()
-                        assert int(got_sel[1][0, gh]) == len(w), (gstep, gh)
-                        assert got_sel[0][0, gh, : len(w)].tolist() == w, (gstep, gh)
+                        assert int(c_nsel[0, gh]) == len(w), (gstep, l, gh)
+                        assert c_sel[0, gh, : len(w)].tolist() == w, (gstep, l, gh)
                 assert_close(got_out[l], want["out"], f"step {gstep} layer {l} ({mode})")
     finally:
         h.close()

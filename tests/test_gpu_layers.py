@@ -211,38 +211,62 @@ def test_dense_attention_paged(h, kw):
     dict(ctx_len=6000, top_k_blocks=40, n_kv_heads=2, spin_limit=0),   # the same, grouped-query
     dict(ctx_len=5000, top_k_blocks=24, n_kv_heads=1, head_dim=64, dec_len=20),   # G = 8, D 64, ragged
     dict(batch=3, ctx_len=3000, top_k_blocks=16, n_kv_heads=4, kv_block=32),      # G = 2, 32-token blocks
+    dict(n_q_heads=28, n_kv_heads=4, ctx_len=6000, top_k_blocks=20),              # G = 7 (Dream-shaped)
+    dict(batch=2, n_q_heads=12, n_kv_heads=4, ctx_len=5000, top_k_blocks=12),     # G = 3, ragged
+    dict(n_q_heads=28, n_kv_heads=4, ctx_len=6000, top_k_blocks=20, spin_limit=0),   # G = 7 never waiting
 ], ids=["list-below-topk", "list-above-topk", "scattered-sinks", "gqa4", "one-split", "641-blocks",
-        "no-wait-fallback", "gqa4-no-wait-fallback", "gqa8-d64-ragged-T20", "gqa2-b3-bt32"])
+        "no-wait-fallback", "gqa4-no-wait-fallback", "gqa8-d64-ragged-T20", "gqa2-b3-bt32", "gqa7",
+        "gqa3-b2-ragged", "gqa7-no-wait-fallback"])
 def test_focus_step_driver(kw, monkeypatch):
     """fdl_focus_step (one call: predict, then dense / source / reuse / reuse layers) against the
-    oracle layer by layer.  The sparse layers run scoring, selection and attention as one fused
-    kernel: with one q-head per KV head the splits of a head share the scoring, with grouped-query
-    heads the G heads of a (KV head, split) group do (the other groups exchange through workspace
-    rows)."""
+    oracle layer by layer: predicted positions, sinks, and every sparse layer's scores and selection
+    bit for bit (the step is also run cut after each sparse layer to read them), outputs within
+    tolerance.  The sparse layers run scoring, selection and attention as one fused kernel: with one
+    q-head per KV head the splits of a head share the scoring, with grouped-query heads the G heads
+    of a (KV head, split) group do (the other groups exchange through workspace rows)."""
     require_gpu()
     from diffusion_long_context_amd import Handle
-    from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
-                                                  fdl_focus_params)
-    from diffusion_long_context_amd.step import geom_for
-    from gpu_util import bf16_out_to_f64, dev, host
+    from layer_util import check_focus_step_layers, focus_step_layers
     kw = dict(kw)
     spin = kw.pop("spin_limit", None)
     if spin is not None:
         monkeypatch.setenv("FDL_SPIN_LIMIT", str(spin))   # read when the handle is created
     cfg = get_config(1).with_(**dict(dict(n_q_heads=8, n_kv_heads=8), **kw))
-    g = geom_for(cfg)
-    B, Hq, Hkv, D, T, nb, ms = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len,
-                                cfg.n_blk, cfg.max_sel_blocks)
     modes = ["dense", "source", "reuse", "reuse"]
-    code = {"dense": FDL_LAYER_DENSE, "source": FDL_LAYER_SOURCE, "reuse": FDL_LAYER_REUSE}
     xs = [make_single(cfg, layer=l) for l in range(len(modes))]
     h = Handle(workspace_bytes=512 << 20)
     try:
-        t = [{k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec")} for x in xs]
-        ks = [torch.zeros((B, Hkv, nb, D), dtype=torch.float32, device="cuda") for _ in modes]
-        outs = [torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device="cuda") for _ in modes]
-        for l in range(len(modes)):
-            h.fdl_pool_keys(g, t[l]["k"], None, cfg.kv_block, ks[l])
+        print(f"focus step driver {kw}", flush=True)
+        got = focus_step_layers(h, cfg, xs, modes, xs[0]["prev_conf"], xs[0]["masked"])
+        # FDL_FLAG_SPLIT_FALLBACK: a fused split scored every block itself (only when it may not wait)
+        assert got["bits"] == (16 if spin == 0 else 0), got["bits"]
+        check_focus_step_layers(cfg, got, xs, modes, xs[0]["prev_conf"], xs[0]["masked"], str(kw))
+    finally:
+        h.close()
+
+
+def test_focus_step_profile_runs():
+    """The profiler's reuse-run records: the two trailing reuse layers of a step are one run of two
+    launches, and a run's time covers its layers."""
+    require_gpu()
+    from diffusion_long_context_amd import Handle
+    from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
+                                                  fdl_focus_params)
+    from diffusion_long_context_amd.step import geom_for
+    cfg = get_config(1).with_(n_q_heads=8, n_kv_heads=8, ctx_len=6000, top_k_blocks=40)
+    g = geom_for(cfg)
+    B, Hq, Hkv, D, T, nb, ms = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len,
+                                cfg.n_blk, cfg.max_sel_blocks)
+    modes = [FDL_LAYER_DENSE, FDL_LAYER_SOURCE, FDL_LAYER_REUSE, FDL_LAYER_REUSE]
+    x = make_single(cfg)
+    h = Handle(workspace_bytes=512 << 20)
+    try:
+        t = {k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec")}
+        ks = torch.zeros((B, Hkv, nb, D), dtype=torch.float32, device="cuda")
+        h.fdl_pool_keys(g, t["k"], None, cfg.kv_block, ks)
+        out = torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device="cuda")
+        table = h.make_layers(g, [dict(q=t["q"], k_cache=t["k"], v_cache=t["v"], k_dec=t["k_dec"], v_dec=t["v_dec"],
+                                       ks=ks, out=out, mode=m) for m in modes])
         pm = torch.zeros(B, dtype=torch.int64, device="cuda")
         npd = torch.zeros(B, dtype=torch.int32, device="cuda")
         sc = torch.zeros((B, Hkv, nb), dtype=torch.float32, device="cuda")
@@ -250,42 +274,42 @@ def test_focus_step_driver(kw, monkeypatch):
         nsk = torch.zeros(B, dtype=torch.int32, device="cuda")
         sel = torch.zeros((B, Hkv, ms), dtype=torch.int32, device="cuda")
         nsel = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
-        params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, ms,
-                                  cfg.sink_tau)
-        table = h.make_layers(g, [dict(q=t[l]["q"], k_cache=t[l]["k"], v_cache=t[l]["v"],
-                                       k_dec=t[l]["k_dec"], v_dec=t[l]["v_dec"], ks=ks[l], out=outs[l],
-                                       mode=code[m]) for l, m in enumerate(modes)])
-        x0 = xs[0]
+        params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, ms, cfg.sink_tau)
         h.fdl_profile_begin(16, kinds=("reuse_run", "layer_reuse", "layer_dense"), every=1)
-        h.fdl_focus_step(g, params, dev(x0["prev_conf"]), dev(x0["masked"]), table, pm, npd, sc, sp, nsk,
-                         sel, nsel)
+        h.fdl_focus_step(g, params, dev(x["prev_conf"]), dev(x["masked"]), table, pm, npd, sc, sp, nsk, sel, nsel)
         prof = h.fdl_profile_end()
-        # the two trailing reuse layers: one run of two launches; a run spans at least its layers
         assert prof["reuse_run"][1] == 2 and prof["layer_reuse"][1] == 2 and prof["layer_dense"][1] == 1
         assert prof["reuse_run"][0] >= 0.9 * prof["layer_reuse"][0] > 0
-        torch.cuda.synchronize()
-        status, bits = h.fdl_get_status_bits()
-        assert status == 0
-        # FDL_FLAG_SPLIT_FALLBACK: a fused split scored every block itself (only when it may not wait)
-        assert bits == (16 if spin == 0 else 0), bits
-        sinks = None
+        assert h.fdl_get_status() == 0
+    finally:
+        h.close()
+
+
+def test_focus_step_dream7b_gqa_16k_full():
+    """The Dream-shaped grouped-query workload (28 query heads over 4 KV heads, G = 7, head_dim 128,
+    16K context, 32 blocks kept per KV head, 8 planted relevant blocks per KV head) at full size
+    through fdl_focus_step, the call the benchmark times: dense, source, reuse, reuse layers, each with
+    its own seeded inputs.  Predicted positions, sinks and every sparse layer's scores and selection
+    bit for bit, outputs within tolerance, and every planted block selected."""
+    require_gpu()
+    from diffusion_long_context_amd import Handle
+    from layer_util import check_focus_step_layers, focus_step_layers
+    cfg = get_config(2)
+    assert (cfg.n_q_heads, cfg.n_kv_heads, cfg.ctx_len) == (28, 4, 16384)
+    modes = ["dense", "source", "reuse", "reuse"]
+    xs = [make_single(cfg, layer=l) for l in range(len(modes))]
+    h = Handle(workspace_bytes=512 << 20)
+    try:
+        print("dream7b-shaped 16K grouped-query step, 4 layers", flush=True)
+        got = focus_step_layers(h, cfg, xs, modes, xs[0]["prev_conf"], xs[0]["masked"])
+        assert got["bits"] == 0, got["bits"]
+        check_focus_step_layers(cfg, got, xs, modes, xs[0]["prev_conf"], xs[0]["masked"], "16K GQA")
         for l, m in enumerate(modes):
-            x = dict(xs[l], prev_conf=x0["prev_conf"], masked=x0["masked"])
-            want = focus_layer_step(cfg, x, m, sinks=sinks)
-            if m == "source":
-                assert want["sink_margin"] > 1e-4 * cfg.sink_tau
-                sinks = (want["sink_pos"], want["n_sinks"])
-                for b in range(B):
-                    nsb = int(want["n_sinks"][b])
-                    assert int(host(nsk)[b]) == nsb
-                    assert host(sp)[b, :nsb].tolist() == want["sink_pos"][b, :nsb].tolist()
-            if l == len(modes) - 1:
-                assert np.array_equal(host(sc).view(np.uint32), want["scores"].view(np.uint32))
-                for b in range(B):
-                    for gh in range(Hkv):
-                        w = want["sel"][b][gh].tolist()
-                        assert int(host(nsel)[b, gh]) == len(w), (b, gh)
-                        assert host(sel)[b, gh, : len(w)].tolist() == w, (b, gh)
-            assert_close(bf16_out_to_f64(outs[l]), want["out"], f"layer {l} ({m})")
+            if m == "dense":
+                continue
+            _, sel, nsel = got["layers"][l]
+            for gh in range(cfg.n_kv_heads):
+                chosen = set(sel[0, gh, :int(nsel[0, gh])].tolist())
+                assert set(xs[l]["planted"][0, gh].tolist()) <= chosen, (l, gh)
     finally:
         h.close()
