@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "fdl_device.h"
@@ -572,30 +573,123 @@ fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* gp, const void*
                     n_sel);
 }
 
+// ---- sparse attention for callers that cannot allocate ------------------------------------------
+//
+// The split partials, the merge tickets and a status word live in one file-scope device array instead
+// of a handle's workspace.  Each GPU holds its own copy for the life of the process; host code
+// reaches it only through the address hipGetSymbolAddress returns for the current device (the array's
+// name on the host is a stand-in, not a device address).  Layout: status word at 0, tickets from
+// kStaticTicketOffset (left at zero by every launch), partials from kStaticPartialOffset.
+namespace {
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+constexpr size_t kStaticTicketOffset = 4096;
+constexpr size_t kStaticPartialOffset =
+    kStaticTicketOffset + (size_t)fdl::kMaxSplitSegs * fdl::kSyncStride * sizeof(uint32_t);
+constexpr size_t kStaticPartialBytes = kStaticScratchBytes - kStaticPartialOffset;
+constexpr int kStaticMaxDevices = 64;
+// the default workspace of fdl_create: the split count the handle calls would choose
+constexpr size_t kDefaultScratchBytes = ((size_t)64 << 20) - fdl::kHeaderBytes;
+
+struct StaticDev {
+  char* ptr = nullptr;   // device address of `scratch` on this device
+  int num_cus = 0;
+};
+std::mutex g_static_mu;
+StaticDev g_static[kStaticMaxDevices];
+}  // namespace
+
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+// Set-up, once per device: the array's device address and the compute-unit count; the status word
+// and the tickets are cleared by a fill kernel on the caller's stream (no memset node, so a first
+// call under graph capture records a kernel).
+static fdl_status static_scratch(hipStream_t stream, StaticDev* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FDL_EHIP;
+  if (dev >= kStaticMaxDevices) return FDL_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDev& d = g_static[dev];
+  if (d.ptr == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FDL_EHIP;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return FDL_EHIP;
+    if (fdl::launch_fill_u32(stream, static_cast<uint32_t*>(p), kStaticPartialOffset / sizeof(uint32_t), 0u) !=
+        hipSuccess)
+      return FDL_EHIP;
+    d.num_cus = cus;
+    d.ptr = static_cast<char*>(p);
+  }
+  *out = d;
+  return FDL_OK;
+}
+
+// Argument checks of the attention calls (h may be NULL: the codes are returned without a message).
+static fdl_status check_attn(fdl_handle h, const fdl_geom* gp, Geom& g, const void* q, const void* k_cache,
+                             const void* v_cache, const void* k_dec, const void* v_dec, const int32_t* page_table,
+                             const int32_t* sel_idx, const int32_t* n_sel, int32_t max_sel, int32_t sel_unit_tokens,
+                             int dense, const void* out, int* unit_log2) {
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!q || !k_dec || !v_dec || !out) return fail(h, FDL_EINVAL, "q, k_dec, v_dec and out must be non-NULL");
+  if (g.L > 0 && (!k_cache || !v_cache)) return fail(h, FDL_EINVAL, "k_cache and v_cache must be non-NULL");
+  if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
+  *unit_log2 = 0;
+  if (!dense) {
+    if (!sel_idx || !n_sel) return fail(h, FDL_EINVAL, "sel_idx and n_sel must be non-NULL");
+    if (max_sel < 1) return fail(h, FDL_EINVAL, "max_sel must be >= 1");
+    if (!is_pow2(sel_unit_tokens) || sel_unit_tokens > 4096)
+      return fail(h, FDL_EINVAL, "sel_unit_tokens must be a power of two in [1, 4096]");
+    *unit_log2 = ilog2(sel_unit_tokens);
+    if ((long long)max_sel * sel_unit_tokens >= (1LL << 30))
+      return fail(h, FDL_EUNSUPPORTED, "selection too large");
+  }
+  if (g.dtype == FDL_BF16 && g.T > 32) return fail(h, FDL_EUNSUPPORTED, "bf16 attention needs dec_len <= 32");
+  return FDL_OK;
+}
+
 static fdl_status attn_common(fdl_handle h, const fdl_geom* gp, const void* q, const void* k_cache,
                               const void* v_cache, const void* k_dec, const void* v_dec,
                               const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
                               int32_t max_sel, int32_t sel_unit_tokens, int dense, void* out) {
   if (!h) return FDL_EINVAL;
   Geom g;
-  fdl_status st = check_geom(h, gp, g);
-  if (st != FDL_OK) return st;
-  if (!q || !k_dec || !v_dec || !out) return fail(h, FDL_EINVAL, "q, k_dec, v_dec and out must be non-NULL");
-  if (g.L > 0 && (!k_cache || !v_cache)) return fail(h, FDL_EINVAL, "k_cache and v_cache must be non-NULL");
-  if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
   int unit_log2 = 0;
-  if (!dense) {
-    if (!sel_idx || !n_sel) return fail(h, FDL_EINVAL, "sel_idx and n_sel must be non-NULL");
-    if (max_sel < 1) return fail(h, FDL_EINVAL, "max_sel must be >= 1");
-    if (!is_pow2(sel_unit_tokens) || sel_unit_tokens > 4096)
-      return fail(h, FDL_EINVAL, "sel_unit_tokens must be a power of two in [1, 4096]");
-    unit_log2 = ilog2(sel_unit_tokens);
-    if ((long long)max_sel * sel_unit_tokens >= (1LL << 30))
-      return fail(h, FDL_EUNSUPPORTED, "selection too large");
-  }
-  if (g.dtype == FDL_BF16 && g.T > 32) return fail(h, FDL_EUNSUPPORTED, "bf16 attention needs dec_len <= 32");
+  const fdl_status st = check_attn(h, gp, g, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel,
+                                   sel_unit_tokens, dense, out, &unit_log2);
+  if (st != FDL_OK) return st;
   return run_attn(h, g, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel, unit_log2,
                   dense, out);
+}
+
+fdl_status fdl_sparse_attn_noalloc(void* hip_stream, const fdl_geom* gp, const void* q, const void* k_cache,
+                                   const void* v_cache, const void* k_dec, const void* v_dec,
+                                   const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
+                                   int32_t max_sel, int32_t sel_unit_tokens, void* out, uint32_t* status) {
+  Geom g;
+  int unit_log2 = 0;
+  fdl_status st = check_attn(nullptr, gp, g, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx, n_sel,
+                             max_sel, sel_unit_tokens, 0, out, &unit_log2);
+  if (st != FDL_OK) return st;
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  StaticDev d;
+  st = static_scratch(stream, &d);
+  if (st != FDL_OK) return st;
+  long long list_tokens = (long long)max_sel << unit_log2;
+  if (list_tokens > g.L) list_tokens = g.L;
+  int n_splits = 1;
+  if (g.dtype == FDL_BF16) {   // the split count fdl_sparse_attn takes with the default workspace
+    n_splits = fdl::mha_choose_splits(g, list_tokens, d.num_cus);
+    while (n_splits > 1 && fdl::attn_scratch_bytes(g, n_splits) > kDefaultScratchBytes) n_splits /= 2;
+  }
+  if (fdl::attn_scratch_bytes(g, n_splits) > kStaticPartialBytes) return FDL_ENOMEM;
+  uint32_t* stat = status ? status : reinterpret_cast<uint32_t*>(d.ptr);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(d.ptr + kStaticTicketOffset);
+  return hip_status(nullptr,
+                    fdl::launch_attn(stream, g, q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx, n_sel,
+                                     max_sel, unit_log2, 0, out, d.ptr + kStaticPartialOffset, n_splits, tickets,
+                                     stat, 0, nullptr),
+                    "attention launch");
 }
 
 fdl_status fdl_sparse_attn(fdl_handle h, const fdl_geom* g, const void* q, const void* k_cache,

@@ -29,6 +29,7 @@ EXPORTED = (
     "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_select_blocks_shared", "fdl_expand_tokens", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_unmask", "fdl_decode_steps", "fdl_capture_begin", "fdl_capture_end", "fdl_graph_launch",
     "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end", "fdl_bandwidth_probe",
+    "fdl_sparse_attn_noalloc",
 )
 
 FDL_LAYER_DENSE, FDL_LAYER_SOURCE, FDL_LAYER_REUSE = 0, 1, 2
@@ -98,6 +99,7 @@ _SIGS = {
     "fdl_profile_begin": (_I, [_P, _I, ctypes.c_uint32, _I]),
     "fdl_profile_end": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "fdl_bandwidth_probe": (_I, [_P, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _I]),
+    "fdl_sparse_attn_noalloc": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -165,6 +167,25 @@ def _ptr(t, nbytes: int | None = None, name: str = "tensor"):
 
 def _stream_ptr():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def fdl_sparse_attn_noalloc(g: "Geom", q, k_cache, v_cache, k_dec, v_dec, page_table, sel_idx, n_sel,
+                            max_sel: int, sel_unit_tokens: int, out, status=None):
+    """The allocation-free sparse attention on the current torch stream (no handle); raises FdlError
+    with the status code on an argument error."""
+    lib = load()
+    B, D, Hkv = g.batch, g.head_dim, g.n_kv_heads
+    qbytes = B * g.n_q_heads * g.dec_len * D * g.elem
+    dbytes = B * Hkv * g.dec_len * D * g.elem
+    kv = g.kv_elems * g.elem if g.ctx_len > 0 else None
+    st = lib.fdl_sparse_attn_noalloc(
+        _stream_ptr(), ctypes.byref(g.c()), _ptr(q, qbytes, "q"), _ptr(k_cache, kv, "k_cache"),
+        _ptr(v_cache, kv, "v_cache"), _ptr(k_dec, dbytes, "k_dec"), _ptr(v_dec, dbytes, "v_dec"),
+        _ptr(page_table, 4 * B * g.pages_per_seq if g.paged else None, "page_table"),
+        _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel"), max_sel,
+        sel_unit_tokens, _ptr(out, qbytes, "out"), _ptr(status, 4, "status"))
+    if st != FDL_OK:
+        raise FdlError(st, lib.fdl_status_string(st).decode())
 
 
 class Handle:

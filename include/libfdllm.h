@@ -279,6 +279,23 @@ fdl_status fdl_sparse_attn(fdl_handle h, const fdl_geom* g, const void* q, const
                            const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
                            int32_t max_sel, int32_t sel_unit_tokens, void* out);
 
+/* fdl_sparse_attn for callers that cannot allocate device memory -- code under HIP-graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc -- and so hold no handle: the same attention,
+ * arguments and results (the same split count as fdl_sparse_attn with the default workspace, so the
+ * outputs are bit for bit those of fdl_sparse_attn on a handle created with workspace_bytes = 0),
+ * launched on `hip_stream` (a hipStream_t; NULL = the null stream) with no allocation of any kind.
+ * The split partials, merge counters and a status word live in a static device array of 8 MiB that
+ * each GPU the library runs on holds until the process ends; every call on a GPU shares that GPU's
+ * array, so calls that overlap on one GPU (two streams, two threads) race and must be ordered by the
+ * caller.  `status` (a device uint32, may be NULL) has FDL_FLAG_* bits OR-ed into it for the
+ * device-side conditions (out-of-range unit or page ids, skipped); with NULL they are not reported.
+ * Argument errors return FDL_EINVAL / FDL_EUNSUPPORTED as fdl_sparse_attn (no message: there is no
+ * handle for fdl_last_error); FDL_ENOMEM when the split partials would exceed the static array. */
+fdl_status fdl_sparse_attn_noalloc(void* hip_stream, const fdl_geom* g, const void* q, const void* k_cache,
+                                   const void* v_cache, const void* k_dec, const void* v_dec,
+                                   const int32_t* page_table, const int32_t* sel_idx, const int32_t* n_sel,
+                                   int32_t max_sel, int32_t sel_unit_tokens, void* out, uint32_t* status);
+
 /* Dense baseline and the shallow full-attention layers ([FS]): the same attention over all L cached
  * tokens plus the own block. */
 fdl_status fdl_dense_attn(fdl_handle h, const fdl_geom* g, const void* q, const void* k_cache,
