@@ -385,6 +385,92 @@ def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
     return out
 
 
+PHASES = ("start", "query sum", "own scores", "score exchange", "scores read back", "selection",
+          "first tile landed", "wave 0 tiles done", "all tiles done", "merge ticket", "merge done",
+          "extra 11", "extra 12", "extra 13", "extra 14")
+
+
+def phase_timeline(samples: int = 24) -> dict:
+    """Phase timeline of the fused score-select-attend kernel on the benchmark's reuse layers, from the
+    diagnostic library built with --phase-stamps: the 32-layer step is run `samples` times (distinct
+    generation steps) and the stamps of its last layer's launch are read after each.  Per phase: the
+    median over workgroups of the time since the first workgroup started, averaged over the samples;
+    also the last workgroup's merge end."""
+    import numpy as np
+    import torch
+
+    from diffusion_long_context_amd import fdllm
+    from diffusion_long_context_amd.fdllm import FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE, fdl_focus_params
+    from diffusion_long_context_amd.step import geom_for
+    from synth import get_config
+    from synth.device import layer_kv, step_qkv_pool
+    from synth.gen import schedule_state
+
+    lib = fdllm.load(os.environ.get("FDL_STAMPS_LIB",
+                                    os.path.join(ROOT, "diffusion_long_context_amd", "libfdllm_stamps.so")))
+    assert lib.fdl_phase_stamps_built() == 1, "the stamps library was not built with --phase-stamps"
+    cfg = get_config(3)
+    g = geom_for(cfg)
+    NL, B, Hq, Hkv, D, T = cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len
+    dev = torch.device("cuda")
+    h = fdllm.Handle(workspace_bytes=WORKSPACE_BYTES)
+    K, V = zip(*[layer_kv(cfg, layer, dev) for layer in range(NL)])
+    Q, KD, VD = step_qkv_pool(cfg, samples + 2, dev)
+    ks = [torch.zeros((B, Hkv, cfg.n_blk, D), dtype=torch.float32, device=dev) for _ in range(NL)]
+    for layer in range(NL):
+        h.fdl_pool_keys(g, K[layer], None, cfg.kv_block, ks[layer])
+    outs = [torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    pm = torch.zeros(B, dtype=torch.int64, device=dev)
+    npd = torch.zeros(B, dtype=torch.int32, device=dev)
+    sc = torch.zeros((B, Hkv, cfg.n_blk), dtype=torch.float32, device=dev)
+    sp = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device=dev)
+    nsk = torch.zeros(B, dtype=torch.int32, device=dev)
+    sel = torch.zeros((B, Hkv, cfg.max_sel_blocks), dtype=torch.int32, device=dev)
+    nsel = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, cfg.max_sel_blocks,
+                              cfg.sink_tau)
+    modes = [FDL_LAYER_DENSE if l < cfg.dense_layers else (FDL_LAYER_SOURCE if l == cfg.source_layer else FDL_LAYER_REUSE)
+             for l in range(NL)]
+    stamps = torch.zeros(4096 * 16, dtype=torch.int64, device=dev)
+    h.fdl_set_phase_buffer(stamps)
+    rel = []
+    for i in range(samples + 2):
+        st = schedule_state(cfg, 33 + i)
+        conf = torch.from_numpy(st["prev_conf"]).to(dev) if st["prev_conf"] is not None else None
+        masked = torch.from_numpy(st["masked"]).to(dev)
+        table = h.make_layers(g, [dict(q=Q[i, l], k_cache=K[l], v_cache=V[l], k_dec=KD[i, l], v_dec=VD[i, l], ks=ks[l],
+                                       out=outs[l], mode=m) for l, m in enumerate(modes)])
+        stamps.zero_()
+        h.fdl_focus_step(g, params, conf, masked, table, pm, npd, sc, sp, nsk, sel, nsel)
+        torch.cuda.synchronize()
+        if i < 2:
+            continue   # warm
+        a = stamps.view(-1, 16).cpu().numpy()
+        live = a[:, 15] < 0   # bit 63 set: a workgroup of this launch
+        a = a[live].astype(np.float64)
+        t0 = a[:, 0].min()
+        rel.append({"wg": a[:, :15] - t0, "xcc": (stamps.view(-1, 16)[:, 15].cpu().numpy()[live] & 0xFFFFFFFF)})
+    assert h.fdl_get_status() == 0
+    h.fdl_set_phase_buffer(None)
+    h.close()
+    res = {"samples": len(rel), "workgroups": int(rel[0]["wg"].shape[0]), "clock_MHz": 100, "phases_us": {},
+           "last_workgroup_us": {}}
+    for j, name in enumerate(PHASES):
+        med, last = [], []
+        for r in rel:
+            col = r["wg"][:, j]
+            col = col[col >= 0] if j != 10 else col[r["wg"][:, 10] > 0]
+            if col.size:
+                med.append(np.median(col) / 100.0)
+                last.append(col.max() / 100.0)
+        res["phases_us"][name] = float(np.mean(med)) if med else None
+        res["last_workgroup_us"][name] = float(np.mean(last)) if last else None
+    x = rel[-1]["xcc"]
+    res["xcc_reg_values"] = sorted(set(int(v) for v in x))
+    res["xcc_reg_first16"] = [int(v) for v in x[:16]]
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,12 +481,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the other workloads' diagnostics")
     ap.add_argument("--cpu-baseline-child", action="store_true")
+    ap.add_argument("--phase-timeline", action="store_true",
+                    help="print the fused kernel's phase timeline (needs the --phase-stamps library) and exit")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, one plain elementwise copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.cpu_baseline_child:
         print(json.dumps(cpu_baseline_child()))
+        return
+    if args.phase_timeline:
+        print(json.dumps(phase_timeline()), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built",

@@ -1,6 +1,6 @@
 """Build libfdllm.so (all HIP sources for gfx950) in-tree.
 
-Usage: python -m diffusion_long_context_amd.build [--debug]
+Usage: python -m diffusion_long_context_amd.build [--phase-stamps] [--debug] [--out PATH]
 """
 from __future__ import annotations
 
@@ -58,6 +58,25 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB)
     return out
 
 
+def main(argv=None) -> str:
+    import argparse
+    ap = argparse.ArgumentParser(description="build libfdllm.so for gfx950")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="record the fused kernel's phase timestamps (diagnostic build)")
+    ap.add_argument("--debug", action="store_true",
+                    help="keep device-side assertions and host symbols (-O1 -g; FDL_DEBUG defined)")
+    ap.add_argument("--out", default=None, help="library path (default: the in-tree libfdllm.so, or "
+                                               "libfdllm_stamps.so / libfdllm_debug.so for the variants)")
+    a = ap.parse_args(argv)
+    extra, out = [], LIB
+    if a.phase_stamps:
+        extra.append("-DFDL_PHASE_STAMPS")
+        out = os.path.join(HERE, "libfdllm_stamps.so")
+    if a.debug:
+        extra += ["-DFDL_DEBUG", "-g"]
+        out = os.path.join(HERE, "libfdllm_debug.so")
+    return build(verbose=True, extra=extra, out=a.out or out)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
-    print(LIB)
+    print(main())

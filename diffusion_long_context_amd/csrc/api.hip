@@ -134,6 +134,7 @@ fdl_status check_sinks(fdl_handle h, const Geom& g, const void* k_cache, const v
     return fail(h, FDL_EUNSUPPORTED, "bf16 sink detection needs dec_len <= 32");
   const size_t need = fdl::sink_scratch_bytes(g, ns, cap);
   if (need > h->scratch_bytes) return fail(h, FDL_ENOMEM, "workspace too small for sink detection");
+  if (h->safe_sync) *ns = 1;   // one workgroup per head: nothing is merged across workgroups
   return FDL_OK;
 }
 
@@ -178,7 +179,7 @@ fdl_status run_attn(fdl_handle h, const Geom& g, const void* q, const void* k_ca
   ProfScope ps(h, dense ? FDL_PROF_DENSE_ATTN : FDL_PROF_SPARSE_ATTN, /*inner=*/true);
   return hip_status(h, fdl::launch_attn(h->stream, g, q, k_cache, v_cache, k_dec, v_dec, page_table,
                                         sel_idx, n_sel, max_sel, unit_log2, dense, out, h->scratch,
-                                        n_splits, h->tickets, h->status, n_hint, ps.timer()),
+                                        n_splits, h->tickets, h->status, n_hint, ps.timer(), h->safe_sync),
                     "attention launch");
 }
 
@@ -204,7 +205,11 @@ fdl_status run_select_attn(fdl_handle h, const Geom& g, const fdl_layer_io& io, 
   int n_splits = attn_splits(h, g, list_tokens);
   const int n_blk = (g.L + g.bt - 1) / g.bt;
   float* xchg = nullptr;
-  if (g.G > 1) {
+  if (g.G == 1 && n_splits > 1 && n_blk <= fdl::kFusedTaggedUnits && !h->safe_sync) {
+    // the splits' tagged score exchange: one 64-bit entry per (sequence, head, unit)
+    if (fused_xchg_offset(g, n_splits) + (size_t)g.B * g.Hkv * n_blk * sizeof(uint64_t) <= h->scratch_bytes)
+      xchg = reinterpret_cast<float*>(h->scratch + fused_xchg_offset(g, n_splits));
+  } else if (g.G > 1) {
     while (n_splits > 1 && ((long long)g.B * g.Hkv * n_splits > fdl::kMaxSplitSegs ||
                             fused_xchg_offset(g, n_splits) + (size_t)g.B * g.Hkv * n_splits * n_blk * sizeof(float) >
                                 h->scratch_bytes))
@@ -214,11 +219,13 @@ fdl_status run_select_attn(fdl_handle h, const Geom& g, const fdl_layer_io& io, 
     xchg = reinterpret_cast<float*>(h->scratch + fused_xchg_offset(g, n_splits));
   }
   const fdl::FusedSelect fs{pred_mask, io.ks,   sink_pos,    n_sinks,        fp->max_sinks, fp->top_k_blocks,
-                            scores,    sel_idx, n_sel,       h->barriers,    h->spin_limit, xchg};
+                            scores,    sel_idx, n_sel,       h->barriers,    h->spin_limit, xchg,
+                            h->stamps, h->stamp_words, h->fused_serial++};
   ProfScope ps(h, FDL_PROF_SPARSE_ATTN, /*inner=*/true);
   return hip_status(h, fdl::launch_attn_mha(h->stream, g, io.q, io.k_cache, io.v_cache, io.k_dec, io.v_dec,
                                             nullptr, sel_idx, n_sel, fp->max_sel, bt_log2, 0, io.out,
-                                            h->scratch, n_splits, h->tickets, h->status, 0, ps.timer(), &fs),
+                                            h->scratch, n_splits, h->tickets, h->status, 0, ps.timer(), &fs,
+                                            h->safe_sync),
                     "select-attention launch");
 }
 
@@ -235,6 +242,7 @@ const char* fdl_status_string(fdl_status s) {
     case FDL_EOVERFLOW: return "device-side capacity overflow (sinks or sink candidates)";
     case FDL_EUNSUPPORTED: return "shape outside the supported kernel set";
     case FDL_EINDEX: return "out-of-range unit or page index (rows skipped)";
+    case FDL_ESYNC: return "workgroups that merge through one L2 ran on different XCDs (outputs invalid)";
   }
   return "unknown status";
 }
@@ -275,6 +283,8 @@ fdl_status fdl_create(fdl_handle* out, void* hip_stream, size_t workspace_bytes)
   {
     const char* e = getenv("FDL_SPIN_LIMIT");
     h->spin_limit = e ? atoi(e) : 200000;
+    const char* safe = getenv("FDL_SAFE_SYNC");
+    h->safe_sync = safe != nullptr && safe[0] != '\0' && safe[0] != '0';
   }
   h->scratch = h->ws + fdl::kHeaderBytes;
   h->scratch_bytes = workspace_bytes - fdl::kHeaderBytes;
@@ -308,7 +318,8 @@ fdl_status fdl_get_status(fdl_handle h) { return fdl_get_status_bits(h, nullptr)
 fdl_status fdl_get_status_bits(fdl_handle h, uint32_t* bits) {
   static_assert(FDL_FLAG_SINK_OVERFLOW == fdl::ST_SINK_OVERFLOW && FDL_FLAG_CAND_OVERFLOW == fdl::ST_CAND_OVERFLOW &&
                     FDL_FLAG_BAD_INDEX == fdl::ST_BAD_INDEX && FDL_FLAG_SEL_OVERFLOW == fdl::ST_SEL_OVERFLOW &&
-                    FDL_FLAG_SPLIT_FALLBACK == fdl::ST_SYNC_FALLBACK,
+                    FDL_FLAG_SPLIT_FALLBACK == fdl::ST_SYNC_FALLBACK && FDL_FLAG_PLACEMENT == fdl::ST_PLACEMENT &&
+                    FDL_FLAG_SPLIT_PLACEMENT == fdl::ST_SPLIT_PLACEMENT,
                 "status bits");
   if (bits) *bits = 0;
   if (!h) return FDL_EINVAL;
@@ -325,6 +336,7 @@ fdl_status fdl_get_status_bits(fdl_handle h, uint32_t* bits) {
     if (st != FDL_OK) return st;
   }
   if (bits) *bits = word;
+  if (word & fdl::ST_SPLIT_PLACEMENT) return FDL_ESYNC;
   if (word & (fdl::ST_SINK_OVERFLOW | fdl::ST_CAND_OVERFLOW | fdl::ST_SEL_OVERFLOW)) return FDL_EOVERFLOW;
   if (word & fdl::ST_BAD_INDEX) return FDL_EINDEX;
   return FDL_OK;
@@ -943,6 +955,23 @@ fdl_status fdl_bandwidth_probe(fdl_handle h, int32_t mode, const void* src, size
   const size_t need = mode == FDL_PROBE_COPY ? bytes : fdl::probe_out_words(nb) * sizeof(uint32_t);
   if (dst_bytes < need) return fail(h, FDL_EINVAL, "dst holds %zu bytes, needs %zu", dst_bytes, need);
   return hip_status(h, fdl::launch_probe(h->stream, mode, src, bytes, dst, nb), "probe launch");
+}
+
+fdl_status fdl_set_phase_buffer(fdl_handle h, uint64_t* stamps, int64_t n_words) {
+  if (!h) return FDL_EINVAL;
+  if ((stamps == nullptr) != (n_words == 0) || n_words < 0)
+    return fail(h, FDL_EINVAL, "stamps and n_words go together");
+  h->stamps = stamps;
+  h->stamp_words = n_words;
+  return FDL_OK;
+}
+
+int32_t fdl_phase_stamps_built(void) {
+#ifdef FDL_PHASE_STAMPS
+  return 1;
+#else
+  return 0;
+#endif
 }
 
 fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask, int32_t every) {

@@ -205,10 +205,10 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
                        const void* k_dec, const void* v_dec, const int32_t* page_table,
                        const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                        int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                       uint32_t* status, int n_hint, const KernelTimer* timer) {
+                       uint32_t* status, int n_hint, const KernelTimer* timer, bool safe) {
   if (g.dtype == FDL_BF16)
     return launch_attn_mha(s, g, q, k, v, k_dec, v_dec, page_table, sel_idx, n_sel, max_sel, unit_log2,
-                           dense, out, scratch, n_splits, tickets, status, n_hint, timer);
+                           dense, out, scratch, n_splits, tickets, status, n_hint, timer, nullptr, safe);
   if (timer) (void)hipEventRecord(timer->a, s);
   const hipError_t err = launch_attn_f32(s, g, q, k, v, k_dec, v_dec, page_table, sel_idx, n_sel,
                                          max_sel, unit_log2, dense, out, status);

@@ -60,11 +60,26 @@ struct MhaParams {
   int n_groups;   // G > 1: (sequence, KV head, split) triples
   int n_hint;   // expected selected units per head (0 = unknown)
   int page_log2, pages_per_seq, n_pages;
+  int merge_here;   // 1: the last split of a head merges the partials; 0: attn_merge_kernel does
   float scale_log2;
   // fused selection (SEL): every workgroup scores the blocks of its head against the predicted
   // queries and selects them itself; split 0 also writes the scores and the selection out
   FusedSelect fs;
 };
+
+// Phase timestamps (diagnostic builds only): thread 0 of the workgroup records the constant-rate
+// clock at point i.
+#ifdef FDL_PHASE_STAMPS
+#define FDL_STAMP(p, i)                                                                                  \
+  do {                                                                                                   \
+    if (threadIdx.x == 0 && (p).fs.stamps != nullptr)                                                    \
+      (p).fs.stamps[(int64_t)blockIdx.x * kStampsPerGroup + (i)] = __builtin_amdgcn_s_memrealtime();     \
+  } while (0)
+#else
+#define FDL_STAMP(p, i) \
+  do {                  \
+  } while (0)
+#endif
 
 constexpr int kMhaWaves = 8;
 constexpr int kMaxSplits = 32;   // workgroups per head (the final merge keeps their weights in LDS)
@@ -197,9 +212,11 @@ __device__ __forceinline__ void mha_load_first_pass(const float* __restrict__ ks
 }
 
 // keys[r] = order_key(score) and, when to_global, scores[r] as well, for the batch at base.
+// xe (may be NULL): the split-exchange row of the head, where row r gets (score bits << 32) | tag.
 template <int D>
 __device__ __forceinline__ void mha_dot_rows(const float (&x)[kScoreBatch][16], int base, int rb, const float (&qv)[16],
-                                             uint32_t* keys, float* __restrict__ scores, bool to_global) {
+                                             uint32_t* keys, float* __restrict__ scores, bool to_global,
+                                             uint64_t* xe = nullptr, uint32_t tag = 0) {
   constexpr int LPR = D / 16, RPW = 64 / LPR, RPP = kMhaWaves * RPW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -210,6 +227,9 @@ __device__ __forceinline__ void mha_dot_rows(const float (&x)[kScoreBatch][16], 
     if (lane % LPR == 0 && r < rb) {
       keys[r] = order_key(sc);
       if (to_global) scores[r] = sc;
+      if (xe != nullptr)
+        __hip_atomic_store(xe + r, ((uint64_t)__float_as_uint(sc) << 32) | tag, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -218,12 +238,13 @@ __device__ __forceinline__ void mha_dot_rows(const float (&x)[kScoreBatch][16], 
 template <int D>
 __device__ __forceinline__ void mha_score_rows(const float* __restrict__ ksh, int ra, int rb, const float (&qv)[16],
                                                uint32_t* keys, float* __restrict__ scores, bool to_global,
-                                               float (&x)[kScoreBatch][16], bool pre) {
+                                               float (&x)[kScoreBatch][16], bool pre, uint64_t* xe = nullptr,
+                                               uint32_t tag = 0) {
   constexpr int RPP = kMhaWaves * (64 / (D / 16));
   if (rb <= ra) return;   // uniform
   for (int base = ra; base < rb; base += kScoreBatch * RPP) {
     mha_load_rows<D>(ksh, base, rb, x, (pre && base == ra) ? 1 : 0);
-    mha_dot_rows<D>(x, base, rb, qv, keys, scores, to_global);
+    mha_dot_rows<D>(x, base, rb, qv, keys, scores, to_global, xe, tag);
   }
 }
 
@@ -294,7 +315,7 @@ __device__ __forceinline__ void mha_forced_list(const uint32_t* forced, int n, i
 }
 
 // kvh: the KV head within sequence b; kvseg = b * Hkv + kvh; bar_i: the group's barrier word.
-template <int D, bool GQA>
+template <int D, bool GQA, bool SAFE>
 __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg, int64_t bar_i, float* sc_out,
                                int m, int M, uint16_t* lds_raw, uint16_t* sel_lds) {
   constexpr int NT = kMhaWaves * 64;
@@ -314,6 +335,13 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
   uint32_t* bar = f.barriers + bar_i * kSyncStride;
   uint32_t g0 = 0;
   if (M > 1 && tid == 0) g0 = head_barrier_gen(bar);
+  // Tagged exchange (one query head per KV head, up to NT units): instead of meeting at a barrier,
+  // every split stores its rows' scores into the head's exchange row as 64-bit entries tagged with
+  // this launch and the split's XCD, and every thread polls the entry of its own unit.  Entries of
+  // an earlier launch carry another tag; entries written on another XCD (whose L2 this one does not
+  // share) carry another XCD id and are not trusted: the split then scores every row itself.
+  const bool tagged = !GQA && !SAFE && M > 1 && n <= NT && f.xchg != nullptr;
+  __shared__ uint32_t s_tag;
 
   // Loads in the order they are needed, so that each wait leaves the later ones in flight (the
   // counter of outstanding loads drains in order): the queries, the sink list (thread t < max_sinks
@@ -332,7 +360,8 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
                                  : reinterpret_cast<const int32_t*>(f.pred_mask + b);
   const int sink_p = *sp;
   const int sink_n = have_sinks ? f.n_sinks[b] : 0;
-  const int ra = (int)((int64_t)n * m / M), rb = (int)((int64_t)n * (m + 1) / M);
+  // safe mode: no member hands scores to another; each scores every unit itself
+  const int ra = SAFE ? 0 : (int)((int64_t)n * m / M), rb = SAFE ? n : (int)((int64_t)n * (m + 1) / M);
   float x[kScoreBatch][16];
   const bool pre = rb > ra;
   __builtin_amdgcn_sched_barrier(0);
@@ -346,7 +375,13 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
   } else {
     qsum_g1_finish<D, 32, NT>(qst, pred, p.T, reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, L.qs);
   }
+  if (tagged && tid == 0) {
+    const uint32_t launch = ((g0 + 1u) ^ (f.serial << 12)) & 0x0FFFFFFFu;
+    s_tag = (launch << 4) | (xcc_reg() & 0xFu);
+    L.flag[0] = 0;
+  }
   block_sync_lds();   // qs and the cleared bits
+  FDL_STAMP(p, 1);
   if (sink_lane && tid < sink_n && sink_p >= 0) {
     const int u = sink_p >> p.unit_log2;
     if (u < n) atomicOr(&L.forced[u >> 5], 1u << (u & 31));
@@ -354,25 +389,63 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
   float qv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) qv[i] = L.qs[16 * j + i];
-  mha_score_rows<D>(ksh, ra, rb, qv, L.keys, sc_out, true, x, pre);
+  const uint32_t tag = tagged ? s_tag : 0u;
+  uint64_t* xe = tagged ? reinterpret_cast<uint64_t*>(f.xchg) + kvseg * n : nullptr;
+  mha_score_rows<D>(ksh, ra, rb, qv, L.keys, sc_out, !SAFE || m == 0, x, pre, xe, tag);
+  FDL_STAMP(p, 2);
   const bool listing = threshold_select_ok(n, f.top_k);   // uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   bool listed = false;
-  if (M > 1) {
+  bool redo = false;   // uniform: some of the others' scores did not come; this split scores them itself
+  if (tagged) {
+    // thread t < n fetches unit t's score: its own split's from LDS, the others' from the
+    // exchange row (polled until this launch's entry is there)
+    bool ok = f.spin_limit > 0;   // a zero spin limit never waits: every split scores every row
+    uint32_t key = 0u;
+    if (ok && tid < n && (tid < ra || tid >= rb)) {
+      int it = 0;
+      for (;;) {
+        const uint64_t v = __hip_atomic_load(xe + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t vt = (uint32_t)v;
+        if (vt == tag) {
+          key = order_key(__uint_as_float((uint32_t)(v >> 32)));
+          break;
+        }
+        if ((vt >> 4) == (tag >> 4) || ++it > f.spin_limit) {   // written on another XCD, or too late
+          if ((vt >> 4) == (tag >> 4)) latch(p.status, ST_PLACEMENT);
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (!ok) atomicOr(reinterpret_cast<uint32_t*>(L.flag), 1u);
+    block_sync_lds();   // own keys, forced bits and the flag
+    if (tid < n && (tid < ra || tid >= rb)) L.keys[tid] = key;
+    if (listing && wave == 0) mha_forced_list<NT>(L.forced, n, p.max_sel, sel_lds, L.flag + 1);
+    listed = true;
+    FDL_STAMP(p, 3);
+    redo = L.flag[0] != 0;
+    if (redo) block_sync_lds();   // the forced list's flag word is read below; the keys are rewritten
+  } else if (M > 1 && !SAFE) {
     const bool synced = head_barrier(bar, g0, M, f.spin_limit, L.flag);   // forced bits are complete
+    FDL_STAMP(p, 3);
     // wave 0 lists the forced units while the others read the scores back
     if (listing && wave == 0) mha_forced_list<NT>(L.forced, n, p.max_sel, sel_lds, L.flag + 1);
     listed = true;
     if (synced) {
       for (int i = tid; i < n; i += NT)
         if (i < ra || i >= rb) L.keys[i] = order_key(sc_out[i]);
-    } else {
-      mha_score_rows<D>(ksh, 0, ra, qv, L.keys, sc_out, false, x, false);
-      mha_score_rows<D>(ksh, rb, n, qv, L.keys, sc_out, false, x, false);
-      if (tid == 0) latch(p.status, ST_SYNC_FALLBACK);
     }
+    redo = !synced;
+  }
+  if (redo) {   // uniform
+    mha_score_rows<D>(ksh, 0, ra, qv, L.keys, sc_out, false, x, false);
+    mha_score_rows<D>(ksh, rb, n, qv, L.keys, sc_out, false, x, false);
+    if (tid == 0) latch(p.status, ST_SYNC_FALLBACK);
   }
   block_sync_lds();   // keys and forced bits complete
+  FDL_STAMP(p, 4);
   if (!listing) return 0;   // uniform
   if (!listed) {
     if (wave == 0) mha_forced_list<NT>(L.forced, n, p.max_sel, sel_lds, L.flag + 1);
@@ -572,7 +645,84 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
   return okm;
 }
 
-template <int D, bool DENSE, bool PAGED, bool SEL, bool GQA = false>
+// Merge of the NS partials (O, max, sum) of head seg into its bf16 output: thread (query qi, chunk
+// pair dg).  Every split's (max, sum) and the partials of the first kMergeBatch splits are requested
+// in one round trip (the statistics first, so that waiting for them leaves the partials in flight);
+// the statistics are shared through LDS (s_ml2: [NS][32]).  Every thread derives its query's split
+// weights itself: the common max, then per split exp2(m - M), the sum of l times the weight and the
+// weighted partials, in split order.  Reads past NS are clamped to the last split and masked, so
+// that they go out together.  Used by the last split of a head in the fused launch and by the safe
+// mode's second launch alike, so both give the same bits.
+template <int D>
+__device__ __forceinline__ void merge_splits(const MhaParams& p, const float* po_base, const float2* pml_base,
+                                             uint16_t* out, int T, int64_t seg, int NS, float2* s_ml2) {
+  constexpr int NT = kMhaWaves * 64;
+  constexpr int HC = D / 8;   // chunks per half row
+  constexpr int kMergeBatch = 8;
+  const int tid = threadIdx.x;
+  const bool item = tid < 32 * HC;
+  const int qi = item ? tid / HC : 0, dg = tid % HC;
+  float2 ml[(kMaxSplits * 32 + NT - 1) / NT];
+#pragma unroll
+  for (int k = 0; k < (kMaxSplits * 32 + NT - 1) / NT; ++k) {
+    const int i = tid + k * NT;
+    if (i < NS * 32) ml[k] = pml_base[seg * NS * 32 + i];
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep the statistics loads ahead of the partials
+  float4 a[kMergeBatch], c[kMergeBatch];
+  auto load_batch = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int t = t0 + j < NS ? t0 + j : NS - 1;
+      const float* src = po_base + ((seg * NS + t) * 32 + qi) * D + 4 * dg;
+      a[j] = *reinterpret_cast<const float4*>(src);
+      c[j] = *reinterpret_cast<const float4*>(src + 4 * HC);
+    }
+  };
+  load_batch(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < (kMaxSplits * 32 + NT - 1) / NT; ++k) {
+    const int i = tid + k * NT;
+    if (i < NS * 32) s_ml2[i] = ml[k];
+  }
+  block_sync_lds();   // the partial loads stay in flight
+  FDL_STAMP(p, 11);
+  float Mh = -__builtin_inff();
+  for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int t = t0 + j < NS ? t0 + j : NS - 1;
+      Mh = fmaxf(Mh, s_ml2[t * 32 + qi].x);
+    }
+  }
+  float Ls = 0.f;
+  float4 o1 = make_float4(0.f, 0.f, 0.f, 0.f), o2 = o1;
+  for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
+    if (t0 > 0) load_batch(t0);
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int t = t0 + j < NS ? t0 + j : NS - 1;
+      const float2 v = s_ml2[t * 32 + qi];
+      const float w = (t0 + j < NS && v.x != -__builtin_inff() && Mh != -__builtin_inff()) ? exp2_fast(v.x - Mh) : 0.f;
+      Ls += v.y * w;
+      o1.x += a[j].x * w; o1.y += a[j].y * w; o1.z += a[j].z * w; o1.w += a[j].w * w;
+      o2.x += c[j].x * w; o2.y += c[j].y * w; o2.z += c[j].z * w; o2.w += c[j].w * w;
+    }
+  }
+  FDL_STAMP(p, 12);
+  if (item && qi < T) {
+    const float inv = 1.f / Ls;
+    uint16_t* dst = out + (seg * T + qi) * D + 4 * dg;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o1.x * inv, o1.y * inv), pack_bf16x2(o1.z * inv, o1.w * inv));
+    *reinterpret_cast<uint2*>(dst + 4 * HC) =
+        make_uint2(pack_bf16x2(o2.x * inv, o2.y * inv), pack_bf16x2(o2.z * inv, o2.w * inv));
+  }
+}
+
+// SAFE (fused selection only): no workgroup hands data to another inside the launch -- every split
+// scores every unit, and the partials are merged by attn_merge_kernel.
+template <int D, bool DENSE, bool PAGED, bool SEL, bool GQA = false, bool SAFE = false>
 __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaParams p) {
   using S = MhaShape<D>;
   constexpr int NT = kMhaWaves * 64;
@@ -608,6 +758,12 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     seg_i = (kv_i / p.Hkv) * p.H + (kv_i % p.Hkv) * p.G + member;
   }
   const int b = kv_i / p.Hkv, h = kv_i % p.Hkv;   // h: KV head within the sequence
+  FDL_STAMP(p, 0);
+#ifdef FDL_PHASE_STAMPS
+  if (threadIdx.x == 0 && p.fs.stamps != nullptr)
+    p.fs.stamps[(int64_t)blockIdx.x * kStampsPerGroup + kStampXcc] =
+        (uint64_t)xcc_reg() | ((uint64_t)s << 32) | ((uint64_t)seg_i << 40) | ((uint64_t)1 << 63);
+#endif
   // the wave index is uniform: in a scalar register, the per-tile bookkeeping stays scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hh = lane >> 5;
@@ -657,9 +813,9 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     int nf;
     if constexpr (GQA) {
       float* xo = s == 0 ? p.fs.scores + kvseg * p.n_units : p.fs.xchg + (int64_t)gi * p.n_units;
-      nf = mha_score_phase<D, true>(p, b, h, kvseg, gi, xo, member, p.G, lds, sel_lds);
+      nf = mha_score_phase<D, true, SAFE>(p, b, h, kvseg, gi, xo, member, p.G, lds, sel_lds);
     } else {
-      nf = mha_score_phase<D, false>(p, b, h, kvseg, seg, p.fs.scores + kvseg * p.n_units, s, NS, lds, sel_lds);
+      nf = mha_score_phase<D, false, SAFE>(p, b, h, kvseg, seg, p.fs.scores + kvseg * p.n_units, s, NS, lds, sel_lds);
     }
     // Known now: tile 0 (the block's own tokens) and the tiles of the nf forced units at the front
     // of the list.  Up to one of them per wave whose slot the selection scratch leaves free is
@@ -682,6 +838,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
       issued = true;
     }
     const int ns = mha_choose_phase<D>(p, kvseg, s == 0 && member == 0, lds, sel_lds);
+    FDL_STAMP(p, 5);
     n_list = p.L == 0 ? 0 : ns << p.unit_log2;
     e1 = 1 + (n_list + kTileTok - 1) / kTileTok;
     if (!issued) mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp, contig);
@@ -732,11 +889,18 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   if (!issued && e < e1)
     vm_next = mha_issue<D, DENSE, PAGED, true, POL>(p, rows, b, h, e, n_list, tp, slot, lane, bad, contig, voff, spt);
   const int swz_k = swz(ql) & (PROW - 1);
+#ifdef FDL_PHASE_STAMPS
+  bool first_tile = true;
+#endif
   for (int en; e < e1; e = en) {
     // This tile's LDS fetches must have landed before the slot is read.  Explicit, because the
     // compiler's own wait for LDS fetches is not placed reliably across the loop back-edge when
     // other vector loads are in flight.
     wait_vm0();
+#ifdef FDL_PHASE_STAMPS
+    if (first_tile) FDL_STAMP(p, 6);
+    first_tile = false;
+#endif
     const uint32_t vm = vm_next;
     en = (SEL && e < e_pre) ? e_rr : e + e_step;
     const bool more = en < e1;
@@ -846,6 +1010,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     }
   }
   latch_bad(p.status, bad);
+  FDL_STAMP(p, 7);
 
   // ---- merge the 8 waves.  Each wave stores its unnormalized O^T (relative to its own running
   //      max) and its (max, sum) as soon as its last tile is done, into its own slot (its fetches
@@ -857,7 +1022,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   //      consecutive d = 64 dtp + 16 rg + 8 hh + [0, 8) of query q (registers r = 4 rg + [0, 4) of
   //      MFMAs 2 dtp and 2 dtp + 1): chunks 16 dtp + 4 rg + 2 hh and the next. ----
   __shared__ float s_m[kMhaWaves][32], s_l[kMhaWaves][32];
-  __shared__ uint32_t s_ticket;
+  __shared__ uint32_t s_ticket, s_here;
   constexpr int CH = D / 4;   // 16-byte chunks per row
   constexpr int HC = D / 8;   // chunks per half row
   static_assert(32 * D * sizeof(float) == sizeof(uint16_t) * S::SLOT, "a wave's rows fill its slot");
@@ -882,11 +1047,14 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     }
   }
   __syncthreads();
+  FDL_STAMP(p, 8);
   static_assert(32 * HC <= NT, "one (query, chunk pair) item per thread");
   const bool item = tid < 32 * HC;
   const int qi = item ? tid / HC : 0, dg = tid % HC;
   float* po_base = p.part_o;
   float2* pml_base = p.part_ml;
+  uint16_t* const p_out = p.out;
+  const int p_T = p.T;
   float Mq = -__builtin_inff(), Lq = 0.f;
   {
     float mw[kMhaWaves];
@@ -921,80 +1089,50 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
       if (dg == 0) pml_base[(seg * NS + s) * 32 + qi] = make_float2(Mq, Lq);
     }
   }
-  if (NS == 1 || GQA) return;   // grouped-query heads: attn_combine_kernel merges the splits
+  // grouped-query heads: attn_combine_kernel merges the splits; the safe mode merges in a second
+  // launch too (attn_merge_kernel, the same arithmetic)
+  if (NS == 1 || GQA || SAFE || (!SEL && !p.merge_here)) return;
 
   // ---- same-XCD hand-over: the last split of this head to finish merges all of them.  The
   //      partials sit in this XCD's L2: wait until our stores are acknowledged by it, take a
-  //      ticket, and the last taker drops its L1 copies before reading the partials back. ----
+  //      ticket (which counts the takers per XCD), and the last taker drops its L1 copies before
+  //      reading the partials back -- if every split ran on its XCD; otherwise the partials of
+  //      the others are not in its L2, and the head's output is reported invalid. ----
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg * kSyncStride], 1u);
+  if (tid == 0) {
+    bool here = true;
+    s_ticket = take_ticket(p.tickets + seg * kSyncStride, NS, &here);
+    s_here = here ? 1u : 0u;
+  }
   __syncthreads();
+  FDL_STAMP(p, 9);
   if (s_ticket != (uint32_t)(NS - 1)) return;
+  if (s_here == 0u) {   // uniform
+    if (tid == 0) {
+      latch(p.status, ST_SPLIT_PLACEMENT);
+      reset_ticket(p.tickets + seg * kSyncStride);
+    }
+    return;
+  }
   asm volatile("buffer_inv sc0" ::: "memory");   // later loads miss L1 and read the partials from L2
-  // Every split's (max, sum) and the partials of the first kMergeBatch splits are requested in one
-  // round trip (the statistics first, so that waiting for them leaves the partials in flight); the
-  // statistics are shared through LDS.  Same thread -> (query, chunk pair) items as above.
-  constexpr int kMergeBatch = 8;
-  float2* s_ml2 = reinterpret_cast<float2*>(lds);   // [NS][32] (the slots are free)
-  float2 ml[(kMaxSplits * 32 + NT - 1) / NT];
-#pragma unroll
-  for (int k = 0; k < (kMaxSplits * 32 + NT - 1) / NT; ++k) {
-    const int i = tid + k * NT;
-    if (i < NS * 32) ml[k] = pml_base[seg * NS * 32 + i];
+  merge_splits<D>(p, po_base, pml_base, p_out, p_T, seg, NS, reinterpret_cast<float2*>(lds));
+  if (tid == 0) {
+    reset_ticket(p.tickets + seg * kSyncStride);
+    // the tagged score exchange of this launch is over for every split: the next launch's tag
+    if (SEL && p.fs.xchg != nullptr && p.n_units <= kMhaWaves * 64)
+      __hip_atomic_fetch_add(&p.fs.barriers[seg * kSyncStride + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __builtin_amdgcn_sched_barrier(0);   // keep the statistics loads ahead of the partials
-  float4 a[kMergeBatch], c[kMergeBatch];
-  auto load_batch = [&](int t0) {
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int t = t0 + j < NS ? t0 + j : NS - 1;
-      const float* src = po_base + ((seg * NS + t) * 32 + qi) * D + 4 * dg;
-      a[j] = *reinterpret_cast<const float4*>(src);
-      c[j] = *reinterpret_cast<const float4*>(src + 4 * HC);
-    }
-  };
-  load_batch(0);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int k = 0; k < (kMaxSplits * 32 + NT - 1) / NT; ++k) {
-    const int i = tid + k * NT;
-    if (i < NS * 32) s_ml2[i] = ml[k];
-  }
-  block_sync_lds();   // the partial loads stay in flight
-  // Every thread derives its query's split weights itself (no separate pass): the common max, then
-  // per split exp2(m - M), the sum of l times the weight and the weighted partials.  Reads past NS
-  // are clamped to the last split and masked, so that they go out together.
-  float Mh = -__builtin_inff();
-  for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int t = t0 + j < NS ? t0 + j : NS - 1;
-      Mh = fmaxf(Mh, s_ml2[t * 32 + qi].x);
-    }
-  }
-  float Ls = 0.f;
-  float4 o1 = make_float4(0.f, 0.f, 0.f, 0.f), o2 = o1;
-  for (int t0 = 0; t0 < NS; t0 += kMergeBatch) {
-    if (t0 > 0) load_batch(t0);
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int t = t0 + j < NS ? t0 + j : NS - 1;
-      const float2 v = s_ml2[t * 32 + qi];
-      const float w = (t0 + j < NS && v.x != -__builtin_inff() && Mh != -__builtin_inff()) ? exp2_fast(v.x - Mh) : 0.f;
-      Ls += v.y * w;
-      o1.x += a[j].x * w; o1.y += a[j].y * w; o1.z += a[j].z * w; o1.w += a[j].w * w;
-      o2.x += c[j].x * w; o2.y += c[j].y * w; o2.z += c[j].z * w; o2.w += c[j].w * w;
-    }
-  }
-  if (item && qi < p.T) {
-    const float inv = 1.f / Ls;
-    uint16_t* dst = p.out + (seg * p.T + qi) * D + 4 * dg;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o1.x * inv, o1.y * inv), pack_bf16x2(o1.z * inv, o1.w * inv));
-    *reinterpret_cast<uint2*>(dst + 4 * HC) =
-        make_uint2(pack_bf16x2(o2.x * inv, o2.y * inv), pack_bf16x2(o2.z * inv, o2.w * inv));
-  }
-  if (tid == 0) p.tickets[seg * kSyncStride] = 0u;
+  FDL_STAMP(p, 10);
+}
+
+// The safe mode's merge: one workgroup per (sequence, query head) merges its NS partials exactly as
+// the last split does in the fused launch (merge_splits), after the kernel boundary has made them
+// visible everywhere.
+template <int D>
+__global__ __launch_bounds__(kMhaWaves * 64) void attn_merge_kernel(const MhaParams p) {
+  __shared__ float2 s_ml2[kMaxSplits * 32];
+  merge_splits<D>(p, p.part_o, p.part_ml, p.out, p.T, (int64_t)blockIdx.x, p.n_splits, s_ml2);
 }
 
 // Merge the per-split partials (max, sum, O) of every head into the bf16 output (grouped-query
@@ -1107,10 +1245,13 @@ static void launch_one(Kern kern, dim3 grid, hipStream_t st, const MhaParams& p,
 template <int D>
 static hipError_t launch_mha_d(hipStream_t st, const MhaParams& p, dim3 grid, bool dense, bool paged, bool sel,
                                const KernelTimer* timer) {
+  const bool safe = !p.merge_here;
   if (sel && p.G > 1) {
-    launch_one(attn_mha_kernel<D, false, false, true, true>, grid, st, p, timer);
+    if (safe) launch_one(attn_mha_kernel<D, false, false, true, true, true>, grid, st, p, timer);
+    else launch_one(attn_mha_kernel<D, false, false, true, true>, grid, st, p, timer);
   } else if (sel) {
-    launch_one(attn_mha_kernel<D, false, false, true>, grid, st, p, timer);
+    if (safe) launch_one(attn_mha_kernel<D, false, false, true, false, true>, grid, st, p, timer);
+    else launch_one(attn_mha_kernel<D, false, false, true>, grid, st, p, timer);
   } else if (p.G > 1) {
     if (dense && paged) launch_one(attn_mha_kernel<D, true, true, false, true>, grid, st, p, timer);
     else if (dense) launch_one(attn_mha_kernel<D, true, false, false, true>, grid, st, p, timer);
@@ -1130,7 +1271,8 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
                            const void* k_dec, const void* v_dec, const int32_t* page_table,
                            const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                            int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                           uint32_t* status, int n_hint, const KernelTimer* timer, const FusedSelect* fsel) {
+                           uint32_t* status, int n_hint, const KernelTimer* timer, const FusedSelect* fsel,
+                           bool safe) {
   MhaParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -1162,15 +1304,25 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
   p.G = g.G;
   p.n_groups = g.B * g.Hkv * n_splits;
   p.n_hint = dense ? 0 : n_hint;
+  p.merge_here = safe ? 0 : 1;
   p.fs = fsel ? *fsel : FusedSelect{};
   // 8 XCDs: the splits of head seg run on XCD seg % 8; grouped-query heads: the G heads of KV
   // group i (a KV head and a split) run on XCD i % 8 (see the kernel)
   const dim3 grid(g.G == 1 ? 8 * ((p.n_segs + 7) / 8) * n_splits : 8 * ((p.n_groups + 7) / 8) * g.G);
+  if (p.fs.stamps != nullptr && p.fs.stamp_words < (int64_t)grid.x * kStampsPerGroup) p.fs.stamps = nullptr;
   const bool sel = fsel != nullptr && !dense && !g.paged;
   if (sel && g.G > 1 && p.n_groups > kMaxSplitSegs) return hipErrorInvalidValue;   // barrier words
   const hipError_t err = g.D == 128 ? launch_mha_d<128>(st, p, grid, dense != 0, g.paged != 0, sel, timer)
                                     : launch_mha_d<64>(st, p, grid, dense != 0, g.paged != 0, sel, timer);
-  if (err != hipSuccess || g.G == 1 || n_splits == 1) return err;
+  if (err != hipSuccess || n_splits == 1) return err;
+  if (g.G == 1) {
+    if (!safe) return err;
+    // safe mode: the partials are merged after the kernel boundary, with the fused merge's arithmetic
+    const dim3 mgrid(g.B * g.Hq), mblock(kMhaWaves * 64);
+    if (g.D == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, mgrid, mblock, 0, st, p);
+    else hipLaunchKernelGGL(attn_merge_kernel<64>, mgrid, mblock, 0, st, p);
+    return hipGetLastError();
+  }
   return launch_attn_combine(st, p.part_o, p.part_ml, out, g.B * g.Hq, n_splits, g.T, g.D);
 }
 

@@ -13,6 +13,8 @@ enum : uint32_t {
   ST_BAD_INDEX = 1u << 2,       // unit / page id out of range (row skipped)
   ST_SEL_OVERFLOW = 1u << 3,    // more selected units than max_sel (list truncated)
   ST_SYNC_FALLBACK = 1u << 4,   // a fused split scored every block itself (informational)
+  ST_PLACEMENT = 1u << 5,       // a split's sibling ran on another XCD (informational; handled)
+  ST_SPLIT_PLACEMENT = 1u << 6, // splits that merge through L2 ran on different XCDs (output invalid)
 };
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -102,6 +104,32 @@ __device__ __forceinline__ void block_sync_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// The raw HW_REG_XCC_ID register of the calling wave (which XCD, accelerator complex die, it runs on).
+__device__ __forceinline__ uint32_t xcc_reg() {
+  return __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 20);
+}
+
+// Merge ticket of the splits of one head that hand partial results over through their XCD's L2.  A
+// 64-bit word (two of the uint32 slots at `word`, 8-byte aligned): the number of takers in bits 0-7
+// and, from bit 8, a 6-bit count of takers per XCD.  Returns the caller's place (0-based); for every
+// caller, *all_here tells whether all NS takers so far counted, itself included, ran on its XCD --
+// for the last taker (place NS - 1) that is every split of the head.  One thread per workgroup.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* word, int NS, bool* all_here) {
+  const uint32_t x = xcc_reg() & 7u;
+  const uint64_t inc = 1ull + (1ull << (8 + 6 * x));
+  const uint64_t old = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(word), inc, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t now = old + inc;
+  *all_here = ((now >> (8 + 6 * x)) & 63ull) == (now & 0xFFull);
+  (void)NS;
+  return (uint32_t)(old & 0xFFull);
+}
+
+// Leaves a ticket word at zero for the next launch (the last taker, after its merge).
+__device__ __forceinline__ void reset_ticket(uint32_t* word) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(word), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void latch(uint32_t* status, uint32_t bit) {

@@ -24,6 +24,10 @@ struct fdl_ctx {
   size_t scratch_bytes;
   char last_error[256];
   bool capturing = false;   // between fdl_capture_begin and fdl_capture_end
+  uint64_t* stamps = nullptr;   // fdl_set_phase_buffer
+  uint32_t fused_serial = 0;    // fused launches issued (part of their score-exchange tag)
+  bool safe_sync = false;       // FDL_SAFE_SYNC: no hand-over between workgroups through L2
+  int64_t stamp_words = 0;
   // optional event timing (fdl_profile_begin / fdl_profile_end)
   struct ProfRec {
     int kind;
@@ -68,6 +72,7 @@ struct KernelTimer {
 constexpr int kFusedMaxUnits = 4096;   // blocks per head the fused path keeps in LDS
 constexpr int kFusedMaxSel = 4096;     // selected blocks per head
 constexpr int kFusedMaxSinks = 512;    // sink list entries (one per thread of the fused kernel)
+constexpr int kFusedTaggedUnits = 512; // blocks per head up to which the splits exchange tagged scores
 struct FusedSelect {
   const uint64_t* pred_mask;   // [B]
   const float* ks;             // pooled keys [B][H][n_units][D]
@@ -81,7 +86,16 @@ struct FusedSelect {
   int spin_limit;              // polls before a split stops waiting for its siblings
   float* xchg;                 // grouped-query heads: [B * Hkv * n_splits][n_units] score exchange
                                // of every (KV head, split) group but split 0's (which uses scores)
+  uint64_t* stamps;            // phase timestamps [grid][kStampsPerGroup] (FDL_PHASE_STAMPS builds)
+  int64_t stamp_words;         // capacity of stamps
+  uint32_t serial;             // launch counter of the handle (part of the exchange tag)
 };
+
+// Phase timestamps of the fused kernel, written only by a library built with FDL_PHASE_STAMPS:
+// thread 0 of every workgroup stores the constant-rate clock (s_memrealtime, 100 MHz) at fixed
+// points; slot kStampXcc holds the workgroup's HW_REG_XCC_ID word and its (split, head) ids.
+constexpr int kStampsPerGroup = 16;
+constexpr int kStampXcc = 15;
 
 struct Geom {
   int B, Hq, Hkv, G, D, L, bt, T, dtype;
@@ -159,16 +173,18 @@ hipError_t launch_attn(hipStream_t s, const Geom& g, const void* q, const void* 
                        const void* k_dec, const void* v_dec, const int32_t* page_table,
                        const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                        int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
-                       uint32_t* status, int n_hint, const KernelTimer* timer);
+                       uint32_t* status, int n_hint, const KernelTimer* timer, bool safe = false);
 
 // bf16, any number of query heads per KV head: the LDS-DMA streaming kernel.
 int mha_choose_splits(const Geom& g, long long max_list_tokens, int num_cus);
+// safe: no workgroup hands data to another through L2 inside the launch (the splits' partials are
+// merged by a second launch); otherwise the last split of a head merges them in place.
 hipError_t launch_attn_mha(hipStream_t s, const Geom& g, const void* q, const void* k, const void* v,
                            const void* k_dec, const void* v_dec, const int32_t* page_table,
                            const int32_t* sel_idx, const int32_t* n_sel, int max_sel, int unit_log2,
                            int dense, void* out, char* scratch, int n_splits, uint32_t* tickets,
                            uint32_t* status, int n_hint, const KernelTimer* timer,
-                           const FusedSelect* fsel = nullptr);
+                           const FusedSelect* fsel = nullptr, bool safe = false);
 
 hipError_t launch_attn_combine(hipStream_t s, const float* part_o, const float2* part_ml, void* out,
                                int n_segs, int n_splits, int T, int D);

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   __shared__ uint32_t s_cand[kSinkWaves][kSinkLocalCand];
   __shared__ uint32_t s_ncand[kSinkWaves], s_cbase;
   __shared__ float s_lse[32];
-  __shared__ uint32_t s_ticket;
+  __shared__ uint32_t s_ticket, s_here;
   const int NS = p.n_splits;
   const int xcd = blockIdx.x & 7, xslot = blockIdx.x >> 3;
   const int s = xslot % NS;
@@ -338,16 +338,26 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     }
   }
 
-  // ---- the last split of the head (same XCD, so the partials are in its L2) finishes it ----
+  // ---- the last split of the head (same XCD, so the partials are in its L2) finishes it; the
+  //      ticket counts the takers per XCD, and a head whose splits ran on different XCDs is
+  //      reported instead (its partials are not all in one L2) ----
   if (NS > 1) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) s_ticket = atomicAdd(&p.tickets[seg * kSyncStride], 1u);
+    if (tid == 0) {
+      bool here = true;
+      s_ticket = take_ticket(p.tickets + seg * kSyncStride, NS, &here);
+      s_here = here ? 1u : 0u;
+    }
     __syncthreads();
     if (s_ticket != (uint32_t)(NS - 1)) return;
+    if (tid == 0) reset_ticket(p.tickets + seg * kSyncStride);
+    if (s_here == 0u) {   // uniform
+      if (tid == 0) latch(p.status, ST_SPLIT_PLACEMENT);
+      return;
+    }
     asm volatile("buffer_inv sc0" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    if (tid == 0) p.tickets[seg * kSyncStride] = 0u;
   } else {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

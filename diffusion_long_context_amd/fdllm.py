@@ -20,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfdllm.so")
 
 FDL_OK, FDL_EINVAL, FDL_ENOMEM, FDL_EHIP, FDL_EOVERFLOW, FDL_EUNSUPPORTED, FDL_EINDEX = 0, -1, -2, -3, -4, -5, -6
+FDL_ESYNC = -7
 FDL_F32, FDL_BF16 = 0, 1
 
 EXPORTED = (
@@ -29,7 +30,7 @@ EXPORTED = (
     "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_select_blocks_shared", "fdl_expand_tokens", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_unmask", "fdl_decode_steps", "fdl_capture_begin", "fdl_capture_end", "fdl_graph_launch",
     "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end", "fdl_bandwidth_probe",
-    "fdl_sparse_attn_noalloc",
+    "fdl_sparse_attn_noalloc", "fdl_set_phase_buffer", "fdl_phase_stamps_built",
 )
 
 FDL_LAYER_DENSE, FDL_LAYER_SOURCE, FDL_LAYER_REUSE = 0, 1, 2
@@ -99,6 +100,8 @@ _SIGS = {
     "fdl_profile_begin": (_I, [_P, _I, ctypes.c_uint32, _I]),
     "fdl_profile_end": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "fdl_bandwidth_probe": (_I, [_P, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _I]),
+    "fdl_set_phase_buffer": (_I, [_P, _P, ctypes.c_int64]),
+    "fdl_phase_stamps_built": (_I, []),
     "fdl_sparse_attn_noalloc": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P]),
 }
 
@@ -467,3 +470,8 @@ class Handle:
         self._check(self.lib.fdl_bandwidth_probe(self.h, mode, _ptr(src, None, "src"), nbytes,
                                                  _ptr(dst, None, "dst"), dst.numel() * dst.element_size(),
                                                  n_blocks))
+
+    def fdl_set_phase_buffer(self, stamps=None):
+        """Phase timestamps of the fused kernel into stamps (device int64 tensor) or off (None)."""
+        n = stamps.numel() if stamps is not None else 0
+        self._check(self.lib.fdl_set_phase_buffer(self.h, _ptr(stamps, None, "stamps"), n))

@@ -30,6 +30,15 @@
  *   - Conditions only the device can see (more sinks than max_sinks, more sink candidates than the
  *     workspace holds, an out-of-range page or unit index) are latched into a device status word
  *     and returned by fdl_get_status().
+ *   - Workgroups of one head hand scores and partial results to each other through the L2 of the
+ *     XCD they run on (workgroup i runs on XCD i mod 8 when the dispatcher assigns workgroups round
+ *     robin, and the kernels give a head's workgroups ids of one residue).  That placement is
+ *     checked at run time: a score hand-over whose writer ran elsewhere is redone locally
+ *     (FDL_FLAG_PLACEMENT), a merge whose inputs are not all on one XCD is not done and reported
+ *     (FDL_ESYNC).  With the environment variable FDL_SAFE_SYNC=1 set when a handle is created, no
+ *     workgroup hands data to another inside a launch (every split scores every unit, split partials
+ *     are merged by a second launch, sink detection runs one workgroup per head): the same results
+ *     with no dependence on placement, at some speed.
  *   - A launch failure returns FDL_EHIP.
  */
 #ifndef LIBFDLLM_H
@@ -49,7 +58,8 @@ typedef enum {
   FDL_EHIP = -3,
   FDL_EOVERFLOW = -4,
   FDL_EUNSUPPORTED = -5,
-  FDL_EINDEX = -6
+  FDL_EINDEX = -6,
+  FDL_ESYNC = -7
 } fdl_status;
 
 typedef enum { FDL_F32 = 0, FDL_BF16 = 1 } fdl_dtype;
@@ -99,6 +109,12 @@ fdl_status fdl_get_status(fdl_handle h);
 #define FDL_FLAG_SPLIT_FALLBACK 16u /* informational: a split of fdl_focus_step's fused kernel did  */
                                     /* not wait for its siblings and scored every block itself;     */
                                     /* results are unaffected (FDL_OK)                               */
+#define FDL_FLAG_PLACEMENT 32u      /* informational: a split of that kernel found a sibling on     */
+                                    /* another XCD (no shared L2) and scored that sibling's blocks  */
+                                    /* itself; results are unaffected (FDL_OK)                       */
+#define FDL_FLAG_SPLIT_PLACEMENT 64u /* the workgroups of a head that merge partial results through */
+                                    /* one XCD's L2 ran on different XCDs: that head's attention    */
+                                    /* output (or sink list) was not written (FDL_ESYNC)            */
 
 /* Like fdl_get_status, but also stores the raw condition bits (FDL_FLAG_*) in *bits (may be NULL)
  * before clearing them. */
@@ -414,6 +430,19 @@ typedef enum {
 
 fdl_status fdl_profile_begin(fdl_handle h, int32_t max_records, uint32_t kind_mask, int32_t every);
 fdl_status fdl_profile_end(fdl_handle h, double* total_us, int64_t* counts);
+
+/* Diagnostic phase timeline of the fused score-select-attend kernel of fdl_focus_step.  Only a
+ * library built with FDL_PHASE_STAMPS defined (python -m diffusion_long_context_amd.build
+ * --phase-stamps) records anything; fdl_phase_stamps_built() tells which build is loaded.  With a
+ * buffer set (stamps: device uint64 array of n_words; NULL and 0 to unset), every later fused launch
+ * on the handle with at most n_words / 16 workgroups has thread 0 of workgroup w store the
+ * 100 MHz constant clock at stamps[16 w + i] as it passes point i: 0 start, 1 predicted-query sum
+ * done, 2 own block scores written, 3 the splits' score exchange done, 4 all scores read back,
+ * 5 selection done, 6 first tile landed, 7 wave 0's tiles done, 8 all waves' tiles done, 9 merge
+ * ticket taken, 10 merge done (the last split of a head only); stamps[16 w + 15] = the XCD-id register
+ * (bits 0-31) | split << 32 | head << 40 | 1 << 63.  Each launch overwrites the previous one's stamps. */
+fdl_status fdl_set_phase_buffer(fdl_handle h, uint64_t* stamps, int64_t n_words);
+int32_t fdl_phase_stamps_built(void);
 
 /* Measurement aid, not part of the method: stream `bytes` (a positive multiple of 1024) of the
  * device buffer `src` once, the way the HBM-bound kernels stream their inputs, so that their rate

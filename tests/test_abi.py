@@ -58,7 +58,7 @@ def test_null_handle_is_einval(lib):
 
 
 def test_status_strings(lib):
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         assert lib.fdl_status_string(s)
     assert lib.fdl_last_error(None) == b"no handle"
 
