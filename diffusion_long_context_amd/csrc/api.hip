@@ -53,6 +53,8 @@ fdl_status check_geom(fdl_handle h, const fdl_geom* g, Geom& o) {
     return fail(h, FDL_EINVAL, "kv_block must be a power of two in [1, 4096]");
   if (g->dec_len < 1 || g->dec_len > 64) return fail(h, FDL_EINVAL, "dec_len must be in [1, 64]");
   if (g->dtype != FDL_F32 && g->dtype != FDL_BF16) return fail(h, FDL_EINVAL, "unknown dtype");
+  if (g->ctx_lens && g->paged)
+    return fail(h, FDL_EUNSUPPORTED, "per-sequence lengths (ctx_lens) take a contiguous cache");
   if (g->paged) {
     if (!is_pow2(g->page_tokens) || g->page_tokens > 4096)
       return fail(h, FDL_EINVAL, "page_tokens must be a power of two in [1, 4096]");
@@ -74,6 +76,7 @@ fdl_status check_geom(fdl_handle h, const fdl_geom* g, Geom& o) {
   o.page_log2 = g->paged ? ilog2(g->page_tokens) : 0;
   o.pps = g->paged ? g->pages_per_seq : 0;
   o.n_pages = g->paged ? g->n_pages : 0;
+  o.lens = g->ctx_lens;
   return FDL_OK;
 }
 
@@ -115,10 +118,16 @@ fdl_status run_predict(fdl_handle h, int batch, int T, const float* prev_conf, c
 }
 
 fdl_status run_score_units(fdl_handle h, const Geom& g, const void* q, const uint64_t* pred_mask,
-                           const float* ks, int n_units, float* scores) {
+                           const float* ks, int n_units, int unit_log2, float* scores) {
   ProfScope ps(h, FDL_PROF_SCORE);
-  return hip_status(h, fdl::launch_score_units(h->stream, g, q, pred_mask, ks, n_units, scores),
+  return hip_status(h, fdl::launch_score_units(h->stream, g, q, pred_mask, ks, n_units, unit_log2, scores),
                     "score_units launch");
+}
+
+// The calls that do not take per-sequence lengths.
+fdl_status no_lens(fdl_handle h, const Geom& g, const char* what) {
+  if (g.lens) return fail(h, FDL_EUNSUPPORTED, "%s does not take per-sequence lengths (ctx_lens)", what);
+  return FDL_OK;
 }
 
 fdl_status check_sinks(fdl_handle h, const Geom& g, const void* k_cache, const void* k_dec,
@@ -367,6 +376,7 @@ fdl_status fdl_cache_write(fdl_handle h, const fdl_geom* gp, const void* k_new, 
   if (st != FDL_OK) return st;
   if (!k_new || !v_new || !k_cache || !v_cache)
     return fail(h, FDL_EINVAL, "k_new, v_new, k_cache and v_cache must be non-NULL");
+  if ((st = no_lens(h, g, "fdl_cache_write")) != FDL_OK) return st;
   if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
   if (t0 < 0 || n_tok < 1 || (long long)t0 + n_tok > g.L)
     return fail(h, FDL_EINVAL, "the rows [t0, t0 + n_tok) must lie in [0, ctx_len) and be non-empty");
@@ -414,6 +424,7 @@ fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* gp, const void* q, con
   const int n_units = (g.L + unit_tokens - 1) / unit_tokens;
   if (cand_idx) {
     if (detect_sinks) return fail(h, FDL_EINVAL, "sink detection is a level-1 (cand_idx == NULL) option");
+    if ((st = no_lens(h, g, "level-2 scoring")) != FDL_OK) return st;
     if (n_cand < 1 || n_cand > n_units) return fail(h, FDL_EINVAL, "n_cand must be in [1, n_units]");
     if (!k_cache) return fail(h, FDL_EINVAL, "level-2 scoring needs k_cache");
     if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
@@ -430,7 +441,7 @@ fdl_status fdl_score_blocks(fdl_handle h, const fdl_geom* gp, const void* q, con
     st = check_sinks(h, g, k_cache, k_dec, sink_tau, max_sinks, sink_pos, n_sinks, &ns, &cap);
     if (st != FDL_OK) return st;
   }
-  st = run_score_units(h, g, q, pred_mask, ks, n_units, scores);
+  st = run_score_units(h, g, q, pred_mask, ks, n_units, ilog2(unit_tokens), scores);
   if (st != FDL_OK || !detect_sinks) return st;
   return run_sinks(h, g, q, pred_mask, k_cache, k_dec, sink_tau, max_sinks, sink_pos, n_sinks, ns, cap);
 }
@@ -446,6 +457,7 @@ fdl_status fdl_score_blocks_max(fdl_handle h, const fdl_geom* gp, const void* q,
     return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
   if (g.dtype != FDL_BF16 || g.T > 32)
     return fail(h, FDL_EUNSUPPORTED, "per-query scoring runs bf16 queries with dec_len <= 32");
+  if ((st = no_lens(h, g, "fdl_score_blocks_max")) != FDL_OK) return st;
   const int n_units = (g.L + unit_tokens - 1) / unit_tokens;
   ProfScope ps(h, FDL_PROF_SCORE);
   return hip_status(h, fdl::launch_score_units_max(h->stream, g, q, pred_mask, ks, n_units, scores),
@@ -463,6 +475,7 @@ fdl_status fdl_score_blocks_mass(fdl_handle h, const fdl_geom* gp, const void* q
     return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
   if (g.dtype != FDL_BF16 || g.T > 32)
     return fail(h, FDL_EUNSUPPORTED, "softmax-mass scoring runs bf16 queries with dec_len <= 32");
+  if ((st = no_lens(h, g, "fdl_score_blocks_mass")) != FDL_OK) return st;
   const int n_units = (g.L + unit_tokens - 1) / unit_tokens;
   if (fdl::mass_scratch_bytes(g, n_units) > h->scratch_bytes)
     return fail(h, FDL_ENOMEM, "workspace too small for softmax-mass scoring");
@@ -482,6 +495,7 @@ static fdl_status select_blocks_impl(fdl_handle h, const fdl_geom* gp, const flo
   fdl_status st = check_geom(h, gp, g);
   if (st != FDL_OK) return st;
   if (shared && g.Hkv > 32) return fail(h, FDL_EUNSUPPORTED, "per-sequence selection takes at most 32 KV heads");
+  if ((cand_idx || shared) && (st = no_lens(h, g, "level-2 and per-sequence selection")) != FDL_OK) return st;
   if (!scores || !sel_idx || !n_sel) return fail(h, FDL_EINVAL, "scores, sel_idx and n_sel must be non-NULL");
   if (!is_pow2(unit_tokens) || unit_tokens > 8192)
     return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 8192]");
@@ -534,6 +548,7 @@ fdl_status fdl_expand_tokens(fdl_handle h, const fdl_geom* gp, const int32_t* se
   fdl_status st = check_geom(h, gp, g);
   if (st != FDL_OK) return st;
   if (!sel_idx || !n_sel || !tok_idx || !n_tok) return fail(h, FDL_EINVAL, "sel_idx, n_sel, tok_idx and n_tok must be non-NULL");
+  if ((st = no_lens(h, g, "fdl_expand_tokens")) != FDL_OK) return st;
   if (!is_pow2(unit_tokens) || unit_tokens > 4096)
     return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
   if ((sink_pos == nullptr) != (n_sinks == nullptr)) return fail(h, FDL_EINVAL, "sink_pos and n_sinks go together");
@@ -558,6 +573,7 @@ fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* gp, const void*
   if (st != FDL_OK) return st;
   if (!q || !pred_mask || !k_cache || !cand_idx || !scores || !sel_idx || !n_sel)
     return fail(h, FDL_EINVAL, "q, pred_mask, k_cache, cand_idx, scores, sel_idx and n_sel must be non-NULL");
+  if ((st = no_lens(h, g, "fdl_score_select_tokens")) != FDL_OK) return st;
   if (!is_pow2(unit_tokens) || unit_tokens > 4096)
     return fail(h, FDL_EINVAL, "unit_tokens must be a power of two in [1, 4096]");
   if (g.L % unit_tokens) return fail(h, FDL_EINVAL, "level-2 scoring needs ctx_len %% unit_tokens == 0");
@@ -803,7 +819,7 @@ static fdl_status focus_step_impl(fdl_handle h, const fdl_geom* gp, const fdl_fo
     }
     const bool fused = fused_select_ok(g, n_blk, fp->max_sel, fp->max_sinks);
     if (!fused) {
-      st = run_score_units(h, g, io.q, pred_mask, io.ks, n_blk, scores);
+      st = run_score_units(h, g, io.q, pred_mask, io.ks, n_blk, bt_log2, scores);
       if (st != FDL_OK) return st;
     }
     if (io.mode == FDL_LAYER_SOURCE) {

@@ -31,6 +31,7 @@ struct F32Params {
   int Hq, Hkv, G, T, L, max_sel, unit_log2, n_units, dense;
   int page_log2, pages_per_seq, n_pages;
   float scale;
+  const int32_t* lens;   // per-sequence lengths (ragged batch), or NULL
 };
 
 // Row i of the extended list (i < T: own block row i; else list position i - T): element offset
@@ -38,7 +39,7 @@ struct F32Params {
 template <int D, bool PAGED>
 __device__ __forceinline__ int64_t f32_row_off(const F32Params& p, const KvRows<PAGED>& rows, int b,
                                                int g, int i, int n_list, const int32_t* sel_row,
-                                               bool& own, bool& ok, bool& bad) {
+                                               bool& own, bool& ok, bool& bad, int Lb, int nb) {
   own = i < p.T;
   if (own) {
     ok = true;
@@ -50,13 +51,13 @@ __device__ __forceinline__ int64_t f32_row_off(const F32Params& p, const KvRows<
   int t = ii;
   if (!p.dense) {
     const int u = sel_row[ii >> p.unit_log2];
-    const bool uok = (unsigned)u < (unsigned)p.n_units;
+    const bool uok = (unsigned)u < (unsigned)nb;
     bad = bad || (ok && !uok);
     ok = ok && uok;
     t = uok ? (u << p.unit_log2) + (ii & ((1 << p.unit_log2) - 1)) : 0;
   }
-  ok = ok && t < p.L;
-  t = t < p.L ? t : 0;
+  ok = ok && t < Lb;
+  t = t < Lb ? t : 0;
   bool pbad = false;
   const int64_t off = rows.off(b, g, t, pbad);
   bad = bad || (ok && pbad);
@@ -82,15 +83,17 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const F32Params p) {
   rows.n_pages = p.n_pages;
   rows.page_table = p.page_table;
   bool bad = false;
+  const int Lb = seq_len(p.lens, b, p.L);   // this sequence's cached tokens
+  const int nb = (Lb + (1 << p.unit_log2) - 1) >> p.unit_log2;
   int n_list;
   if (p.dense) {
-    n_list = p.L;
+    n_list = Lb;
   } else {
     int ns = p.n_sel[seg];
     ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
     n_list = ns << p.unit_log2;
   }
-  if (p.L == 0) n_list = 0;
+  if (Lb == 0) n_list = 0;
   const int32_t* sel_row = p.sel_idx + seg * p.max_sel;
   const int total = p.T + n_list;
   float qr[D], o[D];
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const F32Params p) {
       const int r = threadIdx.x;
       bool own = false, ok = false;
       const int i = c0 + r < total ? c0 + r : total - 1;
-      const int64_t off = f32_row_off<D, PAGED>(p, rows, b, g, i, n_list, sel_row, own, ok, bad);
+      const int64_t off = f32_row_off<D, PAGED>(p, rows, b, g, i, n_list, sel_row, own, ok, bad, Lb, nb);
       ok = ok && (c0 + r < total);
       const float* ks = (own ? p.k_dec : p.k) + off;
       const float* vs = (own ? p.v_dec : p.v) + off;
@@ -190,6 +193,7 @@ static hipError_t launch_attn_f32(hipStream_t s, const Geom& g, const void* q, c
   p.pages_per_seq = g.pps;
   p.n_pages = g.n_pages;
   p.scale = 1.0f / sqrtf((float)g.D);
+  p.lens = g.lens;
   dim3 grid(g.Hq, g.B);
   if (g.D == 128) {
     if (g.paged) hipLaunchKernelGGL((attn_f32_kernel<128, true>), grid, dim3(64), 0, s, p);

@@ -61,6 +61,7 @@ struct MhaParams {
   int n_hint;   // expected selected units per head (0 = unknown)
   int page_log2, pages_per_seq, n_pages;
   int merge_here;   // 1: the last split of a head merges the partials; 0: attn_merge_kernel does
+  const int32_t* lens;   // per-sequence lengths of a ragged batch, or NULL (every sequence has L)
   float scale_log2;
   // fused selection (SEL): every workgroup scores the blocks of its head against the predicted
   // queries and selects them itself; split 0 also writes the scores and the selection out
@@ -315,9 +316,10 @@ __device__ __forceinline__ void mha_forced_list(const uint32_t* forced, int n, i
 }
 
 // kvh: the KV head within sequence b; kvseg = b * Hkv + kvh; bar_i: the group's barrier word.
+// nb: the units of sequence b (all of them unless the batch is ragged); rows are p.n_units apart.
 template <int D, bool GQA, bool SAFE>
 __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg, int64_t bar_i, float* sc_out,
-                               int m, int M, uint16_t* lds_raw, uint16_t* sel_lds) {
+                               int m, int M, uint16_t* lds_raw, uint16_t* sel_lds, int nb) {
   constexpr int NT = kMhaWaves * 64;
   constexpr int LPR = D / 16;
   static_assert((kQbufOffsetF + 32 * D) * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * MhaShape<D>::SLOT,
@@ -330,8 +332,8 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
   const SelLds<D> L(lds_raw);
   const int tid = threadIdx.x;
   const int j = (tid & 63) % LPR;
-  const int n = p.n_units;
-  const float* ksh = f.ks + kvseg * (int64_t)n * D;
+  const int n = nb;
+  const float* ksh = f.ks + kvseg * (int64_t)p.n_units * D;
   uint32_t* bar = f.barriers + bar_i * kSyncStride;
   uint32_t g0 = 0;
   if (M > 1 && tid == 0) g0 = head_barrier_gen(bar);
@@ -340,7 +342,7 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
   // this launch and the split's XCD, and every thread polls the entry of its own unit.  Entries of
   // an earlier launch carry another tag; entries written on another XCD (whose L2 this one does not
   // share) carry another XCD id and are not trusted: the split then scores every row itself.
-  const bool tagged = !GQA && !SAFE && M > 1 && n <= NT && f.xchg != nullptr;
+  const bool tagged = !GQA && !SAFE && M > 1 && p.n_units <= NT && f.xchg != nullptr;
   __shared__ uint32_t s_tag;
 
   // Loads in the order they are needed, so that each wait leaves the later ones in flight (the
@@ -390,7 +392,7 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
 #pragma unroll
   for (int i = 0; i < 16; ++i) qv[i] = L.qs[16 * j + i];
   const uint32_t tag = tagged ? s_tag : 0u;
-  uint64_t* xe = tagged ? reinterpret_cast<uint64_t*>(f.xchg) + kvseg * n : nullptr;
+  uint64_t* xe = tagged ? reinterpret_cast<uint64_t*>(f.xchg) + kvseg * p.n_units : nullptr;
   mha_score_rows<D>(ksh, ra, rb, qv, L.keys, sc_out, !SAFE || m == 0, x, pre, xe, tag);
   FDL_STAMP(p, 2);
   const bool listing = threshold_select_ok(n, f.top_k);   // uniform
@@ -457,12 +459,16 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
 
 // writer: the one workgroup of the KV head that writes the selection out.
 template <int D>
-__device__ int mha_choose_phase(const MhaParams& p, int64_t kvseg, bool writer, uint16_t* lds_raw, uint16_t* sel_lds) {
+__device__ int mha_choose_phase(const MhaParams& p, int64_t kvseg, bool writer, uint16_t* lds_raw, uint16_t* sel_lds,
+                                int nb) {
   constexpr int NT = kMhaWaves * 64;
   const FusedSelect& f = p.fs;
   const SelLds<D> L(lds_raw);
   const int tid = threadIdx.x;
-  const int n = p.n_units;
+  const int n = nb;
+  // a ragged batch: the units past the sequence's own score +0
+  if (writer)
+    for (int i = n + tid; i < p.n_units; i += NT) f.scores[kvseg * p.n_units + i] = 0.f;
   int32_t* gout = f.sel_idx + kvseg * p.max_sel;
   SelResult r;
   if (threshold_select_ok(n, f.top_k)) {
@@ -519,30 +525,31 @@ __device__ __forceinline__ void tile_chunk_offsets(int lane, uint32_t (&voff)[Mh
 // MAYBE_OWN = false: the caller knows e > 0 (a wave's later tiles), so the own-block branch goes.
 // contig (uniform; contiguous caches with units of at least 32 tokens, or dense): a full tile is one
 // run of 32 consecutive cache rows, fetched from a scalar base plus the fixed offsets voff.
+// Lb, nb: the tokens and units of sequence b (the cache rows stay p.L apart).
 template <int D, bool DENSE, bool PAGED, bool MAYBE_OWN = true, int POL = kStreamPolicy>
 __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<PAGED>& rows, int b, int h,
                                               int e, int n_list, const TilePrep<D>& tp, uint16_t* slot,
                                               int lane, bool& bad, bool contig,
-                                              const uint32_t (&voff)[MhaShape<D>::INSTR],
+                                              const uint32_t (&voff)[MhaShape<D>::INSTR], int Lb, int nb,
                                               const int32_t* spt = nullptr) {
   using S = MhaShape<D>;
   constexpr int NI = S::INSTR;
   const int rsub = lane / S::PROW;
   const int sc = lane % S::PROW;
   const int64_t head = (int64_t)b * p.Hkv + h;   // h: the KV head within sequence b
-  const bool dec = MAYBE_OWN && ((e == 0) || (p.L == 0));   // uniform
+  const bool dec = MAYBE_OWN && ((e == 0) || (Lb == 0));   // uniform
   if constexpr (!PAGED) {
     const int t0 = (e - 1) * kTileTok;   // list position of the tile's first row
     int tok0 = t0;
     bool uok = true;
     if (!dec && contig && !DENSE) {
       const int u = __builtin_amdgcn_readfirstlane(tp.u[0]);
-      uok = (unsigned)u < (unsigned)p.n_units;
+      uok = (unsigned)u < (unsigned)nb;
       tok0 = (u << p.unit_log2) + (t0 & ((1 << p.unit_log2) - 1));
     }
     // a full tile of a valid unit that ends inside the cache (a cache whose last unit is partial
     // takes the general path for that unit's tiles)
-    if (!dec && contig && t0 + kTileTok <= n_list && (!uok || tok0 + kTileTok <= p.L)) {   // uniform
+    if (!dec && contig && t0 + kTileTok <= n_list && (!uok || tok0 + kTileTok <= Lb)) {   // uniform
       bad = bad || !uok;
       tok0 = uok ? tok0 : 0;   // an unusable unit reads the head's first rows and is masked out
       const char* kbase = reinterpret_cast<const char*>(p.k + (head * p.L + tok0) * D);
@@ -582,13 +589,13 @@ __device__ __forceinline__ uint32_t mha_issue(const MhaParams& p, const KvRows<P
       t[j] = ok[j] ? i : 0;
       if constexpr (!DENSE) {
         const int u = tp.u[j];
-        const bool uok = (unsigned)u < (unsigned)p.n_units;
+        const bool uok = (unsigned)u < (unsigned)nb;
         bad = bad || (ok[j] && !uok);
         ok[j] = ok[j] && uok;
         t[j] = uok ? (u << p.unit_log2) + (t[j] & ((1 << p.unit_log2) - 1)) : 0;
       }
-      ok[j] = ok[j] && t[j] < p.L;
-      t[j] = t[j] < p.L ? t[j] : 0;
+      ok[j] = ok[j] && t[j] < Lb;
+      t[j] = t[j] < Lb ? t[j] : 0;
     }
     if constexpr (PAGED) {
       kb = p.k;
@@ -758,6 +765,8 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     seg_i = (kv_i / p.Hkv) * p.H + (kv_i % p.Hkv) * p.G + member;
   }
   const int b = kv_i / p.Hkv, h = kv_i % p.Hkv;   // h: KV head within the sequence
+  const int Lb = seq_len(p.lens, b, p.L);         // this sequence's tokens (ragged batches)
+  const int nb = (Lb + (1 << p.unit_log2) - 1) >> p.unit_log2;
   FDL_STAMP(p, 0);
 #ifdef FDL_PHASE_STAMPS
   if (threadIdx.x == 0 && p.fs.stamps != nullptr)
@@ -813,9 +822,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     int nf;
     if constexpr (GQA) {
       float* xo = s == 0 ? p.fs.scores + kvseg * p.n_units : p.fs.xchg + (int64_t)gi * p.n_units;
-      nf = mha_score_phase<D, true, SAFE>(p, b, h, kvseg, gi, xo, member, p.G, lds, sel_lds);
+      nf = mha_score_phase<D, true, SAFE>(p, b, h, kvseg, gi, xo, member, p.G, lds, sel_lds, nb);
     } else {
-      nf = mha_score_phase<D, false, SAFE>(p, b, h, kvseg, seg, p.fs.scores + kvseg * p.n_units, s, NS, lds, sel_lds);
+      nf = mha_score_phase<D, false, SAFE>(p, b, h, kvseg, seg, p.fs.scores + kvseg * p.n_units, s, NS, lds, sel_lds,
+                                           nb);
     }
     // Known now: tile 0 (the block's own tokens) and the tiles of the nf forced units at the front
     // of the list.  Up to one of them per wave whose slot the selection scratch leaves free is
@@ -824,7 +834,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     // fetched early come last in that order.
     constexpr int FW = kFreeSlotWave<D>;
     const int tpu = p.unit_log2 >= 5 ? 1 << (p.unit_log2 - 5) : 0;   // tiles per unit
-    const int n_known = 1 + (p.L > 0 ? nf * tpu : 0);
+    const int n_known = 1 + (Lb > 0 ? nf * tpu : 0);
     const int cap = (kMhaWaves - FW) * NS;
     e_pre = n_known < cap ? n_known : cap;
     const int rr = wave < FW ? wave : FW + (kMhaWaves - 1 - wave);
@@ -834,21 +844,22 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     e = (wave >= FW && jp < e_pre) ? jp : e_rr;
     if (e < e_pre) {   // uniform per wave
       mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp, contig);
-      vm_next = mha_issue<D, false, false, true, POL>(p, rows, b, h, e, nf << p.unit_log2, tp, slot, lane, bad, contig, voff);
+      vm_next = mha_issue<D, false, false, true, POL>(p, rows, b, h, e, nf << p.unit_log2, tp, slot, lane, bad, contig, voff,
+                                                      Lb, nb);
       issued = true;
     }
-    const int ns = mha_choose_phase<D>(p, kvseg, s == 0 && member == 0, lds, sel_lds);
+    const int ns = mha_choose_phase<D>(p, kvseg, s == 0 && member == 0, lds, sel_lds, nb);
     FDL_STAMP(p, 5);
-    n_list = p.L == 0 ? 0 : ns << p.unit_log2;
+    n_list = Lb == 0 ? 0 : ns << p.unit_log2;
     e1 = 1 + (n_list + kTileTok - 1) / kTileTok;
     if (!issued) mha_prepare<D, false, true>(p, e, sel_row, sel_lds, lane, tp, contig);
   } else {
-    int n_part = DENSE ? p.L : (p.n_hint > 0 ? (p.n_hint < p.max_sel ? p.n_hint : p.max_sel) << p.unit_log2 : -1);
+    int n_part = DENSE ? Lb : (p.n_hint > 0 ? (p.n_hint < p.max_sel ? p.n_hint : p.max_sel) << p.unit_log2 : -1);
     if (!DENSE && n_part < 0) {
       const int ns_raw = p.n_sel[kvseg];   // no hint: the count comes first
       n_part = (ns_raw < 0 ? 0 : (ns_raw > p.max_sel ? p.max_sel : ns_raw)) << p.unit_log2;
     }
-    if (p.L == 0) n_part = 0;
+    if (Lb == 0) n_part = 0;
     const int n_tiles_part = 1 + (n_part + kTileTok - 1) / kTileTok;
     const int e0 = (int)((int64_t)n_tiles_part * s / NS);
     e1 = (int)((int64_t)n_tiles_part * (s + 1) / NS);
@@ -859,7 +870,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     if (!DENSE && p.n_hint > 0) {
       int ns = p.n_sel[kvseg];
       ns = ns < 0 ? 0 : (ns > p.max_sel ? p.max_sel : ns);
-      n_list = p.L == 0 ? 0 : ns << p.unit_log2;
+      n_list = Lb == 0 ? 0 : ns << p.unit_log2;
       const int n_tiles = 1 + (n_list + kTileTok - 1) / kTileTok;
       if (s == NS - 1) e1 = n_tiles;
       e1 = e1 < n_tiles ? e1 : n_tiles;
@@ -887,7 +898,8 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   bool fresh = true;   // no tile accumulated yet (uniform)
 
   if (!issued && e < e1)
-    vm_next = mha_issue<D, DENSE, PAGED, true, POL>(p, rows, b, h, e, n_list, tp, slot, lane, bad, contig, voff, spt);
+    vm_next = mha_issue<D, DENSE, PAGED, true, POL>(p, rows, b, h, e, n_list, tp, slot, lane, bad, contig, voff, Lb, nb,
+                                                    spt);
   const int swz_k = swz(ql) & (PROW - 1);
 #ifdef FDL_PHASE_STAMPS
   bool first_tile = true;
@@ -948,7 +960,9 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     }
     wait_lgkm0();
     // ---- fetch the next tile into the same slot; it flies while this one is finished ----
-    if (more) vm_next = mha_issue<D, DENSE, PAGED, false, POL>(p, rows, b, h, en, n_list, tp, slot, lane, bad, contig, voff, spt);
+    if (more)
+      vm_next = mha_issue<D, DENSE, PAGED, false, POL>(p, rows, b, h, en, n_list, tp, slot, lane, bad, contig, voff, Lb,
+                                                       nb, spt);
     float mx = -__builtin_inff();
     if (vm == 0xFFFFFFFFu) {   // uniform: every row of the tile is valid
 #pragma unroll
@@ -1305,6 +1319,7 @@ hipError_t launch_attn_mha(hipStream_t st, const Geom& g, const void* q, const v
   p.n_groups = g.B * g.Hkv * n_splits;
   p.n_hint = dense ? 0 : n_hint;
   p.merge_here = safe ? 0 : 1;
+  p.lens = g.lens;
   p.fs = fsel ? *fsel : FusedSelect{};
   // 8 XCDs: the splits of head seg run on XCD seg % 8; grouped-query heads: the G heads of KV
   // group i (a KV head and a split) run on XCD i % 8 (see the kernel)

@@ -136,6 +136,13 @@ __device__ __forceinline__ void latch(uint32_t* status, uint32_t bit) {
   atomicOr(status, bit);
 }
 
+// Cached tokens of sequence b: lens[b] clamped to [0, L] for a ragged batch, L otherwise.
+__device__ __forceinline__ int seq_len(const int32_t* lens, int b, int L) {
+  if (lens == nullptr) return L;
+  const int v = lens[b];
+  return v < 0 ? 0 : (v > L ? L : v);
+}
+
 // Element offset of row (b, g, t), 0 <= t < L, of a KV cache: contiguous [B][Hkv][L][D] or paged
 // [n_pages][Hkv][page_tokens][D] through page_table [B][pages_per_seq].  Branch-free: a bad page id
 // sets `bad` and the row of page 0 is addressed instead, so every returned offset is dereferenceable
@@ -143,9 +150,13 @@ __device__ __forceinline__ void latch(uint32_t* status, uint32_t bit) {
 // is used after the branch costs a full memory round trip per load).
 template <bool PAGED>
 struct KvRows {
-  int32_t Hkv, L, D;
+  int32_t Hkv, L, D;   // L: the row stride of a sequence (ctx_len)
   int32_t page_log2, pages_per_seq, n_pages;
   const int32_t* page_table;
+  const int32_t* lens = nullptr;   // per-sequence lengths of a ragged batch (contiguous caches)
+
+  // valid rows of sequence b
+  __device__ __forceinline__ int bound(int b) const { return seq_len(lens, b, L); }
 
   __device__ __forceinline__ int64_t off(int b, int g, int t, bool& bad) const {
     if constexpr (!PAGED) {

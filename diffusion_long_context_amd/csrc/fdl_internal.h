@@ -100,6 +100,7 @@ constexpr int kStampXcc = 15;
 struct Geom {
   int B, Hq, Hkv, G, D, L, bt, T, dtype;
   int paged, page_tokens, page_log2, pps, n_pages;
+  const int32_t* lens;   // device [B] per-sequence lengths (<= L after clamping), or NULL
 };
 
 // Cache write of rows [t0, t0 + n_tok) (K and V) with, when ks != NULL, the pooling of the units
@@ -126,7 +127,7 @@ hipError_t launch_pool_keys(hipStream_t s, const Geom& g, const void* k, const i
 hipError_t launch_score_units_max(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                                   const float* ks, int n_units, float* scores);
 hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
-                              const float* ks, int n_units, float* scores);
+                              const float* ks, int n_units, int unit_log2, float* scores);
 // Softmax-mass unit scores, bf16 queries, dec_len <= 32; scratch of mass_scratch_bytes.
 size_t mass_scratch_bytes(const Geom& g, int n_units);
 hipError_t launch_score_units_mass(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,

@@ -62,7 +62,8 @@ __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRo
     else return load_pair<KT>(p);
   };
   Leaf a[LEAVES];
-  const bool run = (t0 & (LEAVES - 1)) == 0 && t0 + LEAVES <= rows.L &&
+  const int Lb = rows.bound(b);   // this sequence's rows (ragged batches); the stride stays rows.L
+  const bool run = (t0 & (LEAVES - 1)) == 0 && t0 + LEAVES <= Lb &&
                    (!PAGED || rows.page_log2 >= ilog2_const(LEAVES));
   // a row whose page id is out of range has no key: it reads a valid row (so that the loads stay
   // unconditional), counts +0 and latches `bad`
@@ -78,12 +79,12 @@ __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRo
     for (int i = 0; i < LEAVES; ++i) {
       const int t = t0 + i;
       bool rb = false;
-      a[i] = load_leaf(k + rows.off(b, g, t < rows.L ? t : rows.L - 1, rb) + 2 * pair);
-      badm |= (uint64_t)(rb && t < rows.L) << i;
+      a[i] = load_leaf(k + rows.off(b, g, t < Lb ? t : (Lb > 0 ? Lb - 1 : 0), rb) + 2 * pair);
+      badm |= (uint64_t)(rb && t < Lb) << i;
     }
   }
   bad = bad || badm != 0;
-  const int live = rows.L - t0;   // leaves at or past it are +0
+  const int live = Lb - t0;   // leaves at or past it are +0
   auto keep = [&](int i) { return i < live && ((badm >> i) & 1ull) == 0; };
   if constexpr (kPacked) {
     float2 s[LEAVES / 2];
@@ -203,6 +204,7 @@ static KvRows<PAGED> make_rows(const Geom& g, const int32_t* page_table) {
   r.pages_per_seq = g.pps;
   r.n_pages = g.n_pages;
   r.page_table = page_table;
+  r.lens = g.lens;
   return r;
 }
 
@@ -444,7 +446,8 @@ __global__ __launch_bounds__(256) void score_units_kernel(const QT* __restrict__
                                                           const uint64_t* __restrict__ pred_mask,
                                                           const float* __restrict__ ks, int Hq,
                                                           int Hkv, int G, int T, int n_units,
-                                                          float* __restrict__ scores) {
+                                                          float* __restrict__ scores, const int32_t* lens,
+                                                          int L, int unit_log2) {
   constexpr int LPR = D / 16;            // lanes per row
   constexpr int kRowsPerWave = 64 / LPR;
   constexpr int kRowsPerPass = 4 * kRowsPerWave;
@@ -476,37 +479,39 @@ __global__ __launch_bounds__(256) void score_units_kernel(const QT* __restrict__
   float qv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
+  // a ragged batch's units past the sequence's own score +0
+  const int nb = lens == nullptr ? n_units : (seq_len(lens, b, L) + (1 << unit_log2) - 1) >> unit_log2;
 #pragma unroll
   for (int ps = 0; ps < kPasses; ++ps) {
     const int n = n0 + ps * kRowsPerPass + wave * kRowsPerWave + lane / LPR;
     const float sc = row_dot<LPR>(x[ps], qv);
-    if (n < n_units && j == 0) scores[((int64_t)b * Hkv + g) * n_units + n] = sc;
+    if (n < n_units && j == 0) scores[((int64_t)b * Hkv + g) * n_units + n] = n < nb ? sc : 0.f;
   }
 }
 
 template <typename QT, int D>
 static void launch_su(hipStream_t s, const Geom& g, const QT* q, const uint64_t* pm, const float* ks,
-                      int n_units, float* scores) {
+                      int n_units, int ulog, float* scores) {
   dim3 grid((n_units + kUnitsPerWg - 1) / kUnitsPerWg, g.Hkv, g.B);
   if (g.T <= 32)
     hipLaunchKernelGGL((score_units_kernel<QT, D, 32>), grid, dim3(256), 0, s, q, pm, ks, g.Hq, g.Hkv,
-                       g.G, g.T, n_units, scores);
+                       g.G, g.T, n_units, scores, g.lens, g.L, ulog);
   else
     hipLaunchKernelGGL((score_units_kernel<QT, D, 64>), grid, dim3(256), 0, s, q, pm, ks, g.Hq, g.Hkv,
-                       g.G, g.T, n_units, scores);
+                       g.G, g.T, n_units, scores, g.lens, g.L, ulog);
 }
 
 hipError_t launch_score_units(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
-                              const float* ks, int n_units, float* scores) {
+                              const float* ks, int n_units, int unit_log2, float* scores) {
   if (n_units == 0) return hipSuccess;
   if (g.dtype == FDL_BF16) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
-    if (g.D == 128) launch_su<uint16_t, 128>(s, g, qq, pred_mask, ks, n_units, scores);
-    else launch_su<uint16_t, 64>(s, g, qq, pred_mask, ks, n_units, scores);
+    if (g.D == 128) launch_su<uint16_t, 128>(s, g, qq, pred_mask, ks, n_units, unit_log2, scores);
+    else launch_su<uint16_t, 64>(s, g, qq, pred_mask, ks, n_units, unit_log2, scores);
   } else {
     const float* qq = static_cast<const float*>(q);
-    if (g.D == 128) launch_su<float, 128>(s, g, qq, pred_mask, ks, n_units, scores);
-    else launch_su<float, 64>(s, g, qq, pred_mask, ks, n_units, scores);
+    if (g.D == 128) launch_su<float, 128>(s, g, qq, pred_mask, ks, n_units, unit_log2, scores);
+    else launch_su<float, 64>(s, g, qq, pred_mask, ks, n_units, unit_log2, scores);
   }
   return hipGetLastError();
 }

@@ -36,7 +36,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int n_units, int unit_log2, const int32_t* __restrict__ sink_pos,
     const int32_t* __restrict__ n_sinks, int max_sinks, const int32_t* __restrict__ cand_idx,
     int n_cand, int top_k, int force_first, int max_sel, int Hkv, int32_t* __restrict__ sel_idx,
-    int32_t* __restrict__ n_sel, uint32_t* __restrict__ status, int shared) {
+    int32_t* __restrict__ n_sel, uint32_t* __restrict__ status, int shared, const int32_t* __restrict__ lens,
+    int L) {
   __shared__ uint32_t keys[kMaxSelN];
   __shared__ uint32_t forced[kMaxSelN / 32];
   __shared__ int hist[4 * 256];
@@ -45,9 +46,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int tid = threadIdx.x;
   const int g = blockIdx.y, b = blockIdx.z, c = blockIdx.x;
   const bool level2 = cand_idx != nullptr;
-  const int n = level2 ? (1 << unit_log2) : n_units;
+  // level 1 of a ragged batch: the sequence's own units; the scores rows keep n_units entries
+  const int n = level2 ? (1 << unit_log2)
+                       : (lens == nullptr ? n_units : (seq_len(lens, b, L) + (1 << unit_log2) - 1) >> unit_log2);
   const int64_t seg = (int64_t)b * Hkv + g;
-  const float* sc = level2 ? scores + (seg * n_cand + c) * (int64_t)n : scores + seg * n;
+  const float* sc = level2 ? scores + (seg * n_cand + c) * (int64_t)n : scores + seg * n_units;
 
   if (shared && !level2) {   // uniform; every head's workgroup derives the same keys
     const float* sb = scores + (int64_t)b * Hkv * n;
@@ -232,7 +235,7 @@ hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int 
   if (grid.x == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), 0, s, scores, n_units, unit_log2,
                      sink_pos, n_sinks, max_sinks, cand_idx, n_cand, top_k, force_first, max_sel,
-                     g.Hkv, sel_idx, n_sel, status, shared);
+                     g.Hkv, sel_idx, n_sel, status, shared, cand_idx == nullptr ? g.lens : nullptr, g.L);
   return hipGetLastError();
 }
 

@@ -70,6 +70,7 @@ struct SinkParams {
   uint32_t* bitmap;      // [B][words], zero on entry; sink_compact_kernel zeroes it again
   uint32_t* tickets;     // per (b, q-head), kSyncStride apart; left at zero
   uint32_t* status;
+  const int32_t* lens;   // per-sequence cached lengths of a ragged batch, or NULL (all L)
   int Hq, Hkv, G, T, L, n_splits, n_segs, cand_cap, words;
   float scale_log2, tau;
 };
@@ -116,6 +117,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   const uint64_t pred = p.pred_mask[b];
   const int n_pred = __popcll(pred);
   const int n_parts = NS * kSinkWaves;
+  const int Lb = seq_len(p.lens, b, p.L);   // this sequence's cached tokens; its rows stay p.L apart
   float m_run = -__builtin_inff(), l_run = 0.f;
   if (tid < kSinkWaves * 32) s_run[tid >> 5][tid & 31] = make_float2(-__builtin_inff(), 0.f);
   __syncthreads();
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
       }
     }
     const float inv_np = 1.f / (float)n_pred;
-    const int n_tiles = 1 + (p.L + kSinkTile - 1) / kSinkTile;
+    const int n_tiles = 1 + (Lb + kSinkTile - 1) / kSinkTile;
     const int e0 = (int)((int64_t)n_tiles * s / NS);
     const int e1 = (int)((int64_t)n_tiles * (s + 1) / NS);
     // tile e -> the wave's slot; rows are clamped so that every fetch is in bounds.  A full cache
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     }
     auto issue = [&](int e) {
       const int rsub = lane / PROW, sc = lane % PROW;
-      if (e > 0 && e * kSinkTile <= p.L) {   // uniform: a full tile of the cache
+      if (e > 0 && e * kSinkTile <= Lb) {   // uniform: a full tile of the cache
         const char* base = reinterpret_cast<const char*>(kctx + (int64_t)(e - 1) * kSinkTile * D);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
         const int r = j * RPI + rsub;
         const int t = (e - 1) * kSinkTile + r;
         const uint16_t* row = (e == 0) ? kdec + (int64_t)(r < p.T ? r : p.T - 1) * D
-                                       : kctx + (int64_t)(t < p.L ? t : p.L - 1) * D;
+                                       : kctx + (int64_t)(t < Lb ? t : Lb - 1) * D;
         const void* src = row + (sc ^ (swz(r) & (PROW - 1))) * 8;
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
       }
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
         }
       wait_lgkm0();
       if (e + kSinkWaves < e1) issue(e + kSinkWaves);   // next tile flies while this one is scored
-      const int nvalid = (e == 0) ? p.T : min(kSinkTile, p.L - (e - 1) * kSinkTile);
+      const int nvalid = (e == 0) ? p.T : min(kSinkTile, Lb - (e - 1) * kSinkTile);
       f32x16 sacc[RB];
       float mx = -__builtin_inff();
       {
@@ -442,7 +444,8 @@ __global__ __launch_bounds__(64) void sink_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ k_dec,
                                                       const uint64_t* __restrict__ pred_mask,
                                                       uint32_t* __restrict__ bitmap, int Hq, int Hkv,
-                                                      int G, int T, int L, int words, float tau) {
+                                                      int G, int T, int L, int words, float tau,
+                                                      const int32_t* __restrict__ lens) {
   __shared__ float kc[32][D + 1];
   __shared__ float ev[32][65];
   const int h = blockIdx.x, b = blockIdx.y, qi = threadIdx.x;
@@ -458,7 +461,8 @@ __global__ __launch_bounds__(64) void sink_f32_kernel(const float* __restrict__ 
   const float scale = 1.0f / sqrtf((float)D);
   const float* kd = k_dec + ((int64_t)b * Hkv + g) * T * D;
   const float* kx = k + ((int64_t)b * Hkv + g) * (int64_t)L * D;
-  const int total = T + L;
+  const int Lb = seq_len(lens, b, L);   // a ragged batch: this sequence's tokens (rows stay L apart)
+  const int total = T + Lb;
   // pass 1: log-sum-exp over own block + cached tokens
   float m = -__builtin_inff(), l = 0.f;
   for (int c0 = 0; c0 < total; c0 += 32) {
@@ -480,11 +484,11 @@ __global__ __launch_bounds__(64) void sink_f32_kernel(const float* __restrict__ 
   }
   const float lse = m + __logf(l);
   // pass 2: masses of cached tokens
-  for (int c0 = 0; c0 < L; c0 += 32) {
+  for (int c0 = 0; c0 < Lb; c0 += 32) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < 32 * D; idx += 64) {
       const int r = idx / D, d = idx % D, t = c0 + r;
-      kc[r][d] = t < L ? kx[(int64_t)t * D + d] : 0.f;
+      kc[r][d] = t < Lb ? kx[(int64_t)t * D + d] : 0.f;
     }
     __syncthreads();
     for (int r = 0; r < 32; ++r) {
@@ -494,7 +498,7 @@ __global__ __launch_bounds__(64) void sink_f32_kernel(const float* __restrict__ 
       ev[r][qi] = live ? __expf(acc * scale - lse) : 0.f;
     }
     __syncthreads();
-    if (qi < 32 && c0 + qi < L) {
+    if (qi < 32 && c0 + qi < Lb) {
       float a = 0.f;
       for (int j = 0; j < 64; ++j) a += ev[qi][j];
       if (a / (float)n_pred >= tau) {
@@ -625,6 +629,7 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
   p.G = g.G;
   p.T = g.T;
   p.L = g.L;
+  p.lens = g.lens;
   p.n_splits = n_splits;
   p.n_segs = g.B * g.Hq;
   p.cand_cap = cand_cap;
@@ -643,10 +648,10 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
     const float* kd = static_cast<const float*>(k_dec);
     if (g.D == 128)
       hipLaunchKernelGGL((sink_f32_kernel<128>), grid, dim3(64), 0, st, qq, kk, kd, pred_mask,
-                         p.bitmap, g.Hq, g.Hkv, g.G, g.T, g.L, words, tau);
+                         p.bitmap, g.Hq, g.Hkv, g.G, g.T, g.L, words, tau, g.lens);
     else
       hipLaunchKernelGGL((sink_f32_kernel<64>), grid, dim3(64), 0, st, qq, kk, kd, pred_mask,
-                         p.bitmap, g.Hq, g.Hkv, g.G, g.T, g.L, words, tau);
+                         p.bitmap, g.Hq, g.Hkv, g.G, g.T, g.L, words, tau, g.lens);
   } else if (g.L > 0) {
     // the splits of slot k run on XCD k % 8 (see the kernel)
     dim3 grid(8 * ((p.n_segs + 7) / 8) * n_splits);

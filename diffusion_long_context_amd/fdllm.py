@@ -48,7 +48,7 @@ class FdlError(RuntimeError):
 class fdl_geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "ctx_len", "kv_block", "dec_len", "dtype",
-        "paged", "page_tokens", "pages_per_seq", "n_pages")]
+        "paged", "page_tokens", "pages_per_seq", "n_pages")] + [("ctx_lens", ctypes.c_void_p)]
 
 
 class fdl_layer_io(ctypes.Structure):
@@ -139,9 +139,11 @@ class Geom:
     page_tokens: int = 0
     pages_per_seq: int = 0
     n_pages: int = 0
+    ctx_lens: object = None   # device int32 tensor [batch] of per-sequence lengths, or None
 
     def c(self) -> fdl_geom:
-        return fdl_geom(*[int(getattr(self, f)) for f, _ in fdl_geom._fields_])
+        ints = [int(getattr(self, f)) for f, _ in fdl_geom._fields_[:-1]]
+        return fdl_geom(*ints, _ptr(self.ctx_lens, 4 * self.batch, "ctx_lens"))
 
     @property
     def elem(self) -> int:

@@ -188,8 +188,10 @@ class ChunkedStep:
         self.attend(q, k_pool, v_pool, page_table, k_dec, v_dec, out)
 
 
-def geom_for(cfg, dtype=None) -> Geom:
-    """Geom from any object with the workload attributes (batch, n_q_heads, ...)."""
+def geom_for(cfg, dtype=None, ctx_lens=None) -> Geom:
+    """Geom from any object with the workload attributes (batch, n_q_heads, ...); ctx_lens: a device
+    int32 tensor [batch] of per-sequence cached lengths (a ragged batch; ctx_len is then the stride
+    and the largest length), or None."""
     dt = dtype if dtype is not None else (FDL_BF16 if cfg.dtype == "bf16" else 0)
     paged = bool(getattr(cfg, "paged", False))
     return Geom(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
@@ -197,4 +199,5 @@ def geom_for(cfg, dtype=None) -> Geom:
                 dec_len=cfg.dec_len, dtype=dt, paged=int(paged),
                 page_tokens=cfg.page_tokens if paged else 0,
                 pages_per_seq=(cfg.ctx_len // cfg.page_tokens) if paged else 0,
-                n_pages=(cfg.batch * (cfg.ctx_len // cfg.page_tokens)) if paged else 0)
+                n_pages=(cfg.batch * (cfg.ctx_len // cfg.page_tokens)) if paged else 0,
+                ctx_lens=ctx_lens)

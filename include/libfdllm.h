@@ -71,7 +71,18 @@ typedef struct fdl_ctx* fdl_handle;
  *   head_dim in {64, 128}; ctx_len >= 0; kv_block a power of two in [1, 4096];
  *   1 <= dec_len <= 64 (<= 32 for FDL_BF16 attention);
  *   paged: page_tokens a power of two in [1, 4096], pages_per_seq * page_tokens >= ctx_len,
- *   n_pages >= 1. */
+ *   n_pages >= 1.
+ * Ragged batches ([FK]: the contexts of a batch need not be equally long): ctx_lens, when not NULL,
+ * is a DEVICE int32 array [batch] of per-sequence cached-token counts; sequence b then has
+ * L_b = clamp(ctx_lens[b], 0, ctx_len) tokens, stored in the first L_b rows of its ctx_len-row
+ * stride of the contiguous cache ([B][Hkv][ctx_len][D]).  Every per-sequence quantity follows L_b:
+ * its units are the ceil(L_b / unit) units of its own tokens (the last one partial when L_b is not a
+ * multiple of the unit, pooled over its valid tokens), the units past them have pooled keys +0,
+ * score +0 and are never selected, sink detection and dense attention cover [0, L_b), and a unit
+ * id at or past a sequence's units is out of range (FDL_EINDEX).  Taken by the pooling, scoring,
+ * sink, selection (level 1), attention and step calls on contiguous caches; the other calls (paged
+ * caches, level 2, the max / mass scorers, token expansion, cache write) return FDL_EUNSUPPORTED
+ * with a non-NULL ctx_lens. */
 typedef struct {
   int32_t batch;          /* B   sequences                                   */
   int32_t n_q_heads;      /* Hq  query heads                                 */
@@ -85,6 +96,7 @@ typedef struct {
   int32_t page_tokens;    /* paged: tokens per page                          */
   int32_t pages_per_seq;  /* paged: page-table row length                    */
   int32_t n_pages;        /* paged: physical pages in the pool               */
+  const int32_t* ctx_lens;  /* device [batch] per-sequence lengths, or NULL   */
 } fdl_geom;
 
 /* ---- handle ------------------------------------------------------------------------------ */

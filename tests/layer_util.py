@@ -9,9 +9,9 @@ import torch
 from gpu_util import assert_close, dev, host, out_buffer, out_to_f64
 
 
-def _focus(h, cfg, x, modes=("source", "reuse"), sink_tokens=False):
+def _focus(h, cfg, x, modes=("source", "reuse"), sink_tokens=False, ctx_lens=None):
     from diffusion_long_context_amd.step import FocusParams, FocusStep, geom_for
-    g = geom_for(cfg)
+    g = geom_for(cfg, ctx_lens=dev(np.asarray(ctx_lens, np.int32)) if ctx_lens is not None else None)
     fs = FocusStep(h, g, FocusParams(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.sink_tau,
                                      cfg.max_sinks))
     t = {k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec", "masked")}
@@ -90,16 +90,17 @@ def _check_chunked(cfg, got, want):
     assert_close(got["out"], want["out"], "chunked")
 
 
-def focus_step_layers(h, cfg, xs, modes, prev_conf, masked):
+def focus_step_layers(h, cfg, xs, modes, prev_conf, masked, ctx_lens=None):
     """fdl_focus_step over one layer table (xs[l] holds layer l's q, k, v, k_dec, v_dec; modes[l] is
     "dense", "source" or "reuse"), with every sparse layer's scores and selection captured: the step
     is run once with the table cut after each sparse layer (the buffers then hold that layer's
-    values), then once in full for the outputs, predicted positions and sinks.  Returns
+    values), then once in full for the outputs, predicted positions and sinks.  ctx_lens: per-sequence
+    cached lengths of a ragged batch, or None.  Returns
     {"layers": {l: (scores, sel, n_sel)}, "outs": [...], "pred_mask", "sink_pos", "n_sinks", "bits"}."""
     from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
                                                   fdl_focus_params)
     from diffusion_long_context_amd.step import geom_for
-    g = geom_for(cfg)
+    g = geom_for(cfg, ctx_lens=dev(np.asarray(ctx_lens, np.int32)) if ctx_lens is not None else None)
     B, Hq, Hkv, D, T, nb, ms = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len,
                                 cfg.n_blk, cfg.max_sel_blocks)
     code = {"dense": FDL_LAYER_DENSE, "source": FDL_LAYER_SOURCE, "reuse": FDL_LAYER_REUSE}
