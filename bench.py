@@ -238,9 +238,11 @@ def time_decode_loop(h, g, cfg, params, Q, K, V, KD, VD, ks, outs, modes, pred_m
 def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
     """Diagnostics on the other workloads of the benchmark description (not the headline): the 8K MHA
     and 16K grouped-query single-layer configurations (per-layer GPU time of each layer kind through
-    fdl_focus_step, 32 layers of one kind per step) and the chunked paged batch-4 32K configuration
-    (the whole select-and-attend chain), each with the dense baseline on the same inputs and the
-    achieved rate on the bytes the sparse path must move.  Inputs are drawn on the device (seeded)."""
+    fdl_focus_step, 32 layers of one kind per step), a ragged batch of three 8K-stride sequences of
+    8192, 5000 and 1000 cached tokens (per-sequence lengths on the device), and the chunked paged
+    batch-4 32K configuration (the whole select-and-attend chain), each with the dense baseline on
+    the same inputs and the achieved rate on the bytes the sparse path must move.  Inputs are drawn
+    on the device (seeded)."""
     import torch
 
     from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
@@ -267,9 +269,11 @@ def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     out = {}
-    for ci in (1, 2):
-        cfg = get_config(ci)
-        g = geom_for(cfg)
+    ragged_lens = [8192, 5000, 1000]
+    for ci, kw, lens in ((1, {}, None), (2, {}, None), (1, dict(batch=3), ragged_lens)):
+        cfg = get_config(ci).with_(**kw)
+        lens_dev = torch.tensor(lens, dtype=torch.int32, device=dev) if lens else None
+        g = geom_for(cfg, ctx_lens=lens_dev)
         B, Hq, Hkv, D, L, T = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len, cfg.dec_len
         # the seeded inputs of the parity tests (sink keys, Beta(2, 5) confidences over the masked
         # positions, and at 16K the planted relevant blocks)
@@ -298,6 +302,13 @@ def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
                                                        sink_pos, n_sinks, sel_idx, n_sel), steps) / 32
         assert h.fdl_get_status() == 0
         sel_blocks = int(n_sel.sum())
+        if lens:
+            out[f"{cfg.name}_ragged_b3"] = {
+                "ctx_lens": lens, "layer_us": per, "speedup_reuse_vs_dense": per["dense"] / per["reuse"],
+                "reuse_kv_tokens_per_s": sum(lens) / (per["reuse"] * 1e-6),
+                "sel_blocks_per_kv_head": sel_blocks / (B * Hkv)}
+            del q, k, v, kd, vd, ks, o
+            continue
         reuse_bytes = sparse_launch_bytes(cfg, sel_blocks)
         out[cfg.name] = {
             "layer_us": per, "speedup_reuse_vs_dense": per["dense"] / per["reuse"],

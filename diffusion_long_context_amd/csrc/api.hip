@@ -26,8 +26,22 @@ fdl_status fail(fdl_handle h, fdl_status s, const char* fmt, ...) {
 }
 
 fdl_status hip_status(fdl_handle h, hipError_t e, const char* what) {
-  if (e == hipSuccess) return FDL_OK;
-  return fail(h, FDL_EHIP, "%s: %s", what, hipGetErrorString(e));
+  if (e != hipSuccess) return fail(h, FDL_EHIP, "%s: %s", what, hipGetErrorString(e));
+#ifdef FDL_DEBUG
+  // Debug build: every launch is waited for at once, so that a failing kernel is reported by the
+  // call that launched it, and a change of the status word is printed with the launch that made it.
+  // (Not for streams that the caller captures into a graph: the wait would end the capture.)
+  if (h && !h->capturing) {
+    const hipError_t w = hipStreamSynchronize(h->stream);
+    if (w != hipSuccess) return fail(h, FDL_EHIP, "%s (debug wait): %s", what, hipGetErrorString(w));
+    uint32_t word = 0;
+    if (hipMemcpy(&word, h->status, sizeof(word), hipMemcpyDeviceToHost) == hipSuccess && word != h->debug_seen) {
+      fprintf(stderr, "libfdllm debug: after %s the status word is 0x%x\n", what, word);
+      h->debug_seen = word;
+    }
+  }
+#endif
+  return FDL_OK;
 }
 
 bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -339,6 +353,7 @@ fdl_status fdl_get_status_bits(fdl_handle h, uint32_t* bits) {
   st = hip_status(h, hipMemcpy(&word, h->status, sizeof(word), hipMemcpyDeviceToHost), "hipMemcpy");
   if (st != FDL_OK) return st;
   if (word) {
+    h->debug_seen = 0;
     st = hip_status(h, hipMemset(h->status, 0, sizeof(uint32_t)), "hipMemset");
     if (st != FDL_OK) return st;
     st = hip_status(h, hipDeviceSynchronize(), "hipDeviceSynchronize");

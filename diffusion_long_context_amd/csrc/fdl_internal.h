@@ -27,6 +27,7 @@ struct fdl_ctx {
   uint64_t* stamps = nullptr;   // fdl_set_phase_buffer
   uint32_t fused_serial = 0;    // fused launches issued (part of their score-exchange tag)
   bool safe_sync = false;       // FDL_SAFE_SYNC: no hand-over between workgroups through L2
+  uint32_t debug_seen = 0;      // debug build: the status word as last reported
   int64_t stamp_words = 0;
   // optional event timing (fdl_profile_begin / fdl_profile_end)
   struct ProfRec {

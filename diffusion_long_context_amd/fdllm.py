@@ -17,7 +17,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfdllm.so")
+# FDLLM_LIB selects another build of the same library (the phase-stamp, debug or sanitized variant)
+LIB_PATH = os.environ.get("FDLLM_LIB") or os.path.join(_HERE, "libfdllm.so")
 
 FDL_OK, FDL_EINVAL, FDL_ENOMEM, FDL_EHIP, FDL_EOVERFLOW, FDL_EUNSUPPORTED, FDL_EINDEX = 0, -1, -2, -3, -4, -5, -6
 FDL_ESYNC = -7
