@@ -616,6 +616,38 @@ fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* gp, const void*
                     n_sel);
 }
 
+fdl_status fdl_select_chunks_tokens(fdl_handle h, const fdl_geom* gp, const void* q, const uint64_t* pred_mask,
+                                    const float* chunk_sums, const void* k_cache, const int32_t* page_table,
+                                    int32_t chunk_tokens, int32_t top_k_chunks, int32_t top_k, int32_t max_sel,
+                                    float* chunk_scores, int32_t* chunks, int32_t* n_chunks_sel,
+                                    float* token_scores, int32_t* sel_idx, int32_t* n_sel) {
+  if (!h) return FDL_EINVAL;
+  Geom g;
+  fdl_status st = check_geom(h, gp, g);
+  if (st != FDL_OK) return st;
+  if (!q || !pred_mask || !chunk_sums || !k_cache || !chunk_scores || !chunks || !n_chunks_sel || !token_scores ||
+      !sel_idx || !n_sel)
+    return fail(h, FDL_EINVAL, "every tensor argument but page_table must be non-NULL");
+  if ((st = no_lens(h, g, "fdl_select_chunks_tokens")) != FDL_OK) return st;
+  if (!is_pow2(chunk_tokens) || chunk_tokens > 4096)
+    return fail(h, FDL_EINVAL, "chunk_tokens must be a power of two in [1, 4096]");
+  if (g.L % chunk_tokens) return fail(h, FDL_EINVAL, "ctx_len %% chunk_tokens must be 0");
+  const int n_chunks = g.L / chunk_tokens;
+  if (top_k_chunks < 1 || top_k_chunks > n_chunks) return fail(h, FDL_EINVAL, "top_k_chunks must be in [1, n_chunks]");
+  if (g.paged && !page_table) return fail(h, FDL_EINVAL, "paged layout needs a page_table");
+  if (top_k < 0 || top_k > chunk_tokens - 1) return fail(h, FDL_EINVAL, "top_k must be in [0, chunk_tokens - 1]");
+  if (max_sel < 1 || (long long)top_k_chunks * (1 + top_k) > max_sel) return fail(h, FDL_EINVAL, "max_sel too small");
+  const int lg = ilog2(chunk_tokens);
+  if (!fdl::select_chunks_tokens_ok(g, lg, n_chunks))
+    return fail(h, FDL_EUNSUPPORTED, "one-launch chunk selection: bf16, dec_len <= 32, chunks of 256 to 4096 "
+                                     "tokens, pages >= 16 tokens, G <= 8 and at most 64 chunks");
+  ProfScope ps(h, FDL_PROF_SCORE);
+  return hip_status(h, fdl::launch_select_chunks_tokens(h->stream, g, q, pred_mask, chunk_sums, k_cache, page_table,
+                                                        lg, top_k_chunks, top_k, max_sel, chunk_scores, chunks,
+                                                        n_chunks_sel, token_scores, sel_idx, n_sel, h->status),
+                    "select_chunks_tokens launch");
+}
+
 // ---- sparse attention for callers that cannot allocate ------------------------------------------
 //
 // The split partials, the merge tickets and a status word live in one file-scope device array instead

@@ -373,7 +373,7 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
   // the query staging area sits above the keys' scratch in the (still unused) tile slots
   if constexpr (GQA) {
     __syncthreads();   // full vector-memory wait: every wave's query fetches have landed
-    qsum_grouped_tree<D, 32, 8>(pred, p.G, p.T, qstage, L.qs);
+    qsum_grouped_tree<D, 32, NT, 8>(pred, p.G, p.T, qstage, L.qs);
   } else {
     qsum_g1_finish<D, 32, NT>(qst, pred, p.T, reinterpret_cast<float*>(lds_raw) + kQbufOffsetF, L.qs);
   }
@@ -471,6 +471,7 @@ __device__ int mha_choose_phase(const MhaParams& p, int64_t kvseg, bool writer, 
     for (int i = n + tid; i < p.n_units; i += NT) f.scores[kvseg * p.n_units + i] = 0.f;
   int32_t* gout = f.sel_idx + kvseg * p.max_sel;
   SelResult r;
+  FDL_STAMP(p, 13);
   if (threshold_select_ok(n, f.top_k)) {
     auto emit = [&](int gpos, int lpos, int i) {
       if (lpos < p.max_sel) sel_lds[lpos] = (uint16_t)i;
@@ -492,6 +493,7 @@ __device__ int mha_choose_phase(const MhaParams& p, int64_t kvseg, bool writer, 
       r = select_core<NT, kFusedMaxUnits / NT>(L.keys, L.forced, n, f.top_k, scr, emit);
     }
   }
+  FDL_STAMP(p, 14);
   if (writer && tid == 0) f.n_sel[kvseg] = r.total < p.max_sel ? r.total : p.max_sel;
   if (tid == 0 && r.total > p.max_sel) latch(p.status, ST_SEL_OVERFLOW);
   block_sync_lds();   // sel_lds complete; the slots are free again

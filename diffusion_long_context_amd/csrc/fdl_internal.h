@@ -155,6 +155,15 @@ hipError_t launch_score_select_tokens(hipStream_t s, const Geom& g, const void* 
                                       const void* k, const int32_t* page_table, int unit_log2,
                                       const int32_t* cand_idx, int n_cand, int top_k, int max_sel,
                                       float* scores, int32_t* sel_idx, int32_t* n_sel, uint32_t* status);
+// Both levels in one launch: level 1 (chunk scores over the chunk sums, top_k_chunks of them
+// ascending) inside the level-2 kernel.  select_chunks_tokens_ok adds: at most 8 query heads per KV
+// head and 64 chunks per sequence.
+bool select_chunks_tokens_ok(const Geom& g, int unit_log2, int n_chunks);
+hipError_t launch_select_chunks_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                                       const float* chunk_sums, const void* k, const int32_t* page_table,
+                                       int unit_log2, int top_k_chunks, int top_k, int max_sel, float* chunk_scores,
+                                       int32_t* chunks, int32_t* n_chunks_sel, float* scores, int32_t* sel_idx,
+                                       int32_t* n_sel, uint32_t* status);
 
 hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int n_units,
                          int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,

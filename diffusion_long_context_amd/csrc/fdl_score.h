@@ -73,7 +73,7 @@ __device__ __forceinline__ void query_sum_to_lds(const QT* __restrict__ q, uint6
 
 // query_sum_to_lds for bf16 queries with every thread of an NT-thread block loading: the TMAX rows
 // of each of the G (<= GMAX) heads go to stage [GMAX][TMAX][D] (bf16 bits, LDS) as 16-byte chunks in
-// one round trip, then threads d < D build the same trees from LDS.  Same bits.  Two halves, so
+// one round trip, then the block's threads build the same trees from LDS.  Same bits.  Two halves, so
 // that a caller can issue other loads between them: qsum_grouped_issue loads this thread's chunks
 // into registers; qsum_grouped_finish (every thread calls it) stages them and sums.
 template <int D, int TMAX, int NT, int GMAX>
@@ -101,38 +101,68 @@ __device__ __forceinline__ void qsum_grouped_issue(const uint16_t* __restrict__ 
   }
 }
 
-// The trees over a filled stage (threads d < D; the stage must be visible to them).
-template <int D, int TMAX, int GMAX>
-__device__ __forceinline__ void qsum_grouped_tree(uint64_t pred, int G, int T, const uint16_t* stage, float* qs_lds) {
+// The trees over a filled stage ([GMAX][TMAX][D] bf16, visible to every thread), by all NT threads:
+// thread t takes the dimension pair (2c, 2c + 1), c = t % (D / 2), of heads t / (D / 2), + NT / (D / 2),
+// ... (one 32-bit read per slot) and builds each head's adjacent-pair tree over the TMAX slots; once
+// every thread's stage reads are done the head sums take the stage's place, and threads d < D build
+// the tree over the heads.  The additions and their order per dimension are those of one thread
+// running both trees; spreading the heads over the block's threads only shortens the chain of reads.
+// Every thread must call it (two barriers); qs_lds is complete after the caller's next barrier.
+template <int D, int TMAX, int NT, int GMAX>
+__device__ __forceinline__ void qsum_grouped_tree(uint64_t pred, int G, int T, uint16_t* stage, float* qs_lds) {
 #pragma clang fp contract(off)
+  constexpr int PAIRS = D / 2;
+  static_assert(NT % PAIRS == 0 && GMAX == 8, "a whole number of heads per pass; the head tree is over 8");
+  constexpr int JSTEP = NT / PAIRS;
+  constexpr int JPER = (GMAX + JSTEP - 1) / JSTEP;
   const int t = threadIdx.x;
-  if (t < D) {
-    const int T2 = pow2_ceil(T);
-    const int G2 = pow2_ceil(G);
-    float hv[GMAX];
+  const int c = t % PAIRS, j0 = t / PAIRS;
+  const int T2 = pow2_ceil(T);
+  const int G2 = pow2_ceil(G);
+  const uint32_t* st32 = reinterpret_cast<const uint32_t*>(stage);
+  float s0[JPER], s1[JPER];
 #pragma unroll
-    for (int j = 0; j < GMAX; ++j) {
-      float a[TMAX];
-      // every read is unconditional (a masked read becomes a branch and a wait per element), and
-      // the head's reads all go out before its tree starts
-      uint32_t raw[TMAX];
+  for (int k = 0; k < JPER; ++k) {
+    const int j = j0 + k * JSTEP;
+    const int jr = j < GMAX ? j : 0;
+    // every read is unconditional (a masked read becomes a branch and a wait per element), and the
+    // head's reads all go out before its tree starts
+    uint32_t raw[TMAX];
 #pragma unroll
-      for (int p = 0; p < TMAX; ++p) raw[p] = stage[(j * TMAX + p) * D + t];
-      __builtin_amdgcn_sched_barrier(0);
+    for (int p = 0; p < TMAX; ++p) raw[p] = st32[(jr * TMAX + p) * PAIRS + c];
+    __builtin_amdgcn_sched_barrier(0);
+    float a0[TMAX], a1[TMAX];
 #pragma unroll
-      for (int p = 0; p < TMAX; ++p) {
-        const bool keep = j < G && p < T && ((pred >> p) & 1ull);
-        a[p] = keep ? bf16_bits_to_f32(raw[p]) : 0.f;
-      }
+    for (int p = 0; p < TMAX; ++p) {
+      const bool keep = j < G && p < T && ((pred >> p) & 1ull);
+      a0[p] = keep ? bf16_bits_to_f32(raw[p] & 0xFFFFu) : 0.f;
+      a1[p] = keep ? bf16_bits_to_f32(raw[p] >> 16) : 0.f;
+    }
 #pragma unroll
-      for (int lvl = 0; lvl < 6; ++lvl) {
-        if ((TMAX >> (lvl + 1)) >= 1 && (1 << lvl) < T2) {
+    for (int lvl = 0; lvl < 6; ++lvl) {
+      if ((TMAX >> (lvl + 1)) >= 1 && (1 << lvl) < T2) {
 #pragma unroll
-          for (int i = 0; i < (TMAX >> (lvl + 1)); ++i) a[i] = a[2 * i] + a[2 * i + 1];
+        for (int i = 0; i < (TMAX >> (lvl + 1)); ++i) {
+          a0[i] = a0[2 * i] + a0[2 * i + 1];
+          a1[i] = a1[2 * i] + a1[2 * i + 1];
         }
       }
-      hv[j] = a[0];
     }
+    s0[k] = a0[0];
+    s1[k] = a1[0];
+  }
+  block_sync_lds();   // every stage read is done: the head sums take the stage's place
+  float* hs = reinterpret_cast<float*>(stage);
+#pragma unroll
+  for (int k = 0; k < JPER; ++k) {
+    const int j = j0 + k * JSTEP;
+    if (j < GMAX) *reinterpret_cast<float2*>(hs + j * D + 2 * c) = make_float2(s0[k], s1[k]);
+  }
+  block_sync_lds();
+  if (t < D) {
+    float hv[GMAX];
+#pragma unroll
+    for (int j = 0; j < GMAX; ++j) hv[j] = hs[j * D + t];
 #pragma unroll
     for (int lvl = 0; lvl < 3; ++lvl) {
       if ((1 << lvl) < G2) {
@@ -152,7 +182,7 @@ __device__ __forceinline__ void qsum_grouped_finish(const QsumGrouped<D, TMAX, N
 #pragma unroll
   for (int k = 0; k < S::PER; ++k) *reinterpret_cast<uint4*>(stage + (k * NT + t) * 8) = st.v[k];
   block_sync_lds();
-  qsum_grouped_tree<D, TMAX, GMAX>(pred, G, T, stage, qs_lds);
+  qsum_grouped_tree<D, TMAX, NT, GMAX>(pred, G, T, stage, qs_lds);
 }
 
 // The same stage filled by LDS fetches (no registers held while they fly): chunk c = k NT + t lands

@@ -7,6 +7,12 @@
 // select_kernel at level 2: the scores use the pinned query sum and row dot of fdl_score.h, the
 // selection is select_core (fdl_select.h).
 //
+// With CHOOSE, level 1 runs in the same launch: every workgroup of a (sequence, KV head) scores its
+// chunks against the same pinned query sum (the chunk sums' rows, as score_units_kernel does) and
+// ranks them (key descending, ties to the lower chunk), exactly as fdl_select_blocks at level 1 with
+// no sinks; slot c then takes the c-th chosen chunk in ascending order, and slot 0 writes the chunk
+// scores and the chosen list.  Two launches and their round trips fewer than the three-call chain.
+//
 // One workgroup per (sequence, KV head, chosen chunk).  The chunk's page-table entries are read once
 // into LDS, so every row address is known without a dependent load; the chunk's K rows then stream
 // in batches of 256 rows, the next batch's loads in flight while the current one is scored (the last
@@ -26,12 +32,24 @@ constexpr int kTsBatchRows = 256;      // rows per streaming batch
 constexpr int kTsMinPage = 16;         // smallest page (tokens) this kernel takes
 constexpr int kTsMaxPages = kTsThreads;   // page entries of one chunk: at most 4096 / 16 = 256
 
-template <int D, bool PAGED>
+constexpr int kTsMaxChunks = 64;      // chunks per sequence when level 1 runs in the same launch
+
+// Level 1 inside the level-2 launch (CHOOSE): chunk_sums [B][Hkv][n_chunks][D] float32, outputs
+// chunk_scores [B][Hkv][n_chunks], the chosen chunks [B][Hkv][n_cand] ascending and their count.
+struct ChunkChoice {
+  const float* chunk_sums;
+  float* chunk_scores;
+  int32_t* chunks;
+  int32_t* n_chunks_sel;
+  int n_chunks;
+};
+
+template <int D, bool PAGED, bool CHOOSE>
 __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
     const uint16_t* __restrict__ q, const uint64_t* __restrict__ pred_mask, const uint16_t* __restrict__ k,
     KvRows<PAGED> rows, int Hq, int G, int T, int unit_log2, const int32_t* __restrict__ cand_idx, int n_cand,
     int top_k, int max_sel, float* __restrict__ scores, int32_t* __restrict__ sel_idx,
-    int32_t* __restrict__ n_sel, uint32_t* __restrict__ status) {
+    int32_t* __restrict__ n_sel, uint32_t* __restrict__ status, const ChunkChoice cc) {
   constexpr int NT = kTsThreads;
   constexpr int LPR = D / 16;           // lanes per row, 16 dimensions each
   constexpr int RPW = 64 / LPR;         // rows per wave and pass
@@ -52,22 +70,39 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
   const int n = 1 << unit_log2;
   const int n_units = rows.L >> unit_log2;   // ctx_len is a multiple of the unit
   const int64_t seg = (int64_t)b * rows.Hkv + g;
-  const int u = cand_idx[seg * n_cand + c];
-  const bool uok = (unsigned)u < (unsigned)n_units;   // uniform
-  const int tok0 = uok ? u << unit_log2 : 0;
-  bool bad = !uok;
+  __shared__ uint32_t s_ck[CHOOSE ? kTsMaxChunks : 1];   // level 1: the chunks' order keys
+  __shared__ int s_u;
 
-  // loads in the order they are needed: the group's query rows, the chunk's page entries, the
-  // first batch of K rows
+  // loads in the order they are needed: the group's query rows (with CHOOSE, then the chunk sums'
+  // rows), the chunk's page entries, the first batch of K rows
   QsumGrouped<D, 32, NT, 8> qst;
   qsum_grouped_issue<D, 32, NT, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
-  const int pg0 = PAGED ? tok0 >> rows.page_log2 : 0;
-  const int n_pg = PAGED ? ((tok0 + n - 1) >> rows.page_log2) - pg0 + 1 : 0;
-  int my_page = 0;
-  if (PAGED) {
-    const int i = tid < n_pg ? tid : 0;
-    my_page = rows.page_table[(int64_t)b * rows.pages_per_seq + pg0 + i];
+  constexpr int CP = CHOOSE ? kTsMaxChunks / RPP : 1;   // level-1 row passes
+  float xc[CP][16];
+  if constexpr (CHOOSE) {
+#pragma unroll
+    for (int ps = 0; ps < CP; ++ps) {
+      int r = ps * RPP + wave * RPW + lane / LPR;
+      r = r < cc.n_chunks ? r : cc.n_chunks - 1;
+      load16<float>(cc.chunk_sums + (seg * cc.n_chunks + r) * D + 16 * j, xc[ps]);
+    }
   }
+  int u = 0;
+  if constexpr (!CHOOSE) u = cand_idx[seg * n_cand + c];
+  // with CHOOSE the chunk is known after level 1; its page entries are read then
+  auto page_loads = [&](int tok0_, int& pg0_, int& n_pg_, int& my_page_) {
+    pg0_ = PAGED ? tok0_ >> rows.page_log2 : 0;
+    n_pg_ = PAGED ? ((tok0_ + n - 1) >> rows.page_log2) - pg0_ + 1 : 0;
+    my_page_ = 0;
+    if (PAGED) {
+      const int i = tid < n_pg_ ? tid : 0;
+      my_page_ = rows.page_table[(int64_t)b * rows.pages_per_seq + pg0_ + i];
+    }
+  };
+  bool uok = (unsigned)u < (unsigned)n_units;   // uniform
+  int tok0 = uok ? u << unit_log2 : 0;
+  int pg0 = 0, n_pg = 0, my_page = 0;
+  if constexpr (!CHOOSE) page_loads(tok0, pg0, n_pg, my_page);
   // row offset of chunk row r (element units); invalid rows read row 0 of the pool and score -inf
   auto row_off = [&](int r, bool& ok) -> int64_t {
     const int t = tok0 + r;
@@ -83,13 +118,51 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
   };
 
   for (int i = tid; i < kTsMaxUnit / 32; i += NT) forced[i] = (i == 0) ? 1u : 0u;   // the anchor
-  if (PAGED && tid < n_pg) s_pages[tid] = my_page;
-  qsum_grouped_finish<D, 32, NT, 8>(qst, pred_mask[b], G, T, big, qs);   // one barrier inside
+  if (!CHOOSE && PAGED && tid < n_pg) s_pages[tid] = my_page;
+  qsum_grouped_finish<D, 32, NT, 8>(qst, pred_mask[b], G, T, big, qs);   // barriers inside
   __syncthreads();   // qs, the page entries and the forced bits; the stage is free again
 
   float qv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
+  if constexpr (CHOOSE) {
+    // level 1: the chunk scores (slot 0 writes them), then the rank of every chunk in one wave
+#pragma unroll
+    for (int ps = 0; ps < CP; ++ps) {
+      const int r = ps * RPP + wave * RPW + lane / LPR;
+      const float sc = row_dot<LPR>(xc[ps], qv);
+      if (j == 0 && r < cc.n_chunks) {
+        s_ck[r] = order_key(sc);
+        if (c == 0) cc.chunk_scores[seg * cc.n_chunks + r] = sc;
+      }
+    }
+    block_sync_lds();
+    if (wave == 0) {
+      const bool v = lane < cc.n_chunks;
+      const uint32_t key = v ? s_ck[lane] : 0u;
+      int rank = 0;
+      for (int i = 0; i < cc.n_chunks; ++i) {   // uniform; ties go to the lower chunk
+        const uint32_t ki = s_ck[i];
+        rank += (ki > key || (ki == key && i < lane)) ? 1 : 0;
+      }
+      const bool chosen = v && rank < n_cand;
+      const uint64_t cm = __ballot(chosen);
+      if (chosen) {
+        const int pos = __popcll(cm & ((1ull << lane) - 1ull));
+        if (pos == c) s_u = lane;
+        if (c == 0) cc.chunks[seg * n_cand + pos] = lane;
+      }
+      if (c == 0 && lane == 0) cc.n_chunks_sel[seg] = n_cand;
+    }
+    block_sync_lds();
+    u = __builtin_amdgcn_readfirstlane(s_u);
+    uok = (unsigned)u < (unsigned)n_units;
+    tok0 = uok ? u << unit_log2 : 0;
+    page_loads(tok0, pg0, n_pg, my_page);
+    if (PAGED && tid < n_pg) s_pages[tid] = my_page;
+    if (PAGED) block_sync_lds();   // the page entries, for every row
+  }
+  bool bad = !uok;
   uint32_t* keys = reinterpret_cast<uint32_t*>(big);
   float* sc_out = scores + (seg * n_cand + c) * (int64_t)n;
   const int nb = (n + kTsBatchRows - 1) / kTsBatchRows;
@@ -154,11 +227,11 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
   if (tid == 0 && c == 0) n_sel[seg] = n_cand * (nf + r.kk);
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool CHOOSE>
 static hipError_t launch_sst(hipStream_t s, const Geom& g, const uint16_t* q, const uint64_t* pm,
                              const uint16_t* k, const int32_t* page_table, int unit_log2,
                              const int32_t* cand_idx, int n_cand, int top_k, int max_sel, float* scores,
-                             int32_t* sel_idx, int32_t* n_sel, uint32_t* status) {
+                             int32_t* sel_idx, int32_t* n_sel, uint32_t* status, const ChunkChoice& cc) {
   KvRows<PAGED> rows;
   rows.Hkv = g.Hkv;
   rows.L = g.L;
@@ -167,10 +240,28 @@ static hipError_t launch_sst(hipStream_t s, const Geom& g, const uint16_t* q, co
   rows.pages_per_seq = g.pps;
   rows.n_pages = g.n_pages;
   rows.page_table = page_table;
-  hipLaunchKernelGGL((score_select_tokens_kernel<D, PAGED>), dim3(n_cand, g.Hkv, g.B), dim3(kTsThreads), 0, s, q,
-                     pm, k, rows, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, top_k, max_sel, scores, sel_idx,
-                     n_sel, status);
+  hipLaunchKernelGGL((score_select_tokens_kernel<D, PAGED, CHOOSE>), dim3(n_cand, g.Hkv, g.B), dim3(kTsThreads), 0,
+                     s, q, pm, k, rows, g.Hq, g.G, g.T, unit_log2, cand_idx, n_cand, top_k, max_sel, scores,
+                     sel_idx, n_sel, status, cc);
   return hipGetLastError();
+}
+
+template <bool CHOOSE>
+static hipError_t dispatch_sst(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask, const void* k,
+                               const int32_t* page_table, int unit_log2, const int32_t* cand_idx, int n_cand,
+                               int top_k, int max_sel, float* scores, int32_t* sel_idx, int32_t* n_sel,
+                               uint32_t* status, const ChunkChoice& cc) {
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  if (g.D == 128)
+    return g.paged ? launch_sst<128, true, CHOOSE>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand,
+                                                   top_k, max_sel, scores, sel_idx, n_sel, status, cc)
+                   : launch_sst<128, false, CHOOSE>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand,
+                                                    top_k, max_sel, scores, sel_idx, n_sel, status, cc);
+  return g.paged ? launch_sst<64, true, CHOOSE>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand,
+                                                top_k, max_sel, scores, sel_idx, n_sel, status, cc)
+                 : launch_sst<64, false, CHOOSE>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand,
+                                                 top_k, max_sel, scores, sel_idx, n_sel, status, cc);
 }
 
 bool score_select_tokens_ok(const Geom& g, int unit_log2) {
@@ -180,22 +271,30 @@ bool score_select_tokens_ok(const Geom& g, int unit_log2) {
          (1 << unit_log2) >= kTsBatchRows && (!g.paged || (1 << g.page_log2) >= kTsMinPage);
 }
 
+bool select_chunks_tokens_ok(const Geom& g, int unit_log2, int n_chunks) {
+  return score_select_tokens_ok(g, unit_log2) && g.G <= 8 && n_chunks >= 1 && n_chunks <= kTsMaxChunks;
+}
+
 hipError_t launch_score_select_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                                       const void* k, const int32_t* page_table, int unit_log2,
                                       const int32_t* cand_idx, int n_cand, int top_k, int max_sel,
                                       float* scores, int32_t* sel_idx, int32_t* n_sel, uint32_t* status) {
   if (!score_select_tokens_ok(g, unit_log2)) return hipErrorInvalidValue;
-  const uint16_t* qq = static_cast<const uint16_t*>(q);
-  const uint16_t* kk = static_cast<const uint16_t*>(k);
-  if (g.D == 128)
-    return g.paged ? launch_sst<128, true>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand, top_k,
-                                           max_sel, scores, sel_idx, n_sel, status)
-                   : launch_sst<128, false>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand, top_k,
-                                            max_sel, scores, sel_idx, n_sel, status);
-  return g.paged ? launch_sst<64, true>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand, top_k,
-                                        max_sel, scores, sel_idx, n_sel, status)
-                 : launch_sst<64, false>(s, g, qq, pred_mask, kk, page_table, unit_log2, cand_idx, n_cand, top_k,
-                                         max_sel, scores, sel_idx, n_sel, status);
+  return dispatch_sst<false>(s, g, q, pred_mask, k, page_table, unit_log2, cand_idx, n_cand, top_k, max_sel, scores,
+                             sel_idx, n_sel, status, ChunkChoice{nullptr, nullptr, nullptr, nullptr, 0});
+}
+
+hipError_t launch_select_chunks_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
+                                       const float* chunk_sums, const void* k, const int32_t* page_table,
+                                       int unit_log2, int top_k_chunks, int top_k, int max_sel, float* chunk_scores,
+                                       int32_t* chunks, int32_t* n_chunks_sel, float* scores, int32_t* sel_idx,
+                                       int32_t* n_sel, uint32_t* status) {
+  const int n_chunks = g.L >> unit_log2;
+  if (!select_chunks_tokens_ok(g, unit_log2, n_chunks) || top_k_chunks < 1 || top_k_chunks > n_chunks)
+    return hipErrorInvalidValue;
+  const ChunkChoice cc{chunk_sums, chunk_scores, chunks, n_chunks_sel, n_chunks};
+  return dispatch_sst<true>(s, g, q, pred_mask, k, page_table, unit_log2, nullptr, top_k_chunks, top_k, max_sel,
+                            scores, sel_idx, n_sel, status, cc);
 }
 
 }  // namespace fdl

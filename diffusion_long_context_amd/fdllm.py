@@ -28,7 +28,7 @@ EXPORTED = (
     "fdl_create", "fdl_destroy", "fdl_set_stream", "fdl_get_status", "fdl_get_status_bits",
     "fdl_status_string",
     "fdl_last_error", "fdl_pool_keys", "fdl_cache_write", "fdl_predict_queries", "fdl_score_blocks",
-    "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_select_blocks_shared", "fdl_expand_tokens", "fdl_score_select_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
+    "fdl_score_blocks_max", "fdl_score_blocks_mass", "fdl_select_blocks", "fdl_select_blocks_shared", "fdl_expand_tokens", "fdl_score_select_tokens", "fdl_select_chunks_tokens", "fdl_sparse_attn", "fdl_dense_attn", "fdl_focus_step",
     "fdl_unmask", "fdl_decode_steps", "fdl_capture_begin", "fdl_capture_end", "fdl_graph_launch",
     "fdl_graph_destroy", "fdl_profile_begin", "fdl_profile_end", "fdl_bandwidth_probe",
     "fdl_sparse_attn_noalloc", "fdl_set_phase_buffer", "fdl_phase_stamps_built",
@@ -87,6 +87,8 @@ _SIGS = {
     "fdl_select_blocks_shared": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _I, _I, _P, _P, _I, _I, _I, _P, _P]),
     "fdl_score_select_tokens": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P,
                                      _P]),
+    "fdl_select_chunks_tokens": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
+                                      _P, _P, _P, _P]),
     "fdl_sparse_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P]),
     "fdl_dense_attn": (_I, [_P, ctypes.POINTER(fdl_geom), _P, _P, _P, _P, _P, _P, _P]),
     "fdl_focus_step": (_I, [_P, ctypes.POINTER(fdl_geom), ctypes.POINTER(fdl_focus_params), _P, _P, _I,
@@ -347,6 +349,22 @@ class Handle:
             _ptr(cand_idx, 4 * B * Hkv * n_cand, "cand_idx"), n_cand, top_k, max_sel,
             _ptr(scores, 4 * B * Hkv * n_cand * unit_tokens, "scores"), _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"),
             _ptr(n_sel, 4 * B * Hkv, "n_sel")))
+
+    def fdl_select_chunks_tokens(self, g: Geom, q, pred_mask, chunk_sums, k_cache, page_table, chunk_tokens: int,
+                                 top_k_chunks: int, top_k: int, max_sel: int, chunk_scores, chunks, n_chunks_sel,
+                                 token_scores, sel_idx, n_sel):
+        self.sync_stream()
+        B, Hkv = g.batch, g.n_kv_heads
+        nc = g.ctx_len // chunk_tokens
+        self._check(self.lib.fdl_select_chunks_tokens(
+            self.h, ctypes.byref(g.c()), _ptr(q, B * g.n_q_heads * g.dec_len * g.head_dim * g.elem, "q"),
+            _ptr(pred_mask, 8 * B, "pred_mask"), _ptr(chunk_sums, 4 * B * Hkv * nc * g.head_dim, "chunk_sums"),
+            _ptr(k_cache, g.kv_elems * g.elem, "k_cache"),
+            _ptr(page_table, 4 * B * g.pages_per_seq if g.paged else None, "page_table"), chunk_tokens,
+            top_k_chunks, top_k, max_sel, _ptr(chunk_scores, 4 * B * Hkv * nc, "chunk_scores"),
+            _ptr(chunks, 4 * B * Hkv * top_k_chunks, "chunks"), _ptr(n_chunks_sel, 4 * B * Hkv, "n_chunks_sel"),
+            _ptr(token_scores, 4 * B * Hkv * top_k_chunks * chunk_tokens, "token_scores"),
+            _ptr(sel_idx, 4 * B * Hkv * max_sel, "sel_idx"), _ptr(n_sel, 4 * B * Hkv, "n_sel")))
 
     def _attn_ptrs(self, g: Geom, q, k_cache, v_cache, k_dec, v_dec, page_table, out):
         B, D = g.batch, g.head_dim

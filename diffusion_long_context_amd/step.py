@@ -157,11 +157,20 @@ class ChunkedStep:
         self.h.fdl_predict_queries(self.g.batch, self.g.dec_len, prev_conf, masked, self.cp.top_k_pos,
                                    self.cp.window, self.pred_mask, self.n_pred)
 
-    def select(self, q, k_pool, page_table, cs, separate: bool = False, per_sequence: bool = False):
+    def select(self, q, k_pool, page_table, cs, separate: bool = False, per_sequence: bool = False,
+               one_launch: bool = True):
         """Level 1 (chunk scores, top chunks per KV head, or with per_sequence=True one chunk set per
         sequence from the scores summed over its KV heads), then level 2 (token scores inside them,
-        anchor + top tokens) -- as one call, or with separate=True as the score and select calls."""
+        anchor + top tokens).  Per KV head, both levels run as one launch (fdl_select_chunks_tokens)
+        where its shape allows and one_launch is set; otherwise level 1 as two calls and level 2 as
+        one call, or with separate=True as the score and select calls."""
         g, cp = self.g, self.cp
+        if one_launch and not separate and not per_sequence and self.one_launch_ok():
+            self.h.fdl_select_chunks_tokens(g, q, self.pred_mask, cs, k_pool, page_table, cp.chunk_tokens,
+                                            cp.top_k_chunks, cp.keep_tokens, self.max_tok, self.chunk_scores,
+                                            self.chunks, self.n_chunks_sel, self.token_scores, self.tokens,
+                                            self.n_tokens)
+            return
         self.h.fdl_score_blocks(g, q, self.pred_mask, cs, cp.chunk_tokens, self.chunk_scores)
         select = self.h.fdl_select_blocks_shared if per_sequence else self.h.fdl_select_blocks
         select(g, self.chunk_scores, self.n_chunks, cp.chunk_tokens, None, None, 1, cp.top_k_chunks, cp.top_k_chunks,
@@ -178,13 +187,21 @@ class ChunkedStep:
                                  cp.keep_tokens, self.max_tok, self.tokens, self.n_tokens,
                                  cand_idx=self.chunks, n_cand=cp.top_k_chunks, force_first=True)
 
+    def one_launch_ok(self) -> bool:
+        """The shapes fdl_select_chunks_tokens takes (see its declaration)."""
+        g, cp = self.g, self.cp
+        page_ok = not g.paged or g.page_tokens >= 16
+        return (g.dtype == FDL_BF16 and g.dec_len <= 32 and g.head_dim in (64, 128) and 256 <= cp.chunk_tokens <= 4096
+                and page_ok and g.n_q_heads // g.n_kv_heads <= 8 and 1 <= self.n_chunks <= 64
+                and 1 <= cp.top_k_chunks <= self.n_chunks)
+
     def attend(self, q, k_pool, v_pool, page_table, k_dec, v_dec, out):
         self.h.fdl_sparse_attn(self.g, q, k_pool, v_pool, k_dec, v_dec, page_table, self.tokens,
                                self.n_tokens, self.max_tok, 1, out)
 
     def run(self, q, k_pool, v_pool, page_table, k_dec, v_dec, cs, out, separate: bool = False,
-            per_sequence: bool = False):
-        self.select(q, k_pool, page_table, cs, separate, per_sequence)
+            per_sequence: bool = False, one_launch: bool = True):
+        self.select(q, k_pool, page_table, cs, separate, per_sequence, one_launch)
         self.attend(q, k_pool, v_pool, page_table, k_dec, v_dec, out)
 
 

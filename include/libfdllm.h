@@ -277,6 +277,24 @@ fdl_status fdl_score_select_tokens(fdl_handle h, const fdl_geom* g, const void* 
                                    const int32_t* cand_idx, int32_t n_cand, int32_t top_k, int32_t max_sel,
                                    float* scores, int32_t* sel_idx, int32_t* n_sel);
 
+/* [PA] both levels of the chunked selection in one launch: the top-K chunks per (sequence, KV head),
+ * then inside each the anchor plus the top `top_k` other tokens.  The same outputs, bit for bit, as
+ *   fdl_score_blocks (level 1: chunk_sums [B][Hkv][n_chunks][D] float32 from fdl_pool_keys with
+ *     unit_tokens = chunk_tokens, scores to chunk_scores [B][Hkv][n_chunks]),
+ *   fdl_select_blocks (level 1, no sinks, top_k = max_sel = top_k_chunks: the chosen chunks
+ *     ascending in chunks [B][Hkv][top_k_chunks], their count in n_chunks_sel [B][Hkv]),
+ *   fdl_score_select_tokens (cand_idx = chunks, n_cand = top_k_chunks; token_scores
+ *     [B][Hkv][top_k_chunks][chunk_tokens], sel_idx [B][Hkv][max_sel], n_sel [B][Hkv]),
+ * with n_chunks = ctx_len / chunk_tokens.  Requirements: those of the three calls, plus bf16,
+ * dec_len <= 32, chunks of 256 to 4096 tokens, pages of at least 16 tokens, at most 8 query heads
+ * per KV head, n_chunks <= 64 and 1 <= top_k_chunks <= n_chunks (FDL_EUNSUPPORTED for a shape
+ * outside them, FDL_EINVAL for bad arguments).  Out-of-range page ids latch FDL_EINDEX. */
+fdl_status fdl_select_chunks_tokens(fdl_handle h, const fdl_geom* g, const void* q, const uint64_t* pred_mask,
+                                    const float* chunk_sums, const void* k_cache, const int32_t* page_table,
+                                    int32_t chunk_tokens, int32_t top_k_chunks, int32_t top_k, int32_t max_sel,
+                                    float* chunk_scores, int32_t* chunks, int32_t* n_chunks_sel,
+                                    float* token_scores, int32_t* sel_idx, int32_t* n_sel);
+
 /* Token-granular sink retention, the other reading of how sinks are kept ([FA] Elamur "Summary":
  * sinks are always preserved; at which granularity is left open): select the units with
  * fdl_select_blocks level 1 WITHOUT sinks (so the top-K comes from all units), then this call

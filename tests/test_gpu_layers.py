@@ -74,30 +74,39 @@ def test_chunked_page_order_bitwise_invariant(h):
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(n_q_heads=8, n_kv_heads=2), dict(chunk_tokens=256, page_tokens=16),
-                                dict(chunk_tokens=1024, head_dim=64)],
-                         ids=["mha", "gqa4", "chunk256-page16", "chunk1024-d64"])
+                                dict(chunk_tokens=1024, head_dim=64), dict(n_q_heads=14, n_kv_heads=2),
+                                dict(ctx_len=16384, chunk_tokens=256, top_k_chunks=7),
+                                dict(top_k_chunks=8)],
+                         ids=["mha", "gqa4", "chunk256-page16", "chunk1024-d64", "gqa7", "64-chunks", "all-chunks"])
 def test_level2_one_call_equals_two_calls(h, kw):
-    """fdl_score_select_tokens (one kernel) against fdl_score_blocks + fdl_select_blocks at level 2:
-    token scores, selections and counts bit for bit."""
+    """The chunk selection three ways, bit for bit: both levels in one launch
+    (fdl_select_chunks_tokens); level 1 as fdl_score_blocks + fdl_select_blocks and level 2 as
+    fdl_score_select_tokens (one kernel); every level as the score and select calls.  Chunk scores,
+    chosen chunks, token scores, selections and counts."""
     from diffusion_long_context_amd.step import ChunkedStep, ChunkParams, geom_for
     cfg = get_config(4).with_(**dict(dict(batch=2, n_q_heads=4, n_kv_heads=4, ctx_len=4096, chunk_tokens=512), **kw))
     x = make_single(cfg)
     g = geom_for(cfg)
     res = []
-    for separate in (False, True):
+    for separate, one in ((False, True), (False, False), (True, False)):
         cs_ = ChunkedStep(h, g, ChunkParams(cfg.top_k_pos, cfg.window, cfg.chunk_tokens, cfg.top_k_chunks,
                                             cfg.tokens_per_chunk_kept))
+        if one:
+            assert cs_.one_launch_ok()
         t = {k: dev(x[k]) for k in ("q", "k_pool", "page_table", "masked", "prev_conf")}
         cs_.predict(t["prev_conf"], t["masked"])
         cs = cs_.new_chunk_sums()
         cs_.pool(t["k_pool"], t["page_table"], cs)
-        cs_.select(t["q"], t["k_pool"], t["page_table"], cs, separate=separate)
+        cs_.select(t["q"], t["k_pool"], t["page_table"], cs, separate=separate, one_launch=one)
         torch.cuda.synchronize()
         assert h.fdl_get_status() == 0
-        res.append([host(v) for v in (cs_.token_scores, cs_.tokens, cs_.n_tokens)])
-    assert np.array_equal(res[0][0].view(np.uint32), res[1][0].view(np.uint32))
-    assert np.array_equal(res[0][1], res[1][1])
-    assert np.array_equal(res[0][2], res[1][2])
+        res.append([host(v).copy() for v in (cs_.chunk_scores, cs_.chunks, cs_.n_chunks_sel, cs_.token_scores,
+                                              cs_.tokens, cs_.n_tokens)])
+    for other in res[1:]:
+        for i, (a, b) in enumerate(zip(res[0], other)):
+            a = a.view(np.uint32) if a.dtype == np.float32 else a
+            b = b.view(np.uint32) if b.dtype == np.float32 else b
+            assert np.array_equal(a, b), i
 
 
 @pytest.mark.parametrize("kw", [dict(batch=2, n_q_heads=4, n_kv_heads=4, ctx_len=4096, chunk_tokens=512),
