@@ -37,7 +37,9 @@ WORKSPACE_BYTES = 256 << 20   # library workspace of the timed handle (sets the 
 # (FETCH_SIZE, WRITE_SIZE; scaled by a 1 GiB copy in the same runs).  Valid only for the kernel
 # sources they were taken on: the file records their hash.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llada8b_32k_32layer_sparse_attn_traffic.json")
-KERNEL_SOURCES = ("diffusion_long_context_amd/csrc/attn_mha.hip", "diffusion_long_context_amd/csrc/fdl_device.h")
+KERNEL_SOURCES = ("diffusion_long_context_amd/csrc/attn_mha.hip", "diffusion_long_context_amd/csrc/fdl_device.h",
+                  "diffusion_long_context_amd/csrc/fdl_score.h", "diffusion_long_context_amd/csrc/fdl_select.h",
+                  "diffusion_long_context_amd/csrc/fdl_stream.h")
 
 
 def measured_traffic():
@@ -398,7 +400,7 @@ def other_workloads(h, dev, steps: int = 10, chunk_runs: int = 20) -> dict:
 
 PHASES = ("start", "query sum", "own scores", "score exchange", "scores read back", "selection",
           "first tile landed", "wave 0 tiles done", "all tiles done", "merge ticket", "merge done",
-          "extra 11", "extra 12", "extra 13", "extra 14")
+          "merge statistics shared", "merge sums done", "selection entered", "selection ranked")
 
 
 def phase_timeline(samples: int = 24) -> dict:
@@ -482,6 +484,133 @@ def phase_timeline(samples: int = 24) -> dict:
     return res
 
 
+# ---- rocprofv3 output -> the short text summaries kept with the measurements -------------------
+
+def _rocprof_rows(d: str, suffix: str) -> list:
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _short(name: str, n: int = 90) -> str:
+    return name if len(name) <= n else name[: n - 3] + "..."
+
+
+def summarize_trace(d: str, title: str, command: str) -> str:
+    """Markdown table of a `rocprofv3 --kernel-trace --stats` run (its *kernel_stats.csv), durations in
+    microseconds, plus each kernel's grid from the trace (*kernel_trace.csv) when present."""
+    stats = _rocprof_rows(d, "kernel_stats.csv")
+    out = [f"# Kernel trace: {title}", "", "Command (from the repository root on the GPU host; "
+           "`cd /tmp && export TMPDIR=/tmp` first, paths absolute):", "", f"    {command}", "",
+           "rocprofv3 kernel statistics of the run (microseconds; the 24 kernels with the most time).", "",
+           "| kernel | calls | total us | avg us | min us | max us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:24]:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                   f"{float(r['AverageNs']) / 1e3:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
+                   f"{float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f} |")
+    try:
+        trace = _rocprof_rows(d, "kernel_trace.csv")
+    except SystemExit:
+        trace = []
+    if trace:
+        # per (kernel, launch grid): kernels that serve several workloads are told apart by their grid
+        def grid(r):
+            xyz = [r.get(f"Grid_Size_{a}") or "" for a in "XYZ"]
+            wg = [r.get(f"Workgroup_Size_{a}") or "" for a in "XYZ"]
+            return f"({', '.join(xyz)}) / ({', '.join(wg)})" if xyz[0] else (r.get("Grid_Size") or "?")
+        groups = {}
+        for r in (r for r in trace if "fdl::" in r["Kernel_Name"]):
+            t = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3
+            groups.setdefault((r["Kernel_Name"], grid(r)), []).append(t)
+        out += ["", "This library's kernels per launch grid (grid size in threads / workgroup size), from the trace:", "",
+                "| kernel | grid | dispatches | avg us | min us | max us |", "|---|---|---:|---:|---:|---:|"]
+        for (k, gsz), ts in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"| `{_short(k)}` | {gsz} | {len(ts)} | {sum(ts) / len(ts):.3f} | {min(ts):.3f} | "
+                       f"{max(ts):.3f} |")
+    return "\n".join(out) + "\n"
+
+
+def _counter_means(d: str) -> dict:
+    """{kernel name: {counter: mean value per dispatch, "dispatches": n}} of a --pmc run."""
+    per = {}
+    for r in _rocprof_rows(d, "counter_collection.csv"):
+        k = r["Kernel_Name"]
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Counter_Name"])
+        per.setdefault(k, {}).setdefault(key, 0.0)
+        per[k][key] += float(r["Counter_Value"])
+    res = {}
+    for k, vals in per.items():
+        byc = {}
+        for (disp, cname), v in vals.items():
+            byc.setdefault(cname, {})[disp] = v
+        res[k] = {c: sum(v.values()) / len(v) for c, v in byc.items()}
+        res[k]["dispatches"] = max(len(v) for v in byc.values())
+    return res
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, commands: list, mfma_dir: str = None,
+                       traffic_json: str = None) -> str:
+    """HBM bytes per dispatch from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled
+    by what the counter reads for the elementwise copy of copy_mib MiB that the runs end with; with
+    mfma_dir, the MFMA counters of a third run.  Writes the fused kernel's figure and the hash of its
+    sources to traffic_json."""
+    fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
+    copy = [k for k in fetch if "neg" in k]
+    assert copy, "the copy calibration kernel (torch.neg) is missing: run with --copy-calib-mib"
+    n_kib = copy_mib * 1024.0
+    fscale = n_kib / fetch[copy[0]]["FETCH_SIZE"]
+    wscale = n_kib / write[copy[0]]["WRITE_SIZE"]
+    out = ["# HBM traffic per dispatch: 32K-context 32-layer focus step (llada8b_32k_32layer)", "",
+           "Commands (one counter per run):", ""] + [f"    {c}" for c in commands] + [
+           "", f"Calibration: one elementwise copy (`torch.neg`) of {copy_mib} MiB read and written by the same "
+           f"runs: FETCH_SIZE {fetch[copy[0]]['FETCH_SIZE']:.1f} KiB, WRITE_SIZE {write[copy[0]]['WRITE_SIZE']:.1f} "
+           f"KiB -> scale factors fetch x{fscale:.4f}, write x{wscale:.4f}.", "",
+           "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |",
+           "|---|---:|---:|---:|---:|"]
+    rows = []
+    for k in fetch:
+        if k not in write:
+            continue
+        f, w = fetch[k]["FETCH_SIZE"], write[k]["WRITE_SIZE"]
+        rows.append((f * fscale + w * wscale, k, fetch[k]["dispatches"], f, w))
+    for hbm, k, n, f, w in sorted(rows, reverse=True):
+        out.append(f"| `{_short(k)}` | {n} | {f:.1f} | {w:.1f} | {hbm * 1024:.4g} |")
+    fused = [r for r in rows if "attn_mha_kernel<128, false, false, true, false, false>" in r[1]]
+    if fused and traffic_json:
+        hbm, k, n, f, w = fused[0]
+        h = hashlib.sha256()
+        for rel in KERNEL_SOURCES:
+            with open(os.path.join(ROOT, rel), "rb") as fh:
+                h.update(fh.read())
+        with open(traffic_json, "w") as fh:
+            json.dump({"kernel": "attn_mha_kernel<128,false,false,true,false>", "fetch_kib_per_dispatch": f,
+                       "write_kib_per_dispatch": w, "fetch_scale": fscale, "write_scale": wscale,
+                       "hbm_bytes_per_dispatch": hbm * 1024, "source_sha256": h.hexdigest(),
+                       "commands": commands}, fh, indent=1)
+    if mfma_dir:
+        m = _counter_means(mfma_dir)
+        out += ["", "MFMA counters (third run, same command with `--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE`): per dispatch, summed over the "
+                "chip. bf16 MFMA flops = MOPS x 512; utilisation = busy cycles / (GPU-active cycles of one XCD "
+                "x 1024 SIMDs), with GRBM_GUI_ACTIVE summed over the 8 XCDs.", "",
+                "| kernel | dispatches | bf16 MFMA GFLOP | MFMA busy cycles | GRBM_GUI_ACTIVE | MFMA util |",
+                "|---|---:|---:|---:|---:|---:|"]
+        for k, v in sorted(m.items(), key=lambda kv: -kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)):
+            busy, act = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), v.get("GRBM_GUI_ACTIVE", 0.0)
+            if busy <= 0:
+                continue
+            util = busy / (act / 8.0 * 1024.0) if act > 0 else float("nan")
+            out.append(f"| `{_short(k)}` | {v['dispatches']} | {v.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0.0) * 512 / 1e9:.3f} "
+                       f"| {busy:.4g} | {act:.4g} | {100 * util:.2f} % |")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -496,7 +625,28 @@ def main():
                     help="print the fused kernel's phase timeline (needs the --phase-stamps library) and exit")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, one plain elementwise copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="markdown summary of a rocprofv3 --stats run; exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="markdown summary of a FETCH_SIZE and a WRITE_SIZE rocprofv3 run; exit")
+    ap.add_argument("--mfma-dir", help="with --summarize-counters: the MFMA counter run")
+    ap.add_argument("--traffic-json", help="with --summarize-counters: write the fused kernel's traffic file")
+    ap.add_argument("--title", default="", help="with --summarize-trace: the title")
+    ap.add_argument("--command", action="append", default=[], help="the profiled command(s), for the summary")
+    ap.add_argument("--summary-out", help="write the summary here instead of stdout")
     args = ap.parse_args()
+
+    if args.summarize_trace or args.summarize_counters:
+        if args.summarize_trace:
+            text = summarize_trace(args.summarize_trace, args.title, " ".join(args.command))
+        else:
+            text = summarize_counters(*args.summarize_counters, args.copy_calib_mib or 1024, args.command,
+                                      args.mfma_dir, args.traffic_json)
+        if args.summary_out:
+            with open(args.summary_out, "w") as f:
+                f.write(text)
+        else:
+            print(text)
+        return
 
     if args.cpu_baseline_child:
         print(json.dumps(cpu_baseline_child()))
