@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-attn step us + KV tokens/s at 32K ctx; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA (no sparsity)
 WORKSPACE_BYTES = 256 << 20   # library workspace of the timed handle (sets the attention split count)
 
 
@@ -42,7 +43,8 @@ KERNEL_SOURCES = ("diffusion_long_context_amd/csrc/attn_mha.hip", "diffusion_lon
                   "diffusion_long_context_amd/csrc/fdl_stream.h")
 
 
-def measured_traffic():
+def measured_counters():
+    """The counter figures of the fused kernel, if they were taken on the current sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             d = json.load(f)
@@ -52,7 +54,23 @@ def measured_traffic():
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    return d["hbm_bytes_per_dispatch"] if h.hexdigest() == d.get("source_sha256") else None
+    return d if h.hexdigest() == d.get("source_sha256") else None
+
+
+def mfma_figures(launch_us: float):
+    """bf16 MFMA work of the fused kernel from the counter run (per dispatch), its rate at this run's
+    launch time against the dense bf16 peak, and the fraction of SIMD cycles the MFMA unit was busy."""
+    d = measured_counters()
+    if not d or "mfma_bf16_flop_per_dispatch" not in d:
+        return None
+    tf = d["mfma_bf16_flop_per_dispatch"] / (launch_us * 1e-6) / 1e12
+    return {"bf16_flop_per_launch": d["mfma_bf16_flop_per_dispatch"], "achieved_tflops": tf,
+            "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS, "busy_frac": d["mfma_busy_frac"]}
+
+
+def measured_traffic():
+    d = measured_counters()
+    return d["hbm_bytes_per_dispatch"] if d else None
 
 
 def log(msg: str):
@@ -581,20 +599,26 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, commands: 
         rows.append((f * fscale + w * wscale, k, fetch[k]["dispatches"], f, w))
     for hbm, k, n, f, w in sorted(rows, reverse=True):
         out.append(f"| `{_short(k)}` | {n} | {f:.1f} | {w:.1f} | {hbm * 1024:.4g} |")
-    fused = [r for r in rows if "attn_mha_kernel<128, false, false, true, false, false>" in r[1]]
+    fused_name = "attn_mha_kernel<128, false, false, true, false, false>"
+    fused = [r for r in rows if fused_name in r[1]]
+    m = _counter_means(mfma_dir) if mfma_dir else {}
     if fused and traffic_json:
         hbm, k, n, f, w = fused[0]
         h = hashlib.sha256()
         for rel in KERNEL_SOURCES:
             with open(os.path.join(ROOT, rel), "rb") as fh:
                 h.update(fh.read())
+        d = {"kernel": "attn_mha_kernel<128,false,false,true,false>", "fetch_kib_per_dispatch": f,
+             "write_kib_per_dispatch": w, "fetch_scale": fscale, "write_scale": wscale,
+             "hbm_bytes_per_dispatch": hbm * 1024, "source_sha256": h.hexdigest(), "commands": commands}
+        mk = [v for kk, v in m.items() if fused_name in kk]
+        if mk:
+            v = mk[0]
+            d["mfma_bf16_flop_per_dispatch"] = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+            d["mfma_busy_frac"] = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0)
         with open(traffic_json, "w") as fh:
-            json.dump({"kernel": "attn_mha_kernel<128,false,false,true,false>", "fetch_kib_per_dispatch": f,
-                       "write_kib_per_dispatch": w, "fetch_scale": fscale, "write_scale": wscale,
-                       "hbm_bytes_per_dispatch": hbm * 1024, "source_sha256": h.hexdigest(),
-                       "commands": commands}, fh, indent=1)
+            json.dump(d, fh, indent=1)
     if mfma_dir:
-        m = _counter_means(mfma_dir)
         out += ["", "MFMA counters (third run, same command with `--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                 "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE`): per dispatch, summed over the "
                 "chip. bf16 MFMA flops = MOPS x 512; utilisation = busy cycles / (GPU-active cycles of one XCD "
@@ -822,7 +846,8 @@ def main():
                      "kernel": "attn_mha_kernel<128,false,false,true,false> (block scoring + selection + sparse attention)",
                      "avg_launch_us": sparse_us, "launches": prof_main["reuse_run"][1],
                      "bytes_per_launch": launch_bytes, "units_per_launch": units,
-                     "unit_bytes": unit_bytes, "frac_of_stream_ref": achieved / best_ref},
+                     "unit_bytes": unit_bytes, "frac_of_stream_ref": achieved / best_ref,
+                     "mfma": mfma_figures(sparse_us)},
         "step_roofline": {"bytes": sb["step"], "GBps": sb["step"] / (ms_per_step * 1e-3) / 1e9,
                           "frac": sb["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
                           "frac_of_stream_ref": sb["step"] / (ms_per_step * 1e-3) / 1e9 / best_ref,
