@@ -421,6 +421,10 @@ PHASES = ("start", "query sum", "own scores", "score exchange", "scores read bac
           "merge statistics shared", "merge sums done", "selection entered", "selection ranked")
 
 
+SINK_PHASES = ("start", "first tile landed (wave 0)", "wave 0 scan done", "all waves done, candidates appended",
+               "merge ticket", "log-sum-exp merged", "candidates re-scored")
+
+
 def phase_timeline(samples: int = 24) -> dict:
     """Phase timeline of the fused score-select-attend kernel on the benchmark's reuse layers, from the
     diagnostic library built with --phase-stamps: the 32-layer step is run `samples` times (distinct
@@ -462,9 +466,12 @@ def phase_timeline(samples: int = 24) -> dict:
                               cfg.sink_tau)
     modes = [FDL_LAYER_DENSE if l < cfg.dense_layers else (FDL_LAYER_SOURCE if l == cfg.source_layer else FDL_LAYER_REUSE)
              for l in range(NL)]
-    stamps = torch.zeros(4096 * 16, dtype=torch.int64, device=dev)
+    # lower half: the fused kernel's stamps (its last launch of the step); upper half: the sink scan's
+    # (the source layer's detection)
+    W = 4096 * 16
+    stamps = torch.zeros(2 * W, dtype=torch.int64, device=dev)
     h.fdl_set_phase_buffer(stamps)
-    rel = []
+    rel, srel = [], []
     for i in range(samples + 2):
         st = schedule_state(cfg, 33 + i)
         conf = torch.from_numpy(st["prev_conf"]).to(dev) if st["prev_conf"] is not None else None
@@ -476,11 +483,15 @@ def phase_timeline(samples: int = 24) -> dict:
         torch.cuda.synchronize()
         if i < 2:
             continue   # warm
-        a = stamps.view(-1, 16).cpu().numpy()
+        a = stamps[:W].view(-1, 16).cpu().numpy()
         live = a[:, 15] < 0   # bit 63 set: a workgroup of this launch
         a = a[live].astype(np.float64)
         t0 = a[:, 0].min()
-        rel.append({"wg": a[:, :15] - t0, "xcc": (stamps.view(-1, 16)[:, 15].cpu().numpy()[live] & 0xFFFFFFFF)})
+        rel.append({"wg": a[:, :15] - t0, "xcc": (stamps[:W].view(-1, 16)[:, 15].cpu().numpy()[live] & 0xFFFFFFFF)})
+        b_ = stamps[W:].view(-1, 16).cpu().numpy()
+        b_ = b_[b_[:, 15] < 0]
+        if b_.shape[0]:
+            srel.append((b_[:, :7].astype(np.float64), b_[:, 7]))
     assert h.fdl_get_status() == 0
     h.fdl_set_phase_buffer(None)
     h.close()
@@ -499,6 +510,22 @@ def phase_timeline(samples: int = 24) -> dict:
     x = rel[-1]["xcc"]
     res["xcc_reg_values"] = sorted(set(int(v) for v in x))
     res["xcc_reg_first16"] = [int(v) for v in x[:16]]
+    if srel:
+        # the sink scan: median over workgroups and the last one, per point (points 5 and 6 only in
+        # the last split of each head), and the candidates per head
+        sk = {"workgroups": int(srel[0][0].shape[0]), "phases_us": {}, "last_workgroup_us": {}}
+        for j, name in enumerate(SINK_PHASES):
+            med, last = [], []
+            for a, _ in srel:
+                t0 = a[:, 0].min()
+                col = a[:, j][a[:, j] > 0] - t0
+                if col.size:
+                    med.append(np.median(col) / 100.0)
+                    last.append(col.max() / 100.0)
+            sk["phases_us"][name] = float(np.mean(med)) if med else None
+            sk["last_workgroup_us"][name] = float(np.mean(last)) if last else None
+        sk["candidates_per_head"] = float(np.mean([c[a[:, 6] > 0].mean() for a, c in srel]))
+        res["sink_scan"] = sk
     return res
 
 

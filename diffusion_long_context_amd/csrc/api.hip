@@ -167,7 +167,10 @@ fdl_status run_sinks(fdl_handle h, const Geom& g, const void* q, const uint64_t*
   ProfScope ps(h, FDL_PROF_SINKS);
   return hip_status(h, fdl::launch_sinks(h->stream, g, q, pred_mask, k_cache, k_dec, tau, max_sinks,
                                          sink_pos, n_sinks, h->scratch, ns, cap, h->status,
-                                         h->num_cus, h->tickets, h->sink_area),
+                                         h->num_cus, h->tickets, h->sink_area,
+                                         // the upper half of the phase buffer (the fused kernel uses the lower)
+                                         h->stamps ? h->stamps + h->stamp_words / 2 : nullptr,
+                                         h->stamp_words / 2),
                     "sinks launch");
 }
 

@@ -145,7 +145,8 @@ hipError_t launch_sinks(hipStream_t s, const Geom& g, const void* q, const uint6
                         const void* k, const void* k_dec, float tau, int max_sinks,
                         int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
                         int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
-                        char* sink_area);
+                        char* sink_area,
+                        uint64_t* stamps = nullptr, int64_t stamp_words = 0);
 
 // Level 2 in one kernel (tokens.hip): launch_score_tokens + launch_select with force_first, same
 // outputs.  score_select_tokens_ok: the shapes it takes (bf16, dec_len <= 32, units of 256 to 4096

@@ -21,6 +21,20 @@
 
 namespace fdl {
 
+// Diagnostic build (FDL_PHASE_STAMPS): thread 0 of each workgroup records s_memrealtime (100 MHz) at
+// the points of the scan; nothing in the normal build.
+#ifdef FDL_PHASE_STAMPS
+#define SINK_STAMP(p, i)                                                                               \
+  do {                                                                                                 \
+    if (threadIdx.x == 0 && (p).stamps != nullptr)                                                     \
+      (p).stamps[(int64_t)blockIdx.x * 16 + (i)] = __builtin_amdgcn_s_memrealtime();                   \
+  } while (0)
+#else
+#define SINK_STAMP(p, i) \
+  do {                   \
+  } while (0)
+#endif
+
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = v;
@@ -71,6 +85,7 @@ struct SinkParams {
   uint32_t* tickets;     // per (b, q-head), kSyncStride apart; left at zero
   uint32_t* status;
   const int32_t* lens;   // per-sequence cached lengths of a ragged batch, or NULL (all L)
+  uint64_t* stamps;      // diagnostic build: per-workgroup phase timestamps, or NULL
   int Hq, Hkv, G, T, L, n_splits, n_segs, cand_cap, words;
   float scale_log2, tau;
 };
@@ -108,6 +123,11 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   const int s = xslot % NS;
   const int k_slot = xcd + 8 * (xslot / NS);
   if (k_slot >= p.n_segs) return;
+  SINK_STAMP(p, 0);
+#ifdef FDL_PHASE_STAMPS
+  if (threadIdx.x == 0 && p.stamps != nullptr)
+    p.stamps[(int64_t)blockIdx.x * 16 + 15] = (uint64_t)xcc_reg() | ((uint64_t)1 << 63);
+#endif
   const int n_kv = p.n_segs / p.G;   // (sequence, KV head) segments
   const int kvs = k_slot % n_kv, jh = k_slot / n_kv;
   const int b = kvs / p.Hkv, g = kvs % p.Hkv, h = g * p.G + jh;
@@ -241,6 +261,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     if (e < e1) issue(e);
     for (; e < e1; e += kSinkWaves) {
       wait_vm0();   // this tile's fetches have landed
+      if (e == e0) SINK_STAMP(p, 1);
       // lane (token ql of block rb, half hh): dims hh*D/2 + 8 ks .. +8, as the MFMA A operand
       uint4 ka[RB][KS];
 #pragma unroll
@@ -313,6 +334,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
       prev_nvalid = nvalid;
     }
     if (prev_e > 0) eval_tile(sprev, prev_e, prev_nvalid);   // the last tile, under the final stats
+    SINK_STAMP(p, 2);
   }
   if (hh == 0) p.stats[((int64_t)seg * n_parts + s * kSinkWaves + wave) * 32 + ql] = make_float2(m_run, l_run);
   // append the workgroup's candidates to the head's list (one global atomic reserves the range)
@@ -346,12 +368,14 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   if (NS > 1) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    SINK_STAMP(p, 3);
     if (tid == 0) {
       bool here = true;
       s_ticket = take_ticket(p.tickets + seg * kSyncStride, NS, &here);
       s_here = here ? 1u : 0u;
     }
     __syncthreads();
+    SINK_STAMP(p, 4);
     if (s_ticket != (uint32_t)(NS - 1)) return;
     if (tid == 0) reset_ticket(p.tickets + seg * kSyncStride);
     if (s_here == 0u) {   // uniform
@@ -404,6 +428,7 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
       s_lse[tid] = M2 + __log2f(S2);
     }
     __syncthreads();
+    SINK_STAMP(p, 5);
   }
   // re-score this head's candidates exactly: one wave per candidate, lane = predicted position
   int count = (int)__hip_atomic_load(&p.cand_count[seg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -435,6 +460,11 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     if (lane == 0 && e / (float)n_pred >= p.tau)
       atomicOr(&p.bitmap[(int64_t)b * p.words + (t >> 5)], 1u << (t & 31));
   }
+#ifdef FDL_PHASE_STAMPS
+  __syncthreads();
+  SINK_STAMP(p, 6);
+  if (threadIdx.x == 0 && p.stamps != nullptr) p.stamps[(int64_t)blockIdx.x * 16 + 7] = (uint64_t)count;
+#endif
 }
 
 // float32 path (small workloads): thread = query row; two passes over the keys.
@@ -601,7 +631,7 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
                         const void* k, const void* k_dec, float tau, int max_sinks,
                         int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
                         int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
-                        char* sink_area) {
+                        char* sink_area, uint64_t* stamps, int64_t stamp_words) {
   (void)num_cus;
   const int words = (g.L + 31) / 32;
   char* cur = scratch;
@@ -630,6 +660,7 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
   p.T = g.T;
   p.L = g.L;
   p.lens = g.lens;
+  p.stamps = nullptr;
   p.n_splits = n_splits;
   p.n_segs = g.B * g.Hq;
   p.cand_cap = cand_cap;
@@ -655,6 +686,7 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
   } else if (g.L > 0) {
     // the splits of slot k run on XCD k % 8 (see the kernel)
     dim3 grid(8 * ((p.n_segs + 7) / 8) * n_splits);
+    if (stamps != nullptr && stamp_words >= (int64_t)grid.x * 16) p.stamps = stamps;
     if (g.D == 128) {
       if (g.G > 1) hipLaunchKernelGGL((sink_scan_kernel<128, true>), grid, dim3(kSinkWaves * 64), 0, st, p);
       else hipLaunchKernelGGL((sink_scan_kernel<128, false>), grid, dim3(kSinkWaves * 64), 0, st, p);
