@@ -110,8 +110,33 @@ def cpu_baseline_child() -> dict:
     t["dense"] = time.perf_counter() - t0
     step = (cfg.dense_layers * t["dense"] + t["source"]
             + (cfg.n_layers - cfg.dense_layers - 1) * t["reuse"] + cfg.n_layers * t["pool"] / cfg.steps_per_block)
+    # the oracle's layer-step time on the other workloads: the tiny, 8K and 16K grouped-query layers
+    # in full (a source layer then a reuse layer, keys pooled inside), the chunked one on a sample of
+    # one sequence and 8 of its 32 heads, scaled by the 16 times more (sequence, head) pairs of the
+    # workload (every part of that step is per (sequence, head))
+    from oracle.pipeline import chunked_layer_step
+    from synth.gen import make_single
+    others = {}
+    for ci in (0, 1, 2):
+        c = get_config(ci)
+        xo = make_single(c)
+        t0 = time.perf_counter()
+        r = focus_layer_step(c, xo, "source")
+        ts = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        focus_layer_step(c, xo, "reuse", sinks=(r["sink_pos"], r["n_sinks"]))
+        others[c.name] = {"source_layer_s": ts, "reuse_layer_s": time.perf_counter() - t0}
+    c4 = get_config(4)
+    cs = c4.with_(batch=1, n_q_heads=8, n_kv_heads=8)
+    xo = make_single(cs)
+    t0 = time.perf_counter()
+    chunked_layer_step(cs, xo)
+    tc = time.perf_counter() - t0
+    scale = (c4.batch * c4.n_kv_heads) / (cs.batch * cs.n_kv_heads)
+    others[c4.name] = {"layer_step_s": tc * scale, "sample": "batch 1, 8 heads, scaled x16",
+                       "sample_s": tc}
     return {"layer_seconds": t, "step_seconds_extrapolated": step,
-            "kv_tokens_per_s": cfg.ctx_len * cfg.n_layers / step}
+            "kv_tokens_per_s": cfg.ctx_len * cfg.n_layers / step, "other_workloads": others}
 
 
 def cpu_baseline() -> dict | None:
@@ -135,6 +160,7 @@ def cpu_baseline() -> dict | None:
                    f"(measured s: dense {lt['dense']:.2f}, source {lt['source']:.2f}, reuse "
                    f"{lt['reuse']:.2f}, pool {lt['pool']:.2f})"),
         "step_ms_extrapolated": 1e3 * d["step_seconds_extrapolated"],
+        "other_workloads": d.get("other_workloads"),
     }
 
 
