@@ -67,6 +67,8 @@ CASES = {
     "16k-gqa7": (2, dict(batch=3, n_q_heads=14, n_kv_heads=2), [16384, 9001, 2100]),
     # float32 path
     "tiny-f32": (0, dict(batch=3), [512, 300, 45]),
+    # a sequence with no cached token at all (its own block only) between two others
+    "8k-empty": (1, dict(batch=3, n_q_heads=8, n_kv_heads=8), [8192, 0, 1000]),
 }
 
 
@@ -94,7 +96,7 @@ def test_ragged_standalone_calls(case):
         _check_seq(cfg, got["reuse"], reu, b, lb, f"{case} b={b} reuse")
 
 
-@pytest.mark.parametrize("case", ["8k-mha", "16k-gqa7"])
+@pytest.mark.parametrize("case", ["8k-mha", "16k-gqa7", "8k-empty"])
 def test_ragged_focus_step(case):
     """fdl_focus_step over dense, source and reuse layers: each sequence against the oracle's
     layer-by-layer run of that sequence alone."""
