@@ -647,7 +647,8 @@ fdl_status fdl_select_chunks_tokens(fdl_handle h, const fdl_geom* gp, const void
   ProfScope ps(h, FDL_PROF_SCORE);
   return hip_status(h, fdl::launch_select_chunks_tokens(h->stream, g, q, pred_mask, chunk_sums, k_cache, page_table,
                                                         lg, top_k_chunks, top_k, max_sel, chunk_scores, chunks,
-                                                        n_chunks_sel, token_scores, sel_idx, n_sel, h->status),
+                                                        n_chunks_sel, token_scores, sel_idx, n_sel, h->status,
+                                                        h->stamps, h->stamp_words),
                     "select_chunks_tokens launch");
 }
 

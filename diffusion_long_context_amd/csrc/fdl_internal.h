@@ -164,7 +164,8 @@ hipError_t launch_select_chunks_tokens(hipStream_t s, const Geom& g, const void*
                                        const float* chunk_sums, const void* k, const int32_t* page_table,
                                        int unit_log2, int top_k_chunks, int top_k, int max_sel, float* chunk_scores,
                                        int32_t* chunks, int32_t* n_chunks_sel, float* scores, int32_t* sel_idx,
-                                       int32_t* n_sel, uint32_t* status);
+                                       int32_t* n_sel, uint32_t* status, uint64_t* stamps = nullptr,
+                                       int64_t stamp_words = 0);
 
 hipError_t launch_select(hipStream_t s, const Geom& g, const float* scores, int n_units,
                          int unit_log2, const int32_t* sink_pos, const int32_t* n_sinks,

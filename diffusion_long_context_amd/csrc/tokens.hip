@@ -42,7 +42,23 @@ struct ChunkChoice {
   int32_t* chunks;
   int32_t* n_chunks_sel;
   int n_chunks;
+  uint64_t* stamps;   // diagnostic build: per-workgroup phase timestamps, or NULL
 };
+
+// Diagnostic build (FDL_PHASE_STAMPS): thread 0 of each workgroup records s_memrealtime (100 MHz);
+// nothing in the normal build.
+#ifdef FDL_PHASE_STAMPS
+#define TS_STAMP(cc, i)                                                                                \
+  do {                                                                                                 \
+    if (threadIdx.x == 0 && (cc).stamps != nullptr)                                                    \
+      (cc).stamps[(((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 16 + (i)] = \
+          __builtin_amdgcn_s_memrealtime() | ((uint64_t)1 << 63);                                      \
+  } while (0)
+#else
+#define TS_STAMP(cc, i) \
+  do {                  \
+  } while (0)
+#endif
 
 template <int D, bool PAGED, bool CHOOSE>
 __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
@@ -70,13 +86,18 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
   const int n = 1 << unit_log2;
   const int n_units = rows.L >> unit_log2;   // ctx_len is a multiple of the unit
   const int64_t seg = (int64_t)b * rows.Hkv + g;
+  TS_STAMP(cc, 0);
   __shared__ uint32_t s_ck[CHOOSE ? kTsMaxChunks : 1];   // level 1: the chunks' order keys
   __shared__ int s_u;
 
   // loads in the order they are needed: the group's query rows (with CHOOSE, then the chunk sums'
   // rows), the chunk's page entries, the first batch of K rows
+  // one query head per KV head: its 32 rows alone (the grouped loader would fetch them once per
+  // possible head); the same tree, so the same bits
   QsumGrouped<D, 32, NT, 8> qst;
-  qsum_grouped_issue<D, 32, NT, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
+  QsumG1<D, 32, NT> qs1;
+  if (G == 1) qsum_g1_issue<D, 32, NT>(q + (seg * T) * D, T, qs1);   // uniform
+  else qsum_grouped_issue<D, 32, NT, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
   constexpr int CP = CHOOSE ? kTsMaxChunks / RPP : 1;   // level-1 row passes
   float xc[CP][16];
   if constexpr (CHOOSE) {
@@ -89,6 +110,16 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
   }
   int u = 0;
   if constexpr (!CHOOSE) u = cand_idx[seg * n_cand + c];
+  // with CHOOSE, the sequence's page entries (up to two per thread) are read now, so that the chosen
+  // chunk's are at hand without a round trip after level 1
+  constexpr int kPrePages = 2 * NT;
+  const bool pre_pages = CHOOSE && PAGED && rows.pages_per_seq <= kPrePages;   // uniform
+  int pp0 = 0, pp1 = 0;
+  if (pre_pages) {
+    const int32_t* ptb = rows.page_table + (int64_t)b * rows.pages_per_seq;
+    pp0 = ptb[tid < rows.pages_per_seq ? tid : 0];
+    pp1 = ptb[tid + NT < rows.pages_per_seq ? tid + NT : 0];
+  }
   // with CHOOSE the chunk is known after level 1; its page entries are read then
   auto page_loads = [&](int tok0_, int& pg0_, int& n_pg_, int& my_page_) {
     pg0_ = PAGED ? tok0_ >> rows.page_log2 : 0;
@@ -119,9 +150,11 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
 
   for (int i = tid; i < kTsMaxUnit / 32; i += NT) forced[i] = (i == 0) ? 1u : 0u;   // the anchor
   if (!CHOOSE && PAGED && tid < n_pg) s_pages[tid] = my_page;
-  qsum_grouped_finish<D, 32, NT, 8>(qst, pred_mask[b], G, T, big, qs);   // barriers inside
+  if (G == 1) qsum_g1_finish<D, 32, NT>(qs1, pred_mask[b], T, reinterpret_cast<float*>(big), qs);
+  else qsum_grouped_finish<D, 32, NT, 8>(qst, pred_mask[b], G, T, big, qs);   // barriers inside
   __syncthreads();   // qs, the page entries and the forced bits; the stage is free again
 
+  TS_STAMP(cc, 1);
   float qv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) qv[i] = qs[16 * j + i];
@@ -158,10 +191,20 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
     u = __builtin_amdgcn_readfirstlane(s_u);
     uok = (unsigned)u < (unsigned)n_units;
     tok0 = uok ? u << unit_log2 : 0;
-    page_loads(tok0, pg0, n_pg, my_page);
-    if (PAGED && tid < n_pg) s_pages[tid] = my_page;
+    if (pre_pages) {
+      pg0 = tok0 >> rows.page_log2;
+      n_pg = ((tok0 + n - 1) >> rows.page_log2) - pg0 + 1;
+      if (tid >= pg0 && tid < pg0 + n_pg) s_pages[tid - pg0] = pp0;
+      if (tid + NT >= pg0 && tid + NT < pg0 + n_pg) s_pages[tid + NT - pg0] = pp1;
+      my_page = 0;   // the range check of the entries reads them back from LDS below
+    } else {
+      page_loads(tok0, pg0, n_pg, my_page);
+      if (PAGED && tid < n_pg) s_pages[tid] = my_page;
+    }
     if (PAGED) block_sync_lds();   // the page entries, for every row
+    if (pre_pages && tid < n_pg) my_page = s_pages[tid];
   }
+  TS_STAMP(cc, 2);
   bool bad = !uok;
   uint32_t* keys = reinterpret_cast<uint32_t*>(big);
   float* sc_out = scores + (seg * n_cand + c) * (int64_t)n;
@@ -203,9 +246,12 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
     }
   };
   issue(0, ka, oka);
+  bool first = true;
   for (int bt = 0; bt < nb; bt += 2) {
     issue(bt + 1 < nb ? bt + 1 : nb - 1, kb, okb);
     consume(bt, ka, oka);
+    if (first) TS_STAMP(cc, 3);
+    first = false;
     issue(bt + 2 < nb ? bt + 2 : nb - 1, ka, oka);
     if (bt + 1 < nb) consume(bt + 1, kb, okb);   // uniform; no load inside
   }
@@ -216,6 +262,7 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
   }
   latch_bad(status, bad);
   block_sync_lds();   // every key
+  TS_STAMP(cc, 4);
 
   const int nf = 1;   // the anchor
   const int per_seg = nf + (top_k < n - nf ? top_k : n - nf);
@@ -225,6 +272,7 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
     out[pos] = uok ? tok0 + i : -1;
   });
   if (tid == 0 && c == 0) n_sel[seg] = n_cand * (nf + r.kk);
+  TS_STAMP(cc, 5);
 }
 
 template <int D, bool PAGED, bool CHOOSE>
@@ -281,18 +329,19 @@ hipError_t launch_score_select_tokens(hipStream_t s, const Geom& g, const void* 
                                       float* scores, int32_t* sel_idx, int32_t* n_sel, uint32_t* status) {
   if (!score_select_tokens_ok(g, unit_log2)) return hipErrorInvalidValue;
   return dispatch_sst<false>(s, g, q, pred_mask, k, page_table, unit_log2, cand_idx, n_cand, top_k, max_sel, scores,
-                             sel_idx, n_sel, status, ChunkChoice{nullptr, nullptr, nullptr, nullptr, 0});
+                             sel_idx, n_sel, status, ChunkChoice{nullptr, nullptr, nullptr, nullptr, 0, nullptr});
 }
 
 hipError_t launch_select_chunks_tokens(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                                        const float* chunk_sums, const void* k, const int32_t* page_table,
                                        int unit_log2, int top_k_chunks, int top_k, int max_sel, float* chunk_scores,
                                        int32_t* chunks, int32_t* n_chunks_sel, float* scores, int32_t* sel_idx,
-                                       int32_t* n_sel, uint32_t* status) {
+                                       int32_t* n_sel, uint32_t* status, uint64_t* stamps, int64_t stamp_words) {
   const int n_chunks = g.L >> unit_log2;
   if (!select_chunks_tokens_ok(g, unit_log2, n_chunks) || top_k_chunks < 1 || top_k_chunks > n_chunks)
     return hipErrorInvalidValue;
-  const ChunkChoice cc{chunk_sums, chunk_scores, chunks, n_chunks_sel, n_chunks};
+  const bool st_ok = stamps != nullptr && stamp_words >= (int64_t)top_k_chunks * g.Hkv * g.B * 16;
+  const ChunkChoice cc{chunk_sums, chunk_scores, chunks, n_chunks_sel, n_chunks, st_ok ? stamps : nullptr};
   return dispatch_sst<true>(s, g, q, pred_mask, k, page_table, unit_log2, nullptr, top_k_chunks, top_k, max_sel,
                             scores, sel_idx, n_sel, status, cc);
 }
