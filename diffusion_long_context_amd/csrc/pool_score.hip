@@ -121,6 +121,28 @@ __device__ __forceinline__ float2 leaf_tree(const KT* __restrict__ k, const KvRo
 // n_sub_all are +0).  The tree over a power-of-two unit is the tree over its aligned 64-token
 // sub-trees, so the bits are those of the one-pass tree.  Thread (unit, dimension pair).
 // Units [n0, n0 + n_cnt) of the n_units.
+// The G query heads' rows of KV head g staged as [8][32][D] bf16 (rows past T repeat row T - 1; heads
+// past G are not read): one query head per KV head loads its 32 rows alone.  Every thread calls it;
+// the stage is complete after it.
+template <int D>
+__device__ __forceinline__ void stage_group_queries(const uint16_t* __restrict__ q, int b, int g, int Hq, int G,
+                                                    int T, uint16_t* stage) {
+  if (G == 1) {   // uniform
+    QsumG1<D, 32, 256> qs1;
+    qsum_g1_issue<D, 32, 256>(q + ((int64_t)b * Hq + g) * T * D, T, qs1);
+#pragma unroll
+    for (int k = 0; k < QsumG1<D, 32, 256>::PER; ++k)
+      if (k * 256 + (int)threadIdx.x < 32 * (D / 8)) *reinterpret_cast<uint4*>(stage + (k * 256 + threadIdx.x) * 8) = qs1.v[k];
+  } else {
+    QsumGrouped<D, 32, 256, 8> qst;
+    qsum_grouped_issue<D, 32, 256, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
+#pragma unroll
+    for (int k = 0; k < QsumGrouped<D, 32, 256, 8>::PER; ++k)
+      *reinterpret_cast<uint4*>(stage + (k * 256 + threadIdx.x) * 8) = qst.v[k];
+  }
+  block_sync_lds();
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void pool_merge_kernel(const float* __restrict__ sub, int n_sub, int n_sub_all,
                                                          int n0, int n_cnt, int n_units, int Hkv,
@@ -469,9 +491,15 @@ __global__ __launch_bounds__(256) void score_units_kernel(const QT* __restrict__
   }
   if constexpr (std::is_same<QT, uint16_t>::value && TMAX == 32) {
     __shared__ __attribute__((aligned(16))) uint16_t stage[8 * 32 * D];
-    QsumGrouped<D, 32, 256, 8> qst;
-    qsum_grouped_issue<D, 32, 256, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
-    qsum_grouped_finish<D, 32, 256, 8>(qst, pred_mask[b], G, T, stage, qs);
+    if (G == 1) {   // uniform: one query head per KV head, its 32 rows alone (the same tree and bits)
+      QsumG1<D, 32, 256> qs1;
+      qsum_g1_issue<D, 32, 256>(q + ((int64_t)b * Hq + g) * T * D, T, qs1);
+      qsum_g1_finish<D, 32, 256>(qs1, pred_mask[b], T, reinterpret_cast<float*>(stage), qs);
+    } else {
+      QsumGrouped<D, 32, 256, 8> qst;
+      qsum_grouped_issue<D, 32, 256, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
+      qsum_grouped_finish<D, 32, 256, 8>(qst, pred_mask[b], G, T, stage, qs);
+    }
   } else {
     query_sum_to_lds<QT, D, TMAX>(q, pred_mask[b], b, g, Hq, G, T, qs);
   }
@@ -545,12 +573,7 @@ __global__ __launch_bounds__(256) void score_units_max_kernel(const uint16_t* __
     n = n < n_units ? n : n_units - 1;
     load16<float>(ksg + (int64_t)n * D + 16 * j, x[ps]);
   }
-  QsumGrouped<D, 32, 256, 8> qst;
-  qsum_grouped_issue<D, 32, 256, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
-#pragma unroll
-  for (int k = 0; k < QsumGrouped<D, 32, 256, 8>::PER; ++k)
-    *reinterpret_cast<uint4*>(stage + (k * 256 + threadIdx.x) * 8) = qst.v[k];
-  block_sync_lds();
+  stage_group_queries<D>(q, b, g, Hq, G, T, stage);
   const uint64_t pred = pred_mask[b] & (T >= 64 ? ~0ull : ((1ull << T) - 1ull));
   float best[kPasses];
 #pragma unroll
@@ -630,12 +653,7 @@ __global__ __launch_bounds__(256) void mass_logits_kernel(const uint16_t* __rest
     const int cnt = (L - first) < (1 << unit_log2) ? (L - first) : (1 << unit_log2);
     scale[ps] = 1.f / ((float)cnt * sqrtf((float)D));
   }
-  QsumGrouped<D, 32, 256, 8> qst;
-  qsum_grouped_issue<D, 32, 256, 8>(q + (int64_t)b * Hq * T * D, g * G, G, T, qst);
-#pragma unroll
-  for (int k = 0; k < QsumGrouped<D, 32, 256, 8>::PER; ++k)
-    *reinterpret_cast<uint4*>(stage + (k * 256 + threadIdx.x) * 8) = qst.v[k];
-  block_sync_lds();
+  stage_group_queries<D>(q, b, g, Hq, G, T, stage);
   const uint64_t pred = pred_mask[b] & (T >= 64 ? ~0ull : ((1ull << T) - 1ull));
   float* zg = z + ((int64_t)b * Hkv + g) * (int64_t)G * T * n_units;
   for (int jh = 0; jh < G; ++jh) {
