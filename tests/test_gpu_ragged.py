@@ -69,6 +69,8 @@ CASES = {
     "tiny-f32": (0, dict(batch=3), [512, 300, 45]),
     # a sequence with no cached token at all (its own block only) between two others
     "8k-empty": (1, dict(batch=3, n_q_heads=8, n_kv_heads=8), [8192, 0, 1000]),
+    # the 32K layer's shapes (64 blocks kept per KV head) at 8 heads
+    "32k": (3, dict(batch=2, n_q_heads=8, n_kv_heads=8), [32768, 20000]),
 }
 
 
@@ -96,7 +98,7 @@ def test_ragged_standalone_calls(case):
         _check_seq(cfg, got["reuse"], reu, b, lb, f"{case} b={b} reuse")
 
 
-@pytest.mark.parametrize("case", ["8k-mha", "16k-gqa7", "8k-empty"])
+@pytest.mark.parametrize("case", ["8k-mha", "16k-gqa7", "8k-empty", "32k"])
 def test_ragged_focus_step(case):
     """fdl_focus_step over dense, source and reuse layers: each sequence against the oracle's
     layer-by-layer run of that sequence alone."""
