@@ -120,7 +120,8 @@ __global__ __launch_bounds__(kTsThreads, 2) void score_select_tokens_kernel(
     pp0 = ptb[tid < rows.pages_per_seq ? tid : 0];
     pp1 = ptb[tid + NT < rows.pages_per_seq ? tid + NT : 0];
   }
-  // with CHOOSE the chunk is known after level 1; its page entries are read then
+  // the chunk's page entries (with CHOOSE and a page table too long to read early, once level 1
+  // has chosen the chunk)
   auto page_loads = [&](int tok0_, int& pg0_, int& n_pg_, int& my_page_) {
     pg0_ = PAGED ? tok0_ >> rows.page_log2 : 0;
     n_pg_ = PAGED ? ((tok0_ + n - 1) >> rows.page_log2) - pg0_ + 1 : 0;
