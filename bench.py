@@ -197,9 +197,11 @@ def step_bytes(cfg, units_per_reuse: int) -> dict:
             "step": cfg.dense_layers * dense + source + n_reuse * reuse, "pool_layer": pool}
 
 
-def stream_reference(h, dev, mib: int = 2048, reps: int = 5) -> dict:
+def stream_reference(h, dev, mib: int = 2048, reps: int = 5, blocks=(0, 768, 8192)) -> dict:
     """The rate a plain coalesced stream reaches on this chip (fdl_bandwidth_probe over a buffer far
-    larger than the last-level cache): read into registers, read by LDS DMA, and copy; best of reps."""
+    larger than the last-level cache): read into registers, read by LDS DMA, and copy; best of reps
+    at each grid size in blocks (0 = the probe's default of 4 workgroups per CU), best grid kept.
+    The read rate moves by about 10% with the grid size alone, so one grid would understate it."""
     import torch
 
     from diffusion_long_context_amd.fdllm import FDL_PROBE_COPY, FDL_PROBE_READ, FDL_PROBE_READ_LDS
@@ -210,16 +212,20 @@ def stream_reference(h, dev, mib: int = 2048, reps: int = 5) -> dict:
     res = {"bytes": n}
     for name, mode, moved in (("read", FDL_PROBE_READ, n), ("read_lds", FDL_PROBE_READ_LDS, n),
                               ("copy", FDL_PROBE_COPY, 2 * n)):
-        best = None
-        for _ in range(reps + 1):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            h.fdl_bandwidth_probe(mode, src, dst if mode == FDL_PROBE_COPY else chk)
-            b.record()
-            torch.cuda.synchronize()
-            t = a.elapsed_time(b) * 1e-3
-            best = t if best is None else min(best, t)
-        res[name + "_GBps"] = moved / best / 1e9
+        per_grid = {}
+        for nb in blocks:
+            best = None
+            for _ in range(reps + 1):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                h.fdl_bandwidth_probe(mode, src, dst if mode == FDL_PROBE_COPY else chk, nb)
+                b.record()
+                torch.cuda.synchronize()
+                t = a.elapsed_time(b) * 1e-3
+                best = t if best is None else min(best, t)
+            per_grid[str(nb or "default")] = round(moved / best / 1e9, 1)
+        res[name + "_GBps"] = max(per_grid.values())
+        res[name + "_by_grid"] = per_grid
     del src, dst, chk
     return res
 

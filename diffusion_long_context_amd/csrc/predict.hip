@@ -14,15 +14,22 @@ namespace fdl {
 // Rank of this lane's position among the masked positions of one sequence: how many masked
 // positions rank strictly above it (higher confidence, or equal and lower position).  *is_masked
 // gets the lane's flag; lanes at or past T are unmasked.  Reads only, each lane its own position.
+// The flag and the confidence are read together (one round trip, not two), and each masked
+// position's key reaches every lane through a scalar register, the masked set being one ballot.
 __device__ __forceinline__ int masked_rank(int T, const float* __restrict__ conf, const uint8_t* masked,
                                            int lane, int* is_masked) {
-  const int m = (lane < T && masked[lane] != 0) ? 1 : 0;
-  const uint32_t key = m ? order_key(conf[lane]) : 0u;
+  const bool in = lane < T;
+  const uint8_t mf = in ? masked[lane] : (uint8_t)0;
+  const float c = in ? conf[lane] : 0.f;
+  const int m = mf != 0 ? 1 : 0;
+  const uint32_t key = order_key(c);
+  uint64_t left = __ballot(m);   // wave-uniform
   int rank = 0;
-  for (int j = 0; j < T; ++j) {
-    const uint32_t kj = __shfl(key, j, 64);
-    const int mj = __shfl(m, j, 64);
-    rank += (mj && (kj > key || (kj == key && j < lane))) ? 1 : 0;
+  while (left != 0ull) {
+    const int j = __builtin_ctzll(left);
+    left &= left - 1ull;
+    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+    rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
   }
   *is_masked = m;
   return rank;
