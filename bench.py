@@ -201,19 +201,23 @@ def stream_reference(h, dev, mib: int = 2048, reps: int = 5, blocks=(0, 768, 819
     """The rate a plain coalesced stream reaches on this chip (fdl_bandwidth_probe over a buffer far
     larger than the last-level cache): read into registers, read by LDS DMA, and copy; best of reps
     at each grid size in blocks (0 = the probe's default of 4 workgroups per CU), best grid kept.
-    The read rate moves by about 10% with the grid size alone, so one grid would understate it."""
+    The read rate moves by about 10% with the grid size alone, so one grid would understate it.
+    "tiles" is the attention kernels' own pattern (one workgroup per CU streaming its own K and V
+    regions, one 16 KiB tile in flight per wave)."""
     import torch
 
-    from diffusion_long_context_amd.fdllm import FDL_PROBE_COPY, FDL_PROBE_READ, FDL_PROBE_READ_LDS
+    from diffusion_long_context_amd.fdllm import FDL_PROBE_COPY, FDL_PROBE_READ, FDL_PROBE_READ_LDS, FDL_PROBE_TILES
     n = mib << 20
     src = torch.ones(n // 4, dtype=torch.int32, device=dev)
     chk = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     res = {"bytes": n}
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    tiles_moved = 2 * n_cu * ((n // 2 // n_cu) & ~8191)   # the K and V regions of one workgroup per CU
     for name, mode, moved in (("read", FDL_PROBE_READ, n), ("read_lds", FDL_PROBE_READ_LDS, n),
-                              ("copy", FDL_PROBE_COPY, 2 * n)):
+                              ("copy", FDL_PROBE_COPY, 2 * n), ("tiles", FDL_PROBE_TILES, tiles_moved)):
         per_grid = {}
-        for nb in blocks:
+        for nb in (blocks if mode != FDL_PROBE_TILES else (0,)):
             best = None
             for _ in range(reps + 1):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -882,7 +886,7 @@ def main():
     sb = step_bytes(cfg, units)
     log("streaming reference (bandwidth probe)")
     sref = stream_reference(h, dev)
-    best_ref = max(sref["read_GBps"], sref["read_lds_GBps"])
+    best_ref = max(sref["read_GBps"], sref["read_lds_GBps"], sref["tiles_GBps"])
     result = {
         "metric": METRIC,
         "value": value,

@@ -1014,11 +1014,13 @@ fdl_status fdl_graph_destroy(fdl_graph g) {
 fdl_status fdl_bandwidth_probe(fdl_handle h, int32_t mode, const void* src, size_t bytes, void* dst,
                                size_t dst_bytes, int32_t n_blocks) {
   if (!h) return FDL_EINVAL;
-  if (mode < FDL_PROBE_READ || mode > FDL_PROBE_COPY) return fail(h, FDL_EINVAL, "unknown probe mode");
+  if (mode < FDL_PROBE_READ || mode > FDL_PROBE_TILES) return fail(h, FDL_EINVAL, "unknown probe mode");
   if (!src || !dst) return fail(h, FDL_EINVAL, "src and dst must be non-NULL");
   if (bytes == 0 || bytes % 1024) return fail(h, FDL_EINVAL, "bytes must be a positive multiple of 1024");
   if (n_blocks < 0) return fail(h, FDL_EINVAL, "n_blocks must be >= 0");
-  const int nb = n_blocks > 0 ? n_blocks : 4 * h->num_cus;
+  const int nb = n_blocks > 0 ? n_blocks : (mode == FDL_PROBE_TILES ? h->num_cus : 4 * h->num_cus);
+  if (mode == FDL_PROBE_TILES && fdl::probe_tile_region(bytes, nb) == 0)
+    return fail(h, FDL_EINVAL, "bytes too small for %d workgroups of 16 KiB tiles", nb);
   const size_t need = mode == FDL_PROBE_COPY ? bytes : fdl::probe_out_words(nb) * sizeof(uint32_t);
   if (dst_bytes < need) return fail(h, FDL_EINVAL, "dst holds %zu bytes, needs %zu", dst_bytes, need);
   return hip_status(h, fdl::launch_probe(h->stream, mode, src, bytes, dst, nb), "probe launch");

@@ -35,7 +35,7 @@ EXPORTED = (
 )
 
 FDL_LAYER_DENSE, FDL_LAYER_SOURCE, FDL_LAYER_REUSE = 0, 1, 2
-FDL_PROBE_READ, FDL_PROBE_READ_LDS, FDL_PROBE_COPY = 0, 1, 2
+FDL_PROBE_READ, FDL_PROBE_READ_LDS, FDL_PROBE_COPY, FDL_PROBE_TILES = 0, 1, 2, 3
 PROF_KINDS = ("predict", "pool", "score", "sinks", "select", "sparse_attn", "dense_attn",
               "layer_dense", "layer_source", "layer_reuse", "reuse_run")
 

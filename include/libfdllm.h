@@ -481,9 +481,13 @@ int32_t fdl_phase_stamps_built(void);
  * thread; FDL_PROBE_READ_LDS: 1 KiB fetches straight into LDS (global_load_lds_dwordx4), eight in
  * flight per wave; both write one xor checksum word per wave to dst (n_blocks * 8 uint32,
  * dst_bytes at least that).  FDL_PROBE_COPY: the same read stream written to dst (dst_bytes >= bytes).
- * n_blocks workgroups of 512 threads (0 = four per compute unit).  Asynchronous on the handle's
- * stream; time it with events around the call. */
-typedef enum { FDL_PROBE_READ = 0, FDL_PROBE_READ_LDS = 1, FDL_PROBE_COPY = 2 } fdl_probe_mode;
+ * FDL_PROBE_TILES: the attention kernels' own pattern -- the first half of src stands for K, the
+ * second for V, each workgroup streams a region of each of bytes / 2 / n_blocks (rounded down to
+ * 8 KiB; EINVAL if that is 0) as 16 KiB K + V tiles into LDS, one tile in flight per wave; only
+ * 16 KiB * (tiles actually read) count, and the checksum goes to dst as for the read modes.
+ * n_blocks workgroups of 512 threads (0 = four per compute unit; one per compute unit for
+ * FDL_PROBE_TILES).  Asynchronous on the handle's stream; time it with events around the call. */
+typedef enum { FDL_PROBE_READ = 0, FDL_PROBE_READ_LDS = 1, FDL_PROBE_COPY = 2, FDL_PROBE_TILES = 3 } fdl_probe_mode;
 fdl_status fdl_bandwidth_probe(fdl_handle h, int32_t mode, const void* src, size_t bytes, void* dst,
                                size_t dst_bytes, int32_t n_blocks);
 
