@@ -815,6 +815,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   // below e_pre (fetched early, one per wave) are followed by the wave's round-robin start e_rr.
   int e, e1, n_list;
   int e_step = kMhaWaves, e_pre = 0, e_rr = 0;
+  int n_rounds = 0;   // dense: tile rounds that every wave of the workgroup completes
   TilePrep<D> tp;
   uint32_t vm_next = 0;
   bool issued = false;
@@ -865,6 +866,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     const int n_tiles_part = 1 + (n_part + kTileTok - 1) / kTileTok;
     const int e0 = (int)((int64_t)n_tiles_part * s / NS);
     e1 = (int)((int64_t)n_tiles_part * (s + 1) / NS);
+    n_rounds = DENSE ? (e1 - e0) / kMhaWaves : 0;   // wave w has ceil((e1 - e0 - w) / 8) >= this many
     e = e0 + wave;
     // unconditional: the last split may grow past the hinted range once the count is known
     mha_prepare<D, DENSE, false>(p, e, sel_row, sel_lds, lane, tp, contig);
@@ -1022,6 +1024,15 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
         const bf16x8 bfr = as_bf16x8(pb);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(as_bf16x8(va[kl][dt]), bfr, oacc[dt]);
+      }
+    }
+    // Dense: the waves of a workgroup meet after every round of tiles.  The memory system serves
+    // them unevenly; left free, the last wave of a workgroup ends up to 14 us after the first and
+    // the tail streams with few waves in flight.  Every wave passes exactly n_rounds barriers.
+    if constexpr (DENSE) {
+      if (n_rounds > 0) {
+        --n_rounds;
+        __builtin_amdgcn_s_barrier();
       }
     }
   }
