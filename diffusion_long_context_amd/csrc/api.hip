@@ -161,16 +161,18 @@ fdl_status check_sinks(fdl_handle h, const Geom& g, const void* k_cache, const v
   return FDL_OK;
 }
 
+// pin: the prediction inputs when this detection is the step's first reader of the prediction (it
+// then computes pred_mask itself, see launch_sinks)
 fdl_status run_sinks(fdl_handle h, const Geom& g, const void* q, const uint64_t* pred_mask,
                      const void* k_cache, const void* k_dec, float tau, int max_sinks,
-                     int32_t* sink_pos, int32_t* n_sinks, int ns, int cap) {
+                     int32_t* sink_pos, int32_t* n_sinks, int ns, int cap, const fdl::PredictIn* pin = nullptr) {
   ProfScope ps(h, FDL_PROF_SINKS);
   return hip_status(h, fdl::launch_sinks(h->stream, g, q, pred_mask, k_cache, k_dec, tau, max_sinks,
                                          sink_pos, n_sinks, h->scratch, ns, cap, h->status,
                                          h->num_cus, h->tickets, h->sink_area,
                                          // the upper half of the phase buffer (the fused kernel uses the lower)
                                          h->stamps ? h->stamps + h->stamp_words / 2 : nullptr,
-                                         h->stamp_words / 2),
+                                         h->stamp_words / 2, pin),
                     "sinks launch");
 }
 
@@ -833,8 +835,21 @@ static fdl_status focus_step_impl(fdl_handle h, const fdl_geom* gp, const fdl_fo
     if (st != FDL_OK) return st;
   }
   if (dry) return FDL_OK;
-  st = run_predict(h, g.B, g.T, prev_conf, masked, fp->top_k_pos, fp->window, pred_mask, n_pred);
-  if (st != FDL_OK) return st;
+  // The prediction is first read by the first layer that is not dense.  When that layer detects the
+  // sinks, the sink scan computes the prediction itself (one launch fewer per step); otherwise it
+  // runs first, on its own.
+  int first_sparse = n_layers;
+  for (int l = 0; l < n_layers; ++l)
+    if (layers[l].mode != FDL_LAYER_DENSE) {
+      first_sparse = l;
+      break;
+    }
+  const bool pred_in_sinks = first_sparse < n_layers && layers[first_sparse].mode == FDL_LAYER_SOURCE;
+  const fdl::PredictIn pin{prev_conf, masked, fp->top_k_pos, fp->window, pred_mask, n_pred};
+  if (!pred_in_sinks) {
+    st = run_predict(h, g.B, g.T, prev_conf, masked, fp->top_k_pos, fp->window, pred_mask, n_pred);
+    if (st != FDL_OK) return st;
+  }
   // runs of consecutive reuse layers, bracketed by one pair of events when FDL_PROF_REUSE_RUN is on
   hipEvent_t run_a = nullptr, run_b = nullptr;
   int run_n = 0;
@@ -869,13 +884,13 @@ static fdl_status focus_step_impl(fdl_handle h, const fdl_geom* gp, const fdl_fo
       continue;
     }
     const bool fused = fused_select_ok(g, n_blk, fp->max_sel, fp->max_sinks);
-    if (!fused) {
-      st = run_score_units(h, g, io.q, pred_mask, io.ks, n_blk, bt_log2, scores);
+    if (io.mode == FDL_LAYER_SOURCE) {   // first: it may compute the prediction the scoring reads
+      st = run_sinks(h, g, io.q, pred_mask, io.k_cache, io.k_dec, fp->sink_tau, fp->max_sinks, sink_pos,
+                     n_sinks, ns, cap, pred_in_sinks && l == first_sparse ? &pin : nullptr);
       if (st != FDL_OK) return st;
     }
-    if (io.mode == FDL_LAYER_SOURCE) {
-      st = run_sinks(h, g, io.q, pred_mask, io.k_cache, io.k_dec, fp->sink_tau, fp->max_sinks, sink_pos,
-                     n_sinks, ns, cap);
+    if (!fused) {
+      st = run_score_units(h, g, io.q, pred_mask, io.ks, n_blk, bt_log2, scores);
       if (st != FDL_OK) return st;
     }
     if (fused) {

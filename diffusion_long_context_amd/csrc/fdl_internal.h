@@ -141,12 +141,20 @@ hipError_t launch_score_tokens(hipStream_t s, const Geom& g, const void* q, cons
 
 // Sink detection.  Needs scratch for per-split statistics, candidates and bitmaps.
 size_t sink_scratch_bytes(const Geom& g, int* n_splits, int* cand_cap);
+// The prediction inputs, when launch_sinks is the step's first reader of the prediction: it then
+// computes the prediction into pred_mask / n_pred (inside the sink scan) instead of reading it.
+struct PredictIn {
+  const float* conf;       // previous step's confidences [B][T], or NULL (the whole block)
+  const uint8_t* masked;   // [B][T]
+  int top_k, window;
+  uint64_t* pred_mask;     // [B], out
+  int32_t* n_pred;         // [B], out
+};
 hipError_t launch_sinks(hipStream_t s, const Geom& g, const void* q, const uint64_t* pred_mask,
                         const void* k, const void* k_dec, float tau, int max_sinks,
                         int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
                         int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
-                        char* sink_area,
-                        uint64_t* stamps = nullptr, int64_t stamp_words = 0);
+                        char* sink_area, uint64_t* stamps, int64_t stamp_words, const PredictIn* pin = nullptr);
 
 // Level 2 in one kernel (tokens.hip): launch_score_tokens + launch_select with force_first, same
 // outputs.  score_select_tokens_ok: the shapes it takes (bf16, dec_len <= 32, units of 256 to 4096

@@ -8,32 +8,9 @@
 // highest confidence (the same ranking) are the ones it decodes.
 #include "fdl_device.h"
 #include "fdl_internal.h"
+#include "fdl_predict.h"
 
 namespace fdl {
-
-// Rank of this lane's position among the masked positions of one sequence: how many masked
-// positions rank strictly above it (higher confidence, or equal and lower position).  *is_masked
-// gets the lane's flag; lanes at or past T are unmasked.  Reads only, each lane its own position.
-// The flag and the confidence are read together (one round trip, not two), and each masked
-// position's key reaches every lane through a scalar register, the masked set being one ballot.
-__device__ __forceinline__ int masked_rank(int T, const float* __restrict__ conf, const uint8_t* masked,
-                                           int lane, int* is_masked) {
-  const bool in = lane < T;
-  const uint8_t mf = in ? masked[lane] : (uint8_t)0;
-  const float c = in ? conf[lane] : 0.f;
-  const int m = mf != 0 ? 1 : 0;
-  const uint32_t key = order_key(c);
-  uint64_t left = __ballot(m);   // wave-uniform
-  int rank = 0;
-  while (left != 0ull) {
-    const int j = __builtin_ctzll(left);
-    left &= left - 1ull;
-    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
-    rank += (kj > key || (kj == key && j < lane)) ? 1 : 0;
-  }
-  *is_masked = m;
-  return rank;
-}
 
 __global__ __launch_bounds__(64) void predict_kernel(int T, const float* __restrict__ prev_conf,
                                                      const uint8_t* __restrict__ masked, int top_k,
@@ -41,22 +18,8 @@ __global__ __launch_bounds__(64) void predict_kernel(int T, const float* __restr
                                                      int32_t* __restrict__ n_pred) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  const uint64_t all = (T == 64) ? ~0ull : ((1ull << T) - 1ull);
-  uint64_t pred;
-  if (prev_conf == nullptr) {
-    pred = all;
-  } else {
-    int m;
-    const int rank = masked_rank(T, prev_conf + (int64_t)b * T, masked + (int64_t)b * T, lane, &m);
-    const uint64_t chosen = __ballot(m && rank < top_k);
-    const int w = window < 64 ? window : 64;
-    pred = 0;
-    for (int s = -w; s <= w; ++s) {
-      if (s >= 64 || s <= -64) continue;
-      pred |= (s >= 0) ? (chosen << s) : (chosen >> (-s));
-    }
-    pred &= all;
-  }
+  const uint64_t pred = predict_mask(T, prev_conf ? prev_conf + (int64_t)b * T : nullptr, masked + (int64_t)b * T,
+                                     top_k, window, lane);
   if (lane == 0) {
     pred_mask[b] = pred;
     n_pred[b] = __popcll(pred);

@@ -17,6 +17,7 @@
 // sink list.
 #include "fdl_device.h"
 #include "fdl_internal.h"
+#include "fdl_predict.h"
 #include "fdl_stream.h"
 
 namespace fdl {
@@ -78,6 +79,13 @@ struct SinkParams {
   const uint16_t* k;
   const uint16_t* k_dec;
   const uint64_t* pred_mask;
+  // when pconf_given: the scan computes the prediction itself from these (the step's first reader
+  // of it) and the workgroup of head 0, split 0 of each sequence writes it to pred_out / n_pred_out
+  const float* pconf;
+  const uint8_t* pmasked;
+  uint64_t* pred_out;
+  int32_t* n_pred_out;
+  int pconf_given, ptop_k, pwindow;
   float2* stats;         // [B * Hq][n_splits * 4][32]  (running max in log2 units, running sum)
   uint32_t* cand_count;  // [B * Hq], zero on entry; sink_compact_kernel zeroes it again
   uint32_t* cand;        // [B * Hq][cand_cap]  token positions
@@ -134,13 +142,29 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   const int seg = b * p.Hq + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
-  const uint64_t pred = p.pred_mask[b];
-  const int n_pred = __popcll(pred);
+  __shared__ uint64_t s_pred;
+  if (p.pconf_given) {   // uniform: wave 0 predicts the sequence's queries
+    if (wave == 0) {
+      const uint64_t pm = predict_mask(p.T, p.pconf ? p.pconf + (int64_t)b * p.T : nullptr,
+                                       p.pmasked + (int64_t)b * p.T, p.ptop_k, p.pwindow, lane);
+      if (lane == 0) {
+        s_pred = pm;
+        if (h == 0 && s == 0) {
+          p.pred_out[b] = pm;
+          p.n_pred_out[b] = __popcll(pm);
+        }
+      }
+    }
+  } else if (tid == 0) {
+    s_pred = p.pred_mask[b];
+  }
   const int n_parts = NS * kSinkWaves;
   const int Lb = seq_len(p.lens, b, p.L);   // this sequence's cached tokens; its rows stay p.L apart
   float m_run = -__builtin_inff(), l_run = 0.f;
   if (tid < kSinkWaves * 32) s_run[tid >> 5][tid & 31] = make_float2(-__builtin_inff(), 0.f);
   __syncthreads();
+  const uint64_t pred = s_pred;
+  const int n_pred = __popcll(pred);
   uint32_t n_local = 0;   // this wave's candidates in s_cand[wave] (uniform)
   const uint16_t* kdec = p.k_dec + ((int64_t)b * p.Hkv + g) * p.T * D;
   const uint16_t* kctx = p.k + ((int64_t)b * p.Hkv + g) * (int64_t)p.L * D;
@@ -631,8 +655,15 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
                         const void* k, const void* k_dec, float tau, int max_sinks,
                         int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
                         int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
-                        char* sink_area, uint64_t* stamps, int64_t stamp_words) {
+                        char* sink_area, uint64_t* stamps, int64_t stamp_words, const PredictIn* pin) {
   (void)num_cus;
+  // the prediction, when it is asked for here: inside the scan when the scan runs, else first
+  const bool scan_runs = g.dtype != FDL_F32 && g.L > 0;
+  if (pin != nullptr && !scan_runs) {
+    const hipError_t e = launch_predict(st, g.B, g.T, pin->conf, pin->masked, pin->top_k, pin->window,
+                                        pin->pred_mask, pin->n_pred);
+    if (e != hipSuccess) return e;
+  }
   const int words = (g.L + 31) / 32;
   char* cur = scratch;
   auto take = [&](size_t bytes) {
@@ -652,6 +683,13 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
   p.k = static_cast<const uint16_t*>(k);
   p.k_dec = static_cast<const uint16_t*>(k_dec);
   p.pred_mask = pred_mask;
+  p.pconf_given = pin != nullptr && scan_runs ? 1 : 0;
+  p.pconf = pin ? pin->conf : nullptr;
+  p.pmasked = pin ? pin->masked : nullptr;
+  p.pred_out = pin ? pin->pred_mask : nullptr;
+  p.n_pred_out = pin ? pin->n_pred : nullptr;
+  p.ptop_k = pin ? pin->top_k : 0;
+  p.pwindow = pin ? pin->window : 0;
   p.tickets = tickets;
   p.status = status;
   p.Hq = g.Hq;

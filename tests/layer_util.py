@@ -136,8 +136,8 @@ def focus_step_layers(h, cfg, xs, modes, prev_conf, masked, ctx_lens=None):
     step(len(modes))
     st, bits = h.fdl_get_status_bits()
     assert st == 0, st
-    res.update(outs=outs, pred_mask=host(pm).view(np.uint64).copy(), sink_pos=host(sp).copy(),
-               n_sinks=host(nsk).copy(), bits=bits)
+    res.update(outs=outs, pred_mask=host(pm).view(np.uint64).copy(), n_pred=host(npd).copy(),
+               sink_pos=host(sp).copy(), n_sinks=host(nsk).copy(), bits=bits)
     return res
 
 
@@ -154,6 +154,7 @@ def check_focus_step_layers(cfg, got, xs, modes, prev_conf, masked, what=""):
         want = focus_layer_step(cfg, x, m, sinks=sinks)
         wants.append(want)
         assert np.array_equal(got["pred_mask"], np.asarray(want["pred_mask"], np.uint64)), (what, l)
+        assert [bin(int(v)).count("1") for v in got["pred_mask"]] == got["n_pred"].tolist(), (what, l)
         if m == "source":
             assert want["sink_margin"] > 1e-4 * cfg.sink_tau, f"flagged case: sink margin {want['sink_margin']:.3g}"
             sinks = (want["sink_pos"], want["n_sinks"])

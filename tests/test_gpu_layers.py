@@ -322,3 +322,64 @@ def test_focus_step_dream7b_gqa_16k_full():
                 assert set(xs[l]["planted"][0, gh].tolist()) <= chosen, (l, gh)
     finally:
         h.close()
+
+
+@pytest.mark.parametrize("cfg_kw,modes", [
+    (dict(), ("dense", "source", "reuse")),                 # the sink scan computes the prediction
+    (dict(), ("dense", "dense")),                           # no sparse layer: the prediction kernel
+    (dict(), ("reuse", "source")),                          # a reuse layer reads it first
+    (dict(top_k_pos=9, window=0), ("source",)),             # no widening
+    (dict(top_k_pos=2, window=40), ("dense", "source")),    # widening past the block's ends
+    ("f32", ("source", "reuse")),                           # float32: predicted before the detection
+])
+def test_focus_step_prediction_paths(cfg_kw, modes):
+    """However the step driver produces the prediction (inside the sink scan when the first sparse
+    layer detects sinks, else a launch of its own), pred_mask and n_pred equal the oracle's, with
+    and without previous confidences; the one-call prediction agrees too."""
+    require_gpu()
+    from diffusion_long_context_amd import Handle
+    from diffusion_long_context_amd.fdllm import FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE, fdl_focus_params
+    from diffusion_long_context_amd.step import geom_for
+    from oracle.predictor import predict_positions
+    if cfg_kw == "f32":
+        cfg = get_config(0).with_(batch=2)
+    else:
+        cfg = get_config(1).with_(batch=3, n_q_heads=4, n_kv_heads=4, ctx_len=3000, top_k_blocks=8, **cfg_kw)
+    code = {"dense": FDL_LAYER_DENSE, "source": FDL_LAYER_SOURCE, "reuse": FDL_LAYER_REUSE}
+    x = make_single(cfg)
+    g = geom_for(cfg)
+    B, Hq, Hkv, D, T, nb, ms = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len,
+                                cfg.n_blk, cfg.max_sel_blocks)
+    fdt = torch.float32 if cfg_kw == "f32" else torch.bfloat16
+    h = Handle(workspace_bytes=256 << 20)
+    try:
+        t = {k: dev(x[k]) for k in ("q", "k", "v", "k_dec", "v_dec")}
+        ks = torch.zeros((B, Hkv, nb, D), dtype=torch.float32, device="cuda")
+        h.fdl_pool_keys(g, t["k"], None, cfg.kv_block, ks)
+        out = torch.zeros((B, Hq, T, D), dtype=fdt, device="cuda")
+        table = h.make_layers(g, [dict(q=t["q"], k_cache=t["k"], v_cache=t["v"], k_dec=t["k_dec"], v_dec=t["v_dec"],
+                                       ks=ks, out=out, mode=code[m]) for m in modes])
+        sc = torch.zeros((B, Hkv, nb), dtype=torch.float32, device="cuda")
+        sp = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device="cuda")
+        nsk = torch.zeros(B, dtype=torch.int32, device="cuda")
+        sel = torch.zeros((B, Hkv, ms), dtype=torch.int32, device="cuda")
+        nsel = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+        params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, ms, cfg.sink_tau)
+        for conf in (x["prev_conf"], None):
+            pm = torch.full((B,), -1, dtype=torch.int64, device="cuda")   # stale values must be overwritten
+            npd = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+            h.fdl_focus_step(g, params, dev(conf) if conf is not None else None, dev(x["masked"]), table, pm, npd,
+                             sc, sp, nsk, sel, nsel)
+            torch.cuda.synchronize()
+            assert h.fdl_get_status() == 0
+            want_bits, want_n = predict_positions(conf, x["masked"], cfg.top_k_pos, cfg.window)
+            assert np.array_equal(host(pm).view(np.uint64), want_bits), (modes, conf is None)
+            assert np.array_equal(host(npd), want_n), (modes, conf is None)
+            pm1 = torch.zeros(B, dtype=torch.int64, device="cuda")
+            np1 = torch.zeros(B, dtype=torch.int32, device="cuda")
+            h.fdl_predict_queries(B, T, dev(conf) if conf is not None else None, dev(x["masked"]), cfg.top_k_pos,
+                                  cfg.window, pm1, np1)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(pm1).view(np.uint64), want_bits) and np.array_equal(host(np1), want_n)
+    finally:
+        h.close()
