@@ -165,14 +165,15 @@ fdl_status check_sinks(fdl_handle h, const Geom& g, const void* k_cache, const v
 // then computes pred_mask itself, see launch_sinks)
 fdl_status run_sinks(fdl_handle h, const Geom& g, const void* q, const uint64_t* pred_mask,
                      const void* k_cache, const void* k_dec, float tau, int max_sinks,
-                     int32_t* sink_pos, int32_t* n_sinks, int ns, int cap, const fdl::PredictIn* pin = nullptr) {
+                     int32_t* sink_pos, int32_t* n_sinks, int ns, int cap, const fdl::PredictIn* pin = nullptr,
+                     bool keep_bitmap = false) {
   ProfScope ps(h, FDL_PROF_SINKS);
   return hip_status(h, fdl::launch_sinks(h->stream, g, q, pred_mask, k_cache, k_dec, tau, max_sinks,
                                          sink_pos, n_sinks, h->scratch, ns, cap, h->status,
                                          h->num_cus, h->tickets, h->sink_area,
                                          // the upper half of the phase buffer (the fused kernel uses the lower)
                                          h->stamps ? h->stamps + h->stamp_words / 2 : nullptr,
-                                         h->stamp_words / 2, pin),
+                                         h->stamp_words / 2, pin, keep_bitmap),
                     "sinks launch");
 }
 
@@ -225,9 +226,18 @@ static size_t fused_xchg_offset(const Geom& g, int n_splits) {
   return (fdl::attn_scratch_bytes(g, n_splits) + 255) & ~(size_t)255;
 }
 
+// How a fused layer handles the sink detection's bitmap (see FusedSelect): read it in place of the
+// list (the detecting layer, whose list it then writes), or clear it (a later layer).
+struct SinkBitmapUse {
+  const uint32_t* read = nullptr;
+  uint32_t* clear = nullptr;
+  int words = 0;
+};
+
 fdl_status run_select_attn(fdl_handle h, const Geom& g, const fdl_layer_io& io, const uint64_t* pred_mask,
-                           const fdl_focus_params* fp, int bt_log2, const int32_t* sink_pos,
-                           const int32_t* n_sinks, float* scores, int32_t* sel_idx, int32_t* n_sel) {
+                           const fdl_focus_params* fp, int bt_log2, int32_t* sink_pos,
+                           int32_t* n_sinks, float* scores, int32_t* sel_idx, int32_t* n_sel,
+                           const SinkBitmapUse& sbm = SinkBitmapUse{}) {
   long long list_tokens = (long long)fp->max_sel << bt_log2;
   if (list_tokens > g.L) list_tokens = g.L;
   int n_splits = attn_splits(h, g, list_tokens);
@@ -246,9 +256,27 @@ fdl_status run_select_attn(fdl_handle h, const Geom& g, const fdl_layer_io& io, 
       return fail(h, FDL_ENOMEM, "workspace too small for the score exchange");
     xchg = reinterpret_cast<float*>(h->scratch + fused_xchg_offset(g, n_splits));
   }
-  const fdl::FusedSelect fs{pred_mask, io.ks,   sink_pos,    n_sinks,        fp->max_sinks, fp->top_k_blocks,
-                            scores,    sel_idx, n_sel,       h->barriers,    h->spin_limit, xchg,
-                            h->stamps, h->stamp_words, h->fused_serial++};
+  fdl::FusedSelect fs{};
+  fs.pred_mask = pred_mask;
+  fs.ks = io.ks;
+  fs.sink_pos = sink_pos;
+  fs.n_sinks = n_sinks;
+  fs.max_sinks = fp->max_sinks;
+  fs.top_k = fp->top_k_blocks;
+  fs.scores = scores;
+  fs.sel_idx = sel_idx;
+  fs.n_sel = n_sel;
+  fs.barriers = h->barriers;
+  fs.spin_limit = h->spin_limit;
+  fs.xchg = xchg;
+  fs.sink_bitmap = sbm.read;
+  fs.sink_pos_out = sink_pos;
+  fs.n_sinks_out = n_sinks;
+  fs.clear_bitmap = sbm.clear;
+  fs.sink_words = sbm.words;
+  fs.stamps = h->stamps;
+  fs.stamp_words = h->stamp_words;
+  fs.serial = h->fused_serial++;
   ProfScope ps(h, FDL_PROF_SPARSE_ATTN, /*inner=*/true);
   return hip_status(h, fdl::launch_attn_mha(h->stream, g, io.q, io.k_cache, io.v_cache, io.k_dec, io.v_dec,
                                             nullptr, sel_idx, n_sel, fp->max_sel, bt_log2, 0, io.out,
@@ -861,6 +889,18 @@ static fdl_status focus_step_impl(fdl_handle h, const fdl_geom* gp, const fdl_fo
     run_a = run_b = nullptr;
     run_n = 0;
   };
+  // The sink detection's bitmap goes straight to the fused kernel of the detecting layer, which forces
+  // the units of its first max_sinks positions and writes the list (no compaction launch), when it
+  // sits in the handle's header and fits the kernel's read; the next fused layer clears it (or a
+  // fill, before another detection or at the end of the step).
+  int bm_words = 0;
+  uint32_t* bm = fdl::sink_bitmap_for(g, h->sink_area, &bm_words);
+  if (bm_words > fdl::kFusedSinkWords) bm = nullptr;
+  bool bm_pending = false;   // bm holds the last detection's bits
+  auto bm_fill = [&]() -> fdl_status {
+    bm_pending = false;
+    return hip_status(h, fdl::launch_fill_u32(h->stream, bm, (size_t)g.B * bm_words, 0u), "sink bitmap clear");
+  };
   for (int l = 0; l < n_layers; ++l) {
     const fdl_layer_io& io = layers[l];
     if (io.mode == FDL_LAYER_REUSE) {
@@ -884,9 +924,14 @@ static fdl_status focus_step_impl(fdl_handle h, const fdl_geom* gp, const fdl_fo
       continue;
     }
     const bool fused = fused_select_ok(g, n_blk, fp->max_sel, fp->max_sinks);
+    const bool keep_bm = fused && bm != nullptr && io.mode == FDL_LAYER_SOURCE;
     if (io.mode == FDL_LAYER_SOURCE) {   // first: it may compute the prediction the scoring reads
+      if (bm_pending) {   // a detection starts from a clear bitmap
+        st = bm_fill();
+        if (st != FDL_OK) return st;
+      }
       st = run_sinks(h, g, io.q, pred_mask, io.k_cache, io.k_dec, fp->sink_tau, fp->max_sinks, sink_pos,
-                     n_sinks, ns, cap, pred_in_sinks && l == first_sparse ? &pin : nullptr);
+                     n_sinks, ns, cap, pred_in_sinks && l == first_sparse ? &pin : nullptr, keep_bm);
       if (st != FDL_OK) return st;
     }
     if (!fused) {
@@ -894,8 +939,17 @@ static fdl_status focus_step_impl(fdl_handle h, const fdl_geom* gp, const fdl_fo
       if (st != FDL_OK) return st;
     }
     if (fused) {
-      st = run_select_attn(h, g, io, pred_mask, fp, bt_log2, sink_pos, n_sinks, scores, sel_idx, n_sel);
+      SinkBitmapUse use;
+      if (keep_bm) {
+        use.read = bm;
+        use.words = bm_words;
+      } else if (bm_pending) {
+        use.clear = bm;
+        use.words = bm_words;
+      }
+      st = run_select_attn(h, g, io, pred_mask, fp, bt_log2, sink_pos, n_sinks, scores, sel_idx, n_sel, use);
       if (st != FDL_OK) return st;
+      bm_pending = keep_bm;
       continue;
     }
     st = run_select(h, g, scores, n_blk, bt_log2, sink_pos, n_sinks, fp->max_sinks, nullptr, 0,
@@ -906,6 +960,7 @@ static fdl_status focus_step_impl(fdl_handle h, const fdl_geom* gp, const fdl_fo
     if (st != FDL_OK) return st;
   }
   if (run_n > 0) run_end();
+  if (bm_pending) return bm_fill();
   return FDL_OK;
 }
 

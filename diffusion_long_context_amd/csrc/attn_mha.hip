@@ -318,8 +318,10 @@ __device__ __forceinline__ void mha_forced_list(const uint32_t* forced, int n, i
 // kvh: the KV head within sequence b; kvseg = b * Hkv + kvh; bar_i: the group's barrier word.
 // nb: the units of sequence b (all of them unless the batch is ragged); rows are p.n_units apart.
 template <int D, bool GQA, bool SAFE>
+// seq_writer: the one workgroup of the sequence (KV head 0, split 0, member 0) that writes the sink
+// list when the sinks come from the detection's bitmap.
 __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg, int64_t bar_i, float* sc_out,
-                               int m, int M, uint16_t* lds_raw, uint16_t* sel_lds, int nb) {
+                               int m, int M, uint16_t* lds_raw, uint16_t* sel_lds, int nb, bool seq_writer) {
   constexpr int NT = kMhaWaves * 64;
   constexpr int LPR = D / 16;
   static_assert((kQbufOffsetF + 32 * D) * sizeof(float) <= sizeof(uint16_t) * kMhaWaves * MhaShape<D>::SLOT,
@@ -356,12 +358,15 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
   // (every load unconditional, from a valid address: a load under a branch would make the waits
   // below count conservatively)
   const uint64_t pred = f.pred_mask[b];
-  const bool have_sinks = f.sink_pos != nullptr;
+  // sinks from the detection's bitmap (thread t holds words 2t and 2t + 1), or from the list
+  const bool from_bitmap = f.sink_bitmap != nullptr;   // uniform
+  const bool have_sinks = !from_bitmap && f.sink_pos != nullptr;
   const bool sink_lane = have_sinks && tid < f.max_sinks;
   const int32_t* sp = have_sinks ? f.sink_pos + (int64_t)b * f.max_sinks + (tid < f.max_sinks ? tid : 0)
                                  : reinterpret_cast<const int32_t*>(f.pred_mask + b);
   const int sink_p = *sp;
   const int sink_n = have_sinks ? f.n_sinks[b] : 0;
+
   // safe mode: no member hands scores to another; each scores every unit itself
   const int ra = SAFE ? 0 : (int)((int64_t)n * m / M), rb = SAFE ? n : (int)((int64_t)n * (m + 1) / M);
   float x[kScoreBatch][16];
@@ -387,6 +392,29 @@ __device__ int mha_score_phase(const MhaParams& p, int b, int kvh, int64_t kvseg
   if (sink_lane && tid < sink_n && sink_p >= 0) {
     const int u = sink_p >> p.unit_log2;
     if (u < n) atomicOr(&L.forced[u >> 5], 1u << (u & 31));
+  }
+  static_assert(2 * NT >= kFusedSinkWords, "two bitmap words per thread");
+  if (from_bitmap) {   // uniform: the ascending set positions, the first max_sinks of them taken
+    const int n_words = f.sink_words;
+    const uint32_t* brow = f.sink_bitmap + (int64_t)b * n_words;
+    const uint32_t bw0 = 2 * tid < n_words ? brow[2 * tid] : 0u;
+    const uint32_t bw1 = 2 * tid + 1 < n_words ? brow[2 * tid + 1] : 0u;
+    int total;
+    int pos = block_excl_scan<NT>(__popc(bw0) + __popc(bw1), L.tmp, total);
+    for (int k = 0; k < 2; ++k)
+      for (uint32_t w = k ? bw1 : bw0; w != 0u && pos < f.max_sinks; w &= w - 1u, ++pos) {
+        const int tok = 32 * (2 * tid + k) + __builtin_ctz(w);
+        const int u = tok >> p.unit_log2;
+        if (u < n) atomicOr(&L.forced[u >> 5], 1u << (u & 31));
+        if (seq_writer) f.sink_pos_out[(int64_t)b * f.max_sinks + pos] = tok;
+      }
+    if (seq_writer) {
+      for (int i = total + tid; i < f.max_sinks; i += NT) f.sink_pos_out[(int64_t)b * f.max_sinks + i] = -1;
+      if (tid == 0) {
+        f.n_sinks_out[b] = total < f.max_sinks ? total : f.max_sinks;
+        if (total > f.max_sinks) latch(p.status, ST_SINK_OVERFLOW);
+      }
+    }
   }
   float qv[16];
 #pragma unroll
@@ -767,6 +795,15 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     seg_i = (kv_i / p.Hkv) * p.H + (kv_i % p.Hkv) * p.G + member;
   }
   const int b = kv_i / p.Hkv, h = kv_i % p.Hkv;   // h: KV head within the sequence
+  // the one workgroup of the sequence that writes its sink list (or clears the detection's bitmap)
+  const bool seq_writer = h == 0 && s == 0 && member == 0;
+  // A bitmap no one reads any more (the detection's, read by the layer before): zeroed for the next
+  // detection by the sequence's writer at its way out, after its own work.
+  auto clear_sinks = [&]() {
+    if (SEL && p.fs.clear_bitmap != nullptr && seq_writer)
+      for (int i = threadIdx.x; i < p.fs.sink_words; i += kMhaWaves * 64)
+        p.fs.clear_bitmap[(int64_t)b * p.fs.sink_words + i] = 0u;
+  };
   const int Lb = seq_len(p.lens, b, p.L);         // this sequence's tokens (ragged batches)
   const int nb = (Lb + (1 << p.unit_log2) - 1) >> p.unit_log2;
   FDL_STAMP(p, 0);
@@ -825,10 +862,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
     int nf;
     if constexpr (GQA) {
       float* xo = s == 0 ? p.fs.scores + kvseg * p.n_units : p.fs.xchg + (int64_t)gi * p.n_units;
-      nf = mha_score_phase<D, true, SAFE>(p, b, h, kvseg, gi, xo, member, p.G, lds, sel_lds, nb);
+      nf = mha_score_phase<D, true, SAFE>(p, b, h, kvseg, gi, xo, member, p.G, lds, sel_lds, nb, seq_writer);
     } else {
       nf = mha_score_phase<D, false, SAFE>(p, b, h, kvseg, seg, p.fs.scores + kvseg * p.n_units, s, NS, lds, sel_lds,
-                                           nb);
+                                           nb, seq_writer);
     }
     // Known now: tile 0 (the block's own tokens) and the tiles of the nf forced units at the front
     // of the list.  Up to one of them per wave whose slot the selection scratch leaves free is
@@ -1118,7 +1155,10 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   }
   // grouped-query heads: attn_combine_kernel merges the splits; the safe mode merges in a second
   // launch too (attn_merge_kernel, the same arithmetic)
-  if (NS == 1 || GQA || SAFE || (!SEL && !p.merge_here)) return;
+  if (NS == 1 || GQA || SAFE || (!SEL && !p.merge_here)) {
+    clear_sinks();
+    return;
+  }
 
   // ---- same-XCD hand-over: the last split of this head to finish merges all of them.  The
   //      partials sit in this XCD's L2: wait until our stores are acknowledged by it, take a
@@ -1134,12 +1174,16 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
   }
   __syncthreads();
   FDL_STAMP(p, 9);
-  if (s_ticket != (uint32_t)(NS - 1)) return;
+  if (s_ticket != (uint32_t)(NS - 1)) {
+    clear_sinks();
+    return;
+  }
   if (s_here == 0u) {   // uniform
     if (tid == 0) {
       latch(p.status, ST_SPLIT_PLACEMENT);
       reset_ticket(p.tickets + seg * kSyncStride);
     }
+    clear_sinks();
     return;
   }
   asm volatile("buffer_inv sc0" ::: "memory");   // later loads miss L1 and read the partials from L2
@@ -1151,6 +1195,7 @@ __global__ __launch_bounds__(kMhaWaves * 64, 1) void attn_mha_kernel(const MhaPa
       __hip_atomic_fetch_add(&p.fs.barriers[seg * kSyncStride + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   FDL_STAMP(p, 10);
+  clear_sinks();
 }
 
 // The safe mode's merge: one workgroup per (sequence, query head) merges its NS partials exactly as

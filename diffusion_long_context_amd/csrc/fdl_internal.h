@@ -73,6 +73,7 @@ struct KernelTimer {
 constexpr int kFusedMaxUnits = 4096;   // blocks per head the fused path keeps in LDS
 constexpr int kFusedMaxSel = 4096;     // selected blocks per head
 constexpr int kFusedMaxSinks = 512;    // sink list entries (one per thread of the fused kernel)
+constexpr int kFusedSinkWords = 1024;  // sink bitmap words the fused kernel reads (two per thread)
 constexpr int kFusedTaggedUnits = 512; // blocks per head up to which the splits exchange tagged scores
 struct FusedSelect {
   const uint64_t* pred_mask;   // [B]
@@ -87,6 +88,17 @@ struct FusedSelect {
   int spin_limit;              // polls before a split stops waiting for its siblings
   float* xchg;                 // grouped-query heads: [B * Hkv * n_splits][n_units] score exchange
                                // of every (KV head, split) group but split 0's (which uses scores)
+  // Sinks straight from the detection's bitmap [B][sink_words] (the layer that detected them): the
+  // units of the first max_sinks set positions are forced instead of those of sink_pos, and the
+  // workgroup of KV head 0, split 0, member 0 of each sequence writes the ascending list (-1 padded)
+  // and its length to sink_pos_out / n_sinks_out, latching ST_SINK_OVERFLOW past max_sinks.
+  const uint32_t* sink_bitmap;
+  int32_t* sink_pos_out;
+  int32_t* n_sinks_out;
+  // a bitmap nothing reads any more (the detection's, one layer later): the same workgroups zero
+  // their sequence's words for the next detection
+  uint32_t* clear_bitmap;
+  int sink_words;
   uint64_t* stamps;            // phase timestamps [grid][kStampsPerGroup] (FDL_PHASE_STAMPS builds)
   int64_t stamp_words;         // capacity of stamps
   uint32_t serial;             // launch counter of the handle (part of the exchange tag)
@@ -154,7 +166,13 @@ hipError_t launch_sinks(hipStream_t s, const Geom& g, const void* q, const uint6
                         const void* k, const void* k_dec, float tau, int max_sinks,
                         int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
                         int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
-                        char* sink_area, uint64_t* stamps, int64_t stamp_words, const PredictIn* pin = nullptr);
+                        char* sink_area, uint64_t* stamps, int64_t stamp_words, const PredictIn* pin = nullptr,
+                        bool keep_bitmap = false);
+// The sink detection's per-sequence bitmap ([B][*words] uint32, one bit per cached token) when the
+// detection keeps it in the handle's header (bf16 scan); NULL otherwise.  With keep_bitmap the
+// detection ends with the bitmap set and no list: the fused kernel of the same layer then forces the
+// units of the first max_sinks set positions, writes the list, and a later launch clears the words.
+uint32_t* sink_bitmap_for(const Geom& g, char* sink_area, int* words);
 
 // Level 2 in one kernel (tokens.hip): launch_score_tokens + launch_select with force_first, same
 // outputs.  score_select_tokens_ok: the shapes it takes (bf16, dec_len <= 32, units of 256 to 4096

@@ -403,7 +403,10 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     if (s_ticket != (uint32_t)(NS - 1)) return;
     if (tid == 0) reset_ticket(p.tickets + seg * kSyncStride);
     if (s_here == 0u) {   // uniform
-      if (tid == 0) latch(p.status, ST_SPLIT_PLACEMENT);
+      if (tid == 0) {
+        latch(p.status, ST_SPLIT_PLACEMENT);
+        p.cand_count[seg] = 0u;
+      }
       return;
     }
     asm volatile("buffer_inv sc0" ::: "memory");
@@ -484,6 +487,10 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     if (lane == 0 && e / (float)n_pred >= p.tau)
       atomicOr(&p.bitmap[(int64_t)b * p.words + (t >> 5)], 1u << (t & 31));
   }
+  // this head's candidates are consumed (every thread read the count before the loop): its count
+  // is left at zero for the next detection (the compaction, when it runs, zeroes it too)
+  __syncthreads();
+  if (tid == 0) p.cand_count[seg] = 0u;
 #ifdef FDL_PHASE_STAMPS
   __syncthreads();
   SINK_STAMP(p, 6);
@@ -636,6 +643,12 @@ static bool sink_state_in_header(const Geom& g) {
   return ((size_t)g.B * g.Hq + (size_t)g.B * words) * sizeof(uint32_t) <= kSinkAreaBytes;
 }
 
+uint32_t* sink_bitmap_for(const Geom& g, char* sink_area, int* words) {
+  *words = (g.L + 31) / 32;
+  if (g.dtype == FDL_F32 || g.L <= 0 || !sink_state_in_header(g)) return nullptr;
+  return reinterpret_cast<uint32_t*>(sink_area) + (size_t)g.B * g.Hq;
+}
+
 size_t sink_scratch_bytes(const Geom& g, int* n_splits, int* cand_cap) {
   const int s = sink_splits(g);
   *n_splits = s;
@@ -655,7 +668,8 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
                         const void* k, const void* k_dec, float tau, int max_sinks,
                         int32_t* sink_pos, int32_t* n_sinks, char* scratch, int n_splits,
                         int cand_cap, uint32_t* status, int num_cus, uint32_t* tickets,
-                        char* sink_area, uint64_t* stamps, int64_t stamp_words, const PredictIn* pin) {
+                        char* sink_area, uint64_t* stamps, int64_t stamp_words, const PredictIn* pin,
+                        bool keep_bitmap) {
   (void)num_cus;
   // the prediction, when it is asked for here: inside the scan when the scan runs, else first
   const bool scan_runs = g.dtype != FDL_F32 && g.L > 0;
@@ -734,6 +748,8 @@ hipError_t launch_sinks(hipStream_t st, const Geom& g, const void* q, const uint
     }
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  // keep_bitmap: the next launch reads the bitmap itself (sink_bitmap_for) and compacts it
+  if (keep_bitmap && scan_runs && in_header) return hipSuccess;
   hipLaunchKernelGGL(sink_compact_kernel, dim3(g.B), dim3(256), 0, st, p.bitmap, words, max_sinks,
                      sink_pos, n_sinks, p.cand_count, g.Hq, status);
   return hipGetLastError();

@@ -154,7 +154,8 @@ def check_focus_step_layers(cfg, got, xs, modes, prev_conf, masked, what=""):
         want = focus_layer_step(cfg, x, m, sinks=sinks)
         wants.append(want)
         assert np.array_equal(got["pred_mask"], np.asarray(want["pred_mask"], np.uint64)), (what, l)
-        assert [bin(int(v)).count("1") for v in got["pred_mask"]] == got["n_pred"].tolist(), (what, l)
+        if "n_pred" in got:
+            assert [bin(int(v)).count("1") for v in got["pred_mask"]] == got["n_pred"].tolist(), (what, l)
         if m == "source":
             assert want["sink_margin"] > 1e-4 * cfg.sink_tau, f"flagged case: sink margin {want['sink_margin']:.3g}"
             sinks = (want["sink_pos"], want["n_sinks"])

@@ -383,3 +383,25 @@ def test_focus_step_prediction_paths(cfg_kw, modes):
             assert np.array_equal(host(pm1).view(np.uint64), want_bits) and np.array_equal(host(np1), want_n)
     finally:
         h.close()
+
+
+@pytest.mark.parametrize("modes", [("source", "reuse", "source", "reuse"), ("source", "source", "dense", "reuse"),
+                                   ("dense", "source", "dense", "dense")])
+def test_focus_step_sink_bitmap_handover(modes):
+    """The detecting layer's fused kernel reads the detection's bitmap and writes the sink list itself;
+    the next fused layer clears the bitmap, or a fill does before another detection or at the end of
+    the step.  A second detection in the same step, a dense layer in between, and a detecting layer
+    last all give the oracle's sinks, selections and outputs, and the next call starts clean."""
+    require_gpu()
+    from diffusion_long_context_amd import Handle
+    from layer_util import check_focus_step_layers, focus_step_layers
+    cfg = get_config(1).with_(n_q_heads=8, n_kv_heads=8, ctx_len=6000, top_k_blocks=20)
+    xs = [make_single(cfg, layer=l) for l in range(len(modes))]
+    h = Handle(workspace_bytes=512 << 20)
+    try:
+        for rep in range(2):   # the second call must not see the first one's bits
+            got = focus_step_layers(h, cfg, xs, list(modes), xs[0]["prev_conf"], xs[0]["masked"])
+            assert got["bits"] == 0, got["bits"]
+            check_focus_step_layers(cfg, got, xs, list(modes), xs[0]["prev_conf"], xs[0]["masked"], f"{modes} {rep}")
+    finally:
+        h.close()

@@ -122,7 +122,7 @@ def test_ragged_focus_step(case):
         one = {"layers": {l: tuple(a[b:b + 1, :, :-(-lb // cfg.kv_block)] if i == 0 else a[b:b + 1]
                                    for i, a in enumerate(v)) for l, v in got["layers"].items()},
                "outs": [o[b:b + 1] for o in got["outs"]],
-               "pred_mask": got["pred_mask"][b:b + 1], "sink_pos": got["sink_pos"][b:b + 1],
+               "pred_mask": got["pred_mask"][b:b + 1], "n_pred": got["n_pred"][b:b + 1], "sink_pos": got["sink_pos"][b:b + 1],
                "n_sinks": got["n_sinks"][b:b + 1]}
         for l, v in got["layers"].items():
             assert np.all(v[0][b, :, -(-lb // cfg.kv_block):].view(np.uint32) == 0), (case, b, l)
