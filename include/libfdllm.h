@@ -359,8 +359,11 @@ fdl_status fdl_dense_attn(fdl_handle h, const fdl_geom* g, const void* q, const 
  *   FDL_LAYER_REUSE : fdl_score_blocks, fdl_select_blocks with the current sink_pos / n_sinks
  *                     (those of the last source layer; on entry, whatever they hold), fdl_sparse_attn.
  * Scores, sinks and selections are identical to issuing those calls one by one, and outputs agree
- * with theirs to rounding: for bf16 contiguous caches of up to 8192 blocks the scoring, selection
+ * with theirs to rounding: for bf16 contiguous caches of up to 4096 blocks the scoring, selection
  * and attention of a sparse layer run as one kernel, whose splits sum the tiles in another order.
+ * When the first layer that is not dense is a source layer, the prediction is computed inside its
+ * sink detection, and (bf16, sink bitmap in the handle's header) that layer's fused kernel turns the
+ * detection's bitmap into sink_pos / n_sinks itself: two launches fewer, the same values.
  * Only launches are issued (no host synchronisation).  Each layer's KV is contiguous (g->paged == 0), its `ks` is the fdl_pool_keys
  * output with unit kv_block.  scores [B][Hkv][n_blk], sel_idx [B][Hkv][max_sel] and n_sel [B][Hkv]
  * are scratch reused layer to layer and hold the last sparse layer's values on return;
