@@ -142,6 +142,62 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   const int seg = b * p.Hq + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
+  const int n_parts = NS * kSinkWaves;
+  const int Lb = seq_len(p.lens, b, p.L);   // this sequence's cached tokens; its rows stay p.L apart
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  if (tid < kSinkWaves * 32) s_run[tid >> 5][tid & 31] = make_float2(-__builtin_inff(), 0.f);
+  const uint16_t* kdec = p.k_dec + ((int64_t)b * p.Hkv + g) * p.T * D;
+  const uint16_t* kctx = p.k + ((int64_t)b * p.Hkv + g) * (int64_t)p.L * D;
+  // The query rows and each wave's first tile are requested before anything waits: the
+  // prediction below (and its barrier) overlaps their round trip.
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qrow = p.q + ((int64_t)seg * p.T + (ql < p.T ? ql : 0)) * D + hh * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + ks * 8);
+      if (ql >= p.T) v = make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+  const int n_tiles = 1 + (Lb + kSinkTile - 1) / kSinkTile;
+  const int e0 = (int)((int64_t)n_tiles * s / NS);
+  const int e1 = (int)((int64_t)n_tiles * (s + 1) / NS);
+  // tile e -> the wave's slot; rows are clamped so that every fetch is in bounds.  A full cache
+  // tile is one run of kSinkTile rows: a scalar base plus per-lane chunk offsets fixed up front.
+  uint16_t* slot = kslot + wave * kSinkTile * D;
+  uint32_t voff[NI];
+  {
+    const int rsub = lane / PROW, sc = lane % PROW;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = j * RPI + rsub;
+      voff[j] = (uint32_t)((r * D + (sc ^ (swz(r) & (PROW - 1))) * 8) * 2);
+    }
+  }
+  auto issue = [&](int e) {
+    const int rsub = lane / PROW, sc = lane % PROW;
+    if (e > 0 && e * kSinkTile <= Lb) {   // uniform: a full tile of the cache
+      const char* base = reinterpret_cast<const char*>(kctx + (int64_t)(e - 1) * kSinkTile * D);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const void* src = base + voff[j];
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = j * RPI + rsub;
+      const int t = (e - 1) * kSinkTile + r;
+      const uint16_t* row = (e == 0) ? kdec + (int64_t)(r < p.T ? r : p.T - 1) * D
+                                     : kctx + (int64_t)(t < Lb ? t : Lb - 1) * D;
+      const void* src = row + (sc ^ (swz(r) & (PROW - 1))) * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
+    }
+  };
+  int e = e0 + wave;
+  if (e < e1) issue(e);
   __shared__ uint64_t s_pred;
   if (p.pconf_given) {   // uniform: wave 0 predicts the sequence's queries
     if (wave == 0) {
@@ -158,65 +214,13 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
   } else if (tid == 0) {
     s_pred = p.pred_mask[b];
   }
-  const int n_parts = NS * kSinkWaves;
-  const int Lb = seq_len(p.lens, b, p.L);   // this sequence's cached tokens; its rows stay p.L apart
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  if (tid < kSinkWaves * 32) s_run[tid >> 5][tid & 31] = make_float2(-__builtin_inff(), 0.f);
-  __syncthreads();
+  __syncthreads();   // also: the queries and the first tiles have landed
   const uint64_t pred = s_pred;
   const int n_pred = __popcll(pred);
   uint32_t n_local = 0;   // this wave's candidates in s_cand[wave] (uniform)
-  const uint16_t* kdec = p.k_dec + ((int64_t)b * p.Hkv + g) * p.T * D;
-  const uint16_t* kctx = p.k + ((int64_t)b * p.Hkv + g) * (int64_t)p.L * D;
   if (n_pred > 0) {   // uniform
     const bool qlive = ql < p.T && ((pred >> ql) & 1ull);
-    bf16x8 qf[KS];
-    {
-      const uint16_t* qrow = p.q + ((int64_t)seg * p.T + (ql < p.T ? ql : 0)) * D + hh * (D / 2);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 v = *reinterpret_cast<const uint4*>(qrow + ks * 8);
-        if (ql >= p.T) v = make_uint4(0u, 0u, 0u, 0u);
-        qf[ks] = as_bf16x8(v);
-      }
-    }
     const float inv_np = 1.f / (float)n_pred;
-    const int n_tiles = 1 + (Lb + kSinkTile - 1) / kSinkTile;
-    const int e0 = (int)((int64_t)n_tiles * s / NS);
-    const int e1 = (int)((int64_t)n_tiles * (s + 1) / NS);
-    // tile e -> the wave's slot; rows are clamped so that every fetch is in bounds.  A full cache
-    // tile is one run of kSinkTile rows: a scalar base plus per-lane chunk offsets fixed up front.
-    uint16_t* slot = kslot + wave * kSinkTile * D;
-    uint32_t voff[NI];
-    {
-      const int rsub = lane / PROW, sc = lane % PROW;
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int r = j * RPI + rsub;
-        voff[j] = (uint32_t)((r * D + (sc ^ (swz(r) & (PROW - 1))) * 8) * 2);
-      }
-    }
-    auto issue = [&](int e) {
-      const int rsub = lane / PROW, sc = lane % PROW;
-      if (e > 0 && e * kSinkTile <= Lb) {   // uniform: a full tile of the cache
-        const char* base = reinterpret_cast<const char*>(kctx + (int64_t)(e - 1) * kSinkTile * D);
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const void* src = base + voff[j];
-          __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
-        }
-        return;
-      }
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int r = j * RPI + rsub;
-        const int t = (e - 1) * kSinkTile + r;
-        const uint16_t* row = (e == 0) ? kdec + (int64_t)(r < p.T ? r : p.T - 1) * D
-                                       : kctx + (int64_t)(t < Lb ? t : Lb - 1) * D;
-        const void* src = row + (sc ^ (swz(r) & (PROW - 1))) * 8;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(slot + j * 512), 16, 0, POL);
-      }
-    };
     const int swz_k = swz(ql) & (PROW - 1);
     // Upper-bound masses of a scored tile under the current running statistics, summed over the
     // predicted queries; tokens whose bound reaches tau become candidates.  A token's mean reaches
@@ -281,8 +285,6 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     };
     f32x16 sprev[RB];
     int prev_e = 0, prev_nvalid = 0;   // prev_e == 0: nothing pending (tile 0 is never evaluated)
-    int e = e0 + wave;
-    if (e < e1) issue(e);
     for (; e < e1; e += kSinkWaves) {
       wait_vm0();   // this tile's fetches have landed
       if (e == e0) SINK_STAMP(p, 1);
