@@ -230,7 +230,8 @@ hipError_t launch_attn_combine(hipStream_t s, const float* part_o, const float2*
 
 hipError_t launch_fill_u32(hipStream_t s, uint32_t* p, size_t n, uint32_t v);
 
-// Streaming-bandwidth probe (probe.hip): mode 0 read into registers, 1 read by LDS DMA, 2 copy.
+// Streaming-bandwidth probe (probe.hip): mode 0 read into registers, 1 read by LDS DMA, 2 copy,
+// 3 the attention kernels' tile pattern.
 // Read modes write probe_out_words(n_blocks) checksum words to dst.
 size_t probe_out_words(int n_blocks);
 // Tiles mode: bytes of K (and of V) each workgroup streams; 0 when the buffer is too small.
