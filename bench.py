@@ -197,13 +197,15 @@ def step_bytes(cfg, units_per_reuse: int) -> dict:
             "step": cfg.dense_layers * dense + source + n_reuse * reuse, "pool_layer": pool}
 
 
-def stream_reference(h, dev, mib: int = 2048, reps: int = 5, blocks=(0, 768, 8192)) -> dict:
+def stream_reference(h, dev, mib: int = 2048, reps: int = 5, blocks=(0, 768, 8192), layer_bytes: int = 0) -> dict:
     """The rate a plain coalesced stream reaches on this chip (fdl_bandwidth_probe over a buffer far
     larger than the last-level cache): read into registers, read by LDS DMA, and copy; best of reps
     at each grid size in blocks (0 = the probe's default of 4 workgroups per CU), best grid kept.
     The read rate moves by about 10% with the grid size alone, so one grid would understate it.
     "tiles" is the attention kernels' own pattern (one workgroup per CU streaming its own K and V
-    regions, one 16 KiB tile in flight per wave)."""
+    regions, one 16 KiB tile in flight per wave).  With layer_bytes, "tiles_same_size" is that pattern
+    over a buffer of the fused kernel's size, as 20 launches back to back (per launch, gaps included,
+    as the fused kernel's time is taken): what a kernel that only streams those bytes needs."""
     import torch
 
     from diffusion_long_context_amd.fdllm import FDL_PROBE_COPY, FDL_PROBE_READ, FDL_PROBE_READ_LDS, FDL_PROBE_TILES
@@ -230,6 +232,23 @@ def stream_reference(h, dev, mib: int = 2048, reps: int = 5, blocks=(0, 768, 819
             per_grid[str(nb or "default")] = round(moved / best / 1e9, 1)
         res[name + "_GBps"] = max(per_grid.values())
         res[name + "_by_grid"] = per_grid
+    if layer_bytes > 0:
+        nb = (layer_bytes + 1023) & ~1023
+        region = (nb // 2 // n_cu) & ~8191
+        moved = 2 * n_cu * region
+        n_launch, best = 20, None
+        for rep in range(reps + 1):
+            off = (rep % 8) * (n // 4 // 8)   # another part of the buffer each time (int32 elements)
+            part = src[off: off + nb // 4]
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n_launch):
+                h.fdl_bandwidth_probe(FDL_PROBE_TILES, part, chk)
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3 / n_launch
+            best = t if best is None else min(best, t)
+        res["tiles_same_size"] = {"bytes": moved, "us": best * 1e6, "GBps": moved / best / 1e9}
     del src, dst, chk
     return res
 
@@ -885,7 +904,7 @@ def main():
     value = cfg.ctx_len * B * NL * args.steps / t_total
     sb = step_bytes(cfg, units)
     log("streaming reference (bandwidth probe)")
-    sref = stream_reference(h, dev)
+    sref = stream_reference(h, dev, layer_bytes=launch_bytes)
     best_ref = max(sref["read_GBps"], sref["read_lds_GBps"], sref["tiles_GBps"])
     result = {
         "metric": METRIC,
@@ -910,6 +929,7 @@ def main():
                      "avg_launch_us": sparse_us, "launches": prof_main["reuse_run"][1],
                      "bytes_per_launch": launch_bytes, "units_per_launch": units,
                      "unit_bytes": unit_bytes, "frac_of_stream_ref": achieved / best_ref,
+                     "frac_of_same_size_stream": achieved / sref["tiles_same_size"]["GBps"],
                      "mfma": mfma_figures(sparse_us)},
         "step_roofline": {"bytes": sb["step"], "GBps": sb["step"] / (ms_per_step * 1e-3) / 1e9,
                           "frac": sb["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
