@@ -70,10 +70,13 @@ def test_sink_overflow_keeps_the_oracle_truncation(h):
     table = h.make_layers(g, [dict(q=t["q"], k_cache=t["k"], v_cache=t["v"], k_dec=t["k_dec"], v_dec=t["v_dec"],
                                    ks=ks, out=out2, mode=FDL_LAYER_SOURCE)])
     params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, fs.max_sel, cfg.sink_tau)
+    fs.sink_pos.fill_(-7)   # the step writes the list itself (from the detection's bitmap)
+    fs.n_sinks.fill_(-7)
     h.fdl_focus_step(g, params, t["prev_conf"], t["masked"], table, fs.pred_mask, fs.n_pred, fs.scores,
                      fs.sink_pos, fs.n_sinks, fs.sel_idx, fs.n_sel)
     st, bits = h.fdl_get_status_bits()
     assert st == FDL_EOVERFLOW and bits & FLAG_SINK, (st, bits)
+    assert int(host(fs.n_sinks)[0]) == n
     assert host(fs.sink_pos)[0, :n].tolist() == want["sink_pos"][0, :n].tolist()
     for gg in range(cfg.n_kv_heads):
         w = want["sel"][0][gg].tolist()
