@@ -26,6 +26,8 @@ Pin status (what each function is checked against in tests/test_oracle_*.py):
   selection        -- hand-worked case, brute force over subsets, invariants
   sinks            -- row masses sum to 1, planted sinks recovered, pure-Python brute force
   attention        -- closed form, constant-V / zero-K cases, torch SDPA in float64, brute force
-  chunked          -- all chunks + all tokens reduces to dense attention; page-order invariance
+  chunked          -- all chunks + all tokens reduces to dense attention; page-order invariance;
+                      token ranking on a strict chunk subset: hand-worked case and integer brute force;
+                      shared chunks: integer brute force
   agreement of the readings with the authors' own code: parity unpinned (the pages print none)
 """
