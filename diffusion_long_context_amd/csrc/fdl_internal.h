@@ -55,8 +55,9 @@ constexpr size_t kTicketOffset = 4096;
 constexpr int kMaxSplitSegs = 256;
 constexpr int kSyncStride = 64;                  // uint32 words between two heads' sync words
 constexpr size_t kBarrierOffset = kTicketOffset + (size_t)kMaxSplitSegs * kSyncStride * sizeof(uint32_t);
-// Sink detection keeps its candidate counts and bitmap here between calls (zero on entry, zeroed
-// again by the compaction) when they fit.
+// Sink detection keeps its candidate counts and bitmap here between calls when they fit: zero on
+// entry, zeroed again after use (the counts by the scan, the bitmap by the compaction or, in the
+// step driver, by a later fused launch or a fill).
 constexpr size_t kSinkOffset = 256u << 10;
 constexpr size_t kSinkAreaBytes = kHeaderBytes - kSinkOffset;
 static_assert(kBarrierOffset + (size_t)kMaxSplitSegs * kSyncStride * sizeof(uint32_t) <= kSinkOffset,

@@ -7,14 +7,16 @@
 // block's own tokens; a cached token whose mean weight over the predicted positions reaches tau for
 // some head is a sink; the union over heads is the sequence's sink list (ascending).
 //
-// One pass over K (the only full-K read of a step): each wave streams 32-token tiles through bf16
+// One pass over K (the only full-K read of a step): each wave streams 64-token tiles through bf16
 // MFMA (S^T = K Q^T) and keeps a running log-sum-exp per query.  Because a running log-sum-exp never
 // exceeds the final one, the mass a token gets under the running statistics is an upper bound of
 // its true mass, so every token whose bound reaches tau (less a small rounding margin) is recorded
 // as a candidate.  In the same kernel, the last workgroup of each head merges the partial
 // statistics into the exact log-sum-exp, re-scores the head's few candidates in float32 and sets
-// the survivors in a per-sequence bitmap; a second kernel compacts the bitmap into the ascending
-// sink list.
+// the survivors in a per-sequence bitmap.  A second kernel compacts the bitmap into the ascending
+// sink list; in the step driver the fused kernel of the same layer, which runs next, reads the
+// bitmap itself and writes the list.  When the scan is the step's first reader of the predicted
+// query set, it also computes that set (wave 0 of every workgroup) and writes it out.
 #include "fdl_device.h"
 #include "fdl_internal.h"
 #include "fdl_predict.h"
@@ -87,9 +89,10 @@ struct SinkParams {
   int32_t* n_pred_out;
   int pconf_given, ptop_k, pwindow;
   float2* stats;         // [B * Hq][n_splits * 4][32]  (running max in log2 units, running sum)
-  uint32_t* cand_count;  // [B * Hq], zero on entry; sink_compact_kernel zeroes it again
+  uint32_t* cand_count;  // [B * Hq], zero on entry; the head's last split zeroes it again
   uint32_t* cand;        // [B * Hq][cand_cap]  token positions
-  uint32_t* bitmap;      // [B][words], zero on entry; sink_compact_kernel zeroes it again
+  uint32_t* bitmap;      // [B][words], zero on entry; zeroed again by sink_compact_kernel or, in
+                         // the step driver, by a later fused launch (or a fill)
   uint32_t* tickets;     // per (b, q-head), kSyncStride apart; left at zero
   uint32_t* status;
   const int32_t* lens;   // per-sequence cached lengths of a ragged batch, or NULL (all L)
