@@ -57,6 +57,13 @@ def test_null_handle_is_einval(lib):
                                None) == FDL_EINVAL
     assert lib.fdl_dense_attn(None, None, None, None, None, None, None, None, None) == FDL_EINVAL
     assert lib.fdl_create(None, None, 0) == FDL_EINVAL
+    # the measurement and diagnostic calls check their handle first as well
+    assert lib.fdl_bandwidth_probe(None, 0, None, 1024, None, 1024, 0) == FDL_EINVAL
+    assert lib.fdl_set_phase_buffer(None, None, 0) == FDL_EINVAL
+    assert lib.fdl_profile_begin(None, 1, 0, 1) == FDL_EINVAL
+    assert lib.fdl_profile_end(None, None, None) == FDL_EINVAL
+    assert lib.fdl_unmask(None, 1, 32, None, None, 1, None) == FDL_EINVAL
+    assert lib.fdl_capture_begin(None) == FDL_EINVAL
 
 
 def test_status_strings(lib):
