@@ -1228,10 +1228,30 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const float2* ml = part_ml + seg * NS * 32 + qc;
   const float* po = part_o + (seg * NS * 32 + qc) * D + 4 * c;
   float M = -__builtin_inff();
-  for (int t = w; t < NS; t += 4) M = fmaxf(M, ml[t * 32].x);
   float Ls = 0.f;
   float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int t0 = w; t0 < NS; t0 += 4 * NB) {
+  if (NS <= 4 * NB) {   // uniform: every split of this lane's in one round trip, statistics and partials
+    float4 a[NB];
+    float2 v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int t = w + 4 * j < NS ? w + 4 * j : 0;   // reads past NS: split 0, never used
+      a[j] = *reinterpret_cast<const float4*>(po + (int64_t)t * 32 * D);
+      v[j] = ml[t * 32];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (w + 4 * j < NS) M = fmaxf(M, v[j].x);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float wt = (w + 4 * j < NS && v[j].x != -__builtin_inff()) ? exp2f(v[j].x - M) : 0.f;
+      Ls += v[j].y * wt;
+      O.x += a[j].x * wt; O.y += a[j].y * wt; O.z += a[j].z * wt; O.w += a[j].w * wt;
+    }
+  }
+  if (NS > 4 * NB)   // uniform: the statistics first, then the partials in batches
+    for (int t = w; t < NS; t += 4) M = fmaxf(M, ml[t * 32].x);
+  for (int t0 = (NS <= 4 * NB ? NS : w); t0 < NS; t0 += 4 * NB) {
     float4 a[NB];
     float2 v[NB];
 #pragma unroll
