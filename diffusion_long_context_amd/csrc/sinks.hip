@@ -414,26 +414,48 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
       }
       return;
     }
+    // later loads miss L1 and read the other splits' statistics and candidates from L2 (no wait:
+    // the invalidation is ordered before them)
     asm volatile("buffer_inv sc0" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);
   } else {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   if (n_pred == 0) return;
+  // What the re-scoring needs is requested before the log-sum-exp merge waits for its statistics:
+  // the head's candidate count, each wave's first candidate and, once that is back, its key row
+  // (lane (q, hh) the half hh of the row; the queries are still in the MFMA fragments qf).  Reads
+  // past the count are clamped in bounds and never used.
+  const int count_raw = (int)__hip_atomic_load(&p.cand_count[seg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t* cand_row = p.cand + (int64_t)seg * p.cand_cap;
+  auto load_key_half = [&](uint32_t t, uint4 (&kr)[KS]) {
+    const uint16_t* row = kctx + (int64_t)(t < (uint32_t)p.L ? t : 0u) * D + hh * (D / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[ks] = *reinterpret_cast<const uint4*>(row + ks * 8);
+  };
+  const uint32_t t_first = cand_row[wave < p.cand_cap ? wave : p.cand_cap - 1];
+  uint4 kr[KS];
   {
     // exact log-sum-exp per query: thread (q, j) merges parts j, j + 8, ...; then 8 -> 1
     const int q = tid & 31, j = tid >> 5;
     float M = -__builtin_inff(), S = 0.f;
     // the parts j, j + 8, ... are loaded kPartBatch at a time before any is used
     constexpr int kPartBatch = 8;
-    for (int i0 = j; i0 < n_parts; i0 += 8 * kPartBatch) {
-      float2 v[kPartBatch];
+    float2 v[kPartBatch];
+    auto load_parts = [&](int i0) {
 #pragma unroll
       for (int u = 0; u < kPartBatch; ++u) {
         const int i = i0 + 8 * u;
         v[u] = p.stats[((int64_t)seg * n_parts + (i < n_parts ? i : j)) * 32 + q];
       }
+    };
+    load_parts(j);
+    __builtin_amdgcn_sched_barrier(0);
+    // the first candidate's key row goes out as soon as its index is back (the statistics stay in
+    // flight: they were requested after it)
+    load_key_half(t_first, kr);
+    for (int i0 = j; i0 < n_parts; i0 += 8 * kPartBatch) {
+      if (i0 != j) load_parts(i0);
 #pragma unroll
       for (int u = 0; u < kPartBatch; ++u) {
         if (i0 + 8 * u >= n_parts) break;
@@ -462,34 +484,35 @@ __global__ __launch_bounds__(kSinkWaves * 64, 2) void sink_scan_kernel(const Sin
     __syncthreads();
     SINK_STAMP(p, 5);
   }
-  // re-score this head's candidates exactly: one wave per candidate, lane = predicted position
-  int count = (int)__hip_atomic_load(&p.cand_count[seg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  count = count < p.cand_cap ? count : p.cand_cap;
-  const uint16_t* qh = p.q + (int64_t)seg * p.T * D;
+  // re-score this head's candidates exactly (float32), one wave per candidate: lane (q, hh) takes
+  // the dot product of query q with half hh of the key row (four interleaved partial sums), the two
+  // halves meet across the row pair, and the 32 queries' probabilities are summed by lane swaps
+  const int count = count_raw < p.cand_cap ? count_raw : p.cand_cap;
+  const bool qlive = ql < p.T && ((pred >> ql) & 1ull);
   for (int c = wave; c < count; c += kSinkWaves) {
-    const int t = (int)p.cand[(int64_t)seg * p.cand_cap + c];
-    float e = 0.f;
-    if (lane < p.T && ((pred >> lane) & 1ull)) {
-      const uint16_t* qr = qh + (int64_t)lane * D;
-      const uint16_t* kr = kctx + (int64_t)t * D;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < D; d += 8) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(qr + d);
-        const uint4 ka2 = *reinterpret_cast<const uint4*>(kr + d);
-        const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
-        const uint32_t kw[4] = {ka2.x, ka2.y, ka2.z, ka2.w};
+    const uint32_t t = c == wave ? t_first : cand_row[c];
+    if (c != wave) load_key_half(t, kr);
+    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc += bf16_bits_to_f32(qw[i] & 0xFFFFu) * bf16_bits_to_f32(kw[i] & 0xFFFFu);
-          acc += bf16_bits_to_f32(qw[i] >> 16) * bf16_bits_to_f32(kw[i] >> 16);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 qa = __builtin_bit_cast(uint4, qf[ks]);
+      const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
+      const uint32_t kw[4] = {kr[ks].x, kr[ks].y, kr[ks].z, kr[ks].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc4[i] += bf16_bits_to_f32(qw[i] & 0xFFFFu) * bf16_bits_to_f32(kw[i] & 0xFFFFu);
+        acc4[i] += bf16_bits_to_f32(qw[i] >> 16) * bf16_bits_to_f32(kw[i] >> 16);
       }
-      e = exp2f(acc * p.scale_log2 - s_lse[lane]);
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) e += wave_shfl_xor(e, o);
-    if (lane == 0 && e / (float)n_pred >= p.tau)
+    float dot = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    dot += lane_xor32f(dot);
+    float e = (hh == 0 && qlive) ? exp2f(dot * p.scale_log2 - s_lse[ql]) : 0.f;
+    e += __uint_as_float(lane_xor<1>(__float_as_uint(e)));
+    e += __uint_as_float(lane_xor<2>(__float_as_uint(e)));
+    e += __uint_as_float(lane_xor<4>(__float_as_uint(e)));
+    e += __uint_as_float(lane_xor<8>(__float_as_uint(e)));
+    e += __uint_as_float(lane_xor<16>(__float_as_uint(e)));
+    if (lane == 0 && e / (float)n_pred >= p.tau && t < (uint32_t)Lb)
       atomicOr(&p.bitmap[(int64_t)b * p.words + (t >> 5)], 1u << (t & 31));
   }
   // this head's candidates are consumed (every thread read the count before the loop): its count
