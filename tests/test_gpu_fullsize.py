@@ -141,11 +141,15 @@ def test_chunked_paged_32k_batch4_full():
         h.close()
 
 
+INDEX_STEPS = (0, 1, 31, 32, 37, 255)   # first and second step, both sides of a block boundary, the last
+
+
 def test_focus_step_32k_every_sparse_layer_selection():
-    """Index parity at every sparse layer of one benchmarked 32K step (generation step 37, mid block):
-    the step is run cut after each of layers 2 .. 31 and that layer's block scores and selection are
-    compared bit for bit with the oracle's (scores and selection only: the outputs of the sampled
-    layers are checked in the test above)."""
+    """Index parity at every sparse layer of the benchmarked 32K step, at six generation steps (the
+    first two, the last of block 0 and the first of block 1, one mid block, the last): each step is
+    run cut after each of layers 2 .. 31 and that layer's block scores and selection are compared bit
+    for bit with the oracle's, as are the predicted positions and the sinks (scores and selection
+    only: the outputs of the sampled layers are checked in the test above)."""
     require_gpu()
     from diffusion_long_context_amd import Handle
     from diffusion_long_context_amd.fdllm import (FDL_LAYER_DENSE, FDL_LAYER_REUSE, FDL_LAYER_SOURCE,
@@ -158,11 +162,10 @@ def test_focus_step_32k_every_sparse_layer_selection():
     NL, B, Hq, Hkv, D, T = cfg.n_layers, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len
     n_blk, max_sel = cfg.n_blk, cfg.max_sel_blocks
     devc = torch.device("cuda")
-    gstep, i = 37, 1
     h = Handle(workspace_bytes=bench.WORKSPACE_BYTES)
     try:
         K, V = zip(*[layer_kv(cfg, layer, devc) for layer in range(NL)])
-        Q, KD, VD = step_qkv_pool(cfg, 2, devc)
+        Q, KD, VD = step_qkv_pool(cfg, len(INDEX_STEPS), devc)
         ks = [torch.zeros((B, Hkv, n_blk, D), dtype=torch.float32, device=devc) for _ in range(NL)]
         outs = [torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device=devc) for _ in range(NL)]
         pred_mask = torch.zeros(B, dtype=torch.int64, device=devc)
@@ -178,37 +181,46 @@ def test_focus_step_32k_every_sparse_layer_selection():
                  (FDL_LAYER_SOURCE if l == cfg.source_layer else FDL_LAYER_REUSE) for l in range(NL)]
         for layer in range(NL):
             h.fdl_pool_keys(g, K[layer], None, cfg.kv_block, ks[layer])
-        st = schedule_state(cfg, gstep)
-        conf = None if st["prev_conf"] is None else torch.from_numpy(st["prev_conf"]).to(devc)
-        masked = torch.from_numpy(st["masked"]).to(devc)
-        table = h.make_layers(g, [dict(q=Q[i, l], k_cache=K[l], v_cache=V[l], k_dec=KD[i, l], v_dec=VD[i, l],
-                                       ks=ks[l], out=outs[l], mode=m) for l, m in enumerate(modes)])
-        got = {}
-        for lc in range(cfg.dense_layers, NL):
-            sub = (table._type_ * (lc + 1))(*table[:lc + 1]) if lc + 1 < NL else table
-            h.fdl_focus_step(g, params, conf, masked, sub, pred_mask, n_pred, scores, sink_pos, n_sinks,
-                             sel_idx, n_sel)
-            torch.cuda.synchronize()
-            assert h.fdl_get_status() == 0
-            got[lc] = (host(scores).copy(), host(sel_idx).copy(), host(n_sel).copy())
-        got_pred = host(pred_mask).view(np.uint64)
-        sinks = None
-        for l in range(cfg.dense_layers, NL):
-            print(f"step {gstep}: layer {l} against the oracle", flush=True)
-            k_h = _bits(K[l])
-            x = {"q": _bits(Q[i, l]), "k": k_h, "v": None, "k_dec": _bits(KD[i, l]), "v_dec": None,
-                 "prev_conf": st["prev_conf"], "masked": st["masked"]}
-            mode = "source" if l == cfg.source_layer else "reuse"
-            want = focus_layer_step(cfg, x, mode, sinks=sinks, ks=pool_keys(k_h, cfg.kv_block), with_output=False)
-            assert np.array_equal(got_pred, np.asarray(want["pred_mask"], np.uint64)), l
-            if mode == "source":
-                assert want["sink_margin"] > 1e-4 * cfg.sink_tau
-                sinks = (want["sink_pos"], want["n_sinks"])
-            c_scores, c_sel, c_nsel = got[l]
-            assert np.array_equal(c_scores.view(np.uint32), want["scores"].view(np.uint32)), l
-            for gh in range(Hkv):
-                w = want["sel"][0][gh].tolist()
-                assert int(c_nsel[0, gh]) == len(w), (l, gh)
-                assert c_sel[0, gh, : len(w)].tolist() == w, (l, gh)
+        # the cache side is the same at every step: the oracle's keys and pooled keys once per layer
+        k_host = {l: _bits(K[l]) for l in range(cfg.dense_layers, NL)}
+        ks_host = {l: pool_keys(k_host[l], cfg.kv_block) for l in k_host}
+        for i, gstep in enumerate(INDEX_STEPS):
+            st = schedule_state(cfg, gstep)
+            conf = None if st["prev_conf"] is None else torch.from_numpy(st["prev_conf"]).to(devc)
+            masked = torch.from_numpy(st["masked"]).to(devc)
+            table = h.make_layers(g, [dict(q=Q[i, l], k_cache=K[l], v_cache=V[l], k_dec=KD[i, l], v_dec=VD[i, l],
+                                           ks=ks[l], out=outs[l], mode=m) for l, m in enumerate(modes)])
+            got = {}
+            for lc in range(cfg.dense_layers, NL):
+                sub = (table._type_ * (lc + 1))(*table[:lc + 1]) if lc + 1 < NL else table
+                sink_pos.fill_(-7)   # sentinels: the step must write the list and its length
+                n_sinks.fill_(-7)
+                h.fdl_focus_step(g, params, conf, masked, sub, pred_mask, n_pred, scores, sink_pos, n_sinks,
+                                 sel_idx, n_sel)
+                torch.cuda.synchronize()
+                assert h.fdl_get_status() == 0
+                got[lc] = (host(scores).copy(), host(sel_idx).copy(), host(n_sel).copy(), host(sink_pos).copy(),
+                           host(n_sinks).copy())
+            got_pred = host(pred_mask).view(np.uint64)
+            sinks = None
+            print(f"step {gstep}: layers {cfg.dense_layers}..{NL - 1} against the oracle", flush=True)
+            for l in range(cfg.dense_layers, NL):
+                x = {"q": _bits(Q[i, l]), "k": k_host[l], "v": None, "k_dec": _bits(KD[i, l]), "v_dec": None,
+                     "prev_conf": st["prev_conf"], "masked": st["masked"]}
+                mode = "source" if l == cfg.source_layer else "reuse"
+                want = focus_layer_step(cfg, x, mode, sinks=sinks, ks=ks_host[l], with_output=False)
+                assert np.array_equal(got_pred, np.asarray(want["pred_mask"], np.uint64)), (gstep, l)
+                if mode == "source":
+                    assert want["sink_margin"] > 1e-4 * cfg.sink_tau, (gstep, "flagged case: sink margin")
+                    sinks = (want["sink_pos"], want["n_sinks"])
+                c_scores, c_sel, c_nsel, c_sp, c_ns = got[l]
+                nsk = int(np.asarray(sinks[1])[0])
+                want_sp = np.asarray(sinks[0])[0, :nsk].tolist()
+                assert int(c_ns[0]) == nsk and c_sp[0, :nsk].tolist() == want_sp, (gstep, l)
+                assert np.array_equal(c_scores.view(np.uint32), want["scores"].view(np.uint32)), (gstep, l)
+                for gh in range(Hkv):
+                    w = want["sel"][0][gh].tolist()
+                    assert int(c_nsel[0, gh]) == len(w), (gstep, l, gh)
+                    assert c_sel[0, gh, : len(w)].tolist() == w, (gstep, l, gh)
     finally:
         h.close()
