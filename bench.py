@@ -584,6 +584,76 @@ def phase_timeline(samples: int = 24) -> dict:
     return res
 
 
+def phase_timeline_single(workload: str, samples: int = 18) -> dict:
+    """Phase timeline of the fused score-select-attend kernel on a single-layer workload (the 8K MHA
+    or the 16K grouped-query one, parity-test inputs), from the --phase-stamps library: one
+    fdl_focus_step of a source layer and 8 reuse layers on the same inputs, run `samples` times after
+    2 warm runs; the stamps are those of the last reuse layer.  Per phase: the median over workgroups
+    and the last workgroup, in us since the first workgroup started, averaged over the runs."""
+    import numpy as np
+    import torch
+
+    from diffusion_long_context_amd import fdllm
+    from diffusion_long_context_amd.fdllm import FDL_LAYER_REUSE, FDL_LAYER_SOURCE, fdl_focus_params
+    from diffusion_long_context_amd.step import geom_for
+    from synth import get_config
+    from synth.gen import make_single
+
+    lib = fdllm.load(os.environ.get("FDL_STAMPS_LIB",
+                                    os.path.join(ROOT, "diffusion_long_context_amd", "libfdllm_stamps.so")))
+    assert lib.fdl_phase_stamps_built() == 1, "the stamps library was not built with --phase-stamps"
+    cfg = {"llada8b_8k": get_config(1), "dream7b_gqa_16k": get_config(2)}[workload]
+    g = geom_for(cfg)
+    B, Hq, Hkv, D, T = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.dec_len
+    dev = torch.device("cuda")
+    h = fdllm.Handle(workspace_bytes=WORKSPACE_BYTES)
+    x = make_single(cfg)
+
+    def bf16_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v, kd, vd = (bf16_dev(x[n]) for n in ("q", "k", "v", "k_dec", "v_dec"))
+    ks = torch.zeros((B, Hkv, cfg.n_blk, D), dtype=torch.float32, device=dev)
+    h.fdl_pool_keys(g, k, None, cfg.kv_block, ks)
+    o = torch.zeros((B, Hq, T, D), dtype=torch.bfloat16, device=dev)
+    pm = torch.zeros(B, dtype=torch.int64, device=dev)
+    npd = torch.zeros(B, dtype=torch.int32, device=dev)
+    sc = torch.zeros((B, Hkv, cfg.n_blk), dtype=torch.float32, device=dev)
+    sp = torch.full((B, cfg.max_sinks), -1, dtype=torch.int32, device=dev)
+    nsk = torch.zeros(B, dtype=torch.int32, device=dev)
+    sel = torch.zeros((B, Hkv, cfg.max_sel_blocks), dtype=torch.int32, device=dev)
+    nsel = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    conf, masked = torch.from_numpy(x["prev_conf"]).to(dev), torch.from_numpy(x["masked"]).to(dev)
+    params = fdl_focus_params(cfg.top_k_pos, cfg.window, cfg.top_k_blocks, cfg.max_sinks, cfg.max_sel_blocks,
+                              cfg.sink_tau)
+    W = 4096 * 16
+    stamps = torch.zeros(2 * W, dtype=torch.int64, device=dev)
+    h.fdl_set_phase_buffer(stamps)
+    table = h.make_layers(g, [dict(q=q, k_cache=k, v_cache=v, k_dec=kd, v_dec=vd, ks=ks, out=o, mode=m)
+                              for m in [FDL_LAYER_SOURCE] + [FDL_LAYER_REUSE] * 8])
+    rel = []
+    for i in range(samples + 2):
+        stamps.zero_()
+        h.fdl_focus_step(g, params, conf, masked, table, pm, npd, sc, sp, nsk, sel, nsel)
+        torch.cuda.synchronize()
+        if i < 2:
+            continue
+        a = stamps[:W].view(-1, 16).cpu().numpy()
+        a = a[a[:, 15] < 0].astype(np.float64)
+        rel.append(a[:, :15] - a[:, 0].min())
+    assert h.fdl_get_status() == 0
+    h.fdl_set_phase_buffer(None)
+    h.close()
+    res = {"workload": workload, "samples": len(rel), "workgroups": int(rel[0].shape[0]), "clock_MHz": 100,
+           "phases_us": {}, "last_workgroup_us": {}}
+    for j, name in enumerate(PHASES):
+        med = [np.median(r[:, j][r[:, j] >= 0]) / 100.0 for r in rel if (r[:, j] >= 0).any()]
+        last = [r[:, j][r[:, j] >= 0].max() / 100.0 for r in rel if (r[:, j] >= 0).any()]
+        res["phases_us"][name] = float(np.mean(med)) if med else None
+        res["last_workgroup_us"][name] = float(np.mean(last)) if last else None
+    return res
+
+
 # ---- rocprofv3 output -> the short text summaries kept with the measurements -------------------
 
 def _rocprof_rows(d: str, suffix: str) -> list:
@@ -729,6 +799,8 @@ def main():
     ap.add_argument("--cpu-baseline-child", action="store_true")
     ap.add_argument("--phase-timeline", action="store_true",
                     help="print the fused kernel's phase timeline (needs the --phase-stamps library) and exit")
+    ap.add_argument("--phase-workload", choices=("llada8b_32k_32layer", "llada8b_8k", "dream7b_gqa_16k"),
+                    default="llada8b_32k_32layer", help="with --phase-timeline: the workload")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the run, one plain elementwise copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="markdown summary of a rocprofv3 --stats run; exit")
@@ -758,7 +830,10 @@ def main():
         print(json.dumps(cpu_baseline_child()))
         return
     if args.phase_timeline:
-        print(json.dumps(phase_timeline()), flush=True)
+        if args.phase_workload == "llada8b_32k_32layer":
+            print(json.dumps(phase_timeline()), flush=True)
+        else:
+            print(json.dumps(phase_timeline_single(args.phase_workload)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built",
