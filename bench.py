@@ -944,6 +944,21 @@ def main():
     torch.cuda.synchronize()
     refresh_ms = ra.elapsed_time(rb) / 4
 
+    # ---- the per-step distribution, from a pass of its own (one event between consecutive steps,
+    # so each step carries one event packet; the timed region above has none) -------------------
+    n_dist = min(args.steps, len(arrays) - args.warmup)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for j in range(n_dist):
+        run(args.warmup + j, 1, arrays)
+        evs[j + 1].record()
+    torch.cuda.synchronize()
+    per_step_ms = np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(n_dist)])
+    step_dist = {"steps": n_dist, "mean_ms": float(per_step_ms.mean()),
+                 "p10_ms": float(np.percentile(per_step_ms, 10)), "p50_ms": float(np.percentile(per_step_ms, 50)),
+                 "p90_ms": float(np.percentile(per_step_ms, 90)), "max_ms": float(per_step_ms.max())}
+
     # ---- diagnostics (not the headline): per-kind breakdown, event overhead, dense baseline -------
     log("diagnostic passes")
     i0 = args.warmup
@@ -1019,6 +1034,7 @@ def main():
         "sparse_attn_layer_step_us": sparse_us,
         "sparse_attn_layer_kv_tokens_per_s": cfg.ctx_len * B / (sparse_us * 1e-6),
         "breakdown_us_instrumented": {k: avg_us(prof_all, k) for k in prof_all if prof_all[k][1]},
+        "step_ms_distribution": step_dist,
         "event_overhead_ms_per_step": 1e3 * (ms_per_step / 1e3 - t_plain),
         "dense_step_ms": 1e3 * t_dense_step,
         "speedup_vs_dense_hip": t_dense_step / t_plain,
