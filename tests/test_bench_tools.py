@@ -80,3 +80,23 @@ def test_summarize_counters_scaling_and_traffic_file(tmp_path):
     finally:
         bench.TRAFFIC_FILE = real
 
+
+
+def test_algorithmic_bytes_of_the_32k_layer_and_step():
+    """The byte counts behind the roofline, term by term for the 32K layer with 65 blocks kept per
+    head (the sink block and the top 64): K and V of 2080 selected 64-token blocks, Q and O and the
+    decode block's own K and V (bf16), the selection indices and counts, the pooled keys (float32)
+    and the scores written."""
+    from synth import get_config
+    cfg = get_config(3)
+    units = 32 * 65
+    terms = {"selected K+V": units * 64 * 128 * 2 * 2, "Q+O": 32 * 32 * 128 * 2 * 2,
+             "own K+V": 32 * 32 * 128 * 2 * 2, "indices": units * 4 + 32 * 4,
+             "pooled keys": 32 * 512 * 128 * 4, "scores": 32 * 512 * 4}
+    assert terms["selected K+V"] == 68_157_440 and terms["pooled keys"] == 8_388_608
+    assert bench.sparse_launch_bytes(cfg, units) == sum(terms.values()) == 77_668_608
+    sb = bench.step_bytes(cfg, units)
+    kv = 32 * 32768 * 128 * 2   # one layer's cached K (or V)
+    assert sb["dense_layer"] == 2 * kv + 2 * 524_288
+    assert sb["source_layer"] == 77_668_608 + kv + 32 * 32 * 128 * 2   # the scan reads every K and the block's own
+    assert sb["step"] == 2 * sb["dense_layer"] + sb["source_layer"] + 29 * 77_668_608 == 3_674_594_816
