@@ -29,5 +29,7 @@ Pin status (what each function is checked against in tests/test_oracle_*.py):
   chunked          -- all chunks + all tokens reduces to dense attention; page-order invariance;
                       token ranking on a strict chunk subset: hand-worked case and integer brute force;
                       shared chunks: integer brute force
-  agreement of the readings with the authors' own code: parity unpinned (the pages print none)
+Every function above is pinned.  What no pin can settle is whether the authors' own code takes the
+same readings: the pages print neither formulas nor code, so that stays an open question about the
+readings (each one is listed with its alternatives), not a gap in the oracle's pins.
 """
